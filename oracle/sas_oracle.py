@@ -1,0 +1,517 @@
+"""SAS gated block-sparse attention: plain fp64 CPU oracle.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The product path (the HIP library
+and its Python binding) never calls it, and it shares no code with them.
+
+What it computes (citations name the page and the passage):
+
+* SAS, "Simple Attention Sparsification" abstract (arXiv 2609.13141 landing
+  page, "The abstract"): a lightweight selector scores context blocks per
+  query; Top-K picks historical blocks; the current block is always retained;
+  the selector's continuous scores enter the attention softmax as log gates;
+  gates are normalised by a softmax that includes the current block.
+* GitHub README, intro items (a)/(b): discrete Top-K is kept, and every
+  selected block carries a continuous soft gate inside the attention logits,
+  so the LM loss has a gradient path to the selector.
+* Hugging Face model card, "Checkpoint configuration" table: KV block 64,
+  Top-K 31 historical blocks, gate hidden size 128, query projection Qproj,
+  key block pooling max + min + average, Q/K normalisation, gate RoPE.
+* Chinese usage guide, pitfall 3: the budget caps tokens attended per query,
+  not the KV-cache size.
+
+Readings where the pages are silent (each is listed in the design doc):
+  gate per KV head, gate query = concatenation of the group's G query heads
+  [R1]; gate inputs are the attention q/k before any backbone RoPE [R2];
+  pooled key = [max; min; mean] channel-wise [R3]; the current block is
+  pooled causally over 64c..t, so every query has its own current-block key
+  [R4]; RMSNorm with a learnable weight, eps 1e-6 [R5]; rotate-half RoPE,
+  inv_freq_i = theta^(-2i/dg), query at position t, block key at 64j [R6];
+  bias-free Qproj [R7]; gate logit scale 1/sqrt(dg) [R8]; softmax over all
+  candidate blocks 0..c including the current one [R9]; log g added to every
+  selected block including the current one [R10]; Top-K over complete
+  historical blocks j < c, K_eff = min(K, c) [R11]; ties -> lower index,
+  near-tie = K-th/(K+1)-th gap < 1e-5 [R12]; attention scale 1/sqrt(D),
+  causal inside the current block [R13]; slots ascending, current block last
+  [R14]; budget = 64 (K + 1) [R15]; decode applies log g too (switchable)
+  [R16]; partial last block keyed by its last token's prefix key [R19].
+
+Everything is float64 on numpy arrays.  Inputs are the bf16-rounded values
+the GPU path consumes (or any float arrays for self-checks).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+BLOCK = 64
+NEAR_TIE_GAP = 1e-5
+
+
+def as64(x) -> np.ndarray:
+    """torch tensor or array -> float64 numpy array (copy)."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Router ("lightweight selector"): Qproj, block pooling, Q/K norm, gate RoPE.
+# Model card, "Checkpoint configuration" table.
+# --------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """Root-mean-square normalisation over the last axis, times weight w [R5]."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+
+
+def rope(x: np.ndarray, pos, theta: float) -> np.ndarray:
+    """Rotate-half rotary embedding over the last axis (size dg) [R6].
+
+    Pair (i, i + dg/2) is rotated by angle pos * theta^(-2i/dg).
+    """
+    dg = x.shape[-1]
+    half = dg // 2
+    inv_freq = theta ** (-2.0 * np.arange(half, dtype=np.float64) / dg)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+    cos, sin = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def gate_query(q, wq, w_qn, theta: float, eps: float, tokens=None) -> np.ndarray:
+    """Gate query per (b, t, kappa): RoPE_t(RMSNorm(x_t Wq[kappa]) * w_qn).
+
+    x_t is the concatenation of the group's G query-head vectors [R1, R7].
+    q [B,T,Hq,D], wq [Hkv, G*D, dg] -> [B, n, Hkv, dg] for the chosen tokens.
+    """
+    q = as64(q)
+    wq = as64(wq)
+    B, T, Hq, D = q.shape
+    Hkv = wq.shape[0]
+    G = Hq // Hkv
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    x = q[:, tok].reshape(B, len(tok), Hkv, G * D)
+    y = np.einsum("bnkf,kfg->bnkg", x, wq)
+    y = rms_norm(y, as64(w_qn), eps)
+    return rope(y, tok[None, :, None], theta)
+
+
+def pooled_key(k: np.ndarray, t: int) -> np.ndarray:
+    """[max; min; mean] over keys 64c..t of t's block c, channel-wise [R3, R4].
+
+    k [B,T,Hkv,D] -> [B, Hkv, 3D].
+    """
+    c = t // BLOCK
+    R = k[:, BLOCK * c: t + 1]
+    return np.concatenate([R.max(axis=1), R.min(axis=1), R.mean(axis=1)], axis=-1)
+
+
+def gate_key(k, wk, w_kn, theta: float, eps: float, tokens=None) -> np.ndarray:
+    """Gate key per (b, t, kappa): RoPE_{64c}(RMSNorm(pool_t Wk[kappa]) * w_kn).
+
+    The key of historical block j is the value at its last token 64j+63.
+    k [B,T,Hkv,D], wk [Hkv, 3D, dg] -> [B, n, Hkv, dg].
+    """
+    k = as64(k)
+    wk = as64(wk)
+    B, T, Hkv, D = k.shape
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    out = np.empty((B, len(tok), Hkv, wk.shape[2]))
+    for n, t in enumerate(tok):
+        p = pooled_key(k, int(t))                       # [B, Hkv, 3D]
+        z = np.einsum("bkf,kfg->bkg", p, wk)
+        z = rms_norm(z, as64(w_kn), eps)
+        out[:, n] = rope(z, (int(t) // BLOCK) * BLOCK, theta)
+    return out
+
+
+def block_key_tokens(T: int) -> np.ndarray:
+    """Token whose prefix-pooled key represents each block (its last token) [R19]."""
+    NB = -(-T // BLOCK)
+    return np.minimum(np.arange(NB) * BLOCK + BLOCK - 1, T - 1)
+
+
+# --------------------------------------------------------------------------
+# Candidate softmax and Top-K (abstract: normalised softmax gates calibrate
+# history against the always-retained current block; README (a)/(b)).
+# --------------------------------------------------------------------------
+
+def gate_logits(qg: np.ndarray, kg_hist: np.ndarray, kg_cur: np.ndarray) -> np.ndarray:
+    """s_j = qg . kg_j / sqrt(dg) for historical blocks j < c, then the current block [R8].
+
+    qg [dg], kg_hist [c, dg], kg_cur [dg] -> s [c+1].
+    """
+    dg = qg.shape[-1]
+    return np.concatenate([kg_hist @ qg, [kg_cur @ qg]]) / math.sqrt(dg)
+
+
+def log_gates(s: np.ndarray):
+    """Softmax over all candidates 0..c [R9]: returns (lse, log g)."""
+    m = s.max()
+    lse = m + math.log(np.exp(s - m).sum())
+    return lse, s - lse
+
+
+def select_blocks(s: np.ndarray, K: int):
+    """Top-K historical blocks by score (ties -> lower index) plus the current block.
+
+    s [c+1] (last entry = current block c).  Returns (sel, near_tie): sel is
+    ascending with c last [R11, R12, R14]; near_tie flags a K-th/(K+1)-th
+    gap below 1e-5.
+    """
+    c = len(s) - 1
+    n = min(K, c)
+    order = sorted(range(c), key=lambda j: (-s[j], j))
+    sel = sorted(order[:n]) + [c]
+    near_tie = bool(K >= 1 and c > K and (s[order[K - 1]] - s[order[K]]) < NEAR_TIE_GAP)
+    return sel, near_tie
+
+
+def route(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float, tokens=None):
+    """Router + candidate softmax + selection for the chosen tokens.
+
+    Returns dict with qg [B,n,Hkv,dg], kg_cur [B,n,Hkv,dg], idx [B,n,Hkv,K+1]
+    (pad -1), logg [B,n,Hkv,K+1] (pad -inf), lse [B,n,Hkv], near_tie
+    [B,n,Hkv], s [B,n,Hkv,NB] (-inf beyond c), probs [B,n,Hkv,NB] (0 beyond c).
+    """
+    q = as64(q)
+    k = as64(k)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    NB = -(-T // BLOCK)
+    S = K + 1
+    qg = gate_query(q, wq, w_qn, theta, eps, tok)
+    kg_cur = gate_key(k, wk, w_kn, theta, eps, tok)
+    kblk_tok = block_key_tokens(T)
+    need = sorted({int(kblk_tok[j]) for t in tok for j in range(int(t) // BLOCK)})
+    kblk = {}
+    if need:
+        kg_need = gate_key(k, wk, w_kn, theta, eps, need)
+        for n, t in enumerate(need):
+            kblk[t // BLOCK] = kg_need[:, n]
+    n_tok = len(tok)
+    idx = np.full((B, n_tok, Hkv, S), -1, dtype=np.int64)
+    logg = np.full((B, n_tok, Hkv, S), -np.inf)
+    lse = np.zeros((B, n_tok, Hkv))
+    near = np.zeros((B, n_tok, Hkv), dtype=bool)
+    s_dense = np.full((B, n_tok, Hkv, NB), -np.inf)
+    probs = np.zeros((B, n_tok, Hkv, NB))
+    for n, t in enumerate(tok):
+        c = int(t) // BLOCK
+        for b in range(B):
+            for kv in range(Hkv):
+                hist = (np.stack([kblk[j][b, kv] for j in range(c)]) if c
+                        else np.zeros((0, qg.shape[-1])))
+                s = gate_logits(qg[b, n, kv], hist, kg_cur[b, n, kv])
+                l, lg = log_gates(s)
+                sel, nt = select_blocks(s, K)
+                idx[b, n, kv, :len(sel)] = sel
+                logg[b, n, kv, :len(sel)] = lg[sel]
+                lse[b, n, kv] = l
+                near[b, n, kv] = nt
+                s_dense[b, n, kv, :c + 1] = s
+                probs[b, n, kv, :c + 1] = np.exp(lg)
+    return dict(qg=qg, kg_cur=kg_cur, idx=idx, logg=logg, lse=lse, near_tie=near,
+                s=s_dense, probs=probs, tokens=tok)
+
+
+# --------------------------------------------------------------------------
+# Gated sparse attention: log g inside the softmax logits (abstract; README (b)).
+# --------------------------------------------------------------------------
+
+def _row_keys(t: int, sel_row: np.ndarray):
+    """Key positions of the selected blocks that are <= t, with their slot ids [R13]."""
+    taus, slots = [], []
+    for s_i, j in enumerate(sel_row):
+        j = int(j)
+        if j < 0:
+            continue
+        hi = min(BLOCK * j + BLOCK, t + 1)
+        r = np.arange(BLOCK * j, hi)
+        taus.append(r)
+        slots.append(np.full(len(r), s_i))
+    return np.concatenate(taus), np.concatenate(slots)
+
+
+def attn_fwd_rows(q, k, v, idx, logg, scale: float, tokens=None):
+    """Gather form: per (b, t, kappa), concatenate the selected blocks' keys.
+
+    l_tau = q.k_tau * scale + logg[slot(tau)];  o = softmax(l) V;  lse = logsumexp(l).
+    idx/logg are [B, T, Hkv, S] (full token axis).  Returns o [B,n,Hq,D],
+    lse [B,n,Hq] for the chosen tokens.
+    """
+    q, k, v, logg = as64(q), as64(k), as64(v), as64(logg)
+    idx = np.asarray(idx)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    o = np.zeros((B, len(tok), Hq, D))
+    lse = np.zeros((B, len(tok), Hq))
+    for n, t in enumerate(tok):
+        t = int(t)
+        for b in range(B):
+            for kv in range(Hkv):
+                taus, slots = _row_keys(t, idx[b, t, kv])
+                Kr, Vr = k[b, taus, kv], v[b, taus, kv]
+                bias = logg[b, t, kv, slots]
+                Q = q[b, t, kv * G:(kv + 1) * G]             # [G, D]
+                L = Q @ Kr.T * scale + bias                    # [G, n]
+                m = L.max(axis=1, keepdims=True)
+                P = np.exp(L - m)
+                l = P.sum(axis=1, keepdims=True)
+                o[b, n, kv * G:(kv + 1) * G] = (P / l) @ Vr
+                lse[b, n, kv * G:(kv + 1) * G] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def dense_bias(idx, logg, T: int) -> np.ndarray:
+    """Dense-masked form: bias [B, Hkv, T, T] = logg of the key's block when the
+    block is selected by the query and tau <= t, else -inf."""
+    idx = np.asarray(idx)
+    logg = as64(logg)
+    B, _, Hkv, S = idx.shape
+    bias = np.full((B, Hkv, T, T), -np.inf)
+    for b in range(B):
+        for t in range(T):
+            for kv in range(Hkv):
+                for s_i in range(S):
+                    j = int(idx[b, t, kv, s_i])
+                    if j < 0:
+                        continue
+                    hi = min(BLOCK * j + BLOCK, t + 1)
+                    bias[b, kv, t, BLOCK * j:hi] = logg[b, t, kv, s_i]
+    return bias
+
+
+def attn_fwd_dense(q, k, v, idx, logg, scale: float):
+    """Dense-masked form: full T x T logits per head plus the block bias, row softmax."""
+    q, k, v = as64(q), as64(k), as64(v)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    bias = dense_bias(idx, logg, T)
+    o = np.zeros_like(q)
+    lse = np.zeros((B, T, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            L = q[b, :, h] @ k[b, :, kv].T * scale + bias[b, kv]
+            m = L.max(axis=1, keepdims=True)
+            P = np.exp(L - m)
+            l = P.sum(axis=1, keepdims=True)
+            o[b, :, h] = (P / l) @ v[b, :, kv]
+            lse[b, :, h] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def attn_bwd(q, k, v, dout, idx, logg, scale: float):
+    """Backward of the gather form for all rows (small T).
+
+    dP = dO.v;  Delta = dO.o;  dS = P (dP - Delta);
+    dq = scale sum dS k;  dk += scale dS q;  dv += P dO;
+    dlogg[slot] = sum over the group's heads and the block's keys of dS
+    (README (b): the gradient reaching the selector through log g).
+    Returns dict(o, lse, dq, dk, dv, dlogg).
+    """
+    q, k, v, dout, logg = as64(q), as64(k), as64(v), as64(dout), as64(logg)
+    idx = np.asarray(idx)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    S = idx.shape[-1]
+    o = np.zeros_like(q)
+    lse = np.zeros((B, T, Hq))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dlogg = np.zeros((B, T, Hkv, S))
+    for b in range(B):
+        for t in range(T):
+            for kv in range(Hkv):
+                taus, slots = _row_keys(t, idx[b, t, kv])
+                Kr, Vr = k[b, taus, kv], v[b, taus, kv]
+                bias = logg[b, t, kv, slots]
+                hs = slice(kv * G, (kv + 1) * G)
+                Q, dO = q[b, t, hs], dout[b, t, hs]
+                L = Q @ Kr.T * scale + bias
+                m = L.max(axis=1, keepdims=True)
+                E = np.exp(L - m)
+                l = E.sum(axis=1, keepdims=True)
+                P = E / l
+                O = P @ Vr
+                o[b, t, hs] = O
+                lse[b, t, hs] = (m + np.log(l))[:, 0]
+                dP = dO @ Vr.T
+                delta = (dO * O).sum(axis=1, keepdims=True)
+                dS = P * (dP - delta)                       # [G, n]
+                dq[b, t, hs] = scale * dS @ Kr
+                np.add.at(dk[b, :, kv], taus, scale * dS.T @ Q)
+                np.add.at(dv[b, :, kv], taus, P.T @ dO)
+                np.add.at(dlogg[b, t, kv], slots, dS.sum(axis=0))
+    pad = idx < 0
+    dlogg[pad] = 0.0
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, dlogg=dlogg)
+
+
+def attn_bwd_rows(q, k, v, dout, idx, logg, scale: float, tokens):
+    """dq [B,n,Hq,D] and dlogg [B,n,Hkv,S] for chosen query tokens (gather form)."""
+    q, k, v, dout, logg = as64(q), as64(k), as64(v), as64(dout), as64(logg)
+    idx = np.asarray(idx)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    S = idx.shape[-1]
+    tok = np.asarray(tokens)
+    dq = np.zeros((B, len(tok), Hq, D))
+    dlogg = np.zeros((B, len(tok), Hkv, S))
+    for n, t in enumerate(tok):
+        t = int(t)
+        for b in range(B):
+            for kv in range(Hkv):
+                taus, slots = _row_keys(t, idx[b, t, kv])
+                Kr, Vr = k[b, taus, kv], v[b, taus, kv]
+                hs = slice(kv * G, (kv + 1) * G)
+                Q, dO = q[b, t, hs], dout[b, t, hs]
+                L = Q @ Kr.T * scale + logg[b, t, kv, slots]
+                P = np.exp(L - L.max(axis=1, keepdims=True))
+                P /= P.sum(axis=1, keepdims=True)
+                O = P @ Vr
+                dS = P * (dO @ Vr.T - (dO * O).sum(axis=1, keepdims=True))
+                dq[b, n, hs] = scale * dS @ Kr
+                np.add.at(dlogg[b, n, kv], slots, dS.sum(axis=0))
+    return dq, dlogg
+
+
+def attn_bwd_block(q, k, v, dout, idx, logg, scale: float, b: int, kv: int, j: int):
+    """dk, dv [64, D] of KV block j of head kv (batch b): sums over every query
+    row that selected block j (its P needs that row's full softmax)."""
+    q, k, v, dout, logg = as64(q), as64(k), as64(v), as64(dout), as64(logg)
+    idx = np.asarray(idx)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    lo, hi = BLOCK * j, min(BLOCK * j + BLOCK, T)
+    dk = np.zeros((hi - lo, D))
+    dv = np.zeros((hi - lo, D))
+    rows = np.nonzero((idx[b, :, kv, :] == j).any(axis=1))[0]
+    for t in rows:
+        t = int(t)
+        taus, slots = _row_keys(t, idx[b, t, kv])
+        Kr, Vr = k[b, taus, kv], v[b, taus, kv]
+        hs = slice(kv * G, (kv + 1) * G)
+        Q, dO = q[b, t, hs], dout[b, t, hs]
+        L = Q @ Kr.T * scale + logg[b, t, kv, slots]
+        P = np.exp(L - L.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        O = P @ Vr
+        dS = P * (dO @ Vr.T - (dO * O).sum(axis=1, keepdims=True))
+        inb = (taus >= lo) & (taus < hi)
+        tb = taus[inb] - lo
+        np.add.at(dk, tb, scale * dS[:, inb].T @ Q)
+        np.add.at(dv, tb, P[:, inb].T @ dO)
+    return dk, dv
+
+
+def gate_logit_grad(dlogg, idx, probs) -> np.ndarray:
+    """Gradient reaching the gate logits s through log g = s - lse(s) [R18]:
+    ds_j = dlogg_j [j selected] - g_j * sum over selected i of dlogg_i, for j <= c.
+
+    dlogg, idx [..., S]; probs [..., NB] (0 beyond c) -> ds [..., NB].
+    """
+    dlogg = as64(dlogg)
+    idx = np.asarray(idx)
+    probs = as64(probs)
+    ds = np.zeros_like(probs)
+    tot = np.where(idx >= 0, dlogg, 0.0).sum(axis=-1)
+    flat_ds = ds.reshape(-1, ds.shape[-1])
+    flat_idx = idx.reshape(-1, idx.shape[-1])
+    flat_dl = dlogg.reshape(-1, dlogg.shape[-1])
+    for r in range(flat_ds.shape[0]):
+        for s_i, j in enumerate(flat_idx[r]):
+            if j >= 0:
+                flat_ds[r, j] += flat_dl[r, s_i]
+    ds -= probs * tot[..., None]
+    return ds
+
+
+# --------------------------------------------------------------------------
+# Budgeted single-token decode (model card: sparse decode budget 1,024 /
+# 2,048 / 4,096 tokens; usage guide pitfall 3: the budget bounds attended
+# tokens per query, not the cache).
+# --------------------------------------------------------------------------
+
+def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, K: int, scale: float,
+           apply_gate: bool = True, units=None):
+    """One decode step per sequence.
+
+    q [B,Hq,D]; q_gate [B,Hkv,dg]; k_cache, v_cache [B,Hkv,Lmax,D];
+    kg_cache [B,Hkv,NBmax,dg] (entry c = current block's prefix-pooled key);
+    ctx_len [B] counts the new token (at position L-1).
+    Returns o [B,Hq,D], idx [B,Hkv,K+1], logg [B,Hkv,K+1], near_tie [B,Hkv]
+    for the chosen (b, kappa) units (others left zero / -1).
+    apply_gate=False is the selection-only variant [R16].
+    """
+    q, q_gate = as64(q), as64(q_gate)
+    ctx = np.asarray(ctx_len.cpu() if hasattr(ctx_len, "cpu") else ctx_len)
+    B, Hq, D = q.shape
+    Hkv = q_gate.shape[1]
+    G = Hq // Hkv
+    S = K + 1
+    o = np.zeros((B, Hq, D))
+    idx = np.full((B, Hkv, S), -1, dtype=np.int64)
+    logg = np.full((B, Hkv, S), -np.inf)
+    near = np.zeros((B, Hkv), dtype=bool)
+    if units is None:
+        units = [(b, kv) for b in range(B) for kv in range(Hkv)]
+    for b, kv in units:
+        L = int(ctx[b])
+        t = L - 1
+        c = t // BLOCK
+        kg = as64(kg_cache[b, kv, :c + 1])
+        s = gate_logits(q_gate[b, kv], kg[:c], kg[c])
+        _, lg = log_gates(s)
+        sel, nt = select_blocks(s, K)
+        idx[b, kv, :len(sel)] = sel
+        logg[b, kv, :len(sel)] = lg[sel]
+        near[b, kv] = nt
+        taus, slots = _row_keys(t, np.array(sel))
+        Kr = as64(k_cache[b, kv, taus])
+        Vr = as64(v_cache[b, kv, taus])
+        bias = lg[np.array(sel)][slots] if apply_gate else np.zeros(len(taus))
+        Q = q[b, kv * G:(kv + 1) * G]
+        Lg = Q @ Kr.T * scale + bias
+        P = np.exp(Lg - Lg.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        o[b, kv * G:(kv + 1) * G] = P @ Vr
+    return dict(o=o, idx=idx, logg=logg, near_tie=near)
+
+
+# --------------------------------------------------------------------------
+# Router size (model card, "Released checkpoints" table).
+# --------------------------------------------------------------------------
+
+def router_param_count(Hq: int, Hkv: int, D: int, dg: int, layers: int,
+                       norm_weights: bool = True) -> int:
+    """Per layer: Qproj Hkv x (G*D) x dg, Kproj Hkv x 3D x dg over [max;min;mean],
+    plus the two dg-wide RMSNorm weights."""
+    G = Hq // Hkv
+    per = Hkv * G * D * dg + Hkv * 3 * D * dg + (2 * dg if norm_weights else 0)
+    return per * layers
+
+
+def brute_force_topk(s_hist, K: int):
+    """Tiny-input reference: the K-subset of historical blocks with the largest
+    score sum; among equal sums the lexicographically smallest ascending subset."""
+    c = len(s_hist)
+    n = min(K, c)
+    best, best_key = None, None
+    for comb in itertools.combinations(range(c), n):
+        key = (-sum(s_hist[j] for j in comb), comb)
+        if best_key is None or key < best_key:
+            best, best_key = comb, key
+    return list(best)
