@@ -1,0 +1,331 @@
+"""Benchmark of the SAS gated block-sparse attention hot path on one MI355X.
+
+One step = one training-layer pass of the whole prefill path on the 32K
+workload (Qwen3-4B attention shape: B=1, T=32768, 32 query / 8 KV heads,
+head dim 128, gate hidden 128, KV block 64, Top-31 + current block):
+gate router -> candidate softmax + Top-K -> sparse attention forward ->
+sparse attention backward (dQ, dK, dV, d log g).  The budgeted decode
+(64 sequences, Qwen3-8B shape, contexts U[8192, 65536], budget 2048) is
+timed in the same run and reported in the "decode" object.
+
+value = effective fwd+bwd attention FLOPs / whole-step time, where the
+effective FLOPs count 4*D (forward) + 10*D (backward) per attended
+(query head, key) pair; router and selection time is inside the step time.
+
+Prints ONE JSON line.  Inputs are synthetic, seeded, resident in HBM before
+the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def attended_pairs(T: int, K: int, block: int = 64) -> int:
+    """Sum over query tokens t of attended keys n_t = 64 min(K, c) + (t mod 64) + 1."""
+    tot = 0
+    for t in range(T):
+        c = t // block
+        tot += block * min(K, c) + (t - block * c) + 1
+    return tot
+
+
+def decode_bytes(ctx_len, Hkv, D, dg, K, G, block=64):
+    """Algorithmic bytes of one decode step: selected K/V blocks (only keys < L),
+    the c+1 gate keys per (sequence, KV head), q, q_gate and o."""
+    kv = 0
+    gk = 0
+    for L in ctx_len:
+        c = (L - 1) // block
+        n_cur = L - block * c
+        kv += (block * min(K, c) + n_cur) * D * 2 * 2 * Hkv
+        gk += (c + 1) * dg * 4 * Hkv
+    B = len(ctx_len)
+    small = B * Hkv * (G * D * 2 * 2 + dg * 4)
+    return kv, gk, small
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, src_hash: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE
+    (profiles/traffic.json), only if taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(kernel_key)
+        if e and e.get("source_hash") == src_hash:
+            return e.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def cpu_baseline(seed: int, n_tokens: int):
+    """The fp64 oracle, as it stands, on a bounded sample of the 32K workload:
+    forward + backward of every query head for n_tokens query tokens spread
+    over the sequence (all 8 KV heads), BLAS limited to one thread."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import sas_oracle as O
+
+    w = synth.TRAIN_32K
+    x = synth.prefill_inputs(w, seed=seed, device="cpu")
+    x64 = {k: O.as64(v) for k, v in x.items()}
+    T = w.T
+    toks = np.unique(np.linspace(64 * (w.topk + 2), T - 1, n_tokens).astype(int))
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        r = O.route(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"], w.topk,
+                    w.theta, w.eps, tokens=toks)
+        S = w.topk + 1
+        idx = np.full((w.B, T, w.Hkv, S), -1, dtype=np.int64)
+        logg = np.full((w.B, T, w.Hkv, S), -np.inf)
+        idx[:, toks] = r["idx"]
+        logg[:, toks] = r["logg"]
+        sc = 1.0 / math.sqrt(w.D)
+        t0 = time.perf_counter()
+        O.attn_bwd(x64["q"], x64["k"], x64["v"], x64["dout"], idx, logg, sc, tokens=toks)
+        dt = time.perf_counter() - t0
+    flops = 0
+    for t in toks:
+        c = t // 64
+        n = 64 * min(w.topk, c) + (t - 64 * c) + 1
+        flops += 14 * w.D * n * w.Hq
+    return dict(value=float(round(flops / dt / 1e12, 6)), unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"{len(toks)} query tokens x {w.Hq} heads of the 32K training layer, "
+                       f"fp64 forward+backward (numpy, 1 BLAS thread), {dt:.1f} s",
+                seconds=round(dt, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--cpu-tokens", type=int, default=160)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards over batch x KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_block_sparse_gate_amd as sas
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sas.load_library()
+
+    # ------------------------------------------------------------ training layer
+    w = synth.TRAIN_32K
+    x = synth.prefill_inputs(w, seed=args.seed, device=dev)
+    B, T, Hq, Hkv, D, dg, K = w.B, w.T, w.Hq, w.Hkv, w.D, w.dg, w.topk
+    S = K + 1
+    NB = w.NB
+    scale = 1.0 / math.sqrt(D)
+    d = sas.make_dims(B, T, Hq, Hkv, D, dg, K, w.theta, w.eps)
+    ws_gate = torch.empty(sas.workspace_size(sas.OP_GATE_SCORE, d), dtype=torch.uint8, device=dev)
+    ws_bwd = torch.empty(sas.workspace_size(sas.OP_BWD, d), dtype=torch.uint8, device=dev)
+    qg = torch.empty((B, T, Hkv, dg), dtype=torch.float32, device=dev)
+    kg = torch.empty_like(qg)
+    idx = torch.empty((B, T, Hkv, S), dtype=torch.int32, device=dev)
+    logg = torch.empty((B, T, Hkv, S), dtype=torch.float32, device=dev)
+    glse = torch.empty((B, T, Hkv), dtype=torch.float32, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(x["q"])
+    dk = torch.empty_like(x["k"])
+    dv = torch.empty_like(x["v"])
+    dlogg = torch.empty_like(logg)
+    stream = torch.cuda.current_stream(dev)
+
+    ev = None
+
+    def step(record=False):
+        if record:
+            ev[0].record(stream)
+        sas.gate_score(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], K, w.theta, w.eps,
+                       q_gate=qg, k_gate=kg, workspace=ws_gate)
+        if record:
+            ev[1].record(stream)
+        sas.topk_blocks(qg, kg, K, Hq, D, out=(idx, logg, glse))
+        if record:
+            ev[2].record(stream)
+        sas.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, logg, scale, o=o, lse=lse)
+        if record:
+            ev[3].record(stream)
+        sas.sparse_attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, scale,
+                            workspace=ws_bwd, out=(dq, dk, dv, dlogg))
+        if record:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stage_ms = [0.0] * 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev = evs[i]
+        step(record=True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    for i in range(args.steps):
+        for s_ in range(4):
+            stage_ms[s_] += evs[i][s_].elapsed_time(evs[i][s_ + 1]) / args.steps
+    ms_per_step = total_ms / args.steps
+
+    pairs = attended_pairs(T, K) * Hq * B
+    fwd_flops = 4.0 * D * pairs
+    bwd_flops = 10.0 * D * pairs
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = fwd_flops / (stage_ms[2] * 1e-3) / 1e12
+    bwd_tflops = bwd_flops / (stage_ms[3] * 1e-3) / 1e12
+    attn_tflops = (fwd_flops + bwd_flops) / ((stage_ms[2] + stage_ms[3]) * 1e-3) / 1e12
+
+    csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
+    fwd_hash = source_hash([os.path.join(csrc, f) for f in ("attn_fwd.hip", "sas_device.h",
+                                                            "sas_kernels.h")])
+    roofline = {
+        "kernel": "sparse_fwd_kernel (sas_sparse_attn_fwd: one launch per call)",
+        "bound": "mfma",
+        "achieved": round(fwd_tflops, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": load_traffic("sparse_fwd_kernel", fwd_hash),
+        "algorithmic_flops_per_launch": fwd_flops,
+        "launch_ms": round(stage_ms[2], 4),
+    }
+
+    out = {
+        "metric": "sparse-attn fwd+bwd TFLOP/s @32K (% MFMA peak); decode KV GB/s @budget 2048",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v/dO, N(0,1)/sqrt(fan_in) bf16 router weights)",
+        "config": {"workload": w.name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D, "dg": dg,
+                   "block": 64, "topk": K, "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "stages_ms": {"gate_score": round(stage_ms[0], 4), "topk": round(stage_ms[1], 4),
+                      "fwd": round(stage_ms[2], 4), "bwd": round(stage_ms[3], 4)},
+        "attn_fwd_tflops": round(fwd_tflops, 2),
+        "attn_bwd_tflops": round(bwd_tflops, 2),
+        "attn_fwd_bwd_tflops": round(attn_tflops, 2),
+        "effective_pairs_per_head": attended_pairs(T, K),
+        "roofline": roofline,
+    }
+
+    # ------------------------------------------------------------ decode
+    if not args.no_decode:
+        del x, qg, kg, idx, logg, glse, o, lse, dq, dk, dv, dlogg, ws_gate, ws_bwd
+        torch.cuda.empty_cache()
+        wd = synth.DECODE_B64
+        xd = synth.decode_inputs(wd, seed=args.seed, device=dev)
+        Kd = wd.topk
+        od = torch.empty((wd.B, wd.Hq, wd.D), dtype=torch.bfloat16, device=dev)
+        ws_d = torch.empty(sas.decode_workspace_size(sas.DecodeDims(
+            wd.B, wd.Hq, wd.Hkv, wd.D, wd.dg, 64, Kd, xd["Lmax"], xd["NBmax"], 1)),
+            dtype=torch.uint8, device=dev)
+        scd = 1.0 / math.sqrt(wd.D)
+
+        def dstep():
+            sas.decode(xd["q"], xd["q_gate"], xd["k_cache"], xd["v_cache"], xd["kg_cache"],
+                       xd["ctx_len"], Kd, scd, apply_gate=True, want_idx=False,
+                       workspace=ws_d, out=(od, None, None))
+
+        for _ in range(3):
+            dstep()
+        torch.cuda.synchronize()
+        # warm: back-to-back steps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.decode_steps):
+            dstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm_us = e0.elapsed_time(e1) / args.decode_steps * 1e3
+        # cold: write 1 GiB between steps so no selected block or gate key is cached
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(args.decode_steps):
+            flush.fill_(1)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            dstep()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a0.elapsed_time(a1) * 1e3)
+        cold.sort()
+        cold_us = cold[len(cold) // 2]
+        lens = xd["ctx_len"].cpu().tolist()
+        kvb, gkb, smb = decode_bytes(lens, wd.Hkv, wd.D, wd.dg, Kd, wd.G)
+        tot = kvb + gkb + smb
+        dec_hash = source_hash([os.path.join(csrc, f) for f in ("decode.hip", "sas_device.h",
+                                                                "sas_kernels.h")])
+        out["decode"] = {
+            "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D, "dg": wd.dg,
+            "budget": 64 * (Kd + 1), "ctx_len_range": [wd.Lmin, wd.Lmax],
+            "us_per_step_cold": round(cold_us, 2), "us_per_step_warm": round(warm_us, 2),
+            "algorithmic_bytes": tot, "kv_bytes": kvb, "gate_key_bytes": gkb,
+            "GBps_cold": round(tot / (cold_us * 1e-6) / 1e9, 1),
+            "KV_GBps_cold": round(kvb / (cold_us * 1e-6) / 1e9, 1),
+            "GBps_warm": round(tot / (warm_us * 1e-6) / 1e9, 1),
+            "roofline": {"kernel": "sas_decode (select + split attention + combine)",
+                         "bound": "hbm", "achieved": round(tot / (cold_us * 1e-6) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(tot / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("sas_decode", dec_hash)},
+        }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

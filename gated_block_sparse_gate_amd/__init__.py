@@ -1,0 +1,299 @@
+"""Python binding of libsas (SAS gated block-sparse attention on MI355X).
+
+Thin ctypes layer over the C ABI declared in include/sas.h: it checks tensor
+dtypes, shapes, contiguity and devices, allocates outputs and workspaces with
+torch, and passes raw device pointers plus the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback path.  Importing works without a GPU (so the CPU tests can check the
+exported symbols); calling any compute function requires the built library
+and a visible GPU and raises otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "Dims", "DecodeDims", "SasError", "load_library", "version", "workspace_size",
+    "decode_workspace_size", "gate_score", "topk_blocks", "sparse_attn_fwd",
+    "sparse_attn_bwd", "decode", "budget_to_topk", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsas.so")
+
+SAS_OK, SAS_ERR_INVALID, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
+OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD = range(4)
+
+EXPORTED_SYMBOLS = (
+    "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
+    "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
+    "sas_decode",
+)
+
+
+class SasError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libsas status {status}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("dg", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_float),
+                ("flags", ctypes.c_int32)]
+
+
+class DecodeDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("dg", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("Lmax", ctypes.c_int32), ("NBmax", ctypes.c_int32),
+                ("apply_gate", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsas.so (built by gated_block_sparse_gate_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libsas.so not found at {path}; build it with "
+                           "`python -m gated_block_sparse_gate_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, S, I32, F32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    lib.sas_version.restype = I32
+    lib.sas_last_error.restype = ctypes.c_char_p
+    lib.sas_workspace_size.argtypes = [I32, ctypes.POINTER(Dims)]
+    lib.sas_workspace_size.restype = S
+    lib.sas_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDims)]
+    lib.sas_decode_workspace_size.restype = S
+    lib.sas_gate_score.argtypes = [ctypes.POINTER(Dims)] + [P] * 8 + [P, S, P]
+    lib.sas_topk_blocks.argtypes = [ctypes.POINTER(Dims)] + [P] * 6 + [P, S, P]
+    lib.sas_sparse_attn_fwd.argtypes = [ctypes.POINTER(Dims)] + [P] * 5 + [F32] + [P] * 2 + [P, S, P]
+    lib.sas_sparse_attn_bwd.argtypes = ([ctypes.POINTER(Dims)] + [P] * 8 + [F32] + [P] * 4
+                                        + [P, S, P])
+    lib.sas_decode.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 6 + [F32] + [P] * 3
+                               + [P, S, P])
+    for fn in ("sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd",
+               "sas_sparse_attn_bwd", "sas_decode"):
+        getattr(lib, fn).restype = I32
+    _lib = lib
+    return lib
+
+
+def version() -> int:
+    return load_library().sas_version()
+
+
+def _check(st: int):
+    if st != SAS_OK:
+        raise SasError(st, load_library().sas_last_error().decode())
+
+
+def make_dims(B, T, Hq, Hkv, D, dg, topk, theta=1.0e6, eps=1.0e-6, block=64) -> Dims:
+    return Dims(B, T, Hq, Hkv, D, dg, block, topk, float(theta), float(eps), 0)
+
+
+def workspace_size(op: int, d: Dims) -> int:
+    n = load_library().sas_workspace_size(op, ctypes.byref(d))
+    if n == ctypes.c_size_t(-1).value:
+        raise SasError(SAS_ERR_INVALID, load_library().sas_last_error().decode())
+    return n
+
+
+def decode_workspace_size(d: DecodeDims) -> int:
+    n = load_library().sas_decode_workspace_size(ctypes.byref(d))
+    if n == ctypes.c_size_t(-1).value:
+        raise SasError(SAS_ERR_INVALID, load_library().sas_last_error().decode())
+    return n
+
+
+def budget_to_topk(budget: int, block: int = 64) -> int:
+    """Decode token budget (counts the current block) -> historical Top-K."""
+    if budget < block or budget % block:
+        raise ValueError("budget must be a positive multiple of the block size")
+    return budget // block - 1
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _req(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ws(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _device_of(t):
+    if t.device.type != "cuda":
+        raise ValueError("libsas tensors must live on a GPU device")
+    return t.device
+
+
+def gate_score(q, k, wq, wk, w_qn, w_kn, topk: int, theta: float = 1.0e6, eps: float = 1.0e-6,
+               q_gate=None, k_gate=None, workspace=None):
+    """Router: returns (q_gate, k_gate) fp32 [B,T,Hkv,dg]."""
+    lib = load_library()
+    dev = _device_of(q)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dg = wq.shape[2]
+    G = Hq // Hkv
+    _req(q, "q", torch.bfloat16, (B, T, Hq, D), dev)
+    _req(k, "k", torch.bfloat16, (B, T, Hkv, D), dev)
+    _req(wq, "wq", torch.bfloat16, (Hkv, G * D, dg), dev)
+    _req(wk, "wk", torch.bfloat16, (Hkv, 3 * D, dg), dev)
+    _req(w_qn, "w_qn", torch.float32, (dg,), dev)
+    _req(w_kn, "w_kn", torch.float32, (dg,), dev)
+    d = make_dims(B, T, Hq, Hkv, D, dg, topk, theta, eps)
+    if q_gate is None:
+        q_gate = torch.empty((B, T, Hkv, dg), dtype=torch.float32, device=dev)
+    if k_gate is None:
+        k_gate = torch.empty((B, T, Hkv, dg), dtype=torch.float32, device=dev)
+    _req(q_gate, "q_gate", torch.float32, (B, T, Hkv, dg), dev)
+    _req(k_gate, "k_gate", torch.float32, (B, T, Hkv, dg), dev)
+    nws = workspace_size(OP_GATE_SCORE, d)
+    ws = workspace if workspace is not None else _ws(nws, dev)
+    _check(lib.sas_gate_score(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(w_qn),
+                              _ptr(w_kn), _ptr(q_gate), _ptr(k_gate), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream(dev)))
+    return q_gate, k_gate
+
+
+def topk_blocks(q_gate, k_gate, topk: int, Hq: int, D: int, want_probs: bool = False,
+                out=None):
+    """Candidate softmax + Top-K: returns (idx, logg, gate_lse, gate_probs or None)."""
+    lib = load_library()
+    dev = _device_of(q_gate)
+    B, T, Hkv, dg = q_gate.shape
+    S = topk + 1
+    NB = -(-T // 64)
+    _req(q_gate, "q_gate", torch.float32, (B, T, Hkv, dg), dev)
+    _req(k_gate, "k_gate", torch.float32, (B, T, Hkv, dg), dev)
+    d = make_dims(B, T, Hq, Hkv, D, dg, topk)
+    if out is None:
+        idx = torch.empty((B, T, Hkv, S), dtype=torch.int32, device=dev)
+        logg = torch.empty((B, T, Hkv, S), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, T, Hkv), dtype=torch.float32, device=dev)
+    else:
+        idx, logg, lse = out
+    probs = torch.empty((B, T, Hkv, NB), dtype=torch.float32, device=dev) if want_probs else None
+    _check(lib.sas_topk_blocks(ctypes.byref(d), _ptr(q_gate), _ptr(k_gate), _ptr(idx), _ptr(logg),
+                               _ptr(lse), _ptr(probs), None, 0, _stream(dev)))
+    return idx, logg, lse, probs
+
+
+def sparse_attn_fwd(q, k, v, idx, logg, scale: float | None = None, o=None, lse=None):
+    """Gated sparse attention forward: returns (o bf16 [B,T,Hq,D], lse fp32 [B,T,Hq])."""
+    lib = load_library()
+    dev = _device_of(q)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    S = idx.shape[-1]
+    _req(q, "q", torch.bfloat16, (B, T, Hq, D), dev)
+    _req(k, "k", torch.bfloat16, (B, T, Hkv, D), dev)
+    _req(v, "v", torch.bfloat16, (B, T, Hkv, D), dev)
+    _req(idx, "idx", torch.int32, (B, T, Hkv, S), dev)
+    _req(logg, "logg", torch.float32, (B, T, Hkv, S), dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    d = make_dims(B, T, Hq, Hkv, D, 128, S - 1)
+    if o is None:
+        o = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    _check(lib.sas_sparse_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                   _ptr(logg), ctypes.c_float(scale), _ptr(o), _ptr(lse), None, 0,
+                                   _stream(dev)))
+    return o, lse
+
+
+def sparse_attn_bwd(q, k, v, o, dout, lse, idx, logg, scale: float | None = None,
+                    workspace=None, out=None):
+    """Backward: returns (dq, dk, dv bf16, dlogg fp32 [B,T,Hkv,S])."""
+    lib = load_library()
+    dev = _device_of(q)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    S = idx.shape[-1]
+    for t, n, dt, sh in ((q, "q", torch.bfloat16, (B, T, Hq, D)), (k, "k", torch.bfloat16, (B, T, Hkv, D)),
+                         (v, "v", torch.bfloat16, (B, T, Hkv, D)), (o, "o", torch.bfloat16, (B, T, Hq, D)),
+                         (dout, "dout", torch.bfloat16, (B, T, Hq, D)),
+                         (lse, "lse", torch.float32, (B, T, Hq)),
+                         (idx, "idx", torch.int32, (B, T, Hkv, S)),
+                         (logg, "logg", torch.float32, (B, T, Hkv, S))):
+        _req(t, n, dt, sh, dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    d = make_dims(B, T, Hq, Hkv, D, 128, S - 1)
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        dlogg = torch.empty((B, T, Hkv, S), dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dv, dlogg = out
+    nws = workspace_size(OP_BWD, d)
+    ws = workspace if workspace is not None else _ws(nws, dev)
+    _check(lib.sas_sparse_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                   _ptr(lse), _ptr(idx), _ptr(logg), ctypes.c_float(scale),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlogg), _ptr(ws),
+                                   ws.numel() if ws is not None else 0, _stream(dev)))
+    return dq, dk, dv, dlogg
+
+
+def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int, scale: float | None = None,
+           apply_gate: bool = True, want_idx: bool = True, workspace=None, out=None):
+    """Budgeted decode step: returns (o bf16 [B,Hq,D], idx [B,Hkv,K+1] or None,
+    logg [B,Hkv,K+1] or None)."""
+    lib = load_library()
+    dev = _device_of(q)
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    dg = q_gate.shape[-1]
+    NBmax = -(-Lmax // 64)
+    S = topk + 1
+    _req(q, "q", torch.bfloat16, (B, Hq, D), dev)
+    _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
+    _req(k_cache, "k_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
+    _req(v_cache, "v_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
+    _req(kg_cache, "kg_cache", torch.float32, (B, Hkv, NBmax, dg), dev)
+    _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0)
+    if out is None:
+        o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev) if want_idx else None
+        logg = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev) if want_idx else None
+    else:
+        o, idx, logg = out
+    nws = decode_workspace_size(d)
+    ws = workspace if workspace is not None else _ws(nws, dev)
+    _check(lib.sas_decode(ctypes.byref(d), _ptr(q), _ptr(q_gate), _ptr(k_cache), _ptr(v_cache),
+                          _ptr(kg_cache), _ptr(ctx_len), ctypes.c_float(scale), _ptr(o), _ptr(idx),
+                          _ptr(logg), _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev)))
+    return o, idx, logg

@@ -1,0 +1,631 @@
+// Gated sparse attention backward (README item (b) / abstract: the LM loss
+// reaches the selector through the log gate inside the softmax).
+//
+//   Delta = rowsum(dO * O);  P = exp(scale q.k + logg - lse);  dS = P (dO.v - Delta)
+//   dq = scale sum dS k;  dk = scale sum dS q;  dv = sum P dO;
+//   dlogg[t, slot] = sum over the group's G heads and the slot block's keys of dS.
+//
+// Kernels (all deterministic, no floating-point atomics):
+//   delta      : Delta per query row.
+//   csr_*      : for every (b, kappa, key block j) the list of (token, slot)
+//                that selected j, in ascending token order (counting sort
+//                with per-(query block, key block) offsets).
+//   dkdv       : KV-block stationary.  One workgroup per (b, kappa, j); wave w
+//                owns keys 16w..16w+15 and keeps dK, dV for them in registers.
+//                The selecting rows are streamed as compacted 32-row tiles
+//                (two tiles of floor(16/G) tokens x G heads), so no MFMA row
+//                is wasted on a query that did not select the block.
+//   dq         : query-block stationary, same walk as the forward; also
+//                produces dlogg (each (t, j) pair is visited exactly once).
+#include "sas_kernels.h"
+
+namespace sas {
+
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const uint16_t* dout,
+                                                        float* delta, long nrows) {
+  constexpr int EPL = D / 16;
+  const long gid = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x;
+  const long row = gid >> 4;
+  const int part = static_cast<int>(gid & 15);
+  float acc = 0.f;
+  if (row < nrows) {
+    const uint16_t* po = o + row * D + part * EPL;
+    const uint16_t* pd = dout + row * D + part * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = fmaf(bf2f(po[e]), bf2f(pd[e]), acc);
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  acc += __shfl_xor(acc, 8, 64);
+  if (part == 0 && row < nrows) delta[row] = acc;
+}
+
+// Per (b, kappa, query block c): which of the 64 tokens selected each block j.
+__device__ __forceinline__ void build_token_masks(const BwdParams& p, unsigned long long* mask,
+                                                  int b, int kv, int c, int ntok) {
+  const size_t rowbase = (static_cast<size_t>(b) * p.T + c * 64) * p.Hkv + kv;
+  for (int e = threadIdx.x; e < ntok * p.S; e += blockDim.x) {
+    const int tl = e / p.S, s = e - tl * p.S;
+    const int j = p.idx[(rowbase + static_cast<size_t>(tl) * p.Hkv) * p.S + s];
+    if (j >= 0 && j <= c) atomicOr(&mask[j], 1ull << tl);
+  }
+}
+
+__global__ __launch_bounds__(256) void csr_count_kernel(BwdParams p) {
+  __shared__ unsigned long long mask[kMaxNB];
+  const int NQB = p.NB;
+  const int bid = blockIdx.x;
+  const int kv = bid % p.Hkv, rest = bid / p.Hkv;
+  const int c = rest % NQB, b = rest / NQB;
+  const int ntok = min(64, p.T - c * 64);
+  for (int j = threadIdx.x; j < p.NB; j += 256) mask[j] = 0ull;
+  __syncthreads();
+  build_token_masks(p, mask, b, kv, c, ntok);
+  __syncthreads();
+  int32_t* out = p.cnt2d + ((static_cast<size_t>(b) * p.Hkv + kv) * NQB + c) * p.NB;
+  for (int j = threadIdx.x; j < p.NB; j += 256) out[j] = __popcll(mask[j]);
+}
+
+// cnt2d[c][j] -> exclusive offset of query block c inside column j; column
+// totals -> rowptr[j].
+__global__ __launch_bounds__(256) void csr_colscan_kernel(BwdParams p) {
+  __shared__ int part[4][64];
+  const int lane = threadIdx.x & 63, sg = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
+  const int bk = blockIdx.y;
+  const int NQB = p.NB;
+  const int seglen = (NQB + 3) / 4;
+  const int c0 = min(NQB, sg * seglen), c1 = min(NQB, c0 + seglen);
+  int32_t* col = p.cnt2d + static_cast<size_t>(bk) * NQB * p.NB + j;
+  int sum = 0;
+  if (j < p.NB)
+    for (int c = c0; c < c1; ++c) sum += col[static_cast<size_t>(c) * p.NB];
+  part[sg][lane] = sum;
+  __syncthreads();
+  int off = 0;
+  for (int s = 0; s < sg; ++s) off += part[s][lane];
+  if (j < p.NB) {
+    for (int c = c0; c < c1; ++c) {
+      const int v = col[static_cast<size_t>(c) * p.NB];
+      col[static_cast<size_t>(c) * p.NB] = off;
+      off += v;
+    }
+    if (sg == 3) p.rowptr[static_cast<size_t>(bk) * (p.NB + 1) + j] = off;
+  }
+}
+
+__global__ __launch_bounds__(1024) void csr_rowptr_kernel(BwdParams p) {
+  __shared__ int wsums[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* rp = p.rowptr + static_cast<size_t>(blockIdx.x) * (p.NB + 1);
+  const int v = (tid < p.NB) ? rp[tid] : 0;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsums[wv] = incl;
+  __syncthreads();
+  if (wv == 0) {
+    const int s = (lane < 16) ? wsums[lane] : 0;
+    const int si = wave_incl_scan(s);
+    if (lane < 16) wsums[lane] = si - s;
+  }
+  __syncthreads();
+  const int excl = incl - v + wsums[wv];
+  if (tid < p.NB) rp[tid] = excl;
+  if (tid == p.NB - 1) rp[p.NB] = excl + v;
+}
+
+__global__ __launch_bounds__(256) void csr_fill_kernel(BwdParams p) {
+  __shared__ unsigned long long mask[kMaxNB];
+  __shared__ int base[kMaxNB];
+  const int NQB = p.NB;
+  const int bid = blockIdx.x;
+  const int kv = bid % p.Hkv, rest = bid / p.Hkv;
+  const int c = rest % NQB, b = rest / NQB;
+  const int ntok = min(64, p.T - c * 64);
+  const size_t bk = static_cast<size_t>(b) * p.Hkv + kv;
+  for (int j = threadIdx.x; j <= c; j += 256) {
+    mask[j] = 0ull;
+    base[j] = p.rowptr[bk * (p.NB + 1) + j] + p.cnt2d[(bk * NQB + c) * p.NB + j];
+  }
+  __syncthreads();
+  build_token_masks(p, mask, b, kv, c, ntok);
+  __syncthreads();
+  const size_t rowbase = (static_cast<size_t>(b) * p.T + c * 64) * p.Hkv + kv;
+  int32_t* ent = p.entries + bk * static_cast<size_t>(p.T) * p.S;
+  for (int e = threadIdx.x; e < ntok * p.S; e += 256) {
+    const int tl = e / p.S, s = e - tl * p.S;
+    const int j = p.idx[(rowbase + static_cast<size_t>(tl) * p.Hkv) * p.S + s];
+    if (j >= 0 && j <= c) {
+      const int pos = base[j] + __popcll(mask[j] & ((1ull << tl) - 1ull));
+      ent[pos] = ((c * 64 + tl) << 6) | s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
+  constexpr int NKS = D / 32, NDT = D / 16;
+  constexpr int RP = D + 8;      // row-major pitch
+  constexpr int TP = 32 + 8;     // transposed pitch (32 rows)
+  constexpr int UNITS = 16 * (D / 8);
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[32 * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TP];
+  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * TP];
+  __shared__ float r_lse2[32], r_delta[32], r_lg2[32];
+  __shared__ int r_t[32];
+  __shared__ int r_src[32];     // query row index (b*T+t)*Hq+h, -1 if none
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int bid = blockIdx.x;
+  const int kv = bid % p.Hkv, rest = bid / p.Hkv;
+  const int j = rest % p.NB, b = rest / p.NB;
+  const size_t bk = static_cast<size_t>(b) * p.Hkv + kv;
+  const int G = p.G, TPT = p.TPT, RT = p.TPT * p.G;
+
+  const int key = j * 64 + wv * 16 + l16;
+  const bool keyok = key < p.T;
+  uint4 kb[NKS], vb[NKS];
+  {
+    const size_t off = ((static_cast<size_t>(b) * p.T + (keyok ? key : 0)) * p.Hkv + kv) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kb[ks] = keyok ? *reinterpret_cast<const uint4*>(p.k + off + ks * 32 + g4 * 8)
+                     : make_uint4(0, 0, 0, 0);
+      vb[ks] = keyok ? *reinterpret_cast<const uint4*>(p.v + off + ks * 32 + g4 * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+  }
+  floatx4 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int e0 = p.rowptr[bk * (p.NB + 1) + j];
+  const int e1 = p.rowptr[bk * (p.NB + 1) + j + 1];
+  const int n = e1 - e0;
+  const int32_t* ent = p.entries + bk * static_cast<size_t>(p.T) * p.S + e0;
+  const float sl2 = p.scale_log2;
+
+  for (int g0 = 0; g0 < n; g0 += 2 * TPT) {
+    if (tid < 32) {
+      const int r = tid, tt = r >> 4, rr = r & 15;
+      const int ti = g0 + tt * TPT + rr / G;
+      int src = -1, t = -1;
+      float l2 = 0.f, dl = 0.f, lg = 0.f;
+      if (rr < RT && ti < n) {
+        const int en = ent[ti];
+        const int tk = en >> 6, s = en & 63;
+        if (tk >= j * 64 && tk < p.T && s < p.S) {
+          const int h = kv * G + (rr - (rr / G) * G);
+          const size_t qrow = (static_cast<size_t>(b) * p.T + tk) * p.Hq + h;
+          const float ls = p.lse[qrow];
+          if (ls > -INFINITY) {
+            t = tk;
+            src = static_cast<int>(qrow);
+            l2 = ls * kLog2e;
+            dl = p.delta[qrow];
+            lg = p.logg[((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + s] * kLog2e;
+          }
+        }
+      }
+      r_t[r] = t;
+      r_src[r] = src;
+      r_lse2[r] = l2;
+      r_delta[r] = dl;
+      r_lg2[r] = lg;
+    }
+    __syncthreads();
+    // stage Q, dO rows (row-major and transposed)
+    for (int u = tid; u < UNITS; u += 256) {
+      const int rp = u / (D / 8), ch = u - rp * (D / 8);
+      const int s0 = r_src[2 * rp], s1 = r_src[2 * rp + 1];
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 q0 = (s0 >= 0) ? *reinterpret_cast<const uint4*>(p.q + static_cast<size_t>(s0) * D + ch * 8) : z;
+      const uint4 q1 = (s1 >= 0) ? *reinterpret_cast<const uint4*>(p.q + static_cast<size_t>(s1) * D + ch * 8) : z;
+      const uint4 d0 = (s0 >= 0) ? *reinterpret_cast<const uint4*>(p.dout + static_cast<size_t>(s0) * D + ch * 8) : z;
+      const uint4 d1 = (s1 >= 0) ? *reinterpret_cast<const uint4*>(p.dout + static_cast<size_t>(s1) * D + ch * 8) : z;
+      *reinterpret_cast<uint4*>(&Qs[(2 * rp) * RP + ch * 8]) = q0;
+      *reinterpret_cast<uint4*>(&Qs[(2 * rp + 1) * RP + ch * 8]) = q1;
+      *reinterpret_cast<uint4*>(&dOs[(2 * rp) * RP + ch * 8]) = d0;
+      *reinterpret_cast<uint4*>(&dOs[(2 * rp + 1) * RP + ch * 8]) = d1;
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&q0);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&q1);
+      const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&d0);
+      const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&d1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = ch * 8 + 2 * i;
+        *reinterpret_cast<uint32_t*>(&Qt[d * TP + 2 * rp]) = (a0[i] & 0xffffu) | (a1[i] << 16);
+        *reinterpret_cast<uint32_t*>(&Qt[(d + 1) * TP + 2 * rp]) = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&dOt[d * TP + 2 * rp]) = (c0[i] & 0xffffu) | (c1[i] << 16);
+        *reinterpret_cast<uint32_t*>(&dOt[(d + 1) * TP + 2 * rp]) = (c0[i] >> 16) | (c1[i] & 0xffff0000u);
+      }
+    }
+    __syncthreads();
+
+    // S, dP for the two row tiles: [rows x 16 keys of this wave]
+    floatx4 sacc[2], pacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      pacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(&Qs[(tt * 16 + l16) * RP + ks * 32 + g4 * 8]);
+        const uint4 da = *reinterpret_cast<const uint4*>(&dOs[(tt * 16 + l16) * RP + ks * 32 + g4 * 8]);
+        sacc[tt] = mfma16x16x32(qa, kb[ks], sacc[tt]);
+        pacc[tt] = mfma16x16x32(da, vb[ks], pacc[tt]);
+      }
+    }
+    float pv[2][4], ds[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = tt * 16 + g4 * 4 + i;
+        const int t = r_t[r];
+        float pp = 0.f;
+        if (t >= 0 && key <= t) pp = exp2f(sacc[tt][i] * sl2 + r_lg2[r] - r_lse2[r]);
+        pv[tt][i] = pp;
+        ds[tt][i] = pp * (pacc[tt][i] - r_delta[r]);
+      }
+    uint4 pb, db;
+    pb.x = pack_bf2(pv[0][0], pv[0][1]);
+    pb.y = pack_bf2(pv[0][2], pv[0][3]);
+    pb.z = pack_bf2(pv[1][0], pv[1][1]);
+    pb.w = pack_bf2(pv[1][2], pv[1][3]);
+    db.x = pack_bf2(ds[0][0], ds[0][1]);
+    db.y = pack_bf2(ds[0][2], ds[0][3]);
+    db.z = pack_bf2(ds[1][0], ds[1][1]);
+    db.w = pack_bf2(ds[1][2], ds[1][3]);
+    // dV^T[d, key] += dO^T[d, rows] P[rows, key];  dK^T += Q^T dS
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint16_t* dr = &dOt[(dt * 16 + l16) * TP + g4 * 4];
+      const uint16_t* qr = &Qt[(dt * 16 + l16) * TP + g4 * 4];
+      const uint2 dlo = *reinterpret_cast<const uint2*>(dr);
+      const uint2 dhi = *reinterpret_cast<const uint2*>(dr + 16);
+      const uint2 qlo = *reinterpret_cast<const uint2*>(qr);
+      const uint2 qhi = *reinterpret_cast<const uint2*>(qr + 16);
+      dv[dt] = mfma16x16x32(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y), pb, dv[dt]);
+      dk[dt] = mfma16x16x32(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), db, dk[dt]);
+    }
+    __syncthreads();
+  }
+  if (keyok) {
+    const size_t off = ((static_cast<size_t>(b) * p.T + key) * p.Hkv + kv) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 pk;
+      pk.x = pack_bf2(dk[dt][0] * p.scale, dk[dt][1] * p.scale);
+      pk.y = pack_bf2(dk[dt][2] * p.scale, dk[dt][3] * p.scale);
+      *reinterpret_cast<uint2*>(p.dk + off + dt * 16 + g4 * 4) = pk;
+      pk.x = pack_bf2(dv[dt][0], dv[dt][1]);
+      pk.y = pack_bf2(dv[dt][2], dv[dt][3]);
+      *reinterpret_cast<uint2*>(p.dv + off + dt * 16 + g4 * 4) = pk;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ, dlogg
+template <int D, int TW>
+__global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
+  constexpr int NW = 8;
+  constexpr int KP = D + 8;
+  constexpr int VP = 64 + 8;
+  constexpr int NKS = D / 32;
+  constexpr int NDT = D / 16;
+  constexpr int PU = 32 * (D / 8);   // (row pair, 8-d chunk) units per block
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * VP];
+  __shared__ uint32_t bits[64][kMaxNBW];
+  __shared__ uint8_t pcnt[64][kMaxNBW];
+  __shared__ uint32_t ubits[kMaxNBW];
+  __shared__ uint16_t ulist[kMaxNB];
+  __shared__ float lgs[64][kMaxS];
+  __shared__ uint8_t slot_of[64][kMaxS];
+  __shared__ float red[NW][16];
+  __shared__ int s_nU;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int NQB = a.NB;
+  const int bid = blockIdx.x;
+  const int kv = bid % a.Hkv;
+  const int rest = bid / a.Hkv;
+  const int c = NQB - 1 - (rest % NQB);
+  const int b = rest / NQB;
+  const int t0 = c * 64;
+  const int ntok = min(64, a.T - t0);
+  const int NBW = (a.NB + 31) >> 5;
+  const int S = a.S;
+
+  for (int i = tid; i < 64 * kMaxNBW; i += 512) (&bits[0][0])[i] = 0u;
+  if (tid < kMaxNBW) ubits[tid] = 0u;
+  __syncthreads();
+  const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
+  for (int e = tid; e < ntok * S; e += 512) {
+    const int tl = e / S, s = e - tl * S;
+    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
+    const int j = a.idx[off];
+    if (j >= 0 && j <= c) {
+      atomicOr(&bits[tl][j >> 5], 1u << (j & 31));
+      atomicOr(&ubits[j >> 5], 1u << (j & 31));
+    } else {
+      a.dlogg[off] = 0.f;     // padding / ignored slot
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int run = 0;
+    for (int w = 0; w < NBW; ++w) {
+      pcnt[tid][w] = static_cast<uint8_t>(run);
+      run += __popc(bits[tid][w]);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < ntok * S; e += 512) {
+    const int tl = e / S, s = e - tl * S;
+    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
+    const int j = a.idx[off];
+    if (j >= 0 && j <= c) {
+      const int rank = pcnt[tl][j >> 5] + __popc(bits[tl][j >> 5] & ((1u << (j & 31)) - 1u));
+      if (rank < kMaxS) {
+        lgs[tl][rank] = a.logg[off] * kLog2e;
+        slot_of[tl][rank] = static_cast<uint8_t>(s);
+      }
+    }
+  }
+  if (wv == 0) {
+    int base = 0;
+    for (int w0 = 0; w0 < NBW; w0 += 64) {
+      const uint32_t word = (w0 + lane < NBW) ? ubits[w0 + lane] : 0u;
+      const int cnt = __popc(word);
+      const int incl = wave_incl_scan(cnt);
+      int pos = base + incl - cnt;
+      uint32_t wb = word;
+      while (wb) {
+        const int bp = __ffs(wb) - 1;
+        wb &= wb - 1;
+        ulist[pos++] = static_cast<uint16_t>((w0 + lane) * 32 + bp);
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) s_nU = base;
+  }
+  __syncthreads();
+  const int nU = s_nU;
+
+  const int G = a.G, TPT = a.TPT;
+  int tl_row[TW];
+  bool valid[TW];
+  uint4 qa[TW][NKS], da[TW][NKS];
+  floatx4 dqa[TW][NDT];
+  float lse2[TW], dlt[TW];
+#pragma unroll
+  for (int ti = 0; ti < TW; ++ti) {
+    const int tile = wv + NW * ti;
+    const int tl = tile * TPT + l16 / G;
+    const int hh = l16 - (l16 / G) * G;
+    bool v = (tile < a.ntiles) && (l16 < TPT * G) && (tl < ntok);
+    tl_row[ti] = v ? tl : 0;
+    const size_t qrow = (static_cast<size_t>(b) * a.T + t0 + tl_row[ti]) * a.Hq + kv * G + hh;
+    const float ls = v ? a.lse[qrow] : -INFINITY;
+    v = v && (ls > -INFINITY);
+    valid[ti] = v;
+    lse2[ti] = v ? ls * kLog2e : 0.f;
+    dlt[ti] = v ? a.delta[qrow] : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qa[ti][ks] = v ? *reinterpret_cast<const uint4*>(a.q + qrow * D + ks * 32 + g4 * 8)
+                     : make_uint4(0, 0, 0, 0);
+      da[ti][ks] = v ? *reinterpret_cast<const uint4*>(a.dout + qrow * D + ks * 32 + g4 * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dqa[ti][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  constexpr int PUT = (PU + 511) / 512;
+  uint4 kreg[PUT][2], vreg[PUT][2];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int x = 0; x < PUT; ++x) {
+      const int u = tid + 512 * x;
+      const int pr = u / (D / 8), ch = u - pr * (D / 8);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int tok = j * 64 + 2 * pr + r;
+        const bool ok = (u < PU) && (tok < a.T);
+        const size_t off = ((static_cast<size_t>(b) * a.T + (ok ? tok : 0)) * a.Hkv + kv) * D + ch * 8;
+        kreg[x][r] = ok ? *reinterpret_cast<const uint4*>(a.k + off) : make_uint4(0, 0, 0, 0);
+        vreg[x][r] = ok ? *reinterpret_cast<const uint4*>(a.v + off) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < PUT; ++x) {
+      const int u = tid + 512 * x;
+      if (u >= PU) continue;
+      const int pr = u / (D / 8), ch = u - pr * (D / 8);
+      *reinterpret_cast<uint4*>(&Ks[buf][(2 * pr) * KP + ch * 8]) = kreg[x][0];
+      *reinterpret_cast<uint4*>(&Ks[buf][(2 * pr + 1) * KP + ch * 8]) = kreg[x][1];
+      *reinterpret_cast<uint4*>(&Vs[buf][(2 * pr) * KP + ch * 8]) = vreg[x][0];
+      *reinterpret_cast<uint4*>(&Vs[buf][(2 * pr + 1) * KP + ch * 8]) = vreg[x][1];
+      const uint32_t* k0 = reinterpret_cast<const uint32_t*>(&kreg[x][0]);
+      const uint32_t* k1 = reinterpret_cast<const uint32_t*>(&kreg[x][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint32_t*>(&Kt[buf][(ch * 8 + 2 * i) * VP + 2 * pr]) =
+            (k0[i] & 0xffffu) | (k1[i] << 16);
+        *reinterpret_cast<uint32_t*>(&Kt[buf][(ch * 8 + 2 * i + 1) * VP + 2 * pr]) =
+            (k0[i] >> 16) | (k1[i] & 0xffff0000u);
+      }
+    }
+  };
+
+  if (nU > 0) {
+    gload(ulist[0]);
+    lstore(0);
+    if (nU > 1) gload(ulist[1]);
+  }
+  __syncthreads();
+
+  const float sl2 = a.scale_log2;
+  for (int u = 0; u < nU; ++u) {
+    const int buf = u & 1;
+    const int j = ulist[u];
+    const uint32_t jbit = 1u << (j & 31);
+    const int jw = j >> 5;
+    bool sel[TW], act[TW];
+    bool any = false;
+#pragma unroll
+    for (int ti = 0; ti < TW; ++ti) {
+      sel[ti] = valid[ti] && (bits[tl_row[ti]][jw] & jbit);
+      act[ti] = ballot64(sel[ti]) != 0;
+      any |= act[ti];
+    }
+    if (any) {
+#pragma unroll
+      for (int ti = 0; ti < TW; ++ti) {
+        if (!act[ti]) continue;
+        floatx4 sacc[4], pacc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          pacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const uint4 ka = *reinterpret_cast<const uint4*>(
+                &Ks[buf][(mt * 16 + l16) * KP + ks * 32 + g4 * 8]);
+            const uint4 va = *reinterpret_cast<const uint4*>(
+                &Vs[buf][(mt * 16 + l16) * KP + ks * 32 + g4 * 8]);
+            sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
+            pacc[mt] = mfma16x16x32(va, da[ti][ks], pacc[mt]);
+          }
+        }
+        const int tl = tl_row[ti];
+        float lgv = 0.f;
+        if (sel[ti]) {
+          const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
+          lgv = lgs[tl][rank];
+        }
+        const int tpos = t0 + tl;
+        float dsv[4][4];
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j * 64 + mt * 16 + g4 * 4 + i;
+            float pp = 0.f;
+            if (sel[ti] && key <= tpos) pp = exp2f(sacc[mt][i] * sl2 + lgv - lse2[ti]);
+            const float dsx = pp * (pacc[mt][i] - dlt[ti]);
+            dsv[mt][i] = dsx;
+            rs += dsx;
+          }
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        // dlogg: sum the G rows of each token of this tile
+        if (g4 == 0) red[wv][l16] = rs;
+        __builtin_amdgcn_wave_barrier();
+        if (g4 == 0 && l16 < TPT) {
+          const int tlr = (wv + NW * ti) * TPT + l16;
+          if (tlr < ntok && (bits[tlr][jw] & jbit)) {
+            float tot = 0.f;
+            for (int h = 0; h < G; ++h) tot += red[wv][l16 * G + h];
+            const int rank = pcnt[tlr][jw] + __popc(bits[tlr][jw] & (jbit - 1u));
+            a.dlogg[(rowbase + static_cast<size_t>(tlr) * a.Hkv) * S + slot_of[tlr][rank]] = tot;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        uint4 dsb[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          dsb[k2].x = pack_bf2(dsv[2 * k2][0], dsv[2 * k2][1]);
+          dsb[k2].y = pack_bf2(dsv[2 * k2][2], dsv[2 * k2][3]);
+          dsb[k2].z = pack_bf2(dsv[2 * k2 + 1][0], dsv[2 * k2 + 1][1]);
+          dsb[k2].w = pack_bf2(dsv[2 * k2 + 1][2], dsv[2 * k2 + 1][3]);
+        }
+        // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row]
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const uint16_t* kr = &Kt[buf][(dt * 16 + l16) * VP + k2 * 32 + g4 * 4];
+            const uint2 lo = *reinterpret_cast<const uint2*>(kr);
+            const uint2 hi = *reinterpret_cast<const uint2*>(kr + 16);
+            dqa[ti][dt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), dsb[k2], dqa[ti][dt]);
+          }
+        }
+      }
+    }
+    if (u + 1 < nU) lstore(buf ^ 1);
+    if (u + 2 < nU) gload(ulist[u + 2]);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int ti = 0; ti < TW; ++ti) {
+    const int tile = wv + NW * ti;
+    const int tl = tile * TPT + l16 / G;
+    const int hh = l16 - (l16 / G) * G;
+    if (!((tile < a.ntiles) && (l16 < TPT * G) && (tl < ntok))) continue;
+    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 pk;
+      pk.x = pack_bf2(dqa[ti][dt][0] * a.scale, dqa[ti][dt][1] * a.scale);
+      pk.y = pack_bf2(dqa[ti][dt][2] * a.scale, dqa[ti][dt][3] * a.scale);
+      *reinterpret_cast<uint2*>(a.dq + row * D + dt * 16 + g4 * 4) = pk;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
+  const long nrows = static_cast<long>(p.B) * p.T * p.Hq;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((nrows * 16 + 255) / 256), dim3(256), 0, st,
+                     p.o, p.dout, p.delta, nrows);
+  const int NQB = p.NB;
+  const unsigned nblk = static_cast<unsigned>(p.B) * p.Hkv * NQB;
+  hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hkv), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hkv), dim3(1024), 0, st, p);
+  hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
+                     dim3(256), 0, st, p);
+  const int tw = (p.ntiles + 7) / 8;
+  switch (tw) {
+    case 1: hipLaunchKernelGGL((dq_kernel<D, 1>), dim3(nblk), dim3(512), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((dq_kernel<D, 2>), dim3(nblk), dim3(512), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((dq_kernel<D, 3>), dim3(nblk), dim3(512), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((dq_kernel<D, 4>), dim3(nblk), dim3(512), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st) {
+  if (p.D == 128) return launch_bwd_d<128>(p, st);
+  if (p.D == 64) return launch_bwd_d<64>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sas

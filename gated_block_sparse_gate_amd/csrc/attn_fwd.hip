@@ -1,0 +1,337 @@
+// Gated sparse attention forward (SAS abstract: log gate inside the attention
+// softmax; README item (b): a continuous gate on every selected block).
+//
+// o[t,h] = softmax_tau( scale * q[t,h].k[tau] + logg[t, slot(block(tau))] ) . v
+// over the keys of the blocks selected for (t, kappa = h/G), tau <= t.
+//
+// Schedule (query-block stationary):
+//   one workgroup = (batch b, KV head kappa, query block c) = 64 tokens x G heads.
+//   The workgroup walks the union of the blocks its 64 tokens selected, in
+//   ascending order.  Each block's K (row-major) and V (transposed) is staged
+//   once into double-buffered LDS and shared by all 8 waves.  A wave owns TW
+//   row tiles of 16 rows = floor(16/G) tokens x G heads; a tile in which no
+//   token selected the block skips it, otherwise S^T = K Q^T and O^T += V^T P^T
+//   run on bf16 MFMA 16x16x32 with rows outside the selection masked to -inf.
+//   Online softmax state stays in registers (one query row per lane column).
+#include "sas_kernels.h"
+
+namespace sas {
+
+namespace {
+
+template <int D, int TW>
+__global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
+  constexpr int NW = 8;
+  constexpr int KP = D + 8;       // K row pitch (bf16 elements)
+  constexpr int VP = 64 + 8;      // V^T row pitch (bf16 elements)
+  constexpr int NKS = D / 32;     // MFMA k-steps over the head dim
+  constexpr int NDT = D / 16;     // 16-wide d tiles of O
+  constexpr int KUN = 64 * (D / 8);        // 16-byte K units per block
+  constexpr int VUN = 32 * (D / 8);        // (key pair, 8-d chunk) V units per block
+  constexpr int KU = (KUN + 511) / 512;    // per thread
+  constexpr int VU = (VUN + 511) / 512;
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ uint32_t bits[64][kMaxNBW];
+  __shared__ uint8_t pcnt[64][kMaxNBW];
+  __shared__ uint32_t ubits[kMaxNBW];
+  __shared__ uint16_t ulist[kMaxNB];
+  __shared__ float lgs[64][kMaxS];
+  __shared__ int s_nU;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int NQB = (a.T + 63) / 64;
+  const int bid = blockIdx.x;
+  const int kv = bid % a.Hkv;
+  const int rest = bid / a.Hkv;
+  const int c = NQB - 1 - (rest % NQB);
+  const int b = rest / NQB;
+  const int t0 = c * 64;
+  const int ntok = min(64, a.T - t0);
+  const int NBW = (a.NB + 31) >> 5;
+  const int S = a.S;
+
+  // ---- selection bitmaps of the 64 tokens, their union, log-gates by rank
+  for (int i = tid; i < 64 * kMaxNBW; i += 512) (&bits[0][0])[i] = 0u;
+  if (tid < kMaxNBW) ubits[tid] = 0u;
+  __syncthreads();
+  const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
+  for (int e = tid; e < ntok * S; e += 512) {
+    const int tl = e / S, s = e - tl * S;
+    const int j = a.idx[(rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s];
+    if (j >= 0 && j <= c) {
+      atomicOr(&bits[tl][j >> 5], 1u << (j & 31));
+      atomicOr(&ubits[j >> 5], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int run = 0;
+    for (int w = 0; w < NBW; ++w) {
+      pcnt[tid][w] = static_cast<uint8_t>(run);
+      run += __popc(bits[tid][w]);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < ntok * S; e += 512) {
+    const int tl = e / S, s = e - tl * S;
+    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
+    const int j = a.idx[off];
+    if (j >= 0 && j <= c) {
+      const uint32_t wbits = bits[tl][j >> 5];
+      const int rank = pcnt[tl][j >> 5] + __popc(wbits & ((1u << (j & 31)) - 1u));
+      if (rank < kMaxS) lgs[tl][rank] = a.logg[off] * kLog2e;
+    }
+  }
+  if (wv == 0) {
+    int base = 0;
+    for (int w0 = 0; w0 < NBW; w0 += 64) {
+      const uint32_t word = (w0 + lane < NBW) ? ubits[w0 + lane] : 0u;
+      const int cnt = __popc(word);
+      const int incl = wave_incl_scan(cnt);
+      int pos = base + incl - cnt;
+      uint32_t wb = word;
+      while (wb) {
+        const int bp = __ffs(wb) - 1;
+        wb &= wb - 1;
+        ulist[pos++] = static_cast<uint16_t>((w0 + lane) * 32 + bp);
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) s_nU = base;
+  }
+  __syncthreads();
+  const int nU = s_nU;
+
+  // ---- per-tile query rows: row r = l16 -> token r/G, head r%G
+  const int G = a.G, TPT = a.TPT;
+  int tl_row[TW];
+  bool valid[TW];
+  uint4 qa[TW][NKS];
+  floatx4 oacc[TW][NDT];
+  float m_run[TW], l_run[TW];
+#pragma unroll
+  for (int ti = 0; ti < TW; ++ti) {
+    const int tile = wv + NW * ti;
+    const int tl = tile * TPT + l16 / G;
+    const int hh = l16 - (l16 / G) * G;
+    valid[ti] = (tile < a.ntiles) && (l16 < TPT * G) && (tl < ntok);
+    tl_row[ti] = valid[ti] ? tl : 0;
+    const uint16_t* qrow =
+        a.q + ((static_cast<size_t>(b) * a.T + t0 + tl_row[ti]) * a.Hq + kv * G + hh) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qa[ti][ks] = valid[ti] ? *reinterpret_cast<const uint4*>(qrow + ks * 32 + g4 * 8)
+                             : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[ti][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m_run[ti] = -INFINITY;
+    l_run[ti] = 0.f;
+  }
+
+  // ---- K/V staging: registers -> LDS (V transposed on the way)
+  uint4 kreg[KU];
+  uint4 vreg[VU][2];
+  auto gload = [&](int j) {
+    const int kbase = j * 64;
+#pragma unroll
+    for (int x = 0; x < KU; ++x) {
+      const int u = tid + 512 * x;
+      const int row = u / (D / 8), ch = u - row * (D / 8);
+      const int tok = kbase + row;
+      kreg[x] = (u < KUN && tok < a.T) ? *reinterpret_cast<const uint4*>(
+                                  a.k + ((static_cast<size_t>(b) * a.T + tok) * a.Hkv + kv) * D + ch * 8)
+                            : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < VU; ++x) {
+      const int u = tid + 512 * x;
+      const int p = u / (D / 8), ch = u - p * (D / 8);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int tok = kbase + 2 * p + r;
+        vreg[x][r] = (u < VUN && tok < a.T) ? *reinterpret_cast<const uint4*>(
+                                       a.v + ((static_cast<size_t>(b) * a.T + tok) * a.Hkv + kv) * D + ch * 8)
+                                 : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < KU; ++x) {
+      const int u = tid + 512 * x;
+      if (u >= KUN) continue;
+      const int row = u / (D / 8), ch = u - row * (D / 8);
+      *reinterpret_cast<uint4*>(&Ks[buf][row * KP + ch * 8]) = kreg[x];
+    }
+#pragma unroll
+    for (int x = 0; x < VU; ++x) {
+      const int u = tid + 512 * x;
+      if (u >= VUN) continue;
+      const int p = u / (D / 8), ch = u - p * (D / 8);
+      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[x][0]);
+      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[x][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (v0[i] & 0xffffu) | (v1[i] << 16);
+        const uint32_t hi = (v0[i] >> 16) | (v1[i] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&Vt[buf][(ch * 8 + 2 * i) * VP + 2 * p]) = lo;
+        *reinterpret_cast<uint32_t*>(&Vt[buf][(ch * 8 + 2 * i + 1) * VP + 2 * p]) = hi;
+      }
+    }
+  };
+
+  if (nU > 0) {
+    gload(ulist[0]);
+    lstore(0);
+    if (nU > 1) gload(ulist[1]);
+  }
+  __syncthreads();
+
+  const float sl2 = a.scale_log2;
+  for (int u = 0; u < nU; ++u) {
+    const int buf = u & 1;
+    const int j = ulist[u];
+    const uint32_t jbit = 1u << (j & 31);
+    const int jw = j >> 5;
+    bool sel[TW];
+    bool act[TW];
+    bool any = false;
+#pragma unroll
+    for (int ti = 0; ti < TW; ++ti) {
+      sel[ti] = valid[ti] && (bits[tl_row[ti]][jw] & jbit);
+      act[ti] = ballot64(sel[ti]) != 0;
+      any |= act[ti];
+    }
+    if (any) {
+#pragma unroll
+      for (int ti = 0; ti < TW; ++ti) {
+        if (!act[ti]) continue;
+        // S^T[key, row] = K[key,:] . Q[row,:]
+        floatx4 sacc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const uint4 ka = *reinterpret_cast<const uint4*>(
+                &Ks[buf][(mt * 16 + l16) * KP + ks * 32 + g4 * 8]);
+            sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
+          }
+        }
+        const int tl = tl_row[ti];
+        float lgv = -INFINITY;
+        if (sel[ti]) {
+          const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
+          lgv = lgs[tl][rank];
+        }
+        const int tpos = t0 + tl;
+        float x[4][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j * 64 + mt * 16 + g4 * 4 + i;
+            float val = sacc[mt][i] * sl2 + lgv;
+            if (key > tpos) val = -INFINITY;
+            x[mt][i] = val;
+            mx = fmaxf(mx, val);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[ti], mx);
+        const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run[ti] - msafe);
+        m_run[ti] = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[mt][i] = exp2f(x[mt][i] - msafe);
+            psum += x[mt][i];
+          }
+        l_run[ti] = l_run[ti] * alpha + psum;
+        uint4 pb[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          pb[k2].x = pack_bf2(x[2 * k2][0], x[2 * k2][1]);
+          pb[k2].y = pack_bf2(x[2 * k2][2], x[2 * k2][3]);
+          pb[k2].z = pack_bf2(x[2 * k2 + 1][0], x[2 * k2 + 1][1]);
+          pb[k2].w = pack_bf2(x[2 * k2 + 1][2], x[2 * k2 + 1][3]);
+        }
+        // O^T[d, row] = alpha O^T + V^T[d, keys] . P^T[keys, row]; inside a
+        // 32-key step the key order follows P's register layout:
+        // {4g..4g+3, 16+4g..16+4g+3}.
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          oacc[ti][dt] *= alpha;
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const uint16_t* vr = &Vt[buf][(dt * 16 + l16) * VP + k2 * 32 + g4 * 4];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+            oacc[ti][dt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[k2], oacc[ti][dt]);
+          }
+        }
+      }
+    }
+    if (u + 1 < nU) lstore(buf ^ 1);
+    if (u + 2 < nU) gload(ulist[u + 2]);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int ti = 0; ti < TW; ++ti) {
+    if (!valid[ti]) continue;
+    float lsum = l_run[ti];
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    const int tl = tl_row[ti];
+    const int hh = l16 - (l16 / G) * G;
+    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh;
+    const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 pk;
+      pk.x = pack_bf2(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv);
+      pk.y = pack_bf2(oacc[ti][dt][2] * inv, oacc[ti][dt][3] * inv);
+      *reinterpret_cast<uint2*>(a.o + row * D + dt * 16 + g4 * 4) = pk;
+    }
+    if (g4 == 0)
+      a.lse[row] = (lsum > 0.f) ? (m_run[ti] + log2f(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
+  const int NQB = (p.T + 63) / 64;
+  const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * NQB);
+  const int tw = (p.ntiles + 7) / 8;
+  switch (tw) {
+    case 1: hipLaunchKernelGGL((sparse_fwd_kernel<D, 1>), grid, dim3(512), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((sparse_fwd_kernel<D, 2>), grid, dim3(512), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((sparse_fwd_kernel<D, 3>), grid, dim3(512), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((sparse_fwd_kernel<D, 4>), grid, dim3(512), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st) {
+  if (p.D == 128) return launch_fwd_d<128>(p, st);
+  if (p.D == 64) return launch_fwd_d<64>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sas

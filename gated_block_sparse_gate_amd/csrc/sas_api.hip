@@ -1,0 +1,292 @@
+// C ABI of libsas: argument validation, workspace layout and dispatch.
+// Every check runs before any launch; on failure nothing is written.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/sas.h"
+#include "sas_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sas_status fail(sas_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sas_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SAS_OK;
+  return fail(SAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+sas_status check_dims(const sas_dims* d) {
+  if (!d) return fail(SAS_ERR_INVALID, "dims pointer is null");
+  if (d->flags != 0) return fail(SAS_ERR_INVALID, "dims.flags must be 0");
+  if (d->B < 1 || d->T < 1 || d->Hq < 1 || d->Hkv < 1)
+    return fail(SAS_ERR_INVALID, "B, T, Hq, Hkv must be >= 1 (got %d, %d, %d, %d)", d->B, d->T,
+                d->Hq, d->Hkv);
+  if (d->Hq % d->Hkv) return fail(SAS_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)",
+                                  d->Hq, d->Hkv);
+  const int G = d->Hq / d->Hkv;
+  if (G > 8) return fail(SAS_ERR_UNSUPPORTED, "G = Hq/Hkv = %d > 8 is not supported", G);
+  if (d->block != 64) return fail(SAS_ERR_UNSUPPORTED, "block must be 64 (got %d)", d->block);
+  if (d->D != 64 && d->D != 128)
+    return fail(SAS_ERR_UNSUPPORTED, "head dim D must be 64 or 128 (got %d)", d->D);
+  if (d->dg != 32 && d->dg != 64 && d->dg != 128)
+    return fail(SAS_ERR_UNSUPPORTED, "gate hidden dg must be 32, 64 or 128 (got %d)", d->dg);
+  if (d->topk < 0) return fail(SAS_ERR_INVALID, "topk must be >= 0 (got %d)", d->topk);
+  if (d->topk + 1 > sas::kMaxS)
+    return fail(SAS_ERR_UNSUPPORTED, "topk must be <= %d (got %d)", sas::kMaxS - 1, d->topk);
+  if (d->T > sas::kMaxNB * 64)
+    return fail(SAS_ERR_UNSUPPORTED, "T must be <= %d (got %d)", sas::kMaxNB * 64, d->T);
+  if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps))
+    return fail(SAS_ERR_INVALID, "norm_eps must be finite and >= 0");
+  if (!(d->rope_theta > 0.0) || !std::isfinite(d->rope_theta))
+    return fail(SAS_ERR_INVALID, "rope_theta must be finite and > 0");
+  if (static_cast<long long>(d->B) * d->Hkv * ((d->T + 63) / 64) > 0x7fffffffLL)
+    return fail(SAS_ERR_UNSUPPORTED, "grid too large");
+  if (static_cast<long long>(d->B) * d->T * d->Hq > 0x7fffffffLL)
+    return fail(SAS_ERR_UNSUPPORTED, "B*T*Hq must be < 2^31");
+  return SAS_OK;
+}
+
+#define REQ_PTR(p)                                                                   \
+  do {                                                                               \
+    if (!(p)) return fail(SAS_ERR_INVALID, "pointer '%s' is null", #p);             \
+    if (!aligned16(p)) return fail(SAS_ERR_INVALID, "pointer '%s' is not 16-byte aligned", #p); \
+  } while (0)
+
+// workspace layouts ------------------------------------------------------
+struct GateWs { size_t wqT, wkT, rope, total; };
+GateWs gate_ws(const sas_dims* d) {
+  const int G = d->Hq / d->Hkv;
+  GateWs w;
+  w.wqT = 0;
+  w.wkT = align_up(w.wqT + sizeof(uint16_t) * d->Hkv * d->dg * G * d->D);
+  w.rope = align_up(w.wkT + sizeof(uint16_t) * d->Hkv * d->dg * 3 * d->D);
+  w.total = align_up(w.rope + sizeof(float2) * static_cast<size_t>(d->T) * (d->dg / 2));
+  return w;
+}
+
+struct BwdWs { size_t delta, cnt2d, rowptr, entries, total; };
+BwdWs bwd_ws(const sas_dims* d) {
+  const size_t NB = (d->T + 63) / 64;
+  const size_t S = d->topk + 1;
+  BwdWs w;
+  w.delta = 0;
+  w.cnt2d = align_up(w.delta + sizeof(float) * static_cast<size_t>(d->B) * d->T * d->Hq);
+  w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
+  w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
+  w.total = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
+  return w;
+}
+
+struct DecWs { size_t idx, logg, part, total; int nsplit; };
+DecWs dec_ws(const sas_decode_dims* d) {
+  const size_t S = d->topk + 1;
+  const size_t G = d->Hq / d->Hkv;
+  DecWs w;
+  w.nsplit = sas::decode_nsplit(static_cast<int>(S));
+  w.idx = 0;
+  w.logg = align_up(w.idx + sizeof(int32_t) * d->B * d->Hkv * S);
+  w.part = align_up(w.logg + sizeof(float) * d->B * d->Hkv * S);
+  w.total = align_up(w.part + sizeof(float) * d->B * d->Hkv * w.nsplit * G * (d->D + 2));
+  return w;
+}
+
+sas_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SAS_OK;
+  if (!ws) return fail(SAS_ERR_WORKSPACE, "workspace is null but %zu bytes are required", need);
+  if (!aligned16(ws)) return fail(SAS_ERR_INVALID, "workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(SAS_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return SAS_OK;
+}
+
+sas_status check_decode_dims(const sas_decode_dims* d) {
+  if (!d) return fail(SAS_ERR_INVALID, "decode dims pointer is null");
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1)
+    return fail(SAS_ERR_INVALID, "B, Hq, Hkv must be >= 1");
+  if (d->Hq % d->Hkv) return fail(SAS_ERR_INVALID, "Hq must be a multiple of Hkv");
+  const int G = d->Hq / d->Hkv;
+  if (G > 8) return fail(SAS_ERR_UNSUPPORTED, "G = Hq/Hkv = %d > 8 is not supported", G);
+  if (d->block != 64) return fail(SAS_ERR_UNSUPPORTED, "block must be 64");
+  if (d->D != 128 && d->D != 64) return fail(SAS_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (d->dg != 32 && d->dg != 64 && d->dg != 128)
+    return fail(SAS_ERR_UNSUPPORTED, "dg must be 32, 64 or 128");
+  if (d->topk < 0) return fail(SAS_ERR_INVALID, "topk must be >= 0");
+  if (d->topk + 1 > sas::kMaxS) return fail(SAS_ERR_UNSUPPORTED, "topk must be <= %d", sas::kMaxS - 1);
+  if (d->Lmax < 1) return fail(SAS_ERR_INVALID, "Lmax must be >= 1");
+  if (d->NBmax != (d->Lmax + 63) / 64)
+    return fail(SAS_ERR_INVALID, "NBmax must equal ceil(Lmax/64) (got %d, Lmax %d)", d->NBmax,
+                d->Lmax);
+  if (d->NBmax > 4096) return fail(SAS_ERR_UNSUPPORTED, "Lmax must be <= 262144");
+  if (d->apply_gate != 0 && d->apply_gate != 1)
+    return fail(SAS_ERR_INVALID, "apply_gate must be 0 or 1");
+  return SAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sas_version(void) { return SAS_VERSION; }
+
+const char* sas_last_error(void) { return g_err.c_str(); }
+
+size_t sas_workspace_size(int op, const sas_dims* d) {
+  if (check_dims(d) != SAS_OK) return static_cast<size_t>(-1);
+  switch (op) {
+    case SAS_OP_GATE_SCORE: return gate_ws(d).total;
+    case SAS_OP_TOPK: return 0;
+    case SAS_OP_FWD: return 0;
+    case SAS_OP_BWD: return bwd_ws(d).total;
+    default: fail(SAS_ERR_INVALID, "unknown op %d", op); return static_cast<size_t>(-1);
+  }
+}
+
+size_t sas_decode_workspace_size(const sas_decode_dims* d) {
+  if (check_decode_dims(d) != SAS_OK) return static_cast<size_t>(-1);
+  return dec_ws(d).total;
+}
+
+sas_status sas_gate_score(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* wq, const uint16_t* wk, const float* w_qn,
+                          const float* w_kn, float* q_gate, float* k_gate, void* ws,
+                          size_t ws_bytes, void* stream) {
+  sas_status st = check_dims(d);
+  if (st) return st;
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(wq); REQ_PTR(wk); REQ_PTR(w_qn); REQ_PTR(w_kn);
+  REQ_PTR(q_gate); REQ_PTR(k_gate);
+  const GateWs w = gate_ws(d);
+  if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+  char* base = static_cast<char*>(ws);
+  sas::RouterParams p{};
+  p.q = q; p.k = k; p.w_qn = w_qn; p.w_kn = w_kn; p.q_gate = q_gate; p.k_gate = k_gate;
+  p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg;
+  p.G = d->Hq / d->Hkv; p.eps = d->norm_eps;
+  g_err.clear();
+  return hip_status(sas::launch_router(p, wq, wk, reinterpret_cast<uint16_t*>(base + w.wqT),
+                                       reinterpret_cast<uint16_t*>(base + w.wkT),
+                                       reinterpret_cast<float2*>(base + w.rope), d->rope_theta,
+                                       static_cast<hipStream_t>(stream)),
+                    "sas_gate_score launch");
+}
+
+sas_status sas_topk_blocks(const sas_dims* d, const float* q_gate, const float* k_gate,
+                           int32_t* idx, float* logg, float* gate_lse, float* gate_probs,
+                           void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  sas_status st = check_dims(d);
+  if (st) return st;
+  REQ_PTR(q_gate); REQ_PTR(k_gate); REQ_PTR(idx); REQ_PTR(logg); REQ_PTR(gate_lse);
+  if (gate_probs && !aligned16(gate_probs))
+    return fail(SAS_ERR_INVALID, "pointer 'gate_probs' is not 16-byte aligned");
+  sas::TopkParams p{};
+  p.q_gate = q_gate; p.k_gate = k_gate; p.idx = idx; p.logg = logg; p.gate_lse = gate_lse;
+  p.gate_probs = gate_probs;
+  p.B = d->B; p.T = d->T; p.Hkv = d->Hkv; p.dg = d->dg; p.K = d->topk; p.S = d->topk + 1;
+  p.NB = (d->T + 63) / 64;
+  const size_t smem = sas::topk_smem_bytes(p.NB, p.dg);
+  if (smem > 160 * 1024) return fail(SAS_ERR_UNSUPPORTED, "T too large for the Top-K kernel");
+  g_err.clear();
+  return hip_status(sas::launch_topk(p, static_cast<hipStream_t>(stream)),
+                    "sas_topk_blocks launch");
+}
+
+sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* idx, const float* logg,
+                               float scale, uint16_t* o, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  sas_status st = check_dims(d);
+  if (st) return st;
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(idx); REQ_PTR(logg); REQ_PTR(o); REQ_PTR(lse);
+  if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
+  sas::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.idx = idx; p.logg = logg; p.o = o; p.lse = lse;
+  p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
+  p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
+  p.TPT = 16 / p.G;
+  p.ntiles = (64 + p.TPT - 1) / p.TPT;
+  p.scale_log2 = scale * sas::kLog2e;
+  g_err.clear();
+  return hip_status(sas::launch_sparse_fwd(p, static_cast<hipStream_t>(stream)),
+                    "sas_sparse_attn_fwd launch");
+}
+
+sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const uint16_t* o, const uint16_t* dout,
+                               const float* lse, const int32_t* idx, const float* logg,
+                               float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                               float* dlogg, void* ws, size_t ws_bytes, void* stream) {
+  sas_status st = check_dims(d);
+  if (st) return st;
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(o); REQ_PTR(dout); REQ_PTR(lse); REQ_PTR(idx);
+  REQ_PTR(logg); REQ_PTR(dq); REQ_PTR(dk); REQ_PTR(dv); REQ_PTR(dlogg);
+  if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
+  const BwdWs w = bwd_ws(d);
+  if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+  char* base = static_cast<char*>(ws);
+  sas::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse; p.idx = idx; p.logg = logg;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dlogg = dlogg;
+  p.delta = reinterpret_cast<float*>(base + w.delta);
+  p.cnt2d = reinterpret_cast<int32_t*>(base + w.cnt2d);
+  p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
+  p.entries = reinterpret_cast<int32_t*>(base + w.entries);
+  p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
+  p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
+  p.TPT = 16 / p.G;
+  p.ntiles = (64 + p.TPT - 1) / p.TPT;
+  p.scale = scale;
+  p.scale_log2 = scale * sas::kLog2e;
+  g_err.clear();
+  return hip_status(sas::launch_sparse_bwd(p, static_cast<hipStream_t>(stream)),
+                    "sas_sparse_attn_bwd launch");
+}
+
+sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const float* kg_cache, const int32_t* ctx_len, float scale,
+                      uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  sas_status st = check_decode_dims(d);
+  if (st) return st;
+  REQ_PTR(q); REQ_PTR(q_gate); REQ_PTR(k_cache); REQ_PTR(v_cache); REQ_PTR(kg_cache);
+  REQ_PTR(ctx_len); REQ_PTR(o);
+  if (idx_out && !aligned16(idx_out)) return fail(SAS_ERR_INVALID, "idx_out is not 16-byte aligned");
+  if (logg_out && !aligned16(logg_out))
+    return fail(SAS_ERR_INVALID, "logg_out is not 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
+  const DecWs w = dec_ws(d);
+  if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+  char* base = static_cast<char*>(ws);
+  sas::DecodeParams p{};
+  p.q = q; p.q_gate = q_gate; p.k_cache = k_cache; p.v_cache = v_cache; p.kg_cache = kg_cache;
+  p.ctx_len = ctx_len; p.o = o; p.idx_out = idx_out; p.logg_out = logg_out;
+  p.ws_idx = reinterpret_cast<int32_t*>(base + w.idx);
+  p.ws_logg = reinterpret_cast<float*>(base + w.logg);
+  p.ws_part = reinterpret_cast<float*>(base + w.part);
+  p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
+  p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
+  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit;
+  p.scale_log2 = scale * sas::kLog2e;
+  g_err.clear();
+  return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)), "sas_decode launch");
+}
+
+}  // extern "C"

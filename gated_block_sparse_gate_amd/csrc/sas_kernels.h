@@ -1,0 +1,107 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sas_device.h"
+
+namespace sas {
+
+constexpr int kMaxNB = 1024;            // T <= 65536
+constexpr int kMaxNBW = kMaxNB / 32;    // bitmap words per token
+constexpr int kMaxS = 64;               // topk <= 63
+
+struct RouterParams {
+  const uint16_t* q;    // [B,T,Hq,D]
+  const uint16_t* k;    // [B,T,Hkv,D]
+  const uint16_t* wqT;  // [Hkv,dg,G*D]  (transposed copy in the workspace)
+  const uint16_t* wkT;  // [Hkv,dg,3*D]
+  const float* w_qn;    // [dg]
+  const float* w_kn;    // [dg]
+  const float2* rope;   // [T, dg/2] (cos, sin)
+  float* q_gate;        // [B,T,Hkv,dg]
+  float* k_gate;        // [B,T,Hkv,dg]
+  int B, T, Hq, Hkv, D, dg, G;
+  float eps;
+};
+
+struct TopkParams {
+  const float* q_gate;  // [B,T,Hkv,dg]
+  const float* k_gate;  // [B,T,Hkv,dg]
+  int32_t* idx;         // [B,T,Hkv,S]
+  float* logg;          // [B,T,Hkv,S]
+  float* gate_lse;      // [B,T,Hkv]
+  float* gate_probs;    // [B,T,Hkv,NB] or null
+  int B, T, Hkv, dg, K, S, NB;
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  const float* logg;
+  uint16_t* o;
+  float* lse;
+  int B, T, Hq, Hkv, D, G, S, NB;
+  int TPT;      // tokens per 16-row tile = floor(16 / G)
+  int ntiles;   // tiles per 64-token query block = ceil(64 / TPT)
+  float scale_log2;   // scale * log2(e)
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  const int32_t* idx;
+  const float* logg;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dlogg;
+  // workspace
+  float* delta;         // [B,T,Hq]
+  int32_t* cnt2d;       // [B,Hkv,NQB,NB]  per (query block, key block) counts -> offsets
+  int32_t* rowptr;      // [B,Hkv,NB+1]
+  int32_t* entries;     // [B,Hkv,T*S] packed (t << 6) | slot
+  int B, T, Hq, Hkv, D, G, S, NB;
+  int TPT, ntiles;
+  float scale, scale_log2;
+};
+
+struct DecodeParams {
+  const uint16_t* q;        // [B,Hq,D]
+  const float* q_gate;      // [B,Hkv,dg]
+  const uint16_t* k_cache;  // [B,Hkv,Lmax,D]
+  const uint16_t* v_cache;
+  const float* kg_cache;    // [B,Hkv,NBmax,dg]
+  const int32_t* ctx_len;   // [B]
+  uint16_t* o;              // [B,Hq,D]
+  int32_t* idx_out;         // [B,Hkv,S] or null
+  float* logg_out;          // [B,Hkv,S] or null
+  // workspace
+  int32_t* ws_idx;          // [B,Hkv,S]
+  float* ws_logg;           // [B,Hkv,S]
+  float* ws_part;           // [B,Hkv,NSPLIT,G,(D+2)] partial (m, l, o[D])
+  int B, Hq, Hkv, D, dg, G, K, S, Lmax, NBmax, apply_gate, nsplit;
+  float scale_log2;
+};
+
+hipError_t launch_router(const RouterParams& p, const uint16_t* wq, const uint16_t* wk,
+                         uint16_t* wqT, uint16_t* wkT, float2* rope, double theta,
+                         hipStream_t st);
+hipError_t launch_topk(const TopkParams& p, hipStream_t st);
+hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st);
+hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
+
+// decode split factor for a given problem (also sizes its workspace)
+int decode_nsplit(int S);
+
+// dynamic LDS bytes of the Top-K kernel
+size_t topk_smem_bytes(int NB, int dg);
+
+}  // namespace sas

@@ -1,0 +1,221 @@
+/*
+ * sas.h - C ABI of libsas: SAS gated block-sparse attention on MI355X (gfx950).
+ *
+ * SAS ("Simple Attention Sparsification via End-to-End Optimization of
+ * Context Ranking", arXiv 2609.13141) lets a lightweight router score 64-token
+ * KV blocks per query, keeps the Top-K historical blocks plus the always-kept
+ * current block, and adds log(gate) of each selected block inside the
+ * attention softmax, so the language-modelling loss reaches the router
+ * (paper abstract; GitHub README, items (a) and (b)).  Router settings come
+ * from the model card's "Checkpoint configuration" table: KV block 64, Top-K
+ * 31, gate hidden 128, Qproj, key pooling max + min + average, Q/K
+ * normalisation, gate RoPE.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a device pointer to contiguous memory in the
+ *     layout stated beside it, 16-byte aligned.  `bf16` tensors are passed as
+ *     uint16_t bit patterns.  The caller owns every buffer.
+ *   - `stream` is a hipStream_t (NULL = default stream).  Work is enqueued
+ *     asynchronously; the library never synchronises the device.
+ *   - The library allocates no device memory.  Calls that need scratch space
+ *     take a caller-provided workspace `ws` of at least the size reported by
+ *     sas_workspace_size() / sas_decode_workspace_size().
+ *   - All arguments are validated before anything is launched.  On any error
+ *     the call returns a non-zero sas_status, writes nothing and records a
+ *     message readable through sas_last_error() (thread-local).
+ *   - Index and selection data computed on the device (idx, ctx_len) are
+ *     range-checked by the kernels: out-of-range entries are ignored, never
+ *     dereferenced.
+ *   - NaN/Inf inputs propagate to outputs; selections made from NaN scores
+ *     are unspecified but always in range.
+ *
+ * Supported specialisations: block = 64; D in {64, 128}; dg in {32, 64, 128};
+ * 1 <= G = Hq / Hkv <= 8 (Hq divisible by Hkv); 0 <= topk <= 63;
+ * 1 <= T <= 65536; B >= 1.
+ */
+#ifndef SAS_H_
+#define SAS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAS_VERSION 1
+
+typedef enum {
+  SAS_OK = 0,
+  SAS_ERR_INVALID = 1,      /* null pointer, bad shape or value, misalignment */
+  SAS_ERR_UNSUPPORTED = 2,  /* dimensions outside the compiled specialisations */
+  SAS_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  SAS_ERR_HIP = 4           /* a HIP launch failed; see sas_last_error() */
+} sas_status;
+
+/* Operation ids for sas_workspace_size(). */
+enum {
+  SAS_OP_GATE_SCORE = 0,
+  SAS_OP_TOPK = 1,
+  SAS_OP_FWD = 2,
+  SAS_OP_BWD = 3
+};
+
+/*
+ * Prefill / training-step dimensions.
+ *   B batch, T tokens, Hq query heads, Hkv KV heads (G = Hq/Hkv query heads
+ *   share one KV head and one gate), D head dim, dg gate hidden size,
+ *   block KV block size (must be 64), topk historical blocks K per query
+ *   (S = K + 1 slots per query: K historical + the current block),
+ *   rope_theta gate-RoPE base, norm_eps RMSNorm epsilon, flags reserved (0).
+ */
+typedef struct {
+  int32_t B, T, Hq, Hkv, D, dg, block, topk;
+  double rope_theta;
+  float norm_eps;
+  int32_t flags;
+} sas_dims;
+
+/*
+ * Decode dimensions.  B sequences with one new token each; KV cache holds up
+ * to Lmax tokens per sequence, the gate-key cache NBmax = ceil(Lmax/64)
+ * blocks.  apply_gate = 1 adds log g to the logits (same function as
+ * training); 0 = selection only, no gate bias.
+ */
+typedef struct {
+  int32_t B, Hq, Hkv, D, dg, block, topk, Lmax, NBmax, apply_gate;
+} sas_decode_dims;
+
+/* Library version (SAS_VERSION). */
+int sas_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sas_last_error(void);
+
+/* Workspace bytes needed by op (SAS_OP_*) for dims d; 0 if none; (size_t)-1
+ * if d is invalid. */
+size_t sas_workspace_size(int op, const sas_dims* d);
+
+/* Workspace bytes needed by sas_decode; (size_t)-1 if d is invalid. */
+size_t sas_decode_workspace_size(const sas_decode_dims* d);
+
+/*
+ * Gate router (model card table: Qproj, max+min+average key pooling, Q/K
+ * normalisation, gate RoPE; abstract: "lightweight selector").
+ *
+ * For batch b, KV head kappa, token t with block c = t/64:
+ *   q_gate[b,t,kappa,:] = RoPE_t( RMSNorm( x_t . wq[kappa] ) * w_qn )
+ *       x_t = concatenation of q[b,t,kappa*G+i,:] for i = 0..G-1  (G*D wide)
+ *   k_gate[b,t,kappa,:] = RoPE_{64c}( RMSNorm( p_t . wk[kappa] ) * w_kn )
+ *       p_t = [max; min; mean] channel-wise over k[b,64c..t,kappa,:]  (3D)
+ * RMSNorm(y) = y / sqrt(mean(y^2) + norm_eps); RoPE rotates pairs
+ * (i, i+dg/2) by pos * rope_theta^(-2i/dg) (angles reduced in double).
+ * k_gate of token 64j+63 is the key of complete block j; the current block
+ * of token t uses its own causal prefix key k_gate[t].
+ *
+ *   q      [B,T,Hq,D]  bf16      k     [B,T,Hkv,D] bf16
+ *   wq     [Hkv,G*D,dg] bf16     wk    [Hkv,3*D,dg] bf16
+ *   w_qn, w_kn [dg] fp32
+ *   q_gate, k_gate [B,T,Hkv,dg] fp32 (outputs, fully overwritten)
+ *   ws: workspace of sas_workspace_size(SAS_OP_GATE_SCORE, d) bytes
+ */
+sas_status sas_gate_score(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* wq, const uint16_t* wk, const float* w_qn,
+                          const float* w_kn, float* q_gate, float* k_gate, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Candidate softmax and Top-K selection (abstract: normalised softmax gates
+ * calibrate history against the always-retained current block; README (a):
+ * discrete Top-K).
+ *
+ * For each (b, t, kappa) with c = t/64:
+ *   s_j = q_gate[t] . k_gate[64j+63] / sqrt(dg)   for historical j < c
+ *   s_c = q_gate[t] . k_gate[t]      / sqrt(dg)   (current block)
+ *   gate_lse = logsumexp_{j<=c} s_j;  log g_j = s_j - gate_lse
+ *   selection = the min(K, c) largest s_j over j < c (equal scores: lower j
+ *   first) in ascending order, then c.  Slots beyond are padding.
+ *
+ *   idx   [B,T,Hkv,K+1] int32  selected block ids, ascending, current last, pad -1
+ *   logg  [B,T,Hkv,K+1] fp32   log g of each slot, pad -inf
+ *   gate_lse [B,T,Hkv] fp32
+ *   gate_probs [B,T,Hkv,NB] fp32 or NULL: dense g_j (0 for j > c), NB = ceil(T/64)
+ *   ws: sas_workspace_size(SAS_OP_TOPK, d) bytes (may be 0 / NULL)
+ */
+sas_status sas_topk_blocks(const sas_dims* d, const float* q_gate, const float* k_gate,
+                           int32_t* idx, float* logg, float* gate_lse, float* gate_probs,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gated sparse attention forward (abstract: log gate inside the attention
+ * softmax; README (b): a continuous gate on each selected block; the
+ * FlashAttention-style kernel mentioned in the abstract).
+ *
+ * For query head h (KV head kappa = h/G) and token t:
+ *   l_tau = scale * q[t,h] . k[tau,kappa] + logg[t,kappa,slot(tau)]
+ *   over the keys tau of the blocks in idx[t,kappa,:] with tau <= t;
+ *   o[t,h] = softmax(l) . v;  lse[t,h] = logsumexp(l)  (natural log).
+ *
+ *   q [B,T,Hq,D], k, v [B,T,Hkv,D] bf16;  idx, logg as produced by
+ *   sas_topk_blocks (entries outside [0, t/64] are ignored; the valid
+ *   entries must be distinct); o [B,T,Hq,D] bf16, lse [B,T,Hq] fp32 outputs.
+ *   ws: sas_workspace_size(SAS_OP_FWD, d) bytes (may be 0 / NULL).
+ *   Deterministic (bitwise repeatable).
+ */
+sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* idx, const float* logg,
+                               float scale, uint16_t* o, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * Gated sparse attention backward (README (b) / abstract: the LM loss
+ * reaches the selector through log g).
+ *
+ * With P the forward probabilities (from lse), Delta = rowsum(dout * o),
+ * dS = P (dout . v - Delta):
+ *   dq = scale sum dS k;  dk = scale sum dS q;  dv = sum P dout;
+ *   dlogg[t,kappa,slot] = sum over the G heads of kappa and the keys of the
+ *   slot's block of dS  (gradient w.r.t. log g; pads 0).
+ *
+ *   q, k, v, o, dout bf16 as in the forward; lse from the forward;
+ *   dq [B,T,Hq,D], dk, dv [B,T,Hkv,D] bf16 (fully overwritten, fp32
+ *   accumulation); dlogg [B,T,Hkv,K+1] fp32.
+ *   ws: sas_workspace_size(SAS_OP_BWD, d) bytes.
+ *   Deterministic (bitwise repeatable).
+ */
+sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const uint16_t* o, const uint16_t* dout,
+                               const float* lse, const int32_t* idx, const float* logg,
+                               float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                               float* dlogg, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Budgeted single-token decode (model card: sparse decode budget of 1,024 /
+ * 2,048 / 4,096 tokens = 64 (topk + 1); usage guide pitfall 3: the budget
+ * bounds the tokens each query attends, not the KV cache).
+ *
+ * Per sequence b with L = ctx_len[b] (the new token sits at position L-1,
+ * c = (L-1)/64) and KV head kappa:
+ *   s_j = q_gate[b,kappa] . kg_cache[b,kappa,j] / sqrt(dg), j = 0..c
+ *   (entry c is the current block's causal prefix key), selection and log g
+ *   as in sas_topk_blocks, then attention of the G query heads over the
+ *   selected blocks' keys tau < L, with log g added when apply_gate = 1.
+ *
+ *   q [B,Hq,D] bf16;  q_gate [B,Hkv,dg] fp32;
+ *   k_cache, v_cache [B,Hkv,Lmax,D] bf16 (head-major contiguous cache);
+ *   kg_cache [B,Hkv,NBmax,dg] fp32;  ctx_len [B] int32 (device);
+ *   o [B,Hq,D] bf16 output;  idx_out [B,Hkv,K+1] int32 and logg_out
+ *   [B,Hkv,K+1] fp32 outputs (either may be NULL).
+ *   A sequence with ctx_len outside [1, Lmax] gets o = NaN, idx = -1.
+ *   ws: sas_decode_workspace_size(d) bytes.
+ */
+sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const float* kg_cache, const int32_t* ctx_len, float scale,
+                      uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAS_H_ */

@@ -309,8 +309,9 @@ def attn_fwd_dense(q, k, v, idx, logg, scale: float):
     return o, lse
 
 
-def attn_bwd(q, k, v, dout, idx, logg, scale: float):
-    """Backward of the gather form for all rows (small T).
+def attn_bwd(q, k, v, dout, idx, logg, scale: float, tokens=None):
+    """Backward of the gather form for all rows (small T), or for the query
+    rows of the chosen tokens only (dk, dv then hold those rows' contributions).
 
     dP = dO.v;  Delta = dO.o;  dS = P (dP - Delta);
     dq = scale sum dS k;  dk += scale dS q;  dv += P dO;
@@ -330,8 +331,9 @@ def attn_bwd(q, k, v, dout, idx, logg, scale: float):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dlogg = np.zeros((B, T, Hkv, S))
+    tok = range(T) if tokens is None else [int(t) for t in tokens]
     for b in range(B):
-        for t in range(T):
+        for t in tok:
             for kv in range(Hkv):
                 taus, slots = _row_keys(t, idx[b, t, kv])
                 Kr, Vr = k[b, taus, kv], v[b, taus, kv]

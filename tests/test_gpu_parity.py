@@ -1,0 +1,275 @@
+"""GPU parity: every libsas call against the fp64 oracle on seeded inputs.
+
+Sizes are small enough for the oracle to finish in seconds while spanning
+several 64-token blocks, ragged tails, GQA group sizes 1/2/4/5/8, K = 0 and
+K beyond the number of blocks.  Tolerances: selected block indices
+bit-exact outside near-tie rows (K-th/(K+1)-th gate-logit gap < 1e-5 in
+fp64); bf16 outputs and gradients within 1e-2 max-abs beyond the bf16
+representation error of the exact value (half a bf16 ulp of the reference,
+which alone reaches 1.6e-2 for |x| in [4, 8)) and 1e-3 mean-abs of the raw
+error; fp32 outputs (log-gate gradient, lse) and router outputs within the
+stated absolute bounds with no allowance.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_block_sparse_gate_amd as sas
+import synth
+from oracle import sas_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 1e-2, 1e-3
+ROUTER_ABS = 1e-4
+
+
+def W(name, T, Hq, Hkv, D, dg, K, B=1, cfg=90):
+    return synth.Workload(name, cfg, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, dg=dg, topk=K)
+
+
+CASES = [
+    synth.TINY,
+    W("g4_ragged", 1000, 8, 2, 128, 128, 7),
+    W("g5", 700, 10, 2, 128, 128, 5),
+    W("g1_b2", 300, 2, 2, 64, 64, 2, B=2),
+    W("short", 50, 4, 1, 128, 128, 3),
+    W("k0", 400, 4, 2, 64, 32, 0),
+    W("kbig", 600, 4, 1, 128, 128, 20),
+    W("g8", 260, 8, 1, 128, 128, 3),
+]
+IDS = [c.name for c in CASES]
+
+_cache = {}
+
+
+def prepared(w, seed=0):
+    key = (w.name, seed)
+    if key in _cache:
+        return _cache[key]
+    x = synth.prefill_inputs(w, seed=seed, device="cpu")
+    x64 = {k: O.as64(v) for k, v in x.items()}
+    r = O.route(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"], w.topk,
+                w.theta, w.eps)
+    kg_all = O.gate_key(x64["k"], x64["wk"], x64["w_kn"], w.theta, w.eps)
+    sc = 1.0 / math.sqrt(w.D)
+    g = O.attn_bwd(x64["q"], x64["k"], x64["v"], x64["dout"], r["idx"], r["logg"], sc)
+    dev = {k: v.cuda() for k, v in x.items()}
+    out = dict(x=x, x64=x64, r=r, kg_all=kg_all, g=g, dev=dev, scale=sc)
+    _cache[key] = out
+    return out
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 ulp (8 significant bits) at |x|."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 8)
+
+
+def errs(gpu, ref):
+    """(raw max-abs, max-abs beyond bf16 representation, raw mean-abs)."""
+    a = gpu.detach().float().cpu().numpy().astype(np.float64)
+    d = np.abs(a - ref)
+    excess = d
+    if gpu.dtype == torch.bfloat16:
+        excess = np.maximum(0.0, d - bf16_half_ulp(np.maximum(np.abs(ref), np.abs(a))))
+    return float(d.max()), float(excess.max()), float(d.mean())
+
+
+def assert_close(name, gpu, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    raw, mx, mn = errs(gpu, ref)
+    print(f"  {name}: max-abs {raw:.3e} (beyond bf16 rounding {mx:.3e}) mean-abs {mn:.3e}",
+          flush=True)
+    assert mx <= max_abs and mn <= mean_abs, (name, raw, mx, mn)
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_gate_score(w):
+    P = prepared(w)
+    d = P["dev"]
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    torch.cuda.synchronize()
+    assert_close("q_gate", qg, P["r"]["qg"], ROUTER_ABS, ROUTER_ABS)
+    assert_close("k_gate", kg, P["kg_all"], ROUTER_ABS, ROUTER_ABS)
+
+
+def _nontie(r):
+    return ~r["near_tie"]
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_topk_on_oracle_gate_vectors(w):
+    """Selection numerics alone: the oracle's q_gate / k_gate rounded to fp32."""
+    P = prepared(w)
+    r = P["r"]
+    qg = torch.tensor(np.ascontiguousarray(r["qg"]), dtype=torch.float32).cuda()
+    kg = torch.tensor(np.ascontiguousarray(P["kg_all"]), dtype=torch.float32).cuda()
+    idx, logg, lse, probs = sas.topk_blocks(qg, kg, w.topk, w.Hq, w.D, want_probs=True)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    ok = _nontie(r)
+    print(f"  near-tie rows: {int((~ok).sum())} of {ok.size}")
+    assert (~ok).mean() < 0.01
+    np.testing.assert_array_equal(gi[ok], r["idx"][ok])
+    lg = logg.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(r["logg"]) & ok[..., None]
+    assert np.all(np.isinf(lg[~np.isfinite(r["logg"])]))
+    assert np.abs(lg[fin] - r["logg"][fin]).max() < ROUTER_ABS
+    assert np.abs(lse.cpu().numpy() - r["lse"]).max() < ROUTER_ABS
+    np.testing.assert_allclose(probs.sum(-1).cpu().numpy(), 1.0, atol=1e-5)
+    assert np.abs(probs.cpu().numpy() - r["probs"]).max() < 1e-5
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_router_and_topk_chain(w):
+    P = prepared(w)
+    d = P["dev"]
+    r = P["r"]
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    idx, logg, lse, _ = sas.topk_blocks(qg, kg, w.topk, w.Hq, w.D)
+    torch.cuda.synchronize()
+    ok = _nontie(r)
+    gi = idx.cpu().numpy()
+    mism = (gi != r["idx"]).any(-1) & ok
+    print(f"  index mismatches on non-near-tie rows: {int(mism.sum())}")
+    np.testing.assert_array_equal(gi[ok], r["idx"][ok])
+    fin = np.isfinite(r["logg"]) & ok[..., None]
+    assert np.abs(logg.cpu().numpy()[fin] - r["logg"][fin]).max() < ROUTER_ABS
+
+
+def _oracle_sel(P):
+    r = P["r"]
+    idx = torch.tensor(np.ascontiguousarray(r["idx"]), dtype=torch.int32).cuda()
+    logg = torch.tensor(np.ascontiguousarray(r["logg"]), dtype=torch.float32).cuda()
+    return idx, logg
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_sparse_attn_fwd(w):
+    P = prepared(w)
+    d = P["dev"]
+    idx, logg = _oracle_sel(P)
+    o, lse = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"])
+    torch.cuda.synchronize()
+    assert_close("o", o, P["g"]["o"])
+    assert_close("lse", lse, P["g"]["lse"], 1e-3, 1e-4)
+    o2, lse2 = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "forward not bitwise repeatable"
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_sparse_attn_bwd(w):
+    P = prepared(w)
+    d = P["dev"]
+    idx, logg = _oracle_sel(P)
+    o, lse = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"])
+    dq, dk, dv, dlogg = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg,
+                                            P["scale"])
+    torch.cuda.synchronize()
+    g = P["g"]
+    assert_close("dq", dq, g["dq"])
+    assert_close("dk", dk, g["dk"])
+    assert_close("dv", dv, g["dv"])
+    assert_close("dlogg", dlogg, g["dlogg"])
+    # gradient w.r.t. log g sums to zero over each row's selected slots
+    assert float(dlogg.sum(-1).abs().max()) < 1e-3
+    out2 = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg, P["scale"])
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv, dlogg), out2):
+        assert torch.equal(a, b), "backward not bitwise repeatable"
+
+
+def test_outputs_stay_in_bounds():
+    """NaN canaries after every output buffer stay untouched."""
+    w = CASES[1]
+    P = prepared(w)
+    d = P["dev"]
+    idx, logg = _oracle_sel(P)
+    B, T, Hq, D, Hkv, S = w.B, w.T, w.Hq, w.D, w.Hkv, w.topk + 1
+    pad = 4096
+
+    def canary(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((n + pad,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[:n].view(shape)
+
+    ob, o = canary((B, T, Hq, D), torch.bfloat16)
+    lb, lse = canary((B, T, Hq), torch.float32)
+    sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"], o=o, lse=lse)
+    bufs = [canary((B, T, Hq, D), torch.bfloat16), canary((B, T, Hkv, D), torch.bfloat16),
+            canary((B, T, Hkv, D), torch.bfloat16), canary((B, T, Hkv, S), torch.float32)]
+    sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg, P["scale"],
+                        out=tuple(b[1] for b in bufs))
+    torch.cuda.synchronize()
+    for b, _ in [(ob, 0), (lb, 0)] + bufs:
+        assert torch.isnan(b[-pad:].float()).all()
+    for _, v in [(ob, o), (lb, lse)] + bufs:
+        assert not torch.isnan(v.float()).any()
+
+
+# ---------------------------------------------------------------- decode
+
+DEC_CASES = [
+    # (B, Hq, Hkv, D, dg, K, Lmax, lengths)
+    (3, 8, 2, 128, 128, 7, 5000, [5000, 1, 64]),
+    (4, 8, 2, 128, 128, 31, 4200, [65, 4200, 2049, 128]),
+    (2, 10, 2, 64, 32, 3, 700, [700, 300]),
+]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=[f"dec{i}" for i in range(len(DEC_CASES))])
+@pytest.mark.parametrize("apply_gate", [True, False])
+def test_decode(case, apply_gate):
+    B, Hq, Hkv, D, dg, K, Lmax, lens = case
+    w = synth.Workload("dec", 91, B=B, T=1, Hq=Hq, Hkv=Hkv, D=D, dg=dg, topk=K, kind="decode",
+                       Lmin=1, Lmax=Lmax)
+    x = synth.decode_inputs(w, seed=1, device="cpu", ctx_len=torch.tensor(lens, dtype=torch.int32))
+    sc = 1.0 / math.sqrt(D)
+    ref = O.decode(x["q"], x["q_gate"], x["k_cache"], x["v_cache"], x["kg_cache"], x["ctx_len"],
+                   K, sc, apply_gate=apply_gate)
+    dev = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in x.items()}
+    o, idx, logg = sas.decode(dev["q"], dev["q_gate"], dev["k_cache"], dev["v_cache"],
+                              dev["kg_cache"], dev["ctx_len"], K, sc, apply_gate=apply_gate)
+    torch.cuda.synchronize()
+    ok = ~ref["near_tie"]
+    np.testing.assert_array_equal(idx.cpu().numpy()[ok], ref["idx"][ok])
+    fin = np.isfinite(ref["logg"]) & ok[..., None]
+    assert np.abs(logg.cpu().numpy()[fin] - ref["logg"][fin]).max() < ROUTER_ABS
+    assert_close("o", o, ref["o"])
+
+
+def test_decode_matches_prefill_row():
+    """Decode of token L-1 equals the prefill row L-1 computed by the library."""
+    w = CASES[1]
+    P = prepared(w)
+    d = P["dev"]
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    idx, logg, _, _ = sas.topk_blocks(qg, kg, w.topk, w.Hq, w.D)
+    o, _ = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"])
+    L = torch.tensor([w.T, 333, 64], dtype=torch.int32)
+    B = len(L)
+    NBmax = -(-w.T // 64)
+    kc = d["k"][0].transpose(0, 1).contiguous()[None].expand(B, -1, -1, -1).contiguous()
+    vc = d["v"][0].transpose(0, 1).contiguous()[None].expand(B, -1, -1, -1).contiguous()
+    kgc = torch.zeros((B, w.Hkv, NBmax, w.dg), dtype=torch.float32, device="cuda")
+    qd = torch.empty((B, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    qgd = torch.empty((B, w.Hkv, w.dg), dtype=torch.float32, device="cuda")
+    for bi, Lb in enumerate(L.tolist()):
+        c = (Lb - 1) // 64
+        for j in range(c):
+            kgc[bi, :, j] = kg[0, 64 * j + 63]
+        kgc[bi, :, c] = kg[0, Lb - 1]
+        qd[bi] = d["q"][0, Lb - 1]
+        qgd[bi] = qg[0, Lb - 1]
+    od, idd, _ = sas.decode(qd, qgd, kc, vc, kgc, L.cuda(), w.topk, P["scale"])
+    torch.cuda.synchronize()
+    for bi, Lb in enumerate(L.tolist()):
+        assert torch.equal(idd[bi], idx[0, Lb - 1])
+        diff = (od[bi].float() - o[0, Lb - 1].float()).abs().max().item()
+        assert diff <= 1e-2, diff
