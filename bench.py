@@ -160,6 +160,7 @@ def main():
     d = sas.make_dims(B, T, Hq, Hkv, D, dg, K, w.theta, w.eps)
     ws_gate = torch.empty(sas.workspace_size(sas.OP_GATE_SCORE, d), dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(sas.workspace_size(sas.OP_BWD, d), dtype=torch.uint8, device=dev)
+    ws_fwd = torch.empty(sas.workspace_size(sas.OP_FWD, d), dtype=torch.uint8, device=dev)
     qg = torch.empty((B, T, Hkv, dg), dtype=torch.float32, device=dev)
     kg = torch.empty_like(qg)
     idx = torch.empty((B, T, Hkv, S), dtype=torch.int32, device=dev)
@@ -167,6 +168,7 @@ def main():
     glse = torch.empty((B, T, Hkv), dtype=torch.float32, device=dev)
     o = torch.empty_like(x["q"])
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    o32 = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
     dq = torch.empty_like(x["q"])
     dk = torch.empty_like(x["k"])
     dv = torch.empty_like(x["v"])
@@ -185,11 +187,12 @@ def main():
         sas.topk_blocks(qg, kg, K, Hq, D, out=(idx, logg, glse))
         if record:
             ev[2].record(stream)
-        sas.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, logg, scale, o=o, lse=lse)
+        sas.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, logg, scale, o=o, lse=lse, o_f32=o32,
+                            workspace=ws_fwd)
         if record:
             ev[3].record(stream)
         sas.sparse_attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, scale,
-                            workspace=ws_bwd, out=(dq, dk, dv, dlogg))
+                            workspace=ws_bwd, out=(dq, dk, dv, dlogg), o_f32=o32)
         if record:
             ev[4].record(stream)
 
@@ -263,7 +266,7 @@ def main():
 
     # ------------------------------------------------------------ decode
     if not args.no_decode:
-        del x, qg, kg, idx, logg, glse, o, lse, dq, dk, dv, dlogg, ws_gate, ws_bwd
+        del x, qg, kg, idx, logg, glse, o, o32, lse, dq, dk, dv, dlogg, ws_gate, ws_bwd, ws_fwd
         torch.cuda.empty_cache()
         wd = synth.DECODE_B64
         xd = synth.decode_inputs(wd, seed=args.seed, device=dev)

@@ -77,8 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sas_decode_workspace_size.restype = S
     lib.sas_gate_score.argtypes = [ctypes.POINTER(Dims)] + [P] * 8 + [P, S, P]
     lib.sas_topk_blocks.argtypes = [ctypes.POINTER(Dims)] + [P] * 6 + [P, S, P]
-    lib.sas_sparse_attn_fwd.argtypes = [ctypes.POINTER(Dims)] + [P] * 5 + [F32] + [P] * 2 + [P, S, P]
-    lib.sas_sparse_attn_bwd.argtypes = ([ctypes.POINTER(Dims)] + [P] * 8 + [F32] + [P] * 4
+    lib.sas_sparse_attn_fwd.argtypes = [ctypes.POINTER(Dims)] + [P] * 5 + [F32] + [P] * 3 + [P, S, P]
+    lib.sas_sparse_attn_bwd.argtypes = ([ctypes.POINTER(Dims)] + [P] * 9 + [F32] + [P] * 4
                                         + [P, S, P])
     lib.sas_decode.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 6 + [F32] + [P] * 3
                                + [P, S, P])
@@ -209,8 +209,11 @@ def topk_blocks(q_gate, k_gate, topk: int, Hq: int, D: int, want_probs: bool = F
     return idx, logg, lse, probs
 
 
-def sparse_attn_fwd(q, k, v, idx, logg, scale: float | None = None, o=None, lse=None):
-    """Gated sparse attention forward: returns (o bf16 [B,T,Hq,D], lse fp32 [B,T,Hq])."""
+def sparse_attn_fwd(q, k, v, idx, logg, scale: float | None = None, o=None, lse=None,
+                    o_f32=None, want_f32: bool = False, workspace=None):
+    """Gated sparse attention forward: returns (o bf16 [B,T,Hq,D], lse fp32 [B,T,Hq])
+    or, with want_f32 / o_f32 given, (o, lse, o_f32) where o_f32 is the fp32
+    result before rounding (pass it to sparse_attn_bwd for an exact Delta)."""
     lib = load_library()
     dev = _device_of(q)
     B, T, Hq, D = q.shape
@@ -227,15 +230,23 @@ def sparse_attn_fwd(q, k, v, idx, logg, scale: float | None = None, o=None, lse=
         o = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    if want_f32 and o_f32 is None:
+        o_f32 = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    if o_f32 is not None:
+        _req(o_f32, "o_f32", torch.float32, (B, T, Hq, D), dev)
+    nws = workspace_size(OP_FWD, d)
+    ws = workspace if workspace is not None else _ws(nws, dev)
     _check(lib.sas_sparse_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                   _ptr(logg), ctypes.c_float(scale), _ptr(o), _ptr(lse), None, 0,
+                                   _ptr(logg), ctypes.c_float(scale), _ptr(o), _ptr(lse),
+                                   _ptr(o_f32), _ptr(ws), ws.numel() if ws is not None else 0,
                                    _stream(dev)))
-    return o, lse
+    return (o, lse, o_f32) if o_f32 is not None else (o, lse)
 
 
 def sparse_attn_bwd(q, k, v, o, dout, lse, idx, logg, scale: float | None = None,
-                    workspace=None, out=None):
-    """Backward: returns (dq, dk, dv bf16, dlogg fp32 [B,T,Hkv,S])."""
+                    workspace=None, out=None, o_f32=None):
+    """Backward: returns (dq, dk, dv bf16, dlogg fp32 [B,T,Hkv,S]).  o_f32 (the
+    forward's fp32 output, optional) makes Delta = rowsum(dout * o) exact."""
     lib = load_library()
     dev = _device_of(q)
     B, T, Hq, D = q.shape
@@ -248,6 +259,8 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, idx, logg, scale: float | None = None
                          (idx, "idx", torch.int32, (B, T, Hkv, S)),
                          (logg, "logg", torch.float32, (B, T, Hkv, S))):
         _req(t, n, dt, sh, dev)
+    if o_f32 is not None:
+        _req(o_f32, "o_f32", torch.float32, (B, T, Hq, D), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     d = make_dims(B, T, Hq, Hkv, D, 128, S - 1)
     if out is None:
@@ -259,7 +272,8 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, idx, logg, scale: float | None = None
         dq, dk, dv, dlogg = out
     nws = workspace_size(OP_BWD, d)
     ws = workspace if workspace is not None else _ws(nws, dev)
-    _check(lib.sas_sparse_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+    _check(lib.sas_sparse_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(o_f32), _ptr(dout),
                                    _ptr(lse), _ptr(idx), _ptr(logg), ctypes.c_float(scale),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlogg), _ptr(ws),
                                    ws.numel() if ws is not None else 0, _stream(dev)))

@@ -24,18 +24,25 @@ namespace sas {
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const uint16_t* dout,
-                                                        float* delta, long nrows) {
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const float* o32,
+                                                        const uint16_t* dout, float* delta,
+                                                        long nrows) {
   constexpr int EPL = D / 16;
   const long gid = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x;
   const long row = gid >> 4;
   const int part = static_cast<int>(gid & 15);
   float acc = 0.f;
   if (row < nrows) {
-    const uint16_t* po = o + row * D + part * EPL;
     const uint16_t* pd = dout + row * D + part * EPL;
+    if (o32) {
+      const float* po = o32 + row * D + part * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc = fmaf(bf2f(po[e]), bf2f(pd[e]), acc);
+      for (int e = 0; e < EPL; ++e) acc = fmaf(po[e], bf2f(pd[e]), acc);
+    } else {
+      const uint16_t* po = o + row * D + part * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc = fmaf(bf2f(po[e]), bf2f(pd[e]), acc);
+    }
   }
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
@@ -146,19 +153,26 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
+// One workgroup = one KV block (b, kappa, j); wave w owns keys 16w..16w+15 and
+// keeps their dK^T, dV^T in registers.  The rows of the queries that selected
+// the block arrive as 32-row tile pairs in ascending token order.  Software
+// pipeline per tile pair `it`: the CSR entry is read 3 pairs ahead, the row
+// metadata (lse, Delta, log g) 2 ahead, the Q / dO rows 1 ahead (registers),
+// so the gathers overlap the MFMA work of the current pair.
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   constexpr int NKS = D / 32, NDT = D / 16;
-  constexpr int RP = D + 8;      // row-major pitch
-  constexpr int TP = 32 + 8;     // transposed pitch (32 rows)
-  constexpr int UNITS = 16 * (D / 8);
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[32 * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * TP];
-  __shared__ float r_lse2[32], r_delta[32], r_lg2[32];
-  __shared__ int r_t[32];
-  __shared__ int r_src[32];     // query row index (b*T+t)*Hq+h, -1 if none
+  constexpr int ROWB = D * 2;          // row-major tile row, 16-byte chunks swizzled
+  constexpr int TP = 36;               // transposed tile pitch (bf16): 32 rows + 4
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int UNITS = 16 * CH;       // (chunk, row pair) units per tile pair
+  constexpr int UPT = (UNITS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t Qs[2][32 * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t dOs[2][32 * ROWB];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TP];
+  __shared__ __attribute__((aligned(16))) uint16_t dOt[2][D * TP];
+  __shared__ float m_lse2[3][32], m_delta[3][32], m_lg2[3][32];
+  __shared__ int m_t[3][32], m_src[3][32];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -188,67 +202,118 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const int e0 = p.rowptr[bk * (p.NB + 1) + j];
-  const int e1 = p.rowptr[bk * (p.NB + 1) + j + 1];
-  const int n = e1 - e0;
+  const int n = p.rowptr[bk * (p.NB + 1) + j + 1] - e0;
   const int32_t* ent = p.entries + bk * static_cast<size_t>(p.T) * p.S + e0;
+  const int nit = (n + 2 * TPT - 1) / (2 * TPT);
   const float sl2 = p.scale_log2;
 
-  for (int g0 = 0; g0 < n; g0 += 2 * TPT) {
-    if (tid < 32) {
-      const int r = tid, tt = r >> 4, rr = r & 15;
-      const int ti = g0 + tt * TPT + rr / G;
-      int src = -1, t = -1;
-      float l2 = 0.f, dl = 0.f, lg = 0.f;
-      if (rr < RT && ti < n) {
-        const int en = ent[ti];
-        const int tk = en >> 6, s = en & 63;
-        if (tk >= j * 64 && tk < p.T && s < p.S) {
-          const int h = kv * G + (rr - (rr / G) * G);
-          const size_t qrow = (static_cast<size_t>(b) * p.T + tk) * p.Hq + h;
-          const float ls = p.lse[qrow];
-          if (ls > -INFINITY) {
-            t = tk;
-            src = static_cast<int>(qrow);
-            l2 = ls * kLog2e;
-            dl = p.delta[qrow];
-            lg = p.logg[((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + s] * kLog2e;
-          }
-        }
-      }
-      r_t[r] = t;
-      r_src[r] = src;
-      r_lse2[r] = l2;
-      r_delta[r] = dl;
-      r_lg2[r] = lg;
+  // ---- per-row metadata (threads 0..31, one row each)
+  const int mr = tid & 31, mtt = mr >> 4, mrr = mr & 15;
+  const int mhh = mrr - (mrr / G) * G;
+  auto load_ent = [&](int it) -> int {
+    const int ti = it * 2 * TPT + mtt * TPT + mrr / G;
+    if (mrr >= RT || ti >= n) return -1;
+    const int en = ent[ti];
+    const int tk = en >> 6, s = en & 63;
+    return (tk >= j * 64 && tk < p.T && s < p.S) ? en : -1;
+  };
+  float r_lse = -INFINITY, r_del = 0.f, r_lg = 0.f;
+  int r_t = -1, r_src = -1;
+  auto meta_issue = [&](int en) {
+    r_t = -1; r_src = -1;
+    if (en >= 0) {
+      const int tk = en >> 6, s = en & 63;
+      const size_t qrow = (static_cast<size_t>(b) * p.T + tk) * p.Hq + kv * G + mhh;
+      r_lse = p.lse[qrow];
+      r_del = p.delta[qrow];
+      r_lg = p.logg[((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + s];
+      r_t = tk;
+      r_src = static_cast<int>(qrow);
     }
-    __syncthreads();
-    // stage Q, dO rows (row-major and transposed)
-    for (int u = tid; u < UNITS; u += 256) {
-      const int rp = u / (D / 8), ch = u - rp * (D / 8);
-      const int s0 = r_src[2 * rp], s1 = r_src[2 * rp + 1];
+  };
+  auto meta_store = [&](int slot) {
+    const bool ok = r_t >= 0 && r_lse > -INFINITY;
+    m_t[slot][mr] = ok ? r_t : -1;
+    m_src[slot][mr] = ok ? r_src : -1;
+    m_lse2[slot][mr] = ok ? r_lse * kLog2e : 0.f;
+    m_delta[slot][mr] = ok ? r_del : 0.f;
+    m_lg2[slot][mr] = ok ? r_lg * kLog2e : 0.f;
+  };
+
+  // ---- Q / dO rows (all threads): unit = (chunk ch, row pair rp)
+  uint4 rq[UPT][2], rd[UPT][2];
+  auto rows_issue = [&](int slot) {
+#pragma unroll
+    for (int x = 0; x < UPT; ++x) {
+      const int u = tid + 256 * x;
+      const int ch = u >> 4, rp = u & 15;
       const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 q0 = (s0 >= 0) ? *reinterpret_cast<const uint4*>(p.q + static_cast<size_t>(s0) * D + ch * 8) : z;
-      const uint4 q1 = (s1 >= 0) ? *reinterpret_cast<const uint4*>(p.q + static_cast<size_t>(s1) * D + ch * 8) : z;
-      const uint4 d0 = (s0 >= 0) ? *reinterpret_cast<const uint4*>(p.dout + static_cast<size_t>(s0) * D + ch * 8) : z;
-      const uint4 d1 = (s1 >= 0) ? *reinterpret_cast<const uint4*>(p.dout + static_cast<size_t>(s1) * D + ch * 8) : z;
-      *reinterpret_cast<uint4*>(&Qs[(2 * rp) * RP + ch * 8]) = q0;
-      *reinterpret_cast<uint4*>(&Qs[(2 * rp + 1) * RP + ch * 8]) = q1;
-      *reinterpret_cast<uint4*>(&dOs[(2 * rp) * RP + ch * 8]) = d0;
-      *reinterpret_cast<uint4*>(&dOs[(2 * rp + 1) * RP + ch * 8]) = d1;
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&q0);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&q1);
-      const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&d0);
-      const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&d1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int src = (u < UNITS) ? m_src[slot][2 * rp + h] : -1;
+        rq[x][h] = (src >= 0) ? *reinterpret_cast<const uint4*>(p.q + static_cast<size_t>(src) * D + ch * 8) : z;
+        rd[x][h] = (src >= 0) ? *reinterpret_cast<const uint4*>(p.dout + static_cast<size_t>(src) * D + ch * 8) : z;
+      }
+    }
+  };
+  auto rows_store = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < UPT; ++x) {
+      const int u = tid + 256 * x;
+      if (u >= UNITS) continue;
+      const int ch = u >> 4, rp = u & 15;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 2 * rp + h;
+        const int off = row * ROWB + ((ch ^ lds_swz<ROWB>(row)) << 4);
+        *reinterpret_cast<uint4*>(&Qs[buf][off]) = rq[x][h];
+        *reinterpret_cast<uint4*>(&dOs[buf][off]) = rd[x][h];
+      }
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&rq[x][0]);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&rq[x][1]);
+      const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&rd[x][0]);
+      const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&rd[x][1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = ch * 8 + 2 * i;
-        *reinterpret_cast<uint32_t*>(&Qt[d * TP + 2 * rp]) = (a0[i] & 0xffffu) | (a1[i] << 16);
-        *reinterpret_cast<uint32_t*>(&Qt[(d + 1) * TP + 2 * rp]) = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&dOt[d * TP + 2 * rp]) = (c0[i] & 0xffffu) | (c1[i] << 16);
-        *reinterpret_cast<uint32_t*>(&dOt[(d + 1) * TP + 2 * rp]) = (c0[i] >> 16) | (c1[i] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&Qt[buf][d * TP + 2 * rp]) = (a0[i] & 0xffffu) | (a1[i] << 16);
+        *reinterpret_cast<uint32_t*>(&Qt[buf][(d + 1) * TP + 2 * rp]) = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&dOt[buf][d * TP + 2 * rp]) = (c0[i] & 0xffffu) | (c1[i] << 16);
+        *reinterpret_cast<uint32_t*>(&dOt[buf][(d + 1) * TP + 2 * rp]) = (c0[i] >> 16) | (c1[i] & 0xffff0000u);
       }
     }
-    __syncthreads();
+  };
+
+  // ---- prologue: metadata of pairs 0, 1; rows of pair 0; entry of pair 2
+  int en_n2 = -1, en_n3 = -1;
+  if (tid < 32) {
+    const int en0 = load_ent(0);
+    const int en1 = (nit > 1) ? load_ent(1) : -1;
+    meta_issue(en0);
+    meta_store(0);
+    meta_issue(en1);
+    meta_store(1);
+    en_n2 = (nit > 2) ? load_ent(2) : -1;
+  }
+  __syncthreads();
+  if (nit > 0) {
+    rows_issue(0);
+    rows_store(0);
+  }
+  wait_vmem_all();
+  __syncthreads();
+
+  int qofs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qofs[ks] = l16 * ROWB + (((ks * 4 + g4) ^ lds_swz<ROWB>(l16)) << 4);
+
+  for (int it = 0; it < nit; ++it) {
+    const int buf = it & 1, ms = it % 3;
+    if (tid < 32) {
+      if (it + 2 < nit) meta_issue(en_n2);
+      en_n3 = (it + 3 < nit) ? load_ent(it + 3) : -1;
+    }
+    if (it + 1 < nit) rows_issue((it + 1) % 3);
 
     // S, dP for the two row tiles: [rows x 16 keys of this wave]
     floatx4 sacc[2], pacc[2];
@@ -258,8 +323,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       pacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(&Qs[(tt * 16 + l16) * RP + ks * 32 + g4 * 8]);
-        const uint4 da = *reinterpret_cast<const uint4*>(&dOs[(tt * 16 + l16) * RP + ks * 32 + g4 * 8]);
+        const uint4 qa = *reinterpret_cast<const uint4*>(&Qs[buf][tt * 16 * ROWB + qofs[ks]]);
+        const uint4 da = *reinterpret_cast<const uint4*>(&dOs[buf][tt * 16 * ROWB + qofs[ks]]);
         sacc[tt] = mfma16x16x32(qa, kb[ks], sacc[tt]);
         pacc[tt] = mfma16x16x32(da, vb[ks], pacc[tt]);
       }
@@ -270,33 +335,43 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = tt * 16 + g4 * 4 + i;
-        const int t = r_t[r];
+        const int t = m_t[ms][r];
         float pp = 0.f;
-        if (t >= 0 && key <= t) pp = exp2f(sacc[tt][i] * sl2 + r_lg2[r] - r_lse2[r]);
+        if (t >= 0 && key <= t) pp = fast_exp2(sacc[tt][i] * sl2 + m_lg2[ms][r] - m_lse2[ms][r]);
         pv[tt][i] = pp;
-        ds[tt][i] = pp * (pacc[tt][i] - r_delta[r]);
+        ds[tt][i] = pp * (pacc[tt][i] - m_delta[ms][r]);
       }
-    uint4 pb, db;
-    pb.x = pack_bf2(pv[0][0], pv[0][1]);
-    pb.y = pack_bf2(pv[0][2], pv[0][3]);
-    pb.z = pack_bf2(pv[1][0], pv[1][1]);
-    pb.w = pack_bf2(pv[1][2], pv[1][3]);
-    db.x = pack_bf2(ds[0][0], ds[0][1]);
-    db.y = pack_bf2(ds[0][2], ds[0][3]);
-    db.z = pack_bf2(ds[1][0], ds[1][1]);
-    db.w = pack_bf2(ds[1][2], ds[1][3]);
+    // P and dS enter the products as bf16 hi + lo parts (exact to ~2^-16)
+    uint4 pb, pl, db, dl;
+    split_bf2(pv[0][0], pv[0][1], pb.x, pl.x);
+    split_bf2(pv[0][2], pv[0][3], pb.y, pl.y);
+    split_bf2(pv[1][0], pv[1][1], pb.z, pl.z);
+    split_bf2(pv[1][2], pv[1][3], pb.w, pl.w);
+    split_bf2(ds[0][0], ds[0][1], db.x, dl.x);
+    split_bf2(ds[0][2], ds[0][3], db.y, dl.y);
+    split_bf2(ds[1][0], ds[1][1], db.z, dl.z);
+    split_bf2(ds[1][2], ds[1][3], db.w, dl.w);
     // dV^T[d, key] += dO^T[d, rows] P[rows, key];  dK^T += Q^T dS
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t* dr = &dOt[(dt * 16 + l16) * TP + g4 * 4];
-      const uint16_t* qr = &Qt[(dt * 16 + l16) * TP + g4 * 4];
+      const uint16_t* dr = &dOt[buf][(dt * 16 + l16) * TP + g4 * 4];
+      const uint16_t* qr = &Qt[buf][(dt * 16 + l16) * TP + g4 * 4];
       const uint2 dlo = *reinterpret_cast<const uint2*>(dr);
       const uint2 dhi = *reinterpret_cast<const uint2*>(dr + 16);
       const uint2 qlo = *reinterpret_cast<const uint2*>(qr);
       const uint2 qhi = *reinterpret_cast<const uint2*>(qr + 16);
-      dv[dt] = mfma16x16x32(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y), pb, dv[dt]);
-      dk[dt] = mfma16x16x32(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), db, dk[dt]);
+      const uint4 dta = make_uint4(dlo.x, dlo.y, dhi.x, dhi.y);
+      const uint4 qta = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
+      dv[dt] = mfma16x16x32(dta, pb, dv[dt]);
+      dv[dt] = mfma16x16x32(dta, pl, dv[dt]);
+      dk[dt] = mfma16x16x32(qta, db, dk[dt]);
+      dk[dt] = mfma16x16x32(qta, dl, dk[dt]);
     }
+    if (tid < 32 && it + 2 < nit) {
+      meta_store((it + 2) % 3);
+      en_n2 = en_n3;
+    }
+    if (it + 1 < nit) rows_store(buf ^ 1);
     __syncthreads();
   }
   if (keyok) {
@@ -318,15 +393,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 template <int D, int TW>
 __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
   constexpr int NW = 8;
-  constexpr int KP = D + 8;
-  constexpr int VP = 64 + 8;
+  constexpr int KROWB = D * 2;              // bytes per K / V row
+  constexpr int KB = 64 * KROWB;            // one tile (K, V or K^T) in bytes
+  constexpr int STAGE = 3 * KB;             // K | V | K^T
+  constexpr int TU = KB / 16;               // 16-byte units per tile
+  constexpr int UPT = 3 * TU / 512;         // units per thread per block
+  constexpr int KCPR = KROWB / 16;
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  constexpr int PU = 32 * (D / 8);   // (row pair, 8-d chunk) units per block
+  static_assert(3 * TU % 512 == 0, "unit split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * VP];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2][STAGE];
   __shared__ uint32_t bits[64][kMaxNBW];
   __shared__ uint8_t pcnt[64][kMaxNBW];
   __shared__ uint32_t ubits[kMaxNBW];
@@ -352,6 +429,7 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
   const int ntok = min(64, a.T - t0);
   const int NBW = (a.NB + 31) >> 5;
   const int S = a.S;
+  const int Tp = a.NB * 64;
 
   for (int i = tid; i < 64 * kMaxNBW; i += 512) (&bits[0][0])[i] = 0u;
   if (tid < kMaxNBW) ubits[tid] = 0u;
@@ -406,8 +484,6 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
     }
     if (lane == 0) s_nU = base;
   }
-  __syncthreads();
-  const int nU = s_nU;
 
   const int G = a.G, TPT = a.TPT;
   int tl_row[TW];
@@ -438,46 +514,57 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dqa[ti][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  wait_vmem_all();
+  __syncthreads();
+  const int nU = s_nU;
 
-  constexpr int PUT = (PU + 511) / 512;
-  uint4 kreg[PUT][2], vreg[PUT][2];
+  // ---- block staging: K and V rows (16-byte-chunk swizzle) and K^T rows
+  // (from the transposed copy; 8-byte-unit swizzle, halves swapped on odd rows)
+  const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
+  const uint16_t* vbase = a.v + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
+  const uint16_t* ktbase =
+      a.kt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
+  uint4 stg[UPT];
+  int soff[UPT];
+  bool sswap[UPT];
+#pragma unroll
+  for (int x = 0; x < UPT; ++x) {
+    const int u = tid + 512 * x;
+    const int tile = u / TU, w = u - tile * TU;
+    if (tile < 2) {
+      const int r = w / KCPR, ch = w - r * KCPR;
+      soff[x] = tile * KB + r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
+      sswap[x] = false;
+    } else {
+      const int d = w >> 3, kc = w & 7;
+      soff[x] = 2 * KB + d * 128 + ((kc ^ ((d >> 1) & 7)) << 4);
+      sswap[x] = (d & 1) != 0;
+    }
+  }
   auto gload = [&](int j) {
 #pragma unroll
-    for (int x = 0; x < PUT; ++x) {
+    for (int x = 0; x < UPT; ++x) {
       const int u = tid + 512 * x;
-      const int pr = u / (D / 8), ch = u - pr * (D / 8);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int tok = j * 64 + 2 * pr + r;
-        const bool ok = (u < PU) && (tok < a.T);
-        const size_t off = ((static_cast<size_t>(b) * a.T + (ok ? tok : 0)) * a.Hkv + kv) * D + ch * 8;
-        kreg[x][r] = ok ? *reinterpret_cast<const uint4*>(a.k + off) : make_uint4(0, 0, 0, 0);
-        vreg[x][r] = ok ? *reinterpret_cast<const uint4*>(a.v + off) : make_uint4(0, 0, 0, 0);
+      const int tile = u / TU, w = u - tile * TU;
+      if (tile < 2) {
+        const int r = w / KCPR, ch = w - r * KCPR;
+        const int tok = min(j * 64 + r, a.T - 1);
+        const uint16_t* base = tile == 0 ? kbase : vbase;
+        stg[x] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(tok) * a.Hkv * D + ch * 8);
+      } else {
+        const int d = w >> 3, kc = w & 7;
+        stg[x] = *reinterpret_cast<const uint4*>(ktbase + static_cast<size_t>(d) * Tp + j * 64 + kc * 8);
       }
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int x = 0; x < PUT; ++x) {
-      const int u = tid + 512 * x;
-      if (u >= PU) continue;
-      const int pr = u / (D / 8), ch = u - pr * (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[buf][(2 * pr) * KP + ch * 8]) = kreg[x][0];
-      *reinterpret_cast<uint4*>(&Ks[buf][(2 * pr + 1) * KP + ch * 8]) = kreg[x][1];
-      *reinterpret_cast<uint4*>(&Vs[buf][(2 * pr) * KP + ch * 8]) = vreg[x][0];
-      *reinterpret_cast<uint4*>(&Vs[buf][(2 * pr + 1) * KP + ch * 8]) = vreg[x][1];
-      const uint32_t* k0 = reinterpret_cast<const uint32_t*>(&kreg[x][0]);
-      const uint32_t* k1 = reinterpret_cast<const uint32_t*>(&kreg[x][1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint32_t*>(&Kt[buf][(ch * 8 + 2 * i) * VP + 2 * pr]) =
-            (k0[i] & 0xffffu) | (k1[i] << 16);
-        *reinterpret_cast<uint32_t*>(&Kt[buf][(ch * 8 + 2 * i + 1) * VP + 2 * pr]) =
-            (k0[i] >> 16) | (k1[i] & 0xffff0000u);
-      }
+    for (int x = 0; x < UPT; ++x) {
+      const uint4 v = stg[x];
+      *reinterpret_cast<uint4*>(&ring[buf][soff[x]]) =
+          sswap[x] ? make_uint4(v.z, v.w, v.x, v.y) : v;
     }
   };
-
   if (nU > 0) {
     gload(ulist[0]);
     lstore(0);
@@ -485,92 +572,101 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
   }
   __syncthreads();
 
+  int kofs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    kofs[ks] = l16 * KROWB + (((ks * 4 + g4) ^ lds_swz<KROWB>(l16)) << 4);
+  int tofs[2][2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    tofs[k2][0] = 2 * KB + l16 * 128 + (((k2 * 8 + g4) ^ l16) << 3);
+    tofs[k2][1] = 2 * KB + l16 * 128 + (((k2 * 8 + 4 + g4) ^ l16) << 3);
+  }
+
   const float sl2 = a.scale_log2;
   for (int u = 0; u < nU; ++u) {
     const int buf = u & 1;
+    const uint8_t* st = ring[buf];
     const int j = ulist[u];
     const uint32_t jbit = 1u << (j & 31);
     const int jw = j >> 5;
+    const bool cur = (j == c);
     bool sel[TW], act[TW];
-    bool any = false;
 #pragma unroll
     for (int ti = 0; ti < TW; ++ti) {
       sel[ti] = valid[ti] && (bits[tl_row[ti]][jw] & jbit);
       act[ti] = ballot64(sel[ti]) != 0;
-      any |= act[ti];
     }
-    if (any) {
 #pragma unroll
-      for (int ti = 0; ti < TW; ++ti) {
-        if (!act[ti]) continue;
-        floatx4 sacc[4], pacc[4];
+    for (int ti = 0; ti < TW; ++ti) {
+      if (!act[ti]) continue;
+      // S^T = K Q^T and dP^T = V dO^T  [16 keys x 16 rows per mt]
+      floatx4 sacc[4], pacc[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-          pacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < 4; ++mt) {
+        sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        pacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            const uint4 ka = *reinterpret_cast<const uint4*>(
-                &Ks[buf][(mt * 16 + l16) * KP + ks * 32 + g4 * 8]);
-            const uint4 va = *reinterpret_cast<const uint4*>(
-                &Vs[buf][(mt * 16 + l16) * KP + ks * 32 + g4 * 8]);
-            sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
-            pacc[mt] = mfma16x16x32(va, da[ti][ks], pacc[mt]);
-          }
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(st + mt * 16 * KROWB + kofs[ks]);
+          const uint4 va = *reinterpret_cast<const uint4*>(st + KB + mt * 16 * KROWB + kofs[ks]);
+          sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
+          pacc[mt] = mfma16x16x32(va, da[ti][ks], pacc[mt]);
         }
-        const int tl = tl_row[ti];
-        float lgv = 0.f;
-        if (sel[ti]) {
-          const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
-          lgv = lgs[tl][rank];
-        }
-        const int tpos = t0 + tl;
-        float dsv[4][4];
-        float rs = 0.f;
+      }
+      const int tl = tl_row[ti];
+      float lgv = 0.f;
+      if (sel[ti]) {
+        const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
+        lgv = lgs[tl][rank];
+      }
+      const float bias = lgv - lse2[ti];
+      const int lim = cur ? (t0 + tl - j * 64 - g4 * 4) : 64;   // causal limit (key offset)
+      float dsv[4][4];
+      float rs = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = j * 64 + mt * 16 + g4 * 4 + i;
-            float pp = 0.f;
-            if (sel[ti] && key <= tpos) pp = exp2f(sacc[mt][i] * sl2 + lgv - lse2[ti]);
-            const float dsx = pp * (pacc[mt][i] - dlt[ti]);
-            dsv[mt][i] = dsx;
-            rs += dsx;
-          }
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
-        // dlogg: sum the G rows of each token of this tile
-        if (g4 == 0) red[wv][l16] = rs;
-        __builtin_amdgcn_wave_barrier();
-        if (g4 == 0 && l16 < TPT) {
-          const int tlr = (wv + NW * ti) * TPT + l16;
-          if (tlr < ntok && (bits[tlr][jw] & jbit)) {
-            float tot = 0.f;
-            for (int h = 0; h < G; ++h) tot += red[wv][l16 * G + h];
-            const int rank = pcnt[tlr][jw] + __popc(bits[tlr][jw] & (jbit - 1u));
-            a.dlogg[(rowbase + static_cast<size_t>(tlr) * a.Hkv) * S + slot_of[tlr][rank]] = tot;
-          }
+        for (int i = 0; i < 4; ++i) {
+          const bool on = sel[ti] && (mt * 16 + i <= lim);
+          const float pp = on ? fast_exp2(sacc[mt][i] * sl2 + bias) : 0.f;
+          const float dsx = pp * (pacc[mt][i] - dlt[ti]);
+          dsv[mt][i] = dsx;
+          rs += dsx;
         }
-        __builtin_amdgcn_wave_barrier();
-        uint4 dsb[2];
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      // dlogg: sum the G rows of each token of this tile
+      if (g4 == 0) red[wv][l16] = rs;
+      __builtin_amdgcn_wave_barrier();
+      if (g4 == 0 && l16 < TPT) {
+        const int tlr = (wv + NW * ti) * TPT + l16;
+        if (tlr < ntok && (bits[tlr][jw] & jbit)) {
+          float tot = 0.f;
+          for (int h = 0; h < G; ++h) tot += red[wv][l16 * G + h];
+          const int rank = pcnt[tlr][jw] + __popc(bits[tlr][jw] & (jbit - 1u));
+          a.dlogg[(rowbase + static_cast<size_t>(tlr) * a.Hkv) * S + slot_of[tlr][rank]] = tot;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint4 dsb[2], dsl[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        split_bf2(dsv[2 * k2][0], dsv[2 * k2][1], dsb[k2].x, dsl[k2].x);
+        split_bf2(dsv[2 * k2][2], dsv[2 * k2][3], dsb[k2].y, dsl[k2].y);
+        split_bf2(dsv[2 * k2 + 1][0], dsv[2 * k2 + 1][1], dsb[k2].z, dsl[k2].z);
+        split_bf2(dsv[2 * k2 + 1][2], dsv[2 * k2 + 1][3], dsb[k2].w, dsl[k2].w);
+      }
+      // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row]
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          dsb[k2].x = pack_bf2(dsv[2 * k2][0], dsv[2 * k2][1]);
-          dsb[k2].y = pack_bf2(dsv[2 * k2][2], dsv[2 * k2][3]);
-          dsb[k2].z = pack_bf2(dsv[2 * k2 + 1][0], dsv[2 * k2 + 1][1]);
-          dsb[k2].w = pack_bf2(dsv[2 * k2 + 1][2], dsv[2 * k2 + 1][3]);
-        }
-        // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row]
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const uint16_t* kr = &Kt[buf][(dt * 16 + l16) * VP + k2 * 32 + g4 * 4];
-            const uint2 lo = *reinterpret_cast<const uint2*>(kr);
-            const uint2 hi = *reinterpret_cast<const uint2*>(kr + 16);
-            dqa[ti][dt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), dsb[k2], dqa[ti][dt]);
-          }
+          const uint2 lo = *reinterpret_cast<const uint2*>(st + dt * 2048 + tofs[k2][0]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(st + dt * 2048 + tofs[k2][1]);
+          const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          dqa[ti][dt] = mfma16x16x32(kta, dsb[k2], dqa[ti][dt]);
+          dqa[ti][dt] = mfma16x16x32(kta, dsl[k2], dqa[ti][dt]);
         }
       }
     }
@@ -600,7 +696,7 @@ template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   const long nrows = static_cast<long>(p.B) * p.T * p.Hq;
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((nrows * 16 + 255) / 256), dim3(256), 0, st,
-                     p.o, p.dout, p.delta, nrows);
+                     p.o, p.o32, p.dout, p.delta, nrows);
   const int NQB = p.NB;
   const unsigned nblk = static_cast<unsigned>(p.B) * p.Hkv * NQB;
   hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);
@@ -609,6 +705,8 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
                      dim3(256), 0, st, p);
+  hipError_t e = launch_transpose_tokens(p.k, p.kt, p.B, p.T, p.Hkv, D, st);
+  if (e != hipSuccess) return e;
   const int tw = (p.ntiles + 7) / 8;
   switch (tw) {
     case 1: hipLaunchKernelGGL((dq_kernel<D, 1>), dim3(nblk), dim3(512), 0, st, p); break;

@@ -7,32 +7,38 @@
 // Schedule (query-block stationary):
 //   one workgroup = (batch b, KV head kappa, query block c) = 64 tokens x G heads.
 //   The workgroup walks the union of the blocks its 64 tokens selected, in
-//   ascending order.  Each block's K (row-major) and V (transposed) is staged
-//   once into double-buffered LDS and shared by all 8 waves.  A wave owns TW
-//   row tiles of 16 rows = floor(16/G) tokens x G heads; a tile in which no
-//   token selected the block skips it, otherwise S^T = K Q^T and O^T += V^T P^T
-//   run on bf16 MFMA 16x16x32 with rows outside the selection masked to -inf.
-//   Online softmax state stays in registers (one query row per lane column).
+//   ascending order.  Each block's K tile and V^T tile (from a transposed copy
+//   of V made once per call) is staged once into double-buffered LDS (plain
+//   16-byte copies, chunks XOR-swizzled per row so the MFMA operand reads are
+//   conflict-free); the next block's loads are in flight in registers while
+//   the current one is computed, with one workgroup barrier per block.  A wave owns TW row tiles of 16 rows =
+//   floor(16/G) tokens x G heads; a tile in which no token selected the block
+//   skips it, otherwise S^T = K Q^T and O^T += V^T P^T run on bf16 MFMA
+//   16x16x32 with rows outside the selection masked to -inf.  Online-softmax
+//   state stays in registers (one query row per lane column).
 #include "sas_kernels.h"
 
 namespace sas {
 
 namespace {
 
-template <int D, int TW>
+// HILO: P enters the PV product as bf16 hi + lo parts (exact to ~2^-16);
+// used when the fp32 output is requested for the backward's Delta.
+template <int D, int TW, bool HILO>
 __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
   constexpr int NW = 8;
-  constexpr int KP = D + 8;       // K row pitch (bf16 elements)
-  constexpr int VP = 64 + 8;      // V^T row pitch (bf16 elements)
-  constexpr int NKS = D / 32;     // MFMA k-steps over the head dim
-  constexpr int NDT = D / 16;     // 16-wide d tiles of O
-  constexpr int KUN = 64 * (D / 8);        // 16-byte K units per block
-  constexpr int VUN = 32 * (D / 8);        // (key pair, 8-d chunk) V units per block
-  constexpr int KU = (KUN + 511) / 512;    // per thread
-  constexpr int VU = (VUN + 511) / 512;
+  constexpr int KROWB = D * 2;              // bytes per K row
+  constexpr int KB = 64 * KROWB;            // K tile bytes
+  constexpr int VB = D * 128;               // V^T tile bytes (D rows x 64 keys)
+  constexpr int STAGE = KB + VB;
+  constexpr int KU = KB / 16;               // 16-byte K units per tile
+  constexpr int UPT = STAGE / 16 / 512;     // 16-byte units per thread per block
+  constexpr int KCPR = KROWB / 16;          // 16-byte chunks per K row
+  constexpr int NKS = D / 32;
+  constexpr int NDT = D / 16;
+  static_assert(STAGE % (16 * 512) == 0, "unit split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2][STAGE];
   __shared__ uint32_t bits[64][kMaxNBW];
   __shared__ uint8_t pcnt[64][kMaxNBW];
   __shared__ uint32_t ubits[kMaxNBW];
@@ -56,6 +62,7 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
   const int ntok = min(64, a.T - t0);
   const int NBW = (a.NB + 31) >> 5;
   const int S = a.S;
+  const int Tp = a.NB * 64;
 
   // ---- selection bitmaps of the 64 tokens, their union, log-gates by rank
   for (int i = tid; i < 64 * kMaxNBW; i += 512) (&bits[0][0])[i] = 0u;
@@ -106,8 +113,6 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
     }
     if (lane == 0) s_nU = base;
   }
-  __syncthreads();
-  const int nU = s_nU;
 
   // ---- per-tile query rows: row r = l16 -> token r/G, head r%G
   const int G = a.G, TPT = a.TPT;
@@ -134,59 +139,59 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
     m_run[ti] = -INFINITY;
     l_run[ti] = 0.f;
   }
+  wait_vmem_all();
+  __syncthreads();
+  const int nU = s_nU;
 
-  // ---- K/V staging: registers -> LDS (V transposed on the way)
-  uint4 kreg[KU];
-  uint4 vreg[VU][2];
+  // ---- block staging: global -> registers (next block) -> LDS (swizzled)
+  const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
+  const uint16_t* vtbase =
+      a.vt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
+  uint4 stg[UPT];
   auto gload = [&](int j) {
-    const int kbase = j * 64;
 #pragma unroll
-    for (int x = 0; x < KU; ++x) {
+    for (int x = 0; x < UPT; ++x) {
       const int u = tid + 512 * x;
-      const int row = u / (D / 8), ch = u - row * (D / 8);
-      const int tok = kbase + row;
-      kreg[x] = (u < KUN && tok < a.T) ? *reinterpret_cast<const uint4*>(
-                                  a.k + ((static_cast<size_t>(b) * a.T + tok) * a.Hkv + kv) * D + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int x = 0; x < VU; ++x) {
-      const int u = tid + 512 * x;
-      const int p = u / (D / 8), ch = u - p * (D / 8);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int tok = kbase + 2 * p + r;
-        vreg[x][r] = (u < VUN && tok < a.T) ? *reinterpret_cast<const uint4*>(
-                                       a.v + ((static_cast<size_t>(b) * a.T + tok) * a.Hkv + kv) * D + ch * 8)
-                                 : make_uint4(0, 0, 0, 0);
+      if (u < KU) {
+        const int r = u / KCPR, ch = u - r * KCPR;
+        const int tok = min(j * 64 + r, a.T - 1);
+        stg[x] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(tok) * a.Hkv * D + ch * 8);
+      } else {
+        const int v = u - KU;
+        const int d = v >> 3, kc = v & 7;
+        stg[x] = *reinterpret_cast<const uint4*>(vtbase + static_cast<size_t>(d) * Tp + j * 64 + kc * 8);
       }
     }
   };
+  // LDS store offsets of this thread's units (loop-invariant).  K rows use a
+  // 16-byte-chunk swizzle; V^T rows (128 B) use an 8-byte-unit swizzle
+  // unit ^ (d & 15), so 16 lanes reading one unit of 16 consecutive rows hit
+  // 16 distinct 8-byte bank pairs; on odd rows this swaps the two halves of
+  // a 16-byte chunk.
+  int soff[UPT];
+  bool sswap[UPT];
+#pragma unroll
+  for (int x = 0; x < UPT; ++x) {
+    const int u = tid + 512 * x;
+    if (u < KU) {
+      const int r = u / KCPR, ch = u - r * KCPR;
+      soff[x] = r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
+      sswap[x] = false;
+    } else {
+      const int v = u - KU;
+      const int d = v >> 3, kc = v & 7;
+      soff[x] = KB + d * 128 + ((kc ^ ((d >> 1) & 7)) << 4);
+      sswap[x] = (d & 1) != 0;
+    }
+  }
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int x = 0; x < KU; ++x) {
-      const int u = tid + 512 * x;
-      if (u >= KUN) continue;
-      const int row = u / (D / 8), ch = u - row * (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[buf][row * KP + ch * 8]) = kreg[x];
-    }
-#pragma unroll
-    for (int x = 0; x < VU; ++x) {
-      const int u = tid + 512 * x;
-      if (u >= VUN) continue;
-      const int p = u / (D / 8), ch = u - p * (D / 8);
-      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[x][0]);
-      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[x][1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (v0[i] & 0xffffu) | (v1[i] << 16);
-        const uint32_t hi = (v0[i] >> 16) | (v1[i] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(ch * 8 + 2 * i) * VP + 2 * p]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(ch * 8 + 2 * i + 1) * VP + 2 * p]) = hi;
-      }
+    for (int x = 0; x < UPT; ++x) {
+      const uint4 v = stg[x];
+      *reinterpret_cast<uint4*>(&ring[buf][soff[x]]) =
+          sswap[x] ? make_uint4(v.z, v.w, v.x, v.y) : v;
     }
   };
-
   if (nU > 0) {
     gload(ulist[0]);
     lstore(0);
@@ -194,92 +199,120 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
   }
   __syncthreads();
 
+  // per-lane LDS read offsets of the MFMA operands (immediate offsets add
+  // the 16-key / 16-d tile steps)
+  int kofs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    kofs[ks] = l16 * KROWB + (((ks * 4 + g4) ^ lds_swz<KROWB>(l16)) << 4);
+  int vofs[2][2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    vofs[k2][0] = KB + l16 * 128 + (((k2 * 8 + g4) ^ l16) << 3);
+    vofs[k2][1] = KB + l16 * 128 + (((k2 * 8 + 4 + g4) ^ l16) << 3);
+  }
+
   const float sl2 = a.scale_log2;
   for (int u = 0; u < nU; ++u) {
     const int buf = u & 1;
+    const uint8_t* st = ring[buf];
     const int j = ulist[u];
     const uint32_t jbit = 1u << (j & 31);
     const int jw = j >> 5;
+    const bool cur = (j == c);
     bool sel[TW];
     bool act[TW];
-    bool any = false;
 #pragma unroll
     for (int ti = 0; ti < TW; ++ti) {
       sel[ti] = valid[ti] && (bits[tl_row[ti]][jw] & jbit);
       act[ti] = ballot64(sel[ti]) != 0;
-      any |= act[ti];
     }
-    if (any) {
 #pragma unroll
-      for (int ti = 0; ti < TW; ++ti) {
-        if (!act[ti]) continue;
-        // S^T[key, row] = K[key,:] . Q[row,:]
-        floatx4 sacc[4];
+    for (int ti = 0; ti < TW; ++ti) {
+      if (!act[ti]) continue;
+      // S^T[key, row] = K[key,:] . Q[row,:]
+      floatx4 sacc[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < 4; ++mt) {
+        sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            const uint4 ka = *reinterpret_cast<const uint4*>(
-                &Ks[buf][(mt * 16 + l16) * KP + ks * 32 + g4 * 8]);
-            sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
-          }
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(st + mt * 16 * KROWB + kofs[ks]);
+          sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
         }
-        const int tl = tl_row[ti];
-        float lgv = -INFINITY;
-        if (sel[ti]) {
-          const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
-          lgv = lgs[tl][rank];
-        }
-        const int tpos = t0 + tl;
-        float x[4][4];
-        float mx = -INFINITY;
+      }
+      const int tl = tl_row[ti];
+      float lgv = -INFINITY;
+      if (sel[ti]) {
+        const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
+        lgv = lgs[tl][rank];
+      }
+      float x[4][4];
+      float mx = -INFINITY;
+      if (cur) {
+        const int lim = t0 + tl - j * 64 - g4 * 4;     // key offset limit for this lane
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = j * 64 + mt * 16 + g4 * 4 + i;
-            float val = sacc[mt][i] * sl2 + lgv;
-            if (key > tpos) val = -INFINITY;
+            const float val = (mt * 16 + i <= lim) ? sacc[mt][i] * sl2 + lgv : -INFINITY;
             x[mt][i] = val;
             mx = fmaxf(mx, val);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[ti], mx);
-        const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run[ti] - msafe);
-        m_run[ti] = m_new;
-        float psum = 0.f;
+      } else {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            x[mt][i] = exp2f(x[mt][i] - msafe);
-            psum += x[mt][i];
+            x[mt][i] = sacc[mt][i] * sl2 + lgv;
+            mx = fmaxf(mx, x[mt][i]);
           }
-        l_run[ti] = l_run[ti] * alpha + psum;
-        uint4 pb[2];
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[ti], mx);
+      const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[ti] - msafe);
+      m_run[ti] = m_new;
+      float psum = 0.f;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[mt][i] = fast_exp2(x[mt][i] - msafe);
+          psum += x[mt][i];
+        }
+      l_run[ti] = l_run[ti] * alpha + psum;
+      if (ballot64(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[ti][dt] *= alpha;
+      }
+      uint4 pb[2], pl[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        if (HILO) {
+          split_bf2(x[2 * k2][0], x[2 * k2][1], pb[k2].x, pl[k2].x);
+          split_bf2(x[2 * k2][2], x[2 * k2][3], pb[k2].y, pl[k2].y);
+          split_bf2(x[2 * k2 + 1][0], x[2 * k2 + 1][1], pb[k2].z, pl[k2].z);
+          split_bf2(x[2 * k2 + 1][2], x[2 * k2 + 1][3], pb[k2].w, pl[k2].w);
+        } else {
           pb[k2].x = pack_bf2(x[2 * k2][0], x[2 * k2][1]);
           pb[k2].y = pack_bf2(x[2 * k2][2], x[2 * k2][3]);
           pb[k2].z = pack_bf2(x[2 * k2 + 1][0], x[2 * k2 + 1][1]);
           pb[k2].w = pack_bf2(x[2 * k2 + 1][2], x[2 * k2 + 1][3]);
         }
-        // O^T[d, row] = alpha O^T + V^T[d, keys] . P^T[keys, row]; inside a
-        // 32-key step the key order follows P's register layout:
-        // {4g..4g+3, 16+4g..16+4g+3}.
+      }
+      // O^T[d, row] += V^T[d, keys] . P^T[keys, row]; inside a 32-key step the
+      // key order follows P's register layout: {4g..4g+3, 16+4g..16+4g+3}.
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          oacc[ti][dt] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const uint16_t* vr = &Vt[buf][(dt * 16 + l16) * VP + k2 * 32 + g4 * 4];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-            oacc[ti][dt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[k2], oacc[ti][dt]);
-          }
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(st + dt * 2048 + vofs[k2][0]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(st + dt * 2048 + vofs[k2][1]);
+          const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          oacc[ti][dt] = mfma16x16x32(va, pb[k2], oacc[ti][dt]);
+          if (HILO) oacc[ti][dt] = mfma16x16x32(va, pl[k2], oacc[ti][dt]);
         }
       }
     }
@@ -305,30 +338,41 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
       pk.x = pack_bf2(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv);
       pk.y = pack_bf2(oacc[ti][dt][2] * inv, oacc[ti][dt][3] * inv);
       *reinterpret_cast<uint2*>(a.o + row * D + dt * 16 + g4 * 4) = pk;
+      if (a.o32)
+        *reinterpret_cast<float4*>(a.o32 + row * D + dt * 16 + g4 * 4) =
+            make_float4(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv, oacc[ti][dt][2] * inv,
+                        oacc[ti][dt][3] * inv);
     }
     if (g4 == 0)
       a.lse[row] = (lsum > 0.f) ? (m_run[ti] + log2f(lsum)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D>
-hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
+template <int D, bool HILO>
+hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
   const int NQB = (p.T + 63) / 64;
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * NQB);
   const int tw = (p.ntiles + 7) / 8;
   switch (tw) {
-    case 1: hipLaunchKernelGGL((sparse_fwd_kernel<D, 1>), grid, dim3(512), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((sparse_fwd_kernel<D, 2>), grid, dim3(512), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((sparse_fwd_kernel<D, 3>), grid, dim3(512), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((sparse_fwd_kernel<D, 4>), grid, dim3(512), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((sparse_fwd_kernel<D, 1, HILO>), grid, dim3(512), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((sparse_fwd_kernel<D, 2, HILO>), grid, dim3(512), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((sparse_fwd_kernel<D, 3, HILO>), grid, dim3(512), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((sparse_fwd_kernel<D, 4, HILO>), grid, dim3(512), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
+  return p.o32 ? launch_fwd_dh<D, true>(p, st) : launch_fwd_dh<D, false>(p, st);
+}
+
 }  // namespace
 
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st) {
+  hipError_t e = launch_transpose_tokens(p.v, p.vt, p.B, p.T, p.Hkv, p.D, st);
+  if (e != hipSuccess) return e;
   if (p.D == 128) return launch_fwd_d<128>(p, st);
   if (p.D == 64) return launch_fwd_d<64>(p, st);
   return hipErrorInvalidValue;

@@ -81,7 +81,12 @@ GateWs gate_ws(const sas_dims* d) {
   return w;
 }
 
-struct BwdWs { size_t delta, cnt2d, rowptr, entries, total; };
+size_t fwd_ws(const sas_dims* d) {
+  const size_t Tp = static_cast<size_t>((d->T + 63) / 64) * 64;
+  return align_up(sizeof(uint16_t) * d->B * d->Hkv * d->D * Tp);
+}
+
+struct BwdWs { size_t delta, cnt2d, rowptr, entries, kt, total; };
 BwdWs bwd_ws(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
   const size_t S = d->topk + 1;
@@ -90,7 +95,8 @@ BwdWs bwd_ws(const sas_dims* d) {
   w.cnt2d = align_up(w.delta + sizeof(float) * static_cast<size_t>(d->B) * d->T * d->Hq);
   w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
   w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
-  w.total = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
+  w.kt = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
+  w.total = align_up(w.kt + sizeof(uint16_t) * static_cast<size_t>(d->B) * d->Hkv * d->D * NB * 64);
   return w;
 }
 
@@ -152,7 +158,7 @@ size_t sas_workspace_size(int op, const sas_dims* d) {
   switch (op) {
     case SAS_OP_GATE_SCORE: return gate_ws(d).total;
     case SAS_OP_TOPK: return 0;
-    case SAS_OP_FWD: return 0;
+    case SAS_OP_FWD: return fwd_ws(d);
     case SAS_OP_BWD: return bwd_ws(d).total;
     default: fail(SAS_ERR_INVALID, "unknown op %d", op); return static_cast<size_t>(-1);
   }
@@ -209,15 +215,17 @@ sas_status sas_topk_blocks(const sas_dims* d, const float* q_gate, const float* 
 
 sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const int32_t* idx, const float* logg,
-                               float scale, uint16_t* o, float* lse, void* ws,
+                               float scale, uint16_t* o, float* lse, float* o_f32, void* ws,
                                size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   sas_status st = check_dims(d);
   if (st) return st;
   REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(idx); REQ_PTR(logg); REQ_PTR(o); REQ_PTR(lse);
+  if (o_f32 && !aligned16(o_f32)) return fail(SAS_ERR_INVALID, "pointer 'o_f32' is not 16-byte aligned");
   if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
+  if ((st = check_ws(ws, ws_bytes, fwd_ws(d)))) return st;
   sas::FwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.idx = idx; p.logg = logg; p.o = o; p.lse = lse;
+  p.vt = static_cast<uint16_t*>(ws);
+  p.q = q; p.k = k; p.v = v; p.idx = idx; p.logg = logg; p.o = o; p.lse = lse; p.o32 = o_f32;
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
   p.TPT = 16 / p.G;
@@ -229,25 +237,29 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
 }
 
 sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
-                               const uint16_t* v, const uint16_t* o, const uint16_t* dout,
-                               const float* lse, const int32_t* idx, const float* logg,
-                               float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                               float* dlogg, void* ws, size_t ws_bytes, void* stream) {
+                               const uint16_t* v, const uint16_t* o, const float* o_f32,
+                               const uint16_t* dout, const float* lse, const int32_t* idx,
+                               const float* logg, float scale, uint16_t* dq, uint16_t* dk,
+                               uint16_t* dv, float* dlogg, void* ws, size_t ws_bytes,
+                               void* stream) {
   sas_status st = check_dims(d);
   if (st) return st;
   REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(o); REQ_PTR(dout); REQ_PTR(lse); REQ_PTR(idx);
   REQ_PTR(logg); REQ_PTR(dq); REQ_PTR(dk); REQ_PTR(dv); REQ_PTR(dlogg);
+  if (o_f32 && !aligned16(o_f32)) return fail(SAS_ERR_INVALID, "pointer 'o_f32' is not 16-byte aligned");
   if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
   const BwdWs w = bwd_ws(d);
   if ((st = check_ws(ws, ws_bytes, w.total))) return st;
   char* base = static_cast<char*>(ws);
   sas::BwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse; p.idx = idx; p.logg = logg;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.o32 = o_f32; p.dout = dout; p.lse = lse; p.idx = idx;
+  p.logg = logg;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dlogg = dlogg;
   p.delta = reinterpret_cast<float*>(base + w.delta);
   p.cnt2d = reinterpret_cast<int32_t*>(base + w.cnt2d);
   p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
   p.entries = reinterpret_cast<int32_t*>(base + w.entries);
+  p.kt = reinterpret_cast<uint16_t*>(base + w.kt);
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
   p.TPT = 16 / p.G;

@@ -28,9 +28,54 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two fp32 -> packed bf16 pair (low = a).
+// Two fp32 -> packed bf16 pair (low = a), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Split two fp32 values into bf16 hi = rne(x) and lo = rne(x - hi) pairs, so
+// that an MFMA fed hi and then lo reproduces x to ~2^-16 relative.
+__device__ __forceinline__ void split_bf2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf2(a, b);
+  lo = pack_bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// s_waitcnt vmcnt(n) for a compile-time n < 16 (expcnt, lgkmcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+
+// Workgroup barrier without the memory fences of __syncthreads(): those
+// fences make the compiler wait for every outstanding LDS-DMA load, which
+// would drain a software pipeline at each step.  Callers wait for exactly the
+// loads they need (wait_vmem) before it; the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// XOR swizzle of the 16-byte chunks of an LDS tile row of ROWB bytes, chosen
+// so that 16 lanes reading the same logical chunk of 16 consecutive rows hit
+// distinct banks (256-byte rows: chunk ^ (r & 15); 128-byte rows, where two
+// rows share the bank space: chunk ^ ((r >> 1) & 7)).
+template <int ROWB>
+__device__ __forceinline__ int lds_swz(int r) {
+  static_assert(ROWB == 256 || ROWB == 128, "row size");
+  return ROWB == 256 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds + 16 * i.  `lds` must be wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds), 16, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -75,5 +120,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// 2^x with the bare hardware instruction (results below 2^-126 flush to 0,
+// which is harmless for softmax weights).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wait until every global load issued so far by this wave has returned.
+// Used once before a software-pipelined loop so that registers loaded before
+// the loop are not treated as possibly pending inside it (which would make
+// the compiler wait for the loop's own prefetches every iteration).
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+}
 
 }  // namespace sas

@@ -43,6 +43,8 @@ struct FwdParams {
   const float* logg;
   uint16_t* o;
   float* lse;
+  float* o32;   // optional fp32 copy of o (null = skip)
+  uint16_t* vt; // workspace: V^T [B,Hkv,D,64*NB]
   int B, T, Hq, Hkv, D, G, S, NB;
   int TPT;      // tokens per 16-row tile = floor(16 / G)
   int ntiles;   // tiles per 64-token query block = ceil(64 / TPT)
@@ -54,6 +56,7 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* o;
+  const float* o32;     // optional fp32 forward output (preferred for Delta)
   const uint16_t* dout;
   const float* lse;
   const int32_t* idx;
@@ -67,6 +70,7 @@ struct BwdParams {
   int32_t* cnt2d;       // [B,Hkv,NQB,NB]  per (query block, key block) counts -> offsets
   int32_t* rowptr;      // [B,Hkv,NB+1]
   int32_t* entries;     // [B,Hkv,T*S] packed (t << 6) | slot
+  uint16_t* kt;         // [B,Hkv,D,64*NB] transposed copy of k
   int B, T, Hq, Hkv, D, G, S, NB;
   int TPT, ntiles;
   float scale, scale_log2;
@@ -95,6 +99,9 @@ hipError_t launch_router(const RouterParams& p, const uint16_t* wq, const uint16
                          hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st);
+// src [B,T,H,D] -> dst [B,H,D,64*ceil(T/64)] (zero tail)
+hipError_t launch_transpose_tokens(const uint16_t* src, uint16_t* dst, int B, int T, int H, int D,
+                                   hipStream_t st);
 hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 

@@ -158,13 +158,16 @@ sas_status sas_topk_blocks(const sas_dims* d, const float* q_gate, const float* 
  *
  *   q [B,T,Hq,D], k, v [B,T,Hkv,D] bf16;  idx, logg as produced by
  *   sas_topk_blocks (entries outside [0, t/64] are ignored; the valid
- *   entries must be distinct); o [B,T,Hq,D] bf16, lse [B,T,Hq] fp32 outputs.
- *   ws: sas_workspace_size(SAS_OP_FWD, d) bytes (may be 0 / NULL).
+ *   entries must be distinct); o [B,T,Hq,D] bf16, lse [B,T,Hq] fp32 outputs;
+ *   o_f32 [B,T,Hq,D] fp32 optional output (NULL = not written): the same
+ *   result before bf16 rounding, for the backward's Delta.
+ *   ws: sas_workspace_size(SAS_OP_FWD, d) bytes (holds a transposed copy of
+ *   v, [B,Hkv,D,64*ceil(T/64)] bf16, rebuilt on every call).
  *   Deterministic (bitwise repeatable).
  */
 sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const int32_t* idx, const float* logg,
-                               float scale, uint16_t* o, float* lse, void* ws,
+                               float scale, uint16_t* o, float* lse, float* o_f32, void* ws,
                                size_t ws_bytes, void* stream);
 
 /*
@@ -178,13 +181,17 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
  *   slot's block of dS  (gradient w.r.t. log g; pads 0).
  *
  *   q, k, v, o, dout bf16 as in the forward; lse from the forward;
+ *   o_f32: the forward's optional fp32 output or NULL.  When given, Delta
+ *   uses it, which removes the bf16 rounding of o from dS (that rounding,
+ *   times |dout| sqrt(D), otherwise dominates the error of dlogg);
  *   dq [B,T,Hq,D], dk, dv [B,T,Hkv,D] bf16 (fully overwritten, fp32
  *   accumulation); dlogg [B,T,Hkv,K+1] fp32.
  *   ws: sas_workspace_size(SAS_OP_BWD, d) bytes.
  *   Deterministic (bitwise repeatable).
  */
 sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
-                               const uint16_t* v, const uint16_t* o, const uint16_t* dout,
+                               const uint16_t* v, const uint16_t* o, const float* o_f32,
+                               const uint16_t* dout,
                                const float* lse, const int32_t* idx, const float* logg,
                                float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                                float* dlogg, void* ws, size_t ws_bytes, void* stream);

@@ -68,7 +68,7 @@ def test_invalid_dims_rejected(bad, code):
     # a call with these dims fails validation before touching any pointer
     st = lib.sas_sparse_attn_fwd(ctypes.byref(d), *([ctypes.c_void_p(16)] * 5),
                                  ctypes.c_float(0.1), ctypes.c_void_p(16), ctypes.c_void_p(16),
-                                 None, 0, None)
+                                 None, None, 0, None)
     assert st == code
     assert lib.sas_last_error()
 
@@ -78,17 +78,18 @@ def test_null_and_misaligned_pointers_rejected():
     d = _dims()
     p = ctypes.c_void_p(4096)
     st = lib.sas_sparse_attn_fwd(ctypes.byref(d), p, p, None, p, p, ctypes.c_float(0.1), p, p,
-                                 None, 0, None)
+                                 None, None, 0, None)
     assert st == sas.SAS_ERR_INVALID
     assert b"'v'" in lib.sas_last_error()
     st = lib.sas_sparse_attn_fwd(ctypes.byref(d), p, p, ctypes.c_void_p(4098), p, p,
-                                 ctypes.c_float(0.1), p, p, None, 0, None)
+                                 ctypes.c_float(0.1), p, p, None, None, 0, None)
     assert st == sas.SAS_ERR_INVALID
     assert b"aligned" in lib.sas_last_error()
-    st = lib.sas_sparse_attn_fwd(None, p, p, p, p, p, ctypes.c_float(0.1), p, p, None, 0, None)
+    st = lib.sas_sparse_attn_fwd(None, p, p, p, p, p, ctypes.c_float(0.1), p, p, None, None, 0,
+                                 None)
     assert st == sas.SAS_ERR_INVALID
     st = lib.sas_sparse_attn_fwd(ctypes.byref(d), p, p, p, p, p, ctypes.c_float(float("nan")), p,
-                                 p, None, 0, None)
+                                 p, None, None, 0, None)
     assert st == sas.SAS_ERR_INVALID
 
 
@@ -97,10 +98,10 @@ def test_workspace_checks():
     d = _dims(T=4096)
     need = sas.workspace_size(sas.OP_BWD, d)
     assert need > 0
-    assert sas.workspace_size(sas.OP_FWD, d) == 0
+    assert sas.workspace_size(sas.OP_FWD, d) == 1 * 2 * 128 * 4096 * 2   # transposed v
     assert sas.workspace_size(sas.OP_TOPK, d) == 0
     p = ctypes.c_void_p(4096)
-    args = [p] * 8 + [ctypes.c_float(0.1)] + [p] * 4
+    args = [p] * 9 + [ctypes.c_float(0.1)] + [p] * 4
     st = lib.sas_sparse_attn_bwd(ctypes.byref(d), *args, None, need, None)
     assert st == sas.SAS_ERR_WORKSPACE
     st = lib.sas_sparse_attn_bwd(ctypes.byref(d), *args, p, need - 1, None)

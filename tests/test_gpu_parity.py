@@ -167,9 +167,10 @@ def test_sparse_attn_bwd(w):
     P = prepared(w)
     d = P["dev"]
     idx, logg = _oracle_sel(P)
-    o, lse = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"])
+    o, lse, o32 = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"], want_f32=True)
+    assert_close("o_f32", o32, P["g"]["o"])
     dq, dk, dv, dlogg = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg,
-                                            P["scale"])
+                                            P["scale"], o_f32=o32)
     torch.cuda.synchronize()
     g = P["g"]
     assert_close("dq", dq, g["dq"])
@@ -178,7 +179,8 @@ def test_sparse_attn_bwd(w):
     assert_close("dlogg", dlogg, g["dlogg"])
     # gradient w.r.t. log g sums to zero over each row's selected slots
     assert float(dlogg.sum(-1).abs().max()) < 1e-3
-    out2 = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg, P["scale"])
+    out2 = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg, P["scale"],
+                               o_f32=o32)
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv, dlogg), out2):
         assert torch.equal(a, b), "backward not bitwise repeatable"
