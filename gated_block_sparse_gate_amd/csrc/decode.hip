@@ -120,17 +120,16 @@ __global__ __launch_bounds__(512) void decode_select_kernel(DecodeParams p) {
       int cnt = 0;
       for (int e = 0; e < E; ++e) {
         const int j = lane + 64 * e;
-        if (j < c && order_key(sc[j]) >= cand) ++cnt;
+        cnt += wave_count(j < c && order_key(sc[j]) >= cand);
       }
-      cnt = wave_sum_i(cnt);
       if (cnt >= K) thr = cand;
     }
     int gt = 0;
     for (int e = 0; e < E; ++e) {
       const int j = lane + 64 * e;
-      if (j < c && order_key(sc[j]) > thr) ++gt;
+      gt += wave_count(j < c && order_key(sc[j]) > thr);
     }
-    need_eq = K - wave_sum_i(gt);
+    need_eq = K - gt;
   }
   int32_t* oid = p.idx_out ? p.idx_out + static_cast<size_t>(unit) * S : nullptr;
   float* olg = p.logg_out ? p.logg_out + static_cast<size_t>(unit) * S : nullptr;

@@ -121,6 +121,10 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
+// Number of lanes of the wave for which p holds (ballot + scalar popcount:
+// no cross-lane data movement, so no LDS round trip).
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
+
 // 2^x with the bare hardware instruction (results below 2^-126 flush to 0,
 // which is harmless for softmax weights).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

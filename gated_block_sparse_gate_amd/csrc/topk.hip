@@ -121,38 +121,42 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
     const size_t rowid = (static_cast<size_t>(b) * p.T + t0 + tl) * p.Hkv + kv;
 
     const int nsel = min(K, c);
+    // order keys of the historical candidates, held in registers
+    constexpr int EMAX = kMaxNB / 64;
+    uint32_t kreg[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      const int j = lane + 64 * e;
+      kreg[e] = (e < E && j < c) ? order_key(row[j]) : 0u;
+    }
     uint32_t thr = 0;
     int need_eq = 0;
     const bool all = (c <= K);
     if (!all) {
-      // largest thr with count(key >= thr) >= K  ->  thr = K-th largest key
+      // largest thr with count(key >= thr) >= K  ->  thr = K-th largest key;
+      // counts by ballot + scalar popcount (no cross-lane data movement)
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = thr | (1u << bit);
         int cnt = 0;
-        for (int e = 0; e < E; ++e) {
-          const int j = lane + 64 * e;
-          if (j < c && order_key(row[j]) >= cand) ++cnt;
-        }
-        cnt = wave_sum_i(cnt);
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+          if (e < E) cnt += wave_count(lane + 64 * e < c && kreg[e] >= cand);
         if (cnt >= K) thr = cand;
       }
       int gt = 0;
-      for (int e = 0; e < E; ++e) {
-        const int j = lane + 64 * e;
-        if (j < c && order_key(row[j]) > thr) ++gt;
-      }
-      need_eq = K - wave_sum_i(gt);
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e < E) gt += wave_count(lane + 64 * e < c && kreg[e] > thr);
+      need_eq = K - gt;
     }
     int base = 0, eq_seen = 0;
-    for (int e = 0; e < E; ++e) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e >= E) break;
       const int j = lane + 64 * e;
       const bool hist = j < c;
-      bool gt = false, eq = false;
-      if (hist && !all) {
-        const uint32_t kk = order_key(row[j]);
-        gt = kk > thr;
-        eq = kk == thr;
-      }
+      const bool gt = hist && !all && kreg[e] > thr;
+      const bool eq = hist && !all && kreg[e] == thr;
       const uint64_t em = ballot64(eq);
       const bool s_in =
           hist && (all || gt || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
