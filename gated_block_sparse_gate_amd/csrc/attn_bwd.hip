@@ -251,8 +251,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int src = (u < UNITS) ? m_src[slot][2 * rp + h] : -1;
-        rq[x][h] = (src >= 0) ? *reinterpret_cast<const uint4*>(p.q + static_cast<size_t>(src) * D + ch * 8) : z;
-        rd[x][h] = (src >= 0) ? *reinterpret_cast<const uint4*>(p.dout + static_cast<size_t>(src) * D + ch * 8) : z;
+        rq[x][h] = (src >= 0) ? ld16(p.q + static_cast<size_t>(src) * D + ch * 8) : z;
+        rd[x][h] = (src >= 0) ? ld16(p.dout + static_cast<size_t>(src) * D + ch * 8) : z;
       }
     }
   };
@@ -266,13 +266,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       for (int h = 0; h < 2; ++h) {
         const int row = 2 * rp + h;
         const int off = row * ROWB + ((ch ^ lds_swz<ROWB>(row)) << 4);
-        *reinterpret_cast<uint4*>(&Qs[buf][off]) = rq[x][h];
-        *reinterpret_cast<uint4*>(&dOs[buf][off]) = rd[x][h];
+        st16(&Qs[buf][off], rq[x][h]);
+        st16(&dOs[buf][off], rd[x][h]);
       }
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&rq[x][0]);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&rq[x][1]);
-      const uint32_t* c0 = reinterpret_cast<const uint32_t*>(&rd[x][0]);
-      const uint32_t* c1 = reinterpret_cast<const uint32_t*>(&rd[x][1]);
+      const uint32_t a0[4] = {rq[x][0].x, rq[x][0].y, rq[x][0].z, rq[x][0].w};
+      const uint32_t a1[4] = {rq[x][1].x, rq[x][1].y, rq[x][1].z, rq[x][1].w};
+      const uint32_t c0[4] = {rd[x][0].x, rd[x][0].y, rd[x][0].z, rd[x][0].w};
+      const uint32_t c1[4] = {rd[x][1].x, rd[x][1].y, rd[x][1].z, rd[x][1].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = ch * 8 + 2 * i;
@@ -390,18 +390,18 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dQ, dlogg
-template <int D, int TW>
-__global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
-  constexpr int NW = 8;
+template <int D, int NW, int TW>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
+  constexpr int NT = NW * 64;
   constexpr int KROWB = D * 2;              // bytes per K / V row
   constexpr int KB = 64 * KROWB;            // one tile (K, V or K^T) in bytes
   constexpr int STAGE = 3 * KB;             // K | V | K^T
   constexpr int TU = KB / 16;               // 16-byte units per tile
-  constexpr int UPT = 3 * TU / 512;         // units per thread per block
+  constexpr int UPT = 3 * TU / NT;         // units per thread per block
   constexpr int KCPR = KROWB / 16;
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  static_assert(3 * TU % 512 == 0, "unit split");
+  static_assert(3 * TU % NT == 0, "unit split");
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[2][STAGE];
   __shared__ uint32_t bits[64][kMaxNBW];
@@ -431,11 +431,11 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
   const int S = a.S;
   const int Tp = a.NB * 64;
 
-  for (int i = tid; i < 64 * kMaxNBW; i += 512) (&bits[0][0])[i] = 0u;
+  for (int i = tid; i < 64 * kMaxNBW; i += NT) (&bits[0][0])[i] = 0u;
   if (tid < kMaxNBW) ubits[tid] = 0u;
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
-  for (int e = tid; e < ntok * S; e += 512) {
+  for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < ntok * S; e += 512) {
+  for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
@@ -518,52 +518,51 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
   __syncthreads();
   const int nU = s_nU;
 
-  // ---- block staging: K and V rows (16-byte-chunk swizzle) and K^T rows
-  // (from the transposed copy; 8-byte-unit swizzle, halves swapped on odd rows)
+  // ---- block staging: K and V rows (lds_swz) and K^T rows (from the
+  // transposed copy, keys in operand order; tr_swz)
   const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
   const uint16_t* vbase = a.v + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
   const uint16_t* ktbase =
       a.kt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
+  // Unit x of this thread belongs to tile x / (TU / NT) (K, V, then K^T):
+  // the split is a compile-time property of x because tid < NT.
+  static_assert(TU % NT == 0, "tile split");
+  constexpr int XPT = TU / NT;        // units per thread per tile
   uint4 stg[UPT];
   int soff[UPT];
-  bool sswap[UPT];
+  int goff[UPT];                      // K/V: row within the block; K^T: d * Tp + chunk
 #pragma unroll
   for (int x = 0; x < UPT; ++x) {
-    const int u = tid + 512 * x;
-    const int tile = u / TU, w = u - tile * TU;
+    const int tile = x / XPT;
+    const int w = tid + NT * (x - tile * XPT);
     if (tile < 2) {
       const int r = w / KCPR, ch = w - r * KCPR;
       soff[x] = tile * KB + r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
-      sswap[x] = false;
+      goff[x] = r;
     } else {
       const int d = w >> 3, kc = w & 7;
-      soff[x] = 2 * KB + d * 128 + ((kc ^ ((d >> 1) & 7)) << 4);
-      sswap[x] = (d & 1) != 0;
+      soff[x] = 2 * KB + d * 128 + ((kc ^ tr_swz(d)) << 4);
+      goff[x] = d * Tp + kc * 8;
     }
   }
-  auto gload = [&](int j) {
+  const size_t tokstride = static_cast<size_t>(a.Hkv) * D;
+  auto gload = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < UPT; ++x) {
-      const int u = tid + 512 * x;
-      const int tile = u / TU, w = u - tile * TU;
+      const int tile = x / XPT;
+      const int w = tid + NT * (x - tile * XPT);
       if (tile < 2) {
-        const int r = w / KCPR, ch = w - r * KCPR;
+        const int r = goff[x], ch = w - r * KCPR;
         const int tok = min(j * 64 + r, a.T - 1);
-        const uint16_t* base = tile == 0 ? kbase : vbase;
-        stg[x] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(tok) * a.Hkv * D + ch * 8);
+        stg[x] = ld16((tile == 0 ? kbase : vbase) + static_cast<size_t>(tok) * tokstride + ch * 8);
       } else {
-        const int d = w >> 3, kc = w & 7;
-        stg[x] = *reinterpret_cast<const uint4*>(ktbase + static_cast<size_t>(d) * Tp + j * 64 + kc * 8);
+        stg[x] = ld16(ktbase + goff[x] + j * 64);
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const uint4 v = stg[x];
-      *reinterpret_cast<uint4*>(&ring[buf][soff[x]]) =
-          sswap[x] ? make_uint4(v.z, v.w, v.x, v.y) : v;
-    }
+    for (int x = 0; x < UPT; ++x) st16(&ring[buf][soff[x]], stg[x]);
   };
   if (nU > 0) {
     gload(ulist[0]);
@@ -576,12 +575,10 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     kofs[ks] = l16 * KROWB + (((ks * 4 + g4) ^ lds_swz<KROWB>(l16)) << 4);
-  int tofs[2][2];
+  int tofs[2];
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    tofs[k2][0] = 2 * KB + l16 * 128 + (((k2 * 8 + g4) ^ l16) << 3);
-    tofs[k2][1] = 2 * KB + l16 * 128 + (((k2 * 8 + 4 + g4) ^ l16) << 3);
-  }
+  for (int k2 = 0; k2 < 2; ++k2)
+    tofs[k2] = 2 * KB + l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
 
   const float sl2 = a.scale_log2;
   for (int u = 0; u < nU; ++u) {
@@ -662,9 +659,7 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdParams a) {
       for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(st + dt * 2048 + tofs[k2][0]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(st + dt * 2048 + tofs[k2][1]);
-          const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const uint4 kta = *reinterpret_cast<const uint4*>(st + dt * 2048 + tofs[k2]);
           dqa[ti][dt] = mfma16x16x32(kta, dsb[k2], dqa[ti][dt]);
           dqa[ti][dt] = mfma16x16x32(kta, dsl[k2], dqa[ti][dt]);
         }
@@ -707,13 +702,16 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
                      dim3(256), 0, st, p);
   hipError_t e = launch_transpose_tokens(p.k, p.kt, p.B, p.T, p.Hkv, D, st);
   if (e != hipSuccess) return e;
-  const int tw = (p.ntiles + 7) / 8;
-  switch (tw) {
-    case 1: hipLaunchKernelGGL((dq_kernel<D, 1>), dim3(nblk), dim3(512), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((dq_kernel<D, 2>), dim3(nblk), dim3(512), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((dq_kernel<D, 3>), dim3(nblk), dim3(512), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((dq_kernel<D, 4>), dim3(nblk), dim3(512), 0, st, p); break;
-    default: return hipErrorInvalidValue;
+  if (p.ntiles <= 8) {
+    hipLaunchKernelGGL((dq_kernel<D, 8, 1>), dim3(nblk), dim3(512), 0, st, p);
+  } else if (p.ntiles <= 16) {
+    hipLaunchKernelGGL((dq_kernel<D, 8, 2>), dim3(nblk), dim3(512), 0, st, p);
+  } else {
+    switch ((p.ntiles + 7) / 8) {
+      case 3: hipLaunchKernelGGL((dq_kernel<D, 8, 3>), dim3(nblk), dim3(512), 0, st, p); break;
+      case 4: hipLaunchKernelGGL((dq_kernel<D, 8, 4>), dim3(nblk), dim3(512), 0, st, p); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }

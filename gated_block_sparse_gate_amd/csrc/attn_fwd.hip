@@ -8,14 +8,17 @@
 //   one workgroup = (batch b, KV head kappa, query block c) = 64 tokens x G heads.
 //   The workgroup walks the union of the blocks its 64 tokens selected, in
 //   ascending order.  Each block's K tile and V^T tile (from a transposed copy
-//   of V made once per call) is staged once into double-buffered LDS (plain
-//   16-byte copies, chunks XOR-swizzled per row so the MFMA operand reads are
-//   conflict-free); the next block's loads are in flight in registers while
-//   the current one is computed, with one workgroup barrier per block.  A wave owns TW row tiles of 16 rows =
+//   of V made once per call, keys in operand order) is staged once into
+//   double-buffered LDS (plain 16-byte copies, chunks XOR-swizzled per row so
+//   the MFMA operand reads are conflict-free); the next block's loads are in
+//   flight in registers while the current one is computed, with one
+//   workgroup barrier per block.  A wave owns TW row tiles of 16 rows =
 //   floor(16/G) tokens x G heads; a tile in which no token selected the block
 //   skips it, otherwise S^T = K Q^T and O^T += V^T P^T run on bf16 MFMA
-//   16x16x32 with rows outside the selection masked to -inf.  Online-softmax
-//   state stays in registers (one query row per lane column).
+//   16x16x32 with rows outside the selection masked out.  Online-softmax
+//   state stays in registers (one query row per lane column); the running
+//   reference maximum is moved only when a row's new maximum exceeds it by
+//   more than 2^kLazyLog2, so the output rescale is rare.
 #include "sas_kernels.h"
 
 namespace sas {
@@ -24,19 +27,21 @@ namespace {
 
 // HILO: P enters the PV product as bf16 hi + lo parts (exact to ~2^-16);
 // used when the fp32 output is requested for the backward's Delta.
-template <int D, int TW, bool HILO>
-__global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
-  constexpr int NW = 8;
+constexpr float kLazyLog2 = 8.f;   // weights stay below 2^8 between rescales
+
+template <int D, int NW, int TW, bool HILO>
+__global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
+  constexpr int NT = NW * 64;
   constexpr int KROWB = D * 2;              // bytes per K row
   constexpr int KB = 64 * KROWB;            // K tile bytes
   constexpr int VB = D * 128;               // V^T tile bytes (D rows x 64 keys)
   constexpr int STAGE = KB + VB;
   constexpr int KU = KB / 16;               // 16-byte K units per tile
-  constexpr int UPT = STAGE / 16 / 512;     // 16-byte units per thread per block
+  constexpr int UPT = STAGE / 16 / NT;      // 16-byte units per thread per block
   constexpr int KCPR = KROWB / 16;          // 16-byte chunks per K row
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  static_assert(STAGE % (16 * 512) == 0, "unit split");
+  static_assert(STAGE % (16 * NT) == 0, "unit split");
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[2][STAGE];
   __shared__ uint32_t bits[64][kMaxNBW];
@@ -65,11 +70,11 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
   const int Tp = a.NB * 64;
 
   // ---- selection bitmaps of the 64 tokens, their union, log-gates by rank
-  for (int i = tid; i < 64 * kMaxNBW; i += 512) (&bits[0][0])[i] = 0u;
+  for (int i = tid; i < 64 * kMaxNBW; i += NT) (&bits[0][0])[i] = 0u;
   if (tid < kMaxNBW) ubits[tid] = 0u;
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
-  for (int e = tid; e < ntok * S; e += 512) {
+  for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const int j = a.idx[(rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s];
     if (j >= 0 && j <= c) {
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < ntok * S; e += 512) {
+  for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
@@ -151,46 +156,36 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
   auto gload = [&](int j) {
 #pragma unroll
     for (int x = 0; x < UPT; ++x) {
-      const int u = tid + 512 * x;
+      const int u = tid + NT * x;
       if (u < KU) {
         const int r = u / KCPR, ch = u - r * KCPR;
         const int tok = min(j * 64 + r, a.T - 1);
-        stg[x] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(tok) * a.Hkv * D + ch * 8);
+        stg[x] = ld16(kbase + static_cast<size_t>(tok) * a.Hkv * D + ch * 8);
       } else {
         const int v = u - KU;
         const int d = v >> 3, kc = v & 7;
-        stg[x] = *reinterpret_cast<const uint4*>(vtbase + static_cast<size_t>(d) * Tp + j * 64 + kc * 8);
+        stg[x] = ld16(vtbase + static_cast<size_t>(d) * Tp + j * 64 + kc * 8);
       }
     }
   };
-  // LDS store offsets of this thread's units (loop-invariant).  K rows use a
-  // 16-byte-chunk swizzle; V^T rows (128 B) use an 8-byte-unit swizzle
-  // unit ^ (d & 15), so 16 lanes reading one unit of 16 consecutive rows hit
-  // 16 distinct 8-byte bank pairs; on odd rows this swaps the two halves of
-  // a 16-byte chunk.
+  // LDS store offsets of this thread's units (loop-invariant): 16-byte-chunk
+  // XOR swizzles for K rows (lds_swz) and V^T rows (tr_swz).
   int soff[UPT];
-  bool sswap[UPT];
 #pragma unroll
   for (int x = 0; x < UPT; ++x) {
-    const int u = tid + 512 * x;
+    const int u = tid + NT * x;
     if (u < KU) {
       const int r = u / KCPR, ch = u - r * KCPR;
       soff[x] = r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
-      sswap[x] = false;
     } else {
       const int v = u - KU;
       const int d = v >> 3, kc = v & 7;
-      soff[x] = KB + d * 128 + ((kc ^ ((d >> 1) & 7)) << 4);
-      sswap[x] = (d & 1) != 0;
+      soff[x] = KB + d * 128 + ((kc ^ tr_swz(d)) << 4);
     }
   }
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const uint4 v = stg[x];
-      *reinterpret_cast<uint4*>(&ring[buf][soff[x]]) =
-          sswap[x] ? make_uint4(v.z, v.w, v.x, v.y) : v;
-    }
+    for (int x = 0; x < UPT; ++x) st16(&ring[buf][soff[x]], stg[x]);
   };
   if (nU > 0) {
     gload(ulist[0]);
@@ -205,12 +200,9 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     kofs[ks] = l16 * KROWB + (((ks * 4 + g4) ^ lds_swz<KROWB>(l16)) << 4);
-  int vofs[2][2];
+  int vofs[2];
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    vofs[k2][0] = KB + l16 * 128 + (((k2 * 8 + g4) ^ l16) << 3);
-    vofs[k2][1] = KB + l16 * 128 + (((k2 * 8 + 4 + g4) ^ l16) << 3);
-  }
+  for (int k2 = 0; k2 < 2; ++k2) vofs[k2] = KB + l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
 
   const float sl2 = a.scale_log2;
   for (int u = 0; u < nU; ++u) {
@@ -230,6 +222,12 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
 #pragma unroll
     for (int ti = 0; ti < TW; ++ti) {
       if (!act[ti]) continue;
+      const int tl = tl_row[ti];
+      float lgv = 0.f;
+      if (sel[ti]) {
+        const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
+        lgv = lgs[tl][rank];
+      }
       // S^T[key, row] = K[key,:] . Q[row,:]
       floatx4 sacc[4];
 #pragma unroll
@@ -241,52 +239,53 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
           sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
         }
       }
-      const int tl = tl_row[ti];
-      float lgv = -INFINITY;
-      if (sel[ti]) {
-        const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
-        lgv = lgs[tl][rank];
-      }
-      float x[4][4];
-      float mx = -INFINITY;
+      // row maximum of the raw scores over the keys this row may see
+      const int lim = t0 + tl - j * 64 - g4 * 4;     // current block: key offset limit
+      float mr = -INFINITY;
       if (cur) {
-        const int lim = t0 + tl - j * 64 - g4 * 4;     // key offset limit for this lane
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (mt * 16 + i <= lim) mr = fmaxf(mr, sacc[mt][i]);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          mr = fmaxf(mr, fmaxf(fmaxf(sacc[mt][0], sacc[mt][1]), fmaxf(sacc[mt][2], sacc[mt][3])));
+      }
+      mr = fmaxf(mr, __shfl_xor(mr, 16, 64));
+      mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+      const float cand = sel[ti] ? mr * sl2 + lgv : -INFINITY;
+      const bool up = cand > m_run[ti] + kLazyLog2;
+      if (ballot64(up)) {
+        const float alpha = up ? fast_exp2(m_run[ti] - cand) : 1.f;
+        m_run[ti] = up ? cand : m_run[ti];
+        l_run[ti] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[ti][dt] *= alpha;
+      }
+      const float bias = sel[ti] ? lgv - m_run[ti] : -INFINITY;
+      float x[4][4];
+      float psum = 0.f;
+      if (cur) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float val = (mt * 16 + i <= lim) ? sacc[mt][i] * sl2 + lgv : -INFINITY;
-            x[mt][i] = val;
-            mx = fmaxf(mx, val);
+            const float e = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
+            x[mt][i] = (mt * 16 + i <= lim) ? e : 0.f;
+            psum += x[mt][i];
           }
       } else {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            x[mt][i] = sacc[mt][i] * sl2 + lgv;
-            mx = fmaxf(mx, x[mt][i]);
+            x[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
+            psum += x[mt][i];
           }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[ti], mx);
-      const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[ti] - msafe);
-      m_run[ti] = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[mt][i] = fast_exp2(x[mt][i] - msafe);
-          psum += x[mt][i];
-        }
-      l_run[ti] = l_run[ti] * alpha + psum;
-      if (ballot64(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[ti][dt] *= alpha;
-      }
+      l_run[ti] += psum;
       uint4 pb[2], pl[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
@@ -303,14 +302,13 @@ __global__ __launch_bounds__(512) void sparse_fwd_kernel(FwdParams a) {
         }
       }
       // O^T[d, row] += V^T[d, keys] . P^T[keys, row]; inside a 32-key step the
-      // key order follows P's register layout: {4g..4g+3, 16+4g..16+4g+3}.
+      // lane's 8 keys are {4g..4g+3, 16+4g..16+4g+3}, stored contiguously in
+      // the transposed copy.
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(st + dt * 2048 + vofs[k2][0]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(st + dt * 2048 + vofs[k2][1]);
-          const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const uint4 va = *reinterpret_cast<const uint4*>(st + dt * 2048 + vofs[k2]);
           oacc[ti][dt] = mfma16x16x32(va, pb[k2], oacc[ti][dt]);
           if (HILO) oacc[ti][dt] = mfma16x16x32(va, pl[k2], oacc[ti][dt]);
         }
@@ -352,12 +350,17 @@ template <int D, bool HILO>
 hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
   const int NQB = (p.T + 63) / 64;
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * NQB);
+  // up to 16 row tiles: one tile per wave, 16 waves (4 per SIMD hide the
+  // latency of the per-tile MFMA -> softmax -> MFMA chain); more tiles
+  // (G >= 5): 8 waves with TW tiles each.
   const int tw = (p.ntiles + 7) / 8;
+  if (p.ntiles <= 16) {
+    hipLaunchKernelGGL((sparse_fwd_kernel<D, 16, 1, HILO>), grid, dim3(1024), 0, st, p);
+    return hipGetLastError();
+  }
   switch (tw) {
-    case 1: hipLaunchKernelGGL((sparse_fwd_kernel<D, 1, HILO>), grid, dim3(512), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((sparse_fwd_kernel<D, 2, HILO>), grid, dim3(512), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((sparse_fwd_kernel<D, 3, HILO>), grid, dim3(512), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((sparse_fwd_kernel<D, 4, HILO>), grid, dim3(512), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((sparse_fwd_kernel<D, 8, 3, HILO>), grid, dim3(512), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((sparse_fwd_kernel<D, 8, 4, HILO>), grid, dim3(512), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

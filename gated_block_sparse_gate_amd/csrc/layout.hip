@@ -1,15 +1,21 @@
 // Layout helpers: per-(batch, KV head) transposed copies of K or V so that a
 // 64-key block of K^T / V^T is D contiguous 128-byte rows (keys fastest).
-// The attention kernels contract over keys on the matrix cores, which needs
-// the key index contiguous per lane; with the transposed copy every tile is
-// a plain 16-byte-granular copy that can be streamed straight into LDS.
+// The attention kernels contract over keys on the matrix cores (O^T += V^T P^T,
+// dQ^T += K^T dS^T), which needs 8 keys contiguous per lane; with the
+// transposed copy every tile is a plain 16-byte-granular copy.
+//
+// Key order inside each 32-key group: the P^T / dS^T operand comes straight
+// out of the score tile's accumulator layout, where lane group g (0..3) holds
+// keys 4g..4g+3 and 16+4g..16+4g+3.  The copy stores exactly those 8 keys at
+// positions 8g..8g+7, so one 16-byte read gives a lane its whole operand.
 #include "sas_kernels.h"
 
 namespace sas {
 
 namespace {
 
-// src [B,T,H,D] -> dst [B,H,D,Tp] (Tp = 64 * ceil(T/64), tail zero-filled).
+// src [B,T,H,D] -> dst [B,H,D,Tp] (Tp = 64 * ceil(T/64), tail zero-filled),
+// keys permuted inside each 32-key group as described above.
 // One workgroup = one 64-token block of one (b, h): reads 64 rows of D
 // coalesced, writes D rows of 64 keys coalesced, through LDS.
 template <int D>
@@ -34,8 +40,11 @@ __global__ __launch_bounds__(256) void transpose_tokens_kernel(const uint16_t* _
   uint16_t* out = dst + (static_cast<size_t>(b) * H + h) * D * static_cast<size_t>(Tp) + j * 64;
   for (int u = tid; u < D * 32; u += 256) {
     const int d = u / 32, kp = u - d * 32;
-    const uint32_t w = static_cast<uint32_t>(tile[d * P + 2 * kp]) |
-                       (static_cast<uint32_t>(tile[d * P + 2 * kp + 1]) << 16);
+    // output positions 2kp, 2kp+1 = group kg, lane group g, slot i (even)
+    const int kg = kp >> 4, g = (kp >> 2) & 3, i = (kp & 3) * 2;
+    const int key = kg * 32 + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
+    const uint32_t w = static_cast<uint32_t>(tile[d * P + key]) |
+                       (static_cast<uint32_t>(tile[d * P + key + 1]) << 16);
     *reinterpret_cast<uint32_t*>(out + static_cast<size_t>(d) * Tp + 2 * kp) = w;
   }
 }

@@ -71,11 +71,31 @@ __device__ __forceinline__ int lds_swz(int r) {
   return ROWB == 256 ? (r & 15) : ((r >> 1) & 7);
 }
 
+// XOR swizzle of the 16-byte chunks of a 128-byte row d of a transposed
+// (K^T / V^T) LDS tile, read as one 16-byte chunk of 16 consecutive rows per
+// 16 lanes.  f(d) = (d & 7) ^ ((d >> 3) & 1) keeps any 8 consecutive rows on
+// distinct chunks and, among rows of equal parity (which share one half of a
+// 256-byte bank window), all 16 rows on distinct chunks: conflict-free both
+// for 128-byte and for 256-byte bank windows.
+__device__ __forceinline__ int tr_swz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+
 // Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
 // lane i's 16 bytes land at lds + 16 * i.  `lds` must be wave-uniform.
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds), 16, 0, 0);
+}
+
+// 16-byte load / store through a native vector type.  A plain uint4 struct
+// copy becomes a memcpy, which keeps arrays of staged values that live across
+// loop iterations from being promoted to registers (they end up in scratch).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -162,13 +162,25 @@ def test_sparse_attn_fwd(w):
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "forward not bitwise repeatable"
 
 
+@pytest.mark.parametrize("use_f32", [False, True], ids=["o_bf16", "o_f32"])
 @pytest.mark.parametrize("w", CASES, ids=IDS)
-def test_sparse_attn_bwd(w):
+def test_sparse_attn_bwd(w, use_f32):
+    """Backward with the fp32 forward output (the training-step path: Delta
+    from o before bf16 rounding) and from the bf16 output alone.  Without
+    o_f32, Delta carries the bf16 rounding of o times |dout| sqrt(D); that
+    error enters dlogg scaled by the slot's attention mass (up to 1) and
+    breaks its zero sum, so in that mode only dq, dk, dv are held to the
+    bound."""
     P = prepared(w)
     d = P["dev"]
     idx, logg = _oracle_sel(P)
-    o, lse, o32 = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"], want_f32=True)
-    assert_close("o_f32", o32, P["g"]["o"])
+    if use_f32:
+        o, lse, o32 = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"],
+                                          want_f32=True)
+        assert_close("o_f32", o32, P["g"]["o"])
+    else:
+        o, lse = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, P["scale"])
+        o32 = None
     dq, dk, dv, dlogg = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg,
                                             P["scale"], o_f32=o32)
     torch.cuda.synchronize()
@@ -176,9 +188,10 @@ def test_sparse_attn_bwd(w):
     assert_close("dq", dq, g["dq"])
     assert_close("dk", dk, g["dk"])
     assert_close("dv", dv, g["dv"])
-    assert_close("dlogg", dlogg, g["dlogg"])
-    # gradient w.r.t. log g sums to zero over each row's selected slots
-    assert float(dlogg.sum(-1).abs().max()) < 1e-3
+    if use_f32:
+        assert_close("dlogg", dlogg, g["dlogg"])
+        # gradient w.r.t. log g sums to zero over each row's selected slots
+        assert float(dlogg.sum(-1).abs().max()) < 1e-3
     out2 = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx, logg, P["scale"],
                                o_f32=o32)
     torch.cuda.synchronize()
