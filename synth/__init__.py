@@ -197,3 +197,40 @@ def decode_inputs(w: Workload, seed: int = 0, device="cpu", Lmax: int | None = N
         ctx_len=ctx_len.to(device=device, dtype=torch.int32),
         Lmax=Lmax, NBmax=NBmax,
     )
+
+
+TID_SEL, TID_SELLOGG = 12, 13
+
+
+def random_selection(w: Workload, seed: int = 0, device="cpu", K: int | None = None):
+    """A selection with the structure of sas_topk_blocks' output, drawn at
+    random (no scoring): for token t of block c, min(K, c) distinct historical
+    blocks j < c chosen uniformly, in ascending order, then c, then pads -1;
+    log-gates logg ~ N(-log(c + 1), 1) on valid slots, -inf on pads.
+
+    With iid inputs the router's own choices are statistically of this kind
+    (adjacent tokens share no more blocks than chance), so this drives the
+    attention kernels at full size with inputs that do not depend on the
+    router implementation.  Returns idx int32, logg fp32 [B,T,Hkv,K+1].
+    """
+    K = w.topk if K is None else K
+    B, T, Hkv, NB = w.B, w.T, w.Hkv, w.NB
+    S = K + 1
+    g = generator("cpu", seed, w.cfg_id, TID_SEL)
+    c = (torch.arange(T) // w.block).view(1, T, 1, 1)
+    idx = torch.full((B, T, Hkv, S), -1, dtype=torch.int64)
+    if K > 0 and NB > 1:
+        keys = torch.rand((B, T, Hkv, NB), generator=g)
+        j = torch.arange(NB).view(1, 1, 1, NB)
+        keys = torch.where(j < c, keys, torch.full_like(keys, -1.0))
+        top = torch.topk(keys, min(K, NB), dim=-1)
+        chosen = torch.where(top.values >= 0, top.indices, torch.full_like(top.indices, NB + 1))
+        chosen, _ = torch.sort(chosen, dim=-1)
+        chosen = torch.where(chosen <= NB, chosen, torch.full_like(chosen, -1))
+        idx[..., :chosen.shape[-1]] = chosen
+    nsel = torch.minimum(c.expand(B, T, Hkv, 1), torch.tensor(K)).squeeze(-1)   # [B,T,Hkv]
+    idx.scatter_(-1, nsel.unsqueeze(-1), c.expand(B, T, Hkv, 1).clone())
+    g2 = generator("cpu", seed, w.cfg_id, TID_SELLOGG)
+    lg = torch.randn((B, T, Hkv, S), generator=g2) - torch.log(c.float() + 1.0)
+    logg = torch.where(idx >= 0, lg, torch.full_like(lg, float("-inf")))
+    return idx.to(torch.int32).to(device), logg.to(torch.float32).to(device)

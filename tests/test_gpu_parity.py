@@ -6,8 +6,9 @@ K beyond the number of blocks.  Tolerances: selected block indices
 bit-exact outside near-tie rows (K-th/(K+1)-th gate-logit gap < 1e-5 in
 fp64); bf16 outputs and gradients within 1e-2 max-abs beyond the bf16
 representation error of the exact value (half a bf16 ulp of the reference,
-which alone reaches 1.6e-2 for |x| in [4, 8)) and 1e-3 mean-abs of the raw
-error; fp32 outputs (log-gate gradient, lse) and router outputs within the
+which alone reaches 1.6e-2 for |x| in [4, 8)) and 1e-3 mean-abs beyond the
+mean of those half-ulps (the mean cost of storing the exact values in bf16);
+fp32 outputs (log-gate gradient, lse) and router outputs within the
 stated absolute bounds with no allowance.
 """
 import math
@@ -80,9 +81,10 @@ def errs(gpu, ref):
 
 def assert_close(name, gpu, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
     raw, mx, mn = errs(gpu, ref)
-    print(f"  {name}: max-abs {raw:.3e} (beyond bf16 rounding {mx:.3e}) mean-abs {mn:.3e}",
-          flush=True)
-    assert mx <= max_abs and mn <= mean_abs, (name, raw, mx, mn)
+    floor = float(bf16_half_ulp(ref).mean()) if gpu.dtype == torch.bfloat16 else 0.0
+    print(f"  {name}: max-abs {raw:.3e} (beyond bf16 rounding {mx:.3e}) mean-abs {mn:.3e} "
+          f"(bf16 floor {floor:.1e})", flush=True)
+    assert mx <= max_abs and mn <= mean_abs + floor, (name, raw, mx, mn, floor)
 
 
 @pytest.mark.parametrize("w", CASES, ids=IDS)
