@@ -80,6 +80,64 @@ def load_traffic(kernel_key: str, src_hash: str):
     return None
 
 
+COPY_BYTES = 1 << 30          # the calibration copy (--copy-calib)
+TRAFFIC_SOURCES = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
+                   "dq_kernel": "attn_bwd.hip", "topk_kernel": "topk.hip",
+                   "decode_attn_kernel": "decode.hip", "decode_select_kernel": "decode.hip"}
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
+    """HBM traffic per launch from two rocprofv3 --pmc runs of this script with
+    --copy-calib (one with FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch).
+    Each counter is scaled by what it reads for the 1 GiB device-to-device
+    copy (rocclr copyBuffer) of the same run, so bytes = counter * 1 GiB /
+    counter(copy).  Writes profiles/traffic.json keyed by kernel, with the
+    hash of the kernel's source so stale entries are ignored."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
+    res, lines = {}, []
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        copies = [v for k, l in vals.items() if "copyBuffer" in k for v in l
+                  if v * 1024 >= COPY_BYTES // 2]
+        if not copies:
+            raise SystemExit(f"no calibration copy found in {d}")
+        ref = sum(copies) / len(copies)
+        factor = COPY_BYTES / ref
+        lines.append(f"{counter}: calibration copy of {COPY_BYTES} B reads {ref:.0f} KiB "
+                     f"per dispatch -> factor {factor:.4f} B per KiB")
+        for key in TRAFFIC_SOURCES:
+            l = [v for k, ll in vals.items() if key + "<" in k or k.startswith(key) or
+                 ("::" + key) in k for v in ll]
+            if not l:
+                continue
+            avg = sum(l) / len(l)
+            e = res.setdefault(key, {})
+            e[counter.lower() + "_kib_per_dispatch"] = round(avg, 1)
+            e[counter.lower() + "_bytes"] = round(avg * factor)
+            e["dispatches"] = len(l)
+    for key, e in res.items():
+        e["bytes_per_launch"] = e.get("fetch_size_bytes", 0) + e.get("write_size_bytes", 0)
+        e["source_hash"] = source_hash([os.path.join(csrc, f) for f in
+                                        (TRAFFIC_SOURCES[key], "sas_device.h", "sas_kernels.h")])
+        lines.append(f"{key}: fetch {e.get('fetch_size_bytes', 0) / 1e9:.3f} GB + write "
+                     f"{e.get('write_size_bytes', 0) / 1e9:.3f} GB per launch "
+                     f"({e['dispatches']} dispatches)")
+    json.dump(res, open(out_json, "w"), indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
 def cpu_baseline(seed: int, n_tokens: int):
     """The fp64 oracle, as it stands, on a bounded sample of the 32K workload:
     forward + backward of every query head for n_tokens query tokens spread
@@ -127,10 +185,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=20)
-    ap.add_argument("--cpu-tokens", type=int, default=160)
+    ap.add_argument("--cpu-tokens", type=int, default=600)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for traffic)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, os.path.join(ROOT, "profiles", "traffic.json"))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -176,6 +242,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     ev = None
+    fev = bev = None
 
     def step(record=False):
         if record:
@@ -187,26 +254,33 @@ def main():
         sas.topk_blocks(qg, kg, K, Hq, D, out=(idx, logg, glse))
         if record:
             ev[2].record(stream)
+            sas.set_timing_events(fev)       # stage boundaries inside the calls
         sas.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, logg, scale, o=o, lse=lse, o_f32=o32,
                             workspace=ws_fwd)
         if record:
             ev[3].record(stream)
+            sas.set_timing_events(bev)
         sas.sparse_attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, scale,
                             workspace=ws_bwd, out=(dq, dk, dv, dlogg), o_f32=o32)
         if record:
             ev[4].record(stream)
+            sas.set_timing_events(None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     stage_ms = [0.0] * 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    bevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for e in [e for l in fevs + bevs for e in l]:
+        e.record(stream)                    # create the events before the timed region
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        ev = evs[i]
+        ev, fev, bev = evs[i], fevs[i], bevs[i]
         step(record=True)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -215,6 +289,21 @@ def main():
         for s_ in range(4):
             stage_ms[s_] += evs[i][s_].elapsed_time(evs[i][s_ + 1]) / args.steps
     ms_per_step = total_ms / args.steps
+
+    def avg_ms(lst, a, b):
+        return sum(l[a].elapsed_time(l[b]) for l in lst) / len(lst)
+
+    kern_ms = {"sparse_fwd_kernel": avg_ms(fevs, 1, 2), "transpose_v": avg_ms(fevs, 0, 1),
+               "bwd_delta+csr": avg_ms(bevs, 0, 1), "dkdv_kernel": avg_ms(bevs, 1, 2),
+               "transpose_k": avg_ms(bevs, 2, 3), "dq_kernel": avg_ms(bevs, 3, 4)}
+
+    if args.copy_calib:
+        src_c = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        for _ in range(3):
+            dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
 
     pairs = attended_pairs(T, K) * Hq * B
     fwd_flops = 4.0 * D * pairs
@@ -225,18 +314,32 @@ def main():
     attn_tflops = (fwd_flops + bwd_flops) / ((stage_ms[2] + stage_ms[3]) * 1e-3) / 1e12
 
     csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
-    fwd_hash = source_hash([os.path.join(csrc, f) for f in ("attn_fwd.hip", "sas_device.h",
+    # algorithmic FLOPs per launch: the contractions each kernel must perform,
+    # 2 D per attended (query head, key) pair each: forward S and PV (4 D);
+    # dK/dV kernel S, dP, dV, dK (8 D); dQ kernel S, dP, dQ (6 D)
+    kflops = {"sparse_fwd_kernel": 4.0 * D * pairs, "dkdv_kernel": 8.0 * D * pairs,
+              "dq_kernel": 6.0 * D * pairs}
+    ksrc = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
+            "dq_kernel": "attn_bwd.hip"}
+    kernels = {}
+    for kname, fl in kflops.items():
+        ms = kern_ms[kname]
+        kernels[kname] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                          "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    dom = max(kflops, key=lambda k: kern_ms[k])
+    dom_tf = kflops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    dom_hash = source_hash([os.path.join(csrc, f) for f in (ksrc[dom], "sas_device.h",
                                                             "sas_kernels.h")])
     roofline = {
-        "kernel": "sparse_fwd_kernel (sas_sparse_attn_fwd: one launch per call)",
+        "kernel": dom,
         "bound": "mfma",
-        "achieved": round(fwd_tflops, 2),
+        "achieved": round(dom_tf, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
-        "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-        "traffic": load_traffic("sparse_fwd_kernel", fwd_hash),
-        "algorithmic_flops_per_launch": fwd_flops,
-        "launch_ms": round(stage_ms[2], 4),
+        "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+        "traffic": load_traffic(dom, dom_hash),
+        "algorithmic_flops_per_launch": kflops[dom],
+        "launch_ms": round(kern_ms[dom], 4),
     }
 
     out = {
@@ -262,6 +365,8 @@ def main():
         "attn_fwd_bwd_tflops": round(attn_tflops, 2),
         "effective_pairs_per_head": attended_pairs(T, K),
         "roofline": roofline,
+        "kernels": kernels,
+        "other_ms": {k: round(v, 4) for k, v in kern_ms.items() if k not in kflops},
     }
 
     # ------------------------------------------------------------ decode

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "Dims", "DecodeDims", "SasError", "load_library", "version", "workspace_size",
     "decode_workspace_size", "gate_score", "topk_blocks", "sparse_attn_fwd",
-    "sparse_attn_bwd", "decode", "budget_to_topk", "EXPORTED_SYMBOLS",
+    "sparse_attn_bwd", "decode", "budget_to_topk", "EXPORTED_SYMBOLS", "set_timing_events",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,7 @@ OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD = range(4)
 EXPORTED_SYMBOLS = (
     "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
     "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
-    "sas_decode",
+    "sas_decode", "sas_set_timing_events",
 )
 
 
@@ -82,8 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         + [P, S, P])
     lib.sas_decode.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 6 + [F32] + [P] * 3
                                + [P, S, P])
+    lib.sas_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     for fn in ("sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd",
-               "sas_sparse_attn_bwd", "sas_decode"):
+               "sas_sparse_attn_bwd", "sas_decode", "sas_set_timing_events"):
         getattr(lib, fn).restype = I32
     _lib = lib
     return lib
@@ -114,6 +115,23 @@ def decode_workspace_size(d: DecodeDims) -> int:
     if n == ctypes.c_size_t(-1).value:
         raise SasError(SAS_ERR_INVALID, load_library().sas_last_error().decode())
     return n
+
+
+def set_timing_events(events=None):
+    """Record the given torch.cuda.Event objects at the stage boundaries of the
+    following sparse_attn_fwd / sparse_attn_bwd calls on this thread (see
+    sas_set_timing_events in sas.h); None or [] switches the hook off."""
+    lib = load_library()
+    if not events:
+        _check(lib.sas_set_timing_events(None, 0))
+        return
+    handles = []
+    for e in events:
+        if not e.cuda_event:          # torch creates the event on first record
+            e.record()
+        handles.append(e.cuda_event)
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    _check(lib.sas_set_timing_events(arr, len(handles)))
 
 
 def budget_to_topk(budget: int, block: int = 64) -> int:

@@ -690,6 +690,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   const long nrows = static_cast<long>(p.B) * p.T * p.Hq;
+  timing_mark(0, st);
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((nrows * 16 + 255) / 256), dim3(256), 0, st,
                      p.o, p.o32, p.dout, p.delta, nrows);
   const int NQB = p.NB;
@@ -698,10 +699,13 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hkv), dim3(256), 0, st, p);
   hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hkv), dim3(1024), 0, st, p);
   hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
+  timing_mark(1, st);
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
                      dim3(256), 0, st, p);
+  timing_mark(2, st);
   hipError_t e = launch_transpose_tokens(p.k, p.kt, p.B, p.T, p.Hkv, D, st);
   if (e != hipSuccess) return e;
+  timing_mark(3, st);
   if (p.ntiles <= 8) {
     hipLaunchKernelGGL((dq_kernel<D, 8, 1>), dim3(nblk), dim3(512), 0, st, p);
   } else if (p.ntiles <= 16) {
@@ -713,6 +717,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
   }
+  timing_mark(4, st);
   return hipGetLastError();
 }
 

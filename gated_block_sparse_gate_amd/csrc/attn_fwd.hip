@@ -374,11 +374,14 @@ hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st) {
+  timing_mark(0, st);
   hipError_t e = launch_transpose_tokens(p.v, p.vt, p.B, p.T, p.Hkv, p.D, st);
   if (e != hipSuccess) return e;
-  if (p.D == 128) return launch_fwd_d<128>(p, st);
-  if (p.D == 64) return launch_fwd_d<64>(p, st);
-  return hipErrorInvalidValue;
+  timing_mark(1, st);
+  e = p.D == 128 ? launch_fwd_d<128>(p, st) : p.D == 64 ? launch_fwd_d<64>(p, st)
+                                                         : hipErrorInvalidValue;
+  timing_mark(2, st);
+  return e;
 }
 
 }  // namespace sas

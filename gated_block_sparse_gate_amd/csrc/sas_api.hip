@@ -11,6 +11,9 @@
 namespace {
 
 thread_local std::string g_err;
+constexpr int kMaxTimingEvents = 8;
+thread_local hipEvent_t g_ev[kMaxTimingEvents];
+thread_local int g_nev = 0;
 
 sas_status fail(sas_status st, const char* fmt, ...) {
   char buf[512];
@@ -147,9 +150,27 @@ sas_status check_decode_dims(const sas_decode_dims* d) {
 
 }  // namespace
 
+namespace sas {
+// Records the caller's timing event of stage boundary i (see
+// sas_set_timing_events) on stream st, if the hook is set.
+void timing_mark(int i, hipStream_t st) {
+  if (i < g_nev) (void)hipEventRecord(g_ev[i], st);
+}
+}  // namespace sas
+
 extern "C" {
 
 int sas_version(void) { return SAS_VERSION; }
+
+sas_status sas_set_timing_events(void* const* events, int n_events) {
+  if (n_events < 0 || n_events > kMaxTimingEvents || (n_events > 0 && !events))
+    return fail(SAS_ERR_INVALID, "n_events must be in [0, %d] with a non-null array",
+                kMaxTimingEvents);
+  g_nev = n_events;
+  for (int i = 0; i < n_events; ++i) g_ev[i] = static_cast<hipEvent_t>(events[i]);
+  g_err.clear();
+  return SAS_OK;
+}
 
 const char* sas_last_error(void) { return g_err.c_str(); }
 

@@ -35,6 +35,9 @@ struct TopkParams {
   int B, T, Hkv, dg, K, S, NB;
 };
 
+// Optional stage-boundary timing events (sas_set_timing_events).
+void timing_mark(int i, hipStream_t st);
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;

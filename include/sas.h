@@ -92,6 +92,19 @@ int sas_version(void);
 /* Message of the last failed call on this thread ("" if none). */
 const char* sas_last_error(void);
 
+/*
+ * Optional timing hook (instrumentation for profiling; no effect on results).
+ * events: n_events caller-created hipEvent_t handles (n_events <= 8), or
+ * NULL / 0 to switch the hook off.  While set (per thread), each following
+ * sas_sparse_attn_fwd / sas_sparse_attn_bwd call records events[i] on its
+ * stream at stage boundary i (boundaries beyond n_events are skipped):
+ *   fwd: 0 start, 1 after the V transpose, 2 after the attention kernel;
+ *   bwd: 0 start, 1 after Delta + the CSR build, 2 after dK/dV,
+ *        3 after the K transpose, 4 after dQ.
+ * The caller owns the events and keeps them alive while the hook is set.
+ */
+sas_status sas_set_timing_events(void* const* events, int n_events);
+
 /* Workspace bytes needed by op (SAS_OP_*) for dims d; 0 if none; (size_t)-1
  * if d is invalid. */
 size_t sas_workspace_size(int op, const sas_dims* d);
