@@ -613,8 +613,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       }
       const int tl = tl_row[ti];
       float lgv = 0.f;
+      int rank = 0;
       if (sel[ti]) {
-        const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
+        rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
         lgv = lgs[tl][rank];
       }
       const float bias = lgv - lse2[ti];
@@ -631,21 +632,26 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
           dsv[mt][i] = dsx;
           rs += dsx;
         }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      // dlogg: sum the G rows of each token of this tile
-      if (g4 == 0) red[wv][l16] = rs;
-      __builtin_amdgcn_wave_barrier();
-      if (g4 == 0 && l16 < TPT) {
-        const int tlr = (wv + NW * ti) * TPT + l16;
-        if (tlr < ntok && (bits[tlr][jw] & jbit)) {
-          float tot = 0.f;
-          for (int h = 0; h < G; ++h) tot += red[wv][l16 * G + h];
-          const int rank = pcnt[tlr][jw] + __popc(bits[tlr][jw] & (jbit - 1u));
-          a.dlogg[(rowbase + static_cast<size_t>(tlr) * a.Hkv) * S + slot_of[tlr][rank]] = tot;
+      rs = row4_sum(rs);
+      // dlogg: sum the G rows of each token of this tile (lanes G*k .. G*k+G-1)
+      if ((G & (G - 1)) == 0) {
+        const float tot = group_sum_pow2(rs, G);
+        if (g4 == 0 && sel[ti] && (l16 & (G - 1)) == 0)
+          a.dlogg[(rowbase + static_cast<size_t>(tl) * a.Hkv) * S + slot_of[tl][rank]] = tot;
+      } else {
+        if (g4 == 0) red[wv][l16] = rs;
+        __builtin_amdgcn_wave_barrier();
+        if (g4 == 0 && l16 < TPT) {
+          const int tlr = (wv + NW * ti) * TPT + l16;
+          if (tlr < ntok && (bits[tlr][jw] & jbit)) {
+            float tot = 0.f;
+            for (int h = 0; h < G; ++h) tot += red[wv][l16 * G + h];
+            const int rk = pcnt[tlr][jw] + __popc(bits[tlr][jw] & (jbit - 1u));
+            a.dlogg[(rowbase + static_cast<size_t>(tlr) * a.Hkv) * S + slot_of[tlr][rk]] = tot;
+          }
         }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
       uint4 dsb[2], dsl[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {

@@ -253,8 +253,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
         for (int mt = 0; mt < 4; ++mt)
           mr = fmaxf(mr, fmaxf(fmaxf(sacc[mt][0], sacc[mt][1]), fmaxf(sacc[mt][2], sacc[mt][3])));
       }
-      mr = fmaxf(mr, __shfl_xor(mr, 16, 64));
-      mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+      mr = row4_max(mr);
       const float cand = sel[ti] ? mr * sl2 + lgv : -INFINITY;
       const bool up = cand > m_run[ti] + kLazyLog2;
       if (ballot64(up)) {
@@ -323,9 +322,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
 #pragma unroll
   for (int ti = 0; ti < TW; ++ti) {
     if (!valid[ti]) continue;
-    float lsum = l_run[ti];
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    const float lsum = row4_sum(l_run[ti]);
     const int tl = tl_row[ti];
     const int hh = l16 - (l16 / G) * G;
     const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh;

@@ -133,6 +133,38 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Reductions over the four 16-lane rows of a wave, per position l = lane % 16
+// (the xor-16 and xor-32 butterflies), with the gfx950 row-swap permutes:
+// permlane16_swap(x, x) yields rows (r0, r0, r2, r2) and (r1, r1, r3, r3),
+// permlane32_swap(x, x) yields (r0, r1, r0, r1) and (r2, r3, r2, r3).  Pure
+// VALU (no LDS round trip); every lane ends with the same, order-fixed result.
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// DPP lane moves inside 16-lane rows (quad_perm / half-row mirror controls).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of n consecutive lanes, n in {1, 2, 4, 8}
+// (wave-uniform n): xor-1, xor-2, then the 8-lane mirror.
+__device__ __forceinline__ float group_sum_pow2(float x, int n) {
+  if (n >= 2) x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  if (n >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  if (n >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
+  return x;
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
