@@ -103,7 +103,7 @@ BwdWs bwd_ws(const sas_dims* d) {
   return w;
 }
 
-struct DecWs { size_t idx, logg, part, total; int nsplit; };
+struct DecWs { size_t idx, logg, part, score, total; int nsplit; };
 DecWs dec_ws(const sas_decode_dims* d) {
   const size_t S = d->topk + 1;
   const size_t G = d->Hq / d->Hkv;
@@ -112,7 +112,8 @@ DecWs dec_ws(const sas_decode_dims* d) {
   w.idx = 0;
   w.logg = align_up(w.idx + sizeof(int32_t) * d->B * d->Hkv * S);
   w.part = align_up(w.logg + sizeof(float) * d->B * d->Hkv * S);
-  w.total = align_up(w.part + sizeof(float) * d->B * d->Hkv * w.nsplit * G * (d->D + 2));
+  w.score = align_up(w.part + sizeof(float) * d->B * d->Hkv * w.nsplit * G * (d->D + 2));
+  w.total = align_up(w.score + sizeof(float) * d->B * d->Hkv * d->NBmax);
   return w;
 }
 
@@ -142,7 +143,8 @@ sas_status check_decode_dims(const sas_decode_dims* d) {
   if (d->NBmax != (d->Lmax + 63) / 64)
     return fail(SAS_ERR_INVALID, "NBmax must equal ceil(Lmax/64) (got %d, Lmax %d)", d->NBmax,
                 d->Lmax);
-  if (d->NBmax > 4096) return fail(SAS_ERR_UNSUPPORTED, "Lmax must be <= 262144");
+  if (d->NBmax > sas::kMaxDecodeNB)
+    return fail(SAS_ERR_UNSUPPORTED, "Lmax must be <= %d", sas::kMaxDecodeNB * 64);
   if (d->apply_gate != 0 && d->apply_gate != 1)
     return fail(SAS_ERR_INVALID, "apply_gate must be 0 or 1");
   return SAS_OK;
@@ -314,6 +316,7 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
   p.ws_idx = reinterpret_cast<int32_t*>(base + w.idx);
   p.ws_logg = reinterpret_cast<float*>(base + w.logg);
   p.ws_part = reinterpret_cast<float*>(base + w.part);
+  p.ws_score = reinterpret_cast<float*>(base + w.score);
   p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
   p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
   p.apply_gate = d->apply_gate; p.nsplit = w.nsplit;

@@ -9,7 +9,8 @@ namespace sas {
 
 constexpr int kMaxNB = 1024;            // T <= 65536
 constexpr int kMaxNBW = kMaxNB / 32;    // bitmap words per token
-constexpr int kMaxS = 64;               // topk <= 63
+constexpr int kMaxS = 64;
+constexpr int kMaxDecodeNB = 4096;      // decode: Lmax <= 262144               // topk <= 63
 
 struct RouterParams {
   const uint16_t* q;    // [B,T,Hq,D]
@@ -93,6 +94,7 @@ struct DecodeParams {
   int32_t* ws_idx;          // [B,Hkv,S]
   float* ws_logg;           // [B,Hkv,S]
   float* ws_part;           // [B,Hkv,NSPLIT,G,(D+2)] partial (m, l, o[D])
+  float* ws_score;          // [B,Hkv,NBmax] gate logits of the candidate blocks
   int B, Hq, Hkv, D, dg, G, K, S, Lmax, NBmax, apply_gate, nsplit;
   float scale_log2;
 };

@@ -135,18 +135,20 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
     if (!all) {
       // largest thr with count(key >= thr) >= K  ->  thr = K-th largest key;
       // counts by ballot + scalar popcount (no cross-lane data movement)
+      // kreg is 0 outside the historical candidates, and every candidate
+      // threshold is >= 1, so no validity test is needed in the counts
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = thr | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int e = 0; e < EMAX; ++e)
-          if (e < E) cnt += wave_count(lane + 64 * e < c && kreg[e] >= cand);
+          if (e < E) cnt += wave_count(kreg[e] >= cand);
         if (cnt >= K) thr = cand;
       }
       int gt = 0;
 #pragma unroll
       for (int e = 0; e < EMAX; ++e)
-        if (e < E) gt += wave_count(lane + 64 * e < c && kreg[e] > thr);
+        if (e < E) gt += wave_count(kreg[e] > thr);
       need_eq = K - gt;
     }
     int base = 0, eq_seen = 0;

@@ -236,6 +236,8 @@ DEC_CASES = [
     (3, 8, 2, 128, 128, 7, 5000, [5000, 1, 64]),
     (4, 8, 2, 128, 128, 31, 4200, [65, 4200, 2049, 128]),
     (2, 10, 2, 64, 32, 3, 700, [700, 300]),
+    # beyond 1,024 blocks (the selection's long-context path); one visible key
+    (2, 2, 1, 64, 32, 5, 70000, [70000, 4161]),
 ]
 
 
