@@ -306,6 +306,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
 #pragma unroll
   for (int sl = 0; sl < SPW; ++sl) {
     if (jsl[sl] < 0) continue;                       // uniform over the workgroup
+    // scores: 8-element partial dots with v_dot2_f32_bf16 (exact bf16
+    // products, fp32 accumulation), then summed over the row's lanes
     float sc[RPT][G];
 #pragma unroll
     for (int x = 0; x < RPT; ++x) {
@@ -315,10 +317,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
         const uint32_t qw[4] = {qr[h].x, qr[h].y, qr[h].z, qr[h].w};
         float a = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a = fmaf(__uint_as_float(qw[i] << 16), __uint_as_float(kw[i] << 16), a);
-          a = fmaf(__uint_as_float(qw[i] & 0xffff0000u), __uint_as_float(kw[i] & 0xffff0000u), a);
-        }
+        for (int i = 0; i < 4; ++i) a = dot2_bf16(qw[i], kw[i], a);
         sc[x][h] = lane_group_sum<CPR>(a);
       }
       const int tok = 64 * jsl[sl] + rg + RPP * x;
@@ -326,6 +325,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
       for (int h = 0; h < G; ++h)
         sc[x][h] = (tok < L) ? fmaf(sc[x][h], sl2, lgl[sl]) : -INFINITY;
     }
+    // online softmax per head (state shared by the wave)
+    float pv[RPT][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = sc[0][h];
@@ -339,25 +340,30 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
       const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[h] - msafe);   // 0 while m_run is -inf
       float ps = 0.f;
-      float pv[RPT];
 #pragma unroll
       for (int x = 0; x < RPT; ++x) {
-        pv[x] = fast_exp2(sc[x][h] - msafe);
-        ps += pv[x];
+        pv[x][h] = fast_exp2(sc[x][h] - msafe);
+        ps += pv[x][h];
       }
       l_run[h] = l_run[h] * alpha + ps;
 #pragma unroll
       for (int e = 0; e < 8; ++e) oacc[h][e] *= alpha;
-#pragma unroll
-      for (int x = 0; x < RPT; ++x) {
-        const uint32_t vw[4] = {vr[sl][x].x, vr[sl][x].y, vr[sl][x].z, vr[sl][x].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          oacc[h][2 * i] = fmaf(pv[x], __uint_as_float(vw[i] << 16), oacc[h][2 * i]);
-          oacc[h][2 * i + 1] = fmaf(pv[x], __uint_as_float(vw[i] & 0xffff0000u), oacc[h][2 * i + 1]);
-        }
-      }
       m_run[h] = m_new;
+    }
+    // O += P V: each V row chunk converted once, used by every head
+#pragma unroll
+    for (int x = 0; x < RPT; ++x) {
+      const uint32_t vw[4] = {vr[sl][x].x, vr[sl][x].y, vr[sl][x].z, vr[sl][x].w};
+      float vf[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[2 * i] = __uint_as_float(vw[i] << 16);
+        vf[2 * i + 1] = __uint_as_float(vw[i] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[h][e] = fmaf(pv[x][h], vf[e], oacc[h][e]);
     }
   }
   // wave totals: sum over the wave's row groups (lanes with equal ch)

@@ -98,6 +98,14 @@ __device__ __forceinline__ void st16(void* p, uint4 v) {
   *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
 }
 
+// a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs (v_dot2_f32_bf16:
+// exact bf16 products, fp32 accumulation).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // C[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.
