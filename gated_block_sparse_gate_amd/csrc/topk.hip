@@ -11,9 +11,11 @@
 //
 // One workgroup = 16 consecutive tokens of one (batch, KV head); all 16 share
 // the same block c, so the historical block keys form one fp32 tile product
-// (LDS tiled, plain fp32 FMA: index parity needs fp32-accurate scores).
+// (fp32 MFMA: index parity needs fp32-accurate scores).
 // Selection: exact K-th largest order key by a 32-step bitwise search with
 // wave-wide counts, then equal keys taken in ascending block order.
+#include <type_traits>
+
 #include "sas_kernels.h"
 
 namespace sas {
@@ -22,177 +24,201 @@ namespace {
 
 constexpr int kTokPerWG = 16;
 
+// 16x16x4 fp32 MFMA: lane l holds A[l%16][l/16] and B[l/16][l%16]; C column
+// l%16 holds rows 4*(l/16) .. +4.
+__device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int DG>
 __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
-  constexpr int KCH = 64;            // block keys per LDS chunk
-  constexpr int KPITCH = DG + 4;
+  constexpr int KCH = 64;            // block keys per chunk (16 per wave)
+  constexpr int KP = DG + 4;         // LDS pitch (floats) of a staged key
+  constexpr int NS = DG / 16;        // 16-wide d groups
+  constexpr int KU = KCH * DG / 4 / 256;   // float4 per thread per chunk
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  float* qs = smem;                            // [16][DG]
-  float* ks = qs + kTokPerWG * DG;             // [64][KPITCH]
-  float* sc = ks + KCH * KPITCH;               // [16][NBP]
+  float* ks = smem;                            // [64][KP]
+  float* sc = ks + KCH * KP;                   // [16][NBP]
   const int NBP = ((p.NB + 3) / 4) * 4;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
   const int kv = blockIdx.y, b = blockIdx.z;
   const int t0 = blockIdx.x * kTokPerWG;
   const int c = t0 / 64;
   const int ntok = min(kTokPerWG, p.T - t0);
   const float inv_sqrt_dg = 1.0f / sqrtf(static_cast<float>(DG));
 
-  for (int e = tid; e < kTokPerWG * DG; e += 256) {
-    const int tl = e / DG, d = e - tl * DG;
-    qs[e] = (tl < ntok)
-                ? p.q_gate[((static_cast<size_t>(b) * p.T + t0 + tl) * p.Hkv + kv) * DG + d]
-                : 0.f;
+  // historical scores S^T[key, token] = K Q^T on fp32 MFMA 16x16x4; the k
+  // index of MFMA step (s, i) is d = 16 s + 4 (lane / 16) + i, the same for
+  // both operands.  Query operand (token = lane % 16) in registers.
+  float qb[NS][4];
+  {
+    const float* qrow =
+        p.q_gate + ((static_cast<size_t>(b) * p.T + t0 + min(l16, ntok - 1)) * p.Hkv + kv) * DG;
+#pragma unroll
+    for (int sg = 0; sg < NS; ++sg) {
+      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * sg + 4 * g4);
+      qb[sg][0] = v.x; qb[sg][1] = v.y; qb[sg][2] = v.z; qb[sg][3] = v.w;
+    }
   }
-
-  // historical scores: thread -> (token tl = tid/16, keys 4*kq .. 4*kq+3)
-  const int tl_s = tid >> 4, kq = tid & 15;
+  // block keys k_gate[64 j + 63], staged per 64-key chunk through registers
+  // (the next chunk's loads are in flight while the current one is used)
+  float4 kst[KU];
+  auto kload = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < KU; ++x) {
+      const int u = tid + 256 * x;
+      const int r = u / (DG / 4), f = u - r * (DG / 4);
+      const int j = j0 + r;
+      kst[x] = (j < c) ? *reinterpret_cast<const float4*>(
+                             p.k_gate + ((static_cast<size_t>(b) * p.T + 64 * j + 63) * p.Hkv + kv) * DG + 4 * f)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (c > 0) kload(0);
   for (int j0 = 0; j0 < c; j0 += KCH) {
     __syncthreads();
-    for (int e = tid; e < KCH * (DG / 4); e += 256) {
-      const int jj = e / (DG / 4), d4 = e - jj * (DG / 4);
-      const int j = j0 + jj;
-      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < c)
-        val = *reinterpret_cast<const float4*>(
-            p.k_gate + ((static_cast<size_t>(b) * p.T + j * 64 + 63) * p.Hkv + kv) * DG + d4 * 4);
-      *reinterpret_cast<float4*>(&ks[jj * KPITCH + d4 * 4]) = val;
+#pragma unroll
+    for (int x = 0; x < KU; ++x) {
+      const int u = tid + 256 * x;
+      const int r = u / (DG / 4), f = u - r * (DG / 4);
+      *reinterpret_cast<float4*>(&ks[r * KP + 4 * f]) = kst[x];
     }
     __syncthreads();
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* qrow = &qs[tl_s * DG];
-#pragma unroll 4
-    for (int d = 0; d < DG; d += 4) {
-      const float4 qv = *reinterpret_cast<const float4*>(qrow + d);
+    if (j0 + KCH < c) kload(j0 + KCH);
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    const float* krow = &ks[(16 * wv + l16) * KP + 4 * g4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 kvv = *reinterpret_cast<const float4*>(&ks[(kq * 4 + e) * KPITCH + d]);
-        acc[e] = fmaf(qv.x, kvv.x, acc[e]);
-        acc[e] = fmaf(qv.y, kvv.y, acc[e]);
-        acc[e] = fmaf(qv.z, kvv.z, acc[e]);
-        acc[e] = fmaf(qv.w, kvv.w, acc[e]);
-      }
+    for (int sg = 0; sg < NS; ++sg) {
+      const float4 a = *reinterpret_cast<const float4*>(krow + 16 * sg);
+      acc = mfma16x16x4f32(a.x, qb[sg][0], acc);
+      acc = mfma16x16x4f32(a.y, qb[sg][1], acc);
+      acc = mfma16x16x4f32(a.z, qb[sg][2], acc);
+      acc = mfma16x16x4f32(a.w, qb[sg][3], acc);
     }
+    const int jb = j0 + 16 * wv + 4 * g4;     // keys jb .. jb+3 of token l16
+    if (l16 < ntok) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = j0 + kq * 4 + e;
-      if (j < c) sc[tl_s * NBP + j] = acc[e] * inv_sqrt_dg;
+      for (int i = 0; i < 4; ++i)
+        if (jb + i < c) sc[l16 * NBP + jb + i] = acc[i] * inv_sqrt_dg;
     }
   }
   __syncthreads();
   // current-block score with the token's own prefix key
   {
-    const int part = tid & 15;
+    const int tl_s = tid >> 4, part = tid & 15;
     float acc = 0.f;
     if (tl_s < ntok) {
-      const float* kg = p.k_gate + ((static_cast<size_t>(b) * p.T + t0 + tl_s) * p.Hkv + kv) * DG;
-      for (int d = part; d < DG; d += 16) acc = fmaf(qs[tl_s * DG + d], kg[d], acc);
+      const size_t rw = (static_cast<size_t>(b) * p.T + t0 + tl_s) * p.Hkv + kv;
+      const float* kg = p.k_gate + rw * DG;
+      const float* qg = p.q_gate + rw * DG;
+      for (int d = part; d < DG; d += 16) acc = fmaf(qg[d], kg[d], acc);
     }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    acc += __shfl_xor(acc, 8, 64);
-    if (part == 0) sc[tl_s * NBP + c] = acc * inv_sqrt_dg;
+    acc += dpp_mov<0xB1>(acc);
+    acc += dpp_mov<0x4E>(acc);
+    acc += dpp_mov<0x141>(acc);
+    acc += dpp_mov<0x140>(acc);
+    if (part == 0 && tl_s < ntok) sc[tl_s * NBP + c] = acc * inv_sqrt_dg;
   }
   __syncthreads();
 
-  // per token row: logsumexp, selection, ascending compaction
+  // per token row (one wave per row): log-sum-exp, selection, ascending
+  // compaction.  All rows of the workgroup share c, so the register count of
+  // the order keys is chosen once per workgroup (no per-step branches).
   const int K = p.K, S = p.S;
   const int ncand = c + 1;
   const int E = (ncand + 63) / 64;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int tl = wv; tl < ntok; tl += 4) {
-    const float* row = &sc[tl * NBP];
-    float mx = -INFINITY;
-    for (int e = 0; e < E; ++e) {
-      const int j = lane + 64 * e;
-      if (j < ncand) mx = fmaxf(mx, row[j]);
-    }
-    mx = wave_max(mx);
-    float se = 0.f;
-    for (int e = 0; e < E; ++e) {
-      const int j = lane + 64 * e;
-      if (j < ncand) se += expf(row[j] - mx);
-    }
-    se = wave_sum(se);
-    const float lse = mx + logf(se);
-    const size_t rowid = (static_cast<size_t>(b) * p.T + t0 + tl) * p.Hkv + kv;
-
-    const int nsel = min(K, c);
-    // order keys of the historical candidates, held in registers
-    constexpr int EMAX = kMaxNB / 64;
-    uint32_t kreg[EMAX];
+  const int nsel = min(K, c);
+  const bool all = (c <= K);
+  auto rows = [&](auto emc) __attribute__((always_inline)) {
+    constexpr int EM = decltype(emc)::value;
+    for (int tl = wv; tl < ntok; tl += 4) {
+      const float* row = &sc[tl * NBP];
+      float sv[EM];
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      const int j = lane + 64 * e;
-      kreg[e] = (e < E && j < c) ? order_key(row[j]) : 0u;
-    }
-    uint32_t thr = 0;
-    int need_eq = 0;
-    const bool all = (c <= K);
-    if (!all) {
-      // largest thr with count(key >= thr) >= K  ->  thr = K-th largest key;
-      // counts by ballot + scalar popcount (no cross-lane data movement)
-      // kreg is 0 outside the historical candidates, and every candidate
-      // threshold is >= 1, so no validity test is needed in the counts
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int e = 0; e < EMAX; ++e)
-          if (e < E) cnt += wave_count(kreg[e] >= cand);
-        if (cnt >= K) thr = cand;
+      for (int e = 0; e < EM; ++e) {
+        const int j = lane + 64 * e;
+        sv[e] = (j < ncand) ? row[j] : -INFINITY;
       }
-      int gt = 0;
+      float mx = sv[0];
 #pragma unroll
-      for (int e = 0; e < EMAX; ++e)
-        if (e < E) gt += wave_count(kreg[e] > thr);
-      need_eq = K - gt;
-    }
-    int base = 0, eq_seen = 0;
+      for (int e = 1; e < EM; ++e) mx = fmaxf(mx, sv[e]);
+      mx = wave_max(mx);
+      float se = 0.f;
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (e >= E) break;
-      const int j = lane + 64 * e;
-      const bool hist = j < c;
-      const bool gt = hist && !all && kreg[e] > thr;
-      const bool eq = hist && !all && kreg[e] == thr;
-      const uint64_t em = ballot64(eq);
-      const bool s_in =
-          hist && (all || gt || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
-      eq_seen += __popcll(em);
-      const uint64_t sm = ballot64(s_in);
-      if (s_in) {
-        const int pos = base + __popcll(sm & lt_mask);
-        p.idx[rowid * S + pos] = j;
-        p.logg[rowid * S + pos] = row[j] - lse;
+      for (int e = 0; e < EM; ++e) se += expf(sv[e] - mx);
+      se = wave_sum(se);
+      const float lse = mx + logf(se);
+      const size_t rowid = (static_cast<size_t>(b) * p.T + t0 + tl) * p.Hkv + kv;
+      // order keys of the historical candidates; 0 elsewhere, which no
+      // candidate threshold (always >= 1) reaches
+      uint32_t kreg[EM];
+#pragma unroll
+      for (int e = 0; e < EM; ++e) kreg[e] = (lane + 64 * e < c) ? order_key(sv[e]) : 0u;
+      uint32_t thr = 0;
+      int need_eq = 0;
+      if (!all) {
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = thr | (1u << bit);
+          int cnt = 0;
+#pragma unroll
+          for (int e = 0; e < EM; ++e) cnt += wave_count(kreg[e] >= cand);
+          if (cnt >= K) thr = cand;
+        }
+        int gt = 0;
+#pragma unroll
+        for (int e = 0; e < EM; ++e) gt += wave_count(kreg[e] > thr);
+        need_eq = K - gt;
       }
-      base += __popcll(sm);
+      int base = 0, eq_seen = 0;
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        const int j = lane + 64 * e;
+        const bool hist = j < c;
+        const bool gt = hist && !all && kreg[e] > thr;
+        const bool eq = hist && !all && kreg[e] == thr;
+        const uint64_t em = ballot64(eq);
+        const bool s_in =
+            hist && (all || gt || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
+        eq_seen += __popcll(em);
+        const uint64_t sm = ballot64(s_in);
+        if (s_in) {
+          const int pos = base + __popcll(sm & lt_mask);
+          p.idx[rowid * S + pos] = j;
+          p.logg[rowid * S + pos] = sv[e] - lse;
+        }
+        base += __popcll(sm);
+      }
+      if (lane == 0) {
+        p.idx[rowid * S + nsel] = c;
+        p.logg[rowid * S + nsel] = row[c] - lse;
+        p.gate_lse[rowid] = lse;
+      }
+      for (int s2 = nsel + 1 + lane; s2 < S; s2 += 64) {
+        p.idx[rowid * S + s2] = -1;
+        p.logg[rowid * S + s2] = -INFINITY;
+      }
+      if (p.gate_probs) {
+        for (int j = lane; j < p.NB; j += 64)
+          p.gate_probs[rowid * p.NB + j] = (j <= c) ? expf(row[j] - lse) : 0.f;
+      }
     }
-    if (lane == 0) {
-      p.idx[rowid * S + nsel] = c;
-      p.logg[rowid * S + nsel] = row[c] - lse;
-      p.gate_lse[rowid] = lse;
-    }
-    for (int s2 = nsel + 1 + lane; s2 < S; s2 += 64) {
-      p.idx[rowid * S + s2] = -1;
-      p.logg[rowid * S + s2] = -INFINITY;
-    }
-    if (p.gate_probs) {
-      for (int j = lane; j < p.NB; j += 64)
-        p.gate_probs[rowid * p.NB + j] = (j <= c) ? expf(row[j] - lse) : 0.f;
-    }
-  }
+  };
+  if (E <= 1) rows(std::integral_constant<int, 1>{});
+  else if (E <= 2) rows(std::integral_constant<int, 2>{});
+  else if (E <= 4) rows(std::integral_constant<int, 4>{});
+  else if (E <= 8) rows(std::integral_constant<int, 8>{});
+  else rows(std::integral_constant<int, kMaxNB / 64>{});
 }
 
 }  // namespace
 
 size_t topk_smem_bytes(int NB, int dg) {
   const int NBP = ((NB + 3) / 4) * 4;
-  return sizeof(float) * (static_cast<size_t>(kTokPerWG) * dg + 64 * (dg + 4) +
-                          static_cast<size_t>(kTokPerWG) * NBP);
+  return sizeof(float) * (64 * (dg + 4) + static_cast<size_t>(kTokPerWG) * NBP);
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
