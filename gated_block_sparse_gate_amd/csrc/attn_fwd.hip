@@ -25,10 +25,11 @@ namespace sas {
 
 namespace {
 
-// HILO: P enters the PV product as bf16 hi + lo parts (exact to ~2^-16);
-// used when the fp32 output is requested for the backward's Delta.
 constexpr float kLazyLog2 = 8.f;   // weights stay below 2^8 between rescales
 
+// HILO (the fp32 output is requested, for the backward's Delta): V^T is the
+// bf16 copy and P enters PV as bf16 hi + lo parts (exact to ~2^-16).
+// Otherwise V^T is the scaled fp16 copy and P enters once, in fp16.
 template <int D, int NW, int TW, bool HILO>
 __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   constexpr int NT = NW * 64;
@@ -294,10 +295,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
           split_bf2(x[2 * k2 + 1][0], x[2 * k2 + 1][1], pb[k2].z, pl[k2].z);
           split_bf2(x[2 * k2 + 1][2], x[2 * k2 + 1][3], pb[k2].w, pl[k2].w);
         } else {
-          pb[k2].x = pack_bf2(x[2 * k2][0], x[2 * k2][1]);
-          pb[k2].y = pack_bf2(x[2 * k2][2], x[2 * k2][3]);
-          pb[k2].z = pack_bf2(x[2 * k2 + 1][0], x[2 * k2 + 1][1]);
-          pb[k2].w = pack_bf2(x[2 * k2 + 1][2], x[2 * k2 + 1][3]);
+          // fp16 (P <= 2^kLazyLog2, 11-bit significand) against the fp16 V^T
+          pb[k2].x = pack_h2(x[2 * k2][0], x[2 * k2][1]);
+          pb[k2].y = pack_h2(x[2 * k2][2], x[2 * k2][3]);
+          pb[k2].z = pack_h2(x[2 * k2 + 1][0], x[2 * k2 + 1][1]);
+          pb[k2].w = pack_h2(x[2 * k2 + 1][2], x[2 * k2 + 1][3]);
         }
       }
       // O^T[d, row] += V^T[d, keys] . P^T[keys, row]; inside a 32-key step the
@@ -308,8 +310,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           const uint4 va = *reinterpret_cast<const uint4*>(st + dt * 2048 + vofs[k2]);
-          oacc[ti][dt] = mfma16x16x32(va, pb[k2], oacc[ti][dt]);
-          if (HILO) oacc[ti][dt] = mfma16x16x32(va, pl[k2], oacc[ti][dt]);
+          if (HILO) {
+            oacc[ti][dt] = mfma16x16x32(va, pb[k2], oacc[ti][dt]);
+            oacc[ti][dt] = mfma16x16x32(va, pl[k2], oacc[ti][dt]);
+          } else {
+            oacc[ti][dt] = mfma16x16x32h(va, pb[k2], oacc[ti][dt]);
+          }
         }
       }
     }
@@ -319,6 +325,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   }
 
   // ---- epilogue
+  const float vsc = HILO ? 1.f : a.vscale[static_cast<size_t>(b) * a.Hkv + kv];
 #pragma unroll
   for (int ti = 0; ti < TW; ++ti) {
     if (!valid[ti]) continue;
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
     const int tl = tl_row[ti];
     const int hh = l16 - (l16 / G) * G;
     const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh;
-    const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+    const float inv = (lsum > 0.f) ? vsc / lsum : 0.f;   // vsc undoes the V^T scaling
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 pk;
@@ -350,12 +357,11 @@ hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
   // up to 16 row tiles: one tile per wave, 16 waves (4 per SIMD hide the
   // latency of the per-tile MFMA -> softmax -> MFMA chain); more tiles
   // (G >= 5): 8 waves with TW tiles each.
-  const int tw = (p.ntiles + 7) / 8;
   if (p.ntiles <= 16) {
     hipLaunchKernelGGL((sparse_fwd_kernel<D, 16, 1, HILO>), grid, dim3(1024), 0, st, p);
     return hipGetLastError();
   }
-  switch (tw) {
+  switch ((p.ntiles + 7) / 8) {
     case 3: hipLaunchKernelGGL((sparse_fwd_kernel<D, 8, 3, HILO>), grid, dim3(512), 0, st, p); break;
     case 4: hipLaunchKernelGGL((sparse_fwd_kernel<D, 8, 4, HILO>), grid, dim3(512), 0, st, p); break;
     default: return hipErrorInvalidValue;
@@ -372,7 +378,10 @@ hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
 
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st) {
   timing_mark(0, st);
-  hipError_t e = launch_transpose_tokens(p.v, p.vt, p.B, p.T, p.Hkv, p.D, st);
+  // V^T: bf16 for the hi/lo product (fp32 output requested), else scaled fp16
+  hipError_t e = p.o32 ? launch_transpose_tokens(p.v, p.vt, p.B, p.T, p.Hkv, p.D, st)
+                       : launch_transpose_tokens_f16(p.v, p.vt, p.vamax, p.vscale, p.B, p.T,
+                                                     p.Hkv, p.D, st);
   if (e != hipSuccess) return e;
   timing_mark(1, st);
   e = p.D == 128 ? launch_fwd_d<128>(p, st) : p.D == 64 ? launch_fwd_d<64>(p, st)

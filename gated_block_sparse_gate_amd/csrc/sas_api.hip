@@ -84,10 +84,17 @@ GateWs gate_ws(const sas_dims* d) {
   return w;
 }
 
-size_t fwd_ws(const sas_dims* d) {
-  const size_t Tp = static_cast<size_t>((d->T + 63) / 64) * 64;
-  return align_up(sizeof(uint16_t) * d->B * d->Hkv * d->D * Tp);
+struct FwdWs { size_t vt, amax, vscale, total; };
+FwdWs fwd_ws_layout(const sas_dims* d) {
+  const size_t NB = (d->T + 63) / 64;
+  FwdWs w;
+  w.vt = 0;
+  w.amax = align_up(sizeof(uint16_t) * d->B * d->Hkv * d->D * NB * 64);
+  w.vscale = align_up(w.amax + sizeof(float) * d->B * d->Hkv * NB);
+  w.total = align_up(w.vscale + sizeof(float) * d->B * d->Hkv);
+  return w;
 }
+size_t fwd_ws(const sas_dims* d) { return fwd_ws_layout(d).total; }
 
 struct BwdWs { size_t delta, cnt2d, rowptr, entries, kt, total; };
 BwdWs bwd_ws(const sas_dims* d) {
@@ -247,7 +254,10 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
   if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
   if ((st = check_ws(ws, ws_bytes, fwd_ws(d)))) return st;
   sas::FwdParams p{};
-  p.vt = static_cast<uint16_t*>(ws);
+  const FwdWs fw = fwd_ws_layout(d);
+  p.vt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fw.vt);
+  p.vamax = reinterpret_cast<float*>(static_cast<char*>(ws) + fw.amax);
+  p.vscale = reinterpret_cast<float*>(static_cast<char*>(ws) + fw.vscale);
   p.q = q; p.k = k; p.v = v; p.idx = idx; p.logg = logg; p.o = o; p.lse = lse; p.o32 = o_f32;
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;

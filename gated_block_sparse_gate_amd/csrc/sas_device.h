@@ -108,6 +108,22 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+// Two fp32 -> packed fp16 pair (low = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const h2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// C[16x16] += A[16x32] * B[32x16], fp16 inputs, fp32 accumulate (same lane
+// layout as the bf16 form below).
+__device__ __forceinline__ floatx4 mfma16x16x32h(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
+                                                __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+
 // C[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.
 // Lane l: A row l%16 / B column l%16 holds k = 8*(l/16) .. +8;
 // C column l%16 holds rows 4*(l/16) .. +4.

@@ -48,7 +48,9 @@ struct FwdParams {
   uint16_t* o;
   float* lse;
   float* o32;   // optional fp32 copy of o (null = skip)
-  uint16_t* vt; // workspace: V^T [B,Hkv,D,64*NB]
+  uint16_t* vt; // workspace: V^T [B,Hkv,D,64*NB] in fp16, scaled by 1/vscale
+  float* vamax; // workspace: [B,Hkv,NB] max |v| per 64-token block
+  float* vscale;// workspace: [B,Hkv] power of two restoring the V^T scaling
   int B, T, Hq, Hkv, D, G, S, NB;
   int TPT;      // tokens per 16-row tile = floor(16 / G)
   int ntiles;   // tiles per 64-token query block = ceil(64 / TPT)
@@ -107,6 +109,12 @@ hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st);
 // src [B,T,H,D] -> dst [B,H,D,64*ceil(T/64)] (zero tail)
 hipError_t launch_transpose_tokens(const uint16_t* src, uint16_t* dst, int B, int T, int H, int D,
                                    hipStream_t st);
+// src [B,T,H,D] bf16 -> dst [B,H,D,64*ceil(T/64)] fp16 of src * 2^-e(b,h), with
+// e(b,h) >= 0 the least exponent bringing max |src| of the head within
+// 32768 (exact scaling); scale_out[b,h] = 2^e.  amax: [B,H,NB] workspace.
+hipError_t launch_transpose_tokens_f16(const uint16_t* src, uint16_t* dst, float* amax,
+                                       float* scale_out, int B, int T, int H, int D,
+                                       hipStream_t st);
 hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 

@@ -175,7 +175,11 @@ sas_status sas_topk_blocks(const sas_dims* d, const float* q_gate, const float* 
  *   o_f32 [B,T,Hq,D] fp32 optional output (NULL = not written): the same
  *   result before bf16 rounding, for the backward's Delta.
  *   ws: sas_workspace_size(SAS_OP_FWD, d) bytes (holds a transposed copy of
- *   v, [B,Hkv,D,64*ceil(T/64)] bf16, rebuilt on every call).
+ *   v, [B,Hkv,D,64*ceil(T/64)], rebuilt on every call, plus per-block maxima
+ *   and per-head scales).  With o_f32 requested, the copy is bf16 and the
+ *   softmax weights P enter the PV product as bf16 hi + lo parts (o_f32 exact
+ *   to ~2^-16); otherwise the copy is fp16, scaled per (b, KV head) by a power
+ *   of two that keeps it finite, and P enters once in fp16 (2^-11 relative).
  *   Deterministic (bitwise repeatable).
  */
 sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,

@@ -98,7 +98,8 @@ def test_workspace_checks():
     d = _dims(T=4096)
     need = sas.workspace_size(sas.OP_BWD, d)
     assert need > 0
-    assert sas.workspace_size(sas.OP_FWD, d) == 1 * 2 * 128 * 4096 * 2   # transposed v
+    # fp16 transposed v, per-block |v| maxima (64 blocks), per-head scales; 256-byte aligned
+    assert sas.workspace_size(sas.OP_FWD, d) == 1 * 2 * 128 * 4096 * 2 + 512 + 256
     assert sas.workspace_size(sas.OP_TOPK, d) == 0
     p = ctypes.c_void_p(4096)
     args = [p] * 9 + [ctypes.c_float(0.1)] + [p] * 4

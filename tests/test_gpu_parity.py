@@ -164,6 +164,22 @@ def test_sparse_attn_fwd(w):
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "forward not bitwise repeatable"
 
 
+@pytest.mark.parametrize("w", CASES[:2], ids=IDS[:2])
+def test_sparse_attn_fwd_large_values(w):
+    """v scaled by 2^17 (exact in bf16, beyond the fp16 range of the transposed
+    copy): the output scales exactly, so o / 2^17 must match the oracle's o."""
+    P = prepared(w)
+    d = P["dev"]
+    idx, logg = _oracle_sel(P)
+    big = float(2 ** 17)
+    o, lse, o32 = sas.sparse_attn_fwd(d["q"], d["k"], (d["v"].float() * big).to(torch.bfloat16),
+                                      idx, logg, P["scale"], want_f32=True)
+    torch.cuda.synchronize()
+    assert_close("o/2^17", (o.float() / big).to(torch.bfloat16), P["g"]["o"])
+    assert_close("o_f32/2^17", o32 / big, P["g"]["o"])
+    assert_close("lse", lse, P["g"]["lse"], 1e-3, 1e-4)
+
+
 @pytest.mark.parametrize("use_f32", [False, True], ids=["o_bf16", "o_f32"])
 @pytest.mark.parametrize("w", CASES, ids=IDS)
 def test_sparse_attn_bwd(w, use_f32):
