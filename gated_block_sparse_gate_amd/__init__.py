@@ -20,6 +20,7 @@ __all__ = [
     "Dims", "DecodeDims", "SasError", "load_library", "version", "workspace_size",
     "decode_workspace_size", "gate_score", "topk_blocks", "sparse_attn_fwd",
     "sparse_attn_bwd", "decode", "budget_to_topk", "EXPORTED_SYMBOLS", "set_timing_events",
+    "take_device_fault",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +32,7 @@ OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD = range(4)
 EXPORTED_SYMBOLS = (
     "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
     "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
-    "sas_decode", "sas_set_timing_events",
+    "sas_decode", "sas_set_timing_events", "sas_take_device_fault",
 )
 
 
@@ -83,8 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sas_decode.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 6 + [F32] + [P] * 3
                                + [P, S, P])
     lib.sas_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
+    lib.sas_take_device_fault.argtypes = [ctypes.POINTER(ctypes.c_uint)]
     for fn in ("sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd",
-               "sas_sparse_attn_bwd", "sas_decode", "sas_set_timing_events"):
+               "sas_sparse_attn_bwd", "sas_decode", "sas_set_timing_events",
+               "sas_take_device_fault"):
         getattr(lib, fn).restype = I32
     _lib = lib
     return lib
@@ -132,6 +135,14 @@ def set_timing_events(events=None):
         handles.append(e.cuda_event)
     arr = (ctypes.c_void_p * len(handles))(*handles)
     _check(lib.sas_set_timing_events(arr, len(handles)))
+
+
+def take_device_fault() -> int:
+    """Read and clear the attention kernels' fault flag (see
+    sas_take_device_fault in sas.h); 0 means no fault.  Synchronises."""
+    v = ctypes.c_uint(0)
+    _check(load_library().sas_take_device_fault(ctypes.byref(v)))
+    return v.value
 
 
 def budget_to_topk(budget: int, block: int = 64) -> int:

@@ -390,28 +390,34 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dQ, dlogg
-template <int D, int NW, int TW>
+template <int D, int NW, int TW, int R>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   constexpr int NT = NW * 64;
   constexpr int KROWB = D * 2;              // bytes per K / V row
   constexpr int KB = 64 * KROWB;            // one tile (K, V or K^T) in bytes
-  constexpr int STAGE = 3 * KB;             // K | V | K^T
+  constexpr int STAGE = 2 * KB;             // K | V
   constexpr int TU = KB / 16;               // 16-byte units per tile
-  constexpr int UPT = 3 * TU / NT;         // units per thread per block
+  constexpr int UPT = 2 * TU / NT;         // units per thread per block
   constexpr int KCPR = KROWB / 16;
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  static_assert(3 * TU % NT == 0, "unit split");
+  static_assert(2 * TU % NT == 0, "unit split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t ring[2][STAGE];
-  __shared__ uint32_t bits[64][kMaxNBW];
-  __shared__ uint8_t pcnt[64][kMaxNBW];
-  __shared__ uint32_t ubits[kMaxNBW];
-  __shared__ uint16_t ulist[kMaxNB];
-  __shared__ float lgs[64][kMaxS];
-  __shared__ uint8_t slot_of[64][kMaxS];
-  __shared__ float red[NW][16];
-  __shared__ int s_nU;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int NBW = (a.NB + 31) >> 5;
+  const int S = a.S;
+  const WalkLds L = walk_lds(R, STAGE, a.NB, S, NW, true);
+  uint8_t* const ring = smem + L.ring;                      // slot sl at ring + sl * STAGE
+  uint32_t* const bits = reinterpret_cast<uint32_t*>(smem + L.bits);   // [64][NBW]
+  uint8_t* const pcnt = smem + L.pcnt;                      // [64][NBW]
+  uint32_t* const ubits = reinterpret_cast<uint32_t*>(smem + L.ubits);
+  uint16_t* const ulist = reinterpret_cast<uint16_t*>(smem + L.ulist);
+  float* const lgs = reinterpret_cast<float*>(smem + L.lgs);          // [64][S]
+  uint8_t* const slot_of = smem + L.slot;                   // [64][S]
+  float* const red = reinterpret_cast<float*>(smem + L.red);          // [NW][16]
+  unsigned* const fill_cnt = reinterpret_cast<unsigned*>(smem + L.cnt);
+  unsigned* const done_cnt = fill_cnt + R;
+  int* const s_nU = reinterpret_cast<int*>(smem + L.nu);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -427,12 +433,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   const int b = rest / NQB;
   const int t0 = c * 64;
   const int ntok = min(64, a.T - t0);
-  const int NBW = (a.NB + 31) >> 5;
-  const int S = a.S;
-  const int Tp = a.NB * 64;
 
-  for (int i = tid; i < 64 * kMaxNBW; i += NT) (&bits[0][0])[i] = 0u;
-  if (tid < kMaxNBW) ubits[tid] = 0u;
+  for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
+  if (tid < NBW) ubits[tid] = 0u;
+  if (tid < 2 * R) fill_cnt[tid] = 0u;          // fill and done counters
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
   for (int e = tid; e < ntok * S; e += NT) {
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
     if (j >= 0 && j <= c) {
-      atomicOr(&bits[tl][j >> 5], 1u << (j & 31));
+      atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
       atomicOr(&ubits[j >> 5], 1u << (j & 31));
     } else {
       a.dlogg[off] = 0.f;     // padding / ignored slot
@@ -450,8 +454,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   if (tid < 64) {
     int run = 0;
     for (int w = 0; w < NBW; ++w) {
-      pcnt[tid][w] = static_cast<uint8_t>(run);
-      run += __popc(bits[tid][w]);
+      pcnt[tid * NBW + w] = static_cast<uint8_t>(run);
+      run += __popc(bits[tid * NBW + w]);
     }
   }
   __syncthreads();
@@ -460,10 +464,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
     if (j >= 0 && j <= c) {
-      const int rank = pcnt[tl][j >> 5] + __popc(bits[tl][j >> 5] & ((1u << (j & 31)) - 1u));
-      if (rank < kMaxS) {
-        lgs[tl][rank] = a.logg[off] * kLog2e;
-        slot_of[tl][rank] = static_cast<uint8_t>(s);
+      const int rank = pcnt[tl * NBW + (j >> 5)] + __popc(bits[tl * NBW + (j >> 5)] & ((1u << (j & 31)) - 1u));
+      if (rank < S) {
+        lgs[tl * S + rank] = a.logg[off] * kLog2e;
+        slot_of[tl * S + rank] = static_cast<uint8_t>(s);
       }
     }
   }
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       }
       base += __shfl(incl, 63, 64);
     }
-    if (lane == 0) s_nU = base;
+    if (lane == 0) *s_nU = base;
   }
 
   const int G = a.G, TPT = a.TPT;
@@ -516,74 +520,99 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   }
   wait_vmem_all();
   __syncthreads();
-  const int nU = s_nU;
+  const int nU = __builtin_amdgcn_readfirstlane(*s_nU);
 
-  // ---- block staging: K and V rows (lds_swz) and K^T rows (from the
-  // transposed copy, keys in operand order; tr_swz)
+  // ---- block staging: K and V rows (chunks XOR-swizzled with lds_swz) into
+  // the LDS ring; K^T operands are read from the K rows with transposing
+  // LDS reads
   const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
   const uint16_t* vbase = a.v + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
-  const uint16_t* ktbase =
-      a.kt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
-  // Unit x of this thread belongs to tile x / (TU / NT) (K, V, then K^T):
-  // the split is a compile-time property of x because tid < NT.
+  // Unit x of this thread belongs to tile x / (TU / NT) (K, then V): the
+  // split is a compile-time property of x because tid < NT.
   static_assert(TU % NT == 0, "tile split");
   constexpr int XPT = TU / NT;        // units per thread per tile
   uint4 stg[UPT];
   int soff[UPT];
-  int goff[UPT];                      // K/V: row within the block; K^T: d * Tp + chunk
+  int grow[UPT];                      // row within the block
 #pragma unroll
   for (int x = 0; x < UPT; ++x) {
     const int tile = x / XPT;
     const int w = tid + NT * (x - tile * XPT);
-    if (tile < 2) {
-      const int r = w / KCPR, ch = w - r * KCPR;
-      soff[x] = tile * KB + r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
-      goff[x] = r;
-    } else {
-      const int d = w >> 3, kc = w & 7;
-      soff[x] = 2 * KB + d * 128 + ((kc ^ tr_swz(d)) << 4);
-      goff[x] = d * Tp + kc * 8;
-    }
+    const int r = w / KCPR, ch = w - r * KCPR;
+    soff[x] = tile * KB + r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
+    grow[x] = r;
   }
-  const size_t tokstride = static_cast<size_t>(a.Hkv) * D;
+  // offsets inside one batch's K / V fit 32 bits (T <= 65536, Hkv * D < 2^15)
+  const int tokstride = a.Hkv * D;
   auto gload = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < UPT; ++x) {
       const int tile = x / XPT;
       const int w = tid + NT * (x - tile * XPT);
-      if (tile < 2) {
-        const int r = goff[x], ch = w - r * KCPR;
-        const int tok = min(j * 64 + r, a.T - 1);
-        stg[x] = ld16((tile == 0 ? kbase : vbase) + static_cast<size_t>(tok) * tokstride + ch * 8);
-      } else {
-        stg[x] = ld16(ktbase + goff[x] + j * 64);
+      const int r = grow[x], ch = w - r * KCPR;
+      const int tok = min(j * 64 + r, a.T - 1);
+      stg[x] = ld16((tile == 0 ? kbase : vbase) + (tok * tokstride + ch * 8));
+    }
+  };
+  // The wave's share of block `nxt` sits in stg; it is written to its slot as
+  // soon as every wave is done with the slot's previous block, and the share
+  // of the following block is fetched right after.
+  int nxt = 0;
+  if (nU > 0) gload(ulist[0]);
+  auto try_write = [&]() __attribute__((always_inline)) {
+    if (nxt < nU) {
+      const int sl = nxt % R;
+      if (ring_count(&done_cnt[sl]) >= static_cast<unsigned>(NW * (nxt / R))) {
+        uint8_t* dst = ring + sl * STAGE;
+#pragma unroll
+        for (int x = 0; x < UPT; ++x) st16(dst + soff[x], stg[x]);
+        ring_bump(&fill_cnt[sl], lane);
+        ++nxt;
+        if (nxt < nU) gload(ulist[nxt]);
       }
     }
   };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int x = 0; x < UPT; ++x) st16(&ring[buf][soff[x]], stg[x]);
-  };
-  if (nU > 0) {
-    gload(ulist[0]);
-    lstore(0);
-    if (nU > 1) gload(ulist[1]);
-  }
-  __syncthreads();
 
   int kofs[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     kofs[ks] = l16 * KROWB + (((ks * 4 + g4) ^ lds_swz<KROWB>(l16)) << 4);
-  int tofs[2];
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2)
-    tofs[k2] = 2 * KB + l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
+  // K^T operand of dQ^T = K^T dS^T for d tile dt and 32-key step k2: lane
+  // (l16, g4) needs K[key][16 dt + l16] for keys 32 k2 + 4 g4 + {0..3} and
+  // 32 k2 + 16 + 4 g4 + {0..3} (the order in which the S^T accumulator hands
+  // over dS).  A transposing read (ds_read_b64_tr_b16) gives each lane of a
+  // 16-lane group one column of a 4-row x 16-column block when source lane s
+  // addresses row base + s / 4, columns 4 (s % 4) .. 4 (s % 4) + 3.  The row's
+  // swizzle depends only on the lane (the steps between reads are multiples of
+  // 16 rows), so one offset per d tile serves all reads.
+  // (2 dt + h) ^ swz = 2 (dt ^ (swz >> 1)) + (h ^ (swz & 1)) for h = 0, 1.
+  const int trow = 4 * g4 + (l16 >> 2);
+  const int tswz = lds_swz<KROWB>(trow);
+  const int tbase0 = trow * KROWB + ((((l16 & 3) >> 1) ^ (tswz & 1)) << 4) + 8 * (l16 & 1);
+  const int tx = tswz >> 1;
 
+  // d log g of (token tl, slot s) of this query block: dlg[tl * HS + s]
+  float* const dlg = a.dlogg + rowbase * S;
+  const int HS = a.Hkv * S;
   const float sl2 = a.scale_log2;
+  bool failed = false;
   for (int u = 0; u < nU; ++u) {
-    const int buf = u & 1;
-    const uint8_t* st = ring[buf];
+    const int sl = u % R;
+    try_write();
+    const unsigned need = static_cast<unsigned>(NW * (u / R + 1));
+    for (int it = 0; ring_count(&fill_cnt[sl]) < need; ++it) {
+      if (it == kSpinLimit) {
+        failed = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      try_write();
+    }
+    if (failed) {
+      ring_fault(lane);
+      break;
+    }
+    const uint8_t* st = ring + sl * STAGE;
     const int j = ulist[u];
     const uint32_t jbit = 1u << (j & 31);
     const int jw = j >> 5;
@@ -591,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     bool sel[TW], act[TW];
 #pragma unroll
     for (int ti = 0; ti < TW; ++ti) {
-      sel[ti] = valid[ti] && (bits[tl_row[ti]][jw] & jbit);
+      sel[ti] = valid[ti] && (bits[tl_row[ti] * NBW + jw] & jbit);
       act[ti] = ballot64(sel[ti]) != 0;
     }
 #pragma unroll
@@ -611,12 +640,15 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
           pacc[mt] = mfma16x16x32(va, da[ti][ks], pacc[mt]);
         }
       }
+      // a block's compute is long: hand over this wave's next share now, so
+      // that the other waves do not wait for its end
+      try_write();
       const int tl = tl_row[ti];
       float lgv = 0.f;
       int rank = 0;
       if (sel[ti]) {
-        rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
-        lgv = lgs[tl][rank];
+        rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
+        lgv = lgs[tl * S + rank];
       }
       const float bias = lgv - lse2[ti];
       const int lim = cur ? (t0 + tl - j * 64 - g4 * 4) : 64;   // causal limit (key offset)
@@ -637,17 +669,17 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       if ((G & (G - 1)) == 0) {
         const float tot = group_sum_pow2(rs, G);
         if (g4 == 0 && sel[ti] && (l16 & (G - 1)) == 0)
-          a.dlogg[(rowbase + static_cast<size_t>(tl) * a.Hkv) * S + slot_of[tl][rank]] = tot;
+          dlg[tl * HS + slot_of[tl * S + rank]] = tot;
       } else {
-        if (g4 == 0) red[wv][l16] = rs;
+        if (g4 == 0) red[wv * 16 + l16] = rs;
         __builtin_amdgcn_wave_barrier();
         if (g4 == 0 && l16 < TPT) {
           const int tlr = (wv + NW * ti) * TPT + l16;
-          if (tlr < ntok && (bits[tlr][jw] & jbit)) {
+          if (tlr < ntok && (bits[tlr * NBW + jw] & jbit)) {
             float tot = 0.f;
-            for (int h = 0; h < G; ++h) tot += red[wv][l16 * G + h];
-            const int rk = pcnt[tlr][jw] + __popc(bits[tlr][jw] & (jbit - 1u));
-            a.dlogg[(rowbase + static_cast<size_t>(tlr) * a.Hkv) * S + slot_of[tlr][rk]] = tot;
+            for (int h = 0; h < G; ++h) tot += red[wv * 16 + l16 * G + h];
+            const int rk = pcnt[tlr * NBW + jw] + __popc(bits[tlr * NBW + jw] & (jbit - 1u));
+            dlg[tlr * HS + slot_of[tlr * S + rk]] = tot;
           }
         }
         __builtin_amdgcn_wave_barrier();
@@ -661,19 +693,29 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
         split_bf2(dsv[2 * k2 + 1][2], dsv[2 * k2 + 1][3], dsb[k2].w, dsl[k2].w);
       }
       // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row]
+      // recomputed per tile rather than kept live: registers are scarce here
+      int tbase = tbase0;
+      asm volatile("" : "+v"(tbase));
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
+        const uint8_t* tp = st + tbase + ((dt ^ tx) << 5);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const uint4 kta = *reinterpret_cast<const uint4*>(st + dt * 2048 + tofs[k2]);
+          const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
+          const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
+          const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
           dqa[ti][dt] = mfma16x16x32(kta, dsb[k2], dqa[ti][dt]);
           dqa[ti][dt] = mfma16x16x32(kta, dsl[k2], dqa[ti][dt]);
         }
       }
     }
-    if (u + 1 < nU) lstore(buf ^ 1);
-    if (u + 2 < nU) gload(ulist[u + 2]);
-    __syncthreads();
+    ring_bump(&done_cnt[sl], lane);
+  }
+  if (failed) {
+#pragma unroll
+    for (int ti = 0; ti < TW; ++ti)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) dqa[ti][dt] = floatx4{NAN, NAN, NAN, NAN};
   }
 
 #pragma unroll
@@ -693,6 +735,28 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   }
 }
 
+// Launch with the deepest LDS ring (4 or 3 slots) whose layout fits.
+template <int D, int NW, int TW>
+hipError_t launch_dq_ring(const BwdParams& p, unsigned nblk, hipStream_t st) {
+  constexpr int STAGE = 256 * D;     // K tile + V tile
+  const WalkLds L4 = walk_lds(4, STAGE, p.NB, p.S, NW, true);
+  const WalkLds L3 = walk_lds(3, STAGE, p.NB, p.S, NW, true);
+  if (L4.total <= kLdsBytes) {
+    auto k = dq_kernel<D, NW, TW, 4>;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, L4.total);
+    hipLaunchKernelGGL(k, dim3(nblk), dim3(NW * 64), L4.total, st, p);
+  } else if (L3.total <= kLdsBytes) {
+    auto k = dq_kernel<D, NW, TW, 3>;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, L3.total);
+    hipLaunchKernelGGL(k, dim3(nblk), dim3(NW * 64), L3.total, st, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   const long nrows = static_cast<long>(p.B) * p.T * p.Hq;
@@ -709,21 +773,20 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
                      dim3(256), 0, st, p);
   timing_mark(2, st);
-  hipError_t e = launch_transpose_tokens(p.k, p.kt, p.B, p.T, p.Hkv, D, st);
-  if (e != hipSuccess) return e;
-  timing_mark(3, st);
+  hipError_t e;
   if (p.ntiles <= 8) {
-    hipLaunchKernelGGL((dq_kernel<D, 8, 1>), dim3(nblk), dim3(512), 0, st, p);
+    e = launch_dq_ring<D, 8, 1>(p, nblk, st);
   } else if (p.ntiles <= 16) {
-    hipLaunchKernelGGL((dq_kernel<D, 8, 2>), dim3(nblk), dim3(512), 0, st, p);
+    e = launch_dq_ring<D, 8, 2>(p, nblk, st);
   } else {
     switch ((p.ntiles + 7) / 8) {
-      case 3: hipLaunchKernelGGL((dq_kernel<D, 8, 3>), dim3(nblk), dim3(512), 0, st, p); break;
-      case 4: hipLaunchKernelGGL((dq_kernel<D, 8, 4>), dim3(nblk), dim3(512), 0, st, p); break;
+      case 3: e = launch_dq_ring<D, 8, 3>(p, nblk, st); break;
+      case 4: e = launch_dq_ring<D, 8, 4>(p, nblk, st); break;
       default: return hipErrorInvalidValue;
     }
   }
-  timing_mark(4, st);
+  if (e != hipSuccess) return e;
+  timing_mark(3, st);
   return hipGetLastError();
 }
 
@@ -733,6 +796,17 @@ hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st) {
   if (p.D == 128) return launch_bwd_d<128>(p, st);
   if (p.D == 64) return launch_bwd_d<64>(p, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t take_ring_fault_bwd(unsigned* out) {
+  unsigned v = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_ring_fault), sizeof(v));
+  if (e == hipSuccess && v != 0) {
+    const unsigned zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_ring_fault), &zero, sizeof(zero));
+  }
+  *out |= v;
+  return e;
 }
 
 }  // namespace sas

@@ -30,7 +30,7 @@ constexpr float kLazyLog2 = 8.f;   // weights stay below 2^8 between rescales
 // HILO (the fp32 output is requested, for the backward's Delta): V^T is the
 // bf16 copy and P enters PV as bf16 hi + lo parts (exact to ~2^-16).
 // Otherwise V^T is the scaled fp16 copy and P enters once, in fp16.
-template <int D, int NW, int TW, bool HILO>
+template <int D, int NW, int TW, bool HILO, int R>
 __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   constexpr int NT = NW * 64;
   constexpr int KROWB = D * 2;              // bytes per K row
@@ -44,13 +44,19 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   constexpr int NDT = D / 16;
   static_assert(STAGE % (16 * NT) == 0, "unit split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t ring[2][STAGE];
-  __shared__ uint32_t bits[64][kMaxNBW];
-  __shared__ uint8_t pcnt[64][kMaxNBW];
-  __shared__ uint32_t ubits[kMaxNBW];
-  __shared__ uint16_t ulist[kMaxNB];
-  __shared__ float lgs[64][kMaxS];
-  __shared__ int s_nU;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int NBW = (a.NB + 31) >> 5;
+  const int S = a.S;
+  const WalkLds L = walk_lds(R, STAGE, a.NB, S, NW, false);
+  uint8_t* const ring = smem + L.ring;                      // slot sl at ring + sl * STAGE
+  uint32_t* const bits = reinterpret_cast<uint32_t*>(smem + L.bits);   // [64][NBW]
+  uint8_t* const pcnt = smem + L.pcnt;                      // [64][NBW]
+  uint32_t* const ubits = reinterpret_cast<uint32_t*>(smem + L.ubits);
+  uint16_t* const ulist = reinterpret_cast<uint16_t*>(smem + L.ulist);
+  float* const lgs = reinterpret_cast<float*>(smem + L.lgs);          // [64][S]
+  unsigned* const fill_cnt = reinterpret_cast<unsigned*>(smem + L.cnt);
+  unsigned* const done_cnt = fill_cnt + R;
+  int* const s_nU = reinterpret_cast<int*>(smem + L.nu);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -66,20 +72,19 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   const int b = rest / NQB;
   const int t0 = c * 64;
   const int ntok = min(64, a.T - t0);
-  const int NBW = (a.NB + 31) >> 5;
-  const int S = a.S;
   const int Tp = a.NB * 64;
 
   // ---- selection bitmaps of the 64 tokens, their union, log-gates by rank
-  for (int i = tid; i < 64 * kMaxNBW; i += NT) (&bits[0][0])[i] = 0u;
-  if (tid < kMaxNBW) ubits[tid] = 0u;
+  for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
+  if (tid < NBW) ubits[tid] = 0u;
+  if (tid < 2 * R) fill_cnt[tid] = 0u;          // fill and done counters
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const int j = a.idx[(rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s];
     if (j >= 0 && j <= c) {
-      atomicOr(&bits[tl][j >> 5], 1u << (j & 31));
+      atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
       atomicOr(&ubits[j >> 5], 1u << (j & 31));
     }
   }
@@ -87,8 +92,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   if (tid < 64) {
     int run = 0;
     for (int w = 0; w < NBW; ++w) {
-      pcnt[tid][w] = static_cast<uint8_t>(run);
-      run += __popc(bits[tid][w]);
+      pcnt[tid * NBW + w] = static_cast<uint8_t>(run);
+      run += __popc(bits[tid * NBW + w]);
     }
   }
   __syncthreads();
@@ -97,9 +102,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
     if (j >= 0 && j <= c) {
-      const uint32_t wbits = bits[tl][j >> 5];
-      const int rank = pcnt[tl][j >> 5] + __popc(wbits & ((1u << (j & 31)) - 1u));
-      if (rank < kMaxS) lgs[tl][rank] = a.logg[off] * kLog2e;
+      const uint32_t wbits = bits[tl * NBW + (j >> 5)];
+      const int rank = pcnt[tl * NBW + (j >> 5)] + __popc(wbits & ((1u << (j & 31)) - 1u));
+      if (rank < S) lgs[tl * S + rank] = a.logg[off] * kLog2e;
     }
   }
   if (wv == 0) {
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
       }
       base += __shfl(incl, 63, 64);
     }
-    if (lane == 0) s_nU = base;
+    if (lane == 0) *s_nU = base;
   }
 
   // ---- per-tile query rows: row r = l16 -> token r/G, head r%G
@@ -147,21 +152,22 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   }
   wait_vmem_all();
   __syncthreads();
-  const int nU = s_nU;
+  const int nU = __builtin_amdgcn_readfirstlane(*s_nU);
 
-  // ---- block staging: global -> registers (next block) -> LDS (swizzled)
+  // ---- block staging: the thread's 16-byte units tid + NT*x of a block go
+  // global -> registers -> its LDS ring slot (chunks XOR-swizzled per row)
   const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
   const uint16_t* vtbase =
       a.vt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
   uint4 stg[UPT];
-  auto gload = [&](int j) {
+  auto gload = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < UPT; ++x) {
       const int u = tid + NT * x;
       if (u < KU) {
         const int r = u / KCPR, ch = u - r * KCPR;
         const int tok = min(j * 64 + r, a.T - 1);
-        stg[x] = ld16(kbase + static_cast<size_t>(tok) * a.Hkv * D + ch * 8);
+        stg[x] = ld16(kbase + (tok * a.Hkv * D + ch * 8));   // < 2^31 within a batch
       } else {
         const int v = u - KU;
         const int d = v >> 3, kc = v & 7;
@@ -184,16 +190,24 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
       soff[x] = KB + d * 128 + ((kc ^ tr_swz(d)) << 4);
     }
   }
-  auto lstore = [&](int buf) {
+  // The wave's share of block `nxt` sits in stg; it is written to its slot as
+  // soon as every wave is done with the slot's previous block, and the share
+  // of the following block is fetched right after.
+  int nxt = 0;
+  if (nU > 0) gload(ulist[0]);
+  auto try_write = [&]() __attribute__((always_inline)) {
+    if (nxt < nU) {
+      const int sl = nxt % R;
+      if (ring_count(&done_cnt[sl]) >= static_cast<unsigned>(NW * (nxt / R))) {
+        uint8_t* dst = ring + sl * STAGE;
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) st16(&ring[buf][soff[x]], stg[x]);
+        for (int x = 0; x < UPT; ++x) st16(dst + soff[x], stg[x]);
+        ring_bump(&fill_cnt[sl], lane);
+        ++nxt;
+        if (nxt < nU) gload(ulist[nxt]);
+      }
+    }
   };
-  if (nU > 0) {
-    gload(ulist[0]);
-    lstore(0);
-    if (nU > 1) gload(ulist[1]);
-  }
-  __syncthreads();
 
   // per-lane LDS read offsets of the MFMA operands (immediate offsets add
   // the 16-key / 16-d tile steps)
@@ -206,9 +220,24 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   for (int k2 = 0; k2 < 2; ++k2) vofs[k2] = KB + l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
 
   const float sl2 = a.scale_log2;
+  bool failed = false;
   for (int u = 0; u < nU; ++u) {
-    const int buf = u & 1;
-    const uint8_t* st = ring[buf];
+    const int sl = u % R;
+    try_write();
+    const unsigned need = static_cast<unsigned>(NW * (u / R + 1));
+    for (int it = 0; ring_count(&fill_cnt[sl]) < need; ++it) {
+      if (it == kSpinLimit) {
+        failed = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      try_write();
+    }
+    if (failed) {
+      ring_fault(lane);
+      break;
+    }
+    const uint8_t* st = ring + sl * STAGE;
     const int j = ulist[u];
     const uint32_t jbit = 1u << (j & 31);
     const int jw = j >> 5;
@@ -217,7 +246,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
     bool act[TW];
 #pragma unroll
     for (int ti = 0; ti < TW; ++ti) {
-      sel[ti] = valid[ti] && (bits[tl_row[ti]][jw] & jbit);
+      sel[ti] = valid[ti] && (bits[tl_row[ti] * NBW + jw] & jbit);
       act[ti] = ballot64(sel[ti]) != 0;
     }
 #pragma unroll
@@ -226,8 +255,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
       const int tl = tl_row[ti];
       float lgv = 0.f;
       if (sel[ti]) {
-        const int rank = pcnt[tl][jw] + __popc(bits[tl][jw] & (jbit - 1u));
-        lgv = lgs[tl][rank];
+        const int rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
+        lgv = lgs[tl * S + rank];
       }
       // S^T[key, row] = K[key,:] . Q[row,:]
       floatx4 sacc[4];
@@ -286,6 +315,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
           }
       }
       l_run[ti] += psum;
+      // a block's compute is long: hand over this wave's next share now, so
+      // that the other waves do not wait for its end
+      try_write();
       uint4 pb[2], pl[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
@@ -319,9 +351,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
         }
       }
     }
-    if (u + 1 < nU) lstore(buf ^ 1);
-    if (u + 2 < nU) gload(ulist[u + 2]);
-    __syncthreads();
+    ring_bump(&done_cnt[sl], lane);
+  }
+  if (failed) {
+#pragma unroll
+    for (int ti = 0; ti < TW; ++ti) l_run[ti] = NAN;
   }
 
   // ---- epilogue
@@ -350,6 +384,28 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   }
 }
 
+// Launch with the deepest LDS ring (4 or 3 slots) whose layout fits.
+template <int D, int NW, int TW, bool HILO>
+hipError_t launch_fwd_ring(const FwdParams& p, dim3 grid, hipStream_t st) {
+  constexpr int STAGE = 256 * D;     // K tile + V^T tile
+  const WalkLds L4 = walk_lds(4, STAGE, p.NB, p.S, NW, false);
+  const WalkLds L3 = walk_lds(3, STAGE, p.NB, p.S, NW, false);
+  if (L4.total <= kLdsBytes) {
+    auto k = sparse_fwd_kernel<D, NW, TW, HILO, 4>;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, L4.total);
+    hipLaunchKernelGGL(k, grid, dim3(NW * 64), L4.total, st, p);
+  } else if (L3.total <= kLdsBytes) {
+    auto k = sparse_fwd_kernel<D, NW, TW, HILO, 3>;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, L3.total);
+    hipLaunchKernelGGL(k, grid, dim3(NW * 64), L3.total, st, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool HILO>
 hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
   const int NQB = (p.T + 63) / 64;
@@ -357,16 +413,12 @@ hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
   // up to 16 row tiles: one tile per wave, 16 waves (4 per SIMD hide the
   // latency of the per-tile MFMA -> softmax -> MFMA chain); more tiles
   // (G >= 5): 8 waves with TW tiles each.
-  if (p.ntiles <= 16) {
-    hipLaunchKernelGGL((sparse_fwd_kernel<D, 16, 1, HILO>), grid, dim3(1024), 0, st, p);
-    return hipGetLastError();
-  }
+  if (p.ntiles <= 16) return launch_fwd_ring<D, 16, 1, HILO>(p, grid, st);
   switch ((p.ntiles + 7) / 8) {
-    case 3: hipLaunchKernelGGL((sparse_fwd_kernel<D, 8, 3, HILO>), grid, dim3(512), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((sparse_fwd_kernel<D, 8, 4, HILO>), grid, dim3(512), 0, st, p); break;
+    case 3: return launch_fwd_ring<D, 8, 3, HILO>(p, grid, st);
+    case 4: return launch_fwd_ring<D, 8, 4, HILO>(p, grid, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int D>
@@ -387,6 +439,17 @@ hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st) {
   e = p.D == 128 ? launch_fwd_d<128>(p, st) : p.D == 64 ? launch_fwd_d<64>(p, st)
                                                          : hipErrorInvalidValue;
   timing_mark(2, st);
+  return e;
+}
+
+hipError_t take_ring_fault_fwd(unsigned* out) {
+  unsigned v = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_ring_fault), sizeof(v));
+  if (e == hipSuccess && v != 0) {
+    const unsigned zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_ring_fault), &zero, sizeof(zero));
+  }
+  *out |= v;
   return e;
 }
 

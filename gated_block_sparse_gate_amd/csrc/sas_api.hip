@@ -55,6 +55,8 @@ sas_status check_dims(const sas_dims* d) {
     return fail(SAS_ERR_UNSUPPORTED, "topk must be <= %d (got %d)", sas::kMaxS - 1, d->topk);
   if (d->T > sas::kMaxNB * 64)
     return fail(SAS_ERR_UNSUPPORTED, "T must be <= %d (got %d)", sas::kMaxNB * 64, d->T);
+  if (static_cast<long long>(d->T) * d->Hkv * d->D > 0x7fffffffLL)
+    return fail(SAS_ERR_UNSUPPORTED, "T * Hkv * D must be < 2^31 (one batch's K fits 32-bit offsets)");
   if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps))
     return fail(SAS_ERR_INVALID, "norm_eps must be finite and >= 0");
   if (!(d->rope_theta > 0.0) || !std::isfinite(d->rope_theta))
@@ -96,7 +98,7 @@ FwdWs fwd_ws_layout(const sas_dims* d) {
 }
 size_t fwd_ws(const sas_dims* d) { return fwd_ws_layout(d).total; }
 
-struct BwdWs { size_t delta, cnt2d, rowptr, entries, kt, total; };
+struct BwdWs { size_t delta, cnt2d, rowptr, entries, total; };
 BwdWs bwd_ws(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
   const size_t S = d->topk + 1;
@@ -105,8 +107,7 @@ BwdWs bwd_ws(const sas_dims* d) {
   w.cnt2d = align_up(w.delta + sizeof(float) * static_cast<size_t>(d->B) * d->T * d->Hq);
   w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
   w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
-  w.kt = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
-  w.total = align_up(w.kt + sizeof(uint16_t) * static_cast<size_t>(d->B) * d->Hkv * d->D * NB * 64);
+  w.total = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
   return w;
 }
 
@@ -182,6 +183,16 @@ sas_status sas_set_timing_events(void* const* events, int n_events) {
 }
 
 const char* sas_last_error(void) { return g_err.c_str(); }
+
+sas_status sas_take_device_fault(unsigned* fault) {
+  if (!fault) return fail(SAS_ERR_INVALID, "fault must be non-null");
+  *fault = 0;
+  hipError_t e = sas::take_ring_fault_fwd(fault);
+  if (e == hipSuccess) e = sas::take_ring_fault_bwd(fault);
+  if (e != hipSuccess) return fail(SAS_ERR_HIP, "reading the fault flag: %s", hipGetErrorString(e));
+  g_err.clear();
+  return SAS_OK;
+}
 
 size_t sas_workspace_size(int op, const sas_dims* d) {
   if (check_dims(d) != SAS_OK) return static_cast<size_t>(-1);
@@ -292,7 +303,6 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
   p.cnt2d = reinterpret_cast<int32_t*>(base + w.cnt2d);
   p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
   p.entries = reinterpret_cast<int32_t*>(base + w.entries);
-  p.kt = reinterpret_cast<uint16_t*>(base + w.kt);
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
   p.TPT = 16 / p.G;

@@ -43,24 +43,6 @@ __device__ __forceinline__ void split_bf2(float a, float b, uint32_t& hi, uint32
   lo = pack_bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-// s_waitcnt vmcnt(n) for a compile-time n < 16 (expcnt, lgkmcnt not waited).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
-}
-
-// Workgroup barrier without the memory fences of __syncthreads(): those
-// fences make the compiler wait for every outstanding LDS-DMA load, which
-// would drain a software pipeline at each step.  Callers wait for exactly the
-// loads they need (wait_vmem) before it; the empty asm statements keep the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_nofence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // XOR swizzle of the 16-byte chunks of an LDS tile row of ROWB bytes, chosen
 // so that 16 lanes reading the same logical chunk of 16 consecutive rows hit
 // distinct banks (256-byte rows: chunk ^ (r & 15); 128-byte rows, where two
@@ -79,11 +61,16 @@ __device__ __forceinline__ int lds_swz(int r) {
 // for 128-byte and for 256-byte bank windows.
 __device__ __forceinline__ int tr_swz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
-// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
-// lane i's 16 bytes land at lds + 16 * i.  `lds` must be wave-uniform.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-  typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds), 16, 0, 0);
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// l receives element l % 4 of the 8-byte words addressed by lanes l / 4 + 4 e
+// (e = 0..3), i.e. one column of the 4 x 16 block of 16-bit values that the
+// group's 16 addresses span when lane s addresses row s / 4, columns
+// 4 (s % 4) .. 4 (s % 4) + 3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+  return __builtin_bit_cast(uint2, v);
 }
 
 // 16-byte load / store through a native vector type.  A plain uint4 struct
@@ -212,6 +199,40 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ void wait_vmem_all() {
   // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
   __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
+// ---- LDS ring shared by the waves of a workgroup, without workgroup barriers.
+// Slot n % R holds block n of the walk.  Each wave writes its share of block n
+// once every wave is done reading block n - R (done[n % R] >= NW * (n / R))
+// and then bumps fill[n % R]; a wave reads block u once
+// fill[u % R] >= NW * (u / R + 1) and bumps done[u % R] after its last read of
+// it.  The counters only grow, so a count names the use of the slot, and a
+// wave can run up to R - 1 blocks ahead of the slowest one.  The LDS accesses
+// of one wave are performed in order, so a bump issued after a wave's stores
+// (or reads) of a slot is observed only after them; the asm statements keep the
+// compiler from moving memory accesses across a bump or a poll.
+constexpr int kSpinLimit = 1 << 21;   // polls (about 0.1 s) before a wait gives up
+
+__device__ __forceinline__ unsigned ring_count(const unsigned* c) {
+  asm volatile("" ::: "memory");
+  const unsigned v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  asm volatile("" ::: "memory");
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ void ring_bump(unsigned* c, int lane) {
+  asm volatile("" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  asm volatile("" ::: "memory");
+}
+
+// Set (never expected) when a ring wait gave up: the kernel then finishes
+// with NaN outputs for the waves concerned instead of hanging.  One copy per
+// source file; read and cleared from the host through take_ring_fault_*().
+static __device__ unsigned g_ring_fault;
+
+__device__ __forceinline__ void ring_fault(int lane) {
+  if (lane == 0) atomicOr(&g_ring_fault, 1u);
 }
 
 }  // namespace sas

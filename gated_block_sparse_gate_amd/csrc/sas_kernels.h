@@ -36,6 +36,32 @@ struct TopkParams {
   int B, T, Hkv, dg, K, S, NB;
 };
 
+// Dynamic LDS of the query-block walks (forward, dQ): R ring slots of `stage`
+// bytes, the per-token selection bitmaps (NBW words per token) with their
+// running popcounts, the union list, the log-gates (and, for dQ, slot numbers)
+// by selection rank, the dQ head-sum scratch, and the ring counters.
+struct WalkLds {
+  int ring, bits, pcnt, ubits, ulist, lgs, slot, red, cnt, nu, total;
+};
+__host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+__host__ __device__ inline WalkLds walk_lds(int R, int stage, int NB, int S, int NW, bool dq) {
+  const int NBW = (NB + 31) >> 5;
+  WalkLds L;
+  L.ring = 0;
+  L.bits = R * stage;
+  L.pcnt = align16(L.bits + 64 * NBW * 4);
+  L.ubits = align16(L.pcnt + 64 * NBW);
+  L.ulist = align16(L.ubits + NBW * 4);
+  L.lgs = align16(L.ulist + NB * 2);
+  L.slot = align16(L.lgs + 64 * S * 4);
+  L.red = align16(L.slot + (dq ? 64 * S : 0));
+  L.cnt = align16(L.red + (dq ? NW * 16 * 4 : 0));
+  L.nu = L.cnt + 2 * R * 4;
+  L.total = align16(L.nu + 4);
+  return L;
+}
+constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+
 // Optional stage-boundary timing events (sas_set_timing_events).
 void timing_mark(int i, hipStream_t st);
 
@@ -76,7 +102,6 @@ struct BwdParams {
   int32_t* cnt2d;       // [B,Hkv,NQB,NB]  per (query block, key block) counts -> offsets
   int32_t* rowptr;      // [B,Hkv,NB+1]
   int32_t* entries;     // [B,Hkv,T*S] packed (t << 6) | slot
-  uint16_t* kt;         // [B,Hkv,D,64*NB] transposed copy of k
   int B, T, Hq, Hkv, D, G, S, NB;
   int TPT, ntiles;
   float scale, scale_log2;
@@ -106,6 +131,8 @@ hipError_t launch_router(const RouterParams& p, const uint16_t* wq, const uint16
                          hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st);
+// OR the ring-wait fault flag of the forward kernels into *out and clear it
+hipError_t take_ring_fault_fwd(unsigned* out);
 // src [B,T,H,D] -> dst [B,H,D,64*ceil(T/64)] (zero tail)
 hipError_t launch_transpose_tokens(const uint16_t* src, uint16_t* dst, int B, int T, int H, int D,
                                    hipStream_t st);
@@ -116,6 +143,8 @@ hipError_t launch_transpose_tokens_f16(const uint16_t* src, uint16_t* dst, float
                                        float* scale_out, int B, int T, int H, int D,
                                        hipStream_t st);
 hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st);
+// OR the ring-wait fault flag of the backward kernels into *out and clear it
+hipError_t take_ring_fault_bwd(unsigned* out);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 
 // decode split factor for a given problem (also sizes its workspace)

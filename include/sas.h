@@ -99,11 +99,20 @@ const char* sas_last_error(void);
  * sas_sparse_attn_fwd / sas_sparse_attn_bwd call records events[i] on its
  * stream at stage boundary i (boundaries beyond n_events are skipped):
  *   fwd: 0 start, 1 after the V transpose, 2 after the attention kernel;
- *   bwd: 0 start, 1 after Delta + the CSR build, 2 after dK/dV,
- *        3 after the K transpose, 4 after dQ.
+ *   bwd: 0 start, 1 after Delta + the CSR build, 2 after dK/dV, 3 after dQ.
  * The caller owns the events and keeps them alive while the hook is set.
  */
 sas_status sas_set_timing_events(void* const* events, int n_events);
+
+/*
+ * Device fault flag of the attention kernels on the current device.  Their
+ * waves share LDS staging slots without workgroup barriers and wait on LDS
+ * counters; a wait that does not end within about 0.1 s (a protocol error,
+ * never expected) is abandoned, the affected outputs are written as NaN and
+ * the flag is set.  *fault receives the flag (0 = none) and the flag is
+ * cleared.  Synchronises with the device.
+ */
+sas_status sas_take_device_fault(unsigned* fault);
 
 /* Workspace bytes needed by op (SAS_OP_*) for dims d; 0 if none; (size_t)-1
  * if d is invalid. */

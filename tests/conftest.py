@@ -26,3 +26,14 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _no_device_fault(request):
+    """After every GPU test: the attention kernels' ring waits all ended
+    normally (a wait that gives up sets a device flag and writes NaNs)."""
+    yield
+    if "gpu" not in request.node.keywords:
+        return
+    import gated_block_sparse_gate_amd as sas
+    assert sas.take_device_fault() == 0, "an attention kernel abandoned an LDS ring wait"
