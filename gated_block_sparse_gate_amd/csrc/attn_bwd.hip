@@ -650,20 +650,30 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
         rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
         lgv = lgs[tl * S + rank];
       }
-      const float bias = lgv - lse2[ti];
-      const int lim = cur ? (t0 + tl - j * 64 - g4 * 4) : 64;   // causal limit (key offset)
+      // rows of tokens that did not select the block get P = 0
+      const float bias = sel[ti] ? lgv - lse2[ti] : -INFINITY;
       float dsv[4][4];
-      float rs = 0.f;
+      if (cur) {
+        const int lim = t0 + tl - j * 64 - g4 * 4;   // causal limit (key offset)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool on = sel[ti] && (mt * 16 + i <= lim);
-          const float pp = on ? fast_exp2(sacc[mt][i] * sl2 + bias) : 0.f;
-          const float dsx = pp * (pacc[mt][i] - dlt[ti]);
-          dsv[mt][i] = dsx;
-          rs += dsx;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const float pp = (mt * 16 + i <= lim) ? fast_exp2(fmaf(sacc[mt][i], sl2, bias)) : 0.f;
+            dsv[mt][i] = pp * (pacc[mt][i] - dlt[ti]);
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dsv[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, bias)) * (pacc[mt][i] - dlt[ti]);
+      }
+      // pairwise row sum of dS over this lane's keys, then over the row's lanes
+      float rq[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) rq[mt] = (dsv[mt][0] + dsv[mt][1]) + (dsv[mt][2] + dsv[mt][3]);
+      float rs = (rq[0] + rq[1]) + (rq[2] + rq[3]);
       rs = row4_sum(rs);
       // dlogg: sum the G rows of each token of this tile (lanes G*k .. G*k+G-1)
       if ((G & (G - 1)) == 0) {

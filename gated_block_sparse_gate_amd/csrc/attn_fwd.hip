@@ -269,7 +269,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
           sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
         }
       }
-      // row maximum of the raw scores over the keys this row may see
+      // maximum of this lane's raw scores over the keys its row may see (the
+      // row's 64 keys are spread over the 4 lanes g4 of the row)
       const int lim = t0 + tl - j * 64 - g4 * 4;     // current block: key offset limit
       float mr = -INFINITY;
       if (cur) {
@@ -283,10 +284,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
         for (int mt = 0; mt < 4; ++mt)
           mr = fmaxf(mr, fmaxf(fmaxf(sacc[mt][0], sacc[mt][1]), fmaxf(sacc[mt][2], sacc[mt][3])));
       }
-      mr = row4_max(mr);
-      const float cand = sel[ti] ? mr * sl2 + lgv : -INFINITY;
-      const bool up = cand > m_run[ti] + kLazyLog2;
-      if (ballot64(up)) {
+      // A row's reference moves only if its maximum passes it by 2^kLazyLog2,
+      // i.e. if one of its lanes does; only then are the 4 lanes' maxima
+      // combined (rare), so the common path needs no cross-lane step.
+      const float cand_l = sel[ti] ? mr * sl2 + lgv : -INFINITY;
+      if (ballot64(cand_l > m_run[ti] + kLazyLog2)) {
+        const float cand = row4_max(cand_l);
+        const bool up = cand > m_run[ti] + kLazyLog2;
         const float alpha = up ? fast_exp2(m_run[ti] - cand) : 1.f;
         m_run[ti] = up ? cand : m_run[ti];
         l_run[ti] *= alpha;
@@ -295,7 +299,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
       }
       const float bias = sel[ti] ? lgv - m_run[ti] : -INFINITY;
       float x[4][4];
-      float psum = 0.f;
       if (cur) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -303,17 +306,18 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
           for (int i = 0; i < 4; ++i) {
             const float e = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
             x[mt][i] = (mt * 16 + i <= lim) ? e : 0.f;
-            psum += x[mt][i];
           }
       } else {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
-            psum += x[mt][i];
-          }
+          for (int i = 0; i < 4; ++i) x[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
       }
+      // pairwise sum (short dependency chain)
+      float ps[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) ps[mt] = (x[mt][0] + x[mt][1]) + (x[mt][2] + x[mt][3]);
+      const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
       l_run[ti] += psum;
       // a block's compute is long: hand over this wave's next share now, so
       // that the other waves do not wait for its end
