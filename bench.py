@@ -316,9 +316,10 @@ def main():
     csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
     # algorithmic FLOPs per launch: the contractions each kernel must perform,
     # 2 D per attended (query head, key) pair each: forward S and PV (4 D);
-    # dK/dV kernel S, dP, dV, dK (8 D); dQ kernel S, dP, dQ (6 D)
+    # dK/dV kernel S, dP, dV, dK (8 D; it also writes dS); dQ kernel dQ = dS K
+    # (2 D, reading dS)
     kflops = {"sparse_fwd_kernel": 4.0 * D * pairs, "dkdv_kernel": 8.0 * D * pairs,
-              "dq_kernel": 6.0 * D * pairs}
+              "dq_kernel": 2.0 * D * pairs}
     ksrc = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
             "dq_kernel": "attn_bwd.hip"}
     kernels = {}

@@ -172,7 +172,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TP];
   __shared__ __attribute__((aligned(16))) uint16_t dOt[2][D * TP];
   __shared__ float m_lse2[3][32], m_delta[3][32], m_lg2[3][32];
-  __shared__ int m_t[3][32], m_src[3][32];
+  __shared__ int m_t[3][32], m_src[3][32], m_ent[3][32];
+  // dS of the tile pair, [32 rows][hi 64 | lo 64] bf16 in operand key order,
+  // and each wave's row sums of dS over its 16 keys
+  __shared__ __attribute__((aligned(16))) uint8_t dsT[32 * 256];
+  __shared__ float dsum[4][32];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -218,9 +222,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     return (tk >= j * 64 && tk < p.T && s < p.S) ? en : -1;
   };
   float r_lse = -INFINITY, r_del = 0.f, r_lg = 0.f;
-  int r_t = -1, r_src = -1;
+  int r_t = -1, r_src = -1, r_en = -1;
   auto meta_issue = [&](int en) {
-    r_t = -1; r_src = -1;
+    r_t = -1; r_src = -1; r_en = en;
     if (en >= 0) {
       const int tk = en >> 6, s = en & 63;
       const size_t qrow = (static_cast<size_t>(b) * p.T + tk) * p.Hq + kv * G + mhh;
@@ -235,6 +239,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const bool ok = r_t >= 0 && r_lse > -INFINITY;
     m_t[slot][mr] = ok ? r_t : -1;
     m_src[slot][mr] = ok ? r_src : -1;
+    m_ent[slot][mr] = r_en;
     m_lse2[slot][mr] = ok ? r_lse * kLog2e : 0.f;
     m_delta[slot][mr] = ok ? r_del : 0.f;
     m_lg2[slot][mr] = ok ? r_lg * kLog2e : 0.f;
@@ -307,6 +312,37 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qofs[ks] = l16 * ROWB + (((ks * 4 + g4) ^ lds_swz<ROWB>(l16)) << 4);
 
+  // position of this lane's key (16 wv + l16) in the stored operand order
+  const int kpos = 32 * (wv >> 1) + 8 * (l16 >> 2) + 4 * (wv & 1) + (l16 & 3);
+  // dS rows of tile pair pp (LDS, complete after a barrier) -> global; d log g
+  // of each (token, slot) = sum of its G heads' dS over the block's 64 keys
+  // (each (token, slot) is in exactly one tile pair of one workgroup)
+  auto store_ds = [&](int pp) __attribute__((always_inline)) {
+    const int msp = pp % 3;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int cidx = tid + 256 * x;
+      const int r = cidx >> 4, part = cidx & 15;
+      const int en = m_ent[msp][r];
+      if (en >= 0) {
+        const int tk = en >> 6, sl = en & 63, hh = (r & 15) % G;
+        uint16_t* dst = p.dsbuf +
+            ((((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + sl) * G + hh) * 128 + part * 8;
+        st16(dst, ld16(dsT + r * 256 + part * 16));
+      }
+    }
+    if (tid < 2 * TPT) {
+      const int tt = tid / TPT, r0 = tt * 16 + (tid - tt * TPT) * G;
+      const int en = m_ent[msp][r0];
+      if (en >= 0) {
+        float tot = 0.f;
+        for (int h = 0; h < G; ++h)
+          tot += (dsum[0][r0 + h] + dsum[1][r0 + h]) + (dsum[2][r0 + h] + dsum[3][r0 + h]);
+        p.dlogg[((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)] = tot;
+      }
+    }
+  };
+
   for (int it = 0; it < nit; ++it) {
     const int buf = it & 1, ms = it % 3;
     if (tid < 32) {
@@ -314,6 +350,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       en_n3 = (it + 3 < nit) ? load_ent(it + 3) : -1;
     }
     if (it + 1 < nit) rows_issue((it + 1) % 3);
+    if (it > 0) store_ds(it - 1);
 
     // S, dP for the two row tiles: [rows x 16 keys of this wave]
     floatx4 sacc[2], pacc[2];
@@ -340,6 +377,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         if (t >= 0 && key <= t) pp = fast_exp2(sacc[tt][i] * sl2 + m_lg2[ms][r] - m_lse2[ms][r]);
         pv[tt][i] = pp;
         ds[tt][i] = pp * (pacc[tt][i] - m_delta[ms][r]);
+      }
+    // the previous pair's dS tile has been read (store_ds) by every thread
+    __syncthreads();
+    // dS as bf16 hi + lo into the tile (row r, this lane's key), and the row
+    // sums of dS over this wave's 16 keys
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = tt * 16 + g4 * 4 + i;
+        const uint16_t hi = f2bf(ds[tt][i]);
+        const uint16_t lo = f2bf(ds[tt][i] - bf2f(hi));
+        *reinterpret_cast<uint16_t*>(dsT + r * 256 + 2 * kpos) = hi;
+        *reinterpret_cast<uint16_t*>(dsT + r * 256 + 128 + 2 * kpos) = lo;
+        const float rsum = row16_sum(ds[tt][i]);
+        if (l16 == 0) dsum[wv][r] = rsum;
       }
     // P and dS enter the products as bf16 hi + lo parts (exact to ~2^-16)
     uint4 pb, pl, db, dl;
@@ -374,6 +427,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     if (it + 1 < nit) rows_store(buf ^ 1);
     __syncthreads();
   }
+  if (nit > 0) store_ds(nit - 1);
   if (keyok) {
     const size_t off = ((static_cast<size_t>(b) * p.T + key) * p.Hkv + kv) * D;
 #pragma unroll
@@ -389,32 +443,60 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   }
 }
 
-// ---------------------------------------------------------------- dQ, dlogg
+// ---------------------------------------------------------------- dQ
+// dQ[t, h] = scale * sum over the selected blocks j of dS[t, h, j, :] K_j,
+// with dS as written by the dK/dV kernel (bf16 hi + lo parts, so the product
+// is exact to ~2^-16).  One workgroup = (b, kappa, 64-token query block); it
+// walks the union of the blocks its tokens selected, staging each block's K
+// tile once into a ring of R LDS slots (shared without workgroup barriers,
+// see the ring protocol in sas_device.h).  Wave w owns row tiles w + NW * ti
+// (16 rows = TPT tokens x G heads) and keeps dQ^T in registers; for a block
+// that some token of a tile selected it loads the tile's dS rows (zero rows
+// for the other tokens) and runs dQ^T += K^T dS^T on bf16 MFMA 16x16x32, the
+// K^T operand read from the K tile with transposing LDS reads.  With one tile
+// per wave, the dS rows of the wave's next active block are loaded while the
+// current one is computed.
+
+// Dynamic LDS of the dQ kernel: ring, selection bitmaps, their popcount
+// prefixes, the union bitmap and list, slot numbers by selection rank, and
+// the ring counters.
+struct DqLds { int ring, bits, pcnt, ubits, ulist, slot, cnt, nu, total; };
+__host__ __device__ inline DqLds dq_lds(int R, int stage, int NB, int S) {
+  const int NBW = (NB + 31) >> 5;
+  DqLds L;
+  L.ring = 0;
+  L.bits = R * stage;
+  L.pcnt = align16(L.bits + 64 * NBW * 4);
+  L.ubits = align16(L.pcnt + 64 * NBW);
+  L.ulist = align16(L.ubits + NBW * 4);
+  L.slot = align16(L.ulist + NB * 2);
+  L.cnt = align16(L.slot + 64 * S);
+  L.nu = L.cnt + 2 * R * 4;
+  L.total = align16(L.nu + 4);
+  return L;
+}
+
 template <int D, int NW, int TW, int R>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   constexpr int NT = NW * 64;
-  constexpr int KROWB = D * 2;              // bytes per K / V row
-  constexpr int KB = 64 * KROWB;            // one tile (K, V or K^T) in bytes
-  constexpr int STAGE = 2 * KB;             // K | V
-  constexpr int TU = KB / 16;               // 16-byte units per tile
-  constexpr int UPT = 2 * TU / NT;         // units per thread per block
+  constexpr int KROWB = D * 2;              // bytes per K row
+  constexpr int STAGE = 64 * KROWB;         // K tile
+  constexpr int TU = STAGE / 16;            // 16-byte units per tile
+  constexpr int UPT = (TU + NT - 1) / NT;   // units per thread per block
   constexpr int KCPR = KROWB / 16;
-  constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  static_assert(2 * TU % NT == 0, "unit split");
+  constexpr bool PF = TW == 1;              // prefetch the next active block's dS
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int NBW = (a.NB + 31) >> 5;
   const int S = a.S;
-  const WalkLds L = walk_lds(R, STAGE, a.NB, S, NW, true);
+  const DqLds L = dq_lds(R, STAGE, a.NB, S);
   uint8_t* const ring = smem + L.ring;                      // slot sl at ring + sl * STAGE
   uint32_t* const bits = reinterpret_cast<uint32_t*>(smem + L.bits);   // [64][NBW]
   uint8_t* const pcnt = smem + L.pcnt;                      // [64][NBW]
   uint32_t* const ubits = reinterpret_cast<uint32_t*>(smem + L.ubits);
   uint16_t* const ulist = reinterpret_cast<uint16_t*>(smem + L.ulist);
-  float* const lgs = reinterpret_cast<float*>(smem + L.lgs);          // [64][S]
   uint8_t* const slot_of = smem + L.slot;                   // [64][S]
-  float* const red = reinterpret_cast<float*>(smem + L.red);          // [NW][16]
   unsigned* const fill_cnt = reinterpret_cast<unsigned*>(smem + L.cnt);
   unsigned* const done_cnt = fill_cnt + R;
   int* const s_nU = reinterpret_cast<int*>(smem + L.nu);
@@ -434,6 +516,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   const int t0 = c * 64;
   const int ntok = min(64, a.T - t0);
 
+  // ---- selection bitmaps of the 64 tokens, their union, slots by rank
   for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
   if (tid < NBW) ubits[tid] = 0u;
   if (tid < 2 * R) fill_cnt[tid] = 0u;          // fill and done counters
@@ -447,7 +530,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
       atomicOr(&ubits[j >> 5], 1u << (j & 31));
     } else {
-      a.dlogg[off] = 0.f;     // padding / ignored slot
+      a.dlogg[off] = 0.f;     // padding / ignored slot (the others come from dK/dV)
     }
   }
   __syncthreads();
@@ -465,10 +548,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     const int j = a.idx[off];
     if (j >= 0 && j <= c) {
       const int rank = pcnt[tl * NBW + (j >> 5)] + __popc(bits[tl * NBW + (j >> 5)] & ((1u << (j & 31)) - 1u));
-      if (rank < S) {
-        lgs[tl * S + rank] = a.logg[off] * kLog2e;
-        slot_of[tl * S + rank] = static_cast<uint8_t>(s);
-      }
+      if (rank < S) slot_of[tl * S + rank] = static_cast<uint8_t>(s);
     }
   }
   if (wv == 0) {
@@ -489,12 +569,11 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     if (lane == 0) *s_nU = base;
   }
 
+  // ---- per-tile rows: row l16 -> token l16 / G, head l16 % G
   const int G = a.G, TPT = a.TPT;
-  int tl_row[TW];
+  int tl_row[TW], hh_row[TW];
   bool valid[TW];
-  uint4 qa[TW][NKS], da[TW][NKS];
   floatx4 dqa[TW][NDT];
-  float lse2[TW], dlt[TW];
 #pragma unroll
   for (int ti = 0; ti < TW; ++ti) {
     const int tile = wv + NW * ti;
@@ -502,19 +581,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     const int hh = l16 - (l16 / G) * G;
     bool v = (tile < a.ntiles) && (l16 < TPT * G) && (tl < ntok);
     tl_row[ti] = v ? tl : 0;
+    hh_row[ti] = hh;
     const size_t qrow = (static_cast<size_t>(b) * a.T + t0 + tl_row[ti]) * a.Hq + kv * G + hh;
-    const float ls = v ? a.lse[qrow] : -INFINITY;
-    v = v && (ls > -INFINITY);
+    v = v && (a.lse[qrow] > -INFINITY);
     valid[ti] = v;
-    lse2[ti] = v ? ls * kLog2e : 0.f;
-    dlt[ti] = v ? a.delta[qrow] : 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qa[ti][ks] = v ? *reinterpret_cast<const uint4*>(a.q + qrow * D + ks * 32 + g4 * 8)
-                     : make_uint4(0, 0, 0, 0);
-      da[ti][ks] = v ? *reinterpret_cast<const uint4*>(a.dout + qrow * D + ks * 32 + g4 * 8)
-                     : make_uint4(0, 0, 0, 0);
-    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dqa[ti][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -522,37 +592,26 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   __syncthreads();
   const int nU = __builtin_amdgcn_readfirstlane(*s_nU);
 
-  // ---- block staging: K and V rows (chunks XOR-swizzled with lds_swz) into
-  // the LDS ring; K^T operands are read from the K rows with transposing
-  // LDS reads
+  // ---- K staging: the thread's 16-byte units tid + NT * x of a block go
+  // global -> registers -> its LDS ring slot (chunks XOR-swizzled per row)
   const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
-  const uint16_t* vbase = a.v + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
-  // Unit x of this thread belongs to tile x / (TU / NT) (K, then V): the
-  // split is a compile-time property of x because tid < NT.
-  static_assert(TU % NT == 0, "tile split");
-  constexpr int XPT = TU / NT;        // units per thread per tile
+  // offsets inside one batch's K fit 32 bits (T * Hkv * D < 2^31)
+  const int tokstride = a.Hkv * D;
   uint4 stg[UPT];
-  int soff[UPT];
-  int grow[UPT];                      // row within the block
+  int soff[UPT], grow[UPT], gch[UPT];
 #pragma unroll
   for (int x = 0; x < UPT; ++x) {
-    const int tile = x / XPT;
-    const int w = tid + NT * (x - tile * XPT);
-    const int r = w / KCPR, ch = w - r * KCPR;
-    soff[x] = tile * KB + r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
+    const int w = tid + NT * x;
+    const int r = min(w, TU - 1) / KCPR, ch = min(w, TU - 1) % KCPR;
+    soff[x] = r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
     grow[x] = r;
+    gch[x] = ch * 8;
   }
-  // offsets inside one batch's K / V fit 32 bits (T <= 65536, Hkv * D < 2^15)
-  const int tokstride = a.Hkv * D;
   auto gload = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int tile = x / XPT;
-      const int w = tid + NT * (x - tile * XPT);
-      const int r = grow[x], ch = w - r * KCPR;
-      const int tok = min(j * 64 + r, a.T - 1);
-      stg[x] = ld16((tile == 0 ? kbase : vbase) + (tok * tokstride + ch * 8));
-    }
+    for (int x = 0; x < UPT; ++x)
+      if (tid + NT * x < TU)
+        stg[x] = ld16(kbase + (min(j * 64 + grow[x], a.T - 1) * tokstride + gch[x]));
   };
   // The wave's share of block `nxt` sits in stg; it is written to its slot as
   // soon as every wave is done with the slot's previous block, and the share
@@ -565,7 +624,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       if (ring_count(&done_cnt[sl]) >= static_cast<unsigned>(NW * (nxt / R))) {
         uint8_t* dst = ring + sl * STAGE;
 #pragma unroll
-        for (int x = 0; x < UPT; ++x) st16(dst + soff[x], stg[x]);
+        for (int x = 0; x < UPT; ++x)
+          if (tid + NT * x < TU) st16(dst + soff[x], stg[x]);
         ring_bump(&fill_cnt[sl], lane);
         ++nxt;
         if (nxt < nU) gload(ulist[nxt]);
@@ -573,28 +633,64 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     }
   };
 
-  int kofs[NKS];
+  // ---- dS rows of a block for the wave's tiles: lane (row l16, g4) takes
+  // operand positions 8 g4 .. 8 g4 + 7 of each 32-key step k2, hi and lo
+  // (rows of tokens that did not select the block: zero)
+  // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hkv * S + sl) * G + hh) * 128
+  // (a 32-bit offset within the query block)
+  const uint16_t* const dsq = a.dsbuf + rowbase * S * a.G * 128;
+  const int HSG = a.Hkv * S;
+  auto tile_sel = [&](int ti, int jw, uint32_t jbit) __attribute__((always_inline)) {
+    return valid[ti] && (bits[tl_row[ti] * NBW + jw] & jbit);
+  };
+  auto load_ds = [&](int j, uint4 (&hb)[TW][2], uint4 (&lb)[TW][2]) __attribute__((always_inline)) {
+    const int jw = j >> 5;
+    const uint32_t jbit = 1u << (j & 31);
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    kofs[ks] = l16 * KROWB + (((ks * 4 + g4) ^ lds_swz<KROWB>(l16)) << 4);
+    for (int ti = 0; ti < TW; ++ti) {
+      const int tl = tl_row[ti];
+      if (tile_sel(ti, jw, jbit)) {
+        const int rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
+        const int sl = slot_of[tl * S + rank];
+        const uint16_t* src = dsq + (((tl * HSG + sl) * G + hh_row[ti]) * 128 + 8 * g4);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          hb[ti][k2] = ld16(src + 32 * k2);
+          lb[ti][k2] = ld16(src + 64 + 32 * k2);
+        }
+      } else {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) hb[ti][k2] = lb[ti][k2] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto block_active = [&](int v) __attribute__((always_inline)) {
+    const int j = ulist[v];
+    bool any = false;
+#pragma unroll
+    for (int ti = 0; ti < TW; ++ti) any = any || tile_sel(ti, j >> 5, 1u << (j & 31));
+    return ballot64(any) != 0;
+  };
+  uint4 nhb[TW][2], nlb[TW][2];     // prefetched dS of block `na`
+  int na = 0;
+  if (PF) {
+    while (na < nU && !block_active(na)) ++na;
+    if (na < nU) load_ds(ulist[na], nhb, nlb);
+  }
+
   // K^T operand of dQ^T = K^T dS^T for d tile dt and 32-key step k2: lane
   // (l16, g4) needs K[key][16 dt + l16] for keys 32 k2 + 4 g4 + {0..3} and
-  // 32 k2 + 16 + 4 g4 + {0..3} (the order in which the S^T accumulator hands
-  // over dS).  A transposing read (ds_read_b64_tr_b16) gives each lane of a
-  // 16-lane group one column of a 4-row x 16-column block when source lane s
-  // addresses row base + s / 4, columns 4 (s % 4) .. 4 (s % 4) + 3.  The row's
-  // swizzle depends only on the lane (the steps between reads are multiples of
-  // 16 rows), so one offset per d tile serves all reads.
-  // (2 dt + h) ^ swz = 2 (dt ^ (swz >> 1)) + (h ^ (swz & 1)) for h = 0, 1.
+  // 32 k2 + 16 + 4 g4 + {0..3} (the stored operand order of dS).  A
+  // transposing read (ds_read_b64_tr_b16) gives each lane of a 16-lane group
+  // one column of a 4-row x 16-column block when source lane s addresses row
+  // base + s / 4, columns 4 (s % 4) .. 4 (s % 4) + 3.  The row's swizzle
+  // depends only on the lane (the steps between reads are multiples of 16
+  // rows); (2 dt + h) ^ swz = 2 (dt ^ (swz >> 1)) + (h ^ (swz & 1)).
   const int trow = 4 * g4 + (l16 >> 2);
   const int tswz = lds_swz<KROWB>(trow);
   const int tbase0 = trow * KROWB + ((((l16 & 3) >> 1) ^ (tswz & 1)) << 4) + 8 * (l16 & 1);
   const int tx = tswz >> 1;
 
-  // d log g of (token tl, slot s) of this query block: dlg[tl * HS + s]
-  float* const dlg = a.dlogg + rowbase * S;
-  const int HS = a.Hkv * S;
-  const float sl2 = a.scale_log2;
   bool failed = false;
   for (int u = 0; u < nU; ++u) {
     const int sl = u % R;
@@ -614,98 +710,36 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     }
     const uint8_t* st = ring + sl * STAGE;
     const int j = ulist[u];
-    const uint32_t jbit = 1u << (j & 31);
-    const int jw = j >> 5;
-    const bool cur = (j == c);
-    bool sel[TW], act[TW];
+    uint4 hb[TW][2], lb[TW][2];
+    bool act[TW];
+    if (PF) {
+      if (u != na) {
+        ring_bump(&done_cnt[sl], lane);
+        continue;
+      }
 #pragma unroll
-    for (int ti = 0; ti < TW; ++ti) {
-      sel[ti] = valid[ti] && (bits[tl_row[ti] * NBW + jw] & jbit);
-      act[ti] = ballot64(sel[ti]) != 0;
+      for (int ti = 0; ti < TW; ++ti) {
+        act[ti] = true;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          hb[ti][k2] = nhb[ti][k2];
+          lb[ti][k2] = nlb[ti][k2];
+        }
+      }
+      ++na;
+      while (na < nU && !block_active(na)) ++na;
+      if (na < nU) load_ds(ulist[na], nhb, nlb);
+    } else {
+#pragma unroll
+      for (int ti = 0; ti < TW; ++ti) act[ti] = ballot64(tile_sel(ti, j >> 5, 1u << (j & 31))) != 0;
+      load_ds(j, hb, lb);
     }
 #pragma unroll
     for (int ti = 0; ti < TW; ++ti) {
       if (!act[ti]) continue;
-      // S^T = K Q^T and dP^T = V dO^T  [16 keys x 16 rows per mt]
-      floatx4 sacc[4], pacc[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        pacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(st + mt * 16 * KROWB + kofs[ks]);
-          const uint4 va = *reinterpret_cast<const uint4*>(st + KB + mt * 16 * KROWB + kofs[ks]);
-          sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
-          pacc[mt] = mfma16x16x32(va, da[ti][ks], pacc[mt]);
-        }
-      }
-      // a block's compute is long: hand over this wave's next share now, so
-      // that the other waves do not wait for its end
-      try_write();
-      const int tl = tl_row[ti];
-      float lgv = 0.f;
-      int rank = 0;
-      if (sel[ti]) {
-        rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
-        lgv = lgs[tl * S + rank];
-      }
-      // rows of tokens that did not select the block get P = 0
-      const float bias = sel[ti] ? lgv - lse2[ti] : -INFINITY;
-      float dsv[4][4];
-      if (cur) {
-        const int lim = t0 + tl - j * 64 - g4 * 4;   // causal limit (key offset)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pp = (mt * 16 + i <= lim) ? fast_exp2(fmaf(sacc[mt][i], sl2, bias)) : 0.f;
-            dsv[mt][i] = pp * (pacc[mt][i] - dlt[ti]);
-          }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            dsv[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, bias)) * (pacc[mt][i] - dlt[ti]);
-      }
-      // pairwise row sum of dS over this lane's keys, then over the row's lanes
-      float rq[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) rq[mt] = (dsv[mt][0] + dsv[mt][1]) + (dsv[mt][2] + dsv[mt][3]);
-      float rs = (rq[0] + rq[1]) + (rq[2] + rq[3]);
-      rs = row4_sum(rs);
-      // dlogg: sum the G rows of each token of this tile (lanes G*k .. G*k+G-1)
-      if ((G & (G - 1)) == 0) {
-        const float tot = group_sum_pow2(rs, G);
-        if (g4 == 0 && sel[ti] && (l16 & (G - 1)) == 0)
-          dlg[tl * HS + slot_of[tl * S + rank]] = tot;
-      } else {
-        if (g4 == 0) red[wv * 16 + l16] = rs;
-        __builtin_amdgcn_wave_barrier();
-        if (g4 == 0 && l16 < TPT) {
-          const int tlr = (wv + NW * ti) * TPT + l16;
-          if (tlr < ntok && (bits[tlr * NBW + jw] & jbit)) {
-            float tot = 0.f;
-            for (int h = 0; h < G; ++h) tot += red[wv * 16 + l16 * G + h];
-            const int rk = pcnt[tlr * NBW + jw] + __popc(bits[tlr * NBW + jw] & (jbit - 1u));
-            dlg[tlr * HS + slot_of[tlr * S + rk]] = tot;
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-      uint4 dsb[2], dsl[2];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        split_bf2(dsv[2 * k2][0], dsv[2 * k2][1], dsb[k2].x, dsl[k2].x);
-        split_bf2(dsv[2 * k2][2], dsv[2 * k2][3], dsb[k2].y, dsl[k2].y);
-        split_bf2(dsv[2 * k2 + 1][0], dsv[2 * k2 + 1][1], dsb[k2].z, dsl[k2].z);
-        split_bf2(dsv[2 * k2 + 1][2], dsv[2 * k2 + 1][3], dsb[k2].w, dsl[k2].w);
-      }
       // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row]
-      // recomputed per tile rather than kept live: registers are scarce here
       int tbase = tbase0;
-      asm volatile("" : "+v"(tbase));
+      asm volatile("" : "+v"(tbase));     // recomputed per tile rather than kept live
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint8_t* tp = st + tbase + ((dt ^ tx) << 5);
@@ -714,8 +748,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
           const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
           const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
           const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          dqa[ti][dt] = mfma16x16x32(kta, dsb[k2], dqa[ti][dt]);
-          dqa[ti][dt] = mfma16x16x32(kta, dsl[k2], dqa[ti][dt]);
+          dqa[ti][dt] = mfma16x16x32(kta, hb[ti][k2], dqa[ti][dt]);
+          dqa[ti][dt] = mfma16x16x32(kta, lb[ti][k2], dqa[ti][dt]);
         }
       }
     }
@@ -745,25 +779,24 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   }
 }
 
-// Launch with the deepest LDS ring (4 or 3 slots) whose layout fits.
-template <int D, int NW, int TW>
+// Launch with the deepest LDS ring (8, 6 or 4 slots of one K tile) whose
+// layout fits.
+template <int D, int TW>
 hipError_t launch_dq_ring(const BwdParams& p, unsigned nblk, hipStream_t st) {
-  constexpr int STAGE = 256 * D;     // K tile + V tile
-  const WalkLds L4 = walk_lds(4, STAGE, p.NB, p.S, NW, true);
-  const WalkLds L3 = walk_lds(3, STAGE, p.NB, p.S, NW, true);
-  if (L4.total <= kLdsBytes) {
-    auto k = dq_kernel<D, NW, TW, 4>;
+  constexpr int STAGE = 128 * D;     // K tile
+  constexpr int NW = 16;
+  const int l8 = dq_lds(8, STAGE, p.NB, p.S).total;
+  const int l6 = dq_lds(6, STAGE, p.NB, p.S).total;
+  const int l4 = dq_lds(4, STAGE, p.NB, p.S).total;
+  auto go = [&](auto k, int bytes) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, L4.total);
-    hipLaunchKernelGGL(k, dim3(nblk), dim3(NW * 64), L4.total, st, p);
-  } else if (L3.total <= kLdsBytes) {
-    auto k = dq_kernel<D, NW, TW, 3>;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, L3.total);
-    hipLaunchKernelGGL(k, dim3(nblk), dim3(NW * 64), L3.total, st, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    hipLaunchKernelGGL(k, dim3(nblk), dim3(NW * 64), bytes, st, p);
+  };
+  if (l8 <= kLdsBytes) go(dq_kernel<D, NW, TW, 8>, l8);
+  else if (l6 <= kLdsBytes) go(dq_kernel<D, NW, TW, 6>, l6);
+  else if (l4 <= kLdsBytes) go(dq_kernel<D, NW, TW, 4>, l4);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -783,18 +816,9 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
                      dim3(256), 0, st, p);
   timing_mark(2, st);
-  hipError_t e;
-  if (p.ntiles <= 8) {
-    e = launch_dq_ring<D, 8, 1>(p, nblk, st);
-  } else if (p.ntiles <= 16) {
-    e = launch_dq_ring<D, 8, 2>(p, nblk, st);
-  } else {
-    switch ((p.ntiles + 7) / 8) {
-      case 3: e = launch_dq_ring<D, 8, 3>(p, nblk, st); break;
-      case 4: e = launch_dq_ring<D, 8, 4>(p, nblk, st); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
+  // 16 waves: one row tile each up to 16 tiles (G <= 4), two beyond
+  const hipError_t e = p.ntiles <= 16 ? launch_dq_ring<D, 1>(p, nblk, st)
+                                      : launch_dq_ring<D, 2>(p, nblk, st);
   if (e != hipSuccess) return e;
   timing_mark(3, st);
   return hipGetLastError();

@@ -98,7 +98,7 @@ FwdWs fwd_ws_layout(const sas_dims* d) {
 }
 size_t fwd_ws(const sas_dims* d) { return fwd_ws_layout(d).total; }
 
-struct BwdWs { size_t delta, cnt2d, rowptr, entries, total; };
+struct BwdWs { size_t delta, cnt2d, rowptr, entries, ds, total; };
 BwdWs bwd_ws(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
   const size_t S = d->topk + 1;
@@ -107,7 +107,9 @@ BwdWs bwd_ws(const sas_dims* d) {
   w.cnt2d = align_up(w.delta + sizeof(float) * static_cast<size_t>(d->B) * d->T * d->Hq);
   w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
   w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
-  w.total = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
+  w.ds = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
+  // dS of every selected (token, head, slot): 64 keys x (hi, lo) bf16
+  w.total = align_up(w.ds + 256 * static_cast<size_t>(d->B) * d->T * d->Hq * S);
   return w;
 }
 
@@ -303,6 +305,7 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
   p.cnt2d = reinterpret_cast<int32_t*>(base + w.cnt2d);
   p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
   p.entries = reinterpret_cast<int32_t*>(base + w.entries);
+  p.dsbuf = reinterpret_cast<uint16_t*>(base + w.ds);
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
   p.TPT = 16 / p.G;

@@ -176,6 +176,12 @@ __device__ __forceinline__ float group_sum_pow2(float x, int n) {
   return x;
 }
 
+// Sum over each row of 16 lanes (the 8-lane sums, then the row mirror).
+__device__ __forceinline__ float row16_sum(float x) {
+  x = group_sum_pow2(x, 8);
+  return x + dpp_mov<0x140>(x);        // row_mirror
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -102,6 +102,11 @@ struct BwdParams {
   int32_t* cnt2d;       // [B,Hkv,NQB,NB]  per (query block, key block) counts -> offsets
   int32_t* rowptr;      // [B,Hkv,NB+1]
   int32_t* entries;     // [B,Hkv,T*S] packed (t << 6) | slot
+  // [B,T,Hkv,S,G][hi 64 | lo 64] bf16: dS of each selected (token, head, slot)
+  // as bf16 hi + lo parts, the 64 keys of the block in MFMA operand order
+  // (position 32 k2 + 8 g + e holds key 32 k2 + 4 g + e for e < 4, else
+  // key 32 k2 + 16 + 4 g + e - 4)
+  uint16_t* dsbuf;
   int B, T, Hq, Hkv, D, G, S, NB;
   int TPT, ntiles;
   float scale, scale_log2;

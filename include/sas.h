@@ -212,7 +212,10 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
  *   times |dout| sqrt(D), otherwise dominates the error of dlogg);
  *   dq [B,T,Hq,D], dk, dv [B,T,Hkv,D] bf16 (fully overwritten, fp32
  *   accumulation); dlogg [B,T,Hkv,K+1] fp32.
- *   ws: sas_workspace_size(SAS_OP_BWD, d) bytes.
+ *   ws: sas_workspace_size(SAS_OP_BWD, d) bytes; it includes dS of every
+ *   selected (token, head, slot) as bf16 hi + lo parts, 256 bytes each
+ *   (B * T * Hq * (K+1) * 256 bytes: 8.6 GB at T = 32768, Hq = 32, K = 31),
+ *   written by the dK/dV kernel and read by the dQ kernel.
  *   Deterministic (bitwise repeatable).
  */
 sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
