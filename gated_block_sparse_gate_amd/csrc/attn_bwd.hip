@@ -671,11 +671,15 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     for (int ti = 0; ti < TW; ++ti) any = any || tile_sel(ti, j >> 5, 1u << (j & 31));
     return ballot64(any) != 0;
   };
-  uint4 nhb[TW][2], nlb[TW][2];     // prefetched dS of block `na`
+  // Prefetch (one row tile per wave): right after a block's products have
+  // read the dS registers, the same registers start loading the dS rows of
+  // the wave's next active block `na`, which are then in flight while the
+  // wave passes the blocks in between.
+  uint4 hb0[TW][2], lb0[TW][2];
   int na = 0;
   if (PF) {
     while (na < nU && !block_active(na)) ++na;
-    if (na < nU) load_ds(ulist[na], nhb, nlb);
+    if (na < nU) load_ds(ulist[na], hb0, lb0);
   }
 
   // K^T operand of dQ^T = K^T dS^T for d tile dt and 32-key step k2: lane
@@ -710,48 +714,42 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     }
     const uint8_t* st = ring + sl * STAGE;
     const int j = ulist[u];
-    uint4 hb[TW][2], lb[TW][2];
-    bool act[TW];
-    if (PF) {
-      if (u != na) {
-        ring_bump(&done_cnt[sl], lane);
-        continue;
-      }
+    // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row] for the active tiles
+    auto tile_mfma = [&](const bool (&act)[TW], const uint4 (&hb)[TW][2], const uint4 (&lb)[TW][2])
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int ti = 0; ti < TW; ++ti) {
-        act[ti] = true;
+        if (!act[ti]) continue;
+        int tbase = tbase0;
+        asm volatile("" : "+v"(tbase));     // recomputed per tile rather than kept live
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          hb[ti][k2] = nhb[ti][k2];
-          lb[ti][k2] = nlb[ti][k2];
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint8_t* tp = st + tbase + ((dt ^ tx) << 5);
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
+            const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
+            const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            dqa[ti][dt] = mfma16x16x32(kta, hb[ti][k2], dqa[ti][dt]);
+            dqa[ti][dt] = mfma16x16x32(kta, lb[ti][k2], dqa[ti][dt]);
+          }
         }
       }
-      ++na;
-      while (na < nU && !block_active(na)) ++na;
-      if (na < nU) load_ds(ulist[na], nhb, nlb);
+    };
+    if (PF) {
+      if (u == na) {
+        const bool all[TW] = {true};
+        tile_mfma(all, hb0, lb0);
+        ++na;
+        while (na < nU && !block_active(na)) ++na;
+        if (na < nU) load_ds(ulist[na], hb0, lb0);
+      }
     } else {
+      bool act[TW];
 #pragma unroll
       for (int ti = 0; ti < TW; ++ti) act[ti] = ballot64(tile_sel(ti, j >> 5, 1u << (j & 31))) != 0;
-      load_ds(j, hb, lb);
-    }
-#pragma unroll
-    for (int ti = 0; ti < TW; ++ti) {
-      if (!act[ti]) continue;
-      // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row]
-      int tbase = tbase0;
-      asm volatile("" : "+v"(tbase));     // recomputed per tile rather than kept live
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint8_t* tp = st + tbase + ((dt ^ tx) << 5);
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
-          const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
-          const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          dqa[ti][dt] = mfma16x16x32(kta, hb[ti][k2], dqa[ti][dt]);
-          dqa[ti][dt] = mfma16x16x32(kta, lb[ti][k2], dqa[ti][dt]);
-        }
-      }
+      load_ds(j, hb0, lb0);
+      tile_mfma(act, hb0, lb0);
     }
     ring_bump(&done_cnt[sl], lane);
   }
