@@ -173,9 +173,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t dOt[2][D * TP];
   __shared__ float m_lse2[3][32], m_delta[3][32], m_lg2[3][32];
   __shared__ int m_t[3][32], m_src[3][32], m_ent[3][32];
-  // dS of the tile pair, [32 rows][hi 64 | lo 64] bf16 in operand key order,
-  // and each wave's row sums of dS over its 16 keys
-  __shared__ __attribute__((aligned(16))) uint8_t dsT[32 * 256];
+  // dS of the tile pair, [32 rows][hi 64 | lo 64] bf16 in operand key order
+  // (row pitch 272 bytes: rows 4 apart start on different banks), and each
+  // wave's row sums of dS over its 16 keys
+  constexpr int DSP = 272;
+  __shared__ __attribute__((aligned(16))) uint8_t dsT[32 * DSP];
   __shared__ float dsum[4][32];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         const int tk = en >> 6, sl = en & 63, hh = (r & 15) % G;
         uint16_t* dst = p.dsbuf +
             ((((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + sl) * G + hh) * 128 + part * 8;
-        st16(dst, ld16(dsT + r * 256 + part * 16));
+        st16(dst, ld16(dsT + r * DSP + part * 16));
       }
     }
     if (tid < 2 * TPT) {
@@ -380,20 +382,42 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       }
     // the previous pair's dS tile has been read (store_ds) by every thread
     __syncthreads();
-    // dS as bf16 hi + lo into the tile (row r, this lane's key), and the row
-    // sums of dS over this wave's 16 keys
+    // dS as bf16 hi + lo into the tile.  Lane (l16, g4) holds rows 4 g4 + i
+    // (i = 0..3) of its key 16 wv + l16; the lanes of an even/odd key pair
+    // (adjacent operand positions) swap halves so that each writes two rows
+    // as 32-bit (two-key) words: the even lane rows 0, 1, the odd lane rows 2, 3.
+    {
+      const bool odd = l16 & 1;
+      const int pe = kpos & ~1;                 // operand position of the even key
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = tt * 16 + g4 * 4 + i;
-        const uint16_t hi = f2bf(ds[tt][i]);
-        const uint16_t lo = f2bf(ds[tt][i] - bf2f(hi));
-        *reinterpret_cast<uint16_t*>(dsT + r * 256 + 2 * kpos) = hi;
-        *reinterpret_cast<uint16_t*>(dsT + r * 256 + 128 + 2 * kpos) = lo;
-        const float rsum = row16_sum(ds[tt][i]);
-        if (l16 == 0) dsum[wv][r] = rsum;
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t h01, l01, h23, l23;           // (row 0 | row 1 << 16), ...
+        split_bf2(ds[tt][0], ds[tt][1], h01, l01);
+        split_bf2(ds[tt][2], ds[tt][3], h23, l23);
+        const uint32_t rh = __float_as_uint(dpp_mov<0xB1>(__uint_as_float(odd ? h01 : h23)));
+        const uint32_t rl = __float_as_uint(dpp_mov<0xB1>(__uint_as_float(odd ? l01 : l23)));
+        const uint32_t ah = odd ? rh : h01, bh = odd ? h23 : rh;   // even key, odd key
+        const uint32_t al = odd ? rl : l01, bl = odd ? l23 : rl;
+        uint8_t* row0 = dsT + (tt * 16 + 4 * g4 + 2 * (l16 & 1)) * DSP + 2 * pe;
+        *reinterpret_cast<uint32_t*>(row0) = __builtin_amdgcn_perm(bh, ah, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(row0 + 128) = __builtin_amdgcn_perm(bl, al, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(row0 + DSP) = __builtin_amdgcn_perm(bh, ah, 0x07060302u);
+        *reinterpret_cast<uint32_t*>(row0 + DSP + 128) = __builtin_amdgcn_perm(bl, al, 0x07060302u);
+        // row sums over the wave's 16 keys: halve the row set per exchange
+        // (xor 1: even lanes keep rows 0, 1; xor 2: one row each), then add
+        // the 4 lanes that hold the same row (rotations by 4 and 8)
+        const float sa = dpp_mov<0xB1>(odd ? ds[tt][0] : ds[tt][2]);
+        const float sb = dpp_mov<0xB1>(odd ? ds[tt][1] : ds[tt][3]);
+        const float y0 = (odd ? ds[tt][2] : ds[tt][0]) + sa;
+        const float y1 = (odd ? ds[tt][3] : ds[tt][1]) + sb;
+        const bool hi2 = l16 & 2;
+        float z = (hi2 ? y1 : y0) + dpp_mov<0x4E>(hi2 ? y0 : y1);
+        z += dpp_mov<0x124>(z);                // row_ror:4
+        z += dpp_mov<0x128>(z);                // row_ror:8
+        // lane l16 < 4 now holds row 2 (l16 & 1) + (l16 >> 1) of its g4 group
+        if (l16 < 4) dsum[wv][tt * 16 + 4 * g4 + 2 * (l16 & 1) + (l16 >> 1)] = z;
       }
+    }
     // P and dS enter the products as bf16 hi + lo parts (exact to ~2^-16)
     uint4 pb, pl, db, dl;
     split_bf2(pv[0][0], pv[0][1], pb.x, pl.x);
