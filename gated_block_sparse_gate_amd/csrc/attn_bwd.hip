@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 // Dynamic LDS of the dQ kernel: ring, selection bitmaps, their popcount
 // prefixes, the union bitmap and list, slot numbers by selection rank, and
 // the ring counters.
-struct DqLds { int ring, bits, pcnt, ubits, ulist, slot, cnt, nu, total; };
+struct DqLds { int ring, bits, pcnt, ubits, ulist, slot, act, cnt, nu, total; };
 __host__ __device__ inline DqLds dq_lds(int R, int stage, int NB, int S) {
   const int NBW = (NB + 31) >> 5;
   DqLds L;
@@ -494,7 +494,8 @@ __host__ __device__ inline DqLds dq_lds(int R, int stage, int NB, int S) {
   L.ubits = align16(L.pcnt + 64 * NBW);
   L.ulist = align16(L.ubits + NBW * 4);
   L.slot = align16(L.ulist + NB * 2);
-  L.cnt = align16(L.slot + 64 * S);
+  L.act = align16(L.slot + 64 * S);        // per wave: which union blocks its tile needs
+  L.cnt = align16(L.act + 16 * NBW * 4);
   L.nu = L.cnt + 2 * R * 4;
   L.total = align16(L.nu + 4);
   return L;
@@ -521,6 +522,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   uint32_t* const ubits = reinterpret_cast<uint32_t*>(smem + L.ubits);
   uint16_t* const ulist = reinterpret_cast<uint16_t*>(smem + L.ulist);
   uint8_t* const slot_of = smem + L.slot;                   // [64][S]
+  uint32_t* const actw = reinterpret_cast<uint32_t*>(smem + L.act);    // [NW][NBW] (one tile per wave)
   unsigned* const fill_cnt = reinterpret_cast<unsigned*>(smem + L.cnt);
   unsigned* const done_cnt = fill_cnt + R;
   int* const s_nU = reinterpret_cast<int*>(smem + L.nu);
@@ -642,7 +644,15 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   // of the following block is fetched right after.
   int nxt = 0;
   if (nU > 0) gload(ulist[0]);
-  auto try_write = [&]() __attribute__((always_inline)) {
+  // With defer set, the load of the following share is left to the caller
+  // (flagged in `pending`): an active block issues it after its products, so
+  // that their wait for the dS registers does not include this load.
+  bool pending = false;
+  auto try_write = [&](bool defer) __attribute__((always_inline)) {
+    if (pending) {              // never write a share whose load was not issued
+      gload(ulist[nxt]);
+      pending = false;
+    }
     if (nxt < nU) {
       const int sl = nxt % R;
       if (ring_count(&done_cnt[sl]) >= static_cast<unsigned>(NW * (nxt / R))) {
@@ -652,8 +662,17 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
           if (tid + NT * x < TU) st16(dst + soff[x], stg[x]);
         ring_bump(&fill_cnt[sl], lane);
         ++nxt;
-        if (nxt < nU) gload(ulist[nxt]);
+        if (nxt < nU) {
+          if (defer) pending = true;
+          else gload(ulist[nxt]);
+        }
       }
+    }
+  };
+  auto issue_pending = [&]() __attribute__((always_inline)) {
+    if (pending) {
+      gload(ulist[nxt]);
+      pending = false;
     }
   };
 
@@ -688,12 +707,35 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       }
     }
   };
-  auto block_active = [&](int v) __attribute__((always_inline)) {
-    const int j = ulist[v];
-    bool any = false;
-#pragma unroll
-    for (int ti = 0; ti < TW; ++ti) any = any || tile_sel(ti, j >> 5, 1u << (j & 31));
-    return ballot64(any) != 0;
+  // activity of the wave's tile (one tile per wave) for every union block:
+  // bit v of actw[wv] = some token of the tile selected block ulist[v]
+  if (PF) {
+    const int tile = wv;
+    for (int v0 = 0; v0 < nU; v0 += 64) {
+      const int v = v0 + lane;
+      bool any = false;
+      if (v < nU && tile < a.ntiles) {
+        const int j = ulist[v];
+        for (int k = 0; k < TPT; ++k) {
+          const int tl = tile * TPT + k;
+          if (tl < ntok) any = any || ((bits[tl * NBW + (j >> 5)] >> (j & 31)) & 1u);
+        }
+      }
+      const uint64_t m = ballot64(any);
+      if (lane == 0) {
+        actw[wv * NBW + (v0 >> 5)] = static_cast<uint32_t>(m);
+        if ((v0 >> 5) + 1 < NBW) actw[wv * NBW + (v0 >> 5) + 1] = static_cast<uint32_t>(m >> 32);
+      }
+    }
+  }
+  // first block >= v that the wave's tile needs (nU if none)
+  auto next_active = [&](int v) __attribute__((always_inline)) {
+    while (v < nU) {
+      const uint32_t w = __builtin_amdgcn_readfirstlane(actw[wv * NBW + (v >> 5)]) >> (v & 31);
+      if (w) return min(v + static_cast<int>(__builtin_ctz(w)), nU);
+      v = (v | 31) + 1;
+    }
+    return nU;
   };
   // Prefetch (one row tile per wave): right after a block's products have
   // read the dS registers, the same registers start loading the dS rows of
@@ -702,7 +744,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   uint4 hb0[TW][2], lb0[TW][2];
   int na = 0;
   if (PF) {
-    while (na < nU && !block_active(na)) ++na;
+    na = next_active(0);
     if (na < nU) load_ds(ulist[na], hb0, lb0);
   }
 
@@ -722,15 +764,16 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   bool failed = false;
   for (int u = 0; u < nU; ++u) {
     const int sl = u % R;
-    try_write();
+    try_write(PF && u == na);
     const unsigned need = static_cast<unsigned>(NW * (u / R + 1));
+    if (ring_count(&fill_cnt[sl]) < need) issue_pending();
     for (int it = 0; ring_count(&fill_cnt[sl]) < need; ++it) {
       if (it == kSpinLimit) {
         failed = true;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-      try_write();
+      try_write(false);
     }
     if (failed) {
       ring_fault(lane);
@@ -764,8 +807,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       if (u == na) {
         const bool all[TW] = {true};
         tile_mfma(all, hb0, lb0);
-        ++na;
-        while (na < nU && !block_active(na)) ++na;
+        issue_pending();
+        na = next_active(na + 1);
         if (na < nU) load_ds(ulist[na], hb0, lb0);
       }
     } else {
