@@ -470,89 +470,84 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------- dQ
 // dQ[t, h] = scale * sum over the selected blocks j of dS[t, h, j, :] K_j,
 // with dS as written by the dK/dV kernel (bf16 hi + lo parts, so the product
-// is exact to ~2^-16).  One workgroup = (b, kappa, 64-token query block); it
-// walks the union of the blocks its tokens selected, staging each block's K
-// tile once into a ring of R LDS slots (shared without workgroup barriers,
-// see the ring protocol in sas_device.h).  Wave w owns row tiles w + NW * ti
-// (16 rows = TPT tokens x G heads) and keeps dQ^T in registers; for a block
-// that some token of a tile selected it loads the tile's dS rows (zero rows
-// for the other tokens) and runs dQ^T += K^T dS^T on bf16 MFMA 16x16x32, the
-// K^T operand read from the K tile with transposing LDS reads.  With one tile
-// per wave, the dS rows of the wave's next active block are loaded while the
-// current one is computed.
+// is exact to ~2^-16).
+//
+// One workgroup = (b, kappa, a group of TPW <= 64 consecutive tokens): NCW
+// compute waves, each owning one 16-row tile (TPT tokens x G heads), plus two
+// stager waves.  The stagers copy the K tile of every block in the union of
+// the group's selections, in ascending order, into a ring of R LDS slots with
+// asynchronous global -> LDS copies (up to L blocks in flight each).  A compute
+// wave visits only the blocks its tile needs: it waits for the block's slot to
+// be filled, runs dQ^T += K^T dS^T on bf16 MFMA 16x16x32 (K^T read from the K
+// rows with transposing LDS reads, dS rows loaded from memory, zero rows for
+// tokens that did not select the block), and the dS rows of its next needed
+// block start loading right after.
+//
+// Protocol (all counters in LDS, only growing; no workgroup barrier):
+//  * prog[c]: compute wave c is done with every block below prog[c] (it sets
+//    it to its next needed block after reading one, nU at the end);
+//  * a stager copies its half of block n into slot n % R once
+//    min_c prog[c] >= n - R + 1, and bumps fill[n % R] once the copies have
+//    landed (s_waitcnt vmcnt); before it waits for a slot it publishes all
+//    its copies in flight;
+//  * a compute wave reads block v once fill[v % R] >= 2 * (v / R + 1).
+// Stagers and compute waves run disjoint code, so the compute waves' LDS reads
+// carry no compiler-inserted wait for the copies.
+constexpr int kDqStagers = 2;
+constexpr int kDqInflight = 3;      // blocks in flight per stager (< R)
 
-// Dynamic LDS of the dQ kernel: ring, selection bitmaps, their popcount
-// prefixes, the union bitmap and list, slot numbers by selection rank, and
-// the ring counters.
-struct DqLds { int ring, bits, pcnt, ubits, ulist, slot, act, cnt, nu, total; };
-__host__ __device__ inline DqLds dq_lds(int R, int stage, int NB, int S) {
-  const int NBW = (NB + 31) >> 5;
-  DqLds L;
-  L.ring = 0;
-  L.bits = R * stage;
-  L.pcnt = align16(L.bits + 64 * NBW * 4);
-  L.ubits = align16(L.pcnt + 64 * NBW);
-  L.ulist = align16(L.ubits + NBW * 4);
-  L.slot = align16(L.ulist + NB * 2);
-  L.act = align16(L.slot + 64 * S);        // per wave: which union blocks its tile needs
-  L.cnt = align16(L.act + 16 * NBW * 4);
-  L.nu = L.cnt + 2 * R * 4;
-  L.total = align16(L.nu + 4);
-  return L;
-}
-
-template <int D, int NW, int TW, int R>
-__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
-  constexpr int NT = NW * 64;
+template <int D, int R>
+__global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw) {
   constexpr int KROWB = D * 2;              // bytes per K row
   constexpr int STAGE = 64 * KROWB;         // K tile
   constexpr int TU = STAGE / 16;            // 16-byte units per tile
-  constexpr int UPT = (TU + NT - 1) / NT;   // units per thread per block
+  constexpr int UPS = TU / kDqStagers;      // units per stager per block
+  constexpr int MPS = UPS / 64;             // copies per stager per block
   constexpr int KCPR = KROWB / 16;
   constexpr int NDT = D / 16;
-  constexpr bool PF = TW == 1;              // prefetch the next active block's dS
+  static_assert(UPS % 64 == 0 && R > kDqInflight, "stager split / ring depth");
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int NBW = (a.NB + 31) >> 5;
-  const int S = a.S;
-  const DqLds L = dq_lds(R, STAGE, a.NB, S);
-  uint8_t* const ring = smem + L.ring;                      // slot sl at ring + sl * STAGE
-  uint32_t* const bits = reinterpret_cast<uint32_t*>(smem + L.bits);   // [64][NBW]
-  uint8_t* const pcnt = smem + L.pcnt;                      // [64][NBW]
-  uint32_t* const ubits = reinterpret_cast<uint32_t*>(smem + L.ubits);
-  uint16_t* const ulist = reinterpret_cast<uint16_t*>(smem + L.ulist);
-  uint8_t* const slot_of = smem + L.slot;                   // [64][S]
-  uint32_t* const actw = reinterpret_cast<uint32_t*>(smem + L.act);    // [NW][NBW] (one tile per wave)
-  unsigned* const fill_cnt = reinterpret_cast<unsigned*>(smem + L.cnt);
-  unsigned* const done_cnt = fill_cnt + R;
-  int* const s_nU = reinterpret_cast<int*>(smem + L.nu);
+  __shared__ __attribute__((aligned(16))) uint8_t ring[R * STAGE];
+  __shared__ uint32_t bits[64 * kMaxNBW];     // per-token selection bitmaps [64][NBW]
+  __shared__ uint8_t pcnt[64 * kMaxNBW];      // popcount prefix per word
+  __shared__ uint32_t ubits[kMaxNBW];
+  __shared__ uint16_t ulist[kMaxNB];
+  __shared__ uint8_t slot_of[64 * kMaxS];     // slot numbers by selection rank [64][S]
+  __shared__ uint32_t actw[14 * kMaxNBW];     // per compute wave: which union blocks it needs
+  __shared__ int prog[16];
+  __shared__ unsigned fill_cnt[R];
+  __shared__ int s_nU;
 
   const int tid = threadIdx.x;
+  const int NT = blockDim.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
+  const int NBW = (a.NB + 31) >> 5;
+  const int S = a.S;
 
-  const int NQB = a.NB;
+  const int ngrp = (a.T + tpw - 1) / tpw;
   const int bid = blockIdx.x;
   const int kv = bid % a.Hkv;
   const int rest = bid / a.Hkv;
-  const int c = NQB - 1 - (rest % NQB);
-  const int b = rest / NQB;
-  const int t0 = c * 64;
-  const int ntok = min(64, a.T - t0);
+  const int grp = ngrp - 1 - (rest % ngrp);   // late (long) groups first
+  const int b = rest / ngrp;
+  const int t0 = grp * tpw;
+  const int ntok = min(tpw, a.T - t0);
 
-  // ---- selection bitmaps of the 64 tokens, their union, slots by rank
+  // ---- selection bitmaps of the group's tokens, their union, slots by rank
   for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
   if (tid < NBW) ubits[tid] = 0u;
-  if (tid < 2 * R) fill_cnt[tid] = 0u;          // fill and done counters
+  if (tid < 16) prog[tid] = 0;
+  if (tid < R) fill_cnt[tid] = 0u;
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
-    if (j >= 0 && j <= c) {
+    if (j >= 0 && j <= (t0 + tl) / 64) {
       atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
       atomicOr(&ubits[j >> 5], 1u << (j & 31));
     } else {
@@ -572,7 +567,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     const int tl = e / S, s = e - tl * S;
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
-    if (j >= 0 && j <= c) {
+    if (j >= 0 && j <= (t0 + tl) / 64) {
       const int rank = pcnt[tl * NBW + (j >> 5)] + __popc(bits[tl * NBW + (j >> 5)] & ((1u << (j & 31)) - 1u));
       if (rank < S) slot_of[tl * S + rank] = static_cast<uint8_t>(s);
     }
@@ -592,143 +587,110 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
       }
       base += __shfl(incl, 63, 64);
     }
-    if (lane == 0) *s_nU = base;
-  }
-
-  // ---- per-tile rows: row l16 -> token l16 / G, head l16 % G
-  const int G = a.G, TPT = a.TPT;
-  int tl_row[TW], hh_row[TW];
-  bool valid[TW];
-  floatx4 dqa[TW][NDT];
-#pragma unroll
-  for (int ti = 0; ti < TW; ++ti) {
-    const int tile = wv + NW * ti;
-    const int tl = tile * TPT + l16 / G;
-    const int hh = l16 - (l16 / G) * G;
-    bool v = (tile < a.ntiles) && (l16 < TPT * G) && (tl < ntok);
-    tl_row[ti] = v ? tl : 0;
-    hh_row[ti] = hh;
-    const size_t qrow = (static_cast<size_t>(b) * a.T + t0 + tl_row[ti]) * a.Hq + kv * G + hh;
-    v = v && (a.lse[qrow] > -INFINITY);
-    valid[ti] = v;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) dqa[ti][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (lane == 0) s_nU = base;
   }
   wait_vmem_all();
   __syncthreads();
-  const int nU = __builtin_amdgcn_readfirstlane(*s_nU);
+  const int nU = __builtin_amdgcn_readfirstlane(s_nU);
+  const unsigned nstg = kDqStagers;
 
-  // ---- K staging: the thread's 16-byte units tid + NT * x of a block go
-  // global -> registers -> its LDS ring slot (chunks XOR-swizzled per row)
-  const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
-  // offsets inside one batch's K fit 32 bits (T * Hkv * D < 2^31)
-  const int tokstride = a.Hkv * D;
-  uint4 stg[UPT];
-  int soff[UPT], grow[UPT], gch[UPT];
+  if (wv >= ncw) {
+    // ================================================================ stager
+    const int sg = wv - ncw;                                // 0 or 1
+    const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
+    const int tokstride = a.Hkv * D;       // offsets inside one batch's K fit 32 bits
+    int grow[MPS], gch[MPS];
 #pragma unroll
-  for (int x = 0; x < UPT; ++x) {
-    const int w = tid + NT * x;
-    const int r = min(w, TU - 1) / KCPR, ch = min(w, TU - 1) % KCPR;
-    soff[x] = r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
-    grow[x] = r;
-    gch[x] = ch * 8;
+    for (int m = 0; m < MPS; ++m) {
+      const int pu = sg * UPS + m * 64 + lane;
+      grow[m] = pu / KCPR;
+      gch[m] = ((pu % KCPR) ^ lds_swz<KROWB>(grow[m])) * 8;
+    }
+    // smallest progress word of the compute waves (lanes < ncw <= 14 < 16)
+    auto min_prog = [&]() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      int v = l16 < ncw ? prog[l16] : 0x7fffffff;
+      asm volatile("" ::: "memory");
+      v = min(v, __float_as_int(dpp_mov<0xB1>(__int_as_float(v))));
+      v = min(v, __float_as_int(dpp_mov<0x4E>(__int_as_float(v))));
+      v = min(v, __float_as_int(dpp_mov<0x141>(__int_as_float(v))));
+      v = min(v, __float_as_int(dpp_mov<0x140>(__int_as_float(v))));
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    int oldest = 0;                  // oldest block copied but not published
+    bool failed = false;
+    for (int n = 0; n < nU && !failed; ++n) {
+      if (min_prog() < n - R + 1) {
+        // publish everything in flight, then wait for the slot
+        wait_vmem_all();
+        asm volatile("" ::: "memory");
+        for (; oldest < n; ++oldest) ring_bump(&fill_cnt[oldest % R], lane);
+        for (int it = 0; min_prog() < n - R + 1; ++it) {
+          if (it == kSpinLimit) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (failed) break;
+      }
+      const int j = ulist[n];
+      uint8_t* dst = ring + (n % R) * STAGE + sg * UPS * 16;
+#pragma unroll
+      for (int m = 0; m < MPS; ++m)
+        load_lds16(kbase + (min(j * 64 + grow[m], a.T - 1) * tokstride + gch[m]), dst + m * 1024);
+      if (n - oldest + 1 == kDqInflight) {
+        // the oldest block's copies are older than the (kDqInflight - 1)
+        // newer blocks' copies: wait for them, then publish it
+        __builtin_amdgcn_s_waitcnt(0x0f70 | (((kDqInflight - 1) * MPS) & 15) |
+                                   ((((kDqInflight - 1) * MPS) >> 4) << 14));
+        asm volatile("" ::: "memory");
+        ring_bump(&fill_cnt[oldest % R], lane);
+        ++oldest;
+      }
+    }
+    wait_vmem_all();       // no copy may still be landing when the workgroup ends
+    asm volatile("" ::: "memory");
+    if (failed) {
+      ring_fault(lane);
+    } else {
+      for (; oldest < nU; ++oldest) ring_bump(&fill_cnt[oldest % R], lane);
+    }
+    return;
   }
-  auto gload = [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-    for (int x = 0; x < UPT; ++x)
-      if (tid + NT * x < TU)
-        stg[x] = ld16(kbase + (min(j * 64 + grow[x], a.T - 1) * tokstride + gch[x]));
-  };
-  // The wave's share of block `nxt` sits in stg; it is written to its slot as
-  // soon as every wave is done with the slot's previous block, and the share
-  // of the following block is fetched right after.
-  int nxt = 0;
-  if (nU > 0) gload(ulist[0]);
-  // With defer set, the load of the following share is left to the caller
-  // (flagged in `pending`): an active block issues it after its products, so
-  // that their wait for the dS registers does not include this load.
-  bool pending = false;
-  auto try_write = [&](bool defer) __attribute__((always_inline)) {
-    if (pending) {              // never write a share whose load was not issued
-      gload(ulist[nxt]);
-      pending = false;
-    }
-    if (nxt < nU) {
-      const int sl = nxt % R;
-      if (ring_count(&done_cnt[sl]) >= static_cast<unsigned>(NW * (nxt / R))) {
-        uint8_t* dst = ring + sl * STAGE;
-#pragma unroll
-        for (int x = 0; x < UPT; ++x)
-          if (tid + NT * x < TU) st16(dst + soff[x], stg[x]);
-        ring_bump(&fill_cnt[sl], lane);
-        ++nxt;
-        if (nxt < nU) {
-          if (defer) pending = true;
-          else gload(ulist[nxt]);
-        }
-      }
-    }
-  };
-  auto issue_pending = [&]() __attribute__((always_inline)) {
-    if (pending) {
-      gload(ulist[nxt]);
-      pending = false;
-    }
-  };
 
-  // ---- dS rows of a block for the wave's tiles: lane (row l16, g4) takes
-  // operand positions 8 g4 .. 8 g4 + 7 of each 32-key step k2, hi and lo
-  // (rows of tokens that did not select the block: zero)
-  // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hkv * S + sl) * G + hh) * 128
-  // (a 32-bit offset within the query block)
-  const uint16_t* const dsq = a.dsbuf + rowbase * S * a.G * 128;
-  const int HSG = a.Hkv * S;
-  auto tile_sel = [&](int ti, int jw, uint32_t jbit) __attribute__((always_inline)) {
-    return valid[ti] && (bits[tl_row[ti] * NBW + jw] & jbit);
-  };
-  auto load_ds = [&](int j, uint4 (&hb)[TW][2], uint4 (&lb)[TW][2]) __attribute__((always_inline)) {
-    const int jw = j >> 5;
-    const uint32_t jbit = 1u << (j & 31);
+  // ================================================================ compute
+  const int G = a.G, TPT = a.TPT;
+  const int tile = wv;
+  const int tl_row = min(tile * TPT + l16 / G, 63);
+  const int hh = l16 - (l16 / G) * G;
+  bool valid = (l16 < TPT * G) && (tile * TPT + l16 / G < ntok);
+  {
+    const size_t qrow = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + kv * G + hh;
+    valid = valid && (a.lse[qrow] > -INFINITY);
+  }
+  floatx4 dqa[NDT];
 #pragma unroll
-    for (int ti = 0; ti < TW; ++ti) {
-      const int tl = tl_row[ti];
-      if (tile_sel(ti, jw, jbit)) {
-        const int rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
-        const int sl = slot_of[tl * S + rank];
-        const uint16_t* src = dsq + (((tl * HSG + sl) * G + hh_row[ti]) * 128 + 8 * g4);
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          hb[ti][k2] = ld16(src + 32 * k2);
-          lb[ti][k2] = ld16(src + 64 + 32 * k2);
-        }
-      } else {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) hb[ti][k2] = lb[ti][k2] = make_uint4(0, 0, 0, 0);
+  for (int dt = 0; dt < NDT; ++dt) dqa[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // activity of the tile for every union block: bit v of actw[wv] = some
+  // token of the tile selected block ulist[v]
+  for (int v0 = 0; v0 < nU; v0 += 64) {
+    const int v = v0 + lane;
+    bool any = false;
+    if (v < nU) {
+      const int j = ulist[v];
+      for (int k = 0; k < TPT; ++k) {
+        const int tl = tile * TPT + k;
+        if (tl < ntok) any = any || ((bits[tl * NBW + (j >> 5)] >> (j & 31)) & 1u);
       }
     }
-  };
-  // activity of the wave's tile (one tile per wave) for every union block:
-  // bit v of actw[wv] = some token of the tile selected block ulist[v]
-  if (PF) {
-    const int tile = wv;
-    for (int v0 = 0; v0 < nU; v0 += 64) {
-      const int v = v0 + lane;
-      bool any = false;
-      if (v < nU && tile < a.ntiles) {
-        const int j = ulist[v];
-        for (int k = 0; k < TPT; ++k) {
-          const int tl = tile * TPT + k;
-          if (tl < ntok) any = any || ((bits[tl * NBW + (j >> 5)] >> (j & 31)) & 1u);
-        }
-      }
-      const uint64_t m = ballot64(any);
-      if (lane == 0) {
-        actw[wv * NBW + (v0 >> 5)] = static_cast<uint32_t>(m);
-        if ((v0 >> 5) + 1 < NBW) actw[wv * NBW + (v0 >> 5) + 1] = static_cast<uint32_t>(m >> 32);
-      }
+    const uint64_t m = ballot64(any);
+    if (lane == 0) {
+      actw[wv * NBW + (v0 >> 5)] = static_cast<uint32_t>(m);
+      if ((v0 >> 5) + 1 < NBW) actw[wv * NBW + (v0 >> 5) + 1] = static_cast<uint32_t>(m >> 32);
     }
   }
-  // first block >= v that the wave's tile needs (nU if none)
   auto next_active = [&](int v) __attribute__((always_inline)) {
     while (v < nU) {
       const uint32_t w = __builtin_amdgcn_readfirstlane(actw[wv * NBW + (v >> 5)]) >> (v & 31);
@@ -737,16 +699,28 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
     }
     return nU;
   };
-  // Prefetch (one row tile per wave): right after a block's products have
-  // read the dS registers, the same registers start loading the dS rows of
-  // the wave's next active block `na`, which are then in flight while the
-  // wave passes the blocks in between.
-  uint4 hb0[TW][2], lb0[TW][2];
-  int na = 0;
-  if (PF) {
-    na = next_active(0);
-    if (na < nU) load_ds(ulist[na], hb0, lb0);
-  }
+
+  // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hkv * S + sl) * G + hh) * 128
+  const uint16_t* const dsq = a.dsbuf + rowbase * S * a.G * 128;
+  const int HSG = a.Hkv * S;
+  uint4 hb[2], lb[2];
+  auto load_ds = [&](int j) __attribute__((always_inline)) {
+    const int jw = j >> 5;
+    const uint32_t jbit = 1u << (j & 31);
+    if (valid && (bits[tl_row * NBW + jw] & jbit)) {
+      const int rank = pcnt[tl_row * NBW + jw] + __popc(bits[tl_row * NBW + jw] & (jbit - 1u));
+      const int sl = slot_of[tl_row * S + rank];
+      const uint16_t* src = dsq + (((tl_row * HSG + sl) * G + hh) * 128 + 8 * g4);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        hb[k2] = ld16(src + 32 * k2);
+        lb[k2] = ld16(src + 64 + 32 * k2);
+      }
+    } else {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) hb[k2] = lb[k2] = make_uint4(0, 0, 0, 0);
+    }
+  };
 
   // K^T operand of dQ^T = K^T dS^T for d tile dt and 32-key step k2: lane
   // (l16, g4) needs K[key][16 dt + l16] for keys 32 k2 + 4 g4 + {0..3} and
@@ -761,107 +735,73 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams a) {
   const int tbase0 = trow * KROWB + ((((l16 & 3) >> 1) ^ (tswz & 1)) << 4) + 8 * (l16 & 1);
   const int tx = tswz >> 1;
 
+  int v = next_active(0);
+  if (v < nU) load_ds(ulist[v]);
+  asm volatile("" ::: "memory");
+  prog[wv] = v;                 // done with every block before its first needed one
   bool failed = false;
-  for (int u = 0; u < nU; ++u) {
-    const int sl = u % R;
-    try_write(PF && u == na);
-    const unsigned need = static_cast<unsigned>(NW * (u / R + 1));
-    if (ring_count(&fill_cnt[sl]) < need) issue_pending();
+  while (v < nU) {
+    const int sl = v % R;
+    const unsigned need = nstg * static_cast<unsigned>(v / R + 1);
     for (int it = 0; ring_count(&fill_cnt[sl]) < need; ++it) {
       if (it == kSpinLimit) {
         failed = true;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-      try_write(false);
     }
-    if (failed) {
-      ring_fault(lane);
-      break;
-    }
+    if (failed) break;
     const uint8_t* st = ring + sl * STAGE;
-    const int j = ulist[u];
-    // dQ^T[d, row] += K^T[d, keys] dS^T[keys, row] for the active tiles
-    auto tile_mfma = [&](const bool (&act)[TW], const uint4 (&hb)[TW][2], const uint4 (&lb)[TW][2])
-        __attribute__((always_inline)) {
+    int tbase = tbase0;
+    asm volatile("" : "+v"(tbase));     // recomputed per block rather than kept live
 #pragma unroll
-      for (int ti = 0; ti < TW; ++ti) {
-        if (!act[ti]) continue;
-        int tbase = tbase0;
-        asm volatile("" : "+v"(tbase));     // recomputed per tile rather than kept live
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint8_t* tp = st + tbase + ((dt ^ tx) << 5);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const uint8_t* tp = st + tbase + ((dt ^ tx) << 5);
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
-            const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
-            const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            dqa[ti][dt] = mfma16x16x32(kta, hb[ti][k2], dqa[ti][dt]);
-            dqa[ti][dt] = mfma16x16x32(kta, lb[ti][k2], dqa[ti][dt]);
-          }
-        }
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
+        const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
+        const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        dqa[dt] = mfma16x16x32(kta, hb[k2], dqa[dt]);
+        dqa[dt] = mfma16x16x32(kta, lb[k2], dqa[dt]);
       }
-    };
-    if (PF) {
-      if (u == na) {
-        const bool all[TW] = {true};
-        tile_mfma(all, hb0, lb0);
-        issue_pending();
-        na = next_active(na + 1);
-        if (na < nU) load_ds(ulist[na], hb0, lb0);
-      }
-    } else {
-      bool act[TW];
-#pragma unroll
-      for (int ti = 0; ti < TW; ++ti) act[ti] = ballot64(tile_sel(ti, j >> 5, 1u << (j & 31))) != 0;
-      load_ds(j, hb0, lb0);
-      tile_mfma(act, hb0, lb0);
     }
-    ring_bump(&done_cnt[sl], lane);
+    v = next_active(v + 1);
+    asm volatile("" ::: "memory");
+    if (lane == 0) prog[wv] = v;      // after this wave's last read of the slot
+    asm volatile("" ::: "memory");
+    if (v < nU) load_ds(ulist[v]);
   }
   if (failed) {
+    ring_fault(lane);
 #pragma unroll
-    for (int ti = 0; ti < TW; ++ti)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) dqa[ti][dt] = floatx4{NAN, NAN, NAN, NAN};
+    for (int dt = 0; dt < NDT; ++dt) dqa[dt] = floatx4{NAN, NAN, NAN, NAN};
+    // let the stagers finish: this wave needs nothing more
+    asm volatile("" ::: "memory");
+    if (lane == 0) prog[wv] = nU;
   }
 
-#pragma unroll
-  for (int ti = 0; ti < TW; ++ti) {
-    const int tile = wv + NW * ti;
-    const int tl = tile * TPT + l16 / G;
-    const int hh = l16 - (l16 / G) * G;
-    if (!((tile < a.ntiles) && (l16 < TPT * G) && (tl < ntok))) continue;
-    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh;
+  if (l16 < TPT * G && tile * TPT + l16 / G < ntok) {
+    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + kv * G + hh;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 pk;
-      pk.x = pack_bf2(dqa[ti][dt][0] * a.scale, dqa[ti][dt][1] * a.scale);
-      pk.y = pack_bf2(dqa[ti][dt][2] * a.scale, dqa[ti][dt][3] * a.scale);
+      pk.x = pack_bf2(dqa[dt][0] * a.scale, dqa[dt][1] * a.scale);
+      pk.y = pack_bf2(dqa[dt][2] * a.scale, dqa[dt][3] * a.scale);
       *reinterpret_cast<uint2*>(a.dq + row * D + dt * 16 + g4 * 4) = pk;
     }
   }
 }
 
-// Launch with the deepest LDS ring (8, 6 or 4 slots of one K tile) whose
-// layout fits.
-template <int D, int TW>
-hipError_t launch_dq_ring(const BwdParams& p, unsigned nblk, hipStream_t st) {
-  constexpr int STAGE = 128 * D;     // K tile
-  constexpr int NW = 16;
-  const int l8 = dq_lds(8, STAGE, p.NB, p.S).total;
-  const int l6 = dq_lds(6, STAGE, p.NB, p.S).total;
-  const int l4 = dq_lds(4, STAGE, p.NB, p.S).total;
-  auto go = [&](auto k, int bytes) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    hipLaunchKernelGGL(k, dim3(nblk), dim3(NW * 64), bytes, st, p);
-  };
-  if (l8 <= kLdsBytes) go(dq_kernel<D, NW, TW, 8>, l8);
-  else if (l6 <= kLdsBytes) go(dq_kernel<D, NW, TW, 6>, l6);
-  else if (l4 <= kLdsBytes) go(dq_kernel<D, NW, TW, 4>, l4);
-  else return hipErrorInvalidValue;
+// Tokens per workgroup: 14 compute waves of TPT tokens each, at most 64.
+// Static LDS: ring of 8 K tiles (D = 128: 128 KiB) plus the selection data.
+template <int D>
+hipError_t launch_dq(const BwdParams& p, hipStream_t st) {
+  const int tpw = min(64, 14 * p.TPT);
+  const int ncw = (tpw + p.TPT - 1) / p.TPT;
+  const unsigned ngrp = (p.T + tpw - 1) / tpw;
+  const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * ngrp);
+  hipLaunchKernelGGL((dq_kernel<D, 8>), grid, dim3((ncw + kDqStagers) * 64), 0, st, p, ncw, tpw);
   return hipGetLastError();
 }
 
@@ -881,9 +821,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
                      dim3(256), 0, st, p);
   timing_mark(2, st);
-  // 16 waves: one row tile each up to 16 tiles (G <= 4), two beyond
-  const hipError_t e = p.ntiles <= 16 ? launch_dq_ring<D, 1>(p, nblk, st)
-                                      : launch_dq_ring<D, 2>(p, nblk, st);
+  const hipError_t e = launch_dq<D>(p, st);
   if (e != hipSuccess) return e;
   timing_mark(3, st);
   return hipGetLastError();

@@ -219,17 +219,34 @@ __device__ __forceinline__ void wait_vmem_all() {
 // compiler from moving memory accesses across a bump or a poll.
 constexpr int kSpinLimit = 1 << 21;   // polls (about 0.1 s) before a wait gives up
 
+// The counters are read with plain LDS loads and bumped with an LDS atomic
+// add written as an instruction without results: the compiler treats atomic
+// (or volatile) LDS accesses as possibly touching the destinations of pending
+// asynchronous global -> LDS copies and would wait for all of them first.  A
+// 32-bit LDS load is single-copy atomic.
 __device__ __forceinline__ unsigned ring_count(const unsigned* c) {
   asm volatile("" ::: "memory");
-  const unsigned v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const unsigned v = *c;
   asm volatile("" ::: "memory");
   return __builtin_amdgcn_readfirstlane(v);
 }
 
 __device__ __forceinline__ void ring_bump(unsigned* c, int lane) {
+  typedef __attribute__((address_space(3))) unsigned* lds_u32_ptr;
+  const unsigned addr = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_u32_ptr)c));
   asm volatile("" ::: "memory");
-  if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
   asm volatile("" ::: "memory");
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds + 16 * i.  `lds` must be wave-uniform.  The
+// copy is complete once the wave's vector-memory counter says so (s_waitcnt
+// vmcnt); the compiler orders later LDS reads that may touch the destination
+// (the same LDS variable, or any atomic / volatile LDS access) after it.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds), 16, 0, 0);
 }
 
 // Set (never expected) when a ring wait gave up: the kernel then finishes

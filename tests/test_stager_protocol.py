@@ -1,0 +1,90 @@
+"""CPU event model of the staging protocol with dedicated stager waves
+(dQ kernel, attn_bwd.hip), checked on random interleavings.
+
+Stager waves copy blocks in order into ring slot n % R with asynchronous
+copies (up to L < R blocks in flight each, so two blocks of one slot are
+never in flight together; copies may land in any order).  Before copying block n a stager waits
+until every compute wave's progress word is >= n - R + 1 (all are done with
+the slot's previous block); it bumps fill[n % R] once its copies of block n
+have landed, and publishes everything in flight before it waits.  A compute
+wave visits only the blocks its tile needs: it waits until
+fill[v % R] >= S * (v // R + 1), reads the slot, then sets its progress word to
+its next needed block (or nU).  Checks: no deadlock, no read before all parts
+landed, no part landing in a slot a compute wave still reads.
+"""
+import random
+
+import pytest
+
+
+def run(S, C, R, L, nU, seed, p_act=0.3):
+    rnd = random.Random(seed)
+    act = [[rnd.random() < p_act for _ in range(nU)] for _ in range(C)]
+    fill = [0] * R
+    held = [[None] * S for _ in range(R)]
+    readers = [set() for _ in range(R)]
+
+    def next_act(c, v):
+        while v < nU and not act[c][v]:
+            v += 1
+        return v
+
+    prog = [next_act(c, 0) for c in range(C)]
+    comp = [dict(v=prog[c], st="wait", busy=0) for c in range(C)]
+    stag = [dict(n=0, inflight=[], st="run") for _ in range(S)]
+    t = 0
+    while any(x["v"] < nU for x in comp) or any(s["n"] < nU or s["inflight"] for s in stag):
+        t += 1
+        assert t < 2_000_000, ("deadlock", prog, fill, [(s["n"], len(s["inflight"])) for s in stag])
+        order = [("c", i) for i in range(C)] + [("s", i) for i in range(S)]
+        rnd.shuffle(order)
+        for kind, i in order:
+            if kind == "s":
+                x = stag[i]
+                for blk, tl in list(x["inflight"]):         # copies land
+                    if tl <= t:
+                        sl = blk % R
+                        assert not readers[sl], ("part landed in a slot being read", blk)
+                        held[sl][i] = blk
+                        x["inflight"].remove((blk, tl))
+                        x.setdefault("landed", []).append(blk)
+                # publish landed blocks in order (s_waitcnt semantics: oldest first)
+                landed = sorted(x.get("landed", []))
+                while landed and (not x["inflight"] or landed[0] < min(b for b, _ in x["inflight"])):
+                    fill[landed.pop(0) % R] += 1
+                x["landed"] = landed
+                n = x["n"]
+                if n >= nU:
+                    continue
+                if min(prog) >= n - R + 1 and len(x["inflight"]) < L:
+                    x["inflight"].append((n, t + rnd.randint(2, 50)))
+                    x["n"] += 1
+            else:
+                x = comp[i]
+                if x["v"] >= nU:
+                    continue
+                if x["busy"] > 0:
+                    x["busy"] -= 1
+                    if x["busy"] == 0:
+                        sl = x["v"] % R
+                        assert all(b == x["v"] for b in held[sl]), ("slot changed while read", x["v"])
+                        readers[sl].discard(i)
+                        x["v"] = next_act(i, x["v"] + 1)
+                        prog[i] = x["v"]
+                    continue
+                v, sl = x["v"], x["v"] % R
+                if fill[sl] >= S * (v // R + 1):
+                    assert all(b == v for b in held[sl]), ("read before all parts landed", v, held[sl])
+                    readers[sl].add(i)
+                    x["busy"] = rnd.randint(1, 30)
+
+
+@pytest.mark.parametrize("S,C", [(1, 8), (2, 14), (4, 12)])
+@pytest.mark.parametrize("R", [2, 4, 8])
+def test_stager_protocol_random_interleavings(S, C, R):
+    for L in (1, 3):
+        if L >= R:
+            continue
+        for nU in (0, 1, 2, 5, 17, 40):
+            for seed in range(4):
+                run(S, C, R, L, nU, seed)
