@@ -4,21 +4,22 @@
 // o[t,h] = softmax_tau( scale * q[t,h].k[tau] + logg[t, slot(block(tau))] ) . v
 // over the keys of the blocks selected for (t, kappa = h/G), tau <= t.
 //
-// Schedule (query-block stationary):
-//   one workgroup = (batch b, KV head kappa, query block c) = 64 tokens x G heads.
-//   The workgroup walks the union of the blocks its 64 tokens selected, in
-//   ascending order.  Each block's K tile and V^T tile (from a transposed copy
-//   of V made once per call, keys in operand order) is staged once into
-//   double-buffered LDS (plain 16-byte copies, chunks XOR-swizzled per row so
-//   the MFMA operand reads are conflict-free); the next block's loads are in
-//   flight in registers while the current one is computed, with one
-//   workgroup barrier per block.  A wave owns TW row tiles of 16 rows =
-//   floor(16/G) tokens x G heads; a tile in which no token selected the block
-//   skips it, otherwise S^T = K Q^T and O^T += V^T P^T run on bf16 MFMA
-//   16x16x32 with rows outside the selection masked out.  Online-softmax
-//   state stays in registers (one query row per lane column); the running
-//   reference maximum is moved only when a row's new maximum exceeds it by
-//   more than 2^kLazyLog2, so the output rescale is rare.
+// Schedule (query-group stationary):
+//   one workgroup = (batch b, KV head kappa, a group of TPW <= 64 consecutive
+//   tokens): NCW compute waves, each owning one row tile of 16 rows = TPT
+//   tokens x G heads, plus two stager waves.  The stagers copy the K tile and
+//   the V^T tile (from a transposed copy of V made once per call, keys in
+//   operand order) of every block in the union of the group's selections, in
+//   ascending order, into a ring of R LDS slots with asynchronous global ->
+//   LDS copies (16-byte chunks XOR-swizzled per row, so that the MFMA operand
+//   reads are conflict-free).  A compute wave visits only the blocks its tile
+//   needs: S^T = K Q^T and O^T += V^T P^T on MFMA 16x16x32, with rows outside
+//   the selection masked out.  Online-softmax state stays in registers (one
+//   query row per lane column); the running reference maximum is moved only
+//   when a row's new maximum exceeds it by more than 2^kLazyLog2, so the
+//   output rescale is rare.  The ring protocol is the dQ kernel's (progress
+//   words of the compute waves, fill counters of the stagers, no workgroup
+//   barrier; see attn_bwd.hip).
 #include "sas_kernels.h"
 
 namespace sas {
@@ -26,64 +27,67 @@ namespace sas {
 namespace {
 
 constexpr float kLazyLog2 = 8.f;   // weights stay below 2^8 between rescales
+constexpr int kFwdStagers = 2;     // stager 0 copies K tiles, stager 1 V^T tiles
+constexpr int kFwdInflight = 3;    // blocks in flight per stager (< R)
 
 // HILO (the fp32 output is requested, for the backward's Delta): V^T is the
 // bf16 copy and P enters PV as bf16 hi + lo parts (exact to ~2^-16).
 // Otherwise V^T is the scaled fp16 copy and P enters once, in fp16.
-template <int D, int NW, int TW, bool HILO, int R>
-__global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
-  constexpr int NT = NW * 64;
+template <int D, bool HILO, int R>
+__global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, int tpw) {
   constexpr int KROWB = D * 2;              // bytes per K row
   constexpr int KB = 64 * KROWB;            // K tile bytes
   constexpr int VB = D * 128;               // V^T tile bytes (D rows x 64 keys)
   constexpr int STAGE = KB + VB;
-  constexpr int KU = KB / 16;               // 16-byte K units per tile
-  constexpr int UPT = STAGE / 16 / NT;      // 16-byte units per thread per block
+  constexpr int KU = KB / 16;               // 16-byte units per tile
+  constexpr int MPS = KU / 64;              // copies per stager per block
   constexpr int KCPR = KROWB / 16;          // 16-byte chunks per K row
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  static_assert(STAGE % (16 * NT) == 0, "unit split");
+  static_assert(KB == VB && KU % 64 == 0, "one tile per stager");
+  static_assert(R > kFwdInflight, "ring depth");
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int NBW = (a.NB + 31) >> 5;
-  const int S = a.S;
-  const WalkLds L = walk_lds(R, STAGE, a.NB, S, NW, false);
-  uint8_t* const ring = smem + L.ring;                      // slot sl at ring + sl * STAGE
-  uint32_t* const bits = reinterpret_cast<uint32_t*>(smem + L.bits);   // [64][NBW]
-  uint8_t* const pcnt = smem + L.pcnt;                      // [64][NBW]
-  uint32_t* const ubits = reinterpret_cast<uint32_t*>(smem + L.ubits);
-  uint16_t* const ulist = reinterpret_cast<uint16_t*>(smem + L.ulist);
-  float* const lgs = reinterpret_cast<float*>(smem + L.lgs);          // [64][S]
-  unsigned* const fill_cnt = reinterpret_cast<unsigned*>(smem + L.cnt);
-  unsigned* const done_cnt = fill_cnt + R;
-  int* const s_nU = reinterpret_cast<int*>(smem + L.nu);
+  __shared__ __attribute__((aligned(16))) uint8_t ring[R * STAGE];
+  __shared__ uint32_t bits[64 * kMaxNBW];     // per-token selection bitmaps [64][NBW]
+  __shared__ uint8_t pcnt[64 * kMaxNBW];      // popcount prefix per word
+  __shared__ uint32_t ubits[kMaxNBW];
+  __shared__ uint16_t ulist[kMaxNB];
+  __shared__ float lgs[64 * kMaxS];           // log2 gates by selection rank [64][S]
+  __shared__ uint32_t actw[14 * kMaxNBW];     // per compute wave: which union blocks it needs
+  __shared__ int prog[16];
+  __shared__ unsigned fill_cnt[R];
+  __shared__ int s_nU;
 
   const int tid = threadIdx.x;
+  const int NT = blockDim.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
+  const int NBW = (a.NB + 31) >> 5;
+  const int S = a.S;
+  const int Tp = a.NB * 64;
 
-  const int NQB = (a.T + 63) / 64;
+  const int ngrp = (a.T + tpw - 1) / tpw;
   const int bid = blockIdx.x;
   const int kv = bid % a.Hkv;
   const int rest = bid / a.Hkv;
-  const int c = NQB - 1 - (rest % NQB);
-  const int b = rest / NQB;
-  const int t0 = c * 64;
-  const int ntok = min(64, a.T - t0);
-  const int Tp = a.NB * 64;
+  const int grp = ngrp - 1 - (rest % ngrp);   // late (long) groups first
+  const int b = rest / ngrp;
+  const int t0 = grp * tpw;
+  const int ntok = min(tpw, a.T - t0);
 
-  // ---- selection bitmaps of the 64 tokens, their union, log-gates by rank
+  // ---- selection bitmaps of the group's tokens, their union, log-gates by rank
   for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
   if (tid < NBW) ubits[tid] = 0u;
-  if (tid < 2 * R) fill_cnt[tid] = 0u;          // fill and done counters
+  if (tid < 16) prog[tid] = 0;
+  if (tid < R) fill_cnt[tid] = 0u;
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const int j = a.idx[(rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s];
-    if (j >= 0 && j <= c) {
+    if (j >= 0 && j <= (t0 + tl) / 64) {
       atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
       atomicOr(&ubits[j >> 5], 1u << (j & 31));
     }
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
     const int tl = e / S, s = e - tl * S;
     const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
     const int j = a.idx[off];
-    if (j >= 0 && j <= c) {
+    if (j >= 0 && j <= (t0 + tl) / 64) {
       const uint32_t wbits = bits[tl * NBW + (j >> 5)];
       const int rank = pcnt[tl * NBW + (j >> 5)] + __popc(wbits & ((1u << (j & 31)) - 1u));
       if (rank < S) lgs[tl * S + rank] = a.logg[off] * kLog2e;
@@ -122,91 +126,140 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
       }
       base += __shfl(incl, 63, 64);
     }
-    if (lane == 0) *s_nU = base;
-  }
-
-  // ---- per-tile query rows: row r = l16 -> token r/G, head r%G
-  const int G = a.G, TPT = a.TPT;
-  int tl_row[TW];
-  bool valid[TW];
-  uint4 qa[TW][NKS];
-  floatx4 oacc[TW][NDT];
-  float m_run[TW], l_run[TW];
-#pragma unroll
-  for (int ti = 0; ti < TW; ++ti) {
-    const int tile = wv + NW * ti;
-    const int tl = tile * TPT + l16 / G;
-    const int hh = l16 - (l16 / G) * G;
-    valid[ti] = (tile < a.ntiles) && (l16 < TPT * G) && (tl < ntok);
-    tl_row[ti] = valid[ti] ? tl : 0;
-    const uint16_t* qrow =
-        a.q + ((static_cast<size_t>(b) * a.T + t0 + tl_row[ti]) * a.Hq + kv * G + hh) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qa[ti][ks] = valid[ti] ? *reinterpret_cast<const uint4*>(qrow + ks * 32 + g4 * 8)
-                             : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[ti][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    m_run[ti] = -INFINITY;
-    l_run[ti] = 0.f;
+    if (lane == 0) s_nU = base;
   }
   wait_vmem_all();
   __syncthreads();
-  const int nU = __builtin_amdgcn_readfirstlane(*s_nU);
+  const int nU = __builtin_amdgcn_readfirstlane(s_nU);
 
-  // ---- block staging: the thread's 16-byte units tid + NT*x of a block go
-  // global -> registers -> its LDS ring slot (chunks XOR-swizzled per row)
-  const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
-  const uint16_t* vtbase =
-      a.vt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
-  uint4 stg[UPT];
-  auto gload = [&](int j) __attribute__((always_inline)) {
+  if (wv >= ncw) {
+    // ================================================================ stager
+    // LDS unit p (16 bytes) of a slot holds, for p < KU, chunk (p % KCPR) ^
+    // lds_swz(r) of K row r = p / KCPR, else chunk (v % 8) ^ tr_swz(d) of V^T
+    // row d = v / 8 (v = p - KU); lane i of copy m fetches unit 64 m + i of
+    // its stager's tile.
+    const int sg = wv - ncw;
+    const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
+    const uint16_t* vtbase =
+        a.vt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
+    const int tokstride = a.Hkv * D;       // offsets inside one batch's K fit 32 bits
+    int grow[MPS], goff[MPS];
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int u = tid + NT * x;
-      if (u < KU) {
-        const int r = u / KCPR, ch = u - r * KCPR;
-        const int tok = min(j * 64 + r, a.T - 1);
-        stg[x] = ld16(kbase + (tok * a.Hkv * D + ch * 8));   // < 2^31 within a batch
+    for (int m = 0; m < MPS; ++m) {
+      const int pu = m * 64 + lane;
+      if (sg == 0) {
+        grow[m] = pu / KCPR;
+        goff[m] = ((pu % KCPR) ^ lds_swz<KROWB>(grow[m])) * 8;
       } else {
-        const int v = u - KU;
-        const int d = v >> 3, kc = v & 7;
-        stg[x] = ld16(vtbase + static_cast<size_t>(d) * Tp + j * 64 + kc * 8);
+        const int d = pu >> 3;
+        grow[m] = 0;
+        goff[m] = d * Tp + ((pu & 7) ^ tr_swz(d)) * 8;       // < 2^31 (D * Tp)
       }
     }
-  };
-  // LDS store offsets of this thread's units (loop-invariant): 16-byte-chunk
-  // XOR swizzles for K rows (lds_swz) and V^T rows (tr_swz).
-  int soff[UPT];
+    auto min_prog = [&]() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      int v = l16 < ncw ? prog[l16] : 0x7fffffff;
+      asm volatile("" ::: "memory");
+      v = min(v, __float_as_int(dpp_mov<0xB1>(__int_as_float(v))));
+      v = min(v, __float_as_int(dpp_mov<0x4E>(__int_as_float(v))));
+      v = min(v, __float_as_int(dpp_mov<0x141>(__int_as_float(v))));
+      v = min(v, __float_as_int(dpp_mov<0x140>(__int_as_float(v))));
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    int oldest = 0;                  // oldest block copied but not published
+    bool failed = false;
+    for (int n = 0; n < nU && !failed; ++n) {
+      if (min_prog() < n - R + 1) {
+        // publish everything in flight, then wait for the slot
+        wait_vmem_all();
+        asm volatile("" ::: "memory");
+        for (; oldest < n; ++oldest) ring_bump(&fill_cnt[oldest % R], lane);
+        for (int it = 0; min_prog() < n - R + 1; ++it) {
+          if (it == kSpinLimit) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (failed) break;
+      }
+      const int j = ulist[n];
+      uint8_t* dst = ring + (n % R) * STAGE + sg * KB;
+      if (sg == 0) {
 #pragma unroll
-  for (int x = 0; x < UPT; ++x) {
-    const int u = tid + NT * x;
-    if (u < KU) {
-      const int r = u / KCPR, ch = u - r * KCPR;
-      soff[x] = r * KROWB + ((ch ^ lds_swz<KROWB>(r)) << 4);
+        for (int m = 0; m < MPS; ++m)
+          load_lds16(kbase + (min(j * 64 + grow[m], a.T - 1) * tokstride + goff[m]), dst + m * 1024);
+      } else {
+#pragma unroll
+        for (int m = 0; m < MPS; ++m) load_lds16(vtbase + (goff[m] + j * 64), dst + m * 1024);
+      }
+      if (n - oldest + 1 == kFwdInflight) {
+        // the oldest block's copies are older than the (kFwdInflight - 1)
+        // newer blocks' copies: wait for them, then publish it
+        constexpr int kNewer = (kFwdInflight - 1) * MPS;
+        static_assert(kNewer < 64, "vmcnt immediate");
+        __builtin_amdgcn_s_waitcnt(0x0f70 | (kNewer & 15) | ((kNewer >> 4) << 14));
+        asm volatile("" ::: "memory");
+        ring_bump(&fill_cnt[oldest % R], lane);
+        ++oldest;
+      }
+    }
+    wait_vmem_all();       // no copy may still be landing when the workgroup ends
+    asm volatile("" ::: "memory");
+    if (failed) {
+      ring_fault(lane);
     } else {
-      const int v = u - KU;
-      const int d = v >> 3, kc = v & 7;
-      soff[x] = KB + d * 128 + ((kc ^ tr_swz(d)) << 4);
+      for (; oldest < nU; ++oldest) ring_bump(&fill_cnt[oldest % R], lane);
+    }
+    return;
+  }
+
+  // ================================================================ compute
+  // row r = l16 of the wave's tile -> token r / G, head r % G
+  const int G = a.G, TPT = a.TPT;
+  const int tile = wv;
+  const int tl = min(tile * TPT + l16 / G, 63);
+  const int hh = l16 - (l16 / G) * G;
+  const bool valid = (l16 < TPT * G) && (tile * TPT + l16 / G < ntok);
+  uint4 qa[NKS];
+  floatx4 oacc[NDT];
+  float m_run = -INFINITY, l_run = 0.f;
+  {
+    const uint16_t* qrow =
+        a.q + ((static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qa[ks] = valid ? *reinterpret_cast<const uint4*>(qrow + ks * 32 + g4 * 8)
+                     : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // activity of the tile for every union block: bit v of actw[wv] = some
+  // token of the tile selected block ulist[v]
+  for (int v0 = 0; v0 < nU; v0 += 64) {
+    const int v = v0 + lane;
+    bool any = false;
+    if (v < nU) {
+      const int j = ulist[v];
+      for (int k = 0; k < TPT; ++k) {
+        const int tk = tile * TPT + k;
+        if (tk < ntok) any = any || ((bits[tk * NBW + (j >> 5)] >> (j & 31)) & 1u);
+      }
+    }
+    const uint64_t m = ballot64(any);
+    if (lane == 0) {
+      actw[wv * NBW + (v0 >> 5)] = static_cast<uint32_t>(m);
+      if ((v0 >> 5) + 1 < NBW) actw[wv * NBW + (v0 >> 5) + 1] = static_cast<uint32_t>(m >> 32);
     }
   }
-  // The wave's share of block `nxt` sits in stg; it is written to its slot as
-  // soon as every wave is done with the slot's previous block, and the share
-  // of the following block is fetched right after.
-  int nxt = 0;
-  if (nU > 0) gload(ulist[0]);
-  auto try_write = [&]() __attribute__((always_inline)) {
-    if (nxt < nU) {
-      const int sl = nxt % R;
-      if (ring_count(&done_cnt[sl]) >= static_cast<unsigned>(NW * (nxt / R))) {
-        uint8_t* dst = ring + sl * STAGE;
-#pragma unroll
-        for (int x = 0; x < UPT; ++x) st16(dst + soff[x], stg[x]);
-        ring_bump(&fill_cnt[sl], lane);
-        ++nxt;
-        if (nxt < nU) gload(ulist[nxt]);
-      }
+  auto next_active = [&](int v) __attribute__((always_inline)) {
+    while (v < nU) {
+      const uint32_t w = __builtin_amdgcn_readfirstlane(actw[wv * NBW + (v >> 5)]) >> (v & 31);
+      if (w) return min(v + static_cast<int>(__builtin_ctz(w)), nU);
+      v = (v | 31) + 1;
     }
+    return nU;
   };
 
   // per-lane LDS read offsets of the MFMA operands (immediate offsets add
@@ -220,209 +273,171 @@ __global__ __launch_bounds__(NW * 64) void sparse_fwd_kernel(FwdParams a) {
   for (int k2 = 0; k2 < 2; ++k2) vofs[k2] = KB + l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
 
   const float sl2 = a.scale_log2;
+  const unsigned nstg = kFwdStagers;
+  const int cfirst = t0 / 64;            // earliest current block of the group's tokens
+  int v = next_active(0);
+  asm volatile("" ::: "memory");
+  if (lane == 0) prog[wv] = v;           // done with every block before its first needed one
   bool failed = false;
-  for (int u = 0; u < nU; ++u) {
-    const int sl = u % R;
-    try_write();
-    const unsigned need = static_cast<unsigned>(NW * (u / R + 1));
+  while (v < nU) {
+    const int sl = v % R;
+    const unsigned need = nstg * static_cast<unsigned>(v / R + 1);
     for (int it = 0; ring_count(&fill_cnt[sl]) < need; ++it) {
       if (it == kSpinLimit) {
         failed = true;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-      try_write();
     }
-    if (failed) {
-      ring_fault(lane);
-      break;
-    }
+    if (failed) break;
     const uint8_t* st = ring + sl * STAGE;
-    const int j = ulist[u];
+    const int j = ulist[v];
     const uint32_t jbit = 1u << (j & 31);
     const int jw = j >> 5;
-    const bool cur = (j == c);
-    bool sel[TW];
-    bool act[TW];
-#pragma unroll
-    for (int ti = 0; ti < TW; ++ti) {
-      sel[ti] = valid[ti] && (bits[tl_row[ti] * NBW + jw] & jbit);
-      act[ti] = ballot64(sel[ti]) != 0;
+    const bool sel = valid && (bits[tl * NBW + jw] & jbit);
+    const bool maybe_cur = j >= cfirst;  // the current block of some token of the group
+    float lgv = 0.f;
+    if (sel) {
+      const int rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
+      lgv = lgs[tl * S + rank];
     }
+    // S^T[key, row] = K[key,:] . Q[row,:]
+    floatx4 sacc[4];
 #pragma unroll
-    for (int ti = 0; ti < TW; ++ti) {
-      if (!act[ti]) continue;
-      const int tl = tl_row[ti];
-      float lgv = 0.f;
-      if (sel[ti]) {
-        const int rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
-        lgv = lgs[tl * S + rank];
+    for (int mt = 0; mt < 4; ++mt) {
+      sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(st + mt * 16 * KROWB + kofs[ks]);
+        sacc[mt] = mfma16x16x32(ka, qa[ks], sacc[mt]);
       }
-      // S^T[key, row] = K[key,:] . Q[row,:]
-      floatx4 sacc[4];
+    }
+    // maximum of this lane's raw scores over the keys its row may see (the
+    // row's 64 keys are spread over the 4 lanes g4 of the row); in the
+    // current block the row sees keys 0 .. t - 64 j
+    const int lim = t0 + tl - j * 64 - g4 * 4;
+    float mr = -INFINITY;
+    if (maybe_cur) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(st + mt * 16 * KROWB + kofs[ks]);
-          sacc[mt] = mfma16x16x32(ka, qa[ti][ks], sacc[mt]);
+        for (int i = 0; i < 4; ++i)
+          if (mt * 16 + i <= lim) mr = fmaxf(mr, sacc[mt][i]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        mr = fmaxf(mr, fmaxf(fmaxf(sacc[mt][0], sacc[mt][1]), fmaxf(sacc[mt][2], sacc[mt][3])));
+    }
+    // A row's reference moves only if its maximum passes it by 2^kLazyLog2,
+    // i.e. if one of its lanes does; only then are the 4 lanes' maxima
+    // combined (rare), so the common path needs no cross-lane step.
+    const float cand_l = sel ? mr * sl2 + lgv : -INFINITY;
+    if (ballot64(cand_l > m_run + kLazyLog2)) {
+      const float cand = row4_max(cand_l);
+      const bool up = cand > m_run + kLazyLog2;
+      const float alpha = up ? fast_exp2(m_run - cand) : 1.f;
+      m_run = up ? cand : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
+    const float bias = sel ? lgv - m_run : -INFINITY;
+    float x[4][4];
+    if (maybe_cur) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
+          x[mt][i] = (mt * 16 + i <= lim) ? e : 0.f;
         }
-      }
-      // maximum of this lane's raw scores over the keys its row may see (the
-      // row's 64 keys are spread over the 4 lanes g4 of the row)
-      const int lim = t0 + tl - j * 64 - g4 * 4;     // current block: key offset limit
-      float mr = -INFINITY;
-      if (cur) {
+    } else {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (mt * 16 + i <= lim) mr = fmaxf(mr, sacc[mt][i]);
+        for (int i = 0; i < 4; ++i) x[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
+    }
+    // pairwise sum (short dependency chain)
+    float ps[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) ps[mt] = (x[mt][0] + x[mt][1]) + (x[mt][2] + x[mt][3]);
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    uint4 pb[2], pl[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      if (HILO) {
+        split_bf2(x[2 * k2][0], x[2 * k2][1], pb[k2].x, pl[k2].x);
+        split_bf2(x[2 * k2][2], x[2 * k2][3], pb[k2].y, pl[k2].y);
+        split_bf2(x[2 * k2 + 1][0], x[2 * k2 + 1][1], pb[k2].z, pl[k2].z);
+        split_bf2(x[2 * k2 + 1][2], x[2 * k2 + 1][3], pb[k2].w, pl[k2].w);
       } else {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          mr = fmaxf(mr, fmaxf(fmaxf(sacc[mt][0], sacc[mt][1]), fmaxf(sacc[mt][2], sacc[mt][3])));
+        // fp16 (P <= 2^kLazyLog2, 11-bit significand) against the fp16 V^T
+        pb[k2].x = pack_h2(x[2 * k2][0], x[2 * k2][1]);
+        pb[k2].y = pack_h2(x[2 * k2][2], x[2 * k2][3]);
+        pb[k2].z = pack_h2(x[2 * k2 + 1][0], x[2 * k2 + 1][1]);
+        pb[k2].w = pack_h2(x[2 * k2 + 1][2], x[2 * k2 + 1][3]);
       }
-      // A row's reference moves only if its maximum passes it by 2^kLazyLog2,
-      // i.e. if one of its lanes does; only then are the 4 lanes' maxima
-      // combined (rare), so the common path needs no cross-lane step.
-      const float cand_l = sel[ti] ? mr * sl2 + lgv : -INFINITY;
-      if (ballot64(cand_l > m_run[ti] + kLazyLog2)) {
-        const float cand = row4_max(cand_l);
-        const bool up = cand > m_run[ti] + kLazyLog2;
-        const float alpha = up ? fast_exp2(m_run[ti] - cand) : 1.f;
-        m_run[ti] = up ? cand : m_run[ti];
-        l_run[ti] *= alpha;
+    }
+    // O^T[d, row] += V^T[d, keys] . P^T[keys, row]; inside a 32-key step the
+    // lane's 8 keys are {4g..4g+3, 16+4g..16+4g+3}, stored contiguously in
+    // the transposed copy.
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[ti][dt] *= alpha;
-      }
-      const float bias = sel[ti] ? lgv - m_run[ti] : -INFINITY;
-      float x[4][4];
-      if (cur) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
-            x[mt][i] = (mt * 16 + i <= lim) ? e : 0.f;
-          }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, bias));
-      }
-      // pairwise sum (short dependency chain)
-      float ps[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) ps[mt] = (x[mt][0] + x[mt][1]) + (x[mt][2] + x[mt][3]);
-      const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      l_run[ti] += psum;
-      // a block's compute is long: hand over this wave's next share now, so
-      // that the other waves do not wait for its end
-      try_write();
-      uint4 pb[2], pl[2];
+    for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
+        const uint4 va = *reinterpret_cast<const uint4*>(st + dt * 2048 + vofs[k2]);
         if (HILO) {
-          split_bf2(x[2 * k2][0], x[2 * k2][1], pb[k2].x, pl[k2].x);
-          split_bf2(x[2 * k2][2], x[2 * k2][3], pb[k2].y, pl[k2].y);
-          split_bf2(x[2 * k2 + 1][0], x[2 * k2 + 1][1], pb[k2].z, pl[k2].z);
-          split_bf2(x[2 * k2 + 1][2], x[2 * k2 + 1][3], pb[k2].w, pl[k2].w);
+          oacc[dt] = mfma16x16x32(va, pb[k2], oacc[dt]);
+          oacc[dt] = mfma16x16x32(va, pl[k2], oacc[dt]);
         } else {
-          // fp16 (P <= 2^kLazyLog2, 11-bit significand) against the fp16 V^T
-          pb[k2].x = pack_h2(x[2 * k2][0], x[2 * k2][1]);
-          pb[k2].y = pack_h2(x[2 * k2][2], x[2 * k2][3]);
-          pb[k2].z = pack_h2(x[2 * k2 + 1][0], x[2 * k2 + 1][1]);
-          pb[k2].w = pack_h2(x[2 * k2 + 1][2], x[2 * k2 + 1][3]);
-        }
-      }
-      // O^T[d, row] += V^T[d, keys] . P^T[keys, row]; inside a 32-key step the
-      // lane's 8 keys are {4g..4g+3, 16+4g..16+4g+3}, stored contiguously in
-      // the transposed copy.
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const uint4 va = *reinterpret_cast<const uint4*>(st + dt * 2048 + vofs[k2]);
-          if (HILO) {
-            oacc[ti][dt] = mfma16x16x32(va, pb[k2], oacc[ti][dt]);
-            oacc[ti][dt] = mfma16x16x32(va, pl[k2], oacc[ti][dt]);
-          } else {
-            oacc[ti][dt] = mfma16x16x32h(va, pb[k2], oacc[ti][dt]);
-          }
+          oacc[dt] = mfma16x16x32h(va, pb[k2], oacc[dt]);
         }
       }
     }
-    ring_bump(&done_cnt[sl], lane);
+    v = next_active(v + 1);
+    asm volatile("" ::: "memory");
+    if (lane == 0) prog[wv] = v;         // after this wave's last read of the slot
+    asm volatile("" ::: "memory");
   }
   if (failed) {
-#pragma unroll
-    for (int ti = 0; ti < TW; ++ti) l_run[ti] = NAN;
+    ring_fault(lane);
+    l_run = NAN;
+    asm volatile("" ::: "memory");
+    if (lane == 0) prog[wv] = nU;        // let the stagers finish
   }
 
   // ---- epilogue
   const float vsc = HILO ? 1.f : a.vscale[static_cast<size_t>(b) * a.Hkv + kv];
-#pragma unroll
-  for (int ti = 0; ti < TW; ++ti) {
-    if (!valid[ti]) continue;
-    const float lsum = row4_sum(l_run[ti]);
-    const int tl = tl_row[ti];
-    const int hh = l16 - (l16 / G) * G;
+  if (valid) {
+    const float lsum = row4_sum(l_run);
     const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh;
     const float inv = (lsum > 0.f) ? vsc / lsum : 0.f;   // vsc undoes the V^T scaling
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 pk;
-      pk.x = pack_bf2(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv);
-      pk.y = pack_bf2(oacc[ti][dt][2] * inv, oacc[ti][dt][3] * inv);
+      pk.x = pack_bf2(oacc[dt][0] * inv, oacc[dt][1] * inv);
+      pk.y = pack_bf2(oacc[dt][2] * inv, oacc[dt][3] * inv);
       *reinterpret_cast<uint2*>(a.o + row * D + dt * 16 + g4 * 4) = pk;
       if (a.o32)
         *reinterpret_cast<float4*>(a.o32 + row * D + dt * 16 + g4 * 4) =
-            make_float4(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv, oacc[ti][dt][2] * inv,
-                        oacc[ti][dt][3] * inv);
+            make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
+                        oacc[dt][3] * inv);
     }
-    if (g4 == 0)
-      a.lse[row] = (lsum > 0.f) ? (m_run[ti] + log2f(lsum)) * kLn2 : -INFINITY;
+    if (g4 == 0) a.lse[row] = (lsum > 0.f) ? (m_run + log2f(lsum)) * kLn2 : -INFINITY;
   }
 }
 
-// Launch with the deepest LDS ring (4 or 3 slots) whose layout fits.
-template <int D, int NW, int TW, bool HILO>
-hipError_t launch_fwd_ring(const FwdParams& p, dim3 grid, hipStream_t st) {
-  constexpr int STAGE = 256 * D;     // K tile + V^T tile
-  const WalkLds L4 = walk_lds(4, STAGE, p.NB, p.S, NW, false);
-  const WalkLds L3 = walk_lds(3, STAGE, p.NB, p.S, NW, false);
-  if (L4.total <= kLdsBytes) {
-    auto k = sparse_fwd_kernel<D, NW, TW, HILO, 4>;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, L4.total);
-    hipLaunchKernelGGL(k, grid, dim3(NW * 64), L4.total, st, p);
-  } else if (L3.total <= kLdsBytes) {
-    auto k = sparse_fwd_kernel<D, NW, TW, HILO, 3>;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, L3.total);
-    hipLaunchKernelGGL(k, grid, dim3(NW * 64), L3.total, st, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
+// Tokens per workgroup: 14 compute waves of TPT tokens each, at most 64;
+// static LDS: a ring of 4 (K, V^T) tile pairs plus the selection data.
 template <int D, bool HILO>
 hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
-  const int NQB = (p.T + 63) / 64;
-  const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * NQB);
-  // up to 16 row tiles: one tile per wave, 16 waves (4 per SIMD hide the
-  // latency of the per-tile MFMA -> softmax -> MFMA chain); more tiles
-  // (G >= 5): 8 waves with TW tiles each.
-  if (p.ntiles <= 16) return launch_fwd_ring<D, 16, 1, HILO>(p, grid, st);
-  switch ((p.ntiles + 7) / 8) {
-    case 3: return launch_fwd_ring<D, 8, 3, HILO>(p, grid, st);
-    case 4: return launch_fwd_ring<D, 8, 4, HILO>(p, grid, st);
-    default: return hipErrorInvalidValue;
-  }
+  const int tpw = min(64, 14 * p.TPT);
+  const int ncw = (tpw + p.TPT - 1) / p.TPT;
+  const unsigned ngrp = (p.T + tpw - 1) / tpw;
+  const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * ngrp);
+  hipLaunchKernelGGL((sparse_fwd_kernel<D, HILO, 4>), grid, dim3((ncw + kFwdStagers) * 64), 0, st,
+                     p, ncw, tpw);
+  return hipGetLastError();
 }
 
 template <int D>
