@@ -17,7 +17,7 @@ import random
 import pytest
 
 
-def run(S, C, R, L, nU, seed, p_act=0.3):
+def run(S, C, R, L, nU, seed, p_act=0.3, free_slack=0, ready_slack=0):
     rnd = random.Random(seed)
     act = [[rnd.random() < p_act for _ in range(nU)] for _ in range(C)]
     fill = [0] * R
@@ -56,7 +56,7 @@ def run(S, C, R, L, nU, seed, p_act=0.3):
                 n = x["n"]
                 if n >= nU:
                     continue
-                if min(prog) >= n - R + 1 and len(x["inflight"]) < L:
+                if min(prog) >= n - R + 1 - free_slack and len(x["inflight"]) < L:
                     x["inflight"].append((n, t + rnd.randint(2, 50)))
                     x["n"] += 1
             else:
@@ -73,7 +73,7 @@ def run(S, C, R, L, nU, seed, p_act=0.3):
                         prog[i] = x["v"]
                     continue
                 v, sl = x["v"], x["v"] % R
-                if fill[sl] >= S * (v // R + 1):
+                if fill[sl] >= S * (v // R + 1) - ready_slack:
                     assert all(b == v for b in held[sl]), ("read before all parts landed", v, held[sl])
                     readers[sl].add(i)
                     x["busy"] = rnd.randint(1, 30)
@@ -88,3 +88,17 @@ def test_stager_protocol_random_interleavings(S, C, R):
         for nU in (0, 1, 2, 5, 17, 40):
             for seed in range(4):
                 run(S, C, R, L, nU, seed)
+
+
+@pytest.mark.parametrize("free_slack,ready_slack", [(1, 0), (0, 1)])
+def test_stager_protocol_off_by_one_fails(free_slack, ready_slack):
+    """Loosening either condition by one must be caught by the model."""
+    caught = False
+    for seed in range(40):
+        try:
+            run(2, 14, 4, 3, 40, seed, p_act=0.6, free_slack=free_slack,
+                ready_slack=ready_slack)
+        except AssertionError:
+            caught = True
+            break
+    assert caught
