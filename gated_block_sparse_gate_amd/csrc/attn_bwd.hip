@@ -155,7 +155,9 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(BwdParams p) {
 // ---------------------------------------------------------------- dK, dV
 // One workgroup = one KV block (b, kappa, j); wave w owns keys 16w..16w+15 and
 // keeps their dK^T, dV^T in registers.  The rows of the queries that selected
-// the block arrive as 32-row tile pairs in ascending token order.  Software
+// the block arrive as 32-row tile pairs, taken in descending token order: all
+// workgroups start at the end of the sequence and sweep it at about the same
+// rate, so the ones in flight on an XCD gather from nearby rows.  Software
 // pipeline per tile pair `it`: the CSR entry is read 3 pairs ahead, the row
 // metadata (lse, Delta, log g) 2 ahead, the Q / dO rows 1 ahead (registers),
 // so the gathers overlap the MFMA work of the current pair.
@@ -216,16 +218,20 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   // ---- per-row metadata (threads 0..31, one row each)
   const int mr = tid & 31, mtt = mr >> 4, mrr = mr & 15;
   const int mhh = mrr - (mrr / G) * G;
+  // raw CSR entry of this row in tile pair `it` (-1 past the list); it is
+  // checked only when used, an iteration later, so the load is not waited for
   auto load_ent = [&](int it) -> int {
-    const int ti = it * 2 * TPT + mtt * TPT + mrr / G;
+    const int ti = (nit - 1 - it) * 2 * TPT + mtt * TPT + mrr / G;
     if (mrr >= RT || ti >= n) return -1;
-    const int en = ent[ti];
-    const int tk = en >> 6, s = en & 63;
-    return (tk >= j * 64 && tk < p.T && s < p.S) ? en : -1;
+    return ent[ti];
   };
   float r_lse = -INFINITY, r_del = 0.f, r_lg = 0.f;
   int r_t = -1, r_src = -1, r_en = -1;
   auto meta_issue = [&](int en) {
+    if (en >= 0) {
+      const int tk = en >> 6, s = en & 63;
+      if (tk < j * 64 || tk >= p.T || s >= p.S) en = -1;
+    }
     r_t = -1; r_src = -1; r_en = en;
     if (en >= 0) {
       const int tk = en >> 6, s = en & 63;
@@ -449,6 +455,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       en_n2 = en_n3;
     }
     if (it + 1 < nit) rows_store(buf ^ 1);
+    // every load of this iteration has been used: with the counter empty at
+    // the back edge, the next iteration's register reuse needs no wait after
+    // its own new loads
+    wait_vmem_all();
     __syncthreads();
   }
   if (nit > 0) store_ds(nit - 1);
