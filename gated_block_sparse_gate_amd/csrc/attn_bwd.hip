@@ -173,14 +173,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t dOs[2][32 * ROWB];
   __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TP];
   __shared__ __attribute__((aligned(16))) uint16_t dOt[2][D * TP];
-  __shared__ float m_lse2[3][32], m_delta[3][32], m_lg2[3][32];
-  __shared__ int m_t[3][32], m_src[3][32], m_ent[3][32];
+  // row metadata of three tile pairs in flight, read as 4-row vectors:
+  // token (-1 = no row), log2-domain bias log g - lse, Delta, source row, entry
+  __shared__ __attribute__((aligned(16))) int m_t[3][32];
+  __shared__ __attribute__((aligned(16))) float m_bias[3][32];
+  __shared__ __attribute__((aligned(16))) float m_delta[3][32];
+  __shared__ __attribute__((aligned(16))) int m_src[3][32];
+  __shared__ __attribute__((aligned(16))) int m_ent[3][32];
   // dS of the tile pair, [32 rows][hi 64 | lo 64] bf16 in operand key order
   // (row pitch 272 bytes: rows 4 apart start on different banks), and each
   // wave's row sums of dS over its 16 keys
   constexpr int DSP = 272;
   __shared__ __attribute__((aligned(16))) uint8_t dsT[32 * DSP];
-  __shared__ float dsum[4][32];
+  __shared__ __attribute__((aligned(16))) float dsum[4][32];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -248,9 +253,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     m_t[slot][mr] = ok ? r_t : -1;
     m_src[slot][mr] = ok ? r_src : -1;
     m_ent[slot][mr] = r_en;
-    m_lse2[slot][mr] = ok ? r_lse * kLog2e : 0.f;
+    m_bias[slot][mr] = ok ? r_lg * kLog2e - r_lse * kLog2e : 0.f;
     m_delta[slot][mr] = ok ? r_del : 0.f;
-    m_lg2[slot][mr] = ok ? r_lg * kLog2e : 0.f;
   };
 
   // ---- Q / dO rows (all threads): unit = (chunk ch, row pair rp)
@@ -261,9 +265,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       const int u = tid + 256 * x;
       const int ch = u >> 4, rp = u & 15;
       const uint4 z = make_uint4(0, 0, 0, 0);
+      const int2 sp = (u < UNITS) ? *reinterpret_cast<const int2*>(&m_src[slot][2 * rp])
+                                  : make_int2(-1, -1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int src = (u < UNITS) ? m_src[slot][2 * rp + h] : -1;
+        const int src = h ? sp.y : sp.x;
         rq[x][h] = (src >= 0) ? ld16(p.q + static_cast<size_t>(src) * D + ch * 8) : z;
         rd[x][h] = (src >= 0) ? ld16(p.dout + static_cast<size_t>(src) * D + ch * 8) : z;
       }
@@ -327,27 +333,42 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   // (each (token, slot) is in exactly one tile pair of one workgroup)
   auto store_ds = [&](int pp) __attribute__((always_inline)) {
     const int msp = pp % 3;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int cidx = tid + 256 * x;
-      const int r = cidx >> 4, part = cidx & 15;
-      const int en = m_ent[msp][r];
-      if (en >= 0) {
-        const int tk = en >> 6, sl = en & 63, hh = (r & 15) % G;
-        uint16_t* dst = p.dsbuf +
-            ((((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + sl) * G + hh) * 128 + part * 8;
-        st16(dst, ld16(dsT + r * DSP + part * 16));
-      }
-    }
-    if (tid < 2 * TPT) {
-      const int tt = tid / TPT, r0 = tt * 16 + (tid - tt * TPT) * G;
-      const int en = m_ent[msp][r0];
-      if (en >= 0) {
-        float tot = 0.f;
+    // thread: 16-byte part `part` of rows r0 and r0 + 16 (same head)
+    const int r0 = tid >> 4, part = tid & 15, hh = r0 % G;
+    const int en0 = m_ent[msp][r0], en1 = m_ent[msp][r0 + 16];
+    const uint4 v0 = ld16(dsT + r0 * DSP + part * 16);
+    const uint4 v1 = ld16(dsT + (r0 + 16) * DSP + part * 16);
+    auto dst = [&](int en) {
+      return p.dsbuf +
+             ((((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)) * G +
+              hh) * 128 + part * 8;
+    };
+    if (en0 >= 0) st16(dst(en0), v0);
+    if (en1 >= 0) st16(dst(en1), v1);
+    // wave 1: d log g of one (token, slot) per lane, summed over the G heads
+    // and the 4 waves' key quarters in a fixed order
+    const int q = tid - 64;
+    if (q >= 0 && q < 2 * TPT) {
+      const int tt = q / TPT, rr = tt * 16 + (q - tt * TPT) * G;
+      const int en = m_ent[msp][rr];
+      float tot = 0.f;
+      if ((G & 3) == 0) {
+        for (int h = 0; h < G; h += 4) {
+          const float4 a0 = *reinterpret_cast<const float4*>(&dsum[0][rr + h]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&dsum[1][rr + h]);
+          const float4 a2 = *reinterpret_cast<const float4*>(&dsum[2][rr + h]);
+          const float4 a3 = *reinterpret_cast<const float4*>(&dsum[3][rr + h]);
+          tot += (a0.x + a1.x) + (a2.x + a3.x);
+          tot += (a0.y + a1.y) + (a2.y + a3.y);
+          tot += (a0.z + a1.z) + (a2.z + a3.z);
+          tot += (a0.w + a1.w) + (a2.w + a3.w);
+        }
+      } else {
         for (int h = 0; h < G; ++h)
-          tot += (dsum[0][r0 + h] + dsum[1][r0 + h]) + (dsum[2][r0 + h] + dsum[3][r0 + h]);
-        p.dlogg[((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)] = tot;
+          tot += (dsum[0][rr + h] + dsum[1][rr + h]) + (dsum[2][rr + h] + dsum[3][rr + h]);
       }
+      if (en >= 0)
+        p.dlogg[((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)] = tot;
     }
   };
 
@@ -376,16 +397,23 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     }
     float pv[2][4], ds[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      const int r = tt * 16 + g4 * 4;
+      const int4 tv = *reinterpret_cast<const int4*>(&m_t[ms][r]);
+      const float4 bv = *reinterpret_cast<const float4*>(&m_bias[ms][r]);
+      const float4 dl = *reinterpret_cast<const float4*>(&m_delta[ms][r]);
+      const int ta[4] = {tv.x, tv.y, tv.z, tv.w};
+      const float ba[4] = {bv.x, bv.y, bv.z, bv.w}, da[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = tt * 16 + g4 * 4 + i;
-        const int t = m_t[ms][r];
-        float pp = 0.f;
-        if (t >= 0 && key <= t) pp = fast_exp2(sacc[tt][i] * sl2 + m_lg2[ms][r] - m_lse2[ms][r]);
+        // masked entries (no query row, or a key past the token) are dropped
+        // by the select, whatever the exponent gives for them
+        const float e = fast_exp2(fmaf(sacc[tt][i], sl2, ba[i]));
+        const float pp = (ta[i] >= 0 && key <= ta[i]) ? e : 0.f;
         pv[tt][i] = pp;
-        ds[tt][i] = pp * (pacc[tt][i] - m_delta[ms][r]);
+        ds[tt][i] = pp * (pacc[tt][i] - da[i]);
       }
+    }
     // the previous pair's dS tile has been read (store_ds) by every thread
     __syncthreads();
     // dS as bf16 hi + lo into the tile.  Lane (l16, g4) holds rows 4 g4 + i
