@@ -165,14 +165,11 @@ template <int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   constexpr int NKS = D / 32, NDT = D / 16;
   constexpr int ROWB = D * 2;          // row-major tile row, 16-byte chunks swizzled
-  constexpr int TP = 36;               // transposed tile pitch (bf16): 32 rows + 4
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int UNITS = 16 * CH;       // (chunk, row pair) units per tile pair
   constexpr int UPT = (UNITS + 255) / 256;
   __shared__ __attribute__((aligned(16))) uint8_t Qs[2][32 * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t dOs[2][32 * ROWB];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[2][D * TP];
   // row metadata of three tile pairs in flight, read as 4-row vectors:
   // token (-1 = no row), log2-domain bias log g - lse, Delta, source row, entry
   __shared__ __attribute__((aligned(16))) int m_t[3][32];
@@ -288,18 +285,6 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         st16(&Qs[buf][off], rq[x][h]);
         st16(&dOs[buf][off], rd[x][h]);
       }
-      const uint32_t a0[4] = {rq[x][0].x, rq[x][0].y, rq[x][0].z, rq[x][0].w};
-      const uint32_t a1[4] = {rq[x][1].x, rq[x][1].y, rq[x][1].z, rq[x][1].w};
-      const uint32_t c0[4] = {rd[x][0].x, rd[x][0].y, rd[x][0].z, rd[x][0].w};
-      const uint32_t c1[4] = {rd[x][1].x, rd[x][1].y, rd[x][1].z, rd[x][1].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = ch * 8 + 2 * i;
-        *reinterpret_cast<uint32_t*>(&Qt[buf][d * TP + 2 * rp]) = (a0[i] & 0xffffu) | (a1[i] << 16);
-        *reinterpret_cast<uint32_t*>(&Qt[buf][(d + 1) * TP + 2 * rp]) = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&dOt[buf][d * TP + 2 * rp]) = (c0[i] & 0xffffu) | (c1[i] << 16);
-        *reinterpret_cast<uint32_t*>(&dOt[buf][(d + 1) * TP + 2 * rp]) = (c0[i] >> 16) | (c1[i] & 0xffff0000u);
-      }
     }
   };
 
@@ -325,6 +310,18 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   int qofs[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qofs[ks] = l16 * ROWB + (((ks * 4 + g4) ^ lds_swz<ROWB>(l16)) << 4);
+
+  // Q^T / dO^T operands of dK^T = Q^T dS, dV^T = dO^T P for d tile dt: lane
+  // (l16, g4) needs column 16 dt + l16 of rows 4 g4 + {0..3} and
+  // 16 + 4 g4 + {0..3} (the operand order of P and dS).  A transposing read
+  // (ds_read_b64_tr_b16) gives each lane of a 16-lane group one column of a
+  // 4-row x 16-column block when source lane s addresses row base + s / 4,
+  // columns 4 (s % 4) .. 4 (s % 4) + 3.  Rows 16 apart share their swizzle, so
+  // (2 dt + h) ^ swz = 2 (dt ^ (swz >> 1)) + (h ^ (swz & 1)).
+  const int trow = 4 * g4 + (l16 >> 2);
+  const int tswz = lds_swz<ROWB>(trow);
+  const int tbase = trow * ROWB + ((((l16 & 3) >> 1) ^ (tswz & 1)) << 4) + 8 * (l16 & 1);
+  const int tx = tswz >> 1;
 
   // position of this lane's key (16 wv + l16) in the stored operand order
   const int kpos = 32 * (wv >> 1) + 8 * (l16 >> 2) + 4 * (wv & 1) + (l16 & 3);
@@ -465,12 +462,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     // dV^T[d, key] += dO^T[d, rows] P[rows, key];  dK^T += Q^T dS
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t* dr = &dOt[buf][(dt * 16 + l16) * TP + g4 * 4];
-      const uint16_t* qr = &Qt[buf][(dt * 16 + l16) * TP + g4 * 4];
-      const uint2 dlo = *reinterpret_cast<const uint2*>(dr);
-      const uint2 dhi = *reinterpret_cast<const uint2*>(dr + 16);
-      const uint2 qlo = *reinterpret_cast<const uint2*>(qr);
-      const uint2 qhi = *reinterpret_cast<const uint2*>(qr + 16);
+      const int o = tbase + ((dt ^ tx) << 5);
+      const uint2 dlo = lds_read_tr16(&dOs[buf][o]);
+      const uint2 dhi = lds_read_tr16(&dOs[buf][o + 16 * ROWB]);
+      const uint2 qlo = lds_read_tr16(&Qs[buf][o]);
+      const uint2 qhi = lds_read_tr16(&Qs[buf][o + 16 * ROWB]);
       const uint4 dta = make_uint4(dlo.x, dlo.y, dhi.x, dhi.y);
       const uint4 qta = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
       dv[dt] = mfma16x16x32(dta, pb, dv[dt]);
