@@ -34,7 +34,9 @@ Readings where the pages are silent (each is listed in the design doc):
   near-tie = K-th/(K+1)-th gap < 1e-5 [R12]; attention scale 1/sqrt(D),
   causal inside the current block [R13]; slots ascending, current block last
   [R14]; budget = 64 (K + 1) [R15]; decode applies log g too (switchable)
-  [R16]; partial last block keyed by its last token's prefix key [R19].
+  [R16]; partial last block keyed by its last token's prefix key [R19];
+  in the router backward a channel's max / min passes its gradient to the
+  first row of the prefix that attains it [R21].
 
 Everything is float64 on numpy arrays.  Inputs are the bf16-rounded values
 the GPU path consumes (or any float arrays for self-checks).
@@ -439,6 +441,123 @@ def gate_logit_grad(dlogg, idx, probs) -> np.ndarray:
                 flat_ds[r, j] += flat_dl[r, s_i]
     ds -= probs * tot[..., None]
     return ds
+
+
+# --------------------------------------------------------------------------
+# Router backward: the gradient that reaches the selector through log g
+# (README intro (b): the gates give the LM loss a path to the selector; model
+# card "Checkpoint configuration" table for the router's layers).  Chain rule
+# through the gate logits, the gate RoPE, the Q/K RMSNorm, the projections and
+# the max + min + average pooling, with the selection held fixed.
+# --------------------------------------------------------------------------
+
+def _rms_norm_bwd(y: np.ndarray, w: np.ndarray, eps: float, dn: np.ndarray):
+    """n = y * r * w with r = (mean(y^2) + eps)^(-1/2) over the last axis [R5].
+
+    Returns (dy, per-element contribution to dw) for upstream gradient dn:
+    dn/dy_k = r u_k - r^3 y_k mean(u * y), u = dn * w;  dn/dw = dn * y * r.
+    """
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+    u = dn * w
+    dy = r * u - r ** 3 * y * np.mean(u * y, axis=-1, keepdims=True)
+    return dy, dn * y * r
+
+
+def _pool_with_args(k: np.ndarray):
+    """Causal prefix [max; min; mean] of every token's block [R3, R4], plus the
+    row that holds each channel's max and min (the first such row on ties)
+    and the number of pooled rows [R21].
+
+    k [B,T,Hkv,D] -> p [B,T,Hkv,3D], amax, amin [B,T,Hkv,D] (token ids), n [T].
+    """
+    B, T, Hkv, D = k.shape
+    p = np.empty((B, T, Hkv, 3 * D))
+    amax = np.empty((B, T, Hkv, D), dtype=np.int64)
+    amin = np.empty((B, T, Hkv, D), dtype=np.int64)
+    n = np.empty(T, dtype=np.int64)
+    for t in range(T):
+        c0 = (t // BLOCK) * BLOCK
+        R = k[:, c0:t + 1]                                   # [B, n, Hkv, D]
+        p[:, t] = np.concatenate([R.max(axis=1), R.min(axis=1), R.mean(axis=1)], axis=-1)
+        amax[:, t] = c0 + R.argmax(axis=1)                   # argmax: first maximum
+        amin[:, t] = c0 + R.argmin(axis=1)
+        n[t] = t + 1 - c0
+    return p, amax, amin, n
+
+
+def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float):
+    """Gradient of L = sum over (b, t, kappa, valid slot) of dlogg * log g with
+    the selection idx held fixed, with respect to the router's inputs and
+    weights [R1-R9, R18].
+
+    q [B,T,Hq,D], k [B,T,Hkv,D], wq [Hkv,G*D,dg], wk [Hkv,3D,dg], w_qn, w_kn
+    [dg]; idx, dlogg [B,T,Hkv,S].  Returns dq, dk (same shapes as q, k), dwq,
+    dwk, dw_qn, dw_kn, and the intermediate gradients dqg, dkg with respect
+    to the gate query and the per-token gate key [B,T,Hkv,dg], and ds
+    [B,T,Hkv,NB] with respect to the gate logits.
+    """
+    q, k, wq, wk = as64(q), as64(k), as64(wq), as64(wk)
+    w_qn, w_kn = as64(w_qn), as64(w_kn)
+    dlogg = np.where(np.asarray(idx) >= 0, as64(dlogg), 0.0)
+    idx = np.asarray(idx)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    dg = wq.shape[2]
+    NB = -(-T // BLOCK)
+    tok = np.arange(T)
+    cblk = tok // BLOCK
+    # forward values the chain rule needs
+    x = q.reshape(B, T, Hkv, G * D)
+    y = np.einsum("btkf,kfg->btkg", x, wq)
+    qn = rms_norm(y, w_qn, eps)
+    qg = rope(qn, tok[None, :, None], theta)
+    p, amax, amin, npool = _pool_with_args(k)
+    z = np.einsum("btkf,kfg->btkg", p, wk)
+    kn = rms_norm(z, w_kn, eps)
+    kg = rope(kn, (cblk * BLOCK)[None, :, None], theta)
+    kblk = kg[:, block_key_tokens(T)]                        # [B, NB, Hkv, dg]
+    # gate logits, probabilities, and ds (gradient w.r.t. s)
+    s = np.full((B, T, Hkv, NB), -np.inf)
+    for t in range(T):
+        c = cblk[t]
+        s[:, t, :, :c] = np.einsum("bkg,bjkg->bkj", qg[:, t], kblk[:, :c]) / math.sqrt(dg)
+        s[:, t, :, c] = np.einsum("bkg,bkg->bk", qg[:, t], kg[:, t]) / math.sqrt(dg)
+    m = s.max(axis=-1, keepdims=True)
+    probs = np.exp(s - m)
+    probs /= probs.sum(axis=-1, keepdims=True)
+    ds = gate_logit_grad(dlogg, idx, probs)
+    # s -> gate query and gate keys
+    dqg = np.zeros_like(qg)
+    dkg = np.zeros_like(kg)
+    for t in range(T):
+        c = cblk[t]
+        dqg[:, t] = (np.einsum("bkj,bjkg->bkg", ds[:, t, :, :c], kblk[:, :c])
+                     + ds[:, t, :, c, None] * kg[:, t]) / math.sqrt(dg)
+        kt = block_key_tokens(T)[:c]
+        dkg[:, kt] += np.einsum("bkj,bkg->bjkg", ds[:, t, :, :c], qg[:, t]) / math.sqrt(dg)
+        dkg[:, t] += ds[:, t, :, c, None] * qg[:, t] / math.sqrt(dg)
+    # RoPE is a rotation: its transpose rotates by the opposite angle
+    dqn = rope(dqg, -tok[None, :, None], theta)
+    dkn = rope(dkg, -(cblk * BLOCK)[None, :, None], theta)
+    dy, dwq_n = _rms_norm_bwd(y, w_qn, eps, dqn)
+    dz, dwk_n = _rms_norm_bwd(z, w_kn, eps, dkn)
+    dwq = np.einsum("btkf,btkg->kfg", x, dy)
+    dwk = np.einsum("btkf,btkg->kfg", p, dz)
+    dq = np.einsum("btkg,kfg->btkf", dy, wq).reshape(B, T, Hq, D)
+    dp = np.einsum("btkg,kfg->btkf", dz, wk)                 # [B,T,Hkv,3D]
+    # pooling: max / min pass the gradient to their row, mean to every row
+    dk = np.zeros_like(k)
+    bi = np.arange(B)[:, None, None]
+    ki = np.arange(Hkv)[None, :, None]
+    di = np.arange(D)[None, None, :]
+    for t in range(T):
+        c0 = cblk[t] * BLOCK
+        np.add.at(dk, (bi, amax[:, t], ki, di), dp[:, t, :, :D])
+        np.add.at(dk, (bi, amin[:, t], ki, di), dp[:, t, :, D:2 * D])
+        dk[:, c0:t + 1] += dp[:, t, None, :, 2 * D:] / npool[t]
+    return dict(dq=dq, dk=dk, dwq=dwq, dwk=dwk, dw_qn=dwq_n.sum(axis=(0, 1, 2)),
+                dw_kn=dwk_n.sum(axis=(0, 1, 2)), dqg=dqg, dkg=dkg, ds=ds)
 
 
 # --------------------------------------------------------------------------

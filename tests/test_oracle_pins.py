@@ -413,3 +413,83 @@ def test_decode_equals_prefill_last_row():
                 ref = sdpa64(q_dec[b, h][None, None, None], Kr[None, :, None], Vr[None, :, None],
                              scale=sc)[0, 0, 0]
                 np.testing.assert_allclose(d0["o"][b, h], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- router backward
+
+def _router_case(seed=11, T=200, Hq=4, Hkv=2, D=16, dg=8, K=1):
+    rng = np.random.default_rng(seed)
+    x = dict(q=rng.standard_normal((1, T, Hq, D)), k=rng.standard_normal((1, T, Hkv, D)),
+             wq=rng.standard_normal((Hkv, Hq // Hkv * D, dg)) / math.sqrt(Hq // Hkv * D),
+             wk=rng.standard_normal((Hkv, 3 * D, dg)) / math.sqrt(3 * D),
+             w_qn=1 + 0.2 * rng.standard_normal(dg), w_kn=1 + 0.2 * rng.standard_normal(dg))
+    return x, K
+
+
+def _frozen_logg_loss(x, K, idx, dlogg, theta=1e4, eps=1e-6):
+    """L = sum dlogg * log g on the fixed slots idx (selection checked unchanged)."""
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], K, theta, eps)
+    assert np.array_equal(r["idx"], idx), "selection moved under the perturbation"
+    s = np.take_along_axis(r["s"], np.maximum(idx, 0), axis=-1)
+    logg = s - r["lse"][..., None]
+    return float(np.where(idx >= 0, dlogg * logg, 0.0).sum())
+
+
+@pytest.mark.parametrize("name", ["q", "k", "wq", "wk", "w_qn", "w_kn"])
+def test_router_backward_finite_differences(name):
+    """Every router gradient vs central differences of L = sum dlogg * log g
+    with the selection frozen; dlogg is arbitrary here (its valid slots need
+    not sum to zero), so the full gate-logit gradient is exercised."""
+    x, K = _router_case()
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], K, 1e4, 1e-6)
+    rng = np.random.default_rng(12)
+    dlogg = rng.standard_normal(r["idx"].shape)
+    g = O.router_bwd(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], r["idx"], dlogg,
+                     1e4, 1e-6)
+    grad = {"q": g["dq"], "k": g["dk"], "wq": g["dwq"], "wk": g["dwk"], "w_qn": g["dw_qn"],
+            "w_kn": g["dw_kn"]}[name]
+    h = 1e-6
+    flat = x[name].reshape(-1)
+    picks = rng.choice(flat.size, size=min(10, flat.size), replace=False)
+    if name == "k":   # include rows that are a channel's max / min of their prefix
+        picks = np.concatenate([picks, [0, 5 * x["k"].shape[-1] + 3]])
+    for i in picks:
+        old = flat[i]
+        flat[i] = old + h
+        lp = _frozen_logg_loss(x, K, r["idx"], dlogg)
+        flat[i] = old - h
+        lm = _frozen_logg_loss(x, K, r["idx"], dlogg)
+        flat[i] = old
+        fd = (lp - lm) / (2 * h)
+        an = grad.reshape(-1)[i]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, i, fd, an)
+
+
+def test_router_backward_zero_sum_dlogg_reaches_selected_logits_only():
+    """With dlogg summing to zero over each row's valid slots (what the gated
+    attention produces), ds is dlogg on the selected blocks and zero elsewhere."""
+    x, K = _router_case(seed=13, T=260, K=2)
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], K, 1e4, 1e-6)
+    rng = np.random.default_rng(14)
+    d = np.where(r["idx"] >= 0, rng.standard_normal(r["idx"].shape), 0.0)
+    nvalid = (r["idx"] >= 0).sum(-1, keepdims=True)
+    d = np.where(r["idx"] >= 0, d - d.sum(-1, keepdims=True) / nvalid, 0.0)
+    g = O.router_bwd(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], r["idx"], d,
+                     1e4, 1e-6)
+    want = np.zeros_like(g["ds"])
+    for pos in np.ndindex(*r["idx"].shape[:-1]):
+        for s_i, j in enumerate(r["idx"][pos]):
+            if j >= 0:
+                want[pos + (j,)] = d[pos + (s_i,)]
+    np.testing.assert_allclose(g["ds"], want, atol=1e-13)
+
+
+def test_router_backward_pooling_ties_go_to_first_row():
+    """bf16 keys tie often; a channel's max / min gradient goes to the first row
+    of the prefix that attains it (reading), checked on a hand-made block."""
+    k = np.zeros((1, 3, 1, 2))
+    k[0, :, 0, 0] = [1.0, 1.0, 0.5]       # max tie at rows 0, 1; min row 2
+    k[0, :, 0, 1] = [0.0, -1.0, -1.0]     # max row 0; min tie at rows 1, 2
+    _, amax, amin, n = O._pool_with_args(k)
+    assert amax[0, 2, 0].tolist() == [0, 0] and amin[0, 2, 0].tolist() == [2, 1]
+    assert n.tolist() == [1, 2, 3]
