@@ -20,19 +20,19 @@ __all__ = [
     "Dims", "DecodeDims", "SasError", "load_library", "version", "workspace_size",
     "decode_workspace_size", "gate_score", "topk_blocks", "sparse_attn_fwd",
     "sparse_attn_bwd", "decode", "budget_to_topk", "EXPORTED_SYMBOLS", "set_timing_events",
-    "take_device_fault",
+    "take_device_fault", "gate_score_bwd",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsas.so")
 
 SAS_OK, SAS_ERR_INVALID, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
-OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD = range(4)
+OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD, OP_GATE_BWD = range(5)
 
 EXPORTED_SYMBOLS = (
     "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
     "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
-    "sas_decode", "sas_set_timing_events", "sas_take_device_fault",
+    "sas_decode", "sas_set_timing_events", "sas_take_device_fault", "sas_gate_score_bwd",
 )
 
 
@@ -78,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sas_decode_workspace_size.restype = S
     lib.sas_gate_score.argtypes = [ctypes.POINTER(Dims)] + [P] * 8 + [P, S, P]
     lib.sas_topk_blocks.argtypes = [ctypes.POINTER(Dims)] + [P] * 6 + [P, S, P]
+    lib.sas_gate_score_bwd.argtypes = [ctypes.POINTER(Dims)] + [P] * 16 + [P, S, P]
     lib.sas_sparse_attn_fwd.argtypes = [ctypes.POINTER(Dims)] + [P] * 5 + [F32] + [P] * 3 + [P, S, P]
     lib.sas_sparse_attn_bwd.argtypes = ([ctypes.POINTER(Dims)] + [P] * 9 + [F32] + [P] * 4
                                         + [P, S, P])
@@ -85,7 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                + [P, S, P])
     lib.sas_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     lib.sas_take_device_fault.argtypes = [ctypes.POINTER(ctypes.c_uint)]
-    for fn in ("sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd",
+    for fn in ("sas_gate_score", "sas_gate_score_bwd", "sas_topk_blocks", "sas_sparse_attn_fwd",
                "sas_sparse_attn_bwd", "sas_decode", "sas_set_timing_events",
                "sas_take_device_fault"):
         getattr(lib, fn).restype = I32
@@ -213,6 +214,42 @@ def gate_score(q, k, wq, wk, w_qn, w_kn, topk: int, theta: float = 1.0e6, eps: f
                               _ptr(w_kn), _ptr(q_gate), _ptr(k_gate), _ptr(ws),
                               ws.numel() if ws is not None else 0, _stream(dev)))
     return q_gate, k_gate
+
+
+def gate_score_bwd(q, k, wq, wk, w_qn, w_kn, q_gate, k_gate, idx, dlogg, theta: float = 1.0e6,
+                   eps: float = 1.0e-6, workspace=None):
+    """Router backward: returns dict of fp32 dq, dk, dwq, dwk, dw_qn, dw_kn from
+    dlogg (as the attention backward gives it) with the selection idx fixed."""
+    lib = load_library()
+    dev = _device_of(q)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dg = wq.shape[2]
+    G = Hq // Hkv
+    S = idx.shape[-1]
+    _req(q, "q", torch.bfloat16, (B, T, Hq, D), dev)
+    _req(k, "k", torch.bfloat16, (B, T, Hkv, D), dev)
+    _req(wq, "wq", torch.bfloat16, (Hkv, G * D, dg), dev)
+    _req(wk, "wk", torch.bfloat16, (Hkv, 3 * D, dg), dev)
+    _req(w_qn, "w_qn", torch.float32, (dg,), dev)
+    _req(w_kn, "w_kn", torch.float32, (dg,), dev)
+    _req(q_gate, "q_gate", torch.float32, (B, T, Hkv, dg), dev)
+    _req(k_gate, "k_gate", torch.float32, (B, T, Hkv, dg), dev)
+    _req(idx, "idx", torch.int32, (B, T, Hkv, S), dev)
+    _req(dlogg, "dlogg", torch.float32, (B, T, Hkv, S), dev)
+    d = make_dims(B, T, Hq, Hkv, D, dg, S - 1, theta, eps)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, Hq, D), **f32), dk=torch.empty((B, T, Hkv, D), **f32),
+               dwq=torch.empty((Hkv, G * D, dg), **f32), dwk=torch.empty((Hkv, 3 * D, dg), **f32),
+               dw_qn=torch.empty((dg,), **f32), dw_kn=torch.empty((dg,), **f32))
+    nws = workspace_size(OP_GATE_BWD, d)
+    ws = workspace if workspace is not None else _ws(nws, dev)
+    _check(lib.sas_gate_score_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk),
+                                  _ptr(w_qn), _ptr(w_kn), _ptr(q_gate), _ptr(k_gate), _ptr(idx),
+                                  _ptr(dlogg), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dwq"]),
+                                  _ptr(out["dwk"]), _ptr(out["dw_qn"]), _ptr(out["dw_kn"]),
+                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev)))
+    return out
 
 
 def topk_blocks(q_gate, k_gate, topk: int, Hq: int, D: int, want_probs: bool = False,

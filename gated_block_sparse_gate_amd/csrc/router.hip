@@ -292,6 +292,21 @@ hipError_t launch_router_t(const RouterParams& p, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_transpose_w(const uint16_t* in, uint16_t* out, int H, int F, int N,
+                              hipStream_t st) {
+  const long n = static_cast<long>(H) * F * N;
+  hipLaunchKernelGGL(transpose_w_kernel, dim3(static_cast<unsigned>(min(2048L, (n + 255) / 256))),
+                     dim3(256), 0, st, in, out, H, F, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2* tab, int T, int dg, double theta, hipStream_t st) {
+  const long nr = static_cast<long>(T) * (dg / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(min(4096L, (nr + 255) / 256))),
+                     dim3(256), 0, st, tab, T, dg, theta);
+  return hipGetLastError();
+}
+
 hipError_t launch_router(const RouterParams& p0, const uint16_t* wq, const uint16_t* wk,
                          uint16_t* wqT, uint16_t* wkT, float2* rope, double theta,
                          hipStream_t st) {

@@ -86,6 +86,40 @@ GateWs gate_ws(const sas_dims* d) {
   return w;
 }
 
+struct GateBwdWs {
+  size_t wqT, wkT, rope, dqg, dkg, dy, dz, dzs, pmm, cnt2d, rowptr, entries, wq_part, wk_part,
+      wn_part, total;
+  int nchunk, nq_part, nk_part;
+};
+GateBwdWs gate_bwd_ws(const sas_dims* d) {
+  const int G = d->Hq / d->Hkv;
+  const size_t NB = (d->T + 63) / 64;
+  const size_t S = d->topk + 1;
+  const size_t rows = static_cast<size_t>(d->B) * d->T;
+  const size_t rk = rows * d->Hkv;
+  GateBwdWs w;
+  w.nchunk = static_cast<int>((rows + sas::kGateBwdChunk - 1) / sas::kGateBwdChunk);
+  w.nq_part = static_cast<int>(d->Hkv * ((rows + 127) / 128));
+  w.nk_part = static_cast<int>(d->B * d->Hkv * NB);
+  w.wqT = 0;
+  w.wkT = align_up(w.wqT + sizeof(uint16_t) * d->Hkv * d->dg * G * d->D);
+  w.rope = align_up(w.wkT + sizeof(uint16_t) * d->Hkv * d->dg * 3 * d->D);
+  w.dqg = align_up(w.rope + sizeof(float2) * static_cast<size_t>(d->T) * (d->dg / 2));
+  w.dkg = align_up(w.dqg + sizeof(float) * rk * d->dg);
+  w.dy = align_up(w.dkg + sizeof(float) * rk * d->dg);
+  w.dz = align_up(w.dy + sizeof(float) * rk * d->dg);
+  w.dzs = align_up(w.dz + sizeof(float) * rk * d->dg);
+  w.pmm = align_up(w.dzs + sizeof(float) * rk * d->dg);
+  w.cnt2d = align_up(w.pmm + sizeof(uint16_t) * rk * 2 * d->D);
+  w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
+  w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
+  w.wq_part = align_up(w.entries + sizeof(int32_t) * rk * S);
+  w.wk_part = align_up(w.wq_part + sizeof(float) * w.nchunk * d->Hkv * G * d->D * d->dg);
+  w.wn_part = align_up(w.wk_part + sizeof(float) * w.nchunk * d->Hkv * 3 * d->D * d->dg);
+  w.total = align_up(w.wn_part + sizeof(float) * (static_cast<size_t>(w.nq_part) + w.nk_part) * d->dg);
+  return w;
+}
+
 struct FwdWs { size_t vt, amax, vscale, total; };
 FwdWs fwd_ws_layout(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
@@ -203,6 +237,7 @@ size_t sas_workspace_size(int op, const sas_dims* d) {
     case SAS_OP_TOPK: return 0;
     case SAS_OP_FWD: return fwd_ws(d);
     case SAS_OP_BWD: return bwd_ws(d).total;
+    case SAS_OP_GATE_BWD: return gate_bwd_ws(d).total;
     default: fail(SAS_ERR_INVALID, "unknown op %d", op); return static_cast<size_t>(-1);
   }
 }
@@ -280,6 +315,58 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
   g_err.clear();
   return hip_status(sas::launch_sparse_fwd(p, static_cast<hipStream_t>(stream)),
                     "sas_sparse_attn_fwd launch");
+}
+
+sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* wq, const uint16_t* wk, const float* w_qn,
+                              const float* w_kn, const float* q_gate, const float* k_gate,
+                              const int32_t* idx, const float* dlogg, float* dq, float* dk,
+                              float* dwq, float* dwk, float* dw_qn, float* dw_kn, void* ws,
+                              size_t ws_bytes, void* stream) {
+  sas_status st = check_dims(d);
+  if (st) return st;
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(wq); REQ_PTR(wk); REQ_PTR(w_qn); REQ_PTR(w_kn);
+  REQ_PTR(q_gate); REQ_PTR(k_gate); REQ_PTR(idx); REQ_PTR(dlogg); REQ_PTR(dq); REQ_PTR(dk);
+  REQ_PTR(dwq); REQ_PTR(dwk); REQ_PTR(dw_qn); REQ_PTR(dw_kn);
+  const GateBwdWs w = gate_bwd_ws(d);
+  if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+  char* base = static_cast<char*>(ws);
+  const int G = d->Hq / d->Hkv;
+  sas::GateBwdParams p{};
+  p.q = q; p.k = k; p.w_qn = w_qn; p.w_kn = w_kn; p.q_gate = q_gate; p.k_gate = k_gate;
+  p.idx = idx; p.dlogg = dlogg;
+  p.dq = dq; p.dk = dk; p.dwq = dwq; p.dwk = dwk; p.dw_qn = dw_qn; p.dw_kn = dw_kn;
+  uint16_t* wqT = reinterpret_cast<uint16_t*>(base + w.wqT);
+  uint16_t* wkT = reinterpret_cast<uint16_t*>(base + w.wkT);
+  float2* rope = reinterpret_cast<float2*>(base + w.rope);
+  p.wqT = wqT; p.wkT = wkT; p.rope = rope;
+  p.dqg = reinterpret_cast<float*>(base + w.dqg);
+  p.dkg = reinterpret_cast<float*>(base + w.dkg);
+  p.dy = reinterpret_cast<float*>(base + w.dy);
+  p.dz = reinterpret_cast<float*>(base + w.dz);
+  p.dzs = reinterpret_cast<float*>(base + w.dzs);
+  p.pmm = reinterpret_cast<uint16_t*>(base + w.pmm);
+  p.cnt2d = reinterpret_cast<int32_t*>(base + w.cnt2d);
+  p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
+  p.entries = reinterpret_cast<int32_t*>(base + w.entries);
+  p.wq_part = reinterpret_cast<float*>(base + w.wq_part);
+  p.wk_part = reinterpret_cast<float*>(base + w.wk_part);
+  p.wn_part = reinterpret_cast<float*>(base + w.wn_part);
+  p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = G;
+  p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
+  p.nchunk = w.nchunk; p.nq_part = w.nq_part; p.nk_part = w.nk_part;
+  p.eps = d->norm_eps;
+  p.inv_sqrt_dg = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d->dg)));
+  g_err.clear();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = sas::launch_rope_table(rope, d->T, d->dg, d->rope_theta, hs);
+  if (e == hipSuccess) e = sas::launch_transpose_w(wq, wqT, d->Hkv, G * d->D, d->dg, hs);
+  if (e == hipSuccess) e = sas::launch_transpose_w(wk, wkT, d->Hkv, 3 * d->D, d->dg, hs);
+  if (e == hipSuccess)
+    e = sas::launch_selection_csr(idx, d->B, d->T, d->Hkv, d->topk + 1, p.cnt2d, p.rowptr,
+                                  p.entries, hs);
+  if (e == hipSuccess) e = sas::launch_gate_bwd(p, hs);
+  return hip_status(e, "sas_gate_score_bwd launch");
 }
 
 sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,

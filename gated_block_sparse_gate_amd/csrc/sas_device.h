@@ -85,6 +85,12 @@ __device__ __forceinline__ void st16(void* p, uint4 v) {
   *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
 }
 
+// 16x16x4 fp32 MFMA: lane l holds A[l%16][l/16] and B[l/16][l%16]; C column
+// l%16 holds rows 4*(l/16) .. +4.
+__device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs (v_dot2_f32_bf16:
 // exact bf16 products, fp32 accumulation).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

@@ -26,6 +26,45 @@ struct RouterParams {
   float eps;
 };
 
+// Router backward: gradients of the router from dL/d log g per selected slot.
+struct GateBwdParams {
+  const uint16_t* q;      // [B,T,Hq,D]
+  const uint16_t* k;      // [B,T,Hkv,D]
+  const uint16_t* wqT;    // [Hkv,dg,G*D]  (transposed copy in the workspace)
+  const uint16_t* wkT;    // [Hkv,dg,3*D]
+  const float* w_qn;      // [dg]
+  const float* w_kn;      // [dg]
+  const float2* rope;     // [T, dg/2] (cos, sin)
+  const float* q_gate;    // [B,T,Hkv,dg]
+  const float* k_gate;    // [B,T,Hkv,dg]
+  const int32_t* idx;     // [B,T,Hkv,S]
+  const float* dlogg;     // [B,T,Hkv,S]
+  float* dq;              // [B,T,Hq,D]    outputs
+  float* dk;              // [B,T,Hkv,D]
+  float* dwq;             // [Hkv,G*D,dg]
+  float* dwk;             // [Hkv,3*D,dg]
+  float* dw_qn;           // [dg]
+  float* dw_kn;           // [dg]
+  // workspace
+  float* dqg;             // [B,T,Hkv,dg] dL/d q_gate
+  float* dkg;             // [B,T,Hkv,dg] dL/d k_gate (per-token key)
+  float* dy;              // [B,T,Hkv,dg] dL/d (x . Wq) before the norm
+  float* dz;              // [B,T,Hkv,dg] dL/d (p . Wk) before the norm
+  float* dzs;             // [B,T,Hkv,dg] suffix sums of dz / n over each block
+  uint16_t* pmm;          // [B,T,Hkv,2D] prefix max | min pools (bf16 values)
+  int32_t* cnt2d;         // selection transpose, as in the attention backward
+  int32_t* rowptr;
+  int32_t* entries;
+  float* wq_part;         // [nchunk,Hkv,G*D,dg] per row-chunk partial sums
+  float* wk_part;         // [nchunk,Hkv,3*D,dg]
+  float* wn_part;         // [nq_part + nk_part, dg] per-workgroup norm-weight sums
+  int B, T, Hq, Hkv, D, dg, G, S, NB, nchunk, nq_part, nk_part;
+  float eps, inv_sqrt_dg;
+};
+
+// rows per chunk of the weight-gradient reductions over tokens
+constexpr int kGateBwdChunk = 1024;
+
 struct TopkParams {
   const float* q_gate;  // [B,T,Hkv,dg]
   const float* k_gate;  // [B,T,Hkv,dg]
@@ -135,6 +174,17 @@ hipError_t launch_router(const RouterParams& p, const uint16_t* wq, const uint16
                          uint16_t* wqT, uint16_t* wkT, float2* rope, double theta,
                          hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
+// out[h][n][f] = in[h][f][n] for bf16 weights
+hipError_t launch_transpose_w(const uint16_t* in, uint16_t* out, int H, int F, int N,
+                              hipStream_t st);
+// (cos, sin) table of the gate RoPE, [T, dg/2]
+hipError_t launch_rope_table(float2* tab, int T, int dg, double theta, hipStream_t st);
+hipError_t launch_gate_bwd(const GateBwdParams& p, hipStream_t st);
+// transpose of the selection: per (b, kappa, block j) the (token << 6 | slot)
+// entries that selected j (tokens ascending), as the attention backward uses
+hipError_t launch_selection_csr(const int32_t* idx, int B, int T, int Hkv, int S,
+                                int32_t* cnt2d, int32_t* rowptr, int32_t* entries,
+                                hipStream_t st);
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st);
 // OR the ring-wait fault flag of the forward kernels into *out and clear it
 hipError_t take_ring_fault_fwd(unsigned* out);

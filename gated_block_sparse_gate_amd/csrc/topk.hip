@@ -24,12 +24,6 @@ namespace {
 
 constexpr int kTokPerWG = 16;
 
-// 16x16x4 fp32 MFMA: lane l holds A[l%16][l/16] and B[l/16][l%16]; C column
-// l%16 holds rows 4*(l/16) .. +4.
-__device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 template <int DG>
 __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   constexpr int KCH = 64;            // block keys per chunk (16 per wave)

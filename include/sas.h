@@ -58,7 +58,8 @@ enum {
   SAS_OP_GATE_SCORE = 0,
   SAS_OP_TOPK = 1,
   SAS_OP_FWD = 2,
-  SAS_OP_BWD = 3
+  SAS_OP_BWD = 3,
+  SAS_OP_GATE_BWD = 4
 };
 
 /*
@@ -145,6 +146,40 @@ sas_status sas_gate_score(const sas_dims* d, const uint16_t* q, const uint16_t* 
                           const uint16_t* wq, const uint16_t* wk, const float* w_qn,
                           const float* w_kn, float* q_gate, float* k_gate, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * Router backward (GitHub README intro (b): the continuous gate on each
+ * selected block gives the LM loss a gradient path to the selector; model
+ * card "Checkpoint configuration": the router's layers).
+ *
+ * Gradients of the router, with the selection idx held fixed, from
+ * dlogg = dL/d log g per slot as sas_sparse_attn_bwd produces it.  log g =
+ * s - lse(s) over the row's candidate blocks, and the row's lse is one
+ * constant inside all of the row's attention logits, so that dlogg sums to
+ * zero over each row's valid slots; the gradient reaching the gate logits is
+ * then dlogg on the selected blocks and zero on the others, which is what
+ * this call uses (for a dlogg without that property the result is the
+ * gradient of sum dlogg * (s_selected - lse) without the lse term).
+ * Chain rule through s_j = q_gate . key_j / sqrt(dg), the gate RoPE (its
+ * transpose rotates back), RMSNorm, the projections and the pooling: a
+ * channel's max / min passes its gradient to the first row of the prefix
+ * that attains it, the mean to every row of the prefix.
+ *
+ *   q, k, wq, wk, w_qn, w_kn as for sas_gate_score;
+ *   q_gate, k_gate: that call's outputs for the same inputs;
+ *   idx, dlogg [B,T,Hkv,K+1] (slots outside [0, t/64] are ignored);
+ *   dq [B,T,Hq,D], dk [B,T,Hkv,D] fp32: the router's part of dL/dq, dL/dk
+ *   (add it to the attention's); dwq [Hkv,G*D,dg], dwk [Hkv,3*D,dg],
+ *   dw_qn, dw_kn [dg] fp32.  All outputs are fully overwritten.
+ *   ws: sas_workspace_size(SAS_OP_GATE_BWD, d) bytes.
+ *   Deterministic (bitwise repeatable); fp32 accumulation.
+ */
+sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* wq, const uint16_t* wk, const float* w_qn,
+                              const float* w_kn, const float* q_gate, const float* k_gate,
+                              const int32_t* idx, const float* dlogg, float* dq, float* dk,
+                              float* dwq, float* dwk, float* dw_qn, float* dw_kn, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * Candidate softmax and Top-K selection (abstract: normalised softmax gates

@@ -217,6 +217,32 @@ def test_sparse_attn_bwd(w, use_f32):
         assert torch.equal(a, b), "backward not bitwise repeatable"
 
 
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_gate_score_bwd(w):
+    """Router backward from the oracle's selection and its attention dlogg
+    (rows summing to zero), against the oracle's chain rule; every output is
+    an fp32 gradient held to the bf16-gradient bound.  Bitwise repeatable."""
+    P = prepared(w)
+    d = P["dev"]
+    x64 = P["x64"]
+    idx, _ = _oracle_sel(P)
+    dl = torch.tensor(np.where(P["r"]["idx"] >= 0, P["g"]["dlogg"], 0.0), dtype=torch.float32)
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    out = sas.gate_score_bwd(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], qg, kg, idx,
+                             dl.cuda(), w.theta, w.eps)
+    torch.cuda.synchronize()
+    ref = O.router_bwd(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"],
+                       P["r"]["idx"], O.as64(dl), w.theta, w.eps)
+    for name in ("dq", "dk", "dwq", "dwk", "dw_qn", "dw_kn"):
+        assert_close(name, out[name], ref[name])
+    out2 = sas.gate_score_bwd(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], qg, kg, idx,
+                              dl.cuda(), w.theta, w.eps)
+    torch.cuda.synchronize()
+    for name in out:
+        assert torch.equal(out[name], out2[name]), (name, "router backward not repeatable")
+
+
 def test_outputs_stay_in_bounds():
     """NaN canaries after every output buffer stay untouched."""
     w = CASES[1]
