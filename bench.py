@@ -6,7 +6,9 @@ head dim 128, gate hidden 128, KV block 64, Top-31 + current block):
 gate router -> candidate softmax + Top-K -> sparse attention forward ->
 sparse attention backward (dQ, dK, dV, d log g).  The budgeted decode
 (64 sequences, Qwen3-8B shape, contexts U[8192, 65536], budget 2048) is
-timed in the same run and reported in the "decode" object.
+timed in the same run and reported in the "decode" object, and the router
+backward (gradients of the gate router from the step's d log g) in the
+"router_bwd" object; neither is part of the step time.
 
 value = effective fwd+bwd attention FLOPs / whole-step time, where the
 effective FLOPs count 4*D (forward) + 10*D (backward) per attended
@@ -30,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 (vector and MFMA)
 
 
 def attended_pairs(T: int, K: int, block: int = 64) -> int:
@@ -188,6 +191,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=600)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-router-bwd", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for traffic)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -369,6 +373,51 @@ def main():
         "kernels": kernels,
         "other_ms": {k: round(v, 4) for k, v in kern_ms.items() if k not in kflops},
     }
+
+    # ------------------------------------------------------------ router backward
+    # (reported beside the step, not inside it): gradients of the router from
+    # the step's dlogg with its selection fixed
+    if not args.no_router_bwd:
+        gws = torch.empty(sas.workspace_size(sas.OP_GATE_BWD, d), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            gout = sas.gate_score_bwd(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], qg,
+                                      kg, idx, dlogg, w.theta, w.eps, workspace=gws)
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nrb = 5
+        r0.record(stream)
+        for _ in range(nrb):
+            sas.gate_score_bwd(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], qg, kg, idx,
+                               dlogg, w.theta, w.eps, workspace=gws)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        rb_ms = r0.elapsed_time(r1) / nrb
+        G = Hq // Hkv
+        rows = B * T
+        # algorithmic bytes: q, k, q_gate, k_gate, idx, dlogg read once; dq, dk
+        # (fp32) written once; weights negligible
+        rb_bytes = (rows * Hq * D * 2 + rows * Hkv * D * 2 + 2 * rows * Hkv * dg * 4
+                    + 2 * rows * Hkv * S * 4 + rows * Hq * D * 4 + rows * Hkv * D * 4)
+        # contractions (2 flops per multiply-add): projections recomputed
+        # (x Wq, p Wk), dx = dy Wq^T, dp = dz Wk^T, dWq = x^T dy, dWk = p^T dz,
+        # and the gate-logit gradients onto q_gate / the keys (2 S dg per row)
+        rb_flops = 2.0 * rows * Hkv * dg * (3 * G * D + 3 * 3 * D + 2 * S)
+        t_hbm = rb_bytes / (PEAK_HBM_GBS * 1e9)
+        t_mfma = rb_flops / (PEAK_FP32_TFLOPS * 1e12)
+        out["router_bwd"] = {
+            "workload": w.name, "ms": round(rb_ms, 4),
+            "algorithmic_bytes": rb_bytes, "algorithmic_flops": rb_flops,
+            "GBps": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 1),
+            "tflops": round(rb_flops / (rb_ms * 1e-3) / 1e12, 2),
+            "roofline": ({"bound": "mfma", "achieved": round(rb_flops / (rb_ms * 1e-3) / 1e12, 2),
+                          "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(t_mfma / (rb_ms * 1e-3), 4), "traffic": None}
+                         if t_mfma >= t_hbm else
+                         {"bound": "hbm", "achieved": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(t_hbm / (rb_ms * 1e-3), 4), "traffic": None}),
+        }
+        del gws, gout
 
     # ------------------------------------------------------------ decode
     if not args.no_decode:

@@ -67,48 +67,86 @@ __global__ __launch_bounds__(256) void gbwd_rows_kernel(GateBwdParams p) {
 }
 
 // ---------------------------------------------------------------- 2. block keys
-// One wave per (b, kappa, block j): the rows that selected j as a historical
-// block add dlogg * q_gate to the key of j (token 64j+63).  Four running
-// sums over the entries in turn, added in a fixed order.
+// The key of historical block j (token 64j+63) receives dlogg * q_gate from
+// every row that selected it.  Workgroup = (tile of kKeyTile blocks j0..,
+// chunk of kGateBwdChunk tokens, b * Hkv + kappa); each wave takes every
+// fourth token of the chunk, finds the token's slots inside the tile with
+// one ballot and adds them into its own LDS rows; the 4 waves' rows are
+// summed in a fixed order and written per chunk, and a second kernel adds
+// the chunks in order.
+constexpr int kKeyTile = 32;
+
 template <int DG>
-__global__ __launch_bounds__(64) void gbwd_blockkey_kernel(GateBwdParams p) {
-  const int lane = threadIdx.x;
-  const int j = blockIdx.x % p.NB;
-  const int bk = blockIdx.x / p.NB;                 // b * Hkv + kappa
+__global__ __launch_bounds__(256) void gbwd_blockkey_kernel(GateBwdParams p) {
+  constexpr int DPL = (DG + 63) / 64;               // gate dims per lane
+  __shared__ float acc[4][kKeyTile][DG];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int j0 = blockIdx.x * kKeyTile, ch = blockIdx.y, bk = blockIdx.z;
   const int kv = bk % p.Hkv;
   const long b = bk / p.Hkv;
-  if (64L * j + 63 >= p.T) return;                  // never a historical block
-  const bool on = 2 * lane < DG;
-  const int dd = on ? 2 * lane : 0;
-  const int e0 = p.rowptr[static_cast<size_t>(bk) * (p.NB + 1) + j];
-  const int e1 = p.rowptr[static_cast<size_t>(bk) * (p.NB + 1) + j + 1];
-  const int32_t* ent = p.entries + static_cast<size_t>(bk) * p.T * p.S;
-  float2 a[4];
+  const int t0 = ch * kGateBwdChunk;
+  const int t1 = min(p.T, t0 + kGateBwdChunk);
+  if ((t1 - 1) / 64 <= j0) return;                  // no token here has a block >= j0 in its history
+  for (int u = tid; u < 4 * kKeyTile * DG; u += 256) (&acc[0][0][0])[u] = 0.f;
+  __syncthreads();
+  for (int t = t0 + wv; t < t1; t += 4) {
+    const int c = t / 64;
+    const long row = (b * p.T + t) * p.Hkv + kv;
+    int j = -1;
+    float dl = 0.f;
+    if (lane < p.S) {                               // slot `lane` of the row (S <= 64)
+      j = p.idx[row * p.S + lane];
+      dl = p.dlogg[row * p.S + lane];
+    }
+    uint64_t m = ballot64(j >= j0 && j < j0 + kKeyTile && j < c);
+    if (m == 0) continue;
+    float qv[DPL];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) a[u] = make_float2(0.f, 0.f);
-  for (int e = e0; e < e1; e += 4) {
+    for (int e = 0; e < DPL; ++e)
+      qv[e] = (lane + 64 * e < DG) ? p.q_gate[row * DG + lane + 64 * e] : 0.f;
+    while (m) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const int jj = __shfl(j, src, 64) - j0;
+      const float w = __shfl(dl, src, 64);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (e + u < e1) {
-        const int en = ent[e + u];
-        const int tk = en >> 6, s = en & 63;
-        if (tk / 64 != j) {                         // current-block rows: step 1
-          const long row = (b * p.T + tk) * p.Hkv + kv;
-          const float dl = p.dlogg[row * p.S + s];
-          const float2 qq = *reinterpret_cast<const float2*>(p.q_gate + row * DG + dd);
-          a[u].x = fmaf(dl, qq.x, a[u].x);
-          a[u].y = fmaf(dl, qq.y, a[u].y);
-        }
-      }
+      for (int e = 0; e < DPL; ++e)
+        if (lane + 64 * e < DG) acc[wv][jj][lane + 64 * e] = fmaf(w, qv[e], acc[wv][jj][lane + 64 * e]);
     }
   }
-  if (!on) return;
-  const float sx = (a[0].x + a[1].x) + (a[2].x + a[3].x);
-  const float sy = (a[0].y + a[1].y) + (a[2].y + a[3].y);
-  float* dst = p.dkg + ((b * p.T + 64L * j + 63) * p.Hkv + kv) * DG + dd;
-  const float2 cur = *reinterpret_cast<const float2*>(dst);
-  *reinterpret_cast<float2*>(dst) =
-      make_float2(cur.x + sx * p.inv_sqrt_dg, cur.y + sy * p.inv_sqrt_dg);
+  __syncthreads();
+  float* out = p.bk_part + ((static_cast<size_t>(bk) * gridDim.y + ch) * p.NB + j0) * DG;
+  const int nj = min(kKeyTile, p.NB - j0);
+  for (int u = tid; u < nj * DG; u += 256) {
+    const int jj = u / DG, dd = u - jj * DG;
+    out[u] = (acc[0][jj][dd] + acc[1][jj][dd]) + (acc[2][jj][dd] + acc[3][jj][dd]);
+  }
+}
+
+// dkg[64j+63] += (sum over the chunks holding rows after block j) / sqrt(dg)
+template <int DG>
+__global__ __launch_bounds__(256) void gbwd_blockkey_sum_kernel(GateBwdParams p, int nchunk) {
+  const long e = blockIdx.x * 256L + threadIdx.x;
+  const long tot = static_cast<long>(p.B) * p.Hkv * p.NB * DG;
+  if (e >= tot) return;
+  const int d = static_cast<int>(e % DG);
+  const long r = e / DG;
+  const int j = static_cast<int>(r % p.NB);
+  const int bk = static_cast<int>(r / p.NB);
+  if (64L * j + 63 >= p.T) return;
+  const int kv = bk % p.Hkv;
+  const long b = bk / p.Hkv;
+  // chunk c holds a row with block j in its history iff its last token's
+  // block is past j (the same test that lets the chunk's workgroup run)
+  const int first = static_cast<int>((64L * (j + 1)) / kGateBwdChunk);
+  float s = 0.f;
+  const float* src = p.bk_part + (static_cast<size_t>(bk) * nchunk * p.NB + j) * DG + d;
+  for (int c = first; c < nchunk; ++c) {
+    const int t1 = min(p.T, (c + 1) * kGateBwdChunk);
+    if ((t1 - 1) / 64 > j) s += src[static_cast<size_t>(c) * p.NB * DG];
+  }
+  float* dst = p.dkg + ((b * p.T + 64L * j + 63) * p.Hkv + kv) * DG + d;
+  *dst += s * p.inv_sqrt_dg;
 }
 
 // RMSNorm backward and inverse RoPE for 4 rows held in MFMA C layout:
@@ -558,9 +596,27 @@ __global__ void gbwd_reduce_kernel(const float* part, float* out, long stride, i
   for (long e = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x; e < count;
        e += static_cast<long>(gridDim.x) * blockDim.x) {
     float s = 0.f;
+#pragma unroll 8
     for (int c = 0; c < n; ++c) s += part[c * stride + e];
     out[e] = s;
   }
+}
+
+// out[col] = sum over the n rows of part[row * ncol + col]: one workgroup per
+// column, thread i adds rows i, i + 256, ..., then a fixed pairwise tree
+__global__ __launch_bounds__(256) void gbwd_colsum_kernel(const float* part, float* out, int n,
+                                                         int ncol) {
+  __shared__ float red[256];
+  const int col = blockIdx.x, tid = threadIdx.x;
+  float s = 0.f;
+  for (int r = tid; r < n; r += 256) s += part[static_cast<size_t>(r) * ncol + col];
+  red[tid] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) out[col] = red[0];
 }
 
 template <int D, int DG>
@@ -569,8 +625,13 @@ hipError_t launch_gate_bwd_t(const GateBwdParams& p, hipStream_t st) {
   const long nrk = nrows * p.Hkv;
   hipLaunchKernelGGL((gbwd_rows_kernel<DG>), dim3(static_cast<unsigned>((nrk + 3) / 4)), dim3(256),
                      0, st, p);
-  hipLaunchKernelGGL((gbwd_blockkey_kernel<DG>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
-                     dim3(64), 0, st, p);
+  const int ntc = (p.T + kGateBwdChunk - 1) / kGateBwdChunk;
+  hipLaunchKernelGGL((gbwd_blockkey_kernel<DG>), dim3((p.NB + kKeyTile - 1) / kKeyTile, ntc,
+                                                      p.B * p.Hkv),
+                     dim3(256), 0, st, p);
+  const long nbk = static_cast<long>(p.B) * p.Hkv * p.NB * DG;
+  hipLaunchKernelGGL((gbwd_blockkey_sum_kernel<DG>), dim3(static_cast<unsigned>((nbk + 255) / 256)),
+                     dim3(256), 0, st, p, ntc);
   hipLaunchKernelGGL((gbwd_query_kernel<DG>), dim3(static_cast<unsigned>((nrows + 127) / 128), p.Hkv),
                      dim3(256), 0, st, p);
   hipLaunchKernelGGL((gbwd_key_kernel<D, DG>), dim3(p.NB, p.Hkv, p.B), dim3(256), 0, st, p);
@@ -595,11 +656,10 @@ hipError_t launch_gate_bwd_t(const GateBwdParams& p, hipStream_t st) {
                      dim3(256), 0, st, p.wq_part, p.dwq, nwq, p.nchunk, nwq);
   hipLaunchKernelGGL(gbwd_reduce_kernel, dim3(static_cast<unsigned>(min(2048L, (nwk + 255) / 256))),
                      dim3(256), 0, st, p.wk_part, p.dwk, nwk, p.nchunk, nwk);
-  hipLaunchKernelGGL(gbwd_reduce_kernel, dim3(1), dim3(256), 0, st, p.wn_part, p.dw_qn,
-                     static_cast<long>(DG), p.nq_part, static_cast<long>(DG));
-  hipLaunchKernelGGL(gbwd_reduce_kernel, dim3(1), dim3(256), 0, st,
-                     p.wn_part + static_cast<size_t>(p.nq_part) * DG, p.dw_kn, static_cast<long>(DG),
-                     p.nk_part, static_cast<long>(DG));
+  hipLaunchKernelGGL(gbwd_colsum_kernel, dim3(DG), dim3(256), 0, st, p.wn_part, p.dw_qn,
+                     p.nq_part, DG);
+  hipLaunchKernelGGL(gbwd_colsum_kernel, dim3(DG), dim3(256), 0, st,
+                     p.wn_part + static_cast<size_t>(p.nq_part) * DG, p.dw_kn, p.nk_part, DG);
   return hipGetLastError();
 }
 

@@ -88,7 +88,7 @@ GateWs gate_ws(const sas_dims* d) {
 
 struct GateBwdWs {
   size_t wqT, wkT, rope, dqg, dkg, dy, dz, dzs, pmm, cnt2d, rowptr, entries, wq_part, wk_part,
-      wn_part, total;
+      wn_part, bk_part, total;
   int nchunk, nq_part, nk_part;
 };
 GateBwdWs gate_bwd_ws(const sas_dims* d) {
@@ -116,7 +116,9 @@ GateBwdWs gate_bwd_ws(const sas_dims* d) {
   w.wq_part = align_up(w.entries + sizeof(int32_t) * rk * S);
   w.wk_part = align_up(w.wq_part + sizeof(float) * w.nchunk * d->Hkv * G * d->D * d->dg);
   w.wn_part = align_up(w.wk_part + sizeof(float) * w.nchunk * d->Hkv * 3 * d->D * d->dg);
-  w.total = align_up(w.wn_part + sizeof(float) * (static_cast<size_t>(w.nq_part) + w.nk_part) * d->dg);
+  w.bk_part = align_up(w.wn_part + sizeof(float) * (static_cast<size_t>(w.nq_part) + w.nk_part) * d->dg);
+  const size_t ntc = (d->T + sas::kGateBwdChunk - 1) / sas::kGateBwdChunk;
+  w.total = align_up(w.bk_part + sizeof(float) * d->B * d->Hkv * ntc * NB * d->dg);
   return w;
 }
 
@@ -352,6 +354,7 @@ sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16
   p.wq_part = reinterpret_cast<float*>(base + w.wq_part);
   p.wk_part = reinterpret_cast<float*>(base + w.wk_part);
   p.wn_part = reinterpret_cast<float*>(base + w.wn_part);
+  p.bk_part = reinterpret_cast<float*>(base + w.bk_part);
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = G;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
   p.nchunk = w.nchunk; p.nq_part = w.nq_part; p.nk_part = w.nk_part;

@@ -58,6 +58,7 @@ struct GateBwdParams {
   float* wq_part;         // [nchunk,Hkv,G*D,dg] per row-chunk partial sums
   float* wk_part;         // [nchunk,Hkv,3*D,dg]
   float* wn_part;         // [nq_part + nk_part, dg] per-workgroup norm-weight sums
+  float* bk_part;         // [B*Hkv, ceil(T / chunk), NB, dg] block-key gradient per token chunk
   int B, T, Hq, Hkv, D, dg, G, S, NB, nchunk, nq_part, nk_part;
   float eps, inv_sqrt_dg;
 };

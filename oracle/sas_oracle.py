@@ -430,15 +430,13 @@ def gate_logit_grad(dlogg, idx, probs) -> np.ndarray:
     dlogg = as64(dlogg)
     idx = np.asarray(idx)
     probs = as64(probs)
-    ds = np.zeros_like(probs)
-    tot = np.where(idx >= 0, dlogg, 0.0).sum(axis=-1)
-    flat_ds = ds.reshape(-1, ds.shape[-1])
-    flat_idx = idx.reshape(-1, idx.shape[-1])
-    flat_dl = dlogg.reshape(-1, dlogg.shape[-1])
-    for r in range(flat_ds.shape[0]):
-        for s_i, j in enumerate(flat_idx[r]):
-            if j >= 0:
-                flat_ds[r, j] += flat_dl[r, s_i]
+    valid = idx >= 0
+    dl = np.where(valid, dlogg, 0.0)
+    tot = dl.sum(axis=-1)
+    ds = np.zeros(probs.shape)
+    lead = np.indices(idx.shape[:-1])                         # row coordinates
+    pos = tuple(np.broadcast_to(c[..., None], idx.shape) for c in lead)
+    np.add.at(ds, pos + (np.where(valid, idx, 0),), dl)      # pads add 0 at block 0
     ds -= probs * tot[..., None]
     return ds
 
@@ -469,93 +467,108 @@ def _pool_with_args(k: np.ndarray):
     and the number of pooled rows [R21].
 
     k [B,T,Hkv,D] -> p [B,T,Hkv,3D], amax, amin [B,T,Hkv,D] (token ids), n [T].
+    Walks the 64 positions of every block at once.
     """
-    B, T, Hkv, D = k.shape
-    p = np.empty((B, T, Hkv, 3 * D))
-    amax = np.empty((B, T, Hkv, D), dtype=np.int64)
-    amin = np.empty((B, T, Hkv, D), dtype=np.int64)
-    n = np.empty(T, dtype=np.int64)
-    for t in range(T):
-        c0 = (t // BLOCK) * BLOCK
-        R = k[:, c0:t + 1]                                   # [B, n, Hkv, D]
-        p[:, t] = np.concatenate([R.max(axis=1), R.min(axis=1), R.mean(axis=1)], axis=-1)
-        amax[:, t] = c0 + R.argmax(axis=1)                   # argmax: first maximum
-        amin[:, t] = c0 + R.argmin(axis=1)
-        n[t] = t + 1 - c0
-    return p, amax, amin, n
+    B, T, H, D = k.shape
+    NB = -(-T // BLOCK)
+    kp = np.zeros((B, NB * BLOCK, H, D))
+    kp[:, :T] = k
+    kb = kp.reshape(B, NB, BLOCK, H, D)
+    pool = np.empty((B, NB, BLOCK, H, 3 * D))
+    amax = np.empty((B, NB, BLOCK, H, D), dtype=np.int64)
+    amin = np.empty((B, NB, BLOCK, H, D), dtype=np.int64)
+    for r in range(BLOCK):
+        v = kb[:, :, r]
+        if r == 0:
+            mx, mn, sm = v.copy(), v.copy(), v.copy()
+            ax = np.zeros(v.shape, dtype=np.int64)
+            an = np.zeros(v.shape, dtype=np.int64)
+        else:
+            up, dn = v > mx, v < mn                           # strict: ties keep the first row
+            mx, ax = np.where(up, v, mx), np.where(up, r, ax)
+            mn, an = np.where(dn, v, mn), np.where(dn, r, an)
+            sm = sm + v
+        pool[:, :, r] = np.concatenate([mx, mn, sm / (r + 1)], axis=-1)
+        amax[:, :, r], amin[:, :, r] = ax, an
+    base = (np.arange(NB) * BLOCK)[None, :, None, None, None]
+    tok = np.arange(T)
+    n = tok - (tok // BLOCK) * BLOCK + 1
+    return (pool.reshape(B, NB * BLOCK, H, 3 * D)[:, :T],
+            (amax + base).reshape(B, NB * BLOCK, H, D)[:, :T],
+            (amin + base).reshape(B, NB * BLOCK, H, D)[:, :T], n)
 
 
-def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float):
+def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float, heads=None):
     """Gradient of L = sum over (b, t, kappa, valid slot) of dlogg * log g with
     the selection idx held fixed, with respect to the router's inputs and
-    weights [R1-R9, R18].
+    weights [R1-R9, R18, R21].
 
     q [B,T,Hq,D], k [B,T,Hkv,D], wq [Hkv,G*D,dg], wk [Hkv,3D,dg], w_qn, w_kn
-    [dg]; idx, dlogg [B,T,Hkv,S].  Returns dq, dk (same shapes as q, k), dwq,
-    dwk, dw_qn, dw_kn, and the intermediate gradients dqg, dkg with respect
-    to the gate query and the per-token gate key [B,T,Hkv,dg], and ds
-    [B,T,Hkv,NB] with respect to the gate logits.
+    [dg]; idx, dlogg [B,T,Hkv,S].  heads: the KV heads to take (default all);
+    the outputs then cover those heads only (dq: their query heads), and
+    dw_qn, dw_kn their share of the sums.  Returns dq, dk, dwq, dwk, dw_qn,
+    dw_kn, and the intermediate gradients dqg, dkg with respect to the gate
+    query and the per-token gate key [B,T,H,dg], and ds [B,T,H,NB] with
+    respect to the gate logits.
     """
     q, k, wq, wk = as64(q), as64(k), as64(wq), as64(wk)
     w_qn, w_kn = as64(w_qn), as64(w_kn)
-    dlogg = np.where(np.asarray(idx) >= 0, as64(dlogg), 0.0)
-    idx = np.asarray(idx)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
+    heads = np.arange(Hkv) if heads is None else np.asarray(heads)
+    H = len(heads)
+    idx = np.asarray(idx)[:, :, heads]
+    dlogg = np.where(idx >= 0, as64(dlogg)[:, :, heads], 0.0)
+    wq, wk = wq[heads], wk[heads]
     dg = wq.shape[2]
     NB = -(-T // BLOCK)
     tok = np.arange(T)
     cblk = tok // BLOCK
+    kt = block_key_tokens(T)
+    sq = math.sqrt(dg)
     # forward values the chain rule needs
-    x = q.reshape(B, T, Hkv, G * D)
+    x = q.reshape(B, T, Hkv, G * D)[:, :, heads]
     y = np.einsum("btkf,kfg->btkg", x, wq)
-    qn = rms_norm(y, w_qn, eps)
-    qg = rope(qn, tok[None, :, None], theta)
-    p, amax, amin, npool = _pool_with_args(k)
+    qg = rope(rms_norm(y, w_qn, eps), tok[None, :, None], theta)
+    p, amax, amin, npool = _pool_with_args(k[:, :, heads])
     z = np.einsum("btkf,kfg->btkg", p, wk)
-    kn = rms_norm(z, w_kn, eps)
-    kg = rope(kn, (cblk * BLOCK)[None, :, None], theta)
-    kblk = kg[:, block_key_tokens(T)]                        # [B, NB, Hkv, dg]
-    # gate logits, probabilities, and ds (gradient w.r.t. s)
-    s = np.full((B, T, Hkv, NB), -np.inf)
-    for t in range(T):
-        c = cblk[t]
-        s[:, t, :, :c] = np.einsum("bkg,bjkg->bkj", qg[:, t], kblk[:, :c]) / math.sqrt(dg)
-        s[:, t, :, c] = np.einsum("bkg,bkg->bk", qg[:, t], kg[:, t]) / math.sqrt(dg)
-    m = s.max(axis=-1, keepdims=True)
-    probs = np.exp(s - m)
+    kg = rope(rms_norm(z, w_kn, eps), (cblk * BLOCK)[None, :, None], theta)
+    kblk = kg[:, kt]                                          # [B, NB, H, dg]
+    # gate logits over the candidates 0..c of every row, probabilities, ds
+    hist = (np.arange(NB)[None, :] < cblk[:, None])[None, :, None, :]   # [1, T, 1, NB]
+    ccol = np.broadcast_to(cblk[None, :, None, None], (B, T, H, 1))
+    s = np.where(hist, np.einsum("btkg,bjkg->btkj", qg, kblk) / sq, -np.inf)
+    np.put_along_axis(s, ccol, (np.einsum("btkg,btkg->btk", qg, kg) / sq)[..., None], axis=-1)
+    probs = np.exp(s - s.max(axis=-1, keepdims=True))
     probs /= probs.sum(axis=-1, keepdims=True)
     ds = gate_logit_grad(dlogg, idx, probs)
+    ds_hist = np.where(hist, ds, 0.0)
+    ds_cur = np.take_along_axis(ds, ccol, axis=-1)[..., 0]
     # s -> gate query and gate keys
-    dqg = np.zeros_like(qg)
-    dkg = np.zeros_like(kg)
-    for t in range(T):
-        c = cblk[t]
-        dqg[:, t] = (np.einsum("bkj,bjkg->bkg", ds[:, t, :, :c], kblk[:, :c])
-                     + ds[:, t, :, c, None] * kg[:, t]) / math.sqrt(dg)
-        kt = block_key_tokens(T)[:c]
-        dkg[:, kt] += np.einsum("bkj,bkg->bjkg", ds[:, t, :, :c], qg[:, t]) / math.sqrt(dg)
-        dkg[:, t] += ds[:, t, :, c, None] * qg[:, t] / math.sqrt(dg)
+    dqg = (np.einsum("btkj,bjkg->btkg", ds_hist, kblk) + ds_cur[..., None] * kg) / sq
+    dkg = ds_cur[..., None] * qg / sq
+    dkg[:, kt] += np.einsum("btkj,btkg->bjkg", ds_hist, qg) / sq
     # RoPE is a rotation: its transpose rotates by the opposite angle
-    dqn = rope(dqg, -tok[None, :, None], theta)
-    dkn = rope(dkg, -(cblk * BLOCK)[None, :, None], theta)
-    dy, dwq_n = _rms_norm_bwd(y, w_qn, eps, dqn)
-    dz, dwk_n = _rms_norm_bwd(z, w_kn, eps, dkn)
+    dy, dwq_n = _rms_norm_bwd(y, w_qn, eps, rope(dqg, -tok[None, :, None], theta))
+    dz, dwk_n = _rms_norm_bwd(z, w_kn, eps, rope(dkg, -(cblk * BLOCK)[None, :, None], theta))
     dwq = np.einsum("btkf,btkg->kfg", x, dy)
     dwk = np.einsum("btkf,btkg->kfg", p, dz)
-    dq = np.einsum("btkg,kfg->btkf", dy, wq).reshape(B, T, Hq, D)
-    dp = np.einsum("btkg,kfg->btkf", dz, wk)                 # [B,T,Hkv,3D]
-    # pooling: max / min pass the gradient to their row, mean to every row
-    dk = np.zeros_like(k)
-    bi = np.arange(B)[:, None, None]
-    ki = np.arange(Hkv)[None, :, None]
-    di = np.arange(D)[None, None, :]
-    for t in range(T):
-        c0 = cblk[t] * BLOCK
-        np.add.at(dk, (bi, amax[:, t], ki, di), dp[:, t, :, :D])
-        np.add.at(dk, (bi, amin[:, t], ki, di), dp[:, t, :, D:2 * D])
-        dk[:, c0:t + 1] += dp[:, t, None, :, 2 * D:] / npool[t]
+    dq = np.einsum("btkg,kfg->btkf", dy, wq).reshape(B, T, H * G, D)
+    dp = np.einsum("btkg,kfg->btkf", dz, wk)                 # [B,T,H,3D]
+    # pooling: max / min pass the gradient to their row, mean to every row of
+    # the prefix (a suffix sum over each block)
+    dk = np.zeros((B, T, H, D))
+    ib = np.broadcast_to(np.arange(B)[:, None, None, None], amax.shape)
+    ih = np.broadcast_to(np.arange(H)[None, None, :, None], amax.shape)
+    idd = np.broadcast_to(np.arange(D)[None, None, None, :], amax.shape)
+    np.add.at(dk, (ib, amax, ih, idd), dp[..., :D])
+    np.add.at(dk, (ib, amin, ih, idd), dp[..., D:2 * D])
+    mean_g = np.zeros((B, NB * BLOCK, H, D))
+    mean_g[:, :T] = dp[..., 2 * D:] / npool[None, :, None, None]
+    mb = mean_g.reshape(B, NB, BLOCK, H, D)
+    suffix = np.flip(np.cumsum(np.flip(mb, axis=2), axis=2), axis=2)
+    dk += suffix.reshape(B, NB * BLOCK, H, D)[:, :T]
     return dict(dq=dq, dk=dk, dwq=dwq, dwk=dwk, dw_qn=dwq_n.sum(axis=(0, 1, 2)),
                 dw_kn=dwk_n.sum(axis=(0, 1, 2)), dqg=dqg, dkg=dkg, ds=ds)
 

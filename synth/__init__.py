@@ -199,7 +199,21 @@ def decode_inputs(w: Workload, seed: int = 0, device="cpu", Lmax: int | None = N
     )
 
 
-TID_SEL, TID_SELLOGG = 12, 13
+TID_SEL, TID_SELLOGG, TID_DLOGG = 12, 13, 14
+
+
+def random_dlogg(w: Workload, idx: torch.Tensor, seed: int = 0, device="cpu"):
+    """An upstream gradient dL/d log g with the structure the gated attention
+    gives it: N(0, 1) on the valid slots of each row, less the row's mean over
+    them (so each row sums to zero), 0 on pads.  fp32 [B,T,Hkv,S]."""
+    idx = idx.to("cpu")
+    g = generator("cpu", seed, w.cfg_id, TID_DLOGG)
+    v = torch.randn(tuple(idx.shape), generator=g, dtype=torch.float64)
+    valid = idx >= 0
+    v = torch.where(valid, v, torch.zeros_like(v))
+    n = valid.sum(-1, keepdim=True).clamp(min=1)
+    v = torch.where(valid, v - v.sum(-1, keepdim=True) / n, torch.zeros_like(v))
+    return v.to(torch.float32).to(device)
 
 
 def random_selection(w: Workload, seed: int = 0, device="cpu", K: int | None = None):

@@ -12,7 +12,9 @@ it), on outputs the fp64 oracle computes one by one:
   that selected the block contributes); on every row, the log-gate gradient
   sums to zero over the selected slots;
 * batched decode at 64 sequences with contexts U[8192, 65536] and budget
-  2,048: indices of every (sequence, KV head) unit, outputs of sampled units.
+  2,048: indices of every (sequence, KV head) unit, outputs of sampled units;
+* router backward at the 32K training shape: every output, against the
+  oracle taken one KV head at a time.
 
 Tolerances are those of the small-shape parity tests: for bf16 outputs the
 max-abs bound applies to the error beyond half a bf16 ulp of the exact value,
@@ -176,6 +178,43 @@ def test_full_attention(w, K, bwd):
 
 
 # ------------------------------------------------------------------- decode
+
+# ------------------------------------------------------------ router backward
+
+def test_full_router_bwd():
+    """Router backward at the 32K training shape, every output in full: the
+    seeded random selection and a seeded upstream d log g whose rows sum to
+    zero (as the gated attention's do), against the oracle's chain rule taken
+    one KV head at a time.  Bitwise repeatable."""
+    w = synth.TRAIN_32K
+    x, x64, d = inputs(w)
+    idx, _ = synth.random_selection(w, seed=0)
+    dl = synth.random_dlogg(w, idx, seed=0)
+    print(f"[router bwd] {w.name}", flush=True)
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    out = sas.gate_score_bwd(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], qg, kg,
+                             idx.cuda(), dl.cuda(), w.theta, w.eps)
+    out2 = sas.gate_score_bwd(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], qg, kg,
+                              idx.cuda(), dl.cuda(), w.theta, w.eps)
+    torch.cuda.synchronize()
+    for name in out:
+        assert torch.equal(out[name], out2[name]), (name, "router backward not repeatable")
+    G = w.Hq // w.Hkv
+    dw_qn = np.zeros(w.dg)
+    dw_kn = np.zeros(w.dg)
+    for kv in range(w.Hkv):
+        r = O.router_bwd(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"],
+                         idx.numpy(), O.as64(dl), w.theta, w.eps, heads=[kv])
+        check(f"dq[kv={kv}]", out["dq"][:, :, kv * G:(kv + 1) * G], r["dq"])
+        check(f"dk[kv={kv}]", out["dk"][:, :, kv:kv + 1], r["dk"])
+        check(f"dwq[kv={kv}]", out["dwq"][kv:kv + 1], r["dwq"])
+        check(f"dwk[kv={kv}]", out["dwk"][kv:kv + 1], r["dwk"])
+        dw_qn += r["dw_qn"]
+        dw_kn += r["dw_kn"]
+    check("dw_qn", out["dw_qn"], dw_qn)
+    check("dw_kn", out["dw_kn"], dw_kn)
+
 
 def test_full_decode():
     w = synth.DECODE_B64
