@@ -46,17 +46,37 @@ __global__ __launch_bounds__(256) void gbwd_rows_kernel(GateBwdParams p) {
   const int dd = on ? 2 * lane : 0;
   float2 acc = make_float2(0.f, 0.f);
   float dcur = 0.f;
-  const int32_t* ir = p.idx + row * p.S;
-  const float* dr = p.dlogg + row * p.S;
-  for (int s = 0; s < p.S; ++s) {
-    const int j = ir[s];
-    if (j < 0 || j > c) continue;
-    const float dl = dr[s];
-    const long krow = (j == c) ? row : ((b * p.T + 64L * j + 63) * p.Hkv + kv);
-    if (j == c) dcur += dl;
-    const float2 kk = *reinterpret_cast<const float2*>(p.k_gate + krow * DG + dd);
-    acc.x = fmaf(dl, kk.x, acc.x);
-    acc.y = fmaf(dl, kk.y, acc.y);
+  // the row's slots on lanes 0..S-1 (S <= 64); valid slots in slot order,
+  // their keys gathered 8 at a time
+  int jl = -1;
+  float dll = 0.f;
+  if (lane < p.S) {
+    jl = p.idx[row * p.S + lane];
+    dll = p.dlogg[row * p.S + lane];
+  }
+  uint64_t m = ballot64(jl >= 0 && jl <= c);
+  while (m) {
+    float w[8];
+    float2 kk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      w[u] = 0.f;
+      kk[u] = make_float2(0.f, 0.f);
+      if (m) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1;
+        const int j = __shfl(jl, src, 64);
+        w[u] = __shfl(dll, src, 64);
+        if (j == c) dcur += w[u];
+        const long krow = (j == c) ? row : ((b * p.T + 64L * j + 63) * p.Hkv + kv);
+        kk[u] = *reinterpret_cast<const float2*>(p.k_gate + krow * DG + dd);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc.x = fmaf(w[u], kk[u].x, acc.x);
+      acc.y = fmaf(w[u], kk[u].y, acc.y);
+    }
   }
   if (!on) return;
   const float2 qq = *reinterpret_cast<const float2*>(p.q_gate + row * DG + dd);
@@ -89,29 +109,44 @@ __global__ __launch_bounds__(256) void gbwd_blockkey_kernel(GateBwdParams p) {
   if ((t1 - 1) / 64 <= j0) return;                  // no token here has a block >= j0 in its history
   for (int u = tid; u < 4 * kKeyTile * DG; u += 256) (&acc[0][0][0])[u] = 0.f;
   __syncthreads();
-  for (int t = t0 + wv; t < t1; t += 4) {
-    const int c = t / 64;
-    const long row = (b * p.T + t) * p.Hkv + kv;
-    int j = -1;
-    float dl = 0.f;
-    if (lane < p.S) {                               // slot `lane` of the row (S <= 64)
-      j = p.idx[row * p.S + lane];
-      dl = p.dlogg[row * p.S + lane];
-    }
-    uint64_t m = ballot64(j >= j0 && j < j0 + kKeyTile && j < c);
-    if (m == 0) continue;
-    float qv[DPL];
+  constexpr int UT = 4;                             // tokens per wave per pass
+  for (int tb = t0 + wv; tb < t1; tb += 4 * UT) {
+    int j[UT];
+    float dl[UT];
+    long row[UT];
+    uint64_t m[UT];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e)
-      qv[e] = (lane + 64 * e < DG) ? p.q_gate[row * DG + lane + 64 * e] : 0.f;
-    while (m) {
-      const int src = __builtin_ctzll(m);
-      m &= m - 1;
-      const int jj = __shfl(j, src, 64) - j0;
-      const float w = __shfl(dl, src, 64);
+    for (int u = 0; u < UT; ++u) {                  // slot `lane` of each row (S <= 64)
+      const int t = tb + 4 * u;
+      row[u] = (b * p.T + min(t, t1 - 1)) * p.Hkv + kv;
+      j[u] = -1;
+      dl[u] = 0.f;
+      if (t < t1 && lane < p.S) {
+        j[u] = p.idx[row[u] * p.S + lane];
+        dl[u] = p.dlogg[row[u] * p.S + lane];
+      }
+    }
+    float qv[UT][DPL];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const int c = (tb + 4 * u) / 64;
+      m[u] = ballot64(j[u] >= j0 && j[u] < j0 + kKeyTile && j[u] < c);
 #pragma unroll
       for (int e = 0; e < DPL; ++e)
-        if (lane + 64 * e < DG) acc[wv][jj][lane + 64 * e] = fmaf(w, qv[e], acc[wv][jj][lane + 64 * e]);
+        qv[u][e] = (m[u] && lane + 64 * e < DG) ? p.q_gate[row[u] * DG + lane + 64 * e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      while (m[u]) {
+        const int src = __builtin_ctzll(m[u]);
+        m[u] &= m[u] - 1;
+        const int jj = __shfl(j[u], src, 64) - j0;
+        const float w = __shfl(dl[u], src, 64);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+          if (lane + 64 * e < DG)
+            acc[wv][jj][lane + 64 * e] = fmaf(w, qv[u][e], acc[wv][jj][lane + 64 * e]);
+      }
     }
   }
   __syncthreads();
@@ -197,6 +232,17 @@ __device__ __forceinline__ void norm_rope_bwd(const floatx4 (&acc)[DG / 16],
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) g[nt][i] = rs * g[nt][i] - cf * acc[nt][i];
   }
+}
+
+// 8 consecutive fp32 values -> MFMA operand words of their bf16 hi and lo
+// parts (v = hi + lo to ~2^-16), in memory order
+__device__ __forceinline__ void split8(const float* src, uint4& hi, uint4& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 b = *reinterpret_cast<const float4*>(src + 4);
+  split_bf2(a.x, a.y, hi.x, lo.x);
+  split_bf2(a.z, a.w, hi.y, lo.y);
+  split_bf2(b.x, b.y, hi.z, lo.z);
+  split_bf2(b.z, b.w, hi.w, lo.w);
 }
 
 // Per-workgroup column sums of the norm-weight gradient: wsum of every lane
@@ -293,24 +339,33 @@ __global__ __launch_bounds__(256) void gbwd_query_kernel(GateBwdParams p) {
   store_wn_partial<DG>(wsum, red, p.wn_part + (static_cast<size_t>(kv) * gridDim.x + blockIdx.x) * DG,
                        wv, lane);
 
-  // dq[row, f] = sum_n dy[row, n] Wq[f, n]   (16x16x4 fp32 MFMA, 8 f tiles at a time)
-  const uint16_t* wtk = p.wqT + static_cast<size_t>(kv) * DG * F;
+  // dq[row, f] = sum_n dy[row, n] Wq[f, n]: bf16 MFMA with dy as hi + lo
+  // parts against the bf16 weights (8 f tiles at a time)
+  uint4 ah[2][DG / 32], al[2][DG / 32];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < DG / 32; ++ks)
+      split8(&dyl[wv][mt * 16 + l16][ks * 32 + g4 * 8], ah[mt][ks], al[mt][ks]);
+  const uint16_t* wqk = p.wq + static_cast<size_t>(kv) * F * DG;
   for (int f0 = 0; f0 < F; f0 += 128) {
     floatx4 o[2][8];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int ft = 0; ft < 8; ++ft) o[mt][ft] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int n0 = 0; n0 < DG; n0 += 4) {
-      const float a0 = dyl[wv][l16][n0 + g4];
-      const float a1 = dyl[wv][16 + l16][n0 + g4];
-      const uint16_t* wrow = wtk + static_cast<size_t>(n0 + g4) * F + f0 + l16;
 #pragma unroll
-      for (int ft = 0; ft < 8; ++ft) {
-        if (f0 + ft * 16 >= F) break;               // F = G * D is a multiple of 64
-        const float bw = bf2f(wrow[ft * 16]);
-        o[0][ft] = mfma16x16x4f32(a0, bw, o[0][ft]);
-        o[1][ft] = mfma16x16x4f32(a1, bw, o[1][ft]);
+    for (int ft = 0; ft < 8; ++ft) {
+      if (f0 + ft * 16 >= F) break;                 // F = G * D is a multiple of 64
+      const uint16_t* wrow = wqk + static_cast<size_t>(f0 + ft * 16 + l16) * DG + g4 * 8;
+#pragma unroll
+      for (int ks = 0; ks < DG / 32; ++ks) {
+        const uint4 bw = *reinterpret_cast<const uint4*>(wrow + ks * 32);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          o[mt][ft] = mfma16x16x32(ah[mt][ks], bw, o[mt][ft]);
+          o[mt][ft] = mfma16x16x32(al[mt][ks], bw, o[mt][ft]);
+        }
       }
     }
 #pragma unroll
@@ -495,23 +550,32 @@ __global__ __launch_bounds__(256) void gbwd_key_kernel(GateBwdParams p) {
   // dp = dz . Wk^T for the max part, then the min part: wave w rows 16w..
   // (16x16x4 fp32 MFMA), scattered per channel to the first row attaining it
   for (int u = tid; u < 64 * D; u += 256) dkb[(u / D) * DP + u % D] = 0.f;
+  // dz rows of the wave as bf16 hi + lo MFMA operands (against bf16 Wk)
+  constexpr int DT = D / 16;
+  const uint16_t* wkk = p.wk + static_cast<size_t>(kv) * (3 * D) * DG;
+  uint4 zh[DG / 32], zl[DG / 32];
+#pragma unroll
+  for (int ks = 0; ks < DG / 32; ++ks) split8(&zt[wv * 16 + l16][ks * 32 + g4 * 8], zh[ks], zl[ks]);
 #pragma unroll 1
   for (int part = 0; part < 2; ++part) {
-    for (int d0 = 0; d0 < D; d0 += 128) {
-      constexpr int DT = D < 128 ? D / 16 : 8;
+    {
       floatx4 o[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      for (int n0 = 0; n0 < DG; n0 += 4) {
-        const float a = zt[wv * 16 + l16][n0 + g4];
-        const uint16_t* wrow = wt + static_cast<size_t>(n0 + g4) * (3 * D) + part * D + d0 + l16;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16x16x4f32(a, bf2f(wrow[dt * 16]), o[dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* wrow = wkk + static_cast<size_t>(part * D + dt * 16 + l16) * DG + g4 * 8;
+#pragma unroll
+        for (int ks = 0; ks < DG / 32; ++ks) {
+          const uint4 bw = *reinterpret_cast<const uint4*>(wrow + ks * 32);
+          o[dt] = mfma16x16x32(zh[ks], bw, o[dt]);
+          o[dt] = mfma16x16x32(zl[ks], bw, o[dt]);
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dpb[(wv * 16 + g4 * 4 + i) * DP + d0 + dt * 16 + l16] = o[dt][i];
+        for (int i = 0; i < 4; ++i) dpb[(wv * 16 + g4 * 4 + i) * DP + dt * 16 + l16] = o[dt][i];
     }
     __syncthreads();
     if (tid < D) {
@@ -532,24 +596,30 @@ __global__ __launch_bounds__(256) void gbwd_key_kernel(GateBwdParams p) {
   }
   __syncthreads();
   // mean part: dk[r] += dzs[r] . Wk[2D:3D]^T; then store dk rows
-  for (int d0 = 0; d0 < D; d0 += 128) {
-    constexpr int DT = D < 128 ? D / 16 : 8;
+  {
+#pragma unroll
+    for (int ks = 0; ks < DG / 32; ++ks)
+      split8(&zt[wv * 16 + l16][ks * 32 + g4 * 8], zh[ks], zl[ks]);
     floatx4 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int n0 = 0; n0 < DG; n0 += 4) {
-      const float a = zt[wv * 16 + l16][n0 + g4];
-      const uint16_t* wrow = wt + static_cast<size_t>(n0 + g4) * (3 * D) + 2 * D + d0 + l16;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16x16x4f32(a, bf2f(wrow[dt * 16]), o[dt]);
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* wrow = wkk + static_cast<size_t>(2 * D + dt * 16 + l16) * DG + g4 * 8;
+#pragma unroll
+      for (int ks = 0; ks < DG / 32; ++ks) {
+        const uint4 bw = *reinterpret_cast<const uint4*>(wrow + ks * 32);
+        o[dt] = mfma16x16x32(zh[ks], bw, o[dt]);
+        o[dt] = mfma16x16x32(zl[ks], bw, o[dt]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tl = wv * 16 + g4 * 4 + i;
       if (tl >= ntok) continue;
-      float* dst = p.dk + (rowbase + static_cast<size_t>(tl) * p.Hkv) * D + d0 + l16;
+      float* dst = p.dk + (rowbase + static_cast<size_t>(tl) * p.Hkv) * D + l16;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dst[dt * 16] = dkb[tl * DP + d0 + dt * 16 + l16] + o[dt][i];
+      for (int dt = 0; dt < DT; ++dt) dst[dt * 16] = dkb[tl * DP + dt * 16 + l16] + o[dt][i];
     }
   }
 }
@@ -557,34 +627,64 @@ __global__ __launch_bounds__(256) void gbwd_key_kernel(GateBwdParams p) {
 // ---------------------------------------------------------------- 5. weights
 // part[chunk][kappa][f][n] = sum over the chunk's token rows of A[row][f] *
 // Bm[row][n]; A bf16 (row stride a_rs, kappa stride a_ks), Bm fp32 [rows,
-// Hkv, dg].  Workgroup: 64 f x dg; wave w: f tile w (16x16x4 fp32 MFMA).
+// Hkv, dg].  Workgroup: 64 f x dg, wave w: f tile w.  Per 32-row step the
+// workgroup stages A and Bm (as bf16 hi and lo parts) row-major in LDS and
+// the waves read both operands with transposing LDS reads, so that the rows
+// are the contraction index of a bf16 MFMA.
 template <int DG>
 __global__ __launch_bounds__(256) void gbwd_wsum_kernel(const uint16_t* A, long a_rs, long a_ks,
                                                         const float* Bm, float* part, int F,
                                                         int f_off, int Ftot, long nrows,
                                                         int Hkv) {
   constexpr int NT = DG / 16;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int AP = 64 + 8, BP = DG + 8;           // row pitches (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t As[32 * AP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bh[32 * BP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bl[32 * BP];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int f0 = blockIdx.x * 64 + wv * 16;
+  const int fw = blockIdx.x * 64;                   // F is a multiple of 64
   const int chunk = blockIdx.y, kv = blockIdx.z;
-  if (f0 >= F) return;
   const long r0 = static_cast<long>(chunk) * kGateBwdChunk;
   const long r1 = min(nrows, r0 + kGateBwdChunk);
   floatx4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* ab = A + kv * a_ks + f0 + l16;
-  const float* bb = Bm + static_cast<long>(kv) * DG + l16;
-  for (long r = r0; r < r1; r += 4) {
-    const long rr = r + g4;
-    const bool ok = rr < r1;
-    const float a = ok ? bf2f(ab[(ok ? rr : r0) * a_rs]) : 0.f;
-    const float* brow = bb + (ok ? rr : r0) * static_cast<long>(Hkv) * DG;
+  // operand k order (shared by both): rows 4 g4 + {0..3}, then 16 + 4 g4 + {0..3}
+  const int trow = 4 * g4 + (l16 >> 2);
+  const int tcol = 4 * (l16 & 3);
+  for (long r = r0; r < r1; r += 32) {
+    __syncthreads();                                // the previous step's reads are done
+    {
+      const int row = tid >> 3, ch = tid & 7;
+      const long rr = r + row;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rr < r1) v = ld16(A + kv * a_ks + rr * a_rs + fw + ch * 8);
+      st16(&As[row * AP + ch * 8], v);
+    }
+    for (int u = tid; u < 32 * (DG / 8); u += 256) {
+      const int row = u / (DG / 8), ch = u - row * (DG / 8);
+      const long rr = r + row;
+      uint4 hi = make_uint4(0, 0, 0, 0), lo = hi;
+      if (rr < r1) split8(Bm + (rr * Hkv + kv) * DG + ch * 8, hi, lo);
+      st16(&Bh[row * BP + ch * 8], hi);
+      st16(&Bl[row * BP + ch * 8], lo);
+    }
+    __syncthreads();
+    const uint2 a0 = lds_read_tr16(&As[trow * AP + wv * 16 + tcol]);
+    const uint2 a1 = lds_read_tr16(&As[(trow + 16) * AP + wv * 16 + tcol]);
+    const uint4 av = make_uint4(a0.x, a0.y, a1.x, a1.y);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16x16x4f32(a, ok ? brow[nt * 16] : 0.f, acc[nt]);
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint2 h0 = lds_read_tr16(&Bh[trow * BP + nt * 16 + tcol]);
+      const uint2 h1 = lds_read_tr16(&Bh[(trow + 16) * BP + nt * 16 + tcol]);
+      const uint2 q0 = lds_read_tr16(&Bl[trow * BP + nt * 16 + tcol]);
+      const uint2 q1 = lds_read_tr16(&Bl[(trow + 16) * BP + nt * 16 + tcol]);
+      acc[nt] = mfma16x16x32(av, make_uint4(h0.x, h0.y, h1.x, h1.y), acc[nt]);
+      acc[nt] = mfma16x16x32(av, make_uint4(q0.x, q0.y, q1.x, q1.y), acc[nt]);
+    }
   }
-  float* dst = part + ((static_cast<size_t>(chunk) * Hkv + kv) * Ftot + f_off + f0) * DG;
+  float* dst = part + ((static_cast<size_t>(chunk) * Hkv + kv) * Ftot + f_off + fw + wv * 16) * DG;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll

@@ -341,7 +341,7 @@ sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16
   uint16_t* wqT = reinterpret_cast<uint16_t*>(base + w.wqT);
   uint16_t* wkT = reinterpret_cast<uint16_t*>(base + w.wkT);
   float2* rope = reinterpret_cast<float2*>(base + w.rope);
-  p.wqT = wqT; p.wkT = wkT; p.rope = rope;
+  p.wq = wq; p.wk = wk; p.wqT = wqT; p.wkT = wkT; p.rope = rope;
   p.dqg = reinterpret_cast<float*>(base + w.dqg);
   p.dkg = reinterpret_cast<float*>(base + w.dkg);
   p.dy = reinterpret_cast<float*>(base + w.dy);

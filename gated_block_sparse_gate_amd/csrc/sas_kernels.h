@@ -30,6 +30,8 @@ struct RouterParams {
 struct GateBwdParams {
   const uint16_t* q;      // [B,T,Hq,D]
   const uint16_t* k;      // [B,T,Hkv,D]
+  const uint16_t* wq;     // [Hkv,G*D,dg]
+  const uint16_t* wk;     // [Hkv,3*D,dg]
   const uint16_t* wqT;    // [Hkv,dg,G*D]  (transposed copy in the workspace)
   const uint16_t* wkT;    // [Hkv,dg,3*D]
   const float* w_qn;      // [dg]
