@@ -869,21 +869,6 @@ hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_selection_csr(const int32_t* idx, int B, int T, int Hkv, int S,
-                                int32_t* cnt2d, int32_t* rowptr, int32_t* entries,
-                                hipStream_t st) {
-  BwdParams p{};
-  p.idx = idx;
-  p.B = B; p.T = T; p.Hkv = Hkv; p.S = S; p.NB = (T + 63) / 64;
-  p.cnt2d = cnt2d; p.rowptr = rowptr; p.entries = entries;
-  const unsigned nblk = static_cast<unsigned>(p.B) * p.Hkv * p.NB;
-  hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hkv), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hkv), dim3(1024), 0, st, p);
-  hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
-  return hipGetLastError();
-}
-
 hipError_t take_ring_fault_bwd(unsigned* out) {
   unsigned v = 0;
   hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_ring_fault), sizeof(v));

@@ -15,7 +15,7 @@
 // block, k_gate[t] for the current one):
 //   1. per row: dq_gate and the current-block part of dk_gate;
 //   2. per historical block: the block key's gradient, summed over the rows
-//      that selected it (selection transpose, rows in token order);
+//      that selected it (dense tiles of the selection on MFMA);
 //   3. query side: inverse RoPE, RMSNorm backward, dx = dy Wq^T;
 //   4. key side: inverse RoPE, RMSNorm backward, dp = dz Wk^T, and the
 //      pooling backward (max and min pass their gradient to the first row of
@@ -28,6 +28,17 @@
 namespace sas {
 
 namespace {
+
+// 8 consecutive fp32 values -> MFMA operand words of their bf16 hi and lo
+// parts (v = hi + lo to ~2^-16), in memory order
+__device__ __forceinline__ void split8(const float* src, uint4& hi, uint4& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 b = *reinterpret_cast<const float4*>(src + 4);
+  split_bf2(a.x, a.y, hi.x, lo.x);
+  split_bf2(a.z, a.w, hi.y, lo.y);
+  split_bf2(b.x, b.y, hi.z, lo.z);
+  split_bf2(b.z, b.w, hi.w, lo.w);
+}
 
 // ---------------------------------------------------------------- 1. rows
 // One wave per row (b, t, kappa); lane l owns gate dims 2l, 2l + 1.
@@ -88,77 +99,95 @@ __global__ __launch_bounds__(256) void gbwd_rows_kernel(GateBwdParams p) {
 
 // ---------------------------------------------------------------- 2. block keys
 // The key of historical block j (token 64j+63) receives dlogg * q_gate from
-// every row that selected it.  Workgroup = (tile of kKeyTile blocks j0..,
-// chunk of kGateBwdChunk tokens, b * Hkv + kappa); each wave takes every
-// fourth token of the chunk, finds the token's slots inside the tile with
-// one ballot and adds them into its own LDS rows; the 4 waves' rows are
-// summed in a fixed order and written per chunk, and a second kernel adds
-// the chunks in order.
-constexpr int kKeyTile = 32;
+// every row that selected it: per KV head, dK_blk [NB x dg] = DS^T Q_gate
+// with DS [T x NB] holding dlogg at the selected historical slots.  Dense
+// per tile: workgroup = (64-block tile j0.., chunk of query blocks,
+// b * Hkv + kappa); per query block c of the chunk it builds the DS^T tile
+// [64 j x 64 tokens] and the Q_gate tile [64 tokens x dg] in LDS as bf16 hi
+// and lo parts and adds their product (hi.hi + hi.lo + lo.hi) on MFMA; the
+// chunk partials are added in order by a second kernel.
+constexpr int kKeyTile = 64;
+constexpr int kKeyChunk = kGateBwdKeyChunk;         // query blocks per workgroup
 
 template <int DG>
 __global__ __launch_bounds__(256) void gbwd_blockkey_kernel(GateBwdParams p) {
-  constexpr int DPL = (DG + 63) / 64;               // gate dims per lane
-  __shared__ float acc[4][kKeyTile][DG];
+  constexpr int NT = DG / 16;
+  constexpr int SP = 64 + 8;                        // DS^T row pitch (bf16)
+  constexpr int QP = DG + 8;                        // Q tile row pitch (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t dsh[64 * SP], dsl[64 * SP];
+  __shared__ __attribute__((aligned(16))) uint16_t qh[64 * QP], ql[64 * QP];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int j0 = blockIdx.x * kKeyTile, ch = blockIdx.y, bk = blockIdx.z;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int j0 = blockIdx.x * kKeyTile, cc = blockIdx.y, bk = blockIdx.z;
   const int kv = bk % p.Hkv;
   const long b = bk / p.Hkv;
-  const int t0 = ch * kGateBwdChunk;
-  const int t1 = min(p.T, t0 + kGateBwdChunk);
-  if ((t1 - 1) / 64 <= j0) return;                  // no token here has a block >= j0 in its history
-  for (int u = tid; u < 4 * kKeyTile * DG; u += 256) (&acc[0][0][0])[u] = 0.f;
-  __syncthreads();
-  constexpr int UT = 4;                             // tokens per wave per pass
-  for (int tb = t0 + wv; tb < t1; tb += 4 * UT) {
-    int j[UT];
-    float dl[UT];
-    long row[UT];
-    uint64_t m[UT];
+  const int c0 = cc * kKeyChunk, c1 = min(p.NB, c0 + kKeyChunk);
+  if (c1 - 1 <= j0) return;                         // no block of the tile is history here
+  floatx4 acc[NT];
 #pragma unroll
-    for (int u = 0; u < UT; ++u) {                  // slot `lane` of each row (S <= 64)
-      const int t = tb + 4 * u;
-      row[u] = (b * p.T + min(t, t1 - 1)) * p.Hkv + kv;
-      j[u] = -1;
-      dl[u] = 0.f;
-      if (t < t1 && lane < p.S) {
-        j[u] = p.idx[row[u] * p.S + lane];
-        dl[u] = p.dlogg[row[u] * p.S + lane];
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // B operand (Q tile) k order: tokens 8 g4 + {0..3}, then 8 g4 + 4 + {0..3}
+  const int trow = 8 * g4 + (l16 >> 2);
+  const int tcol = 4 * (l16 & 3);
+  for (int c = max(c0, j0 + 1); c < c1; ++c) {
+    const int ntok = min(64, p.T - 64 * c);
+    __syncthreads();                                // previous block's reads are done
+    for (int u = tid; u < 64 * SP / 8; u += 256) {
+      st16(&dsh[u * 8], make_uint4(0, 0, 0, 0));
+      st16(&dsl[u * 8], make_uint4(0, 0, 0, 0));
+    }
+    for (int u = tid; u < 64 * (DG / 8); u += 256) {
+      const int tl = u / (DG / 8), ch = u - tl * (DG / 8);
+      uint4 hi = make_uint4(0, 0, 0, 0), lo = hi;
+      if (tl < ntok)
+        split8(p.q_gate + ((b * p.T + 64L * c + tl) * p.Hkv + kv) * DG + ch * 8, hi, lo);
+      st16(&qh[tl * QP + ch * 8], hi);
+      st16(&ql[tl * QP + ch * 8], lo);
+    }
+    __syncthreads();                                // zeroed DS^T before the scatter
+    for (int u = tid; u < ntok * p.S; u += 256) {
+      const int tl = u / p.S, s = u - tl * p.S;
+      const long row = (b * p.T + 64L * c + tl) * p.Hkv + kv;
+      const int j = p.idx[row * p.S + s];
+      if (j >= j0 && j < j0 + kKeyTile && j < c) {
+        const float dl = p.dlogg[row * p.S + s];
+        const uint32_t h = pack_bf2(dl, 0.f) & 0xffffu;
+        const float lo = dl - __uint_as_float(h << 16);
+        dsh[(j - j0) * SP + tl] = static_cast<uint16_t>(h);
+        dsl[(j - j0) * SP + tl] = static_cast<uint16_t>(pack_bf2(lo, 0.f) & 0xffffu);
       }
     }
-    float qv[UT][DPL];
+    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < UT; ++u) {
-      const int c = (tb + 4 * u) / 64;
-      m[u] = ballot64(j[u] >= j0 && j[u] < j0 + kKeyTile && j[u] < c);
+    for (int ks = 0; ks < 2; ++ks) {                // 64 tokens = 2 steps of 32
+      const uint4 ah = ld16(&dsh[(wv * 16 + l16) * SP + ks * 32 + g4 * 8]);
+      const uint4 al = ld16(&dsl[(wv * 16 + l16) * SP + ks * 32 + g4 * 8]);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e)
-        qv[u][e] = (m[u] && lane + 64 * e < DG) ? p.q_gate[row[u] * DG + lane + 64 * e] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < UT; ++u) {
-      while (m[u]) {
-        const int src = __builtin_ctzll(m[u]);
-        m[u] &= m[u] - 1;
-        const int jj = __shfl(j[u], src, 64) - j0;
-        const float w = __shfl(dl[u], src, 64);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e)
-          if (lane + 64 * e < DG)
-            acc[wv][jj][lane + 64 * e] = fmaf(w, qv[u][e], acc[wv][jj][lane + 64 * e]);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int o0 = (ks * 32 + trow) * QP + nt * 16 + tcol;
+        const uint2 h0 = lds_read_tr16(&qh[o0]), h1 = lds_read_tr16(&qh[o0 + 4 * QP]);
+        const uint2 q0 = lds_read_tr16(&ql[o0]), q1 = lds_read_tr16(&ql[o0 + 4 * QP]);
+        const uint4 bh = make_uint4(h0.x, h0.y, h1.x, h1.y);
+        const uint4 bl = make_uint4(q0.x, q0.y, q1.x, q1.y);
+        acc[nt] = mfma16x16x32(ah, bh, acc[nt]);
+        acc[nt] = mfma16x16x32(ah, bl, acc[nt]);
+        acc[nt] = mfma16x16x32(al, bh, acc[nt]);
       }
     }
   }
-  __syncthreads();
-  float* out = p.bk_part + ((static_cast<size_t>(bk) * gridDim.y + ch) * p.NB + j0) * DG;
   const int nj = min(kKeyTile, p.NB - j0);
-  for (int u = tid; u < nj * DG; u += 256) {
-    const int jj = u / DG, dd = u - jj * DG;
-    out[u] = (acc[0][jj][dd] + acc[1][jj][dd]) + (acc[2][jj][dd] + acc[3][jj][dd]);
-  }
+  float* out = p.bk_part + ((static_cast<size_t>(bk) * gridDim.y + cc) * p.NB + j0) * DG;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jj = wv * 16 + g4 * 4 + i;
+      if (jj < nj) out[jj * DG + nt * 16 + l16] = acc[nt][i];
+    }
 }
 
-// dkg[64j+63] += (sum over the chunks holding rows after block j) / sqrt(dg)
+// dkg[64j+63] += (sum of the chunk partials of j's tile) / sqrt(dg), over
+// the chunks whose workgroup ran, in order
 template <int DG>
 __global__ __launch_bounds__(256) void gbwd_blockkey_sum_kernel(GateBwdParams p, int nchunk) {
   const long e = blockIdx.x * 256L + threadIdx.x;
@@ -171,14 +200,12 @@ __global__ __launch_bounds__(256) void gbwd_blockkey_sum_kernel(GateBwdParams p,
   if (64L * j + 63 >= p.T) return;
   const int kv = bk % p.Hkv;
   const long b = bk / p.Hkv;
-  // chunk c holds a row with block j in its history iff its last token's
-  // block is past j (the same test that lets the chunk's workgroup run)
-  const int first = static_cast<int>((64L * (j + 1)) / kGateBwdChunk);
+  const int j0 = (j / kKeyTile) * kKeyTile;
   float s = 0.f;
   const float* src = p.bk_part + (static_cast<size_t>(bk) * nchunk * p.NB + j) * DG + d;
-  for (int c = first; c < nchunk; ++c) {
-    const int t1 = min(p.T, (c + 1) * kGateBwdChunk);
-    if ((t1 - 1) / 64 > j) s += src[static_cast<size_t>(c) * p.NB * DG];
+  for (int c = 0; c < nchunk; ++c) {
+    const int c1 = min(p.NB, (c + 1) * kKeyChunk);
+    if (c1 - 1 > j0) s += src[static_cast<size_t>(c) * p.NB * DG];
   }
   float* dst = p.dkg + ((b * p.T + 64L * j + 63) * p.Hkv + kv) * DG + d;
   *dst += s * p.inv_sqrt_dg;
@@ -232,17 +259,6 @@ __device__ __forceinline__ void norm_rope_bwd(const floatx4 (&acc)[DG / 16],
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) g[nt][i] = rs * g[nt][i] - cf * acc[nt][i];
   }
-}
-
-// 8 consecutive fp32 values -> MFMA operand words of their bf16 hi and lo
-// parts (v = hi + lo to ~2^-16), in memory order
-__device__ __forceinline__ void split8(const float* src, uint4& hi, uint4& lo) {
-  const float4 a = *reinterpret_cast<const float4*>(src);
-  const float4 b = *reinterpret_cast<const float4*>(src + 4);
-  split_bf2(a.x, a.y, hi.x, lo.x);
-  split_bf2(a.z, a.w, hi.y, lo.y);
-  split_bf2(b.x, b.y, hi.z, lo.z);
-  split_bf2(b.z, b.w, hi.w, lo.w);
 }
 
 // Per-workgroup column sums of the norm-weight gradient: wsum of every lane
@@ -725,7 +741,7 @@ hipError_t launch_gate_bwd_t(const GateBwdParams& p, hipStream_t st) {
   const long nrk = nrows * p.Hkv;
   hipLaunchKernelGGL((gbwd_rows_kernel<DG>), dim3(static_cast<unsigned>((nrk + 3) / 4)), dim3(256),
                      0, st, p);
-  const int ntc = (p.T + kGateBwdChunk - 1) / kGateBwdChunk;
+  const int ntc = (p.NB + kKeyChunk - 1) / kKeyChunk;
   hipLaunchKernelGGL((gbwd_blockkey_kernel<DG>), dim3((p.NB + kKeyTile - 1) / kKeyTile, ntc,
                                                       p.B * p.Hkv),
                      dim3(256), 0, st, p);

@@ -87,14 +87,12 @@ GateWs gate_ws(const sas_dims* d) {
 }
 
 struct GateBwdWs {
-  size_t wqT, wkT, rope, dqg, dkg, dy, dz, dzs, pmm, cnt2d, rowptr, entries, wq_part, wk_part,
-      wn_part, bk_part, total;
+  size_t wqT, wkT, rope, dqg, dkg, dy, dz, dzs, pmm, wq_part, wk_part, wn_part, bk_part, total;
   int nchunk, nq_part, nk_part;
 };
 GateBwdWs gate_bwd_ws(const sas_dims* d) {
   const int G = d->Hq / d->Hkv;
   const size_t NB = (d->T + 63) / 64;
-  const size_t S = d->topk + 1;
   const size_t rows = static_cast<size_t>(d->B) * d->T;
   const size_t rk = rows * d->Hkv;
   GateBwdWs w;
@@ -110,14 +108,11 @@ GateBwdWs gate_bwd_ws(const sas_dims* d) {
   w.dz = align_up(w.dy + sizeof(float) * rk * d->dg);
   w.dzs = align_up(w.dz + sizeof(float) * rk * d->dg);
   w.pmm = align_up(w.dzs + sizeof(float) * rk * d->dg);
-  w.cnt2d = align_up(w.pmm + sizeof(uint16_t) * rk * 2 * d->D);
-  w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
-  w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
-  w.wq_part = align_up(w.entries + sizeof(int32_t) * rk * S);
+  w.wq_part = align_up(w.pmm + sizeof(uint16_t) * rk * 2 * d->D);
   w.wk_part = align_up(w.wq_part + sizeof(float) * w.nchunk * d->Hkv * G * d->D * d->dg);
   w.wn_part = align_up(w.wk_part + sizeof(float) * w.nchunk * d->Hkv * 3 * d->D * d->dg);
   w.bk_part = align_up(w.wn_part + sizeof(float) * (static_cast<size_t>(w.nq_part) + w.nk_part) * d->dg);
-  const size_t ntc = (d->T + sas::kGateBwdChunk - 1) / sas::kGateBwdChunk;
+  const size_t ntc = (NB + sas::kGateBwdKeyChunk - 1) / sas::kGateBwdKeyChunk;
   w.total = align_up(w.bk_part + sizeof(float) * d->B * d->Hkv * ntc * NB * d->dg);
   return w;
 }
@@ -348,9 +343,6 @@ sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16
   p.dz = reinterpret_cast<float*>(base + w.dz);
   p.dzs = reinterpret_cast<float*>(base + w.dzs);
   p.pmm = reinterpret_cast<uint16_t*>(base + w.pmm);
-  p.cnt2d = reinterpret_cast<int32_t*>(base + w.cnt2d);
-  p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
-  p.entries = reinterpret_cast<int32_t*>(base + w.entries);
   p.wq_part = reinterpret_cast<float*>(base + w.wq_part);
   p.wk_part = reinterpret_cast<float*>(base + w.wk_part);
   p.wn_part = reinterpret_cast<float*>(base + w.wn_part);
@@ -365,9 +357,6 @@ sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16
   hipError_t e = sas::launch_rope_table(rope, d->T, d->dg, d->rope_theta, hs);
   if (e == hipSuccess) e = sas::launch_transpose_w(wq, wqT, d->Hkv, G * d->D, d->dg, hs);
   if (e == hipSuccess) e = sas::launch_transpose_w(wk, wkT, d->Hkv, 3 * d->D, d->dg, hs);
-  if (e == hipSuccess)
-    e = sas::launch_selection_csr(idx, d->B, d->T, d->Hkv, d->topk + 1, p.cnt2d, p.rowptr,
-                                  p.entries, hs);
   if (e == hipSuccess) e = sas::launch_gate_bwd(p, hs);
   return hip_status(e, "sas_gate_score_bwd launch");
 }

@@ -54,19 +54,18 @@ struct GateBwdParams {
   float* dz;              // [B,T,Hkv,dg] dL/d (p . Wk) before the norm
   float* dzs;             // [B,T,Hkv,dg] suffix sums of dz / n over each block
   uint16_t* pmm;          // [B,T,Hkv,2D] prefix max | min pools (bf16 values)
-  int32_t* cnt2d;         // selection transpose, as in the attention backward
-  int32_t* rowptr;
-  int32_t* entries;
   float* wq_part;         // [nchunk,Hkv,G*D,dg] per row-chunk partial sums
   float* wk_part;         // [nchunk,Hkv,3*D,dg]
   float* wn_part;         // [nq_part + nk_part, dg] per-workgroup norm-weight sums
-  float* bk_part;         // [B*Hkv, ceil(T / chunk), NB, dg] block-key gradient per token chunk
+  float* bk_part;         // [B*Hkv, ceil(NB / key chunk), NB, dg] block-key gradient per chunk
   int B, T, Hq, Hkv, D, dg, G, S, NB, nchunk, nq_part, nk_part;
   float eps, inv_sqrt_dg;
 };
 
-// rows per chunk of the weight-gradient reductions over tokens
+// rows per chunk of the weight-gradient reductions over tokens, and query
+// blocks per chunk of the block-key gradient
 constexpr int kGateBwdChunk = 1024;
+constexpr int kGateBwdKeyChunk = 32;
 
 struct TopkParams {
   const float* q_gate;  // [B,T,Hkv,dg]
@@ -183,11 +182,7 @@ hipError_t launch_transpose_w(const uint16_t* in, uint16_t* out, int H, int F, i
 // (cos, sin) table of the gate RoPE, [T, dg/2]
 hipError_t launch_rope_table(float2* tab, int T, int dg, double theta, hipStream_t st);
 hipError_t launch_gate_bwd(const GateBwdParams& p, hipStream_t st);
-// transpose of the selection: per (b, kappa, block j) the (token << 6 | slot)
-// entries that selected j (tokens ascending), as the attention backward uses
-hipError_t launch_selection_csr(const int32_t* idx, int B, int T, int Hkv, int S,
-                                int32_t* cnt2d, int32_t* rowptr, int32_t* entries,
-                                hipStream_t st);
+
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st);
 // OR the ring-wait fault flag of the forward kernels into *out and clear it
 hipError_t take_ring_fault_fwd(unsigned* out);
