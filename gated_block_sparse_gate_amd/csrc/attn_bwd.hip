@@ -737,22 +737,32 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hkv * S + sl) * G + hh) * 128
   const uint16_t* const dsq = a.dsbuf + rowbase * S * a.G * 128;
   const int HSG = a.Hkv * S;
-  uint4 hb[2], lb[2];
-  auto load_ds = [&](int j) __attribute__((always_inline)) {
-    const int jw = j >> 5;
-    const uint32_t jbit = 1u << (j & 31);
-    if (valid && (bits[tl_row * NBW + jw] & jbit)) {
-      const int rank = pcnt[tl_row * NBW + jw] + __popc(bits[tl_row * NBW + jw] & (jbit - 1u));
-      const int sl = slot_of[tl_row * S + rank];
-      const uint16_t* src = dsq + (((tl_row * HSG + sl) * G + hh) * 128 + 8 * g4);
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        hb[k2] = ld16(src + 32 * k2);
-        lb[k2] = ld16(src + 64 + 32 * k2);
+  // dS rows of the tile for union block v (two blocks in flight).  Every
+  // lane issues its loads, so the loads of one block never wait behind the
+  // other's; through a buffer over this group's dS rows, a lane whose row did
+  // not select the block (or that has no row) reads at an offset past the
+  // buffer, which returns zeros without a memory request.
+  // bytes from this group's first row to the end of its last token's rows of kappa
+  const unsigned dsbytes = static_cast<unsigned>(((ntok - 1) * HSG + S) * G) * 256u;
+  const auto dsr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dsq), 0,
+                                                     static_cast<int>(dsbytes), kBufferWord3);
+  struct DsRows { uint4 h[2], l[2]; };
+  auto load_ds = [&](int v, DsRows& r) __attribute__((always_inline)) {
+    unsigned off = dsbytes;
+    if (v < nU) {
+      const int j = ulist[v];
+      const int jw = j >> 5;
+      const uint32_t jbit = 1u << (j & 31);
+      if (valid && (bits[tl_row * NBW + jw] & jbit)) {
+        const int rank = pcnt[tl_row * NBW + jw] + __popc(bits[tl_row * NBW + jw] & (jbit - 1u));
+        const int sl = slot_of[tl_row * S + rank];
+        off = static_cast<unsigned>(((tl_row * HSG + sl) * G + hh) * 256 + 16 * g4);
       }
-    } else {
+    }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) hb[k2] = lb[k2] = make_uint4(0, 0, 0, 0);
+    for (int k2 = 0; k2 < 2; ++k2) {
+      r.h[k2] = buffer_ld16(dsr, off + 64 * k2);
+      r.l[k2] = buffer_ld16(dsr, off + 128 + 64 * k2);
     }
   };
 
@@ -769,22 +779,18 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   const int tbase0 = trow * KROWB + ((((l16 & 3) >> 1) ^ (tswz & 1)) << 4) + 8 * (l16 & 1);
   const int tx = tswz >> 1;
 
-  int v = next_active(0);
-  if (v < nU) load_ds(ulist[v]);
-  asm volatile("" ::: "memory");
-  prog[wv] = v;                 // done with every block before its first needed one
   bool failed = false;
-  while (v < nU) {
+  // block v from ring slot v % R with its dS rows r
+  auto process = [&](int v, const DsRows& r) __attribute__((always_inline)) {
     const int sl = v % R;
     const unsigned need = nstg * static_cast<unsigned>(v / R + 1);
     for (int it = 0; ring_count(&fill_cnt[sl]) < need; ++it) {
       if (it == kSpinLimit) {
         failed = true;
-        break;
+        return;
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (failed) break;
     const uint8_t* st = ring + sl * STAGE;
     int tbase = tbase0;
     asm volatile("" : "+v"(tbase));     // recomputed per block rather than kept live
@@ -796,16 +802,39 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
         const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
         const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
         const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        dqa[dt] = mfma16x16x32(kta, hb[k2], dqa[dt]);
-        dqa[dt] = mfma16x16x32(kta, lb[k2], dqa[dt]);
+        dqa[dt] = mfma16x16x32(kta, r.h[k2], dqa[dt]);
+        dqa[dt] = mfma16x16x32(kta, r.l[k2], dqa[dt]);
       }
     }
-    v = next_active(v + 1);
+  };
+  // two active blocks in flight: A holds v0's rows, B v1's
+  DsRows ra, rb;
+  int v0 = next_active(0);
+  load_ds(v0, ra);
+  int v1 = next_active(v0 + 1);
+  load_ds(v1, rb);
+  asm volatile("" ::: "memory");
+  prog[wv] = v0;                // done with every block before its first needed one
+  while (v0 < nU) {
+    process(v0, ra);
+    if (failed) break;
     asm volatile("" ::: "memory");
-    if (lane == 0) prog[wv] = v;      // after this wave's last read of the slot
+    if (lane == 0) prog[wv] = v1;     // after this wave's last read of v0's slot
     asm volatile("" ::: "memory");
-    if (v < nU) load_ds(ulist[v]);
+    const int v2 = next_active(v1 + 1);
+    load_ds(v2, ra);
+    if (v1 >= nU) break;
+    process(v1, rb);
+    if (failed) break;
+    asm volatile("" ::: "memory");
+    if (lane == 0) prog[wv] = v2;
+    asm volatile("" ::: "memory");
+    const int v3 = next_active(v2 + 1);
+    load_ds(v3, rb);
+    v0 = v2;
+    v1 = v3;
   }
+  wait_vmem_all();              // the last prefetches are unused
   if (failed) {
     ring_fault(lane);
 #pragma unroll

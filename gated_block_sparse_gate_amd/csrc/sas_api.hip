@@ -373,6 +373,8 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
   REQ_PTR(logg); REQ_PTR(dq); REQ_PTR(dk); REQ_PTR(dv); REQ_PTR(dlogg);
   if (o_f32 && !aligned16(o_f32)) return fail(SAS_ERR_INVALID, "pointer 'o_f32' is not 16-byte aligned");
   if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
+  if (64LL * d->Hq * (d->topk + 1) * 256 >= (1LL << 31))
+    return fail(SAS_ERR_UNSUPPORTED, "Hq * (topk + 1) too large (64 tokens' dS rows must fit 2 GiB)");
   const BwdWs w = bwd_ws(d);
   if ((st = check_ws(ws, ws_bytes, w.total))) return st;
   char* base = static_cast<char*>(ws);

@@ -85,6 +85,17 @@ __device__ __forceinline__ void st16(void* p, uint4 v) {
   *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
 }
 
+// Raw buffer resources (stride 0, no swizzle) with the fourth descriptor word
+// of the gfx9 family (32-bit data format).  A lane whose byte offset is at or
+// beyond the resource's size reads zeros and makes no memory request.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t rs, unsigned off) {
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = __builtin_bit_cast(
+      u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(off), 0, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 16x16x4 fp32 MFMA: lane l holds A[l%16][l/16] and B[l/16][l%16]; C column
 // l%16 holds rows 4*(l/16) .. +4.
 __device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
