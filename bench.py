@@ -451,11 +451,13 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         warm_us = e0.elapsed_time(e1) / args.decode_steps * 1e3
-        # cold: write 1 GiB between steps so no selected block or gate key is cached
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # cold: read 1 GiB between steps so no selected block or gate key is
+        # cached (a read leaves no dirty lines whose write-back would compete
+        # with the step, as a 1 GiB write would)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         cold = []
         for _ in range(args.decode_steps):
-            flush.fill_(1)
+            flush.sum()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
             dstep()
