@@ -9,8 +9,9 @@
 //           lower j) + block c (one wave per unit).
 //   attend: the G query heads attend to the selected blocks' keys tau < L
 //           with log g added (apply_gate = 1), split over NSPLIT workgroups
-//           of 2 slots whose K/V blocks (16 KiB each per tensor, contiguous
-//           in the head-major cache) are all loaded before any arithmetic.
+//           of 4 slots whose K/V blocks (16 KiB each per tensor, contiguous
+//           in the head-major cache) are all loaded before any arithmetic;
+//           scores and P V on MFMA.
 //   merge: one workgroup per unit merges the per-split (max, sum, o)
 //           partials.
 #include <type_traits>
@@ -21,7 +22,7 @@ namespace sas {
 
 namespace {
 
-constexpr int kSlotsPerSplit = 2;
+constexpr int kSlotsPerSplit = 4;
 
 // Score step: workgroup = (unit, chunk of 128 candidate blocks), 256
 // threads, 8 lanes per candidate; all of the chunk's gate-key loads are issued
@@ -218,192 +219,242 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit, in
                                              bool ok) {
   __shared__ float wsp[kMaxS][G];
   __shared__ float inv_l[G];
+  constexpr int RF = decode_part_floats(G, D);
   const int tid = threadIdx.x;
-  const float* base = p.ws_part + static_cast<size_t>(unit) * p.nsplit * G * (D + 2);
+  const float* base = p.ws_part + static_cast<size_t>(unit) * p.nsplit * RF;
   if (tid < G) {
     const int h = tid;
     float M = -INFINITY;
-    for (int sp = 0; sp < p.nsplit; ++sp) M = fmaxf(M, base[(sp * G + h) * (D + 2) + D]);
+    for (int sp = 0; sp < p.nsplit; ++sp) M = fmaxf(M, base[sp * RF + G * D + h]);
     float l = 0.f;
     for (int sp = 0; sp < p.nsplit; ++sp) {
-      const float m = base[(sp * G + h) * (D + 2) + D];
+      const float m = base[sp * RF + G * D + h];
       const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
       wsp[sp][h] = w;
-      l += base[(sp * G + h) * (D + 2) + D + 1] * w;
+      l += base[sp * RF + G * D + 16 + h] * w;
     }
     inv_l[h] = (ok && l > 0.f) ? 1.f / l : __builtin_nanf("");
   }
   __syncthreads();
   for (int e = tid; e < G * D; e += 256) {
-    const int h = e / D, d = e - h * D;
+    const int h = e / D;
     float o = 0.f;
-    for (int sp = 0; sp < p.nsplit; ++sp) o = fmaf(base[(sp * G + h) * (D + 2) + d], wsp[sp][h], o);
-    p.o[(static_cast<size_t>(b) * p.Hq + kv * G + h) * D + d] = f2bf(o * inv_l[h]);
+    for (int sp = 0; sp < p.nsplit; ++sp) o = fmaf(base[sp * RF + e], wsp[sp][h], o);
+    p.o[(static_cast<size_t>(b) * p.Hq + kv * G) * D + e] = f2bf(o * inv_l[h]);
   }
 }
 
-// Workgroup = (unit, split of kSlotsPerSplit selected blocks), 256 threads.
-// Thread t owns 16-byte chunk ch = t % (D/8) of rows rg + (256/(D/8)) x of
-// each block, so one block of K (and of V) is one coalesced 16 KiB read per
-// tensor; every K/V load of the split is issued before any arithmetic, which
-// keeps 64 KiB per workgroup in flight.  Scores: per-thread 8-element partial
-// dots, reduced over the row's lanes with DPP; softmax state and the output
-// partials are per wave (online over the split's blocks), merged across the
-// wave's row groups with lane permutes and across the 4 waves in LDS once.
+// Workgroup = (unit, split of four selected blocks), 256 threads, in two
+// passes of two blocks; in a pass, wave w takes keys 16w .. 16w + 15 of each
+// of the two blocks (32 keys), so the scores and P V of a wave are single
+// MFMA tiles with the G heads padded to 16 columns:
+//   S^T[key][h] = K Q^T      A = the wave's 16 keys of one block, loaded from
+//                            HBM straight into the operand layout (16 bytes
+//                            per lane, 64 contiguous bytes per key and load);
+//   O^T[d][h]  += V^T P^T    A = V^T from LDS with transposing reads, B = the
+//                            bf16 softmax weights as they sit in S's
+//                            accumulator lanes (k slot 8g + i <-> key 4g + i
+//                            of the pass's first block for i < 4, of its
+//                            second block for i >= 4, on both operands).
+// Every K and V load of the workgroup (128 KiB) is issued before any
+// arithmetic: the first pass's V rows go HBM -> LDS by DMA into a per-wave
+// region, the second pass's wait in registers and take their place once the
+// first pass has read them (no workgroup barrier).  The softmax state is
+// carried online across the passes.  Keys at or beyond the context length
+// read as zeros (K: buffer range) or as the last valid row (V, with weight
+// 0); a slot without a block reads no K and zeroes its V operand.  The
+// per-wave (max, sum, O) are merged across the 4 waves in LDS, each wave's in
+// place of its own V rows, into one partial per split, written in whole
+// 128-byte lines.
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
+  static_assert(kSlotsPerSplit == 4, "two passes of two 16-key tiles per wave");
+  static_assert(G >= 1 && G <= 16, "heads per KV head");
+  constexpr int NKS = D / 32;             // k steps of S
+  constexpr int NDT = D / 16;             // d tiles of O
+  constexpr int ROWB = 2 * D;             // bytes per key row
   constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;          // rows per pass of the workgroup
-  constexpr int RPT = 64 / RPP;           // rows per thread per block
-  constexpr int SPW = kSlotsPerSplit;
-  __shared__ float red_m[4][G], red_l[4][G];
-  __shared__ __attribute__((aligned(16))) float red_o[4][G][D];
+  constexpr int RPI = 64 / CPR;           // rows per 1 KiB wave load
+  constexpr int NVT = 16 / RPI;           // wave loads per 16-row tile
+  constexpr int G4 = (G + 3) / 4 * 4;     // keeps o 16-byte aligned
+  // a wave's (max, sum, O) replace its own V rows once it has read them
+  struct WaveRed {
+    float m[G4], l[G4];
+    float o[G][D];
+  };
+  static_assert(sizeof(WaveRed) <= 32 * ROWB, "wave partial fits the wave's V rows");
+  __shared__ __attribute__((aligned(16))) unsigned char vs[4 * 32 * ROWB];   // [wave][32 rows][ROWB], chunk-swizzled
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int ch = tid % CPR, rg = tid / CPR;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
   const int unit = blockIdx.x, split = blockIdx.y;
   const int b = unit / p.Hkv, kv = unit - b * p.Hkv;
   const int L = p.ctx_len[b];
   const bool ok = (L >= 1 && L <= p.Lmax);
-  const int s0 = split * SPW;
-  float* part = p.ws_part + (static_cast<size_t>(unit) * p.nsplit + split) * G * (D + 2);
+  const int s0 = split * 4;
+  float* part = p.ws_part + (static_cast<size_t>(unit) * p.nsplit + split) * decode_part_floats(G, D);
 
-  int jsl[SPW];
-  float lgl[SPW];
+  int jsl[4];
+  float lgl[4];
 #pragma unroll
-  for (int sl = 0; sl < SPW; ++sl) {
-    const int s = s0 + sl;
+  for (int t = 0; t < 4; ++t) {
+    const int s = s0 + t;
     const int j = (ok && s < p.S) ? p.ws_idx[static_cast<size_t>(unit) * p.S + s] : -1;
-    jsl[sl] = (j >= 0 && 64 * j < L) ? j : -1;
-    lgl[sl] = (jsl[sl] >= 0 && p.apply_gate)
-                  ? p.ws_logg[static_cast<size_t>(unit) * p.S + s] * kLog2e : 0.f;
+    jsl[t] = (j >= 0 && 64 * j < L) ? j : -1;
+    lgl[t] = (jsl[t] >= 0 && p.apply_gate)
+                 ? p.ws_logg[static_cast<size_t>(unit) * p.S + s] * kLog2e : 0.f;
   }
-  const size_t ubase = (static_cast<size_t>(b) * p.Hkv + kv) * p.Lmax * D + ch * 8;
-  uint4 kr[SPW][RPT], vr[SPW][RPT];
+  // Q^T operand: column h = r (zero for r >= G)
+  uint4 qb[NKS];
+  {
+    const int h = min(r, G - 1);
+    const uint16_t* qp = p.q + (static_cast<size_t>(b) * p.Hq + kv * G + h) * D + 8 * g;
 #pragma unroll
-  for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-    for (int x = 0; x < RPT; ++x) {
-      const int tok = 64 * jsl[sl] + rg + RPP * x;
-      const bool in = jsl[sl] >= 0 && tok < L;
-      kr[sl][x] = in ? ld16(p.k_cache + ubase + static_cast<size_t>(tok) * D) : make_uint4(0, 0, 0, 0);
-      vr[sl][x] = in ? ld16(p.v_cache + ubase + static_cast<size_t>(tok) * D) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint4 v = ld16(qp + 32 * ks);
+      qb[ks] = (r < G) ? v : make_uint4(0, 0, 0, 0);
     }
-  uint4 qr[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    qr[h] = ld16(p.q + (static_cast<size_t>(b) * p.Hq + kv * G + h) * D + ch * 8);
-
-  float m_run[G], l_run[G], oacc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) oacc[h][e] = 0.f;
   }
+  const size_t ubase = (static_cast<size_t>(b) * p.Hkv + kv) * p.Lmax * D;
+  // K: keys >= L lie beyond the resource and read as zeros
+  const unsigned krec = ok ? static_cast<unsigned>(L) * ROWB : 0u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k_cache + ubase), 0, krec, kBufferWord3);
+  uint4 ka[4][NKS];
+  // V: wave row 16 u + i (u = t % 2) = key 16 w + i of slot t's block; rows
+  // of a slot without a block repeat block 0 and are zeroed on reading, which
+  // keeps the loads branch-free
+  unsigned char* vw = vs + w * 32 * ROWB;
+  uint4 vr[2][NVT];
+  auto vsrc = [&](int t, int n) {
+    const int rho = 16 * (t & 1) + RPI * n + lane / CPR;
+    const int c = (lane % CPR) ^ lds_swz<ROWB>(rho);
+    const int tok = max(min(64 * max(jsl[t], 0) + 16 * w + (rho & 15), L - 1), 0);
+    return p.v_cache + ubase + static_cast<size_t>(tok) * D + c * 8;
+  };
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const unsigned row = static_cast<unsigned>(64 * jsl[t] + 16 * w + r);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      ka[t][ks] = buffer_ld16(krs, jsl[t] >= 0 ? row * ROWB + 64 * ks + 16 * g : krec);
+#pragma unroll
+    for (int n = 0; n < NVT; ++n) {
+      if (t < 2)
+        load_lds16(vsrc(t, n), vw + (16 * t + RPI * n) * ROWB);
+      else
+        vr[t - 2][n] = ld16(vsrc(t, n));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);               // every load issued before the MFMAs
   const float sl2 = p.scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4 oacc[NDT];
 #pragma unroll
-  for (int sl = 0; sl < SPW; ++sl) {
-    if (jsl[sl] < 0) continue;                       // uniform over the workgroup
-    // scores: 8-element partial dots with v_dot2_f32_bf16 (exact bf16
-    // products, fp32 accumulation), then summed over the row's lanes
-    float sc[RPT][G];
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // transposing reads: lane s of group g addresses row 4g + s/4 (of each
+  // tile), columns 16 dt + 4 (s % 4) .. +3 and receives column 16 dt + s
+  const int rho0 = 4 * g + (r >> 2);
+  const int cb = (r & 3) >> 1, hb = 8 * (r & 1);
 #pragma unroll
-    for (int x = 0; x < RPT; ++x) {
-      const uint32_t kw[4] = {kr[sl][x].x, kr[sl][x].y, kr[sl][x].z, kr[sl][x].w};
+  for (int ps = 0; ps < 2; ++ps) {
+    const int t0 = 2 * ps;
+    // S^T tiles: lane holds head r, keys 4g .. 4g + 3 of each tile
+    floatx4 sacc[2];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t qw[4] = {qr[h].x, qr[h].y, qr[h].z, qr[h].w};
-        float a = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      sacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a = dot2_bf16(qw[i], kw[i], a);
-        sc[x][h] = lane_group_sum<CPR>(a);
-      }
-      const int tok = 64 * jsl[sl] + rg + RPP * x;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        sc[x][h] = (tok < L) ? fmaf(sc[x][h], sl2, lgl[sl]) : -INFINITY;
+      for (int ks = 0; ks < NKS; ++ks) sacc[u] = mfma16x16x32(ka[t0 + u][ks], qb[ks], sacc[u]);
     }
-    // online softmax per head (state shared by the wave)
-    float pv[RPT][G];
+    float sv[2][4];
+    float mx = m_run;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = sc[0][h];
-#pragma unroll
-      for (int x = 1; x < RPT; ++x) mx = fmaxf(mx, sc[x][h]);
-      if (CPR == 8) mx = fmaxf(mx, dpp_mov<0x140>(mx));   // the two row groups of a 16-lane row
-      mx = row4_max(mx);
-      // a wave may hold no visible key of a partial current block: keep its
-      // state at -inf without forming -inf - -inf
-      const float m_new = fmaxf(m_run[h], mx);
-      const float msafe = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[h] - msafe);   // 0 while m_run is -inf
-      float ps = 0.f;
-#pragma unroll
-      for (int x = 0; x < RPT; ++x) {
-        pv[x][h] = fast_exp2(sc[x][h] - msafe);
-        ps += pv[x][h];
-      }
-      l_run[h] = l_run[h] * alpha + ps;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) oacc[h][e] *= alpha;
-      m_run[h] = m_new;
-    }
-    // O += P V: each V row chunk converted once, used by every head
-#pragma unroll
-    for (int x = 0; x < RPT; ++x) {
-      const uint32_t vw[4] = {vr[sl][x].x, vr[sl][x].y, vr[sl][x].z, vr[sl][x].w};
-      float vf[8];
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        vf[2 * i] = __uint_as_float(vw[i] << 16);
-        vf[2 * i + 1] = __uint_as_float(vw[i] & 0xffff0000u);
+        const int tok = 64 * jsl[t0 + u] + 16 * w + 4 * g + i;
+        sv[u][i] = (jsl[t0 + u] >= 0 && tok < L) ? fmaf(sacc[u][i], sl2, lgl[t0 + u]) : -INFINITY;
+        mx = fmaxf(mx, sv[u][i]);
       }
+    mx = row4_max(mx);
+    // a wave may see no valid key: keep its state at -inf, weights 0
+    const float msafe = (mx == -INFINITY) ? 0.f : mx;
+    const float alpha = fast_exp2(m_run - msafe);   // 0 while m_run is -inf
+    float ls = 0.f, pw[2][4];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) oacc[h][e] = fmaf(pv[x][h], vf[e], oacc[h][e]);
+      for (int i = 0; i < 4; ++i) {
+        pw[u][i] = fast_exp2(sv[u][i] - msafe);
+        ls += pw[u][i];
+      }
+    l_run = l_run * alpha + row4_sum(ls);
+    m_run = mx;
+    const uint4 pb = make_uint4(pack_bf2(pw[0][0], pw[0][1]), pack_bf2(pw[0][2], pw[0][3]),
+                                pack_bf2(pw[1][0], pw[1][1]), pack_bf2(pw[1][2], pw[1][3]));
+    if (ps == 0) {
+      wait_vmem_all();
+    } else {
+      // the second pass's rows replace the first's (this wave's LDS accesses
+      // complete in order, after its reads of them)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int n = 0; n < NVT; ++n) st16(vw + (16 * u + RPI * n) * ROWB + 16 * lane, vr[u][n]);
+    }
+    // O^T tiles: lane holds head r, d = 16 dt + 4g .. +3
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 v0 = lds_read_tr16(vw + rho0 * ROWB + (((2 * dt + cb) ^ lds_swz<ROWB>(rho0)) << 4) + hb);
+      uint2 v1 = lds_read_tr16(vw + (rho0 + 16) * ROWB +
+                               (((2 * dt + cb) ^ lds_swz<ROWB>(rho0 + 16)) << 4) + hb);
+      if (jsl[t0] < 0) v0 = make_uint2(0, 0);
+      if (jsl[t0 + 1] < 0) v1 = make_uint2(0, 0);
+      oacc[dt] = mfma16x16x32(make_uint4(v0.x, v0.y, v1.x, v1.y), pb, oacc[dt] * alpha);
     }
   }
-  // wave totals: sum over the wave's row groups (lanes with equal ch)
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float l = l_run[h];
-    if (CPR == 8) l += dpp_mov<0x140>(l);
-    l = row4_sum(l);
-    if (lane == 0) {
-      red_m[wv][h] = m_run[h];
-      red_l[wv][h] = l;
+  // the wave's LDS accesses complete in order: its reads of its V rows are
+  // done before these stores reach them
+  WaveRed& mine = *reinterpret_cast<WaveRed*>(vw);
+  if (r < G) {
+    if (g == 0) {
+      mine.m[r] = m_run;
+      mine.l[r] = l_run;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float o = oacc[h][e];
-      if (CPR == 8) o += dpp_mov<0x128>(o);          // row_ror:8 pairs lanes i, i+8
-      o = row4_sum(o);
-      if (lane < CPR) red_o[wv][h][ch * 8 + e] = o;
-    }
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<floatx4*>(&mine.o[r][16 * dt + 4 * g]) = oacc[dt];
   }
   __syncthreads();
+  // the split's partial, written in whole 128-byte lines
+  auto wred = [&](int q) -> const WaveRed& { return *reinterpret_cast<const WaveRed*>(vs + q * 32 * ROWB); };
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, d = e - h * D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][h]);
-    float o = 0.f, l = 0.f;
+    for (int q = 0; q < 4; ++q) M = fmaxf(M, wred(q).m[h]);
+    float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = red_m[w][h];
-      if (mw == -INFINITY) continue;
-      const float f = fast_exp2(mw - M);
-      o += red_o[w][h][d] * f;
-      l += red_l[w][h] * f;
+    for (int q = 0; q < 4; ++q) {
+      const float mq = wred(q).m[h];
+      if (mq != -INFINITY) o += wred(q).o[h][d] * fast_exp2(mq - M);
     }
-    part[h * (D + 2) + d] = o;
-    if (d == 0) {
-      part[h * (D + 2) + D] = M;
-      part[h * (D + 2) + D + 1] = l;
+    part[e] = o;
+  }
+  if (tid < 32) {
+    const int h = tid & 15;
+    float M = -INFINITY, l = 0.f;
+    if (h < G) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) M = fmaxf(M, wred(q).m[h]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float mq = wred(q).m[h];
+        if (mq != -INFINITY) l += wred(q).l[h] * fast_exp2(mq - M);
+      }
     }
+    part[G * D + tid] = tid < 16 ? M : l;
   }
 }
 

@@ -153,7 +153,8 @@ DecWs dec_ws(const sas_decode_dims* d) {
   w.idx = 0;
   w.logg = align_up(w.idx + sizeof(int32_t) * d->B * d->Hkv * S);
   w.part = align_up(w.logg + sizeof(float) * d->B * d->Hkv * S);
-  w.score = align_up(w.part + sizeof(float) * d->B * d->Hkv * w.nsplit * G * (d->D + 2));
+  w.score = align_up(w.part + sizeof(float) * d->B * d->Hkv * w.nsplit *
+                             sas::decode_part_floats(static_cast<int>(G), d->D));
   w.total = align_up(w.score + sizeof(float) * d->B * d->Hkv * d->NBmax);
   return w;
 }

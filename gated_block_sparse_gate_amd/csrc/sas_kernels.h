@@ -166,7 +166,7 @@ struct DecodeParams {
   // workspace
   int32_t* ws_idx;          // [B,Hkv,S]
   float* ws_logg;           // [B,Hkv,S]
-  float* ws_part;           // [B,Hkv,NSPLIT,G,(D+2)] partial (m, l, o[D])
+  float* ws_part;           // [B,Hkv,NSPLIT] records of decode_part_floats(G, D)
   float* ws_score;          // [B,Hkv,NBmax] gate logits of the candidate blocks
   int B, Hq, Hkv, D, dg, G, K, S, Lmax, NBmax, apply_gate, nsplit;
   float scale_log2;
@@ -202,6 +202,10 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 
 // decode split factor for a given problem (also sizes its workspace)
 int decode_nsplit(int S);
+// floats per decode split partial: o[G][D], then one 128-byte line holding the
+// per-head running max (16 slots) and sum (16 slots); a multiple of 32 floats,
+// so every partial starts on a 128-byte line and is written in whole lines
+constexpr int decode_part_floats(int G, int D) { return G * D + 32; }
 
 // dynamic LDS bytes of the Top-K kernel
 size_t topk_smem_bytes(int NB, int dg);
