@@ -8,12 +8,14 @@
 //   top-k : log-sum-exp; the min(K, c) best historical blocks (ties ->
 //           lower j) + block c (one wave per unit).
 //   attend: the G query heads attend to the selected blocks' keys tau < L
-//           with log g added (apply_gate = 1), split over NSPLIT workgroups
-//           of 4 slots whose K/V blocks (16 KiB each per tensor, contiguous
-//           in the head-major cache) are all loaded before any arithmetic;
-//           scores and P V on MFMA.
+//           with log g added (apply_gate = 1); a workgroup walks its unit's
+//           selected blocks (16 KiB each per tensor, contiguous in the
+//           head-major cache) two at a time, software-pipelined, with scores
+//           and P V on MFMA.  With fewer units than the chip needs, each
+//           unit's slots are split over NSPLIT workgroups and
 //   merge: one workgroup per unit merges the per-split (max, sum, o)
 //           partials.
+#include <algorithm>
 #include <type_traits>
 
 #include "sas_kernels.h"
@@ -22,7 +24,9 @@ namespace sas {
 
 namespace {
 
-constexpr int kSlotsPerSplit = 4;
+// workgroups the attention step aims for: two per compute unit (each holds
+// 64 KiB of loads in flight while it computes)
+constexpr int kDecodeWorkgroups = 512;
 
 // Score step: workgroup = (unit, chunk of 128 candidate blocks), 256
 // threads, 8 lanes per candidate; all of the chunk's gate-key loads are issued
@@ -244,10 +248,10 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit, in
   }
 }
 
-// Workgroup = (unit, split of four selected blocks), 256 threads, in two
-// passes of two blocks; in a pass, wave w takes keys 16w .. 16w + 15 of each
-// of the two blocks (32 keys), so the scores and P V of a wave are single
-// MFMA tiles with the G heads padded to 16 columns:
+// Workgroup = (unit, split of spw selected blocks), 256 threads, walking the
+// split in passes of two blocks; in a pass, wave w takes keys 16w .. 16w + 15
+// of each of the two blocks (32 keys), so the scores and P V of a wave are
+// single MFMA tiles with the G heads padded to 16 columns:
 //   S^T[key][h] = K Q^T      A = the wave's 16 keys of one block, loaded from
 //                            HBM straight into the operand layout (16 bytes
 //                            per lane, 64 contiguous bytes per key and load);
@@ -256,19 +260,18 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit, in
 //                            accumulator lanes (k slot 8g + i <-> key 4g + i
 //                            of the pass's first block for i < 4, of its
 //                            second block for i >= 4, on both operands).
-// Every K and V load of the workgroup (128 KiB) is issued before any
-// arithmetic: the first pass's V rows go HBM -> LDS by DMA into a per-wave
-// region, the second pass's wait in registers and take their place once the
-// first pass has read them (no workgroup barrier).  The softmax state is
-// carried online across the passes.  Keys at or beyond the context length
-// read as zeros (K: buffer range) or as the last valid row (V, with weight
-// 0); a slot without a block reads no K and zeroes its V operand.  The
-// per-wave (max, sum, O) are merged across the 4 waves in LDS, each wave's in
-// place of its own V rows, into one partial per split, written in whole
-// 128-byte lines.
+// The walk is software-pipelined over two register buffers: the next pass's
+// K and V loads (64 KiB per workgroup) are in flight while the current pass
+// computes; its V rows go through a per-wave LDS region (no workgroup
+// barrier).  The softmax state is carried online across the passes.  K and V
+// are read through buffer resources that end at the context length, so keys
+// at or beyond it, slots without a block and passes past the split's end
+// read zeros and make no memory request.  The per-wave (max, sum, O) are
+// merged across the 4 waves in LDS, each wave's in place of its own V rows;
+// with one split per unit the workgroup writes the normalised output,
+// otherwise one partial per split (whole 128-byte lines) for the merge.
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
-  static_assert(kSlotsPerSplit == 4, "two passes of two 16-key tiles per wave");
   static_assert(G >= 1 && G <= 16, "heads per KV head");
   constexpr int NKS = D / 32;             // k steps of S
   constexpr int NDT = D / 16;             // d tiles of O
@@ -284,6 +287,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
   };
   static_assert(sizeof(WaveRed) <= 32 * ROWB, "wave partial fits the wave's V rows");
   __shared__ __attribute__((aligned(16))) unsigned char vs[4 * 32 * ROWB];   // [wave][32 rows][ROWB], chunk-swizzled
+  struct PassBuf {
+    uint4 k[2][NKS];
+    uint4 v[2][NVT];
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -291,19 +298,23 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
   const int b = unit / p.Hkv, kv = unit - b * p.Hkv;
   const int L = p.ctx_len[b];
   const bool ok = (L >= 1 && L <= p.Lmax);
-  const int s0 = split * 4;
-  float* part = p.ws_part + (static_cast<size_t>(unit) * p.nsplit + split) * decode_part_floats(G, D);
+  const int spw = p.spw, npass = spw / 2;
+  const int s0 = split * spw;
 
-  int jsl[4];
-  float lgl[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int s = s0 + t;
+  // slot table: lane i < spw holds slot s0 + i (block, log2-domain gate bias)
+  int jv = -1;
+  float lv = 0.f;
+  if (lane < spw) {
+    const int s = s0 + lane;
     const int j = (ok && s < p.S) ? p.ws_idx[static_cast<size_t>(unit) * p.S + s] : -1;
-    jsl[t] = (j >= 0 && 64 * j < L) ? j : -1;
-    lgl[t] = (jsl[t] >= 0 && p.apply_gate)
-                 ? p.ws_logg[static_cast<size_t>(unit) * p.S + s] * kLog2e : 0.f;
+    jv = (j >= 0 && 64 * j < L) ? j : -1;
+    lv = (jv >= 0 && p.apply_gate) ? p.ws_logg[static_cast<size_t>(unit) * p.S + s] * kLog2e : 0.f;
   }
+  auto slot_j = [&](int t) { return t < spw ? __builtin_amdgcn_readlane(jv, t) : -1; };
+  auto slot_lg = [&](int t) {
+    return t < spw ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), t)) : 0.f;
+  };
+
   // Q^T operand: column h = r (zero for r >= G)
   uint4 qb[NKS];
   {
@@ -316,37 +327,32 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
     }
   }
   const size_t ubase = (static_cast<size_t>(b) * p.Hkv + kv) * p.Lmax * D;
-  // K: keys >= L lie beyond the resource and read as zeros
-  const unsigned krec = ok ? static_cast<unsigned>(L) * ROWB : 0u;
+  const unsigned rec = ok ? static_cast<unsigned>(L) * ROWB : 0u;
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k_cache + ubase), 0, krec, kBufferWord3);
-  uint4 ka[4][NKS];
-  // V: wave row 16 u + i (u = t % 2) = key 16 w + i of slot t's block; rows
-  // of a slot without a block repeat block 0 and are zeroed on reading, which
-  // keeps the loads branch-free
-  unsigned char* vw = vs + w * 32 * ROWB;
-  uint4 vr[2][NVT];
-  auto vsrc = [&](int t, int n) {
-    const int rho = 16 * (t & 1) + RPI * n + lane / CPR;
-    const int c = (lane % CPR) ^ lds_swz<ROWB>(rho);
-    const int tok = max(min(64 * max(jsl[t], 0) + 16 * w + (rho & 15), L - 1), 0);
-    return p.v_cache + ubase + static_cast<size_t>(tok) * D + c * 8;
-  };
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k_cache + ubase), 0, rec, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v_cache + ubase), 0, rec, kBufferWord3);
+  // V rows of a pass: wave row 16 u + i = key 16 w + i of block u, lane's
+  // 16-byte chunk stored at its swizzled place
+  const int vrow = lane / CPR;
+  auto issue = [&](PassBuf& pb, int ps) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const unsigned row = static_cast<unsigned>(64 * jsl[t] + 16 * w + r);
+    for (int u = 0; u < 2; ++u) {
+      const int j = slot_j(2 * ps + u);
+      const unsigned krow = static_cast<unsigned>(64 * j + 16 * w + r);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      ka[t][ks] = buffer_ld16(krs, jsl[t] >= 0 ? row * ROWB + 64 * ks + 16 * g : krec);
+      for (int ks = 0; ks < NKS; ++ks)
+        pb.k[u][ks] = buffer_ld16(krs, j >= 0 ? krow * ROWB + 64 * ks + 16 * g : rec);
 #pragma unroll
-    for (int n = 0; n < NVT; ++n) {
-      if (t < 2)
-        load_lds16(vsrc(t, n), vw + (16 * t + RPI * n) * ROWB);
-      else
-        vr[t - 2][n] = ld16(vsrc(t, n));
+      for (int n = 0; n < NVT; ++n) {
+        const int rho = 16 * u + RPI * n + vrow;
+        const int c = (lane % CPR) ^ lds_swz<ROWB>(rho);
+        const unsigned vr = static_cast<unsigned>(64 * j + 16 * w + RPI * n + vrow);
+        pb.v[u][n] = buffer_ld16(vrs, j >= 0 ? vr * ROWB + 16 * c : rec);
+      }
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);               // every load issued before the MFMAs
+  };
+  unsigned char* vw = vs + w * 32 * ROWB;
   const float sl2 = p.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
   floatx4 oacc[NDT];
@@ -356,16 +362,21 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
   // tile), columns 16 dt + 4 (s % 4) .. +3 and receives column 16 dt + s
   const int rho0 = 4 * g + (r >> 2);
   const int cb = (r & 3) >> 1, hb = 8 * (r & 1);
+  auto attend = [&](const PassBuf& pb, int ps) {
+    int jt[2];
+    float lg[2];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    const int t0 = 2 * ps;
+    for (int u = 0; u < 2; ++u) {
+      jt[u] = slot_j(2 * ps + u);
+      lg[u] = slot_lg(2 * ps + u);
+    }
     // S^T tiles: lane holds head r, keys 4g .. 4g + 3 of each tile
     floatx4 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       sacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) sacc[u] = mfma16x16x32(ka[t0 + u][ks], qb[ks], sacc[u]);
+      for (int ks = 0; ks < NKS; ++ks) sacc[u] = mfma16x16x32(pb.k[u][ks], qb[ks], sacc[u]);
     }
     float sv[2][4];
     float mx = m_run;
@@ -373,8 +384,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 64 * jsl[t0 + u] + 16 * w + 4 * g + i;
-        sv[u][i] = (jsl[t0 + u] >= 0 && tok < L) ? fmaf(sacc[u][i], sl2, lgl[t0 + u]) : -INFINITY;
+        const int tok = 64 * jt[u] + 16 * w + 4 * g + i;
+        sv[u][i] = (jt[u] >= 0 && tok < L) ? fmaf(sacc[u][i], sl2, lg[u]) : -INFINITY;
         mx = fmaxf(mx, sv[u][i]);
       }
     mx = row4_max(mx);
@@ -391,29 +402,32 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
       }
     l_run = l_run * alpha + row4_sum(ls);
     m_run = mx;
-    const uint4 pb = make_uint4(pack_bf2(pw[0][0], pw[0][1]), pack_bf2(pw[0][2], pw[0][3]),
-                                pack_bf2(pw[1][0], pw[1][1]), pack_bf2(pw[1][2], pw[1][3]));
-    if (ps == 0) {
-      wait_vmem_all();
-    } else {
-      // the second pass's rows replace the first's (this wave's LDS accesses
-      // complete in order, after its reads of them)
+    const uint4 pbf = make_uint4(pack_bf2(pw[0][0], pw[0][1]), pack_bf2(pw[0][2], pw[0][3]),
+                                 pack_bf2(pw[1][0], pw[1][1]), pack_bf2(pw[1][2], pw[1][3]));
+    // this pass's rows replace the previous pass's (the wave's LDS accesses
+    // complete in order, after its reads of them)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int n = 0; n < NVT; ++n) st16(vw + (16 * u + RPI * n) * ROWB + 16 * lane, vr[u][n]);
-    }
+      for (int n = 0; n < NVT; ++n) st16(vw + (16 * u + RPI * n) * ROWB + 16 * lane, pb.v[u][n]);
     // O^T tiles: lane holds head r, d = 16 dt + 4g .. +3
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      uint2 v0 = lds_read_tr16(vw + rho0 * ROWB + (((2 * dt + cb) ^ lds_swz<ROWB>(rho0)) << 4) + hb);
-      uint2 v1 = lds_read_tr16(vw + (rho0 + 16) * ROWB +
-                               (((2 * dt + cb) ^ lds_swz<ROWB>(rho0 + 16)) << 4) + hb);
-      if (jsl[t0] < 0) v0 = make_uint2(0, 0);
-      if (jsl[t0 + 1] < 0) v1 = make_uint2(0, 0);
-      oacc[dt] = mfma16x16x32(make_uint4(v0.x, v0.y, v1.x, v1.y), pb, oacc[dt] * alpha);
+      const uint2 v0 = lds_read_tr16(vw + rho0 * ROWB + (((2 * dt + cb) ^ lds_swz<ROWB>(rho0)) << 4) + hb);
+      const uint2 v1 = lds_read_tr16(vw + (rho0 + 16) * ROWB +
+                                     (((2 * dt + cb) ^ lds_swz<ROWB>(rho0 + 16)) << 4) + hb);
+      oacc[dt] = mfma16x16x32(make_uint4(v0.x, v0.y, v1.x, v1.y), pbf, oacc[dt] * alpha);
     }
+  };
+  PassBuf bufa, bufb;
+  issue(bufa, 0);
+  for (int ps = 0; ps < npass; ps += 2) {
+    issue(bufb, ps + 1);          // past the end: no memory request
+    attend(bufa, ps);
+    issue(bufa, ps + 2);
+    if (ps + 1 < npass) attend(bufb, ps + 1);
   }
+  wait_vmem_all();
   // the wave's LDS accesses complete in order: its reads of its V rows are
   // done before these stores reach them
   WaveRed& mine = *reinterpret_cast<WaveRed*>(vw);
@@ -427,8 +441,37 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
       *reinterpret_cast<floatx4*>(&mine.o[r][16 * dt + 4 * g]) = oacc[dt];
   }
   __syncthreads();
-  // the split's partial, written in whole 128-byte lines
   auto wred = [&](int q) -> const WaveRed& { return *reinterpret_cast<const WaveRed*>(vs + q * 32 * ROWB); };
+  auto head_ml = [&](int h, float& M, float& l) {
+    M = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) M = fmaxf(M, wred(q).m[h]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float mq = wred(q).m[h];
+      if (mq != -INFINITY) l += wred(q).l[h] * fast_exp2(mq - M);
+    }
+  };
+  if (p.nsplit == 1) {
+    // the unit's output, normalised (NaN for an invalid context length)
+    for (int e = tid; e < G * D; e += 256) {
+      const int h = e / D, d = e - h * D;
+      float M, l;
+      head_ml(h, M, l);
+      float o = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float mq = wred(q).m[h];
+        if (mq != -INFINITY) o += wred(q).o[h][d] * fast_exp2(mq - M);
+      }
+      const float inv_l = (ok && l > 0.f) ? 1.f / l : __builtin_nanf("");
+      p.o[(static_cast<size_t>(b) * p.Hq + kv * G) * D + e] = f2bf(o * inv_l);
+    }
+    return;
+  }
+  // the split's partial, written in whole 128-byte lines
+  float* part = p.ws_part + (static_cast<size_t>(unit) * p.nsplit + split) * decode_part_floats(G, D);
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, d = e - h * D;
     float M = -INFINITY;
@@ -445,15 +488,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
   if (tid < 32) {
     const int h = tid & 15;
     float M = -INFINITY, l = 0.f;
-    if (h < G) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) M = fmaxf(M, wred(q).m[h]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float mq = wred(q).m[h];
-        if (mq != -INFINITY) l += wred(q).l[h] * fast_exp2(mq - M);
-      }
-    }
+    if (h < G) head_ml(h, M, l);
     part[G * D + tid] = tid < 16 ? M : l;
   }
 }
@@ -469,7 +504,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 
 }  // namespace
 
-int decode_nsplit(int S) { return (S + kSlotsPerSplit - 1) / kSlotsPerSplit; }
+void decode_split(int S, int units, int* nsplit, int* spw) {
+  // about kDecodeWorkgroups workgroups over the chip; a split walks an even
+  // number of slots (passes of two blocks)
+  const int pairs = (S + 1) / 2;
+  const int want = (kDecodeWorkgroups + units - 1) / units;
+  const int ns = std::max(1, std::min(pairs, want));
+  const int ppw = (pairs + ns - 1) / ns;
+  *spw = 2 * ppw;
+  *nsplit = (pairs + ppw - 1) / ppw;
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st) {
   const unsigned units = static_cast<unsigned>(p.B) * p.Hkv;
@@ -485,81 +529,29 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t st) {
   else
     hipLaunchKernelGGL((decode_topk_kernel<true>), dim3((units + 3) / 4), dim3(256), 0, st, p);
   const dim3 agrid(units, p.nsplit);
-  if (p.D == 128) {
+  auto attend = [&](auto dc, auto gc) {
+    constexpr int D = decltype(dc)::value, G = decltype(gc)::value;
+    hipLaunchKernelGGL((decode_attn_kernel<D, G>), agrid, dim3(256), 0, st, p);
+    if (p.nsplit > 1)
+      hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(units), dim3(256), 0, st, p);
+  };
+  auto by_g = [&](auto dc) -> bool {
     switch (p.G) {
-      case 1:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 1>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 1>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 2:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 2>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 2>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 3:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 3>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 3>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 4:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 4>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 4>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 5:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 5>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 5>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 6:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 6>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 6>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 7:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 7>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 7>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 8:
-        hipLaunchKernelGGL((decode_attn_kernel<128, 8>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<128, 8>), dim3(units), dim3(256), 0, st, p);
-        break;
-      default: return hipErrorInvalidValue;
+      case 1: attend(dc, std::integral_constant<int, 1>{}); return true;
+      case 2: attend(dc, std::integral_constant<int, 2>{}); return true;
+      case 3: attend(dc, std::integral_constant<int, 3>{}); return true;
+      case 4: attend(dc, std::integral_constant<int, 4>{}); return true;
+      case 5: attend(dc, std::integral_constant<int, 5>{}); return true;
+      case 6: attend(dc, std::integral_constant<int, 6>{}); return true;
+      case 7: attend(dc, std::integral_constant<int, 7>{}); return true;
+      case 8: attend(dc, std::integral_constant<int, 8>{}); return true;
+      default: return false;
     }
-  } else if (p.D == 64) {
-    switch (p.G) {
-      case 1:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 1>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 1>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 2:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 2>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 2>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 3:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 3>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 3>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 4:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 4>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 4>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 5:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 5>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 5>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 6:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 6>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 6>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 7:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 7>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 7>), dim3(units), dim3(256), 0, st, p);
-        break;
-      case 8:
-        hipLaunchKernelGGL((decode_attn_kernel<64, 8>), agrid, dim3(256), 0, st, p);
-        hipLaunchKernelGGL((decode_merge_kernel<64, 8>), dim3(units), dim3(256), 0, st, p);
-        break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    return hipErrorInvalidValue;
-  }
+  };
+  bool launched = false;
+  if (p.D == 128) launched = by_g(std::integral_constant<int, 128>{});
+  else if (p.D == 64) launched = by_g(std::integral_constant<int, 64>{});
+  if (!launched) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

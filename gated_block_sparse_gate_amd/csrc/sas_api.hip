@@ -144,17 +144,18 @@ BwdWs bwd_ws(const sas_dims* d) {
   return w;
 }
 
-struct DecWs { size_t idx, logg, part, score, total; int nsplit; };
+struct DecWs { size_t idx, logg, part, score, total; int nsplit, spw; };
 DecWs dec_ws(const sas_decode_dims* d) {
   const size_t S = d->topk + 1;
   const size_t G = d->Hq / d->Hkv;
   DecWs w;
-  w.nsplit = sas::decode_nsplit(static_cast<int>(S));
+  sas::decode_split(static_cast<int>(S), d->B * d->Hkv, &w.nsplit, &w.spw);
   w.idx = 0;
   w.logg = align_up(w.idx + sizeof(int32_t) * d->B * d->Hkv * S);
   w.part = align_up(w.logg + sizeof(float) * d->B * d->Hkv * S);
-  w.score = align_up(w.part + sizeof(float) * d->B * d->Hkv * w.nsplit *
-                             sas::decode_part_floats(static_cast<int>(G), d->D));
+  // split partials (none with one split per unit)
+  const size_t nparts = w.nsplit > 1 ? static_cast<size_t>(d->B) * d->Hkv * w.nsplit : 0;
+  w.score = align_up(w.part + sizeof(float) * nparts * sas::decode_part_floats(static_cast<int>(G), d->D));
   w.total = align_up(w.score + sizeof(float) * d->B * d->Hkv * d->NBmax);
   return w;
 }
@@ -424,7 +425,7 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
   p.ws_score = reinterpret_cast<float*>(base + w.score);
   p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
   p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
-  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit;
+  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw;
   p.scale_log2 = scale * sas::kLog2e;
   g_err.clear();
   return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)), "sas_decode launch");

@@ -168,7 +168,8 @@ struct DecodeParams {
   float* ws_logg;           // [B,Hkv,S]
   float* ws_part;           // [B,Hkv,NSPLIT] records of decode_part_floats(G, D)
   float* ws_score;          // [B,Hkv,NBmax] gate logits of the candidate blocks
-  int B, Hq, Hkv, D, dg, G, K, S, Lmax, NBmax, apply_gate, nsplit;
+  int B, Hq, Hkv, D, dg, G, K, S, Lmax, NBmax, apply_gate;
+  int nsplit, spw;          // attention splits per unit, slots per split
   float scale_log2;
 };
 
@@ -200,8 +201,9 @@ hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st);
 hipError_t take_ring_fault_bwd(unsigned* out);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 
-// decode split factor for a given problem (also sizes its workspace)
-int decode_nsplit(int S);
+// decode attention splits per unit and (even) slots per split for S slots and
+// units = B * Hkv (also sizes the workspace)
+void decode_split(int S, int units, int* nsplit, int* spw);
 // floats per decode split partial: o[G][D], then one 128-byte line holding the
 // per-head running max (16 slots) and sum (16 slots); a multiple of 32 floats,
 // so every partial starts on a 128-byte line and is written in whole lines
