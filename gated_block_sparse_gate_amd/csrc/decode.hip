@@ -82,13 +82,14 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeParams p) {
 }
 
 // Selection step: one wave per unit (4 units per workgroup).  Log-sum-exp
-// over the c + 1 scores, then the min(K, c) largest historical scores by a
-// 32-step bitwise search on order keys with ballot counts (ties -> lower
-// block), ascending, then block c; pads -1 / -inf.
+// over the c + 1 scores, then the min(K, c) largest historical scores by
+// bitwise searches on order keys with ballot counts (ties -> lower block),
+// ascending, then block c; pads -1 / -inf.
 template <bool LONG>
 __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ uint32_t gath[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int unit = blockIdx.x * 4 + wv;
   if (unit >= p.B * p.Hkv) return;
   const int b = unit / p.Hkv;
   const int L = p.ctx_len[b];
@@ -165,12 +166,46 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
     uint32_t thr = 0;
     int need_eq = 0;
     if (!all) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
+      // thr = the largest t with #(keys >= t) >= K, by a bitwise search.
+      // The K-th largest lane maximum t0 bounds it from below (the K largest
+      // lane maxima are K keys at or above t0; at least K lanes hold a
+      // candidate since c > K and K < 64), so when the keys >= t0 fit one per
+      // lane the search runs over them alone (same counts for every t >= t0).
+      uint32_t lmax = 0;
 #pragma unroll
-        for (int e = 0; e < ne; ++e) cnt += wave_count(key(e) >= cand);
-        if (cnt >= K) thr = cand;
+      for (int e = 0; e < ne; ++e) lmax = max(lmax, key(e));
+      uint32_t t0 = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = t0 | (1u << bit);
+        if (wave_count(lmax >= cand) >= K) t0 = cand;
+      }
+      int n0 = 0;
+#pragma unroll
+      for (int e = 0; e < ne; ++e) n0 += wave_count(key(e) >= t0);
+      if (n0 <= 64) {
+        int nb = 0;
+#pragma unroll
+        for (int e = 0; e < ne; ++e) {
+          const uint32_t kk = key(e);
+          const bool in = kk >= t0;
+          const uint64_t m = ballot64(in);
+          if (in) gath[wv][nb + __popcll(m & lt_mask)] = kk;
+          nb += __popcll(m);
+        }
+        // the wave's LDS accesses complete in order
+        const uint32_t v = lane < n0 ? gath[wv][lane] : 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = thr | (1u << bit);
+          if (wave_count(v >= cand) >= K) thr = cand;
+        }
+      } else {
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = thr | (1u << bit);
+          int cnt = 0;
+#pragma unroll
+          for (int e = 0; e < ne; ++e) cnt += wave_count(key(e) >= cand);
+          if (cnt >= K) thr = cand;
+        }
       }
       int gt = 0;
 #pragma unroll
