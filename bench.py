@@ -87,6 +87,7 @@ COPY_BYTES = 1 << 30          # the calibration copy (--copy-calib)
 TRAFFIC_SOURCES = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
                    "dq_kernel": "attn_bwd.hip", "topk_kernel": "topk.hip",
                    "decode_attn_kernel": "decode.hip", "decode_score_kernel": "decode.hip",
+                   "decode_topk_kernel": "decode.hip", "decode_merge_kernel": "decode.hip",
                    "gbwd_key_kernel": "router_bwd.hip", "gbwd_query_kernel": "router_bwd.hip",
                    "gbwd_blockkey_kernel": "router_bwd.hip", "gbwd_wsum_kernel": "router_bwd.hip",
                    "gbwd_rows_kernel": "router_bwd.hip"}
@@ -140,6 +141,16 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
         lines.append(f"{key}: fetch {e.get('fetch_size_bytes', 0) / 1e9:.3f} GB + write "
                      f"{e.get('write_size_bytes', 0) / 1e9:.3f} GB per launch "
                      f"({e['dispatches']} dispatches)")
+    # the decode step as a whole: each of its kernels runs once per step
+    dec = [k for k in res if k.startswith("decode_")]
+    if dec:
+        res["sas_decode"] = {
+            "bytes_per_launch": sum(res[k]["bytes_per_launch"] for k in dec),
+            "kernels": sorted(dec),
+            "source_hash": source_hash([os.path.join(csrc, f) for f in
+                                        ("decode.hip", "sas_device.h", "sas_kernels.h")])}
+        lines.append(f"sas_decode: {res['sas_decode']['bytes_per_launch'] / 1e9:.3f} GB per step "
+                     f"({' + '.join(sorted(dec))})")
     json.dump(res, open(out_json, "w"), indent=1, sort_keys=True)
     print("\n".join(lines))
 
@@ -479,7 +490,7 @@ def main():
             "GBps_cold": round(tot / (cold_us * 1e-6) / 1e9, 1),
             "KV_GBps_cold": round(kvb / (cold_us * 1e-6) / 1e9, 1),
             "GBps_warm": round(tot / (warm_us * 1e-6) / 1e9, 1),
-            "roofline": {"kernel": "sas_decode (select + split attention + combine)",
+            "roofline": {"kernel": "sas_decode (score + select + attention)",
                          "bound": "hbm", "achieved": round(tot / (cold_us * 1e-6) / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(tot / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
