@@ -280,6 +280,13 @@ DEC_CASES = [
     (2, 10, 2, 64, 32, 3, 700, [700, 300]),
     # beyond 1,024 blocks (the selection's long-context path); one visible key
     (2, 2, 1, 64, 32, 5, 70000, [70000, 4161]),
+    # 512 units: one workgroup walks all of a unit's slots and writes the
+    # output (no split partials); an odd number of two-block passes, one-token
+    # and partial current blocks, contexts shorter than the budget
+    (128, 8, 4, 64, 32, 5, 700,
+     [1, 64, 65, 700] + [int(v) for v in np.random.default_rng(5).integers(1, 701, size=124)]),
+    (128, 12, 4, 128, 64, 3, 400,
+     [1, 64, 65, 400] + [int(v) for v in np.random.default_rng(6).integers(1, 401, size=124)]),
 ]
 
 
