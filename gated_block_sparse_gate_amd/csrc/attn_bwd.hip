@@ -23,136 +23,32 @@ namespace sas {
 
 namespace {
 
-// Per (b, kappa) maxima of |k| and |v| over token chunk blockIdx.x (bf16
-// magnitudes compared as integers: the bit patterns of non-negative bf16
-// values order like the values).
-template <int D>
-__global__ __launch_bounds__(256) void kv_amax_kernel(const uint16_t* k, const uint16_t* v,
-                                                      float* part, int T, int Hkv) {
-  constexpr int CPR = D / 8;
-  __shared__ uint32_t red[2][4];
-  const int bk = blockIdx.y, b = bk / Hkv, kv = bk - b * Hkv;
-  const int per = (T + kAmaxChunks - 1) / kAmaxChunks;
-  const int t0 = blockIdx.x * per, t1 = min(T, t0 + per);
-  uint32_t mk = 0, mv = 0;
-  for (int i = threadIdx.x; i < (t1 - t0) * CPR; i += 256) {
-    const int t = t0 + i / CPR, c = i - (i / CPR) * CPR;
-    const size_t off = ((static_cast<size_t>(b) * T + t) * Hkv + kv) * D + 8 * c;
-    const uint4 x = ld16(k + off), y = ld16(v + off);
-    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      mk = max(mk, max(xs[e] & 0x7fffu, (xs[e] >> 16) & 0x7fffu));
-      mv = max(mv, max(ys[e] & 0x7fffu, (ys[e] >> 16) & 0x7fffu));
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mk = max(mk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mk), o, 64)));
-    mv = max(mv, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mv), o, 64)));
-  }
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    red[0][wv] = mk;
-    red[1][wv] = mv;
-  }
-  __syncthreads();
-  if (threadIdx.x < 2) {
-    const uint32_t* r = red[threadIdx.x];
-    const uint32_t m = max(max(r[0], r[1]), max(r[2], r[3]));
-    part[(static_cast<size_t>(bk) * kAmaxChunks + blockIdx.x) * 2 + threadIdx.x] =
-        bf2f(static_cast<uint16_t>(m));
-  }
-}
-
-// Power of two 2^e with x * 2^-e in [2^14, 2^15) (1 for x = 0 or not finite).
-__device__ __forceinline__ int exp_below_2p15(float x) {
-  if (!(x > 0.f) || !(x < INFINITY)) return 0;
-  return max(-100, min(100, ilogbf(x) - 14));
-}
-
-// kmul = 2^e_k of max |k| (the fp16 k copy holds k * 2^-e_k, exact for every
-// k whose scaled magnitude is at least 2^-14), vamax = max |v|.
-__global__ __launch_bounds__(64) void kv_amax_final_kernel(const float* part, float* kmul,
-                                                           float* vamax, int nbk) {
-  const int bk = blockIdx.x * 64 + threadIdx.x;
-  if (bk >= nbk) return;
-  float mk = 0.f, mv = 0.f;
-  for (int c = 0; c < kAmaxChunks; ++c) {
-    mk = fmaxf(mk, part[(static_cast<size_t>(bk) * kAmaxChunks + c) * 2]);
-    mv = fmaxf(mv, part[(static_cast<size_t>(bk) * kAmaxChunks + c) * 2 + 1]);
-  }
-  kmul[bk] = ldexpf(1.f, exp_below_2p15(mk));
-  vamax[bk] = mv;
-}
-
-// kf16 = fp16(k / kmul), 8 elements per thread; rows (b, t, kappa).
-template <int D>
-__global__ __launch_bounds__(256) void k_f16_kernel(const uint16_t* k, uint16_t* kf,
-                                                    const float* kmul, long nrows, int T, int Hkv) {
-  constexpr int CPR = D / 8;
-  const long gid = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x;
-  if (gid >= nrows * CPR) return;
-  const long row = gid / CPR;
-  const long b = row / (static_cast<long>(T) * Hkv);
-  const int kv = static_cast<int>(row % Hkv);
-  const float inv = 1.f / kmul[b * Hkv + kv];        // a power of two: exact
-  const uint4 x = ld16(k + gid * 8);
-  const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-  uint32_t ys[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    ys[e] = pack_h2(__uint_as_float(xs[e] << 16) * inv, __uint_as_float(xs[e] & 0xffff0000u) * inv);
-  st16(kf + gid * 8, make_uint4(ys[0], ys[1], ys[2], ys[3]));
-}
-
-// Delta = rowsum(dO * o) per (b, t, h), from o_f32 when given, and the
-// power of two dsscale = 2^-e that keeps the row's dS below 2^15 in fp16:
-// |dS_k| = P_k |dO . (v_k - o)| <= 2 |dO| max_k |v_k| <= 2 |dO| sqrt(D) max|v|
-// (P_k <= 1, o a convex combination of the v_k), doubled for rounding.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const float* o32,
                                                         const uint16_t* dout, float* delta,
-                                                        float* dsscale, const float* vamax,
-                                                        long nrows, int T, int Hq, int Hkv, int G) {
+                                                        long nrows) {
   constexpr int EPL = D / 16;
   const long gid = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x;
   const long row = gid >> 4;
   const int part = static_cast<int>(gid & 15);
-  float acc = 0.f, nrm = 0.f;
+  float acc = 0.f;
   if (row < nrows) {
     const uint16_t* pd = dout + row * D + part * EPL;
     if (o32) {
       const float* po = o32 + row * D + part * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float g = bf2f(pd[e]);
-        acc = fmaf(po[e], g, acc);
-        nrm = fmaf(g, g, nrm);
-      }
+      for (int e = 0; e < EPL; ++e) acc = fmaf(po[e], bf2f(pd[e]), acc);
     } else {
       const uint16_t* po = o + row * D + part * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float g = bf2f(pd[e]);
-        acc = fmaf(bf2f(po[e]), g, acc);
-        nrm = fmaf(g, g, nrm);
-      }
+      for (int e = 0; e < EPL; ++e) acc = fmaf(bf2f(po[e]), bf2f(pd[e]), acc);
     }
   }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    acc += __shfl_xor(acc, m, 64);
-    nrm += __shfl_xor(nrm, m, 64);
-  }
-  if (part == 0 && row < nrows) {
-    delta[row] = acc;
-    // row = (b * T + t) * Hq + h; its KV head is (b, h / G)
-    const long b = row / (static_cast<long>(T) * Hq);
-    const int h = static_cast<int>(row % Hq);
-    const float bound = 4.f * sqrtf(nrm) * sqrtf(static_cast<float>(D)) * vamax[b * Hkv + h / G];
-    dsscale[row] = ldexpf(1.f, -exp_below_2p15(bound));
-  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  acc += __shfl_xor(acc, 8, 64);
+  if (part == 0 && row < nrows) delta[row] = acc;
 }
 
 // Per (b, kappa, query block c): which of the 64 tokens selected each block j.
@@ -263,10 +159,8 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(BwdParams p) {
 // workgroups start at the end of the sequence and sweep it at about the same
 // rate, so the ones in flight on an XCD gather from nearby rows.  Software
 // pipeline per tile pair `it`: the CSR entry is read 3 pairs ahead, the row
-// metadata (lse, Delta, log g, dS scale) 2 ahead, the Q / dO rows 1 ahead
-// (registers), so the gathers overlap the MFMA work of the current pair.  dS
-// leaves for the dQ kernel as fp16 of dS times the row's dsscale, a power of
-// two below the a-priori bound of the row's |dS|, so it cannot overflow.
+// metadata (lse, Delta, log g) 2 ahead, the Q / dO rows 1 ahead (registers),
+// so the gathers overlap the MFMA work of the current pair.
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   constexpr int NKS = D / 32, NDT = D / 16;
@@ -281,13 +175,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) int m_t[3][32];
   __shared__ __attribute__((aligned(16))) float m_bias[3][32];
   __shared__ __attribute__((aligned(16))) float m_delta[3][32];
-  __shared__ __attribute__((aligned(16))) float m_dsc[3][32];
   __shared__ __attribute__((aligned(16))) int m_src[3][32];
   __shared__ __attribute__((aligned(16))) int m_ent[3][32];
-  // dS of the tile pair, [32 rows][64] scaled fp16 in operand key order
-  // (row pitch 144 bytes: consecutive rows start on different banks), and
-  // each wave's row sums of dS over its 16 keys
-  constexpr int DSP = 144;
+  // dS of the tile pair, [32 rows][hi 64 | lo 64] bf16 in operand key order
+  // (row pitch 272 bytes: rows 4 apart start on different banks), and each
+  // wave's row sums of dS over its 16 keys
+  constexpr int DSP = 272;
   __shared__ __attribute__((aligned(16))) uint8_t dsT[32 * DSP];
   __shared__ __attribute__((aligned(16))) float dsum[4][32];
 
@@ -334,7 +227,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     if (mrr >= RT || ti >= n) return -1;
     return ent[ti];
   };
-  float r_lse = -INFINITY, r_del = 0.f, r_lg = 0.f, r_dsc = 0.f;
+  float r_lse = -INFINITY, r_del = 0.f, r_lg = 0.f;
   int r_t = -1, r_src = -1, r_en = -1;
   auto meta_issue = [&](int en) {
     if (en >= 0) {
@@ -347,7 +240,6 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       const size_t qrow = (static_cast<size_t>(b) * p.T + tk) * p.Hq + kv * G + mhh;
       r_lse = p.lse[qrow];
       r_del = p.delta[qrow];
-      r_dsc = p.dsscale[qrow];
       r_lg = p.logg[((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + s];
       r_t = tk;
       r_src = static_cast<int>(qrow);
@@ -360,7 +252,6 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     m_ent[slot][mr] = r_en;
     m_bias[slot][mr] = ok ? r_lg * kLog2e - r_lse * kLog2e : 0.f;
     m_delta[slot][mr] = ok ? r_del : 0.f;
-    m_dsc[slot][mr] = ok ? r_dsc : 0.f;
   };
 
   // ---- Q / dO rows (all threads): unit = (chunk ch, row pair rp)
@@ -439,15 +330,18 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   // (each (token, slot) is in exactly one tile pair of one workgroup)
   auto store_ds = [&](int pp) __attribute__((always_inline)) {
     const int msp = pp % 3;
-    // thread: 16-byte part `part` of row r (head (r % 16) % G)
-    const int r = tid >> 3, part = tid & 7, hh = (r & 15) % G;
-    const int en = m_ent[msp][r];
-    const uint4 v = ld16(dsT + r * DSP + part * 16);
-    if (en >= 0)
-      st16(p.dsbuf +
-               ((((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)) * G +
-                hh) * 64 + part * 8,
-           v);
+    // thread: 16-byte part `part` of rows r0 and r0 + 16 (same head)
+    const int r0 = tid >> 4, part = tid & 15, hh = r0 % G;
+    const int en0 = m_ent[msp][r0], en1 = m_ent[msp][r0 + 16];
+    const uint4 v0 = ld16(dsT + r0 * DSP + part * 16);
+    const uint4 v1 = ld16(dsT + (r0 + 16) * DSP + part * 16);
+    auto dst = [&](int en) {
+      return p.dsbuf +
+             ((((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)) * G +
+              hh) * 128 + part * 8;
+    };
+    if (en0 >= 0) st16(dst(en0), v0);
+    if (en1 >= 0) st16(dst(en1), v1);
     // wave 1: d log g of one (token, slot) per lane, summed over the G heads
     // and the 4 waves' key quarters in a fixed order
     const int q = tid - 64;
@@ -498,17 +392,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         pacc[tt] = mfma16x16x32(da, vb[ks], pacc[tt]);
       }
     }
-    float pv[2][4], ds[2][4], dsc[2][4];
+    float pv[2][4], ds[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int r = tt * 16 + g4 * 4;
       const int4 tv = *reinterpret_cast<const int4*>(&m_t[ms][r]);
       const float4 bv = *reinterpret_cast<const float4*>(&m_bias[ms][r]);
       const float4 dl = *reinterpret_cast<const float4*>(&m_delta[ms][r]);
-      const float4 dc = *reinterpret_cast<const float4*>(&m_dsc[ms][r]);
       const int ta[4] = {tv.x, tv.y, tv.z, tv.w};
       const float ba[4] = {bv.x, bv.y, bv.z, bv.w}, da[4] = {dl.x, dl.y, dl.z, dl.w};
-      dsc[tt][0] = dc.x; dsc[tt][1] = dc.y; dsc[tt][2] = dc.z; dsc[tt][3] = dc.w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // masked entries (no query row, or a key past the token) are dropped
@@ -521,24 +413,27 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     }
     // the previous pair's dS tile has been read (store_ds) by every thread
     __syncthreads();
-    // dS times the row's dsscale as fp16 into the tile.  Lane (l16, g4) holds
-    // rows 4 g4 + i (i = 0..3) of its key 16 wv + l16; the lanes of an
-    // even/odd key pair (adjacent operand positions) swap halves so that each
-    // writes two rows as 32-bit (two-key) words: the even lane rows 0, 1, the
-    // odd lane rows 2, 3.
+    // dS as bf16 hi + lo into the tile.  Lane (l16, g4) holds rows 4 g4 + i
+    // (i = 0..3) of its key 16 wv + l16; the lanes of an even/odd key pair
+    // (adjacent operand positions) swap halves so that each writes two rows
+    // as 32-bit (two-key) words: the even lane rows 0, 1, the odd lane rows 2, 3.
     {
       const bool odd = l16 & 1;
       const int pe = kpos & ~1;                 // operand position of the even key
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        // (row 0 | row 1 << 16), (row 2 | row 3 << 16)
-        const uint32_t h01 = pack_h2(ds[tt][0] * dsc[tt][0], ds[tt][1] * dsc[tt][1]);
-        const uint32_t h23 = pack_h2(ds[tt][2] * dsc[tt][2], ds[tt][3] * dsc[tt][3]);
+        uint32_t h01, l01, h23, l23;           // (row 0 | row 1 << 16), ...
+        split_bf2(ds[tt][0], ds[tt][1], h01, l01);
+        split_bf2(ds[tt][2], ds[tt][3], h23, l23);
         const uint32_t rh = __float_as_uint(dpp_mov<0xB1>(__uint_as_float(odd ? h01 : h23)));
+        const uint32_t rl = __float_as_uint(dpp_mov<0xB1>(__uint_as_float(odd ? l01 : l23)));
         const uint32_t ah = odd ? rh : h01, bh = odd ? h23 : rh;   // even key, odd key
+        const uint32_t al = odd ? rl : l01, bl = odd ? l23 : rl;
         uint8_t* row0 = dsT + (tt * 16 + 4 * g4 + 2 * (l16 & 1)) * DSP + 2 * pe;
         *reinterpret_cast<uint32_t*>(row0) = __builtin_amdgcn_perm(bh, ah, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(row0 + 128) = __builtin_amdgcn_perm(bl, al, 0x05040100u);
         *reinterpret_cast<uint32_t*>(row0 + DSP) = __builtin_amdgcn_perm(bh, ah, 0x07060302u);
+        *reinterpret_cast<uint32_t*>(row0 + DSP + 128) = __builtin_amdgcn_perm(bl, al, 0x07060302u);
         // row sums over the wave's 16 keys: halve the row set per exchange
         // (xor 1: even lanes keep rows 0, 1; xor 2: one row each), then add
         // the 4 lanes that hold the same row (rotations by 4 and 8)
@@ -608,10 +503,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ
 // dQ[t, h] = scale * sum over the selected blocks j of dS[t, h, j, :] K_j,
-// with dS as written by the dK/dV kernel (fp16 of dS times the row's power of
-// two dsscale: 2^-12 relative) and K as its exact fp16 copy (k / kmul); the
-// fp16 products are exact, accumulated in fp32, and the row is multiplied by
-// kmul / dsscale at the end.
+// with dS as written by the dK/dV kernel (bf16 hi + lo parts, so the product
+// is exact to ~2^-16).
 //
 // One workgroup = (b, kappa, a group of TPW <= 64 consecutive tokens): NCW
 // compute waves, each owning one 16-row tile (TPT tokens x G heads), plus two
@@ -619,7 +512,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 // the group's selections, in ascending order, into a ring of R LDS slots with
 // asynchronous global -> LDS copies (up to L blocks in flight each).  A compute
 // wave visits only the blocks its tile needs: it waits for the block's slot to
-// be filled, runs dQ^T += K^T dS^T on fp16 MFMA 16x16x32 (K^T read from the K
+// be filled, runs dQ^T += K^T dS^T on bf16 MFMA 16x16x32 (K^T read from the K
 // rows with transposing LDS reads, dS rows loaded from memory, zero rows for
 // tokens that did not select the block), and the dS rows of its next needed
 // block start loading right after.
@@ -738,7 +631,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   if (wv >= ncw) {
     // ================================================================ stager
     const int sg = wv - ncw;                                // 0 or 1
-    const uint16_t* kbase = a.kf16 + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
+    const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
     const int tokstride = a.Hkv * D;       // offsets inside one batch's K fit 32 bits
     int grow[MPS], gch[MPS];
 #pragma unroll
@@ -841,8 +734,8 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
     return nU;
   };
 
-  // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hkv * S + sl) * G + hh) * 64
-  const uint16_t* const dsq = a.dsbuf + rowbase * S * a.G * 64;
+  // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hkv * S + sl) * G + hh) * 128
+  const uint16_t* const dsq = a.dsbuf + rowbase * S * a.G * 128;
   const int HSG = a.Hkv * S;
   // dS rows of the tile for union block v (two blocks in flight).  Every
   // lane issues its loads, so the loads of one block never wait behind the
@@ -850,10 +743,10 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   // not select the block (or that has no row) reads at an offset past the
   // buffer, which returns zeros without a memory request.
   // bytes from this group's first row to the end of its last token's rows of kappa
-  const unsigned dsbytes = static_cast<unsigned>(((ntok - 1) * HSG + S) * G) * 128u;
+  const unsigned dsbytes = static_cast<unsigned>(((ntok - 1) * HSG + S) * G) * 256u;
   const auto dsr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dsq), 0,
                                                      static_cast<int>(dsbytes), kBufferWord3);
-  struct DsRows { uint4 f[2]; };
+  struct DsRows { uint4 h[2], l[2]; };
   auto load_ds = [&](int v, DsRows& r) __attribute__((always_inline)) {
     unsigned off = dsbytes;
     if (v < nU) {
@@ -863,11 +756,14 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
       if (valid && (bits[tl_row * NBW + jw] & jbit)) {
         const int rank = pcnt[tl_row * NBW + jw] + __popc(bits[tl_row * NBW + jw] & (jbit - 1u));
         const int sl = slot_of[tl_row * S + rank];
-        off = static_cast<unsigned>(((tl_row * HSG + sl) * G + hh) * 128 + 16 * g4);
+        off = static_cast<unsigned>(((tl_row * HSG + sl) * G + hh) * 256 + 16 * g4);
       }
     }
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) r.f[k2] = buffer_ld16(dsr, off + 64 * k2);
+    for (int k2 = 0; k2 < 2; ++k2) {
+      r.h[k2] = buffer_ld16(dsr, off + 64 * k2);
+      r.l[k2] = buffer_ld16(dsr, off + 128 + 64 * k2);
+    }
   };
 
   // K^T operand of dQ^T = K^T dS^T for d tile dt and 32-key step k2: lane
@@ -906,7 +802,8 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
         const uint2 lo = lds_read_tr16(tp + k2 * 32 * KROWB);
         const uint2 hi = lds_read_tr16(tp + (k2 * 32 + 16) * KROWB);
         const uint4 kta = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        dqa[dt] = mfma16x16x32h(kta, r.f[k2], dqa[dt]);
+        dqa[dt] = mfma16x16x32(kta, r.h[k2], dqa[dt]);
+        dqa[dt] = mfma16x16x32(kta, r.l[k2], dqa[dt]);
       }
     }
   };
@@ -949,14 +846,11 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
 
   if (l16 < TPT * G && tile * TPT + l16 / G < ntok) {
     const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + kv * G + hh;
-    // undo the fp16 scalings of dS (the row's dsscale) and of K (kmul): both
-    // powers of two
-    const float sc = a.scale * (a.kmul[static_cast<size_t>(b) * a.Hkv + kv] / a.dsscale[row]);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 pk;
-      pk.x = pack_bf2(dqa[dt][0] * sc, dqa[dt][1] * sc);
-      pk.y = pack_bf2(dqa[dt][2] * sc, dqa[dt][3] * sc);
+      pk.x = pack_bf2(dqa[dt][0] * a.scale, dqa[dt][1] * a.scale);
+      pk.y = pack_bf2(dqa[dt][2] * a.scale, dqa[dt][3] * a.scale);
       *reinterpret_cast<uint2*>(a.dq + row * D + dt * 16 + g4 * 4) = pk;
     }
   }
@@ -978,17 +872,8 @@ template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   const long nrows = static_cast<long>(p.B) * p.T * p.Hq;
   timing_mark(0, st);
-  const int nbk = p.B * p.Hkv;
-  hipLaunchKernelGGL((kv_amax_kernel<D>), dim3(kAmaxChunks, nbk), dim3(256), 0, st, p.k, p.v,
-                     p.amax_part, p.T, p.Hkv);
-  hipLaunchKernelGGL(kv_amax_final_kernel, dim3((nbk + 63) / 64), dim3(64), 0, st, p.amax_part,
-                     p.kmul, p.vamax, nbk);
-  const long krows = static_cast<long>(p.B) * p.T * p.Hkv;
-  hipLaunchKernelGGL((k_f16_kernel<D>), dim3((krows * (D / 8) + 255) / 256), dim3(256), 0, st,
-                     p.k, p.kf16, p.kmul, krows, p.T, p.Hkv);
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((nrows * 16 + 255) / 256), dim3(256), 0, st,
-                     p.o, p.o32, p.dout, p.delta, p.dsscale, p.vamax, nrows, p.T, p.Hq, p.Hkv,
-                     p.G);
+                     p.o, p.o32, p.dout, p.delta, nrows);
   const int NQB = p.NB;
   const unsigned nblk = static_cast<unsigned>(p.B) * p.Hkv * NQB;
   hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);

@@ -129,7 +129,7 @@ FwdWs fwd_ws_layout(const sas_dims* d) {
 }
 size_t fwd_ws(const sas_dims* d) { return fwd_ws_layout(d).total; }
 
-struct BwdWs { size_t delta, cnt2d, rowptr, entries, ds, dsscale, kf16, kmul, vamax, amax_part, total; };
+struct BwdWs { size_t delta, cnt2d, rowptr, entries, ds, total; };
 BwdWs bwd_ws(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
   const size_t S = d->topk + 1;
@@ -139,13 +139,8 @@ BwdWs bwd_ws(const sas_dims* d) {
   w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
   w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
   w.ds = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
-  // dS of every selected (token, head, slot): 64 keys, scaled fp16
-  w.dsscale = align_up(w.ds + 128 * static_cast<size_t>(d->B) * d->T * d->Hq * S);
-  w.kf16 = align_up(w.dsscale + sizeof(float) * static_cast<size_t>(d->B) * d->T * d->Hq);
-  w.kmul = align_up(w.kf16 + sizeof(uint16_t) * static_cast<size_t>(d->B) * d->T * d->Hkv * d->D);
-  w.vamax = align_up(w.kmul + sizeof(float) * d->B * d->Hkv);
-  w.amax_part = align_up(w.vamax + sizeof(float) * d->B * d->Hkv);
-  w.total = align_up(w.amax_part + sizeof(float) * 2 * sas::kAmaxChunks * d->B * d->Hkv);
+  // dS of every selected (token, head, slot): 64 keys x (hi, lo) bf16
+  w.total = align_up(w.ds + 256 * static_cast<size_t>(d->B) * d->T * d->Hq * S);
   return w;
 }
 
@@ -380,7 +375,7 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
   REQ_PTR(logg); REQ_PTR(dq); REQ_PTR(dk); REQ_PTR(dv); REQ_PTR(dlogg);
   if (o_f32 && !aligned16(o_f32)) return fail(SAS_ERR_INVALID, "pointer 'o_f32' is not 16-byte aligned");
   if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
-  if (64LL * d->Hq * (d->topk + 1) * 128 >= (1LL << 31))
+  if (64LL * d->Hq * (d->topk + 1) * 256 >= (1LL << 31))
     return fail(SAS_ERR_UNSUPPORTED, "Hq * (topk + 1) too large (64 tokens' dS rows must fit 2 GiB)");
   const BwdWs w = bwd_ws(d);
   if ((st = check_ws(ws, ws_bytes, w.total))) return st;
@@ -394,11 +389,6 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
   p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
   p.entries = reinterpret_cast<int32_t*>(base + w.entries);
   p.dsbuf = reinterpret_cast<uint16_t*>(base + w.ds);
-  p.dsscale = reinterpret_cast<float*>(base + w.dsscale);
-  p.kf16 = reinterpret_cast<uint16_t*>(base + w.kf16);
-  p.kmul = reinterpret_cast<float*>(base + w.kmul);
-  p.vamax = reinterpret_cast<float*>(base + w.vamax);
-  p.amax_part = reinterpret_cast<float*>(base + w.amax_part);
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
   p.TPT = 16 / p.G;

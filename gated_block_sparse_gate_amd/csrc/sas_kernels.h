@@ -124,8 +124,6 @@ struct FwdParams {
   float scale_log2;   // scale * log2(e)
 };
 
-constexpr int kAmaxChunks = 64;         // token chunks of the k / v maxima
-
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -145,16 +143,11 @@ struct BwdParams {
   int32_t* cnt2d;       // [B,Hkv,NQB,NB]  per (query block, key block) counts -> offsets
   int32_t* rowptr;      // [B,Hkv,NB+1]
   int32_t* entries;     // [B,Hkv,T*S] packed (t << 6) | slot
-  // [B,T,Hkv,S,G][64] fp16: dS of each selected (token, head, slot) times
-  // the row's dsscale, the 64 keys of the block in MFMA operand order
+  // [B,T,Hkv,S,G][hi 64 | lo 64] bf16: dS of each selected (token, head, slot)
+  // as bf16 hi + lo parts, the 64 keys of the block in MFMA operand order
   // (position 32 k2 + 8 g + e holds key 32 k2 + 4 g + e for e < 4, else
   // key 32 k2 + 16 + 4 g + e - 4)
   uint16_t* dsbuf;
-  float* dsscale;       // [B,T,Hq] power of two bringing the row's dS bound below 2^15
-  uint16_t* kf16;       // [B,T,Hkv,D] fp16 of k times 1 / kmul (exact)
-  float* kmul;          // [B,Hkv] power of two bringing max |k| below 2^15
-  float* vamax;         // [B,Hkv] max |v|
-  float* amax_part;     // [B,Hkv,kAmaxChunks,2] max |k|, max |v| per token chunk
   int B, T, Hq, Hkv, D, G, S, NB;
   int TPT, ntiles;
   float scale, scale_log2;

@@ -248,13 +248,9 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
  *   dq [B,T,Hq,D], dk, dv [B,T,Hkv,D] bf16 (fully overwritten, fp32
  *   accumulation); dlogg [B,T,Hkv,K+1] fp32.
  *   ws: sas_workspace_size(SAS_OP_BWD, d) bytes; it includes dS of every
- *   selected (token, head, slot) as fp16, 128 bytes each (B * T * Hq *
- *   (K+1) * 128 bytes: 4.3 GB at T = 32768, Hq = 32, K = 31), written by the
- *   dK/dV kernel and read by the dQ kernel.  Each row is stored times a
- *   power of two that keeps the a-priori bound 4 |dout| sqrt(D) max|v| of
- *   its |dS| below 2^15 (no overflow; 2^-12 relative rounding), and the dQ
- *   product uses an exact fp16 copy of k scaled by a power of two; dk, dv and
- *   dlogg use dS in fp32.
+ *   selected (token, head, slot) as bf16 hi + lo parts, 256 bytes each
+ *   (B * T * Hq * (K+1) * 256 bytes: 8.6 GB at T = 32768, Hq = 32, K = 31),
+ *   written by the dK/dV kernel and read by the dQ kernel.
  *   Deterministic (bitwise repeatable).
  */
 sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
