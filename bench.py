@@ -477,6 +477,43 @@ def main():
             cold.append(a0.elapsed_time(a1) * 1e3)
         cold.sort()
         cold_us = cold[len(cold) // 2]
+        # the same step over a paged cache: every (sequence, block) in its own
+        # page of a shuffled pool, through sas_decode_paged
+        NBd = xd["NBmax"]
+        npages = wd.B * NBd
+        gen = torch.Generator().manual_seed(args.seed + 11)
+        perm = torch.randperm(npages, generator=gen).to(torch.int32).view(wd.B, NBd).to(dev)
+        flat = perm.flatten().long()
+
+        def paged(c):
+            pool = torch.empty((npages, wd.Hkv, 64, wd.D), dtype=c.dtype, device=dev)
+            pool[flat] = c.view(wd.B, wd.Hkv, NBd, 64, wd.D).permute(0, 2, 1, 3, 4).reshape(
+                npages, wd.Hkv, 64, wd.D)
+            return pool
+
+        kpool, vpool = paged(xd["k_cache"]), paged(xd["v_cache"])
+        gpool = torch.empty((npages, wd.Hkv, wd.dg), dtype=torch.float32, device=dev)
+        gpool[flat] = xd["kg_cache"].permute(0, 2, 1, 3).reshape(npages, wd.Hkv, wd.dg)
+
+        def dstep_paged():
+            sas.decode_paged(xd["q"], xd["q_gate"], kpool, vpool, gpool, perm, xd["ctx_len"], Kd,
+                             scd, apply_gate=True, want_idx=False, workspace=ws_d,
+                             out=(od, None, None))
+
+        for _ in range(3):
+            dstep_paged()
+        cold_p = []
+        for _ in range(args.decode_steps):
+            flush.sum()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            dstep_paged()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            cold_p.append(a0.elapsed_time(a1) * 1e3)
+        cold_p.sort()
+        cold_paged_us = cold_p[len(cold_p) // 2]
+        del kpool, vpool, gpool
         lens = xd["ctx_len"].cpu().tolist()
         kvb, gkb, smb = decode_bytes(lens, wd.Hkv, wd.D, wd.dg, Kd, wd.G)
         tot = kvb + gkb + smb
@@ -486,6 +523,7 @@ def main():
             "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D, "dg": wd.dg,
             "budget": 64 * (Kd + 1), "ctx_len_range": [wd.Lmin, wd.Lmax],
             "us_per_step_cold": round(cold_us, 2), "us_per_step_warm": round(warm_us, 2),
+            "us_per_step_cold_paged": round(cold_paged_us, 2),
             "algorithmic_bytes": tot, "kv_bytes": kvb, "gate_key_bytes": gkb,
             "GBps_cold": round(tot / (cold_us * 1e-6) / 1e9, 1),
             "KV_GBps_cold": round(kvb / (cold_us * 1e-6) / 1e9, 1),

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "Dims", "DecodeDims", "SasError", "load_library", "version", "workspace_size",
     "decode_workspace_size", "gate_score", "topk_blocks", "sparse_attn_fwd",
-    "sparse_attn_bwd", "decode", "budget_to_topk", "EXPORTED_SYMBOLS", "set_timing_events",
+    "sparse_attn_bwd", "decode", "decode_paged", "budget_to_topk", "EXPORTED_SYMBOLS",
+    "set_timing_events",
     "take_device_fault", "gate_score_bwd",
 ]
 
@@ -33,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
     "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
     "sas_decode", "sas_set_timing_events", "sas_take_device_fault", "sas_gate_score_bwd",
+    "sas_decode_paged",
 )
 
 
@@ -84,10 +86,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         + [P, S, P])
     lib.sas_decode.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 6 + [F32] + [P] * 3
                                + [P, S, P])
+    lib.sas_decode_paged.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 5 + [I32] + [P] * 2
+                                     + [F32] + [P] * 3 + [P, S, P])
     lib.sas_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     lib.sas_take_device_fault.argtypes = [ctypes.POINTER(ctypes.c_uint)]
     for fn in ("sas_gate_score", "sas_gate_score_bwd", "sas_topk_blocks", "sas_sparse_attn_fwd",
-               "sas_sparse_attn_bwd", "sas_decode", "sas_set_timing_events",
+               "sas_sparse_attn_bwd", "sas_decode", "sas_decode_paged", "sas_set_timing_events",
                "sas_take_device_fault"):
         getattr(lib, fn).restype = I32
     _lib = lib
@@ -376,4 +380,45 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int, scale: flo
     _check(lib.sas_decode(ctypes.byref(d), _ptr(q), _ptr(q_gate), _ptr(k_cache), _ptr(v_cache),
                           _ptr(kg_cache), _ptr(ctx_len), ctypes.c_float(scale), _ptr(o), _ptr(idx),
                           _ptr(logg), _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev)))
+    return o, idx, logg
+
+
+def decode_paged(q, q_gate, k_pages, v_pages, kg_pages, block_table, ctx_len, topk: int,
+                 scale: float | None = None, apply_gate: bool = True, want_idx: bool = True,
+                 workspace=None, out=None):
+    """decode() over a paged KV cache: k_pages, v_pages [P,Hkv,64,D] bf16,
+    kg_pages [P,Hkv,dg] fp32, block_table [B,NBmax] int32 (page of each block).
+    Returns (o, idx or None, logg or None) as decode()."""
+    lib = load_library()
+    dev = _device_of(q)
+    B, Hq, D = q.shape
+    P, Hkv, blk, _ = k_pages.shape
+    if blk != 64:
+        raise ValueError("pages hold 64-token blocks")
+    dg = q_gate.shape[-1]
+    NBmax = block_table.shape[1]
+    Lmax = 64 * NBmax
+    S = topk + 1
+    _req(q, "q", torch.bfloat16, (B, Hq, D), dev)
+    _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
+    _req(k_pages, "k_pages", torch.bfloat16, (P, Hkv, 64, D), dev)
+    _req(v_pages, "v_pages", torch.bfloat16, (P, Hkv, 64, D), dev)
+    _req(kg_pages, "kg_pages", torch.float32, (P, Hkv, dg), dev)
+    _req(block_table, "block_table", torch.int32, (B, NBmax), dev)
+    _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0)
+    if out is None:
+        o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev) if want_idx else None
+        logg = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev) if want_idx else None
+    else:
+        o, idx, logg = out
+    nws = decode_workspace_size(d)
+    ws = workspace if workspace is not None else _ws(nws, dev)
+    _check(lib.sas_decode_paged(ctypes.byref(d), _ptr(q), _ptr(q_gate), _ptr(k_pages),
+                                _ptr(v_pages), _ptr(kg_pages), ctypes.c_int32(P),
+                                _ptr(block_table), _ptr(ctx_len), ctypes.c_float(scale), _ptr(o),
+                                _ptr(idx), _ptr(logg), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(dev)))
     return o, idx, logg

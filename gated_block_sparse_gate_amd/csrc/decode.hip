@@ -46,17 +46,26 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeParams p) {
   const int j0 = chunk * 32 * NPASS;
   if (j0 >= ncand) return;
   const int sub = tid & (LPC - 1), cl = tid / LPC;    // 32 candidates per pass
+  const int kv = unit - b * p.Hkv;
   const float* kgb = p.kg_cache + static_cast<size_t>(unit) * p.NBmax * DG;
   const float* qgp = p.q_gate + static_cast<size_t>(unit) * DG;
+  // candidate j's gate key: row j of the unit's cache, or (paged) the key of
+  // the block's page (a page outside the pool reads as zeros)
+  auto key_row = [&](int j) -> const float* {
+    if (j >= ncand) return nullptr;
+    if (!p.btab) return kgb + static_cast<size_t>(j) * DG;
+    const int pg = p.btab[static_cast<size_t>(b) * p.NBmax + j];
+    return (pg >= 0 && pg < p.num_pages) ? p.kg_cache + (static_cast<size_t>(pg) * p.Hkv + kv) * DG
+                                         : nullptr;
+  };
   float4 qv[F4], kvv[NPASS][F4];
 #pragma unroll
   for (int pss = 0; pss < NPASS; ++pss) {
-    const int j = j0 + pss * 32 + cl;
+    const float* kr = key_row(j0 + pss * 32 + cl);
 #pragma unroll
     for (int f = 0; f < F4; ++f)
-      kvv[pss][f] = (j < ncand) ? *reinterpret_cast<const float4*>(
-                                      kgb + static_cast<size_t>(j) * DG + (f * LPC + sub) * 4)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      kvv[pss][f] = kr ? *reinterpret_cast<const float4*>(kr + (f * LPC + sub) * 4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int f = 0; f < F4; ++f) qv[f] = *reinterpret_cast<const float4*>(qgp + (f * LPC + sub) * 4);
@@ -298,10 +307,12 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit, in
 // The walk is software-pipelined over two register buffers: the next pass's
 // K and V loads (64 KiB per workgroup) are in flight while the current pass
 // computes; its V rows go through a per-wave LDS region (no workgroup
-// barrier).  The softmax state is carried online across the passes.  K and V
-// are read through buffer resources that end at the context length, so keys
-// at or beyond it, slots without a block and passes past the split's end
-// read zeros and make no memory request.  The per-wave (max, sum, O) are
+// barrier).  The softmax state is carried online across the passes.  Each
+// block is read through a buffer resource over its rows below the context
+// length (rows 64 j.. of the contiguous cache, or the block's page of a paged
+// cache), so keys at or beyond it, slots without a block, pages outside the
+// pool and passes past the split's end read zeros and make no memory
+// request.  The per-wave (max, sum, O) are
 // merged across the 4 waves in LDS, each wave's in place of its own V rows;
 // with one split per unit the workgroup writes the normalised output,
 // otherwise one partial per split (whole 128-byte lines) for the merge.
@@ -336,14 +347,19 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
   const int spw = p.spw, npass = spw / 2;
   const int s0 = split * spw;
 
-  // slot table: lane i < spw holds slot s0 + i (block, log2-domain gate bias)
-  int jv = -1;
+  // slot table: lane i < spw holds slot s0 + i (block, log2-domain gate
+  // bias, and for a paged cache the block's page, -1 outside the pool)
+  int jv = -1, pgv = -1;
   float lv = 0.f;
   if (lane < spw) {
     const int s = s0 + lane;
     const int j = (ok && s < p.S) ? p.ws_idx[static_cast<size_t>(unit) * p.S + s] : -1;
     jv = (j >= 0 && 64 * j < L) ? j : -1;
     lv = (jv >= 0 && p.apply_gate) ? p.ws_logg[static_cast<size_t>(unit) * p.S + s] * kLog2e : 0.f;
+    if (p.btab && jv >= 0) {
+      const int pg = p.btab[static_cast<size_t>(b) * p.NBmax + jv];
+      pgv = (pg >= 0 && pg < p.num_pages) ? pg : -1;
+    }
   }
   auto slot_j = [&](int t) { return t < spw ? __builtin_amdgcn_readlane(jv, t) : -1; };
   auto slot_lg = [&](int t) {
@@ -361,29 +377,41 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
       qb[ks] = (r < G) ? v : make_uint4(0, 0, 0, 0);
     }
   }
+  // slot t's block of K (or V) as a buffer resource over its rows below the
+  // context length: contiguous cache rows 64 j.., or the block's page; no
+  // rows for a slot without a block or a page outside the pool
   const size_t ubase = (static_cast<size_t>(b) * p.Hkv + kv) * p.Lmax * D;
-  const unsigned rec = ok ? static_cast<unsigned>(L) * ROWB : 0u;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k_cache + ubase), 0, rec, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v_cache + ubase), 0, rec, kBufferWord3);
+  auto block_rsrc = [&](const uint16_t* cache, int t) {
+    const int j = slot_j(t);
+    size_t off;
+    int rows;
+    if (p.btab) {
+      const int pg = t < spw ? __builtin_amdgcn_readlane(pgv, t) : -1;
+      off = (static_cast<size_t>(max(pg, 0)) * p.Hkv + kv) * 64 * D;
+      rows = (j >= 0 && pg >= 0) ? min(64, L - 64 * j) : 0;
+    } else {
+      off = ubase + static_cast<size_t>(max(j, 0)) * 64 * D;
+      rows = j >= 0 ? min(64, L - 64 * j) : 0;
+    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(cache + off), 0, rows * ROWB,
+                                             kBufferWord3);
+  };
   // V rows of a pass: wave row 16 u + i = key 16 w + i of block u, lane's
   // 16-byte chunk stored at its swizzled place
   const int vrow = lane / CPR;
   auto issue = [&](PassBuf& pb, int ps) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int j = slot_j(2 * ps + u);
-      const unsigned krow = static_cast<unsigned>(64 * j + 16 * w + r);
+      const __amdgpu_buffer_rsrc_t krs = block_rsrc(p.k_cache, 2 * ps + u);
+      const __amdgpu_buffer_rsrc_t vrs = block_rsrc(p.v_cache, 2 * ps + u);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        pb.k[u][ks] = buffer_ld16(krs, j >= 0 ? krow * ROWB + 64 * ks + 16 * g : rec);
+        pb.k[u][ks] = buffer_ld16(krs, (16 * w + r) * ROWB + 64 * ks + 16 * g);
 #pragma unroll
       for (int n = 0; n < NVT; ++n) {
         const int rho = 16 * u + RPI * n + vrow;
         const int c = (lane % CPR) ^ lds_swz<ROWB>(rho);
-        const unsigned vr = static_cast<unsigned>(64 * j + 16 * w + RPI * n + vrow);
-        pb.v[u][n] = buffer_ld16(vrs, j >= 0 ? vr * ROWB + 16 * c : rec);
+        pb.v[u][n] = buffer_ld16(vrs, (16 * w + RPI * n + vrow) * ROWB + 16 * c);
       }
     }
   };

@@ -431,4 +431,39 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
   return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)), "sas_decode launch");
 }
 
+sas_status sas_decode_paged(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                            const uint16_t* k_pages, const uint16_t* v_pages,
+                            const float* kg_pages, int32_t num_pages,
+                            const int32_t* block_table, const int32_t* ctx_len, float scale,
+                            uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  sas_status st = check_decode_dims(d);
+  if (st) return st;
+  REQ_PTR(q); REQ_PTR(q_gate); REQ_PTR(k_pages); REQ_PTR(v_pages); REQ_PTR(kg_pages);
+  REQ_PTR(block_table); REQ_PTR(ctx_len); REQ_PTR(o);
+  if (num_pages < 1) return fail(SAS_ERR_INVALID, "num_pages must be positive (got %d)", num_pages);
+  if (idx_out && !aligned16(idx_out)) return fail(SAS_ERR_INVALID, "idx_out is not 16-byte aligned");
+  if (logg_out && !aligned16(logg_out))
+    return fail(SAS_ERR_INVALID, "logg_out is not 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
+  const DecWs w = dec_ws(d);
+  if ((st = check_ws(ws, ws_bytes, w.total))) return st;
+  char* base = static_cast<char*>(ws);
+  sas::DecodeParams p{};
+  p.q = q; p.q_gate = q_gate; p.k_cache = k_pages; p.v_cache = v_pages; p.kg_cache = kg_pages;
+  p.btab = block_table; p.num_pages = num_pages;
+  p.ctx_len = ctx_len; p.o = o; p.idx_out = idx_out; p.logg_out = logg_out;
+  p.ws_idx = reinterpret_cast<int32_t*>(base + w.idx);
+  p.ws_logg = reinterpret_cast<float*>(base + w.logg);
+  p.ws_part = reinterpret_cast<float*>(base + w.part);
+  p.ws_score = reinterpret_cast<float*>(base + w.score);
+  p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
+  p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
+  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw;
+  p.scale_log2 = scale * sas::kLog2e;
+  g_err.clear();
+  return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)),
+                    "sas_decode_paged launch");
+}
+
 }  // extern "C"

@@ -158,7 +158,9 @@ struct DecodeParams {
   const float* q_gate;      // [B,Hkv,dg]
   const uint16_t* k_cache;  // [B,Hkv,Lmax,D]
   const uint16_t* v_cache;
-  const float* kg_cache;    // [B,Hkv,NBmax,dg]
+  const float* kg_cache;    // [B,Hkv,NBmax,dg]; paged: k/v [P,Hkv,64,D], kg [P,Hkv,dg]
+  const int32_t* btab;      // paged: [B,NBmax] page of each block, else null
+  int num_pages;
   const int32_t* ctx_len;   // [B]
   uint16_t* o;              // [B,Hq,D]
   int32_t* idx_out;         // [B,Hkv,S] or null

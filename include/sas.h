@@ -286,6 +286,31 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
                       uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
                       size_t ws_bytes, void* stream);
 
+/*
+ * sas_decode over a paged KV cache: a serving backend keeps each sequence's
+ * 64-token blocks in pages of a shared pool (the model card's decode runs a
+ * batch of sequences of different lengths; a page is one KV block, so a
+ * selected block is one page read).  Same computation and outputs as
+ * sas_decode; only where block j of sequence b lives differs.
+ *
+ *   k_pages, v_pages [num_pages, Hkv, 64, D] bf16: page p holds one block's
+ *   64 keys / values of every KV head (16 KiB contiguous per head at D = 128);
+ *   kg_pages [num_pages, Hkv, dg] fp32: the block's gate key (for a
+ *   sequence's current block, its causal prefix key);
+ *   block_table [B, NBmax] int32 (device): page of block j of sequence b for
+ *   j <= (ctx_len[b] - 1) / 64; later entries are not read.  A page outside
+ *   [0, num_pages) reads as zeros (gate score 0, zero keys and values): the
+ *   result is then meaningless but nothing outside the pool is touched.
+ *   d->Lmax bounds ctx_len (NBmax = ceil(Lmax / 64) table columns); other
+ *   arguments as in sas_decode.  ws: sas_decode_workspace_size(d) bytes.
+ */
+sas_status sas_decode_paged(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                            const uint16_t* k_pages, const uint16_t* v_pages,
+                            const float* kg_pages, int32_t num_pages,
+                            const int32_t* block_table, const int32_t* ctx_len, float scale,
+                            uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
+                            size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -311,6 +311,53 @@ def test_decode(case, apply_gate):
     assert_close("o", o, ref["o"])
 
 
+@pytest.mark.parametrize("case", DEC_CASES, ids=[f"dec{i}" for i in range(len(DEC_CASES))])
+def test_decode_paged(case):
+    """Paged cache: every (sequence, block) in its own page of a shuffled pool
+    (spare pages and every page row past a context filled with NaN, table
+    entries past a sequence's blocks pointing outside the pool): the same
+    arithmetic in the same order as the contiguous cache, so the outputs
+    must be bitwise equal to sas_decode's (which the oracle pins above)."""
+    B, Hq, Hkv, D, dg, K, Lmax, lens = case
+    w = synth.Workload("dec", 91, B=B, T=1, Hq=Hq, Hkv=Hkv, D=D, dg=dg, topk=K, kind="decode",
+                       Lmin=1, Lmax=Lmax)
+    x = synth.decode_inputs(w, seed=1, device="cuda", ctx_len=torch.tensor(lens, dtype=torch.int32))
+    sc = 1.0 / math.sqrt(D)
+    o_c, idx_c, lg_c = sas.decode(x["q"], x["q_gate"], x["k_cache"], x["v_cache"], x["kg_cache"],
+                                  x["ctx_len"], K, sc)
+    NB = -(-Lmax // 64)
+    npages = B * NB + 5
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(npages)[:B * NB].astype(np.int32))
+    perm = perm.view(B, NB).cuda()
+    nan = float("nan")
+    kp = torch.full((npages, Hkv, 64, D), nan, dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, nan)
+    gp = torch.full((npages, Hkv, dg), nan, dtype=torch.float32, device="cuda")
+    # rows at or past each context length stay NaN in the pages
+    tok = torch.arange(NB * 64, device="cuda")
+    live = (tok[None, :] < x["ctx_len"][:, None].long()).view(B, 1, NB * 64, 1)
+
+    def blocks(c):
+        pad = torch.full((B, Hkv, NB * 64, D), nan, dtype=c.dtype, device="cuda")
+        pad[:, :, :c.shape[2]] = c
+        pad = torch.where(live, pad, torch.full_like(pad, nan))
+        return pad.view(B, Hkv, NB, 64, D).permute(0, 2, 1, 3, 4).reshape(B * NB, Hkv, 64, D)
+
+    flat = perm.flatten().long()
+    kp[flat] = blocks(x["k_cache"])
+    vp[flat] = blocks(x["v_cache"])
+    gp[flat] = x["kg_cache"].permute(0, 2, 1, 3).reshape(B * NB, Hkv, dg)
+    nblk = (x["ctx_len"].long() - 1) // 64 + 1
+    table = torch.where(torch.arange(NB, device="cuda")[None, :] < nblk[:, None], perm,
+                        torch.full_like(perm, npages + 3))
+    o_p, idx_p, lg_p = sas.decode_paged(x["q"], x["q_gate"], kp, vp, gp, table.contiguous(),
+                                        x["ctx_len"], K, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_c)
+    assert torch.equal(lg_p.nan_to_num(), lg_c.nan_to_num())
+    assert torch.equal(o_p.view(torch.int16), o_c.view(torch.int16))
+
+
 def test_decode_matches_prefill_row():
     """Decode of token L-1 equals the prefill row L-1 computed by the library."""
     w = CASES[1]
