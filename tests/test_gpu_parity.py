@@ -280,6 +280,10 @@ DEC_CASES = [
     (2, 10, 2, 64, 32, 3, 700, [700, 300]),
     # beyond 1,024 blocks (the selection's long-context path); one visible key
     (2, 2, 1, 64, 32, 5, 70000, [70000, 4161]),
+    # budgets 1,024 and 4,096 (K = 15, 63; at K = 63 more than 64 keys pass
+    # the lane-maximum bound, so the selection searches all keys)
+    (4, 8, 2, 128, 128, 15, 9000, [9000, 1100, 64, 4097]),
+    (3, 8, 2, 128, 128, 63, 20000, [20000, 4100, 12000]),
     # 512 units: one workgroup walks all of a unit's slots and writes the
     # output (no split partials); an odd number of two-block passes, one-token
     # and partial current blocks, contexts shorter than the budget
