@@ -514,6 +514,28 @@ def main():
         cold_p.sort()
         cold_paged_us = cold_p[len(cold_p) // 2]
         del kpool, vpool, gpool
+        # the contiguous step with the gate-key cache in bf16 (kg_dtype = 1)
+        kg16 = xd["kg_cache"].to(torch.bfloat16)
+
+        def dstep_kg16():
+            sas.decode(xd["q"], xd["q_gate"], xd["k_cache"], xd["v_cache"], kg16, xd["ctx_len"],
+                       Kd, scd, apply_gate=True, want_idx=False, workspace=ws_d,
+                       out=(od, None, None))
+
+        for _ in range(3):
+            dstep_kg16()
+        cold_b = []
+        for _ in range(args.decode_steps):
+            flush.sum()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            dstep_kg16()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            cold_b.append(a0.elapsed_time(a1) * 1e3)
+        cold_b.sort()
+        cold_kg16_us = cold_b[len(cold_b) // 2]
+        del kg16
         lens = xd["ctx_len"].cpu().tolist()
         kvb, gkb, smb = decode_bytes(lens, wd.Hkv, wd.D, wd.dg, Kd, wd.G)
         tot = kvb + gkb + smb
@@ -524,6 +546,7 @@ def main():
             "budget": 64 * (Kd + 1), "ctx_len_range": [wd.Lmin, wd.Lmax],
             "us_per_step_cold": round(cold_us, 2), "us_per_step_warm": round(warm_us, 2),
             "us_per_step_cold_paged": round(cold_paged_us, 2),
+            "us_per_step_cold_kg_bf16": round(cold_kg16_us, 2),
             "algorithmic_bytes": tot, "kv_bytes": kvb, "gate_key_bytes": gkb,
             "GBps_cold": round(tot / (cold_us * 1e-6) / 1e9, 1),
             "KV_GBps_cold": round(kvb / (cold_us * 1e-6) / 1e9, 1),

@@ -56,7 +56,7 @@ class DecodeDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("dg", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("Lmax", ctypes.c_int32), ("NBmax", ctypes.c_int32),
-                ("apply_gate", ctypes.c_int32)]
+                ("apply_gate", ctypes.c_int32), ("kg_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -365,10 +365,13 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int, scale: flo
     _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
     _req(k_cache, "k_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
     _req(v_cache, "v_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
-    _req(kg_cache, "kg_cache", torch.float32, (B, Hkv, NBmax, dg), dev)
+    kg_bf16 = kg_cache.dtype == torch.bfloat16
+    _req(kg_cache, "kg_cache", torch.bfloat16 if kg_bf16 else torch.float32, (B, Hkv, NBmax, dg),
+         dev)
     _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0)
+    d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0,
+                   1 if kg_bf16 else 0)
     if out is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
         idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev) if want_idx else None
@@ -403,11 +406,13 @@ def decode_paged(q, q_gate, k_pages, v_pages, kg_pages, block_table, ctx_len, to
     _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
     _req(k_pages, "k_pages", torch.bfloat16, (P, Hkv, 64, D), dev)
     _req(v_pages, "v_pages", torch.bfloat16, (P, Hkv, 64, D), dev)
-    _req(kg_pages, "kg_pages", torch.float32, (P, Hkv, dg), dev)
+    kg_bf16 = kg_pages.dtype == torch.bfloat16
+    _req(kg_pages, "kg_pages", torch.bfloat16 if kg_bf16 else torch.float32, (P, Hkv, dg), dev)
     _req(block_table, "block_table", torch.int32, (B, NBmax), dev)
     _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0)
+    d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0,
+                   1 if kg_bf16 else 0)
     if out is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
         idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev) if want_idx else None

@@ -4,7 +4,7 @@
 //
 // Unit = (sequence b, KV head kappa), L = ctx_len[b], c = (L-1)/64:
 //   score : s_j = q_gate . kg_cache[j] / sqrt(dg), j = 0..c (chunks of 128
-//           candidates per workgroup);
+//           candidates per workgroup; gate keys fp32 or bf16);
 //   top-k : log-sum-exp; the min(K, c) best historical blocks (ties ->
 //           lower j) + block c (one wave per unit).
 //   attend: the G query heads attend to the selected blocks' keys tau < L
@@ -32,7 +32,7 @@ constexpr int kDecodeWorkgroups = 512;
 // threads, 8 lanes per candidate; all of the chunk's gate-key loads are issued
 // before any arithmetic.  s_j = q_gate . kg_cache[j] / sqrt(dg) for j <= c
 // goes to the workspace.
-template <int DG>
+template <int DG, bool BF>
 __global__ __launch_bounds__(256) void decode_score_kernel(DecodeParams p) {
   constexpr int LPC = 8;                 // lanes per candidate
   constexpr int F4 = DG / 4 / LPC;       // float4 per lane per candidate
@@ -47,25 +47,33 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeParams p) {
   if (j0 >= ncand) return;
   const int sub = tid & (LPC - 1), cl = tid / LPC;    // 32 candidates per pass
   const int kv = unit - b * p.Hkv;
-  const float* kgb = p.kg_cache + static_cast<size_t>(unit) * p.NBmax * DG;
   const float* qgp = p.q_gate + static_cast<size_t>(unit) * DG;
-  // candidate j's gate key: row j of the unit's cache, or (paged) the key of
-  // the block's page (a page outside the pool reads as zeros)
-  auto key_row = [&](int j) -> const float* {
-    if (j >= ncand) return nullptr;
-    if (!p.btab) return kgb + static_cast<size_t>(j) * DG;
+  // element index of candidate j's gate key: row j of the unit's cache, or
+  // (paged) the key of the block's page; -1 past the candidates or for a page
+  // outside the pool (reads as zeros)
+  auto key_row = [&](int j) -> long {
+    if (j >= ncand) return -1;
+    if (!p.btab) return (static_cast<long>(unit) * p.NBmax + j) * DG;
     const int pg = p.btab[static_cast<size_t>(b) * p.NBmax + j];
-    return (pg >= 0 && pg < p.num_pages) ? p.kg_cache + (static_cast<size_t>(pg) * p.Hkv + kv) * DG
-                                         : nullptr;
+    return (pg >= 0 && pg < p.num_pages) ? (static_cast<long>(pg) * p.Hkv + kv) * DG : -1;
+  };
+  // 4 consecutive key elements (fp32, or bf16 widened exactly)
+  auto load4 = [&](long e) -> float4 {
+    if constexpr (BF) {
+      const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.kg_cache) + e);
+      return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                         __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    } else {
+      return *reinterpret_cast<const float4*>(p.kg_cache + e);
+    }
   };
   float4 qv[F4], kvv[NPASS][F4];
 #pragma unroll
   for (int pss = 0; pss < NPASS; ++pss) {
-    const float* kr = key_row(j0 + pss * 32 + cl);
+    const long kr = key_row(j0 + pss * 32 + cl);
 #pragma unroll
     for (int f = 0; f < F4; ++f)
-      kvv[pss][f] = kr ? *reinterpret_cast<const float4*>(kr + (f * LPC + sub) * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      kvv[pss][f] = kr >= 0 ? load4(kr + (f * LPC + sub) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int f = 0; f < F4; ++f) qv[f] = *reinterpret_cast<const float4*>(qgp + (f * LPC + sub) * 4);
@@ -581,10 +589,17 @@ void decode_split(int S, int units, int* nsplit, int* spw) {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st) {
   const unsigned units = static_cast<unsigned>(p.B) * p.Hkv;
   const dim3 sgrid(units, (p.NBmax + 127) / 128);
+  auto score = [&](auto dgc) {
+    constexpr int DG = decltype(dgc)::value;
+    if (p.kg_bf16)
+      hipLaunchKernelGGL((decode_score_kernel<DG, true>), sgrid, dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((decode_score_kernel<DG, false>), sgrid, dim3(256), 0, st, p);
+  };
   switch (p.dg) {
-    case 128: hipLaunchKernelGGL((decode_score_kernel<128>), sgrid, dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((decode_score_kernel<64>), sgrid, dim3(256), 0, st, p); break;
-    case 32: hipLaunchKernelGGL((decode_score_kernel<32>), sgrid, dim3(256), 0, st, p); break;
+    case 128: score(std::integral_constant<int, 128>{}); break;
+    case 64: score(std::integral_constant<int, 64>{}); break;
+    case 32: score(std::integral_constant<int, 32>{}); break;
     default: return hipErrorInvalidValue;
   }
   if (p.NBmax <= kMaxNB)

@@ -190,6 +190,8 @@ sas_status check_decode_dims(const sas_decode_dims* d) {
     return fail(SAS_ERR_UNSUPPORTED, "Lmax must be <= %d", sas::kMaxDecodeNB * 64);
   if (d->apply_gate != 0 && d->apply_gate != 1)
     return fail(SAS_ERR_INVALID, "apply_gate must be 0 or 1");
+  if (d->kg_dtype != 0 && d->kg_dtype != 1)
+    return fail(SAS_ERR_INVALID, "kg_dtype must be 0 (fp32) or 1 (bf16)");
   return SAS_OK;
 }
 
@@ -425,7 +427,7 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
   p.ws_score = reinterpret_cast<float*>(base + w.score);
   p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
   p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
-  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw;
+  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw; p.kg_bf16 = d->kg_dtype;
   p.scale_log2 = scale * sas::kLog2e;
   g_err.clear();
   return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)), "sas_decode launch");
@@ -459,7 +461,7 @@ sas_status sas_decode_paged(const sas_decode_dims* d, const uint16_t* q, const f
   p.ws_score = reinterpret_cast<float*>(base + w.score);
   p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
   p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
-  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw;
+  p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw; p.kg_bf16 = d->kg_dtype;
   p.scale_log2 = scale * sas::kLog2e;
   g_err.clear();
   return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)),

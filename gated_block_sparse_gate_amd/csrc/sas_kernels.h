@@ -172,6 +172,7 @@ struct DecodeParams {
   float* ws_score;          // [B,Hkv,NBmax] gate logits of the candidate blocks
   int B, Hq, Hkv, D, dg, G, K, S, Lmax, NBmax, apply_gate;
   int nsplit, spw;          // attention splits per unit, slots per split
+  int kg_bf16;              // gate keys stored as bf16 (else fp32)
   float scale_log2;
 };
 

@@ -81,10 +81,12 @@ typedef struct {
  * Decode dimensions.  B sequences with one new token each; KV cache holds up
  * to Lmax tokens per sequence, the gate-key cache NBmax = ceil(Lmax/64)
  * blocks.  apply_gate = 1 adds log g to the logits (same function as
- * training); 0 = selection only, no gate bias.
+ * training); 0 = selection only, no gate bias.  kg_dtype: element type of
+ * the gate-key cache, 0 = fp32, 1 = bf16 (half the bytes of the scoring
+ * step; the scores are the same fp32 dot products of the bf16 values).
  */
 typedef struct {
-  int32_t B, Hq, Hkv, D, dg, block, topk, Lmax, NBmax, apply_gate;
+  int32_t B, Hq, Hkv, D, dg, block, topk, Lmax, NBmax, apply_gate, kg_dtype;
 } sas_decode_dims;
 
 /* Library version (SAS_VERSION). */
@@ -274,7 +276,8 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
  *
  *   q [B,Hq,D] bf16;  q_gate [B,Hkv,dg] fp32;
  *   k_cache, v_cache [B,Hkv,Lmax,D] bf16 (head-major contiguous cache);
- *   kg_cache [B,Hkv,NBmax,dg] fp32;  ctx_len [B] int32 (device);
+ *   kg_cache [B,Hkv,NBmax,dg] fp32 (bf16 with kg_dtype = 1);  ctx_len [B]
+ *   int32 (device);
  *   o [B,Hq,D] bf16 output;  idx_out [B,Hkv,K+1] int32 and logg_out
  *   [B,Hkv,K+1] fp32 outputs (either may be NULL).
  *   A sequence with ctx_len outside [1, Lmax] gets o = NaN, idx = -1.
@@ -295,8 +298,8 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
  *
  *   k_pages, v_pages [num_pages, Hkv, 64, D] bf16: page p holds one block's
  *   64 keys / values of every KV head (16 KiB contiguous per head at D = 128);
- *   kg_pages [num_pages, Hkv, dg] fp32: the block's gate key (for a
- *   sequence's current block, its causal prefix key);
+ *   kg_pages [num_pages, Hkv, dg] fp32 (bf16 with kg_dtype = 1): the
+ *   block's gate key (for a sequence's current block, its causal prefix key);
  *   block_table [B, NBmax] int32 (device): page of block j of sequence b for
  *   j <= (ctx_len[b] - 1) / 64; later entries are not read.  A page outside
  *   [0, num_pages) reads as zeros (gate score 0, zero keys and values): the

@@ -315,6 +315,29 @@ def test_decode(case, apply_gate):
     assert_close("o", o, ref["o"])
 
 
+@pytest.mark.parametrize("case", [DEC_CASES[i] for i in (0, 1, 3, 4)], ids=["dec0", "dec1", "dec3", "dec4"])
+def test_decode_bf16_gate_keys(case):
+    """Gate-key cache in bf16 (kg_dtype = 1): the oracle scores the same
+    bf16 values; selection bit-exact outside near ties, as with fp32 keys."""
+    B, Hq, Hkv, D, dg, K, Lmax, lens = case
+    w = synth.Workload("dec", 91, B=B, T=1, Hq=Hq, Hkv=Hkv, D=D, dg=dg, topk=K, kind="decode",
+                       Lmin=1, Lmax=Lmax)
+    x = synth.decode_inputs(w, seed=2, device="cpu", ctx_len=torch.tensor(lens, dtype=torch.int32))
+    kg16 = x["kg_cache"].to(torch.bfloat16)
+    sc = 1.0 / math.sqrt(D)
+    ref = O.decode(x["q"], x["q_gate"], x["k_cache"], x["v_cache"], kg16.float(), x["ctx_len"], K,
+                   sc)
+    dev = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in x.items()}
+    o, idx, logg = sas.decode(dev["q"], dev["q_gate"], dev["k_cache"], dev["v_cache"], kg16.cuda(),
+                              dev["ctx_len"], K, sc)
+    torch.cuda.synchronize()
+    ok = ~ref["near_tie"]
+    np.testing.assert_array_equal(idx.cpu().numpy()[ok], ref["idx"][ok])
+    fin = np.isfinite(ref["logg"]) & ok[..., None]
+    assert np.abs(logg.cpu().numpy()[fin] - ref["logg"][fin]).max() < ROUTER_ABS
+    assert_close("o", o, ref["o"])
+
+
 @pytest.mark.parametrize("case", DEC_CASES, ids=[f"dec{i}" for i in range(len(DEC_CASES))])
 def test_decode_paged(case):
     """Paged cache: every (sequence, block) in its own page of a shuffled pool
@@ -356,6 +379,15 @@ def test_decode_paged(case):
                         torch.full_like(perm, npages + 3))
     o_p, idx_p, lg_p = sas.decode_paged(x["q"], x["q_gate"], kp, vp, gp, table.contiguous(),
                                         x["ctx_len"], K, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_c)
+    assert torch.equal(lg_p.nan_to_num(), lg_c.nan_to_num())
+    assert torch.equal(o_p.view(torch.int16), o_c.view(torch.int16))
+    # the same with bf16 gate keys on both sides
+    o_c, idx_c, lg_c = sas.decode(x["q"], x["q_gate"], x["k_cache"], x["v_cache"],
+                                  x["kg_cache"].to(torch.bfloat16), x["ctx_len"], K, sc)
+    o_p, idx_p, lg_p = sas.decode_paged(x["q"], x["q_gate"], kp, vp, gp.to(torch.bfloat16),
+                                        table.contiguous(), x["ctx_len"], K, sc)
     torch.cuda.synchronize()
     assert torch.equal(idx_p, idx_c)
     assert torch.equal(lg_p.nan_to_num(), lg_c.nan_to_num())
