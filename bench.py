@@ -86,7 +86,9 @@ def load_traffic(kernel_key: str, src_hash: str):
 COPY_BYTES = 1 << 30          # the calibration copy (--copy-calib)
 TRAFFIC_SOURCES = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
                    "dq_kernel": "attn_bwd.hip", "topk_kernel": "topk.hip",
-                   "decode_attn_kernel": "decode.hip", "decode_score_kernel": "decode.hip",
+                   "decode_attn_kernel": "decode.hip",
+                   # fp32 gate keys (the bench also runs the bf16-key variant)
+                   "decode_score_kernel<128, false>": "decode.hip",
                    "decode_topk_kernel": "decode.hip", "decode_merge_kernel": "decode.hip",
                    "gbwd_key_kernel": "router_bwd.hip", "gbwd_query_kernel": "router_bwd.hip",
                    "gbwd_blockkey_kernel": "router_bwd.hip", "gbwd_wsum_kernel": "router_bwd.hip",
