@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "Dims", "DecodeDims", "SasError", "load_library", "version", "workspace_size",
     "decode_workspace_size", "gate_score", "topk_blocks", "sparse_attn_fwd",
-    "sparse_attn_bwd", "decode", "decode_paged", "budget_to_topk", "EXPORTED_SYMBOLS",
+    "sparse_attn_bwd", "decode", "decode_paged", "decode_gate_key", "budget_to_topk",
+    "EXPORTED_SYMBOLS",
     "set_timing_events",
     "take_device_fault", "gate_score_bwd",
 ]
@@ -34,7 +35,7 @@ EXPORTED_SYMBOLS = (
     "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
     "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
     "sas_decode", "sas_set_timing_events", "sas_take_device_fault", "sas_gate_score_bwd",
-    "sas_decode_paged",
+    "sas_decode_paged", "sas_decode_gate_key",
 )
 
 
@@ -88,10 +89,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                + [P, S, P])
     lib.sas_decode_paged.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 5 + [I32] + [P] * 2
                                      + [F32] + [P] * 3 + [P, S, P])
+    lib.sas_decode_gate_key.argtypes = ([ctypes.POINTER(DecodeDims)] + [P, P, I32, P, P]
+                                        + [ctypes.c_double, F32] + [P, P, P])
     lib.sas_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     lib.sas_take_device_fault.argtypes = [ctypes.POINTER(ctypes.c_uint)]
     for fn in ("sas_gate_score", "sas_gate_score_bwd", "sas_topk_blocks", "sas_sparse_attn_fwd",
-               "sas_sparse_attn_bwd", "sas_decode", "sas_decode_paged", "sas_set_timing_events",
+               "sas_sparse_attn_bwd", "sas_decode", "sas_decode_paged", "sas_decode_gate_key",
+               "sas_set_timing_events",
                "sas_take_device_fault"):
         getattr(lib, fn).restype = I32
     _lib = lib
@@ -427,3 +431,41 @@ def decode_paged(q, q_gate, k_pages, v_pages, kg_pages, block_table, ctx_len, to
                                 _ptr(idx), _ptr(logg), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream(dev)))
     return o, idx, logg
+
+
+def decode_gate_key(k_cache, wk, w_kn, ctx_len, kg_cache, theta: float, eps: float,
+                    block_table=None):
+    """Refresh the gate-key cache entry of each sequence's current block from
+    the KV cache rows 64c .. L-1 (see sas_decode_gate_key).  k_cache
+    [B,Hkv,Lmax,D] (block_table None) or pages [P,Hkv,64,D] with block_table
+    [B,NBmax]; kg_cache [B,Hkv,NBmax,dg] or [P,Hkv,dg], fp32 or bf16, updated
+    in place."""
+    lib = load_library()
+    dev = _device_of(k_cache)
+    B = ctx_len.shape[0]
+    Hkv, D = k_cache.shape[1], k_cache.shape[3]
+    dg = kg_cache.shape[-1]
+    if block_table is None:
+        Lmax = k_cache.shape[2]
+        NBmax = -(-Lmax // 64)
+        npages = 0
+        _req(kg_cache, "kg_cache", kg_cache.dtype, (B, Hkv, NBmax, dg), dev)
+    else:
+        NBmax = block_table.shape[1]
+        Lmax = 64 * NBmax
+        npages = k_cache.shape[0]
+        _req(block_table, "block_table", torch.int32, (B, NBmax), dev)
+        _req(kg_cache, "kg_cache", kg_cache.dtype, (npages, Hkv, dg), dev)
+    if kg_cache.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("kg_cache must be float32 or bfloat16")
+    _req(k_cache, "k_cache", torch.bfloat16, tuple(k_cache.shape), dev)
+    _req(wk, "wk", torch.bfloat16, (Hkv, 3 * D, dg), dev)
+    _req(w_kn, "w_kn", torch.float32, (dg,), dev)
+    _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
+    d = DecodeDims(B, Hkv, Hkv, D, dg, 64, 0, Lmax, NBmax, 1,
+                   1 if kg_cache.dtype == torch.bfloat16 else 0)
+    _check(lib.sas_decode_gate_key(ctypes.byref(d), _ptr(k_cache), _ptr(block_table),
+                                   ctypes.c_int32(npages), _ptr(wk), _ptr(w_kn),
+                                   ctypes.c_double(theta), ctypes.c_float(eps), _ptr(ctx_len),
+                                   _ptr(kg_cache), _stream(dev)))
+    return kg_cache

@@ -433,6 +433,31 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
   return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)), "sas_decode launch");
 }
 
+sas_status sas_decode_gate_key(const sas_decode_dims* d, const uint16_t* k_cache,
+                               const int32_t* block_table, int32_t num_pages, const uint16_t* wk,
+                               const float* w_kn, double rope_theta, float norm_eps,
+                               const int32_t* ctx_len, void* kg_cache, void* stream) {
+  sas_status st = check_decode_dims(d);
+  if (st) return st;
+  REQ_PTR(k_cache); REQ_PTR(wk); REQ_PTR(w_kn); REQ_PTR(ctx_len); REQ_PTR(kg_cache);
+  if (block_table && !aligned16(block_table))
+    return fail(SAS_ERR_INVALID, "block_table is not 16-byte aligned");
+  if (block_table && num_pages < 1)
+    return fail(SAS_ERR_INVALID, "num_pages must be positive (got %d)", num_pages);
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(SAS_ERR_INVALID, "rope_theta must be positive and finite");
+  if (!(norm_eps >= 0.f) || !std::isfinite(norm_eps))
+    return fail(SAS_ERR_INVALID, "norm_eps must be non-negative and finite");
+  sas::DecodeKeyParams p{};
+  p.k = k_cache; p.btab = block_table; p.num_pages = num_pages; p.wk = wk; p.w_kn = w_kn;
+  p.ctx_len = ctx_len; p.kg = kg_cache;
+  p.B = d->B; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
+  p.kg_bf16 = d->kg_dtype; p.theta = rope_theta; p.eps = norm_eps;
+  g_err.clear();
+  return hip_status(sas::launch_decode_gate_key(p, static_cast<hipStream_t>(stream)),
+                    "sas_decode_gate_key launch");
+}
+
 sas_status sas_decode_paged(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
                             const uint16_t* k_pages, const uint16_t* v_pages,
                             const float* kg_pages, int32_t num_pages,

@@ -204,6 +204,20 @@ hipError_t launch_sparse_bwd(const BwdParams& p, hipStream_t st);
 hipError_t take_ring_fault_bwd(unsigned* out);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 
+struct DecodeKeyParams {
+  const uint16_t* k;        // [B,Hkv,Lmax,D], or paged [P,Hkv,64,D]
+  const int32_t* btab;      // paged: [B,NBmax], else null
+  int num_pages;
+  const uint16_t* wk;       // [Hkv,3D,dg] bf16
+  const float* w_kn;        // [dg]
+  const int32_t* ctx_len;   // [B]
+  void* kg;                 // [B,Hkv,NBmax,dg] or paged [P,Hkv,dg]; fp32 or bf16
+  int B, Hkv, D, dg, Lmax, NBmax, kg_bf16;
+  double theta;
+  float eps;
+};
+hipError_t launch_decode_gate_key(const DecodeKeyParams& p, hipStream_t st);
+
 // decode attention splits per unit and (even) slots per split for S slots and
 // units = B * Hkv (also sizes the workspace)
 void decode_split(int S, int units, int* nsplit, int* spw);

@@ -290,6 +290,31 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
                       size_t ws_bytes, void* stream);
 
 /*
+ * Gate key of each sequence's current block for decode (model card,
+ * checkpoint configuration: block pooling max + min + average, K norm, gate
+ * RoPE).  With L = ctx_len[b] (the new token already written at position
+ * L-1 of the KV cache) and c = (L-1)/64, per KV head kappa:
+ *   p = [max; min; mean] over the cache rows 64c .. L-1 (channel-wise),
+ *   kg = RoPE_{64c}(RMSNorm(p Wk[kappa]) * w_kn)
+ * — the prefill gate key of token L-1 (sas_gate_score's k_gate) — written to
+ * the gate-key cache entry of block c, which sas_decode / sas_decode_paged
+ * then score as the current block.  Called after each appended token.
+ *
+ *   k_cache: [B,Hkv,Lmax,D] bf16 (block_table NULL), or the paged pool
+ *   [num_pages,Hkv,64,D] with block_table [B,NBmax] as in sas_decode_paged;
+ *   wk [Hkv,3D,dg] bf16, w_kn [dg] fp32, rope_theta, norm_eps as in
+ *   sas_gate_score;  kg_cache: [B,Hkv,NBmax,dg] (or [num_pages,Hkv,dg]),
+ *   fp32 or bf16 per d->kg_dtype; only the entries of the current blocks
+ *   are written.  Sequences with ctx_len outside [1, Lmax], or whose current
+ *   block's page is outside the pool, are left untouched.  fp32 arithmetic,
+ *   deterministic.  No workspace.
+ */
+sas_status sas_decode_gate_key(const sas_decode_dims* d, const uint16_t* k_cache,
+                               const int32_t* block_table, int32_t num_pages, const uint16_t* wk,
+                               const float* w_kn, double rope_theta, float norm_eps,
+                               const int32_t* ctx_len, void* kg_cache, void* stream);
+
+/*
  * sas_decode over a paged KV cache: a serving backend keeps each sequence's
  * 64-token blocks in pages of a shared pool (the model card's decode runs a
  * batch of sequences of different lengths; a page is one KV block, so a

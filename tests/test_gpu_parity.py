@@ -394,6 +394,60 @@ def test_decode_paged(case):
     assert torch.equal(o_p.view(torch.int16), o_c.view(torch.int16))
 
 
+@pytest.mark.parametrize("w", CASES[:3], ids=IDS[:3])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+@pytest.mark.parametrize("kg_dtype", [torch.float32, torch.bfloat16], ids=["kg32", "kg16"])
+def test_decode_gate_key(w, paged, kg_dtype):
+    """Current-block gate key refreshed from the KV cache after an append:
+    for sequences at positions t (block starts, block ends, partial blocks)
+    the entry of block t // 64 must equal the oracle's prefill gate key of
+    token t; every other entry stays as it was."""
+    x = synth.prefill_inputs(w, seed=3, device="cpu", with_dout=False)
+    T, Hkv, D, dg = w.T, w.Hkv, w.D, w.dg
+    w_kn = 1.0 + 0.25 * torch.randn(dg, generator=torch.Generator().manual_seed(9))
+    ts = sorted({0, 1, 63, 64, 65, T // 2, T - 2, T - 1} & set(range(T)))
+    B = len(ts)
+    ref = O.gate_key(x["k"], x["wk"], w_kn.numpy(), w.theta, w.eps, tokens=ts)[0]  # [n,Hkv,dg]
+    NB = -(-T // 64)
+    kc = x["k"][0].transpose(0, 1).contiguous()[None].expand(B, -1, -1, -1).contiguous().cuda()
+    ctx = torch.tensor([t + 1 for t in ts], dtype=torch.int32, device="cuda")
+    wk, wkn = x["wk"].cuda(), w_kn.cuda()
+    if not paged:
+        kg = torch.full((B, Hkv, NB, dg), 7.0, dtype=kg_dtype, device="cuda")
+        sas.decode_gate_key(kc, wk, wkn, ctx, kg, w.theta, w.eps)
+        torch.cuda.synchronize()
+        got = torch.stack([kg[b, :, t // 64] for b, t in enumerate(ts)]).float().cpu().numpy()
+        mask = torch.ones((B, NB), dtype=torch.bool)
+        for b, t in enumerate(ts):
+            mask[b, t // 64] = False
+        rest = kg.permute(0, 2, 1, 3)[mask.cuda()]
+    else:
+        Tp = NB * 64
+        pad = torch.zeros((B, Hkv, Tp, D), dtype=torch.bfloat16, device="cuda")
+        pad[:, :, :T] = kc
+        npages = B * NB + 3
+        perm = torch.from_numpy(np.random.default_rng(8).permutation(npages)[:B * NB]
+                                .astype(np.int32)).view(B, NB).cuda()
+        pool = torch.zeros((npages, Hkv, 64, D), dtype=torch.bfloat16, device="cuda")
+        pool[perm.flatten().long()] = pad.view(B, Hkv, NB, 64, D).permute(0, 2, 1, 3, 4).reshape(
+            B * NB, Hkv, 64, D)
+        kg = torch.full((npages, Hkv, dg), 7.0, dtype=kg_dtype, device="cuda")
+        sas.decode_gate_key(pool, wk, wkn, ctx, kg, w.theta, w.eps, block_table=perm)
+        torch.cuda.synchronize()
+        pages = [int(perm[b, t // 64]) for b, t in enumerate(ts)]
+        got = kg[pages].float().cpu().numpy()
+        mask = torch.ones(npages, dtype=torch.bool)
+        mask[pages] = False
+        rest = kg[mask.cuda()]
+    assert bool((rest.float() == 7.0).all()), "entries other than the current blocks changed"
+    if kg_dtype == torch.float32:
+        assert np.abs(got - ref).max() < ROUTER_ABS
+    else:
+        r16 = torch.from_numpy(ref).float().to(torch.bfloat16).float().numpy()
+        half_ulp = np.abs(r16) * 2.0 ** -8
+        assert (np.abs(got - ref) <= half_ulp + ROUTER_ABS).all()
+
+
 def test_decode_matches_prefill_row():
     """Decode of token L-1 equals the prefill row L-1 computed by the library."""
     w = CASES[1]
