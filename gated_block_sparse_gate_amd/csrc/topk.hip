@@ -12,8 +12,9 @@
 // One workgroup = 16 consecutive tokens of one (batch, KV head); all 16 share
 // the same block c, so the historical block keys form one fp32 tile product
 // (fp32 MFMA: index parity needs fp32-accurate scores).
-// Selection: exact K-th largest order key by a 32-step bitwise search with
-// wave-wide counts, then equal keys taken in ascending block order.
+// Selection: exact K-th largest order key by bitwise searches with wave-wide
+// counts (over the keys above the K-th largest lane maximum when they fit one
+// per lane), then equal keys taken in ascending block order.
 #include <type_traits>
 
 #include "sas_kernels.h"
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   constexpr int NS = DG / 16;        // 16-wide d groups
   constexpr int KU = KCH * DG / 4 / 256;   // float4 per thread per chunk
   extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ uint32_t gath[4][64];             // per wave: keys above the lane-maximum bound
   float* ks = smem;                            // [64][KP]
   float* sc = ks + KCH * KP;                   // [16][NBP]
   const int NBP = ((p.NB + 3) / 4) * 4;
@@ -155,12 +157,46 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       uint32_t thr = 0;
       int need_eq = 0;
       if (!all) {
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = thr | (1u << bit);
-          int cnt = 0;
+        // thr = the largest t with #(keys >= t) >= K, by a bitwise search.
+        // The K-th largest lane maximum t0 bounds it from below (the K
+        // largest lane maxima are K keys at or above t0; at least K lanes hold
+        // a candidate since c > K and K < 64), so when the keys >= t0 fit one
+        // per lane the search runs over them alone (same counts for every
+        // t >= t0).
+        uint32_t lmax = 0;
 #pragma unroll
-          for (int e = 0; e < EM; ++e) cnt += wave_count(kreg[e] >= cand);
-          if (cnt >= K) thr = cand;
+        for (int e = 0; e < EM; ++e) lmax = max(lmax, kreg[e]);
+        uint32_t t0k = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = t0k | (1u << bit);
+          if (wave_count(lmax >= cand) >= K) t0k = cand;
+        }
+        int n0 = 0;
+#pragma unroll
+        for (int e = 0; e < EM; ++e) n0 += wave_count(kreg[e] >= t0k);
+        if (n0 <= 64) {
+          int nb = 0;
+#pragma unroll
+          for (int e = 0; e < EM; ++e) {
+            const bool in = kreg[e] >= t0k;
+            const uint64_t m = ballot64(in);
+            if (in) gath[wv][nb + __popcll(m & lt_mask)] = kreg[e];
+            nb += __popcll(m);
+          }
+          // the wave's LDS accesses complete in order
+          const uint32_t v = lane < n0 ? gath[wv][lane] : 0u;
+          for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            if (wave_count(v >= cand) >= K) thr = cand;
+          }
+        } else {
+          for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < EM; ++e) cnt += wave_count(kreg[e] >= cand);
+            if (cnt >= K) thr = cand;
+          }
         }
         int gt = 0;
 #pragma unroll
