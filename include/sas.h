@@ -23,9 +23,9 @@
  *   - All arguments are validated before anything is launched.  On any error
  *     the call returns a non-zero sas_status, writes nothing and records a
  *     message readable through sas_last_error() (thread-local).
- *   - Index and selection data computed on the device (idx, ctx_len) are
- *     range-checked by the kernels: out-of-range entries are ignored, never
- *     dereferenced.
+ *   - Index and selection data computed on the device (idx, ctx_len,
+ *     block_table) are range-checked by the kernels: out-of-range entries are
+ *     ignored, never dereferenced.
  *   - NaN/Inf inputs propagate to outputs; selections made from NaN scores
  *     are unspecified but always in range.
  *
