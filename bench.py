@@ -220,7 +220,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards over batch x KV head with no exchange; see DESIGN.md)",
+              "(the path shards over batch x KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -20,7 +20,7 @@ What it computes (citations name the page and the passage):
 * Chinese usage guide, pitfall 3: the budget caps tokens attended per query,
   not the KV-cache size.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   gate per KV head, gate query = concatenation of the group's G query heads
   [R1]; gate inputs are the attention q/k before any backbone RoPE [R2];
   pooled key = [max; min; mean] channel-wise [R3]; the current block is
