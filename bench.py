@@ -92,7 +92,9 @@ TRAFFIC_SOURCES = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd
                    "decode_topk_kernel": "decode.hip", "decode_merge_kernel": "decode.hip",
                    "gbwd_key_kernel": "router_bwd.hip", "gbwd_query_kernel": "router_bwd.hip",
                    "gbwd_blockkey_kernel": "router_bwd.hip", "gbwd_wsum_kernel": "router_bwd.hip",
-                   "gbwd_rows_kernel": "router_bwd.hip"}
+                   "gbwd_rows_kernel": "router_bwd.hip", "gbwd_reduce_kernel": "router_bwd.hip",
+                   "gbwd_colsum_kernel": "router_bwd.hip",
+                   "gbwd_blockkey_sum_kernel": "router_bwd.hip"}
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
@@ -143,6 +145,19 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
         lines.append(f"{key}: fetch {e.get('fetch_size_bytes', 0) / 1e9:.3f} GB + write "
                      f"{e.get('write_size_bytes', 0) / 1e9:.3f} GB per launch "
                      f"({e['dispatches']} dispatches)")
+    # one router-backward call: its kernels' bytes per dispatch times their
+    # dispatches, per call (gbwd_key_kernel runs once per call)
+    gb = [k for k in res if k.startswith("gbwd_")]
+    if "gbwd_key_kernel" in res:
+        calls = res["gbwd_key_kernel"]["dispatches"]
+        res["sas_gate_score_bwd"] = {
+            "bytes_per_launch": round(sum(res[k]["bytes_per_launch"] * res[k]["dispatches"]
+                                          for k in gb) / calls),
+            "kernels": sorted(gb),
+            "source_hash": source_hash([os.path.join(csrc, f) for f in
+                                        ("router_bwd.hip", "sas_device.h", "sas_kernels.h")])}
+        lines.append(f"sas_gate_score_bwd: {res['sas_gate_score_bwd']['bytes_per_launch'] / 1e9:.3f}"
+                     f" GB per call ({' + '.join(sorted(gb))})")
     # the decode step as a whole: each of its kernels runs once per step
     dec = [k for k in res if k.startswith("decode_")]
     if dec:
@@ -420,6 +435,8 @@ def main():
         rb_flops = 2.0 * rows * Hkv * dg * (3 * G * D + 3 * 3 * D + 2 * S)
         t_hbm = rb_bytes / (PEAK_HBM_GBS * 1e9)
         t_mfma = rb_flops / (PEAK_FP32_TFLOPS * 1e12)
+        rb_traffic = load_traffic("sas_gate_score_bwd", source_hash(
+            [os.path.join(csrc, f) for f in ("router_bwd.hip", "sas_device.h", "sas_kernels.h")]))
         out["router_bwd"] = {
             "workload": w.name, "ms": round(rb_ms, 4),
             "algorithmic_bytes": rb_bytes, "algorithmic_flops": rb_flops,
@@ -427,11 +444,11 @@ def main():
             "tflops": round(rb_flops / (rb_ms * 1e-3) / 1e12, 2),
             "roofline": ({"bound": "mfma", "achieved": round(rb_flops / (rb_ms * 1e-3) / 1e12, 2),
                           "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(t_mfma / (rb_ms * 1e-3), 4), "traffic": None}
+                          "frac": round(t_mfma / (rb_ms * 1e-3), 4), "traffic": rb_traffic}
                          if t_mfma >= t_hbm else
                          {"bound": "hbm", "achieved": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 1),
                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": round(t_hbm / (rb_ms * 1e-3), 4), "traffic": None}),
+                          "frac": round(t_hbm / (rb_ms * 1e-3), 4), "traffic": rb_traffic}),
         }
         del gws, gout
 
