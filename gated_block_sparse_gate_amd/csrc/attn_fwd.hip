@@ -28,7 +28,7 @@ namespace {
 
 constexpr float kLazyLog2 = 8.f;   // weights stay below 2^8 between rescales
 constexpr int kFwdStagers = 2;     // stager 0 copies K tiles, stager 1 V^T tiles
-constexpr int kFwdInflight = 3;    // blocks in flight per stager (< R)
+constexpr int kFwdInflight = 1;    // blocks in flight per stager (< R): each is published as soon as it lands
 
 // HILO (the fp32 output is requested, for the backward's Delta): V^T is the
 // bf16 copy and P enters PV as bf16 hi + lo parts (exact to ~2^-16).
