@@ -172,6 +172,49 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
     print("\n".join(lines))
 
 
+def selection_stats(idx: torch.Tensor, block: int = 64) -> dict:
+    """Locality statistics of a selection idx [B,T,H,S] (pads -1; the last
+    valid slot is the current block): mean overlap of the historical blocks
+    of adjacent tokens (|A & B| / |A|, tokens of the same block), mean size of
+    the union of historical blocks over groups of 16 consecutive tokens, and
+    the share of all historical selections that go to the top 5 % of blocks
+    (per head).  Counting only; no scores are involved."""
+    import torch
+    idx = idx.to("cpu").long()
+    B, T, H, S = idx.shape
+    NB = -(-T // block)
+    c = (torch.arange(T) // block).view(1, T, 1, 1)
+    hist = (idx >= 0) & (idx < c)
+    onehot = torch.zeros((B, T, H, NB + 1), dtype=torch.bool)
+    onehot.scatter_(-1, torch.where(hist, idx, torch.full_like(idx, NB)), True)
+    onehot = onehot[..., :NB]
+    a, b_ = onehot[:, :-1], onehot[:, 1:]
+    same = (torch.arange(T - 1) // block == torch.arange(1, T) // block).view(1, T - 1, 1)
+    na = a.sum(-1).float()
+    keep = same & (na > 0)
+    overlap = ((a & b_).sum(-1).float() / na.clamp(min=1))[keep].mean().item()
+    G16 = T // 16
+    union = onehot[:, :G16 * 16].view(B, G16, 16, H, NB).any(2).sum(-1).float().mean().item()
+    cnt = onehot.sum(1).float()                                   # [B,H,NB]
+    top = max(1, NB // 20)
+    share = (cnt.sort(-1, descending=True).values[..., :top].sum(-1) /
+             cnt.sum(-1).clamp(min=1)).mean().item()
+    return dict(adjacent_overlap=round(overlap, 4), union16=round(union, 2),
+                top5pct_share=round(share, 4))
+
+
+def assert_sound(sas, what: str, **tensors):
+    """Exit non-zero (printing no metric) if an attention kernel abandoned a
+    ring wait since the last check or any given output holds NaN / Inf."""
+    import torch
+    fault = sas.take_device_fault()
+    bad = [n for n, t in tensors.items() if not bool(torch.isfinite(t.float()).all())]
+    if fault or bad:
+        print(f"bench.py: {what}: device fault flag {fault}, non-finite outputs {bad}; "
+              "no result reported", file=sys.stderr, flush=True)
+        sys.exit(3)
+
+
 def cpu_baseline(seed: int, n_tokens: int):
     """The fp64 oracle, as it stands, on a bounded sample of the 32K workload:
     forward + backward of every query head for n_tokens query tokens spread
@@ -304,6 +347,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    assert_sound(sas, "warm-up", o=o, o_f32=o32, dq=dq, dk=dk, dv=dv, dlogg=dlogg)
     stage_ms = [0.0] * 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -320,6 +364,11 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    # A ring wait in the attention kernels that gives up ends the kernel
+    # early with NaN outputs, which would time as a faster step: refuse to
+    # report a number unless no wait gave up and every output is finite.
+    assert_sound(sas, "training step", o=o, lse=lse, o_f32=o32, dq=dq, dk=dk, dv=dv,
+                 dlogg=dlogg, logg_valid=logg[idx >= 0])
     for i in range(args.steps):
         for s_ in range(4):
             stage_ms[s_] += evs[i][s_].elapsed_time(evs[i][s_ + 1]) / args.steps
@@ -419,7 +468,7 @@ def main():
         r0.record(stream)
         for _ in range(nrb):
             sas.gate_score_bwd(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], qg, kg, idx,
-                               dlogg, w.theta, w.eps, workspace=gws)
+                               dlogg, w.theta, w.eps, workspace=gws, check_row_sums=False)
         r1.record(stream)
         torch.cuda.synchronize()
         rb_ms = r0.elapsed_time(r1) / nrb
@@ -481,6 +530,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         warm_us = e0.elapsed_time(e1) / args.decode_steps * 1e3
+        assert_sound(sas, "decode (contiguous, warm)", o=od)
         # cold: read 1 GiB between steps so no selected block or gate key is
         # cached (a read leaves no dirty lines whose write-back would compete
         # with the step, as a 1 GiB write would)
@@ -496,6 +546,7 @@ def main():
             cold.append(a0.elapsed_time(a1) * 1e3)
         cold.sort()
         cold_us = cold[len(cold) // 2]
+        assert_sound(sas, "decode (contiguous, cold)", o=od)
         # the same step over a paged cache: every (sequence, block) in its own
         # page of a shuffled pool, through sas_decode_paged
         NBd = xd["NBmax"]
@@ -532,6 +583,7 @@ def main():
             cold_p.append(a0.elapsed_time(a1) * 1e3)
         cold_p.sort()
         cold_paged_us = cold_p[len(cold_p) // 2]
+        assert_sound(sas, "decode (paged)", o=od)
         del kpool, vpool, gpool
         # the contiguous step with the gate-key cache in bf16 (kg_dtype = 1)
         kg16 = xd["kg_cache"].to(torch.bfloat16)
@@ -554,6 +606,7 @@ def main():
             cold_b.append(a0.elapsed_time(a1) * 1e3)
         cold_b.sort()
         cold_kg16_us = cold_b[len(cold_b) // 2]
+        assert_sound(sas, "decode (bf16 gate keys)", o=od)
         del kg16
         lens = xd["ctx_len"].cpu().tolist()
         kvb, gkb, smb = decode_bytes(lens, wd.Hkv, wd.D, wd.dg, Kd, wd.G)

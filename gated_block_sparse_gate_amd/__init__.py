@@ -13,6 +13,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import warnings
 
 import torch
 
@@ -225,9 +226,14 @@ def gate_score(q, k, wq, wk, w_qn, w_kn, topk: int, theta: float = 1.0e6, eps: f
 
 
 def gate_score_bwd(q, k, wq, wk, w_qn, w_kn, q_gate, k_gate, idx, dlogg, theta: float = 1.0e6,
-                   eps: float = 1.0e-6, workspace=None):
+                   eps: float = 1.0e-6, workspace=None, check_row_sums: bool = True,
+                   row_sum_tol: float = 1e-3):
     """Router backward: returns dict of fp32 dq, dk, dwq, dwk, dw_qn, dw_kn from
-    dlogg (as the attention backward gives it) with the selection idx fixed."""
+    dlogg (as the attention backward gives it) with the selection idx fixed.
+    With check_row_sums, warns when a row of dlogg does not sum to zero within
+    row_sum_tol (the library then returns the gradient with each row's gate
+    lse held constant; see sas_gate_score_bwd in sas.h).  The check reads
+    dlogg back and synchronises; pass check_row_sums=False in timed loops."""
     lib = load_library()
     dev = _device_of(q)
     B, T, Hq, D = q.shape
@@ -246,6 +252,15 @@ def gate_score_bwd(q, k, wq, wk, w_qn, w_kn, q_gate, k_gate, idx, dlogg, theta: 
     _req(idx, "idx", torch.int32, (B, T, Hkv, S), dev)
     _req(dlogg, "dlogg", torch.float32, (B, T, Hkv, S), dev)
     d = make_dims(B, T, Hq, Hkv, D, dg, S - 1, theta, eps)
+    if check_row_sums:
+        # the library drops the -g * sum(dlogg) term of the gate-logit
+        # gradient, which vanishes for the attention's dlogg (rows sum to 0)
+        worst = float(torch.where(idx >= 0, dlogg, torch.zeros_like(dlogg)).sum(-1).abs().max())
+        if worst > row_sum_tol:
+            warnings.warn(f"dlogg rows do not sum to zero (max |row sum| {worst:.3g} > "
+                          f"{row_sum_tol:g}); sas_gate_score_bwd holds each row's gate lse "
+                          "constant, so the -g * sum(dlogg) term is not included",
+                          UserWarning, stacklevel=2)
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dq=torch.empty((B, T, Hq, D), **f32), dk=torch.empty((B, T, Hkv, D), **f32),
                dwq=torch.empty((Hkv, G * D, dg), **f32), dwk=torch.empty((Hkv, 3 * D, dg), **f32),

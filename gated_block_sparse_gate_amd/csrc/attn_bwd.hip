@@ -17,6 +17,7 @@
 //                is wasted on a query that did not select the block.
 //   dq         : query-block stationary, same walk as the forward; also
 //                produces dlogg (each (t, j) pair is visited exactly once).
+#include "bwd_index.h"
 #include "sas_kernels.h"
 
 namespace sas {
@@ -696,9 +697,10 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   // ================================================================ compute
   const int G = a.G, TPT = a.TPT;
   const int tile = wv;
-  const int tl_row = min(tile * TPT + l16 / G, 63);
-  const int hh = l16 - (l16 / G) * G;
-  bool valid = (l16 < TPT * G) && (tile * TPT + l16 / G < ntok);
+  const WalkRow wrow = walk_row(tile, l16, TPT, G, ntok);
+  const int tl_row = wrow.tl;
+  const int hh = wrow.hh;
+  bool valid = wrow.live;
   {
     const size_t qrow = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + kv * G + hh;
     valid = valid && (a.lse[qrow] > -INFINITY);
@@ -743,7 +745,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   // not select the block (or that has no row) reads at an offset past the
   // buffer, which returns zeros without a memory request.
   // bytes from this group's first row to the end of its last token's rows of kappa
-  const unsigned dsbytes = static_cast<unsigned>(((ntok - 1) * HSG + S) * G) * 256u;
+  const unsigned dsbytes = dq_ds_bytes(ntok, HSG, S, G);
   const auto dsr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dsq), 0,
                                                      static_cast<int>(dsbytes), kBufferWord3);
   struct DsRows { uint4 h[2], l[2]; };
@@ -753,11 +755,13 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
       const int j = ulist[v];
       const int jw = j >> 5;
       const uint32_t jbit = 1u << (j & 31);
-      if (valid && (bits[tl_row * NBW + jw] & jbit)) {
+      const bool take = valid && (bits[tl_row * NBW + jw] & jbit);
+      int sl = 0;
+      if (take) {
         const int rank = pcnt[tl_row * NBW + jw] + __popc(bits[tl_row * NBW + jw] & (jbit - 1u));
-        const int sl = slot_of[tl_row * S + rank];
-        off = static_cast<unsigned>(((tl_row * HSG + sl) * G + hh) * 256 + 16 * g4);
+        sl = slot_of[tl_row * S + rank];
       }
+      off = dq_ds_offset(take, tl_row, HSG, sl, G, hh, g4, dsbytes);
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -860,8 +864,8 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
 // Static LDS: ring of 8 K tiles (D = 128: 128 KiB) plus the selection data.
 template <int D>
 hipError_t launch_dq(const BwdParams& p, hipStream_t st) {
-  const int tpw = min(64, 14 * p.TPT);
-  const int ncw = (tpw + p.TPT - 1) / p.TPT;
+  const int tpw = walk_tpw(p.TPT);
+  const int ncw = walk_ncw(p.TPT);
   const unsigned ngrp = (p.T + tpw - 1) / tpw;
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * ngrp);
   hipLaunchKernelGGL((dq_kernel<D, 8>), grid, dim3((ncw + kDqStagers) * 64), 0, st, p, ncw, tpw);

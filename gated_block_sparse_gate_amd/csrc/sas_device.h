@@ -199,9 +199,12 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x + dpp_mov<0x140>(x);        // row_mirror
 }
 
-// Order-preserving map fp32 -> uint32 (larger float -> larger key).
+// Order-preserving map fp32 -> uint32 (larger float -> larger key).  -0.0
+// and +0.0 compare equal as numbers, so both map to the key of +0.0 and an
+// exact tie between them goes to the lower block index like any other tie.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -83,6 +83,12 @@ def rope(x: np.ndarray, pos, theta: float) -> np.ndarray:
     return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
 
 
+def head_proj(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Per-head linear map without bias [R7]: out[..., h, :] = x[..., h, :] @ w[h].
+    x [B, n, H, F], w [H, F, dg] -> [B, n, H, dg]."""
+    return np.matmul(np.moveaxis(x, 2, 0), as64(w)[:, None]).transpose(1, 2, 0, 3)
+
+
 def gate_query(q, wq, w_qn, theta: float, eps: float, tokens=None) -> np.ndarray:
     """Gate query per (b, t, kappa): RoPE_t(RMSNorm(x_t Wq[kappa]) * w_qn).
 
@@ -96,7 +102,7 @@ def gate_query(q, wq, w_qn, theta: float, eps: float, tokens=None) -> np.ndarray
     G = Hq // Hkv
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     x = q[:, tok].reshape(B, len(tok), Hkv, G * D)
-    y = np.einsum("bnkf,kfg->bnkg", x, wq)
+    y = head_proj(x, wq)
     y = rms_norm(y, as64(w_qn), eps)
     return rope(y, tok[None, :, None], theta)
 
@@ -172,6 +178,18 @@ def select_blocks(s: np.ndarray, K: int):
     return sel, near_tie
 
 
+def kth_gap(s: np.ndarray, K: int) -> float:
+    """Gap between the K-th and (K+1)-th largest historical scores of a row
+    (s [c+1], current block last); +inf when no historical block is left out
+    (c <= K or K = 0).  0 means an exact tie across the selection boundary,
+    which the lower-index rule decides [R12]."""
+    c = len(s) - 1
+    if K < 1 or c <= K:
+        return math.inf
+    h = np.sort(np.asarray(s[:c]))[::-1]
+    return float(h[K - 1] - h[K])
+
+
 def route(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float, tokens=None):
     """Router + candidate softmax + selection for the chosen tokens.
 
@@ -200,6 +218,7 @@ def route(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float, tokens=Non
     logg = np.full((B, n_tok, Hkv, S), -np.inf)
     lse = np.zeros((B, n_tok, Hkv))
     near = np.zeros((B, n_tok, Hkv), dtype=bool)
+    gap = np.full((B, n_tok, Hkv), np.inf)
     s_dense = np.full((B, n_tok, Hkv, NB), -np.inf)
     probs = np.zeros((B, n_tok, Hkv, NB))
     for n, t in enumerate(tok):
@@ -215,9 +234,10 @@ def route(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float, tokens=Non
                 logg[b, n, kv, :len(sel)] = lg[sel]
                 lse[b, n, kv] = l
                 near[b, n, kv] = nt
+                gap[b, n, kv] = kth_gap(s, K)
                 s_dense[b, n, kv, :c + 1] = s
                 probs[b, n, kv, :c + 1] = np.exp(lg)
-    return dict(qg=qg, kg_cur=kg_cur, idx=idx, logg=logg, lse=lse, near_tie=near,
+    return dict(qg=qg, kg_cur=kg_cur, idx=idx, logg=logg, lse=lse, near_tie=near, gap=gap,
                 s=s_dense, probs=probs, tokens=tok)
 
 
@@ -421,6 +441,207 @@ def attn_bwd_block(q, k, v, dout, idx, logg, scale: float, b: int, kv: int, j: i
     return dk, dv
 
 
+# --------------------------------------------------------------------------
+# Whole-sequence evaluation of the same definitions, for full-size checks:
+# the router and selection of every token, and the gather-form attention
+# (forward and backward) of every query row of one KV head.  Each restates
+# the per-row definitions above with the rows of a query block (router) or a
+# batch of tokens (attention) stacked along a leading axis; nothing is
+# reordered inside a row.  Pinned against route() and attn_bwd() on small
+# shapes.
+# --------------------------------------------------------------------------
+
+def gate_key_all(k, wk, w_kn, theta: float, eps: float) -> np.ndarray:
+    """gate_key() of every token at once: the causal prefix [max; min; mean]
+    of each token's block [R3, R4], Kproj, RMSNorm, RoPE at 64c [R6].
+    k [B,T,Hkv,D], wk [Hkv,3D,dg] -> [B,T,Hkv,dg]."""
+    k = as64(k)
+    B, T, Hkv, D = k.shape
+    NB = -(-T // BLOCK)
+    kp = np.zeros((B, NB * BLOCK, Hkv, D))
+    kp[:, :T] = k
+    kb = kp.reshape(B, NB, BLOCK, Hkv, D)
+    n = np.arange(1, BLOCK + 1, dtype=np.float64)[None, None, :, None, None]
+    pool = np.concatenate([np.maximum.accumulate(kb, axis=2), np.minimum.accumulate(kb, axis=2),
+                           np.cumsum(kb, axis=2) / n], axis=-1)
+    pool = pool.reshape(B, NB * BLOCK, Hkv, 3 * D)[:, :T]
+    z = rms_norm(head_proj(pool, wk), as64(w_kn), eps)
+    tok = np.arange(T)
+    return rope(z, ((tok // BLOCK) * BLOCK)[None, :, None], theta)
+
+
+def select_rows(s_hist: np.ndarray, K: int):
+    """select_blocks() for many rows with the same c at once: s_hist [m, c]
+    historical scores -> (sel [m, min(K, c)] ascending block ids, gap [m]
+    K-th/(K+1)-th gap or +inf).  A stable sort on -s keeps equal scores in
+    ascending block order, so ties go to the lower index [R11, R12]."""
+    m, c = s_hist.shape
+    n = min(K, c)
+    order = np.argsort(-s_hist, axis=1, kind="stable")
+    sel = np.sort(order[:, :n], axis=1)
+    gap = np.full(m, np.inf)
+    if K >= 1 and c > K:
+        srt = np.take_along_axis(s_hist, order, axis=1)
+        gap = srt[:, K - 1] - srt[:, K]
+    return sel, gap
+
+
+def route_all(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float):
+    """route() for every token: gate vectors, candidate softmax and Top-K.
+
+    Selection heads Hs = wq.shape[0] (Hkv: one gate per KV head [R1]); head
+    sg scores the gate keys of KV head sg * (Hq / Hs) // G.  Historical blocks
+    are ranked by a stable sort on -s, which keeps equal scores in ascending
+    block order (ties -> lower index [R12]).
+    Returns qg [B,T,Hs,dg], kg [B,T,Hkv,dg], idx, logg [B,T,Hs,K+1],
+    lse, gap [B,T,Hs] (K-th/(K+1)-th gap, +inf when nothing is left out),
+    near_tie [B,T,Hs].
+    """
+    q, k = as64(q), as64(k)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    Hs = as64(wq).shape[0]
+    G, Gs = Hq // Hkv, Hq // Hs
+    S = K + 1
+    qg = gate_query(q, wq, w_qn, theta, eps)
+    kg = gate_key_all(k, wk, w_kn, theta, eps)
+    kblk = kg[:, block_key_tokens(T)]                       # [B,NB,Hkv,dg]
+    rdg = math.sqrt(qg.shape[-1])
+    idx = np.full((B, T, Hs, S), -1, dtype=np.int64)
+    logg = np.full((B, T, Hs, S), -np.inf)
+    lse = np.zeros((B, T, Hs))
+    gap = np.full((B, T, Hs), np.inf)
+    NB = -(-T // BLOCK)
+    for c in range(NB):
+        t0, t1 = BLOCK * c, min(BLOCK * c + BLOCK, T)
+        n = min(K, c)
+        for b in range(B):
+            for sg in range(Hs):
+                kv = sg * Gs // G
+                Q = qg[b, t0:t1, sg]                                   # [m, dg]
+                s = np.concatenate([Q @ kblk[b, :c, kv].T,
+                                    (Q * kg[b, t0:t1, kv]).sum(-1, keepdims=True)], axis=1) / rdg
+                m = s.max(axis=1, keepdims=True)
+                l = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+                sel, gp = select_rows(s[:, :c], K)
+                idx[b, t0:t1, sg, :n] = sel
+                idx[b, t0:t1, sg, n] = c
+                logg[b, t0:t1, sg, :n] = np.take_along_axis(s, sel, axis=1) - l[:, None]
+                logg[b, t0:t1, sg, n] = s[:, c] - l
+                lse[b, t0:t1, sg] = l
+                gap[b, t0:t1, sg] = gp
+    return dict(qg=qg, kg=kg, idx=idx, logg=logg, lse=lse, gap=gap,
+                near_tie=gap < NEAR_TIE_GAP)
+
+
+def attn_head(q, k, v, idx, logg, scale: float, b: int, sg: int, dout=None, batch: int = 32):
+    """Gather-form attention of every query row of selection head sg (batch b).
+
+    Selection heads Hs = idx.shape[2]; sg covers query heads sg*Gs ..
+    (sg+1)*Gs - 1 (Gs = Hq/Hs) and KV head sg*Gs // G.  Per token t: the keys
+    of its selected blocks with tau <= t [R13], l = q.k * scale + logg[slot]
+    [R10], P = softmax(l), o = P V, lse = logsumexp(l); with dout, the
+    backward of attn_bwd(): Delta = dO.o, dS = P (dO.v - Delta),
+    dq = scale dS K, dlogg[slot] = sum over the heads and the block's keys of
+    dS.  dk, dv of the KV head are the sums over every row that selected a
+    key's block (rows of this selection head only; with one gate per KV head
+    that is all of them): per key block j, the rows that chose j, with P taken
+    from each row's lse.
+    Returns dict with o [T,Gs,D], lse [T,Gs] and, with dout, dq [T,Gs,D],
+    dlogg [T,S], dk, dv [T,D].
+    """
+    import torch
+
+    f64 = torch.float64
+    q, k, v = (torch.as_tensor(as64(x)) for x in (q, k, v))
+    lg_all = torch.as_tensor(as64(logg))
+    idx = torch.as_tensor(np.asarray(idx)).long()
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    Hs, S = idx.shape[2], idx.shape[3]
+    G, Gs = Hq // Hkv, Hq // Hs
+    kv = sg * Gs // G
+    hs = slice(sg * Gs, (sg + 1) * Gs)
+    NB = -(-T // BLOCK)
+    Kb = torch.zeros((NB * BLOCK, D), dtype=f64)
+    Vb = torch.zeros((NB * BLOCK, D), dtype=f64)
+    Kb[:T], Vb[:T] = k[b, :, kv], v[b, :, kv]
+    Kb, Vb = Kb.view(NB, BLOCK, D), Vb.view(NB, BLOCK, D)
+    Qh = q[b, :, hs]                                           # [T,Gs,D]
+    lg = lg_all[b, :, sg]                                      # [T,S]
+    sel_all = idx[b, :, sg]
+    tok = torch.arange(T)
+    valid_all = (sel_all >= 0) & (sel_all <= (tok // BLOCK)[:, None])
+    o = torch.zeros((T, Gs, D), dtype=f64)
+    lse = torch.zeros((T, Gs), dtype=f64)
+    if dout is not None:
+        dO_all = torch.as_tensor(as64(dout))[b, :, hs]
+        dq = torch.zeros((T, Gs, D), dtype=f64)
+        dlogg = torch.zeros((T, S), dtype=f64)
+        delta = torch.zeros((T, Gs), dtype=f64)
+    ar = torch.arange(BLOCK)
+    # rows: per batch of tokens, the selected blocks gathered and concatenated
+    for t0 in range(0, T, batch):
+        ts = tok[t0:min(T, t0 + batch)]
+        n = len(ts)
+        valid = valid_all[ts]
+        j = torch.where(valid, sel_all[ts], torch.zeros_like(sel_all[ts]))
+        Kg = Kb[j].view(n, S * BLOCK, D)
+        Vg = Vb[j].view(n, S * BLOCK, D)
+        tau = (j[..., None] * BLOCK + ar).view(n, S * BLOCK)
+        mask = (valid[..., None] & (tau.view(n, S, BLOCK) <= ts[:, None, None])).view(n, 1, S * BLOCK)
+        bias = lg[ts].repeat_interleave(BLOCK, dim=1)[:, None, :]     # [n,1,S*64]
+        Q = Qh[ts]
+        L = torch.bmm(Q, Kg.transpose(1, 2)) * scale + bias
+        L = torch.where(mask, L, torch.full_like(L, -math.inf))
+        m = L.amax(dim=2, keepdim=True)
+        E = torch.exp(L - m)
+        lsum = E.sum(dim=2, keepdim=True)
+        P = E / lsum
+        O = torch.bmm(P, Vg)
+        o[ts] = O
+        lse[ts] = (m + torch.log(lsum))[..., 0]
+        if dout is None:
+            continue
+        dO = dO_all[ts]
+        dP = torch.bmm(dO, Vg.transpose(1, 2))
+        dlt = (dO * O).sum(-1)
+        dS = P * (dP - dlt[..., None])
+        dq[ts] = scale * torch.bmm(dS, Kg)
+        per_slot = dS.sum(dim=1).view(n, S, BLOCK).sum(-1)
+        dlogg[ts] = torch.where(valid, per_slot, torch.zeros_like(per_slot))
+        delta[ts] = dlt
+    out = dict(o=o.numpy(), lse=lse.numpy())
+    if dout is None:
+        return out
+    # keys: per block j, the rows (token, head) whose selection holds j
+    dkb = torch.zeros((NB, BLOCK, D), dtype=f64)
+    dvb = torch.zeros((NB, BLOCK, D), dtype=f64)
+    tt, ss = torch.nonzero(valid_all, as_tuple=True)
+    jj = sel_all[tt, ss]
+    order = torch.argsort(jj, stable=True)
+    tt, ss, jj = tt[order], ss[order], jj[order]
+    bounds = torch.searchsorted(jj, torch.arange(NB + 1))
+    for jb in range(NB):
+        lo, hi = int(bounds[jb]), int(bounds[jb + 1])
+        if lo == hi:
+            continue
+        rt, rs = tt[lo:hi], ss[lo:hi]
+        QR = Qh[rt].reshape(-1, D)                                 # [m*Gs, D]
+        dOR = dO_all[rt].reshape(-1, D)
+        trow = rt.repeat_interleave(Gs)
+        bias = lg[rt, rs].repeat_interleave(Gs)
+        Sm = QR @ Kb[jb].T * scale + bias[:, None]
+        keep = (jb * BLOCK + ar)[None, :] <= trow[:, None]
+        P = torch.where(keep, torch.exp(Sm - lse[rt].reshape(-1)[:, None]), torch.zeros_like(Sm))
+        dvb[jb] = P.T @ dOR
+        dS = P * (dOR @ Vb[jb].T - delta[rt].reshape(-1)[:, None])
+        dkb[jb] = scale * dS.T @ QR
+    out.update(dq=dq.numpy(), dlogg=dlogg.numpy(),
+               dk=dkb.view(NB * BLOCK, D)[:T].numpy(), dv=dvb.view(NB * BLOCK, D)[:T].numpy())
+    return out
+
+
 def gate_logit_grad(dlogg, idx, probs) -> np.ndarray:
     """Gradient reaching the gate logits s through log g = s - lse(s) [R18]:
     ds_j = dlogg_j [j selected] - g_j * sum over selected i of dlogg_i, for j <= c.
@@ -498,7 +719,8 @@ def _pool_with_args(k: np.ndarray):
             (amin + base).reshape(B, NB * BLOCK, H, D)[:, :T], n)
 
 
-def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float, heads=None):
+def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float, heads=None,
+               lse_term: bool = True):
     """Gradient of L = sum over (b, t, kappa, valid slot) of dlogg * log g with
     the selection idx held fixed, with respect to the router's inputs and
     weights [R1-R9, R18, R21].
@@ -509,7 +731,10 @@ def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float, h
     dw_qn, dw_kn their share of the sums.  Returns dq, dk, dwq, dwk, dw_qn,
     dw_kn, and the intermediate gradients dqg, dkg with respect to the gate
     query and the per-token gate key [B,T,H,dg], and ds [B,T,H,NB] with
-    respect to the gate logits.
+    respect to the gate logits.  lse_term=False differentiates
+    L = sum dlogg * s over the selected logits instead (the row's lse held
+    constant): ds = dlogg on the selected blocks, 0 elsewhere, which equals the
+    full gradient whenever each row's dlogg sums to zero [R18].
     """
     q, k, wq, wk = as64(q), as64(k), as64(wq), as64(wk)
     w_qn, w_kn = as64(w_qn), as64(w_kn)
@@ -542,7 +767,7 @@ def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float, h
     np.put_along_axis(s, ccol, (np.einsum("btkg,btkg->btk", qg, kg) / sq)[..., None], axis=-1)
     probs = np.exp(s - s.max(axis=-1, keepdims=True))
     probs /= probs.sum(axis=-1, keepdims=True)
-    ds = gate_logit_grad(dlogg, idx, probs)
+    ds = gate_logit_grad(dlogg, idx, probs if lse_term else np.zeros_like(probs))
     ds_hist = np.where(hist, ds, 0.0)
     ds_cur = np.take_along_axis(ds, ccol, axis=-1)[..., 0]
     # s -> gate query and gate keys
@@ -600,6 +825,7 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, K: int, scale: float,
     idx = np.full((B, Hkv, S), -1, dtype=np.int64)
     logg = np.full((B, Hkv, S), -np.inf)
     near = np.zeros((B, Hkv), dtype=bool)
+    gap = np.full((B, Hkv), np.inf)
     if units is None:
         units = [(b, kv) for b in range(B) for kv in range(Hkv)]
     for b, kv in units:
@@ -613,6 +839,7 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, K: int, scale: float,
         idx[b, kv, :len(sel)] = sel
         logg[b, kv, :len(sel)] = lg[sel]
         near[b, kv] = nt
+        gap[b, kv] = kth_gap(s, K)
         taus, slots = _row_keys(t, np.array(sel))
         Kr = as64(k_cache[b, kv, taus])
         Vr = as64(v_cache[b, kv, taus])
@@ -622,7 +849,7 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, K: int, scale: float,
         P = np.exp(Lg - Lg.max(axis=1, keepdims=True))
         P /= P.sum(axis=1, keepdims=True)
         o[b, kv * G:(kv + 1) * G] = P @ Vr
-    return dict(o=o, idx=idx, logg=logg, near_tie=near)
+    return dict(o=o, idx=idx, logg=logg, near_tie=near, gap=gap)
 
 
 # --------------------------------------------------------------------------

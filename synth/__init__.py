@@ -107,7 +107,14 @@ DECODE_B64 = Workload("qwen3_8b_decode_B64_budget2048", 4, B=64, T=1, Hq=32, Hkv
 SKEW_32K = Workload("qwen3_14b_train_T32768_G5_skew", 5, B=1, T=32768, Hq=40, Hkv=8, D=128,
                     dg=128, topk=31, kind="train", skew="lognormal_block")
 
-WORKLOADS = {w.name: w for w in (TINY, PREFILL_8K, TRAIN_32K, DECODE_B64, SKEW_32K)}
+# The same shape with rankings skewed on purpose: shared per-head directions
+# in q and k with a per-block lognormal weight (k = z + s_j u, q = z' + 4 w),
+# so that adjacent tokens choose largely the same blocks and a few blocks are
+# chosen by many tokens (a per-block scale alone cancels in the gate's Q/K
+# normalisation and leaves the rankings uniform).
+SKEW5B_32K = SKEW_32K.replace(name="qwen3_14b_train_T32768_G5_shared", skew="shared_dir")
+
+WORKLOADS = {w.name: w for w in (TINY, PREFILL_8K, TRAIN_32K, DECODE_B64, SKEW_32K, SKEW5B_32K)}
 
 
 def budget_to_topk(budget: int, block: int = 64) -> int:

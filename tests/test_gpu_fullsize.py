@@ -2,14 +2,16 @@
 configuration (the forward also writes its fp32 output, the backward consumes
 it), on outputs the fp64 oracle computes one by one:
 
-* router + Top-K (8K prefill, 32K training, 32K G=5 skewed shapes): gate
-  vectors, indices and log-gates of sampled query tokens against the oracle
-  router; structural properties of every row (ascending historical slots,
-  current block last, pads, gates summing to at most 1);
+* router + Top-K (8K prefill, 32K training, 32K G=5 with per-block scale and
+  with shared-direction skew): gate vectors, indices (outside near ties),
+  log-gates and lse of every token against the oracle router; structural
+  properties of every row (ascending historical slots, current block last,
+  pads, gates summing to at most 1);
 * attention forward / backward on a seeded random selection with the router's
-  structure (independent of the router implementation): o, lse, o_f32 and
-  dq, dlogg of sampled query rows; dk, dv of sampled KV blocks (every query
-  that selected the block contributes); on every row, the log-gate gradient
+  structure (independent of the router implementation), and on the oracle
+  router's own selection for the shared-direction workload: one KV head in
+  full (every query row's o, lse, o_f32, dq, d log g; every key block's dk,
+  dv) plus sampled rows of every head; on every row, the log-gate gradient
   sums to zero over the selected slots;
 * batched decode at 64 sequences with contexts U[8192, 65536] and budget
   2,048: indices of every (sequence, KV head) unit, outputs of sampled units;
@@ -17,10 +19,11 @@ it), on outputs the fp64 oracle computes one by one:
   oracle taken one KV head at a time.
 
 Tolerances are those of the small-shape parity tests: for bf16 outputs the
-max-abs bound applies to the error beyond half a bf16 ulp of the exact value,
-and the mean-abs bound to the error beyond the mean of those half-ulps (the
-G=5 skewed workload drives some gradients into the hundreds, where storing
-the exact value in bf16 alone costs more than 1e-3 on average).
+max-abs bound applies to the error beyond half a bf16 ulp of the exact value
+and the mean-abs bound is raw, except for the gradients of the G=5 skewed
+workloads, which reach the hundreds, where storing the exact value in bf16
+alone costs more than 1e-3 on average: there the mean bound applies beyond
+the mean of those half-ulps.
 """
 import math
 
@@ -37,23 +40,25 @@ pytestmark = pytest.mark.gpu
 MAX_ABS, MEAN_ABS = 1e-2, 1e-3
 ROUTER_ABS = 1e-4
 
-FULL = [synth.PREFILL_8K, synth.TRAIN_32K, synth.SKEW_32K]
-FULL_IDS = [w.name for w in FULL]
-
-
 def bf16_half_ulp(x):
     a = np.maximum(np.abs(x), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(a)) - 8)
 
 
-def check(name, gpu, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+def check(name, gpu, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rounding_floor=False):
+    """Max-abs beyond the bf16 rounding of the exact value; raw mean-abs,
+    plus the mean bf16 rounding of the exact values only where
+    rounding_floor is set (the G=5 skewed workload, whose gradients reach the
+    hundreds, where storing the exact value in bf16 alone costs more than
+    1e-3 on average)."""
     a = gpu.detach().float().cpu().numpy().astype(np.float64)
     d = np.abs(a - ref)
     excess, floor = d, 0.0
     if gpu.dtype == torch.bfloat16:
         hu = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(a)))
         excess = np.maximum(0.0, d - hu)
-        floor = float(bf16_half_ulp(ref).mean())   # mean rounding error of bf16(exact)
+        if rounding_floor:
+            floor = float(bf16_half_ulp(ref).mean())   # mean rounding error of bf16(exact)
     print(f"  {name}: max-abs {d.max():.3e} (beyond bf16 rounding {excess.max():.3e}) "
           f"mean-abs {d.mean():.3e} (bf16 floor {floor:.1e})", flush=True)
     assert excess.max() <= max_abs and d.mean() <= mean_abs + floor, (name, d.max(), excess.max(),
@@ -83,6 +88,20 @@ def inputs(w):
 
 # ------------------------------------------------------------ router + Top-K
 
+FULL = [synth.PREFILL_8K, synth.TRAIN_32K, synth.SKEW_32K, synth.SKEW5B_32K]
+FULL_IDS = [w.name for w in FULL]
+_route_cache = {}
+
+
+def oracle_route(w, x64):
+    """The oracle's router and selection of every token (cached per workload)."""
+    if w.name not in _route_cache:
+        _route_cache.clear()
+        _route_cache[w.name] = O.route_all(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"],
+                                           x64["w_kn"], w.topk, w.theta, w.eps)
+    return _route_cache[w.name]
+
+
 @pytest.mark.parametrize("w", FULL, ids=FULL_IDS)
 def test_full_router_topk(w):
     x, x64, d = inputs(w)
@@ -107,34 +126,49 @@ def test_full_router_topk(w):
     assert bool(torch.isfinite(logg[~pad.expand_as(ii)]).all())
     assert float(logg[~pad.expand_as(ii)].max()) <= 1e-6
     assert float(torch.where(pad.expand_as(ii), 0.0, logg.exp()).sum(-1).max()) <= 1.0 + 1e-5
-    # sampled rows against the oracle router
-    tok = sample_tokens(w.T, 768, seed=w.cfg_id)
-    r = O.route(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"], w.topk,
-                w.theta, w.eps, tokens=tok)
-    tt = torch.as_tensor(tok, device="cuda")
-    check("q_gate", qg[:, tt], r["qg"], ROUTER_ABS, ROUTER_ABS)
-    check("k_gate", kg[:, tt], r["kg_cur"], ROUTER_ABS, ROUTER_ABS)
-    ok = ~r["near_tie"]
-    gi = idx[:, tt].cpu().numpy()
+    # every row against the oracle: gate vectors, indices (outside near ties),
+    # log-gates, lse
+    ra = oracle_route(w, x64)
+    check("q_gate", qg, ra["qg"], ROUTER_ABS, ROUTER_ABS)
+    check("k_gate", kg, ra["kg"], ROUTER_ABS, ROUTER_ABS)
+    ok = ~ra["near_tie"]
+    print(f"  near-tie rows {int((~ok).sum())} of {ok.size}", flush=True)
     assert ok.mean() > 0.99, "too many near-tie rows"
-    np.testing.assert_array_equal(gi[ok], r["idx"][ok])
-    gl = logg[:, tt].cpu().numpy()
-    fin = np.isfinite(r["logg"]) & ok[..., None]
-    assert np.abs(gl[fin] - r["logg"][fin]).max() < ROUTER_ABS
-    assert np.abs(glse[:, tt].cpu().numpy() - r["lse"]).max() < ROUTER_ABS
+    gi = idx.cpu().numpy()
+    bad = (gi != ra["idx"]).any(-1) & ok
+    assert not bad.any(), f"{int(bad.sum())} rows differ, first at {np.argwhere(bad)[0].tolist()}"
+    gl = logg.cpu().numpy()
+    fin = np.isfinite(ra["logg"]) & ok[..., None]
+    assert np.abs(gl[fin] - ra["logg"][fin]).max() < ROUTER_ABS
+    assert np.abs(glse.cpu().numpy() - ra["lse"]).max() < ROUTER_ABS
 
 
 # --------------------------------------------------- attention forward/backward
 
-ATT = [(synth.PREFILL_8K, 31, False), (synth.TRAIN_32K, 31, True),
-       (synth.SKEW_32K, 15, True), (synth.SKEW_32K, 31, True), (synth.SKEW_32K, 63, True)]
-ATT_IDS = [f"{w.name}_K{K}" for w, K, _ in ATT]
+# (workload, K, backward, selection): "random" = synth.random_selection (the
+# router's structure, no scoring); "router" = the oracle router's own
+# selection, whose locality the shared-direction workload skews
+ATT = [(synth.PREFILL_8K, 31, False, "random"), (synth.TRAIN_32K, 31, True, "random"),
+       (synth.SKEW_32K, 15, True, "random"), (synth.SKEW_32K, 31, True, "random"),
+       (synth.SKEW_32K, 63, True, "random"), (synth.SKEW5B_32K, 31, True, "router")]
+ATT_IDS = [f"{w.name}_K{K}_{sel}" for w, K, _, sel in ATT]
 
 
-@pytest.mark.parametrize("w,K,bwd", ATT, ids=ATT_IDS)
-def test_full_attention(w, K, bwd):
+@pytest.mark.parametrize("w,K,bwd,sel", ATT, ids=ATT_IDS)
+def test_full_attention(w, K, bwd, sel):
+    """Forward (and backward) in the benchmark's launch configuration.  One
+    KV head in full (every query row: o, lse, o_f32, dq, d log g; every key
+    block: dk, dv) and sampled rows of every head, against the oracle; on
+    every row, d log g sums to zero over the selected slots."""
     x, x64, d = inputs(w)
-    idx_c, logg_c = synth.random_selection(w, seed=0, K=K)
+    if sel == "random":
+        idx_c, logg_c = synth.random_selection(w, seed=0, K=K)
+        idx_n, logg_n = idx_c.numpy(), logg_c.double().numpy()
+    else:
+        ra = oracle_route(w, x64)
+        idx_n, logg_n = ra["idx"], ra["logg"]
+        idx_c = torch.from_numpy(idx_n.astype(np.int32))
+        logg_c = torch.from_numpy(logg_n.astype(np.float32))
     idx, logg = idx_c.cuda(), logg_c.cuda()
     sc = 1.0 / math.sqrt(w.D)
     o, lse, o32 = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx, logg, sc, want_f32=True)
@@ -142,39 +176,55 @@ def test_full_attention(w, K, bwd):
         dq, dk, dv, dlogg = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx,
                                                 logg, sc, o_f32=o32)
     torch.cuda.synchronize()
-    idx_n, logg_n = idx_c.numpy(), logg_c.double().numpy()
-    ntok = 1024 if w is synth.TRAIN_32K else 512
-    tok = sample_tokens(w.T, ntok, seed=100 + K)
+    skew = w.skew != "none"
+
+    def lse_check(name, got, ref):
+        # fp32 logits from D-term dot products: rounding grows with the
+        # logits' magnitude (the skewed workloads reach the hundreds):
+        # |err| <= 1e-4 + 2e-5 |lse| (D * 2^-24 = 7.6e-6 relative, 2.6x margin)
+        err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
+        print(f"  {name}: max-abs {err.max():.3e}, max |lse| {np.abs(ref).max():.1f}", flush=True)
+        assert (err <= 1e-4 + 2e-5 * np.abs(ref)).all()
+
+    # one KV head in full
+    kv = K % w.Hkv
+    G = w.G
+    hs = slice(kv * G, (kv + 1) * G)
+    print(f"[{w.name} K={K}] KV head {kv} in full", flush=True)
+    a = O.attn_head(x64["q"], x64["k"], x64["v"], idx_n, logg_n, sc, 0, kv,
+                    dout=x64["dout"] if bwd else None)
+    check(f"o[kv={kv}]", o[0, :, hs], a["o"])
+    check(f"o_f32[kv={kv}]", o32[0, :, hs], a["o"])
+    lse_check(f"lse[kv={kv}]", lse[0, :, hs], a["lse"])
+    if bwd:
+        check(f"dq[kv={kv}]", dq[0, :, hs], a["dq"], rounding_floor=skew)
+        check(f"dlogg[kv={kv}]", dlogg[0, :, kv], a["dlogg"])
+        check(f"dk[kv={kv}]", dk[0, :, kv], a["dk"], rounding_floor=skew)
+        check(f"dv[kv={kv}]", dv[0, :, kv], a["dv"], rounding_floor=skew)
+    # sampled rows of every head
+    tok = sample_tokens(w.T, 256, seed=100 + K)
     tt = torch.as_tensor(tok, device="cuda")
     ro, rl = O.attn_fwd_rows(x64["q"], x64["k"], x64["v"], idx_n, logg_n, sc, tokens=tok)
-    check("o", o[:, tt], ro)
-    check("o_f32", o32[:, tt], ro)
-    # lse (fp32): the logits come from fp32-accumulated dot products over D
-    # terms, whose rounding error scales with the logits' magnitude (which the
-    # skewed workload drives into the hundreds): |err| <= 1e-4 + 2e-5 |lse|
-    # (D * 2^-24 = 7.6e-6 relative, with a 2.6x margin).
-    err = np.abs(lse[:, tt].cpu().numpy().astype(np.float64) - rl)
-    print(f"  lse: max-abs {err.max():.3e}, max |lse| {np.abs(rl).max():.1f}", flush=True)
-    assert (err <= 1e-4 + 2e-5 * np.abs(rl)).all()
+    check("o (sampled rows, all heads)", o[:, tt], ro)
+    check("o_f32 (sampled rows, all heads)", o32[:, tt], ro)
+    lse_check("lse (sampled rows, all heads)", lse[:, tt], rl)
     if not bwd:
         return
     # every row: the log-gate gradient sums to zero over the selected slots
     assert float(dlogg.sum(-1).abs().max()) < 1e-3
     assert bool((dlogg[idx < 0] == 0).all())
-    btok = tok[:: max(1, len(tok) // 256)]
+    btok = tok[::2]
     bt = torch.as_tensor(btok, device="cuda")
     rdq, rdl = O.attn_bwd_rows(x64["q"], x64["k"], x64["v"], x64["dout"], idx_n, logg_n, sc, btok)
-    check("dq", dq[:, bt], rdq)
-    check("dlogg", dlogg[:, bt], rdl)
+    check("dq (sampled rows, all heads)", dq[:, bt], rdq, rounding_floor=skew)
+    check("dlogg (sampled rows, all heads)", dlogg[:, bt], rdl)
     rng = np.random.default_rng(7 + K)
-    blocks = [(0, 0, w.NB - 1), (0, w.Hkv - 1, w.NB - 2), (0, 1, 1)] + [
-        (0, int(rng.integers(w.Hkv)), int(j)) for j in rng.integers(w.NB // 2, w.NB - 2, 3)]
-    for b, kv, j in blocks:
+    for b, kv2, j in [(0, int(rng.integers(w.Hkv)), int(rng.integers(w.NB))) for _ in range(2)]:
         rdk, rdv = O.attn_bwd_block(x64["q"], x64["k"], x64["v"], x64["dout"], idx_n, logg_n,
-                                    sc, b, kv, j)
+                                    sc, b, kv2, j)
         lo, hi = 64 * j, min(64 * j + 64, w.T)
-        check(f"dk[{kv},{j}]", dk[b, lo:hi, kv], rdk)
-        check(f"dv[{kv},{j}]", dv[b, lo:hi, kv], rdv)
+        check(f"dk[{kv2},{j}]", dk[b, lo:hi, kv2], rdk, rounding_floor=skew)
+        check(f"dv[{kv2},{j}]", dv[b, lo:hi, kv2], rdv, rounding_floor=skew)
 
 
 # ------------------------------------------------------------------- decode

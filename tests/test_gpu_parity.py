@@ -4,10 +4,10 @@ Sizes are small enough for the oracle to finish in seconds while spanning
 several 64-token blocks, ragged tails, GQA group sizes 1/2/4/5/8, K = 0 and
 K beyond the number of blocks.  Tolerances: selected block indices
 bit-exact outside near-tie rows (K-th/(K+1)-th gate-logit gap < 1e-5 in
-fp64); bf16 outputs and gradients within 1e-2 max-abs beyond the bf16
+fp64; exact ties go to the lower index and are compared like any other
+row); bf16 outputs and gradients within 1e-2 max-abs beyond the bf16
 representation error of the exact value (half a bf16 ulp of the reference,
-which alone reaches 1.6e-2 for |x| in [4, 8)) and 1e-3 mean-abs beyond the
-mean of those half-ulps (the mean cost of storing the exact values in bf16);
+which alone reaches 1.6e-2 for |x| in [4, 8)) and a raw 1e-3 mean-abs;
 fp32 outputs (log-gate gradient, lse) and router outputs within the
 stated absolute bounds with no allowance.
 """
@@ -80,11 +80,12 @@ def errs(gpu, ref):
 
 
 def assert_close(name, gpu, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    """Max-abs beyond the bf16 rounding of the exact value (a bf16 output
+    cannot be closer than that), raw mean-abs with no allowance."""
     raw, mx, mn = errs(gpu, ref)
-    floor = float(bf16_half_ulp(ref).mean()) if gpu.dtype == torch.bfloat16 else 0.0
-    print(f"  {name}: max-abs {raw:.3e} (beyond bf16 rounding {mx:.3e}) mean-abs {mn:.3e} "
-          f"(bf16 floor {floor:.1e})", flush=True)
-    assert mx <= max_abs and mn <= mean_abs + floor, (name, raw, mx, mn, floor)
+    print(f"  {name}: max-abs {raw:.3e} (beyond bf16 rounding {mx:.3e}) mean-abs {mn:.3e}",
+          flush=True)
+    assert mx <= max_abs and mn <= mean_abs, (name, raw, mx, mn)
 
 
 @pytest.mark.parametrize("w", CASES, ids=IDS)
@@ -243,6 +244,31 @@ def test_gate_score_bwd(w):
         assert torch.equal(out[name], out2[name]), (name, "router backward not repeatable")
 
 
+@pytest.mark.parametrize("w", CASES[:3], ids=IDS[:3])
+def test_gate_score_bwd_nonzero_row_sums(w):
+    """A dlogg whose rows do not sum to zero (e.g. from an extra loss on log
+    g): the library differentiates sum dlogg * s over the selected logits with
+    the row's lse held constant (documented in sas.h), which the oracle's
+    router backward computes with lse_term=False; the binding warns."""
+    P = prepared(w)
+    d = P["dev"]
+    x64 = P["x64"]
+    idx, _ = _oracle_sel(P)
+    rng = np.random.default_rng(17)
+    dl = torch.tensor(np.where(P["r"]["idx"] >= 0, rng.standard_normal(P["r"]["idx"].shape), 0.0),
+                      dtype=torch.float32)
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    with pytest.warns(UserWarning, match="do not sum to zero"):
+        out = sas.gate_score_bwd(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], qg, kg,
+                                 idx, dl.cuda(), w.theta, w.eps)
+    torch.cuda.synchronize()
+    ref = O.router_bwd(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"],
+                       P["r"]["idx"], O.as64(dl), w.theta, w.eps, lse_term=False)
+    for name in ("dq", "dk", "dwq", "dwk", "dw_qn", "dw_kn"):
+        assert_close(name, out[name], ref[name])
+
+
 def test_outputs_stay_in_bounds():
     """NaN canaries after every output buffer stay untouched."""
     w = CASES[1]
@@ -342,9 +368,10 @@ def test_decode_bf16_gate_keys(case):
 def test_decode_paged(case):
     """Paged cache: every (sequence, block) in its own page of a shuffled pool
     (spare pages and every page row past a context filled with NaN, table
-    entries past a sequence's blocks pointing outside the pool): the same
-    arithmetic in the same order as the contiguous cache, so the outputs
-    must be bitwise equal to sas_decode's (which the oracle pins above)."""
+    entries past a sequence's blocks pointing outside the pool), with fp32
+    and bf16 gate keys: indices bit-exact with the oracle outside near ties
+    and outputs within the bound, and, since the arithmetic is the same in the
+    same order, bitwise equal to sas_decode's on the contiguous cache."""
     B, Hq, Hkv, D, dg, K, Lmax, lens = case
     w = synth.Workload("dec", 91, B=B, T=1, Hq=Hq, Hkv=Hkv, D=D, dg=dg, topk=K, kind="decode",
                        Lmin=1, Lmax=Lmax)
@@ -380,6 +407,17 @@ def test_decode_paged(case):
     o_p, idx_p, lg_p = sas.decode_paged(x["q"], x["q_gate"], kp, vp, gp, table.contiguous(),
                                         x["ctx_len"], K, sc)
     torch.cuda.synchronize()
+    # against the oracle directly (not only against the contiguous path)
+    xc = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in x.items()}
+    ref = O.decode(xc["q"], xc["q_gate"], xc["k_cache"], xc["v_cache"], xc["kg_cache"],
+                   xc["ctx_len"], K, sc)
+    ok = ~ref["near_tie"]
+    np.testing.assert_array_equal(idx_p.cpu().numpy()[ok], ref["idx"][ok])
+    fin = np.isfinite(ref["logg"]) & ok[..., None]
+    assert np.abs(lg_p.cpu().numpy()[fin] - ref["logg"][fin]).max() < ROUTER_ABS
+    G = Hq // Hkv
+    okh = np.repeat(ok, G, axis=1)
+    assert_close("o (paged)", o_p[torch.from_numpy(okh).cuda()], ref["o"][okh])
     assert torch.equal(idx_p, idx_c)
     assert torch.equal(lg_p.nan_to_num(), lg_c.nan_to_num())
     assert torch.equal(o_p.view(torch.int16), o_c.view(torch.int16))
@@ -389,6 +427,12 @@ def test_decode_paged(case):
     o_p, idx_p, lg_p = sas.decode_paged(x["q"], x["q_gate"], kp, vp, gp.to(torch.bfloat16),
                                         table.contiguous(), x["ctx_len"], K, sc)
     torch.cuda.synchronize()
+    ref = O.decode(xc["q"], xc["q_gate"], xc["k_cache"], xc["v_cache"],
+                   xc["kg_cache"].to(torch.bfloat16).float(), xc["ctx_len"], K, sc)
+    ok = ~ref["near_tie"]
+    np.testing.assert_array_equal(idx_p.cpu().numpy()[ok], ref["idx"][ok])
+    okh = np.repeat(ok, G, axis=1)
+    assert_close("o (paged, bf16 keys)", o_p[torch.from_numpy(okh).cuda()], ref["o"][okh])
     assert torch.equal(idx_p, idx_c)
     assert torch.equal(lg_p.nan_to_num(), lg_c.nan_to_num())
     assert torch.equal(o_p.view(torch.int16), o_c.view(torch.int16))
@@ -474,7 +518,18 @@ def test_decode_matches_prefill_row():
         qgd[bi] = qg[0, Lb - 1]
     od, idd, _ = sas.decode(qd, qgd, kc, vc, kgc, L.cuda(), w.topk, P["scale"])
     torch.cuda.synchronize()
+    # prefill scores come from fp32 MFMA tiles, decode scores from a differently
+    # ordered fp32 reduction: rows the oracle marks near-tie (K-th/(K+1)-th gap
+    # < 1e-5) may legitimately differ and are left out, as in the other tests
+    G = w.Hq // w.Hkv
+    checked = 0
     for bi, Lb in enumerate(L.tolist()):
-        assert torch.equal(idd[bi], idx[0, Lb - 1])
-        diff = (od[bi].float() - o[0, Lb - 1].float()).abs().max().item()
-        assert diff <= 1e-2, diff
+        for kv in range(w.Hkv):
+            if P["r"]["near_tie"][0, Lb - 1, kv]:
+                continue
+            checked += 1
+            assert torch.equal(idd[bi, kv], idx[0, Lb - 1, kv])
+            hs = slice(kv * G, (kv + 1) * G)
+            diff = (od[bi, hs].float() - o[0, Lb - 1, hs].float()).abs().max().item()
+            assert diff <= 1e-2, diff
+    assert checked >= len(L) * w.Hkv - 1

@@ -465,6 +465,40 @@ def test_router_backward_finite_differences(name):
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, i, fd, an)
 
 
+def _frozen_logit_loss(x, K, idx, dlogg, theta=1e4, eps=1e-6):
+    """L = sum dlogg * s over the fixed selected slots (no lse term)."""
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], K, theta, eps)
+    assert np.array_equal(r["idx"], idx), "selection moved under the perturbation"
+    s = np.take_along_axis(r["s"], np.maximum(idx, 0), axis=-1)
+    return float(np.where(idx >= 0, dlogg * s, 0.0).sum())
+
+
+@pytest.mark.parametrize("name", ["q", "k", "wq", "wk"])
+def test_router_backward_without_lse_term_finite_differences(name):
+    """lse_term=False: the gradient of sum dlogg * s_selected (what the
+    library's router backward computes for any dlogg) vs central differences,
+    with a dlogg whose rows do not sum to zero."""
+    x, K = _router_case(seed=15)
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], K, 1e4, 1e-6)
+    rng = np.random.default_rng(16)
+    dlogg = rng.standard_normal(r["idx"].shape)
+    g = O.router_bwd(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], r["idx"], dlogg,
+                     1e4, 1e-6, lse_term=False)
+    grad = {"q": g["dq"], "k": g["dk"], "wq": g["dwq"], "wk": g["dwk"]}[name]
+    h = 1e-6
+    flat = x[name].reshape(-1)
+    for i in rng.choice(flat.size, size=min(10, flat.size), replace=False):
+        old = flat[i]
+        flat[i] = old + h
+        lp = _frozen_logit_loss(x, K, r["idx"], dlogg)
+        flat[i] = old - h
+        lm = _frozen_logit_loss(x, K, r["idx"], dlogg)
+        flat[i] = old
+        fd = (lp - lm) / (2 * h)
+        an = grad.reshape(-1)[i]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, i, fd, an)
+
+
 def test_router_backward_zero_sum_dlogg_reaches_selected_logits_only():
     """With dlogg summing to zero over each row's valid slots (what the gated
     attention produces), ds is dlogg on the selected blocks and zero elsewhere."""
@@ -493,3 +527,78 @@ def test_router_backward_pooling_ties_go_to_first_row():
     _, amax, amin, n = O._pool_with_args(k)
     assert amax[0, 2, 0].tolist() == [0, 0] and amin[0, 2, 0].tolist() == [2, 1]
     assert n.tolist() == [1, 2, 3]
+
+
+# ------------------------------------------------ whole-sequence evaluations
+
+def test_select_rows_matches_brute_force_with_ties():
+    """The many-row selection against the subset brute force, on integer
+    scores full of exact ties (ties -> lower index), and its K-th gap."""
+    rng = np.random.default_rng(11)
+    for _ in range(60):
+        c = int(rng.integers(0, 9))
+        K = int(rng.integers(0, 6))
+        s = rng.integers(-2, 3, size=(7, c)).astype(float)
+        sel, gap = O.select_rows(s, K)
+        for r in range(7):
+            assert list(sel[r]) == O.brute_force_topk(list(s[r]), K)
+            full = np.concatenate([s[r], [0.0]])
+            assert gap[r] == O.kth_gap(full, K)
+            if c > K >= 1:
+                srt = sorted(s[r], reverse=True)
+                assert gap[r] == srt[K - 1] - srt[K]
+
+
+@pytest.mark.parametrize("shape", [dict(T=1000, Hq=8, Hkv=2, D=16, dg=8, K=7),
+                                   dict(T=700, Hq=10, Hkv=2, D=16, dg=8, K=5),
+                                   dict(T=300, B=2, Hq=2, Hkv=2, D=16, dg=8, K=2),
+                                   dict(T=400, Hq=4, Hkv=2, D=16, dg=8, K=0),
+                                   dict(T=600, Hq=4, Hkv=1, D=16, dg=8, K=20),
+                                   dict(T=50, Hq=4, Hkv=1, D=16, dg=8, K=3)])
+def test_route_all_matches_route(shape):
+    """route_all (every token at once) equals route (token by token)."""
+    K = shape.pop("K")
+    w, x = small_case(K=K, bf16=True, **shape)
+    args = (x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], w.topk, w.theta, w.eps)
+    r, ra = O.route(*args), O.route_all(*args)
+    np.testing.assert_array_equal(ra["idx"], r["idx"])
+    np.testing.assert_array_equal(np.isinf(ra["logg"]), np.isinf(r["logg"]))
+    fin = np.isfinite(r["logg"])
+    assert np.abs(ra["logg"][fin] - r["logg"][fin]).max() < 1e-12
+    assert np.abs(ra["lse"] - r["lse"]).max() < 1e-12
+    assert np.abs(ra["qg"] - r["qg"]).max() < 1e-12
+    assert np.abs(ra["kg"] - r["kg_cur"]).max() < 1e-12
+    np.testing.assert_array_equal(np.isinf(ra["gap"]), np.isinf(r["gap"]))
+    g = np.isfinite(r["gap"])
+    assert not g.any() or np.abs(ra["gap"][g] - r["gap"][g]).max() < 1e-12
+    np.testing.assert_array_equal(ra["near_tie"], r["near_tie"])
+
+
+@pytest.mark.parametrize("shape", [dict(T=1000, Hq=8, Hkv=2, D=16, dg=8, K=7),
+                                   dict(T=700, Hq=10, Hkv=2, D=16, dg=8, K=5),
+                                   dict(T=300, B=2, Hq=2, Hkv=2, D=16, dg=8, K=2),
+                                   dict(T=130, Hq=4, Hkv=1, D=16, dg=8, K=0)])
+def test_attn_head_matches_row_form_and_sdpa(shape):
+    """attn_head (all rows of one head, keys grouped per block for dk/dv)
+    equals attn_bwd (row by row), and its o equals SDPA with the additive
+    block bias (-inf on keys the row did not select)."""
+    K = shape.pop("K")
+    w, x = small_case(K=K, **shape)
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], w.topk, w.theta, w.eps)
+    sc = 1.0 / math.sqrt(w.D)
+    g = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], r["idx"], r["logg"], sc)
+    bias = O.dense_bias(r["idx"], r["logg"], w.T)               # [B,Hkv,T,T]
+    G = w.G
+    for b in range(w.B):
+        for kv in range(w.Hkv):
+            a = O.attn_head(x["q"], x["k"], x["v"], r["idx"], r["logg"], sc, b, kv,
+                            dout=x["dout"], batch=7)
+            hs = slice(kv * G, (kv + 1) * G)
+            for name, ref in (("o", g["o"][b, :, hs]), ("lse", g["lse"][b, :, hs]),
+                              ("dq", g["dq"][b, :, hs]), ("dlogg", g["dlogg"][b, :, kv]),
+                              ("dk", g["dk"][b, :, kv]), ("dv", g["dv"][b, :, kv])):
+                assert np.abs(a[name] - ref).max() < 1e-11, name
+            mask = torch.tensor(bias[b:b + 1, kv:kv + 1])
+            ref_o = sdpa64(x["q"][b:b + 1, :, hs], x["k"][b:b + 1, :, kv:kv + 1],
+                           x["v"][b:b + 1, :, kv:kv + 1], mask=mask, scale=sc)
+            assert np.abs(a["o"] - ref_o[0]).max() < 1e-11
