@@ -23,7 +23,7 @@ __all__ = [
     "sparse_attn_bwd", "decode", "decode_paged", "decode_gate_key", "budget_to_topk",
     "EXPORTED_SYMBOLS",
     "set_timing_events",
-    "take_device_fault", "gate_score_bwd",
+    "take_device_fault", "gate_score_bwd", "decode_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
     "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
     "sas_decode", "sas_set_timing_events", "sas_take_device_fault", "sas_gate_score_bwd",
-    "sas_decode_paged", "sas_decode_gate_key",
+    "sas_decode_paged", "sas_decode_gate_key", "sas_decode_noalloc",
 )
 
 
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         + [P, S, P])
     lib.sas_decode.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 6 + [F32] + [P] * 3
                                + [P, S, P])
+    lib.sas_decode_noalloc.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 6 + [F32] + [P] * 3
+                                       + [P])
     lib.sas_decode_paged.argtypes = ([ctypes.POINTER(DecodeDims)] + [P] * 5 + [I32] + [P] * 2
                                      + [F32] + [P] * 3 + [P, S, P])
     lib.sas_decode_gate_key.argtypes = ([ctypes.POINTER(DecodeDims)] + [P, P, I32, P, P]
@@ -96,6 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sas_take_device_fault.argtypes = [ctypes.POINTER(ctypes.c_uint)]
     for fn in ("sas_gate_score", "sas_gate_score_bwd", "sas_topk_blocks", "sas_sparse_attn_fwd",
                "sas_sparse_attn_bwd", "sas_decode", "sas_decode_paged", "sas_decode_gate_key",
+               "sas_decode_noalloc",
                "sas_set_timing_events",
                "sas_take_device_fault"):
         getattr(lib, fn).restype = I32
@@ -402,6 +405,43 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int, scale: flo
     _check(lib.sas_decode(ctypes.byref(d), _ptr(q), _ptr(q_gate), _ptr(k_cache), _ptr(v_cache),
                           _ptr(kg_cache), _ptr(ctx_len), ctypes.c_float(scale), _ptr(o), _ptr(idx),
                           _ptr(logg), _ptr(ws), ws.numel() if ws is not None else 0, _stream(dev)))
+    return o, idx, logg
+
+
+def decode_noalloc(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int,
+                   scale: float | None = None, apply_gate: bool = True, out=None):
+    """decode() without a workspace: the library's fixed per-device scratch
+    (see sas_decode_noalloc in sas.h; calls on one GPU must not overlap).
+    With out=(o, idx, logg) preallocated, nothing is allocated at all.
+    Returns (o, idx, logg)."""
+    lib = load_library()
+    dev = _device_of(q)
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    dg = q_gate.shape[-1]
+    NBmax = -(-Lmax // 64)
+    S = topk + 1
+    _req(q, "q", torch.bfloat16, (B, Hq, D), dev)
+    _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
+    _req(k_cache, "k_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
+    _req(v_cache, "v_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
+    kg_bf16 = kg_cache.dtype == torch.bfloat16
+    _req(kg_cache, "kg_cache", torch.bfloat16 if kg_bf16 else torch.float32, (B, Hkv, NBmax, dg),
+         dev)
+    _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0,
+                   1 if kg_bf16 else 0)
+    if out is None:
+        o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev)
+        logg = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+    else:
+        o, idx, logg = out
+    _check(lib.sas_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(q_gate), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(kg_cache), _ptr(ctx_len),
+                                  ctypes.c_float(scale), _ptr(o), _ptr(idx), _ptr(logg),
+                                  _stream(dev)))
     return o, idx, logg
 
 

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/sas.h"
@@ -192,6 +193,42 @@ sas_status check_decode_dims(const sas_decode_dims* d) {
     return fail(SAS_ERR_INVALID, "apply_gate must be 0 or 1");
   if (d->kg_dtype != 0 && d->kg_dtype != 1)
     return fail(SAS_ERR_INVALID, "kg_dtype must be 0 (fp32) or 1 (bf16)");
+  return SAS_OK;
+}
+
+}  // namespace
+
+// Device scratch of sas_decode_noalloc (for callers that cannot allocate):
+// one fixed-size array per device, held until the process ends.  Host code
+// never uses the array's name as an address: its device address on each GPU
+// comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device (first call per device
+// looks it up with that device current).
+sas_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(SAS_ERR_UNSUPPORTED, "device %d: at most %d devices are supported", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SAS_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return SAS_OK;
 }
 
@@ -402,22 +439,32 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
                     "sas_sparse_attn_bwd launch");
 }
 
-sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
-                      const uint16_t* k_cache, const uint16_t* v_cache,
-                      const float* kg_cache, const int32_t* ctx_len, float scale,
-                      uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
-                      size_t ws_bytes, void* stream) {
-  sas_status st = check_decode_dims(d);
-  if (st) return st;
+}  // extern "C"
+
+namespace {
+
+// Shared by sas_decode and sas_decode_noalloc: validation of the tensor
+// arguments, then the launch over a workspace at `base` of at least
+// dec_ws(d).total bytes.
+sas_status decode_checked(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                          const uint16_t* k_cache, const uint16_t* v_cache,
+                          const float* kg_cache, const int32_t* ctx_len, float scale,
+                          uint16_t* o, int32_t* idx_out, float* logg_out) {
   REQ_PTR(q); REQ_PTR(q_gate); REQ_PTR(k_cache); REQ_PTR(v_cache); REQ_PTR(kg_cache);
   REQ_PTR(ctx_len); REQ_PTR(o);
   if (idx_out && !aligned16(idx_out)) return fail(SAS_ERR_INVALID, "idx_out is not 16-byte aligned");
   if (logg_out && !aligned16(logg_out))
     return fail(SAS_ERR_INVALID, "logg_out is not 16-byte aligned");
   if (!std::isfinite(scale)) return fail(SAS_ERR_INVALID, "scale must be finite");
+  return SAS_OK;
+}
+
+sas_status decode_launch(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                         const uint16_t* k_cache, const uint16_t* v_cache,
+                         const float* kg_cache, const int32_t* ctx_len, float scale,
+                         uint16_t* o, int32_t* idx_out, float* logg_out, char* base,
+                         const char* what, hipStream_t stream) {
   const DecWs w = dec_ws(d);
-  if ((st = check_ws(ws, ws_bytes, w.total))) return st;
-  char* base = static_cast<char*>(ws);
   sas::DecodeParams p{};
   p.q = q; p.q_gate = q_gate; p.k_cache = k_cache; p.v_cache = v_cache; p.kg_cache = kg_cache;
   p.ctx_len = ctx_len; p.o = o; p.idx_out = idx_out; p.logg_out = logg_out;
@@ -430,7 +477,48 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
   p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw; p.kg_bf16 = d->kg_dtype;
   p.scale_log2 = scale * sas::kLog2e;
   g_err.clear();
-  return hip_status(sas::launch_decode(p, static_cast<hipStream_t>(stream)), "sas_decode launch");
+  return hip_status(sas::launch_decode(p, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const float* kg_cache, const int32_t* ctx_len, float scale,
+                      uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  sas_status st = check_decode_dims(d);
+  if (st) return st;
+  if ((st = decode_checked(d, q, q_gate, k_cache, v_cache, kg_cache, ctx_len, scale, o, idx_out,
+                           logg_out)))
+    return st;
+  if ((st = check_ws(ws, ws_bytes, dec_ws(d).total))) return st;
+  return decode_launch(d, q, q_gate, k_cache, v_cache, kg_cache, ctx_len, scale, o, idx_out,
+                       logg_out, static_cast<char*>(ws), "sas_decode launch",
+                       static_cast<hipStream_t>(stream));
+}
+
+sas_status sas_decode_noalloc(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                              const uint16_t* k_cache, const uint16_t* v_cache,
+                              const float* kg_cache, const int32_t* ctx_len, float scale,
+                              uint16_t* o, int32_t* idx_out, float* logg_out, void* stream) {
+  sas_status st = check_decode_dims(d);
+  if (st) return st;
+  if ((st = decode_checked(d, q, q_gate, k_cache, v_cache, kg_cache, ctx_len, scale, o, idx_out,
+                           logg_out)))
+    return st;
+  const size_t need = dec_ws(d).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(SAS_ERR_WORKSPACE,
+                "sas_decode_noalloc: these dimensions need %zu bytes of scratch, more than the "
+                "fixed %zu; call sas_decode with a workspace instead", need, kNoAllocScratchBytes);
+  void* base = nullptr;
+  if ((st = scratch_address(&base))) return st;
+  return decode_launch(d, q, q_gate, k_cache, v_cache, kg_cache, ctx_len, scale, o, idx_out,
+                       logg_out, static_cast<char*>(base), "sas_decode_noalloc launch",
+                       static_cast<hipStream_t>(stream));
 }
 
 sas_status sas_decode_gate_key(const sas_decode_dims* d, const uint16_t* k_cache,

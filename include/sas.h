@@ -19,7 +19,8 @@
  *     asynchronously; the library never synchronises the device.
  *   - The library allocates no device memory.  Calls that need scratch space
  *     take a caller-provided workspace `ws` of at least the size reported by
- *     sas_workspace_size() / sas_decode_workspace_size().
+ *     sas_workspace_size() / sas_decode_workspace_size(); the one exception,
+ *     sas_decode_noalloc, uses a fixed static scratch array of the library.
  *   - All arguments are validated before anything is launched.  On any error
  *     the call returns a non-zero sas_status, writes nothing and records a
  *     message readable through sas_last_error() (thread-local).
@@ -288,6 +289,26 @@ sas_status sas_decode(const sas_decode_dims* d, const uint16_t* q, const float* 
                       const float* kg_cache, const int32_t* ctx_len, float scale,
                       uint16_t* o, int32_t* idx_out, float* logg_out, void* ws,
                       size_t ws_bytes, void* stream);
+
+/*
+ * sas_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and outputs as sas_decode, with the workspace
+ * taken from a fixed 16 MiB scratch array that the library holds on each GPU
+ * it runs on until the process ends.  No workspace argument; nothing is
+ * allocated.  The scratch is enough for the dimensions of a serving batch
+ * (for example B = 256 sequences x 8 KV heads at Lmax = 131072); dimensions
+ * whose sas_decode_workspace_size exceeds 16 MiB are rejected with
+ * SAS_ERR_WORKSPACE before anything is launched.  Every call on one GPU uses
+ * the same scratch, which keeps the previous call's contents (nothing in it
+ * needs to start at zero): calls that can overlap on one GPU (different
+ * streams, or threads) race and must be ordered by the caller.  Call with the
+ * device that owns the buffers current.
+ */
+sas_status sas_decode_noalloc(const sas_decode_dims* d, const uint16_t* q, const float* q_gate,
+                              const uint16_t* k_cache, const uint16_t* v_cache,
+                              const float* kg_cache, const int32_t* ctx_len, float scale,
+                              uint16_t* o, int32_t* idx_out, float* logg_out, void* stream);
 
 /*
  * Gate key of each sequence's current block for decode (model card,
