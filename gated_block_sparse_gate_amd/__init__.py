@@ -30,6 +30,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsas.so")
 
 SAS_OK, SAS_ERR_INVALID, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
+FLAG_GATE_PER_QUERY_HEAD = 1
 OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD, OP_GATE_BWD = range(5)
 
 EXPORTED_SYMBOLS = (
@@ -58,7 +59,8 @@ class DecodeDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("dg", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("Lmax", ctypes.c_int32), ("NBmax", ctypes.c_int32),
-                ("apply_gate", ctypes.c_int32), ("kg_dtype", ctypes.c_int32)]
+                ("apply_gate", ctypes.c_int32), ("kg_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -115,8 +117,19 @@ def _check(st: int):
         raise SasError(st, load_library().sas_last_error().decode())
 
 
-def make_dims(B, T, Hq, Hkv, D, dg, topk, theta=1.0e6, eps=1.0e-6, block=64) -> Dims:
-    return Dims(B, T, Hq, Hkv, D, dg, block, topk, float(theta), float(eps), 0)
+def make_dims(B, T, Hq, Hkv, D, dg, topk, theta=1.0e6, eps=1.0e-6, block=64, flags=0) -> Dims:
+    return Dims(B, T, Hq, Hkv, D, dg, block, topk, float(theta), float(eps), flags)
+
+
+def _sel_flags(Hs, Hq, Hkv, what):
+    """Gate mode from the number of selection heads of a gate-side tensor:
+    Hkv (one gate per KV head) or Hq (one gate per query head)."""
+    if Hs == Hkv:
+        return 0
+    if Hs == Hq:
+        return FLAG_GATE_PER_QUERY_HEAD
+    raise ValueError(f"{what}: {Hs} gate heads; expected Hkv = {Hkv} (one gate per KV head) "
+                     f"or Hq = {Hq} (one gate per query head)")
 
 
 def workspace_size(op: int, d: Dims) -> int:
@@ -199,26 +212,29 @@ def _device_of(t):
 
 
 def gate_score(q, k, wq, wk, w_qn, w_kn, topk: int, theta: float = 1.0e6, eps: float = 1.0e-6,
-               q_gate=None, k_gate=None, workspace=None):
-    """Router: returns (q_gate, k_gate) fp32 [B,T,Hkv,dg]."""
+               q_gate=None, k_gate=None, workspace=None, per_query_head: bool = False):
+    """Router: returns (q_gate [B,T,Hs,dg], k_gate [B,T,Hkv,dg]) fp32, with
+    Hs = Hkv (wq [Hkv,G*D,dg]) or, per_query_head, Hs = Hq (wq [Hq,D,dg])."""
     lib = load_library()
     dev = _device_of(q)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     dg = wq.shape[2]
     G = Hq // Hkv
+    Hs, Gs = (Hq, 1) if per_query_head else (Hkv, G)
     _req(q, "q", torch.bfloat16, (B, T, Hq, D), dev)
     _req(k, "k", torch.bfloat16, (B, T, Hkv, D), dev)
-    _req(wq, "wq", torch.bfloat16, (Hkv, G * D, dg), dev)
+    _req(wq, "wq", torch.bfloat16, (Hs, Gs * D, dg), dev)
     _req(wk, "wk", torch.bfloat16, (Hkv, 3 * D, dg), dev)
     _req(w_qn, "w_qn", torch.float32, (dg,), dev)
     _req(w_kn, "w_kn", torch.float32, (dg,), dev)
-    d = make_dims(B, T, Hq, Hkv, D, dg, topk, theta, eps)
+    d = make_dims(B, T, Hq, Hkv, D, dg, topk, theta, eps,
+                  flags=FLAG_GATE_PER_QUERY_HEAD if per_query_head else 0)
     if q_gate is None:
-        q_gate = torch.empty((B, T, Hkv, dg), dtype=torch.float32, device=dev)
+        q_gate = torch.empty((B, T, Hs, dg), dtype=torch.float32, device=dev)
     if k_gate is None:
         k_gate = torch.empty((B, T, Hkv, dg), dtype=torch.float32, device=dev)
-    _req(q_gate, "q_gate", torch.float32, (B, T, Hkv, dg), dev)
+    _req(q_gate, "q_gate", torch.float32, (B, T, Hs, dg), dev)
     _req(k_gate, "k_gate", torch.float32, (B, T, Hkv, dg), dev)
     nws = workspace_size(OP_GATE_SCORE, d)
     ws = workspace if workspace is not None else _ws(nws, dev)
@@ -280,22 +296,26 @@ def gate_score_bwd(q, k, wq, wk, w_qn, w_kn, q_gate, k_gate, idx, dlogg, theta: 
 
 def topk_blocks(q_gate, k_gate, topk: int, Hq: int, D: int, want_probs: bool = False,
                 out=None):
-    """Candidate softmax + Top-K: returns (idx, logg, gate_lse, gate_probs or None)."""
+    """Candidate softmax + Top-K: returns (idx, logg, gate_lse, gate_probs or None),
+    per selection head (q_gate [B,T,Hs,dg] with Hs = Hkv, or Hq for one gate
+    per query head; k_gate [B,T,Hkv,dg])."""
     lib = load_library()
     dev = _device_of(q_gate)
-    B, T, Hkv, dg = q_gate.shape
+    B, T, Hs, dg = q_gate.shape
+    Hkv = k_gate.shape[2]
     S = topk + 1
     NB = -(-T // 64)
-    _req(q_gate, "q_gate", torch.float32, (B, T, Hkv, dg), dev)
+    flags = _sel_flags(Hs, Hq, Hkv, "q_gate")
+    _req(q_gate, "q_gate", torch.float32, (B, T, Hs, dg), dev)
     _req(k_gate, "k_gate", torch.float32, (B, T, Hkv, dg), dev)
-    d = make_dims(B, T, Hq, Hkv, D, dg, topk)
+    d = make_dims(B, T, Hq, Hkv, D, dg, topk, flags=flags)
     if out is None:
-        idx = torch.empty((B, T, Hkv, S), dtype=torch.int32, device=dev)
-        logg = torch.empty((B, T, Hkv, S), dtype=torch.float32, device=dev)
-        lse = torch.empty((B, T, Hkv), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, T, Hs, S), dtype=torch.int32, device=dev)
+        logg = torch.empty((B, T, Hs, S), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, T, Hs), dtype=torch.float32, device=dev)
     else:
         idx, logg, lse = out
-    probs = torch.empty((B, T, Hkv, NB), dtype=torch.float32, device=dev) if want_probs else None
+    probs = torch.empty((B, T, Hs, NB), dtype=torch.float32, device=dev) if want_probs else None
     _check(lib.sas_topk_blocks(ctypes.byref(d), _ptr(q_gate), _ptr(k_gate), _ptr(idx), _ptr(logg),
                                _ptr(lse), _ptr(probs), None, 0, _stream(dev)))
     return idx, logg, lse, probs
@@ -310,14 +330,15 @@ def sparse_attn_fwd(q, k, v, idx, logg, scale: float | None = None, o=None, lse=
     dev = _device_of(q)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    S = idx.shape[-1]
+    Hs, S = idx.shape[2], idx.shape[-1]
+    flags = _sel_flags(Hs, Hq, Hkv, "idx")
     _req(q, "q", torch.bfloat16, (B, T, Hq, D), dev)
     _req(k, "k", torch.bfloat16, (B, T, Hkv, D), dev)
     _req(v, "v", torch.bfloat16, (B, T, Hkv, D), dev)
-    _req(idx, "idx", torch.int32, (B, T, Hkv, S), dev)
-    _req(logg, "logg", torch.float32, (B, T, Hkv, S), dev)
+    _req(idx, "idx", torch.int32, (B, T, Hs, S), dev)
+    _req(logg, "logg", torch.float32, (B, T, Hs, S), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    d = make_dims(B, T, Hq, Hkv, D, 128, S - 1)
+    d = make_dims(B, T, Hq, Hkv, D, 128, S - 1, flags=flags)
     if o is None:
         o = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=dev)
     if lse is None:
@@ -343,23 +364,24 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, idx, logg, scale: float | None = None
     dev = _device_of(q)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    S = idx.shape[-1]
+    Hs, S = idx.shape[2], idx.shape[-1]
+    flags = _sel_flags(Hs, Hq, Hkv, "idx")
     for t, n, dt, sh in ((q, "q", torch.bfloat16, (B, T, Hq, D)), (k, "k", torch.bfloat16, (B, T, Hkv, D)),
                          (v, "v", torch.bfloat16, (B, T, Hkv, D)), (o, "o", torch.bfloat16, (B, T, Hq, D)),
                          (dout, "dout", torch.bfloat16, (B, T, Hq, D)),
                          (lse, "lse", torch.float32, (B, T, Hq)),
-                         (idx, "idx", torch.int32, (B, T, Hkv, S)),
-                         (logg, "logg", torch.float32, (B, T, Hkv, S))):
+                         (idx, "idx", torch.int32, (B, T, Hs, S)),
+                         (logg, "logg", torch.float32, (B, T, Hs, S))):
         _req(t, n, dt, sh, dev)
     if o_f32 is not None:
         _req(o_f32, "o_f32", torch.float32, (B, T, Hq, D), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    d = make_dims(B, T, Hq, Hkv, D, 128, S - 1)
+    d = make_dims(B, T, Hq, Hkv, D, 128, S - 1, flags=flags)
     if out is None:
         dq = torch.empty_like(q)
         dk = torch.empty_like(k)
         dv = torch.empty_like(v)
-        dlogg = torch.empty((B, T, Hkv, S), dtype=torch.float32, device=dev)
+        dlogg = torch.empty((B, T, Hs, S), dtype=torch.float32, device=dev)
     else:
         dq, dk, dv, dlogg = out
     nws = workspace_size(OP_BWD, d)
@@ -384,7 +406,9 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int, scale: flo
     NBmax = -(-Lmax // 64)
     S = topk + 1
     _req(q, "q", torch.bfloat16, (B, Hq, D), dev)
-    _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
+    Hs = q_gate.shape[1]
+    flags = _sel_flags(Hs, Hq, Hkv, "q_gate")
+    _req(q_gate, "q_gate", torch.float32, (B, Hs, dg), dev)
     _req(k_cache, "k_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
     _req(v_cache, "v_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
     kg_bf16 = kg_cache.dtype == torch.bfloat16
@@ -393,11 +417,11 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int, scale: flo
     _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0,
-                   1 if kg_bf16 else 0)
+                   1 if kg_bf16 else 0, flags)
     if out is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev) if want_idx else None
-        logg = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev) if want_idx else None
+        idx = torch.empty((B, Hs, S), dtype=torch.int32, device=dev) if want_idx else None
+        logg = torch.empty((B, Hs, S), dtype=torch.float32, device=dev) if want_idx else None
     else:
         o, idx, logg = out
     nws = decode_workspace_size(d)
@@ -422,7 +446,9 @@ def decode_noalloc(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int,
     NBmax = -(-Lmax // 64)
     S = topk + 1
     _req(q, "q", torch.bfloat16, (B, Hq, D), dev)
-    _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
+    Hs = q_gate.shape[1]
+    flags = _sel_flags(Hs, Hq, Hkv, "q_gate")
+    _req(q_gate, "q_gate", torch.float32, (B, Hs, dg), dev)
     _req(k_cache, "k_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
     _req(v_cache, "v_cache", torch.bfloat16, (B, Hkv, Lmax, D), dev)
     kg_bf16 = kg_cache.dtype == torch.bfloat16
@@ -431,11 +457,11 @@ def decode_noalloc(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, topk: int,
     _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0,
-                   1 if kg_bf16 else 0)
+                   1 if kg_bf16 else 0, flags)
     if out is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev)
-        logg = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Hs, S), dtype=torch.int32, device=dev)
+        logg = torch.empty((B, Hs, S), dtype=torch.float32, device=dev)
     else:
         o, idx, logg = out
     _check(lib.sas_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(q_gate), _ptr(k_cache),
@@ -462,7 +488,9 @@ def decode_paged(q, q_gate, k_pages, v_pages, kg_pages, block_table, ctx_len, to
     Lmax = 64 * NBmax
     S = topk + 1
     _req(q, "q", torch.bfloat16, (B, Hq, D), dev)
-    _req(q_gate, "q_gate", torch.float32, (B, Hkv, dg), dev)
+    Hs = q_gate.shape[1]
+    flags = _sel_flags(Hs, Hq, Hkv, "q_gate")
+    _req(q_gate, "q_gate", torch.float32, (B, Hs, dg), dev)
     _req(k_pages, "k_pages", torch.bfloat16, (P, Hkv, 64, D), dev)
     _req(v_pages, "v_pages", torch.bfloat16, (P, Hkv, 64, D), dev)
     kg_bf16 = kg_pages.dtype == torch.bfloat16
@@ -471,11 +499,11 @@ def decode_paged(q, q_gate, k_pages, v_pages, kg_pages, block_table, ctx_len, to
     _req(ctx_len, "ctx_len", torch.int32, (B,), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     d = DecodeDims(B, Hq, Hkv, D, dg, 64, topk, Lmax, NBmax, 1 if apply_gate else 0,
-                   1 if kg_bf16 else 0)
+                   1 if kg_bf16 else 0, flags)
     if out is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        idx = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev) if want_idx else None
-        logg = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev) if want_idx else None
+        idx = torch.empty((B, Hs, S), dtype=torch.int32, device=dev) if want_idx else None
+        logg = torch.empty((B, Hs, S), dtype=torch.float32, device=dev) if want_idx else None
     else:
         o, idx, logg = out
     nws = decode_workspace_size(d)

@@ -3,18 +3,22 @@
 //
 //   Delta = rowsum(dO * O);  P = exp(scale q.k + logg - lse);  dS = P (dO.v - Delta)
 //   dq = scale sum dS k;  dk = scale sum dS q;  dv = sum P dO;
-//   dlogg[t, slot] = sum over the group's G heads and the slot block's keys of dS.
+//   dlogg[t, sg, slot] = sum over the Gs query heads of selection head sg
+//   and the slot block's keys of dS (sg: a KV head's gate shared by its G
+//   heads, Gs = G; or one query head's own gate, Gs = 1).
 //
 // Kernels (all deterministic, no floating-point atomics):
 //   delta      : Delta per query row.
-//   csr_*      : for every (b, kappa, key block j) the list of (token, slot)
-//                that selected j, in ascending token order (counting sort
-//                with per-(query block, key block) offsets).
+//   csr_*      : for every (b, selection head sg, key block j) the list of
+//                (token, slot) that selected j, in ascending token order
+//                (counting sort with per-(query block, key block) offsets).
 //   dkdv       : KV-block stationary.  One workgroup per (b, kappa, j); wave w
 //                owns keys 16w..16w+15 and keeps dK, dV for them in registers.
-//                The selecting rows are streamed as compacted 32-row tiles
-//                (two tiles of floor(16/G) tokens x G heads), so no MFMA row
-//                is wasted on a query that did not select the block.
+//                The rows that selected the block (the lists of every
+//                selection head of kappa, one after the other) are streamed
+//                as compacted 32-row tiles (two tiles of floor(16/Gs) entries
+//                x Gs heads), so no MFMA row is wasted on a query that did not
+//                select the block.
 //   dq         : query-block stationary, same walk as the forward; also
 //                produces dlogg (each (t, j) pair is visited exactly once).
 #include "bwd_index.h"
@@ -52,13 +56,14 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const
   if (part == 0 && row < nrows) delta[row] = acc;
 }
 
-// Per (b, kappa, query block c): which of the 64 tokens selected each block j.
+// Per (b, selection head sg, query block c): which of the 64 tokens selected
+// each block j.
 __device__ __forceinline__ void build_token_masks(const BwdParams& p, unsigned long long* mask,
-                                                  int b, int kv, int c, int ntok) {
-  const size_t rowbase = (static_cast<size_t>(b) * p.T + c * 64) * p.Hkv + kv;
+                                                  int b, int sg, int c, int ntok) {
+  const size_t rowbase = (static_cast<size_t>(b) * p.T + c * 64) * p.Hs + sg;
   for (int e = threadIdx.x; e < ntok * p.S; e += blockDim.x) {
     const int tl = e / p.S, s = e - tl * p.S;
-    const int j = p.idx[(rowbase + static_cast<size_t>(tl) * p.Hkv) * p.S + s];
+    const int j = p.idx[(rowbase + static_cast<size_t>(tl) * p.Hs) * p.S + s];
     if (j >= 0 && j <= c) atomicOr(&mask[j], 1ull << tl);
   }
 }
@@ -67,14 +72,14 @@ __global__ __launch_bounds__(256) void csr_count_kernel(BwdParams p) {
   __shared__ unsigned long long mask[kMaxNB];
   const int NQB = p.NB;
   const int bid = blockIdx.x;
-  const int kv = bid % p.Hkv, rest = bid / p.Hkv;
+  const int sg = bid % p.Hs, rest = bid / p.Hs;
   const int c = rest % NQB, b = rest / NQB;
   const int ntok = min(64, p.T - c * 64);
   for (int j = threadIdx.x; j < p.NB; j += 256) mask[j] = 0ull;
   __syncthreads();
-  build_token_masks(p, mask, b, kv, c, ntok);
+  build_token_masks(p, mask, b, sg, c, ntok);
   __syncthreads();
-  int32_t* out = p.cnt2d + ((static_cast<size_t>(b) * p.Hkv + kv) * NQB + c) * p.NB;
+  int32_t* out = p.cnt2d + ((static_cast<size_t>(b) * p.Hs + sg) * NQB + c) * p.NB;
   for (int j = threadIdx.x; j < p.NB; j += 256) out[j] = __popcll(mask[j]);
 }
 
@@ -130,22 +135,22 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(BwdParams p) {
   __shared__ int base[kMaxNB];
   const int NQB = p.NB;
   const int bid = blockIdx.x;
-  const int kv = bid % p.Hkv, rest = bid / p.Hkv;
+  const int sg = bid % p.Hs, rest = bid / p.Hs;
   const int c = rest % NQB, b = rest / NQB;
   const int ntok = min(64, p.T - c * 64);
-  const size_t bk = static_cast<size_t>(b) * p.Hkv + kv;
+  const size_t bk = static_cast<size_t>(b) * p.Hs + sg;
   for (int j = threadIdx.x; j <= c; j += 256) {
     mask[j] = 0ull;
     base[j] = p.rowptr[bk * (p.NB + 1) + j] + p.cnt2d[(bk * NQB + c) * p.NB + j];
   }
   __syncthreads();
-  build_token_masks(p, mask, b, kv, c, ntok);
+  build_token_masks(p, mask, b, sg, c, ntok);
   __syncthreads();
-  const size_t rowbase = (static_cast<size_t>(b) * p.T + c * 64) * p.Hkv + kv;
+  const size_t rowbase = (static_cast<size_t>(b) * p.T + c * 64) * p.Hs + sg;
   int32_t* ent = p.entries + bk * static_cast<size_t>(p.T) * p.S;
   for (int e = threadIdx.x; e < ntok * p.S; e += 256) {
     const int tl = e / p.S, s = e - tl * p.S;
-    const int j = p.idx[(rowbase + static_cast<size_t>(tl) * p.Hkv) * p.S + s];
+    const int j = p.idx[(rowbase + static_cast<size_t>(tl) * p.Hs) * p.S + s];
     if (j >= 0 && j <= c) {
       const int pos = base[j] + __popcll(mask[j] & ((1ull << tl) - 1ull));
       ent[pos] = ((c * 64 + tl) << 6) | s;
@@ -190,8 +195,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const int bid = blockIdx.x;
   const int kv = bid % p.Hkv, rest = bid / p.Hkv;
   const int j = rest % p.NB, b = rest / p.NB;
-  const size_t bk = static_cast<size_t>(b) * p.Hkv + kv;
-  const int G = p.G, TPT = p.TPT, RT = p.TPT * p.G;
+  // rows per CSR entry: the Gs query heads of the entry's selection head
+  const int G = p.Gs, TPT = p.TPT, RT = p.TPT * G;
 
   const int key = j * 64 + wv * 16 + l16;
   const bool keyok = key < p.T;
@@ -212,36 +217,56 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     dk[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  const int e0 = p.rowptr[bk * (p.NB + 1) + j];
-  const int n = p.rowptr[bk * (p.NB + 1) + j + 1] - e0;
-  const int32_t* ent = p.entries + bk * static_cast<size_t>(p.T) * p.S + e0;
+  // The selections that chose this block come from the kdiv selection heads
+  // sg = kappa * kdiv + i of this KV head (one, with one gate per KV head):
+  // their CSR lists for block j, concatenated in head order.
+  __shared__ long long seg_base[8];     // first entry of head i's list for block j
+  __shared__ int seg_cum[9];            // entries before head i's list
+  if (tid == 0) {
+    int cum = 0;
+    for (int i = 0; i < p.kdiv; ++i) {
+      const size_t bs = static_cast<size_t>(b) * p.Hs + kv * p.kdiv + i;
+      const int e0 = p.rowptr[bs * (p.NB + 1) + j];
+      seg_base[i] = static_cast<long long>(bs * static_cast<size_t>(p.T) * p.S + e0);
+      seg_cum[i] = cum;
+      cum += p.rowptr[bs * (p.NB + 1) + j + 1] - e0;
+    }
+    seg_cum[p.kdiv] = cum;
+  }
+  __syncthreads();
+  const int n = seg_cum[p.kdiv];
   const int nit = (n + 2 * TPT - 1) / (2 * TPT);
   const float sl2 = p.scale_log2;
 
   // ---- per-row metadata (threads 0..31, one row each)
   const int mr = tid & 31, mtt = mr >> 4, mrr = mr & 15;
   const int mhh = mrr - (mrr / G) * G;
-  // raw CSR entry of this row in tile pair `it` (-1 past the list); it is
+  // CSR entry of this row in tile pair `it` (-1 past the lists), repacked as
+  // (token << 9) | (head index i in the KV head's group << 6) | slot; it is
   // checked only when used, an iteration later, so the load is not waited for
   auto load_ent = [&](int it) -> int {
     const int ti = (nit - 1 - it) * 2 * TPT + mtt * TPT + mrr / G;
     if (mrr >= RT || ti >= n) return -1;
-    return ent[ti];
+    int i = 0;
+    while (i + 1 < p.kdiv && seg_cum[i + 1] <= ti) ++i;
+    const int raw = p.entries[seg_base[i] + (ti - seg_cum[i])];
+    return ((raw >> 6) << 9) | (i << 6) | (raw & 63);
   };
   float r_lse = -INFINITY, r_del = 0.f, r_lg = 0.f;
   int r_t = -1, r_src = -1, r_en = -1;
   auto meta_issue = [&](int en) {
     if (en >= 0) {
-      const int tk = en >> 6, s = en & 63;
+      const int tk = en >> 9, s = en & 63;
       if (tk < j * 64 || tk >= p.T || s >= p.S) en = -1;
     }
     r_t = -1; r_src = -1; r_en = en;
     if (en >= 0) {
-      const int tk = en >> 6, s = en & 63;
-      const size_t qrow = (static_cast<size_t>(b) * p.T + tk) * p.Hq + kv * G + mhh;
+      const int tk = en >> 9, s = en & 63;
+      const int sg = kv * p.kdiv + ((en >> 6) & 7);
+      const size_t qrow = (static_cast<size_t>(b) * p.T + tk) * p.Hq + sg * G + mhh;
       r_lse = p.lse[qrow];
       r_del = p.delta[qrow];
-      r_lg = p.logg[((static_cast<size_t>(b) * p.T + tk) * p.Hkv + kv) * p.S + s];
+      r_lg = p.logg[((static_cast<size_t>(b) * p.T + tk) * p.Hs + sg) * p.S + s];
       r_t = tk;
       r_src = static_cast<int>(qrow);
     }
@@ -337,8 +362,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const uint4 v0 = ld16(dsT + r0 * DSP + part * 16);
     const uint4 v1 = ld16(dsT + (r0 + 16) * DSP + part * 16);
     auto dst = [&](int en) {
+      const int sg = kv * p.kdiv + ((en >> 6) & 7);
       return p.dsbuf +
-             ((((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)) * G +
+             ((((static_cast<size_t>(b) * p.T + (en >> 9)) * p.Hs + sg) * p.S + (en & 63)) * G +
               hh) * 128 + part * 8;
     };
     if (en0 >= 0) st16(dst(en0), v0);
@@ -366,7 +392,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
           tot += (dsum[0][rr + h] + dsum[1][rr + h]) + (dsum[2][rr + h] + dsum[3][rr + h]);
       }
       if (en >= 0)
-        p.dlogg[((static_cast<size_t>(b) * p.T + (en >> 6)) * p.Hkv + kv) * p.S + (en & 63)] = tot;
+        p.dlogg[((static_cast<size_t>(b) * p.T + (en >> 9)) * p.Hs + kv * p.kdiv +
+                 ((en >> 6) & 7)) * p.S + (en & 63)] = tot;
     }
   };
 
@@ -564,8 +591,9 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
 
   const int ngrp = (a.T + tpw - 1) / tpw;
   const int bid = blockIdx.x;
-  const int kv = bid % a.Hkv;
-  const int rest = bid / a.Hkv;
+  const int sg = bid % a.Hs;             // selection head
+  const int kv = sg / a.kdiv;            // its KV head
+  const int rest = bid / a.Hs;
   const int grp = ngrp - 1 - (rest % ngrp);   // late (long) groups first
   const int b = rest / ngrp;
   const int t0 = grp * tpw;
@@ -577,10 +605,10 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   if (tid < 16) prog[tid] = 0;
   if (tid < R) fill_cnt[tid] = 0u;
   __syncthreads();
-  const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
+  const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hs + sg;
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
-    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
+    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hs) * S + s;
     const int j = a.idx[off];
     if (j >= 0 && j <= (t0 + tl) / 64) {
       atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
@@ -600,7 +628,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   __syncthreads();
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
-    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
+    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hs) * S + s;
     const int j = a.idx[off];
     if (j >= 0 && j <= (t0 + tl) / 64) {
       const int rank = pcnt[tl * NBW + (j >> 5)] + __popc(bits[tl * NBW + (j >> 5)] & ((1u << (j & 31)) - 1u));
@@ -631,13 +659,13 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
 
   if (wv >= ncw) {
     // ================================================================ stager
-    const int sg = wv - ncw;                                // 0 or 1
+    const int stg = wv - ncw;                                // 0 or 1
     const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
     const int tokstride = a.Hkv * D;       // offsets inside one batch's K fit 32 bits
     int grow[MPS], gch[MPS];
 #pragma unroll
     for (int m = 0; m < MPS; ++m) {
-      const int pu = sg * UPS + m * 64 + lane;
+      const int pu = stg * UPS + m * 64 + lane;
       grow[m] = pu / KCPR;
       gch[m] = ((pu % KCPR) ^ lds_swz<KROWB>(grow[m])) * 8;
     }
@@ -670,7 +698,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
         if (failed) break;
       }
       const int j = ulist[n];
-      uint8_t* dst = ring + (n % R) * STAGE + sg * UPS * 16;
+      uint8_t* dst = ring + (n % R) * STAGE + stg * UPS * 16;
 #pragma unroll
       for (int m = 0; m < MPS; ++m)
         load_lds16(kbase + (min(j * 64 + grow[m], a.T - 1) * tokstride + gch[m]), dst + m * 1024);
@@ -695,14 +723,14 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   }
 
   // ================================================================ compute
-  const int G = a.G, TPT = a.TPT;
+  const int G = a.Gs, TPT = a.TPT;       // query heads per token row group
   const int tile = wv;
   const WalkRow wrow = walk_row(tile, l16, TPT, G, ntok);
   const int tl_row = wrow.tl;
   const int hh = wrow.hh;
   bool valid = wrow.live;
   {
-    const size_t qrow = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + kv * G + hh;
+    const size_t qrow = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + sg * G + hh;
     valid = valid && (a.lse[qrow] > -INFINITY);
   }
   floatx4 dqa[NDT];
@@ -736,9 +764,9 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
     return nU;
   };
 
-  // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hkv * S + sl) * G + hh) * 128
-  const uint16_t* const dsq = a.dsbuf + rowbase * S * a.G * 128;
-  const int HSG = a.Hkv * S;
+  // dS of (token tl, slot sl, head hh) at dsq + ((tl * Hs * S + sl) * G + hh) * 128
+  const uint16_t* const dsq = a.dsbuf + rowbase * S * G * 128;
+  const int HSG = a.Hs * S;
   // dS rows of the tile for union block v (two blocks in flight).  Every
   // lane issues its loads, so the loads of one block never wait behind the
   // other's; through a buffer over this group's dS rows, a lane whose row did
@@ -849,7 +877,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   }
 
   if (l16 < TPT * G && tile * TPT + l16 / G < ntok) {
-    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + kv * G + hh;
+    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl_row) * a.Hq + sg * G + hh;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 pk;
@@ -867,7 +895,7 @@ hipError_t launch_dq(const BwdParams& p, hipStream_t st) {
   const int tpw = walk_tpw(p.TPT);
   const int ncw = walk_ncw(p.TPT);
   const unsigned ngrp = (p.T + tpw - 1) / tpw;
-  const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * ngrp);
+  const dim3 grid(static_cast<unsigned>(p.B) * p.Hs * ngrp);
   hipLaunchKernelGGL((dq_kernel<D, 8>), grid, dim3((ncw + kDqStagers) * 64), 0, st, p, ncw, tpw);
   return hipGetLastError();
 }
@@ -879,10 +907,10 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((nrows * 16 + 255) / 256), dim3(256), 0, st,
                      p.o, p.o32, p.dout, p.delta, nrows);
   const int NQB = p.NB;
-  const unsigned nblk = static_cast<unsigned>(p.B) * p.Hkv * NQB;
+  const unsigned nblk = static_cast<unsigned>(p.B) * p.Hs * NQB;
   hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hkv), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hkv), dim3(1024), 0, st, p);
+  hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hs), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hs), dim3(1024), 0, st, p);
   hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
   timing_mark(1, st);
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),

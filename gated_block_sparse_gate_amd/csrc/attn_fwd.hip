@@ -5,9 +5,11 @@
 // over the keys of the blocks selected for (t, kappa = h/G), tau <= t.
 //
 // Schedule (query-group stationary):
-//   one workgroup = (batch b, KV head kappa, a group of TPW <= 64 consecutive
-//   tokens): NCW compute waves, each owning one row tile of 16 rows = TPT
-//   tokens x G heads, plus two stager waves.  The stagers copy the K tile and
+//   one workgroup = (batch b, selection head sg, a group of TPW <= 64
+//   consecutive tokens): NCW compute waves, each owning one row tile of 16
+//   rows = TPT tokens x Gs heads (the Gs query heads that share sg's
+//   selection: the G heads of a KV head, or one head when every query head
+//   has its own gate), plus two stager waves.  The stagers copy the K tile and
 //   the V^T tile (from a transposed copy of V made once per call, keys in
 //   operand order) of every block in the union of the group's selections, in
 //   ascending order, into a ring of R LDS slots with asynchronous global ->
@@ -70,8 +72,9 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 
   const int ngrp = (a.T + tpw - 1) / tpw;
   const int bid = blockIdx.x;
-  const int kv = bid % a.Hkv;
-  const int rest = bid / a.Hkv;
+  const int sg = bid % a.Hs;             // selection head
+  const int kv = sg / a.kdiv;            // its KV head
+  const int rest = bid / a.Hs;
   const int grp = ngrp - 1 - (rest % ngrp);   // late (long) groups first
   const int b = rest / ngrp;
   const int t0 = grp * tpw;
@@ -83,10 +86,10 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   if (tid < 16) prog[tid] = 0;
   if (tid < R) fill_cnt[tid] = 0u;
   __syncthreads();
-  const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hkv + kv;
+  const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hs + sg;
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
-    const int j = a.idx[(rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s];
+    const int j = a.idx[(rowbase + static_cast<size_t>(tl) * a.Hs) * S + s];
     if (j >= 0 && j <= (t0 + tl) / 64) {
       atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
       atomicOr(&ubits[j >> 5], 1u << (j & 31));
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   __syncthreads();
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
-    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hkv) * S + s;
+    const size_t off = (rowbase + static_cast<size_t>(tl) * a.Hs) * S + s;
     const int j = a.idx[off];
     if (j >= 0 && j <= (t0 + tl) / 64) {
       const uint32_t wbits = bits[tl * NBW + (j >> 5)];
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     // lds_swz(r) of K row r = p / KCPR, else chunk (v % 8) ^ tr_swz(d) of V^T
     // row d = v / 8 (v = p - KU); lane i of copy m fetches unit 64 m + i of
     // its stager's tile.
-    const int sg = wv - ncw;
+    const int stg = wv - ncw;
     const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
     const uint16_t* vtbase =
         a.vt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 #pragma unroll
     for (int m = 0; m < MPS; ++m) {
       const int pu = m * 64 + lane;
-      if (sg == 0) {
+      if (stg == 0) {
         grow[m] = pu / KCPR;
         goff[m] = ((pu % KCPR) ^ lds_swz<KROWB>(grow[m])) * 8;
       } else {
@@ -184,8 +187,8 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         if (failed) break;
       }
       const int j = ulist[n];
-      uint8_t* dst = ring + (n % R) * STAGE + sg * KB;
-      if (sg == 0) {
+      uint8_t* dst = ring + (n % R) * STAGE + stg * KB;
+      if (stg == 0) {
 #pragma unroll
         for (int m = 0; m < MPS; ++m)
           load_lds16(kbase + (min(j * 64 + grow[m], a.T - 1) * tokstride + goff[m]), dst + m * 1024);
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 
   // ================================================================ compute
   // row r = l16 of the wave's tile -> token r / G, head r % G
-  const int G = a.G, TPT = a.TPT;
+  const int G = a.Gs, TPT = a.TPT;       // query heads per token row group
   const int tile = wv;
   const int tl = min(tile * TPT + l16 / G, 63);
   const int hh = l16 - (l16 / G) * G;
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   float m_run = -INFINITY, l_run = 0.f;
   {
     const uint16_t* qrow =
-        a.q + ((static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh) * D;
+        a.q + ((static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + sg * G + hh) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qa[ks] = valid ? *reinterpret_cast<const uint4*>(qrow + ks * 32 + g4 * 8)
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   const float vsc = HILO ? 1.f : a.vscale[static_cast<size_t>(b) * a.Hkv + kv];
   if (valid) {
     const float lsum = row4_sum(l_run);
-    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + kv * G + hh;
+    const size_t row = (static_cast<size_t>(b) * a.T + t0 + tl) * a.Hq + sg * G + hh;
     const float inv = (lsum > 0.f) ? vsc / lsum : 0.f;   // vsc undoes the V^T scaling
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -434,7 +437,7 @@ hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
   const int tpw = min(64, 14 * p.TPT);
   const int ncw = (tpw + p.TPT - 1) / p.TPT;
   const unsigned ngrp = (p.T + tpw - 1) / tpw;
-  const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv * ngrp);
+  const dim3 grid(static_cast<unsigned>(p.B) * p.Hs * ngrp);
   hipLaunchKernelGGL((sparse_fwd_kernel<D, HILO, 4>), grid, dim3((ncw + kFwdStagers) * 64), 0, st,
                      p, ncw, tpw);
   return hipGetLastError();

@@ -2,12 +2,14 @@
 // by default, 1,024 and 4,096 also supported; usage guide pitfall 3: the
 // budget limits the tokens each query attends, not the cache).
 //
-// Unit = (sequence b, KV head kappa), L = ctx_len[b], c = (L-1)/64:
-//   score : s_j = q_gate . kg_cache[j] / sqrt(dg), j = 0..c (chunks of 128
-//           candidates per workgroup; gate keys fp32 or bf16);
+// Unit = (sequence b, selection head sg), L = ctx_len[b], c = (L-1)/64; the
+// selection head is a KV head kappa whose gate its G query heads share, or
+// (one gate per query head) a single query head of KV head kappa = sg / kdiv:
+//   score : s_j = q_gate[sg] . kg_cache[kappa, j] / sqrt(dg), j = 0..c
+//           (chunks of 128 candidates per workgroup; gate keys fp32 or bf16);
 //   top-k : log-sum-exp; the min(K, c) best historical blocks (ties ->
 //           lower j) + block c (one wave per unit).
-//   attend: the G query heads attend to the selected blocks' keys tau < L
+//   attend: the unit's query heads attend to the selected blocks' keys tau < L
 //           with log g added (apply_gate = 1); a workgroup walks its unit's
 //           selected blocks (16 KiB each per tensor, contiguous in the
 //           head-major cache) two at a time, software-pipelined, with scores
@@ -39,21 +41,21 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeParams p) {
   constexpr int NPASS = 4;               // 4 x 32 candidates per workgroup
   const int tid = threadIdx.x;
   const int unit = blockIdx.x, chunk = blockIdx.y;
-  const int b = unit / p.Hkv;
+  const int b = unit / p.Hs;
   const int L = p.ctx_len[b];
   if (!(L >= 1 && L <= p.Lmax)) return;
   const int ncand = (L - 1) / 64 + 1;
   const int j0 = chunk * 32 * NPASS;
   if (j0 >= ncand) return;
   const int sub = tid & (LPC - 1), cl = tid / LPC;    // 32 candidates per pass
-  const int kv = unit - b * p.Hkv;
+  const int kv = (unit - b * p.Hs) / p.kdiv;          // KV head of the unit's gate keys
   const float* qgp = p.q_gate + static_cast<size_t>(unit) * DG;
   // element index of candidate j's gate key: row j of the unit's cache, or
   // (paged) the key of the block's page; -1 past the candidates or for a page
   // outside the pool (reads as zeros)
   auto key_row = [&](int j) -> long {
     if (j >= ncand) return -1;
-    if (!p.btab) return (static_cast<long>(unit) * p.NBmax + j) * DG;
+    if (!p.btab) return ((static_cast<long>(b) * p.Hkv + kv) * p.NBmax + j) * DG;
     const int pg = p.btab[static_cast<size_t>(b) * p.NBmax + j];
     return (pg >= 0 && pg < p.num_pages) ? (static_cast<long>(pg) * p.Hkv + kv) * DG : -1;
   };
@@ -107,8 +109,8 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
   __shared__ uint32_t gath[4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int unit = blockIdx.x * 4 + wv;
-  if (unit >= p.B * p.Hkv) return;
-  const int b = unit / p.Hkv;
+  if (unit >= p.B * p.Hs) return;
+  const int b = unit / p.Hs;
   const int L = p.ctx_len[b];
   const bool ok = (L >= 1 && L <= p.Lmax);
   const int S = p.S, K = p.K;
@@ -271,7 +273,7 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 // over the unit's splits (one workgroup of 256 threads).  The per-split
 // weights are formed once per (split, head) in LDS.
 template <int D, int G>
-__device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit, int b, int kv,
+__device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit, int b, int sg,
                                              bool ok) {
   __shared__ float wsp[kMaxS][G];
   __shared__ float inv_l[G];
@@ -296,7 +298,7 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& p, int unit, in
     const int h = e / D;
     float o = 0.f;
     for (int sp = 0; sp < p.nsplit; ++sp) o = fmaf(base[sp * RF + e], wsp[sp][h], o);
-    p.o[(static_cast<size_t>(b) * p.Hq + kv * G) * D + e] = f2bf(o * inv_l[h]);
+    p.o[(static_cast<size_t>(b) * p.Hq + sg * G) * D + e] = f2bf(o * inv_l[h]);
   }
 }
 
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int unit = blockIdx.x, split = blockIdx.y;
-  const int b = unit / p.Hkv, kv = unit - b * p.Hkv;
+  const int b = unit / p.Hs, sg = unit - b * p.Hs, kv = sg / p.kdiv;
   const int L = p.ctx_len[b];
   const bool ok = (L >= 1 && L <= p.Lmax);
   const int spw = p.spw, npass = spw / 2;
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
   uint4 qb[NKS];
   {
     const int h = min(r, G - 1);
-    const uint16_t* qp = p.q + (static_cast<size_t>(b) * p.Hq + kv * G + h) * D + 8 * g;
+    const uint16_t* qp = p.q + (static_cast<size_t>(b) * p.Hq + sg * G + h) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const uint4 v = ld16(qp + 32 * ks);
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
         if (mq != -INFINITY) o += wred(q).o[h][d] * fast_exp2(mq - M);
       }
       const float inv_l = (ok && l > 0.f) ? 1.f / l : __builtin_nanf("");
-      p.o[(static_cast<size_t>(b) * p.Hq + kv * G) * D + e] = f2bf(o * inv_l);
+      p.o[(static_cast<size_t>(b) * p.Hq + sg * G) * D + e] = f2bf(o * inv_l);
     }
     return;
   }
@@ -568,9 +570,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int unit = blockIdx.x;
-  const int b = unit / p.Hkv, kv = unit - b * p.Hkv;
+  const int b = unit / p.Hs, sg = unit - b * p.Hs;
   const int L = p.ctx_len[b];
-  merge_splits<D, G>(p, unit, b, kv, L >= 1 && L <= p.Lmax);
+  merge_splits<D, G>(p, unit, b, sg, L >= 1 && L <= p.Lmax);
 }
 
 }  // namespace
@@ -587,7 +589,7 @@ void decode_split(int S, int units, int* nsplit, int* spw) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st) {
-  const unsigned units = static_cast<unsigned>(p.B) * p.Hkv;
+  const unsigned units = static_cast<unsigned>(p.B) * p.Hs;
   const dim3 sgrid(units, (p.NBmax + 127) / 128);
   auto score = [&](auto dgc) {
     constexpr int DG = decltype(dgc)::value;

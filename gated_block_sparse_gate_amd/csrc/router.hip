@@ -2,7 +2,9 @@
 // max + min + average, Q/K normalisation, gate RoPE; abstract: lightweight
 // selector that scores context blocks).
 //
-//   q_gate[t] = RoPE_t( RMSNorm( concat_i q[t, kappa*G+i] . Wq[kappa] ) * w_qn )
+//   q_gate[t] = RoPE_t( RMSNorm( concat_i q[t, sg*Gs+i] . Wq[sg] ) * w_qn )
+//     per selection head sg: Gs = G query heads of KV head sg (one gate per KV
+//     head), or Gs = 1, query head sg alone (one gate per query head)
 //   k_gate[t] = RoPE_{64c}( RMSNorm( [max; min; mean]_{64c..t} k . Wk[kappa] ) * w_kn )
 //
 // Both projections run on bf16 MFMA with fp32 accumulation.  The inputs and
@@ -75,14 +77,15 @@ __device__ __forceinline__ void norm_rope_store(floatx4 (&acc)[DG / 16], const f
   }
 }
 
-// One wave = 32 token rows x DG gate columns; workgroup = 4 waves = 128 rows.
+// One wave = 32 token rows x DG gate columns; workgroup = 4 waves = 128 rows
+// of one selection head.
 template <int DG>
 __global__ __launch_bounds__(256) void gate_query_kernel(RouterParams p) {
   constexpr int NT = DG / 16;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int kv = blockIdx.y;
-  const int F = p.G * p.D;
+  const int sg = blockIdx.y;
+  const int F = p.Gs * p.D;
   const long nrows = static_cast<long>(p.B) * p.T;
   const long r0 = static_cast<long>(blockIdx.x) * 128 + wv * 32;
 
@@ -98,9 +101,9 @@ __global__ __launch_bounds__(256) void gate_query_kernel(RouterParams p) {
   for (int mt = 0; mt < 2; ++mt) {
     const long r = r0 + mt * 16 + l16;
     ok[mt] = r < nrows;
-    xr[mt] = p.q + ((ok[mt] ? r : 0) * p.Hq + static_cast<long>(kv) * p.G) * p.D;
+    xr[mt] = p.q + ((ok[mt] ? r : 0) * p.Hq + static_cast<long>(sg) * p.Gs) * p.D;
   }
-  const uint16_t* wt = p.wqT + static_cast<size_t>(kv) * DG * F;
+  const uint16_t* wt = p.wqT + static_cast<size_t>(sg) * DG * F;
   for (int f = 0; f < F; f += 32) {
     uint4 av[2];
 #pragma unroll
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(256) void gate_query_kernel(RouterParams p) {
       const long r = r0 + mt * 16 + g4 * 4 + i;
       const bool v = r < nrows;
       pos[i] = v ? static_cast<int>(r % p.T) : 0;
-      out[i] = v ? p.q_gate + (r * p.Hkv + kv) * DG : nullptr;
+      out[i] = v ? p.q_gate + (r * p.Hs + sg) * DG : nullptr;
     }
     norm_rope_store<DG>(acc[mt], p.w_qn, p.eps, p.rope, pos, out, l16);
   }
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
 template <int D, int DG>
 hipError_t launch_router_t(const RouterParams& p, hipStream_t st) {
   const long nrows = static_cast<long>(p.B) * p.T;
-  hipLaunchKernelGGL((gate_query_kernel<DG>), dim3((nrows + 127) / 128, p.Hkv), dim3(256), 0,
+  hipLaunchKernelGGL((gate_query_kernel<DG>), dim3((nrows + 127) / 128, p.Hs), dim3(256), 0,
                      st, p);
   const int NB = (p.T + 63) / 64;
   hipLaunchKernelGGL((gate_key_kernel<D, DG>), dim3(NB, p.Hkv, p.B), dim3(256), 0, st, p);
@@ -317,10 +320,10 @@ hipError_t launch_router(const RouterParams& p0, const uint16_t* wq, const uint1
   const long nr = static_cast<long>(p.T) * (p.dg / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(min(4096L, (nr + 255) / 256))),
                      dim3(256), 0, st, rope, p.T, p.dg, theta);
-  const long nq = static_cast<long>(p.Hkv) * p.G * p.D * p.dg;
+  const long nq = static_cast<long>(p.Hs) * p.Gs * p.D * p.dg;
   const long nk = static_cast<long>(p.Hkv) * 3 * p.D * p.dg;
   hipLaunchKernelGGL(transpose_w_kernel, dim3(static_cast<unsigned>(min(2048L, (nq + 255) / 256))),
-                     dim3(256), 0, st, wq, wqT, p.Hkv, p.G * p.D, p.dg);
+                     dim3(256), 0, st, wq, wqT, p.Hs, p.Gs * p.D, p.dg);
   hipLaunchKernelGGL(transpose_w_kernel, dim3(static_cast<unsigned>(min(2048L, (nk + 255) / 256))),
                      dim3(256), 0, st, wk, wkT, p.Hkv, 3 * p.D, p.dg);
   hipError_t e = hipGetLastError();

@@ -36,9 +36,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Selection heads (the heads that carry one gate each): the KV heads, whose
+// gate the G query heads of each share, or with SAS_FLAG_GATE_PER_QUERY_HEAD
+// every query head.  Gs query heads per selection head; selection head sg
+// attends KV head sg / kdiv.
+struct SelHeads { int Hs, Gs, kdiv; };
+SelHeads sel_heads(int Hq, int Hkv, int flags) {
+  const int G = Hq / Hkv;
+  if (flags & SAS_FLAG_GATE_PER_QUERY_HEAD) return SelHeads{Hq, 1, G};
+  return SelHeads{Hkv, G, 1};
+}
+
 sas_status check_dims(const sas_dims* d) {
   if (!d) return fail(SAS_ERR_INVALID, "dims pointer is null");
-  if (d->flags != 0) return fail(SAS_ERR_INVALID, "dims.flags must be 0");
+  if (d->flags & ~SAS_FLAG_GATE_PER_QUERY_HEAD)
+    return fail(SAS_ERR_INVALID, "dims.flags: unknown bits 0x%x", d->flags & ~SAS_FLAG_GATE_PER_QUERY_HEAD);
   if (d->B < 1 || d->T < 1 || d->Hq < 1 || d->Hkv < 1)
     return fail(SAS_ERR_INVALID, "B, T, Hq, Hkv must be >= 1 (got %d, %d, %d, %d)", d->B, d->T,
                 d->Hq, d->Hkv);
@@ -78,10 +90,10 @@ sas_status check_dims(const sas_dims* d) {
 // workspace layouts ------------------------------------------------------
 struct GateWs { size_t wqT, wkT, rope, total; };
 GateWs gate_ws(const sas_dims* d) {
-  const int G = d->Hq / d->Hkv;
+  const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
   GateWs w;
   w.wqT = 0;
-  w.wkT = align_up(w.wqT + sizeof(uint16_t) * d->Hkv * d->dg * G * d->D);
+  w.wkT = align_up(w.wqT + sizeof(uint16_t) * sh.Hs * d->dg * sh.Gs * d->D);
   w.rope = align_up(w.wkT + sizeof(uint16_t) * d->Hkv * d->dg * 3 * d->D);
   w.total = align_up(w.rope + sizeof(float2) * static_cast<size_t>(d->T) * (d->dg / 2));
   return w;
@@ -134,12 +146,13 @@ struct BwdWs { size_t delta, cnt2d, rowptr, entries, ds, total; };
 BwdWs bwd_ws(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
   const size_t S = d->topk + 1;
+  const size_t Hs = sel_heads(d->Hq, d->Hkv, d->flags).Hs;
   BwdWs w;
   w.delta = 0;
   w.cnt2d = align_up(w.delta + sizeof(float) * static_cast<size_t>(d->B) * d->T * d->Hq);
-  w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * d->Hkv * NB * NB);
-  w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * d->Hkv * (NB + 1));
-  w.ds = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * d->Hkv * d->T * S);
+  w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * Hs * NB * NB);
+  w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * Hs * (NB + 1));
+  w.ds = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * Hs * d->T * S);
   // dS of every selected (token, head, slot): 64 keys x (hi, lo) bf16
   w.total = align_up(w.ds + 256 * static_cast<size_t>(d->B) * d->T * d->Hq * S);
   return w;
@@ -148,16 +161,17 @@ BwdWs bwd_ws(const sas_dims* d) {
 struct DecWs { size_t idx, logg, part, score, total; int nsplit, spw; };
 DecWs dec_ws(const sas_decode_dims* d) {
   const size_t S = d->topk + 1;
-  const size_t G = d->Hq / d->Hkv;
+  const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+  const size_t units = static_cast<size_t>(d->B) * sh.Hs;    // (sequence, selection head)
   DecWs w;
-  sas::decode_split(static_cast<int>(S), d->B * d->Hkv, &w.nsplit, &w.spw);
+  sas::decode_split(static_cast<int>(S), static_cast<int>(units), &w.nsplit, &w.spw);
   w.idx = 0;
-  w.logg = align_up(w.idx + sizeof(int32_t) * d->B * d->Hkv * S);
-  w.part = align_up(w.logg + sizeof(float) * d->B * d->Hkv * S);
+  w.logg = align_up(w.idx + sizeof(int32_t) * units * S);
+  w.part = align_up(w.logg + sizeof(float) * units * S);
   // split partials (none with one split per unit)
-  const size_t nparts = w.nsplit > 1 ? static_cast<size_t>(d->B) * d->Hkv * w.nsplit : 0;
-  w.score = align_up(w.part + sizeof(float) * nparts * sas::decode_part_floats(static_cast<int>(G), d->D));
-  w.total = align_up(w.score + sizeof(float) * d->B * d->Hkv * d->NBmax);
+  const size_t nparts = w.nsplit > 1 ? units * w.nsplit : 0;
+  w.score = align_up(w.part + sizeof(float) * nparts * sas::decode_part_floats(sh.Gs, d->D));
+  w.total = align_up(w.score + sizeof(float) * units * d->NBmax);
   return w;
 }
 
@@ -193,6 +207,9 @@ sas_status check_decode_dims(const sas_decode_dims* d) {
     return fail(SAS_ERR_INVALID, "apply_gate must be 0 or 1");
   if (d->kg_dtype != 0 && d->kg_dtype != 1)
     return fail(SAS_ERR_INVALID, "kg_dtype must be 0 (fp32) or 1 (bf16)");
+  if (d->flags & ~SAS_FLAG_GATE_PER_QUERY_HEAD)
+    return fail(SAS_ERR_INVALID, "decode dims.flags: unknown bits 0x%x",
+                d->flags & ~SAS_FLAG_GATE_PER_QUERY_HEAD);
   return SAS_OK;
 }
 
@@ -300,6 +317,8 @@ sas_status sas_gate_score(const sas_dims* d, const uint16_t* q, const uint16_t* 
   p.q = q; p.k = k; p.w_qn = w_qn; p.w_kn = w_kn; p.q_gate = q_gate; p.k_gate = k_gate;
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg;
   p.G = d->Hq / d->Hkv; p.eps = d->norm_eps;
+  const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+  p.Hs = sh.Hs; p.Gs = sh.Gs;
   g_err.clear();
   return hip_status(sas::launch_router(p, wq, wk, reinterpret_cast<uint16_t*>(base + w.wqT),
                                        reinterpret_cast<uint16_t*>(base + w.wkT),
@@ -321,6 +340,10 @@ sas_status sas_topk_blocks(const sas_dims* d, const float* q_gate, const float* 
   p.q_gate = q_gate; p.k_gate = k_gate; p.idx = idx; p.logg = logg; p.gate_lse = gate_lse;
   p.gate_probs = gate_probs;
   p.B = d->B; p.T = d->T; p.Hkv = d->Hkv; p.dg = d->dg; p.K = d->topk; p.S = d->topk + 1;
+  {
+    const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+    p.Hs = sh.Hs; p.kdiv = sh.kdiv;
+  }
   p.NB = (d->T + 63) / 64;
   const size_t smem = sas::topk_smem_bytes(p.NB, p.dg);
   if (smem > 160 * 1024) return fail(SAS_ERR_UNSUPPORTED, "T too large for the Top-K kernel");
@@ -347,7 +370,11 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
   p.q = q; p.k = k; p.v = v; p.idx = idx; p.logg = logg; p.o = o; p.lse = lse; p.o32 = o_f32;
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
-  p.TPT = 16 / p.G;
+  {
+    const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+    p.Hs = sh.Hs; p.Gs = sh.Gs; p.kdiv = sh.kdiv;
+  }
+  p.TPT = 16 / p.Gs;
   p.ntiles = (64 + p.TPT - 1) / p.TPT;
   p.scale_log2 = scale * sas::kLog2e;
   g_err.clear();
@@ -363,6 +390,9 @@ sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16
                               size_t ws_bytes, void* stream) {
   sas_status st = check_dims(d);
   if (st) return st;
+  if (d->flags & SAS_FLAG_GATE_PER_QUERY_HEAD)
+    return fail(SAS_ERR_UNSUPPORTED,
+                "sas_gate_score_bwd covers one gate per KV head (flags must be 0)");
   REQ_PTR(q); REQ_PTR(k); REQ_PTR(wq); REQ_PTR(wk); REQ_PTR(w_qn); REQ_PTR(w_kn);
   REQ_PTR(q_gate); REQ_PTR(k_gate); REQ_PTR(idx); REQ_PTR(dlogg); REQ_PTR(dq); REQ_PTR(dk);
   REQ_PTR(dwq); REQ_PTR(dwk); REQ_PTR(dw_qn); REQ_PTR(dw_kn);
@@ -430,7 +460,11 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
   p.dsbuf = reinterpret_cast<uint16_t*>(base + w.ds);
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
-  p.TPT = 16 / p.G;
+  {
+    const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+    p.Hs = sh.Hs; p.Gs = sh.Gs; p.kdiv = sh.kdiv;
+  }
+  p.TPT = 16 / p.Gs;
   p.ntiles = (64 + p.TPT - 1) / p.TPT;
   p.scale = scale;
   p.scale_log2 = scale * sas::kLog2e;
@@ -472,7 +506,12 @@ sas_status decode_launch(const sas_decode_dims* d, const uint16_t* q, const floa
   p.ws_logg = reinterpret_cast<float*>(base + w.logg);
   p.ws_part = reinterpret_cast<float*>(base + w.part);
   p.ws_score = reinterpret_cast<float*>(base + w.score);
-  p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
+  p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg;
+  {
+    const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+    p.Hs = sh.Hs; p.Gs = sh.Gs; p.kdiv = sh.kdiv;
+    p.G = sh.Gs;                 // query heads per unit
+  }
   p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
   p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw; p.kg_bf16 = d->kg_dtype;
   p.scale_log2 = scale * sas::kLog2e;
@@ -572,7 +611,12 @@ sas_status sas_decode_paged(const sas_decode_dims* d, const uint16_t* q, const f
   p.ws_logg = reinterpret_cast<float*>(base + w.logg);
   p.ws_part = reinterpret_cast<float*>(base + w.part);
   p.ws_score = reinterpret_cast<float*>(base + w.score);
-  p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg; p.G = d->Hq / d->Hkv;
+  p.B = d->B; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.dg = d->dg;
+  {
+    const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+    p.Hs = sh.Hs; p.Gs = sh.Gs; p.kdiv = sh.kdiv;
+    p.G = sh.Gs;                 // query heads per unit
+  }
   p.K = d->topk; p.S = d->topk + 1; p.Lmax = d->Lmax; p.NBmax = d->NBmax;
   p.apply_gate = d->apply_gate; p.nsplit = w.nsplit; p.spw = w.spw; p.kg_bf16 = d->kg_dtype;
   p.scale_log2 = scale * sas::kLog2e;

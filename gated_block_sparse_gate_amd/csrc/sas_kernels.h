@@ -12,17 +12,22 @@ constexpr int kMaxNBW = kMaxNB / 32;    // bitmap words per token
 constexpr int kMaxS = 64;
 constexpr int kMaxDecodeNB = 4096;      // decode: Lmax <= 262144               // topk <= 63
 
+// Selection heads: the heads that each carry one gate and one selection.
+// One gate per KV head: Hs = Hkv, Gs = G query heads per gate.  One gate per
+// query head: Hs = Hq, Gs = 1.  Selection head sg attends KV head
+// sg / kdiv (kdiv = Hs / Hkv) with query heads sg * Gs .. sg * Gs + Gs - 1.
 struct RouterParams {
   const uint16_t* q;    // [B,T,Hq,D]
   const uint16_t* k;    // [B,T,Hkv,D]
-  const uint16_t* wqT;  // [Hkv,dg,G*D]  (transposed copy in the workspace)
+  const uint16_t* wqT;  // [Hs,dg,Gs*D]  (transposed copy in the workspace)
   const uint16_t* wkT;  // [Hkv,dg,3*D]
   const float* w_qn;    // [dg]
   const float* w_kn;    // [dg]
   const float2* rope;   // [T, dg/2] (cos, sin)
-  float* q_gate;        // [B,T,Hkv,dg]
+  float* q_gate;        // [B,T,Hs,dg]
   float* k_gate;        // [B,T,Hkv,dg]
   int B, T, Hq, Hkv, D, dg, G;
+  int Hs, Gs;
   float eps;
 };
 
@@ -68,13 +73,14 @@ constexpr int kGateBwdChunk = 1024;
 constexpr int kGateBwdKeyChunk = 32;
 
 struct TopkParams {
-  const float* q_gate;  // [B,T,Hkv,dg]
+  const float* q_gate;  // [B,T,Hs,dg]
   const float* k_gate;  // [B,T,Hkv,dg]
-  int32_t* idx;         // [B,T,Hkv,S]
-  float* logg;          // [B,T,Hkv,S]
-  float* gate_lse;      // [B,T,Hkv]
-  float* gate_probs;    // [B,T,Hkv,NB] or null
+  int32_t* idx;         // [B,T,Hs,S]
+  float* logg;          // [B,T,Hs,S]
+  float* gate_lse;      // [B,T,Hs]
+  float* gate_probs;    // [B,T,Hs,NB] or null
   int B, T, Hkv, dg, K, S, NB;
+  int Hs, kdiv;
 };
 
 // Dynamic LDS of the query-block walks (forward, dQ): R ring slots of `stage`
@@ -119,7 +125,8 @@ struct FwdParams {
   float* vamax; // workspace: [B,Hkv,NB] max |v| per 64-token block
   float* vscale;// workspace: [B,Hkv] power of two restoring the V^T scaling
   int B, T, Hq, Hkv, D, G, S, NB;
-  int TPT;      // tokens per 16-row tile = floor(16 / G)
+  int Hs, Gs, kdiv;   // selection heads (idx, logg [B,T,Hs,S]); rows per token = Gs
+  int TPT;      // tokens per 16-row tile = floor(16 / Gs)
   int ntiles;   // tiles per 64-token query block = ceil(64 / TPT)
   float scale_log2;   // scale * log2(e)
 };
@@ -140,22 +147,23 @@ struct BwdParams {
   float* dlogg;
   // workspace
   float* delta;         // [B,T,Hq]
-  int32_t* cnt2d;       // [B,Hkv,NQB,NB]  per (query block, key block) counts -> offsets
-  int32_t* rowptr;      // [B,Hkv,NB+1]
-  int32_t* entries;     // [B,Hkv,T*S] packed (t << 6) | slot
-  // [B,T,Hkv,S,G][hi 64 | lo 64] bf16: dS of each selected (token, head, slot)
+  int32_t* cnt2d;       // [B,Hs,NQB,NB]  per (query block, key block) counts -> offsets
+  int32_t* rowptr;      // [B,Hs,NB+1]
+  int32_t* entries;     // [B,Hs,T*S] packed (t << 6) | slot
+  // [B,T,Hs,S,Gs][hi 64 | lo 64] bf16: dS of each selected (token, head, slot)
   // as bf16 hi + lo parts, the 64 keys of the block in MFMA operand order
   // (position 32 k2 + 8 g + e holds key 32 k2 + 4 g + e for e < 4, else
   // key 32 k2 + 16 + 4 g + e - 4)
   uint16_t* dsbuf;
   int B, T, Hq, Hkv, D, G, S, NB;
-  int TPT, ntiles;
+  int Hs, Gs, kdiv;     // selection heads (idx, logg, dlogg [B,T,Hs,S])
+  int TPT, ntiles;      // tokens per 16-row tile = floor(16 / Gs)
   float scale, scale_log2;
 };
 
 struct DecodeParams {
   const uint16_t* q;        // [B,Hq,D]
-  const float* q_gate;      // [B,Hkv,dg]
+  const float* q_gate;      // [B,Hs,dg]
   const uint16_t* k_cache;  // [B,Hkv,Lmax,D]
   const uint16_t* v_cache;
   const float* kg_cache;    // [B,Hkv,NBmax,dg]; paged: k/v [P,Hkv,64,D], kg [P,Hkv,dg]
@@ -163,14 +171,15 @@ struct DecodeParams {
   int num_pages;
   const int32_t* ctx_len;   // [B]
   uint16_t* o;              // [B,Hq,D]
-  int32_t* idx_out;         // [B,Hkv,S] or null
-  float* logg_out;          // [B,Hkv,S] or null
-  // workspace
-  int32_t* ws_idx;          // [B,Hkv,S]
-  float* ws_logg;           // [B,Hkv,S]
-  float* ws_part;           // [B,Hkv,NSPLIT] records of decode_part_floats(G, D)
-  float* ws_score;          // [B,Hkv,NBmax] gate logits of the candidate blocks
+  int32_t* idx_out;         // [B,Hs,S] or null
+  float* logg_out;          // [B,Hs,S] or null
+  // workspace (one unit = one (sequence, selection head))
+  int32_t* ws_idx;          // [B,Hs,S]
+  float* ws_logg;           // [B,Hs,S]
+  float* ws_part;           // [B,Hs,NSPLIT] records of decode_part_floats(Gs, D)
+  float* ws_score;          // [B,Hs,NBmax] gate logits of the candidate blocks
   int B, Hq, Hkv, D, dg, G, K, S, Lmax, NBmax, apply_gate;
+  int Hs, Gs, kdiv;         // units per sequence = selection heads; G = Gs query heads per unit
   int nsplit, spw;          // attention splits per unit, slots per split
   int kg_bf16;              // gate keys stored as bf16 (else fp32)
   float scale_log2;

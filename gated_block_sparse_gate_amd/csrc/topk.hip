@@ -2,14 +2,16 @@
 // gates calibrate history against the always-retained current block; README
 // item (a): discrete Top-K selection).
 //
-// For token t of block c and KV head kappa:
-//   s_j = q_gate[t] . k_gate[64j+63] / sqrt(dg)   (complete historical blocks j < c)
-//   s_c = q_gate[t] . k_gate[t] / sqrt(dg)        (current block, causal prefix key)
+// For token t of block c and selection head sg (KV head kappa = sg / kdiv):
+//   s_j = q_gate[t,sg] . k_gate[64j+63,kappa] / sqrt(dg)   (historical blocks j < c)
+//   s_c = q_gate[t,sg] . k_gate[t,kappa] / sqrt(dg)        (current block, prefix key)
 //   gate_lse = logsumexp_{j<=c} s_j,  log g_j = s_j - gate_lse
 //   selection = min(K, c) largest s_j over j < c, equal scores -> lower j,
 //   written in ascending order, then c; padding -1 / -inf.
 //
-// One workgroup = 16 consecutive tokens of one (batch, KV head); all 16 share
+// One workgroup = 16 consecutive tokens of one (batch, selection head: a KV
+// head, or a query head when every query head has its own gate, scoring the
+// gate keys of its KV head); all 16 share
 // the same block c, so the historical block keys form one fp32 tile product
 // (fp32 MFMA: index parity needs fp32-accurate scores).
 // Selection: exact K-th largest order key by bitwise searches with wave-wide
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int kv = blockIdx.y, b = blockIdx.z;
+  const int sg = blockIdx.y, b = blockIdx.z;   // selection head
+  const int kv = sg / p.kdiv;                    // its KV head (gate keys)
   const int t0 = blockIdx.x * kTokPerWG;
   const int c = t0 / 64;
   const int ntok = min(kTokPerWG, p.T - t0);
@@ -52,11 +55,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   float qb[NS][4];
   {
     const float* qrow =
-        p.q_gate + ((static_cast<size_t>(b) * p.T + t0 + min(l16, ntok - 1)) * p.Hkv + kv) * DG;
+        p.q_gate + ((static_cast<size_t>(b) * p.T + t0 + min(l16, ntok - 1)) * p.Hs + sg) * DG;
 #pragma unroll
-    for (int sg = 0; sg < NS; ++sg) {
-      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * sg + 4 * g4);
-      qb[sg][0] = v.x; qb[sg][1] = v.y; qb[sg][2] = v.z; qb[sg][3] = v.w;
+    for (int dq = 0; dq < NS; ++dq) {
+      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * dq + 4 * g4);
+      qb[dq][0] = v.x; qb[dq][1] = v.y; qb[dq][2] = v.z; qb[dq][3] = v.w;
     }
   }
   // block keys k_gate[64 j + 63], staged per 64-key chunk through registers
@@ -87,12 +90,12 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
     const float* krow = &ks[(16 * wv + l16) * KP + 4 * g4];
 #pragma unroll
-    for (int sg = 0; sg < NS; ++sg) {
-      const float4 a = *reinterpret_cast<const float4*>(krow + 16 * sg);
-      acc = mfma16x16x4f32(a.x, qb[sg][0], acc);
-      acc = mfma16x16x4f32(a.y, qb[sg][1], acc);
-      acc = mfma16x16x4f32(a.z, qb[sg][2], acc);
-      acc = mfma16x16x4f32(a.w, qb[sg][3], acc);
+    for (int dq = 0; dq < NS; ++dq) {
+      const float4 a = *reinterpret_cast<const float4*>(krow + 16 * dq);
+      acc = mfma16x16x4f32(a.x, qb[dq][0], acc);
+      acc = mfma16x16x4f32(a.y, qb[dq][1], acc);
+      acc = mfma16x16x4f32(a.z, qb[dq][2], acc);
+      acc = mfma16x16x4f32(a.w, qb[dq][3], acc);
     }
     const int jb = j0 + 16 * wv + 4 * g4;     // keys jb .. jb+3 of token l16
     if (l16 < ntok) {
@@ -107,9 +110,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
     const int tl_s = tid >> 4, part = tid & 15;
     float acc = 0.f;
     if (tl_s < ntok) {
-      const size_t rw = (static_cast<size_t>(b) * p.T + t0 + tl_s) * p.Hkv + kv;
-      const float* kg = p.k_gate + rw * DG;
-      const float* qg = p.q_gate + rw * DG;
+      const size_t tok = static_cast<size_t>(b) * p.T + t0 + tl_s;
+      const float* kg = p.k_gate + (tok * p.Hkv + kv) * DG;
+      const float* qg = p.q_gate + (tok * p.Hs + sg) * DG;
       for (int d = part; d < DG; d += 16) acc = fmaf(qg[d], kg[d], acc);
     }
     acc += dpp_mov<0xB1>(acc);
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       for (int e = 0; e < EM; ++e) se += expf(sv[e] - mx);
       se = wave_sum(se);
       const float lse = mx + logf(se);
-      const size_t rowid = (static_cast<size_t>(b) * p.T + t0 + tl) * p.Hkv + kv;
+      const size_t rowid = (static_cast<size_t>(b) * p.T + t0 + tl) * p.Hs + sg;
       // order keys of the historical candidates; 0 elsewhere, which no
       // candidate threshold (always >= 1) reaches
       uint32_t kreg[EM];
@@ -252,7 +255,7 @@ size_t topk_smem_bytes(int NB, int dg) {
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
-  const dim3 grid((p.T + kTokPerWG - 1) / kTokPerWG, p.Hkv, p.B);
+  const dim3 grid((p.T + kTokPerWG - 1) / kTokPerWG, p.Hs, p.B);
   const size_t sm = topk_smem_bytes(p.NB, p.dg);
   switch (p.dg) {
     case 128:

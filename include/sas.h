@@ -54,6 +54,24 @@ typedef enum {
   SAS_ERR_HIP = 4           /* a HIP launch failed; see sas_last_error() */
 } sas_status;
 
+/*
+ * sas_dims.flags / sas_decode_dims.flags.
+ *
+ * SAS_FLAG_GATE_PER_QUERY_HEAD: one gate per query head instead of one per KV
+ * head (the README's "per query" selection read at head granularity; the
+ * released checkpoints' parameter count fits both, since Hq x D x dg =
+ * Hkv x G*D x dg).  Every query head h gets its own gate query
+ * q_gate[b,t,h] = RoPE_t(RMSNorm(q[b,t,h] . wq[h]) * w_qn) with wq [Hq,D,dg],
+ * scores the gate keys of its KV head h/G (k_gate stays [B,T,Hkv,dg]), and
+ * has its own selection and log-gates.  The "selection heads" Hs are then Hq
+ * (else Hkv): q_gate [B,T,Hs,dg]; idx, logg, dlogg [B,T,Hs,K+1]; gate_lse
+ * [B,T,Hs]; gate_probs [B,T,Hs,NB]; decode q_gate [B,Hs,dg] and idx_out,
+ * logg_out [B,Hs,K+1].  In the attention, query head h uses its selection
+ * head's slots; d log g sums over that selection head's query heads (all G
+ * of a KV head, or h alone).  sas_gate_score_bwd supports only flags = 0.
+ */
+#define SAS_FLAG_GATE_PER_QUERY_HEAD 1
+
 /* Operation ids for sas_workspace_size(). */
 enum {
   SAS_OP_GATE_SCORE = 0,
@@ -66,10 +84,13 @@ enum {
 /*
  * Prefill / training-step dimensions.
  *   B batch, T tokens, Hq query heads, Hkv KV heads (G = Hq/Hkv query heads
- *   share one KV head and one gate), D head dim, dg gate hidden size,
- *   block KV block size (must be 64), topk historical blocks K per query
- *   (S = K + 1 slots per query: K historical + the current block),
- *   rope_theta gate-RoPE base, norm_eps RMSNorm epsilon, flags reserved (0).
+ *   share one KV head and, with flags = 0, one gate), D head dim, dg gate
+ *   hidden size, block KV block size (must be 64), topk historical blocks K
+ *   per query (S = K + 1 slots per query: K historical + the current block),
+ *   rope_theta gate-RoPE base, norm_eps RMSNorm epsilon, flags 0 or
+ *   SAS_FLAG_GATE_PER_QUERY_HEAD.  The layouts below are written for
+ *   flags = 0 (Hkv selection heads); with the flag, read Hq for Hkv in every
+ *   gate-side shape (q_gate, wq [Hq,D,dg], idx, logg, dlogg, gate_lse, gate_probs).
  */
 typedef struct {
   int32_t B, T, Hq, Hkv, D, dg, block, topk;
@@ -88,6 +109,7 @@ typedef struct {
  */
 typedef struct {
   int32_t B, Hq, Hkv, D, dg, block, topk, Lmax, NBmax, apply_gate, kg_dtype;
+  int32_t flags;   /* 0 or SAS_FLAG_GATE_PER_QUERY_HEAD (q_gate, idx_out, logg_out per query head) */
 } sas_decode_dims;
 
 /* Library version (SAS_VERSION). */

@@ -193,14 +193,19 @@ def kth_gap(s: np.ndarray, K: int) -> float:
 def route(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float, tokens=None):
     """Router + candidate softmax + selection for the chosen tokens.
 
-    Returns dict with qg [B,n,Hkv,dg], kg_cur [B,n,Hkv,dg], idx [B,n,Hkv,K+1]
-    (pad -1), logg [B,n,Hkv,K+1] (pad -inf), lse [B,n,Hkv], near_tie
-    [B,n,Hkv], s [B,n,Hkv,NB] (-inf beyond c), probs [B,n,Hkv,NB] (0 beyond c).
+    Selection heads Hs = wq.shape[0] (see sel_heads): Hkv with one gate per KV
+    head [R1], Hq with one gate per query head; head sg scores the gate keys of
+    KV head sg * (Hq / Hs) // G.
+    Returns dict with qg [B,n,Hs,dg], kg_cur [B,n,Hkv,dg], idx [B,n,Hs,K+1]
+    (pad -1), logg [B,n,Hs,K+1] (pad -inf), lse [B,n,Hs], near_tie, gap
+    [B,n,Hs], s [B,n,Hs,NB] (-inf beyond c), probs [B,n,Hs,NB] (0 beyond c).
     """
     q = as64(q)
     k = as64(k)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
+    Hs = as64(wq).shape[0]
+    _, kv_of = sel_heads(Hq, Hkv, Hs)
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     NB = -(-T // BLOCK)
     S = K + 1
@@ -214,29 +219,30 @@ def route(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float, tokens=Non
         for n, t in enumerate(need):
             kblk[t // BLOCK] = kg_need[:, n]
     n_tok = len(tok)
-    idx = np.full((B, n_tok, Hkv, S), -1, dtype=np.int64)
-    logg = np.full((B, n_tok, Hkv, S), -np.inf)
-    lse = np.zeros((B, n_tok, Hkv))
-    near = np.zeros((B, n_tok, Hkv), dtype=bool)
-    gap = np.full((B, n_tok, Hkv), np.inf)
-    s_dense = np.full((B, n_tok, Hkv, NB), -np.inf)
-    probs = np.zeros((B, n_tok, Hkv, NB))
+    idx = np.full((B, n_tok, Hs, S), -1, dtype=np.int64)
+    logg = np.full((B, n_tok, Hs, S), -np.inf)
+    lse = np.zeros((B, n_tok, Hs))
+    near = np.zeros((B, n_tok, Hs), dtype=bool)
+    gap = np.full((B, n_tok, Hs), np.inf)
+    s_dense = np.full((B, n_tok, Hs, NB), -np.inf)
+    probs = np.zeros((B, n_tok, Hs, NB))
     for n, t in enumerate(tok):
         c = int(t) // BLOCK
         for b in range(B):
-            for kv in range(Hkv):
+            for sg in range(Hs):
+                kv = kv_of(sg)
                 hist = (np.stack([kblk[j][b, kv] for j in range(c)]) if c
                         else np.zeros((0, qg.shape[-1])))
-                s = gate_logits(qg[b, n, kv], hist, kg_cur[b, n, kv])
+                s = gate_logits(qg[b, n, sg], hist, kg_cur[b, n, kv])
                 l, lg = log_gates(s)
                 sel, nt = select_blocks(s, K)
-                idx[b, n, kv, :len(sel)] = sel
-                logg[b, n, kv, :len(sel)] = lg[sel]
-                lse[b, n, kv] = l
-                near[b, n, kv] = nt
-                gap[b, n, kv] = kth_gap(s, K)
-                s_dense[b, n, kv, :c + 1] = s
-                probs[b, n, kv, :c + 1] = np.exp(lg)
+                idx[b, n, sg, :len(sel)] = sel
+                logg[b, n, sg, :len(sel)] = lg[sel]
+                lse[b, n, sg] = l
+                near[b, n, sg] = nt
+                gap[b, n, sg] = kth_gap(s, K)
+                s_dense[b, n, sg, :c + 1] = s
+                probs[b, n, sg, :c + 1] = np.exp(lg)
     return dict(qg=qg, kg_cur=kg_cur, idx=idx, logg=logg, lse=lse, near_tie=near, gap=gap,
                 s=s_dense, probs=probs, tokens=tok)
 
@@ -259,54 +265,69 @@ def _row_keys(t: int, sel_row: np.ndarray):
     return np.concatenate(taus), np.concatenate(slots)
 
 
+def sel_heads(Hq: int, Hkv: int, Hs: int):
+    """Selection heads: the heads that each carry one gate and one selection.
+    With one gate per KV head [R1], Hs = Hkv and selection head sg covers the
+    query heads sg*G .. sg*G+G-1; with one gate per query head (the
+    alternative reading of "per query"), Hs = Hq and sg covers query head sg
+    alone.  Returns (Gs, kv_of): query heads per selection head and the KV head
+    (sg * Gs // G) whose keys selection head sg attends."""
+    if Hs not in (Hkv, Hq):
+        raise ValueError(f"selection heads must be Hkv ({Hkv}) or Hq ({Hq}), got {Hs}")
+    G, Gs = Hq // Hkv, Hq // Hs
+    return Gs, (lambda sg: sg * Gs // G)
+
+
 def attn_fwd_rows(q, k, v, idx, logg, scale: float, tokens=None):
-    """Gather form: per (b, t, kappa), concatenate the selected blocks' keys.
+    """Gather form: per (b, t, selection head), concatenate the selected blocks' keys.
 
     l_tau = q.k_tau * scale + logg[slot(tau)];  o = softmax(l) V;  lse = logsumexp(l).
-    idx/logg are [B, T, Hkv, S] (full token axis).  Returns o [B,n,Hq,D],
-    lse [B,n,Hq] for the chosen tokens.
+    idx/logg are [B, T, Hs, S] (full token axis; Hs selection heads, see
+    sel_heads).  Returns o [B,n,Hq,D], lse [B,n,Hq] for the chosen tokens.
     """
     q, k, v, logg = as64(q), as64(k), as64(v), as64(logg)
     idx = np.asarray(idx)
     B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
-    G = Hq // Hkv
+    Hkv, Hs = k.shape[2], idx.shape[2]
+    Gs, kv_of = sel_heads(Hq, Hkv, Hs)
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     o = np.zeros((B, len(tok), Hq, D))
     lse = np.zeros((B, len(tok), Hq))
     for n, t in enumerate(tok):
         t = int(t)
         for b in range(B):
-            for kv in range(Hkv):
-                taus, slots = _row_keys(t, idx[b, t, kv])
+            for sg in range(Hs):
+                kv = kv_of(sg)
+                taus, slots = _row_keys(t, idx[b, t, sg])
                 Kr, Vr = k[b, taus, kv], v[b, taus, kv]
-                bias = logg[b, t, kv, slots]
-                Q = q[b, t, kv * G:(kv + 1) * G]             # [G, D]
-                L = Q @ Kr.T * scale + bias                    # [G, n]
+                bias = logg[b, t, sg, slots]
+                hs = slice(sg * Gs, (sg + 1) * Gs)
+                Q = q[b, t, hs]                                # [Gs, D]
+                L = Q @ Kr.T * scale + bias                    # [Gs, n]
                 m = L.max(axis=1, keepdims=True)
                 P = np.exp(L - m)
                 l = P.sum(axis=1, keepdims=True)
-                o[b, n, kv * G:(kv + 1) * G] = (P / l) @ Vr
-                lse[b, n, kv * G:(kv + 1) * G] = (m + np.log(l))[:, 0]
+                o[b, n, hs] = (P / l) @ Vr
+                lse[b, n, hs] = (m + np.log(l))[:, 0]
     return o, lse
 
 
 def dense_bias(idx, logg, T: int) -> np.ndarray:
-    """Dense-masked form: bias [B, Hkv, T, T] = logg of the key's block when the
-    block is selected by the query and tau <= t, else -inf."""
+    """Dense-masked form: bias [B, Hs, T, T] (per selection head) = logg of the
+    key's block when the block is selected by the query and tau <= t, else -inf."""
     idx = np.asarray(idx)
     logg = as64(logg)
-    B, _, Hkv, S = idx.shape
-    bias = np.full((B, Hkv, T, T), -np.inf)
+    B, _, Hs, S = idx.shape
+    bias = np.full((B, Hs, T, T), -np.inf)
     for b in range(B):
         for t in range(T):
-            for kv in range(Hkv):
+            for sg in range(Hs):
                 for s_i in range(S):
-                    j = int(idx[b, t, kv, s_i])
+                    j = int(idx[b, t, sg, s_i])
                     if j < 0:
                         continue
                     hi = min(BLOCK * j + BLOCK, t + 1)
-                    bias[b, kv, t, BLOCK * j:hi] = logg[b, t, kv, s_i]
+                    bias[b, sg, t, BLOCK * j:hi] = logg[b, t, sg, s_i]
     return bias
 
 
@@ -316,13 +337,14 @@ def attn_fwd_dense(q, k, v, idx, logg, scale: float):
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
+    Gs, _ = sel_heads(Hq, Hkv, np.asarray(idx).shape[2])
     bias = dense_bias(idx, logg, T)
     o = np.zeros_like(q)
     lse = np.zeros((B, T, Hq))
     for b in range(B):
         for h in range(Hq):
             kv = h // G
-            L = q[b, :, h] @ k[b, :, kv].T * scale + bias[b, kv]
+            L = q[b, :, h] @ k[b, :, kv].T * scale + bias[b, h // Gs]
             m = L.max(axis=1, keepdims=True)
             P = np.exp(L - m)
             l = P.sum(axis=1, keepdims=True)
@@ -337,30 +359,31 @@ def attn_bwd(q, k, v, dout, idx, logg, scale: float, tokens=None):
 
     dP = dO.v;  Delta = dO.o;  dS = P (dP - Delta);
     dq = scale sum dS k;  dk += scale dS q;  dv += P dO;
-    dlogg[slot] = sum over the group's heads and the block's keys of dS
-    (README (b): the gradient reaching the selector through log g).
-    Returns dict(o, lse, dq, dk, dv, dlogg).
+    dlogg[slot] = sum over the selection head's query heads and the block's
+    keys of dS (README (b): the gradient reaching the selector through log g).
+    Returns dict(o, lse, dq, dk, dv, dlogg [B,T,Hs,S]).
     """
     q, k, v, dout, logg = as64(q), as64(k), as64(v), as64(dout), as64(logg)
     idx = np.asarray(idx)
     B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
-    G = Hq // Hkv
+    Hkv, Hs = k.shape[2], idx.shape[2]
+    Gs, kv_of = sel_heads(Hq, Hkv, Hs)
     S = idx.shape[-1]
     o = np.zeros_like(q)
     lse = np.zeros((B, T, Hq))
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    dlogg = np.zeros((B, T, Hkv, S))
+    dlogg = np.zeros((B, T, Hs, S))
     tok = range(T) if tokens is None else [int(t) for t in tokens]
     for b in range(B):
         for t in tok:
-            for kv in range(Hkv):
-                taus, slots = _row_keys(t, idx[b, t, kv])
+            for sg in range(Hs):
+                kv = kv_of(sg)
+                taus, slots = _row_keys(t, idx[b, t, sg])
                 Kr, Vr = k[b, taus, kv], v[b, taus, kv]
-                bias = logg[b, t, kv, slots]
-                hs = slice(kv * G, (kv + 1) * G)
+                bias = logg[b, t, sg, slots]
+                hs = slice(sg * Gs, (sg + 1) * Gs)
                 Q, dO = q[b, t, hs], dout[b, t, hs]
                 L = Q @ Kr.T * scale + bias
                 m = L.max(axis=1, keepdims=True)
@@ -376,60 +399,62 @@ def attn_bwd(q, k, v, dout, idx, logg, scale: float, tokens=None):
                 dq[b, t, hs] = scale * dS @ Kr
                 np.add.at(dk[b, :, kv], taus, scale * dS.T @ Q)
                 np.add.at(dv[b, :, kv], taus, P.T @ dO)
-                np.add.at(dlogg[b, t, kv], slots, dS.sum(axis=0))
+                np.add.at(dlogg[b, t, sg], slots, dS.sum(axis=0))
     pad = idx < 0
     dlogg[pad] = 0.0
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, dlogg=dlogg)
 
 
 def attn_bwd_rows(q, k, v, dout, idx, logg, scale: float, tokens):
-    """dq [B,n,Hq,D] and dlogg [B,n,Hkv,S] for chosen query tokens (gather form)."""
+    """dq [B,n,Hq,D] and dlogg [B,n,Hs,S] for chosen query tokens (gather form)."""
     q, k, v, dout, logg = as64(q), as64(k), as64(v), as64(dout), as64(logg)
     idx = np.asarray(idx)
     B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
-    G = Hq // Hkv
+    Hkv, Hs = k.shape[2], idx.shape[2]
+    Gs, kv_of = sel_heads(Hq, Hkv, Hs)
     S = idx.shape[-1]
     tok = np.asarray(tokens)
     dq = np.zeros((B, len(tok), Hq, D))
-    dlogg = np.zeros((B, len(tok), Hkv, S))
+    dlogg = np.zeros((B, len(tok), Hs, S))
     for n, t in enumerate(tok):
         t = int(t)
         for b in range(B):
-            for kv in range(Hkv):
-                taus, slots = _row_keys(t, idx[b, t, kv])
+            for sg in range(Hs):
+                kv = kv_of(sg)
+                taus, slots = _row_keys(t, idx[b, t, sg])
                 Kr, Vr = k[b, taus, kv], v[b, taus, kv]
-                hs = slice(kv * G, (kv + 1) * G)
+                hs = slice(sg * Gs, (sg + 1) * Gs)
                 Q, dO = q[b, t, hs], dout[b, t, hs]
-                L = Q @ Kr.T * scale + logg[b, t, kv, slots]
+                L = Q @ Kr.T * scale + logg[b, t, sg, slots]
                 P = np.exp(L - L.max(axis=1, keepdims=True))
                 P /= P.sum(axis=1, keepdims=True)
                 O = P @ Vr
                 dS = P * (dO @ Vr.T - (dO * O).sum(axis=1, keepdims=True))
                 dq[b, n, hs] = scale * dS @ Kr
-                np.add.at(dlogg[b, n, kv], slots, dS.sum(axis=0))
+                np.add.at(dlogg[b, n, sg], slots, dS.sum(axis=0))
     return dq, dlogg
 
 
 def attn_bwd_block(q, k, v, dout, idx, logg, scale: float, b: int, kv: int, j: int):
     """dk, dv [64, D] of KV block j of head kv (batch b): sums over every query
-    row that selected block j (its P needs that row's full softmax)."""
+    row, of every selection head attending kv, that selected block j (its P
+    needs that row's full softmax)."""
     q, k, v, dout, logg = as64(q), as64(k), as64(v), as64(dout), as64(logg)
     idx = np.asarray(idx)
     B, T, Hq, D = q.shape
-    Hkv = k.shape[2]
-    G = Hq // Hkv
+    Hkv, Hs = k.shape[2], idx.shape[2]
+    Gs, kv_of = sel_heads(Hq, Hkv, Hs)
     lo, hi = BLOCK * j, min(BLOCK * j + BLOCK, T)
     dk = np.zeros((hi - lo, D))
     dv = np.zeros((hi - lo, D))
-    rows = np.nonzero((idx[b, :, kv, :] == j).any(axis=1))[0]
-    for t in rows:
-        t = int(t)
-        taus, slots = _row_keys(t, idx[b, t, kv])
+    rows = [(sg, int(t)) for sg in range(Hs) if kv_of(sg) == kv
+            for t in np.nonzero((idx[b, :, sg, :] == j).any(axis=1))[0]]
+    for sg, t in rows:
+        taus, slots = _row_keys(t, idx[b, t, sg])
         Kr, Vr = k[b, taus, kv], v[b, taus, kv]
-        hs = slice(kv * G, (kv + 1) * G)
+        hs = slice(sg * Gs, (sg + 1) * Gs)
         Q, dO = q[b, t, hs], dout[b, t, hs]
-        L = Q @ Kr.T * scale + logg[b, t, kv, slots]
+        L = Q @ Kr.T * scale + logg[b, t, sg, slots]
         P = np.exp(L - L.max(axis=1, keepdims=True))
         P /= P.sum(axis=1, keepdims=True)
         O = P @ Vr
@@ -501,7 +526,7 @@ def route_all(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float):
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     Hs = as64(wq).shape[0]
-    G, Gs = Hq // Hkv, Hq // Hs
+    _, kv_of = sel_heads(Hq, Hkv, Hs)
     S = K + 1
     qg = gate_query(q, wq, w_qn, theta, eps)
     kg = gate_key_all(k, wk, w_kn, theta, eps)
@@ -517,7 +542,7 @@ def route_all(q, k, wq, wk, w_qn, w_kn, K: int, theta: float, eps: float):
         n = min(K, c)
         for b in range(B):
             for sg in range(Hs):
-                kv = sg * Gs // G
+                kv = kv_of(sg)
                 Q = qg[b, t0:t1, sg]                                   # [m, dg]
                 s = np.concatenate([Q @ kblk[b, :c, kv].T,
                                     (Q * kg[b, t0:t1, kv]).sum(-1, keepdims=True)], axis=1) / rdg
@@ -741,6 +766,8 @@ def router_bwd(q, k, wq, wk, w_qn, w_kn, idx, dlogg, theta: float, eps: float, h
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
+    if as64(wq).shape[0] != Hkv:
+        raise ValueError("router_bwd covers one gate per KV head")
     heads = np.arange(Hkv) if heads is None else np.asarray(heads)
     H = len(heads)
     idx = np.asarray(idx)[:, :, heads]
@@ -808,47 +835,51 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, K: int, scale: float,
            apply_gate: bool = True, units=None):
     """One decode step per sequence.
 
-    q [B,Hq,D]; q_gate [B,Hkv,dg]; k_cache, v_cache [B,Hkv,Lmax,D];
-    kg_cache [B,Hkv,NBmax,dg] (entry c = current block's prefix-pooled key);
-    ctx_len [B] counts the new token (at position L-1).
-    Returns o [B,Hq,D], idx [B,Hkv,K+1], logg [B,Hkv,K+1], near_tie [B,Hkv]
-    for the chosen (b, kappa) units (others left zero / -1).
+    q [B,Hq,D]; q_gate [B,Hs,dg] (Hs selection heads, see sel_heads);
+    k_cache, v_cache [B,Hkv,Lmax,D]; kg_cache [B,Hkv,NBmax,dg] (entry c =
+    current block's prefix-pooled key); ctx_len [B] counts the new token (at
+    position L-1).
+    Returns o [B,Hq,D], idx, logg [B,Hs,K+1], near_tie, gap [B,Hs] for the
+    chosen (b, selection head) units (others left zero / -1).
     apply_gate=False is the selection-only variant [R16].
     """
     q, q_gate = as64(q), as64(q_gate)
     ctx = np.asarray(ctx_len.cpu() if hasattr(ctx_len, "cpu") else ctx_len)
     B, Hq, D = q.shape
-    Hkv = q_gate.shape[1]
-    G = Hq // Hkv
+    Hs = q_gate.shape[1]
+    Hkv = k_cache.shape[1]
+    Gs, kv_of = sel_heads(Hq, Hkv, Hs)
     S = K + 1
     o = np.zeros((B, Hq, D))
-    idx = np.full((B, Hkv, S), -1, dtype=np.int64)
-    logg = np.full((B, Hkv, S), -np.inf)
-    near = np.zeros((B, Hkv), dtype=bool)
-    gap = np.full((B, Hkv), np.inf)
+    idx = np.full((B, Hs, S), -1, dtype=np.int64)
+    logg = np.full((B, Hs, S), -np.inf)
+    near = np.zeros((B, Hs), dtype=bool)
+    gap = np.full((B, Hs), np.inf)
     if units is None:
-        units = [(b, kv) for b in range(B) for kv in range(Hkv)]
-    for b, kv in units:
+        units = [(b, sg) for b in range(B) for sg in range(Hs)]
+    for b, sg in units:
+        kv = kv_of(sg)
         L = int(ctx[b])
         t = L - 1
         c = t // BLOCK
         kg = as64(kg_cache[b, kv, :c + 1])
-        s = gate_logits(q_gate[b, kv], kg[:c], kg[c])
+        s = gate_logits(q_gate[b, sg], kg[:c], kg[c])
         _, lg = log_gates(s)
         sel, nt = select_blocks(s, K)
-        idx[b, kv, :len(sel)] = sel
-        logg[b, kv, :len(sel)] = lg[sel]
-        near[b, kv] = nt
-        gap[b, kv] = kth_gap(s, K)
+        idx[b, sg, :len(sel)] = sel
+        logg[b, sg, :len(sel)] = lg[sel]
+        near[b, sg] = nt
+        gap[b, sg] = kth_gap(s, K)
         taus, slots = _row_keys(t, np.array(sel))
         Kr = as64(k_cache[b, kv, taus])
         Vr = as64(v_cache[b, kv, taus])
         bias = lg[np.array(sel)][slots] if apply_gate else np.zeros(len(taus))
-        Q = q[b, kv * G:(kv + 1) * G]
+        hs = slice(sg * Gs, (sg + 1) * Gs)
+        Q = q[b, hs]
         Lg = Q @ Kr.T * scale + bias
         P = np.exp(Lg - Lg.max(axis=1, keepdims=True))
         P /= P.sum(axis=1, keepdims=True)
-        o[b, kv * G:(kv + 1) * G] = P @ Vr
+        o[b, hs] = P @ Vr
     return dict(o=o, idx=idx, logg=logg, near_tie=near, gap=gap)
 
 
@@ -857,11 +888,13 @@ def decode(q, q_gate, k_cache, v_cache, kg_cache, ctx_len, K: int, scale: float,
 # --------------------------------------------------------------------------
 
 def router_param_count(Hq: int, Hkv: int, D: int, dg: int, layers: int,
-                       norm_weights: bool = True) -> int:
-    """Per layer: Qproj Hkv x (G*D) x dg, Kproj Hkv x 3D x dg over [max;min;mean],
-    plus the two dg-wide RMSNorm weights."""
+                       norm_weights: bool = True, per_query_head: bool = False) -> int:
+    """Per layer: Qproj Hkv x (G*D) x dg (one gate per KV head) or Hq x D x dg
+    (one gate per query head), Kproj Hkv x 3D x dg over [max;min;mean], plus
+    the two dg-wide RMSNorm weights."""
     G = Hq // Hkv
-    per = Hkv * G * D * dg + Hkv * 3 * D * dg + (2 * dg if norm_weights else 0)
+    qproj = Hq * D * dg if per_query_head else Hkv * G * D * dg
+    per = qproj + Hkv * 3 * D * dg + (2 * dg if norm_weights else 0)
     return per * layers
 
 

@@ -80,6 +80,7 @@ class Workload:
     eps: float = 1.0e-6
     kind: str = "prefill"          # "prefill" | "train" | "decode"
     skew: str = "none"             # "none" | "lognormal_block" | "shared_dir"
+    gate: str = "kv"               # "kv": one gate per KV head; "q": one per query head
     Lmin: int = 0                  # decode context length range (inclusive)
     Lmax: int = 0
 
@@ -90,6 +91,11 @@ class Workload:
     @property
     def NB(self) -> int:
         return -(-self.T // self.block)
+
+    @property
+    def Hs(self) -> int:
+        """Selection heads: heads that carry one gate each."""
+        return self.Hq if self.gate == "q" else self.Hkv
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -126,9 +132,9 @@ def budget_to_topk(budget: int, block: int = 64) -> int:
 
 def prefill_inputs(w: Workload, seed: int = 0, device="cpu", with_dout: bool = True,
                    dtype=torch.bfloat16) -> dict:
-    """q, k, v [B,T,H,D]; router weights Wq [Hkv,G*D,dg], Wk [Hkv,3D,dg]
-    (N(0,1)/sqrt(fan_in), bf16-representable); RMSNorm weights = 1 (fp32);
-    dO [B,T,Hq,D] when requested.
+    """q, k, v [B,T,H,D]; router weights Wq [Hkv,G*D,dg] (gate="q": [Hq,D,dg]),
+    Wk [Hkv,3D,dg] (N(0,1)/sqrt(fan_in), bf16-representable); RMSNorm weights
+    = 1 (fp32); dO [B,T,Hq,D] when requested.
 
     skew="lognormal_block": every 64-token block j of KV head kappa draws one
     s ~ LogNormal(0, 1) that multiplies all q rows of that head group and all
@@ -161,8 +167,12 @@ def prefill_inputs(w: Workload, seed: int = 0, device="cpu", with_dout: bool = T
             raise ValueError(w.skew)
         q, k = q32.to(dtype), k32.to(dtype)
     v = normal((B, T, Hkv, D), seed, c, TID_V, device=device, dtype=dtype)
-    wq = normal((Hkv, G * D, dg), seed, c, TID_WQ, device=device,
-                scale=1.0 / math.sqrt(G * D), dtype=torch.bfloat16)
+    if w.gate == "q":
+        wq = normal((Hq, D, dg), seed, c, TID_WQ, device=device,
+                    scale=1.0 / math.sqrt(D), dtype=torch.bfloat16)
+    else:
+        wq = normal((Hkv, G * D, dg), seed, c, TID_WQ, device=device,
+                    scale=1.0 / math.sqrt(G * D), dtype=torch.bfloat16)
     wk = normal((Hkv, 3 * D, dg), seed, c, TID_WK, device=device,
                 scale=1.0 / math.sqrt(3 * D), dtype=torch.bfloat16)
     out = dict(q=q, k=k, v=v, wq=wq, wk=wk,
@@ -184,7 +194,7 @@ def decode_inputs(w: Workload, seed: int = 0, device="cpu", Lmax: int | None = N
     """Batched single-token decode inputs in head-major cache layout.
 
     q [B,Hq,D] bf16; k_cache, v_cache [B,Hkv,Lmax,D] bf16 ~ N(0,1);
-    q_gate [B,Hkv,dg] and kg_cache [B,Hkv,NBmax,dg] fp32 ~ N(0,1) (the
+    q_gate [B,Hs,dg] and kg_cache [B,Hkv,NBmax,dg] fp32 ~ N(0,1) (the
     statistics of unit-RMS, norm-preserving-rotated router outputs; decode
     consumes them as given inputs); ctx_len [B] int32.
     """
@@ -195,7 +205,7 @@ def decode_inputs(w: Workload, seed: int = 0, device="cpu", Lmax: int | None = N
     c = w.cfg_id
     return dict(
         q=normal((w.B, w.Hq, w.D), seed, c, TID_Q, device=device),
-        q_gate=normal((w.B, w.Hkv, w.dg), seed, c, TID_QGATE, device=device,
+        q_gate=normal((w.B, w.Hs, w.dg), seed, c, TID_QGATE, device=device,
                       dtype=torch.float32),
         k_cache=normal((w.B, w.Hkv, Lmax, w.D), seed, c, TID_K, device=device),
         v_cache=normal((w.B, w.Hkv, Lmax, w.D), seed, c, TID_V, device=device),
@@ -232,16 +242,17 @@ def random_selection(w: Workload, seed: int = 0, device="cpu", K: int | None = N
     With iid inputs the router's own choices are statistically of this kind
     (adjacent tokens share no more blocks than chance), so this drives the
     attention kernels at full size with inputs that do not depend on the
-    router implementation.  Returns idx int32, logg fp32 [B,T,Hkv,K+1].
+    router implementation.  Returns idx int32, logg fp32 [B,T,Hs,K+1] (Hs
+    selection heads: Hkv, or Hq with one gate per query head).
     """
     K = w.topk if K is None else K
-    B, T, Hkv, NB = w.B, w.T, w.Hkv, w.NB
+    B, T, H, NB = w.B, w.T, w.Hs, w.NB
     S = K + 1
     g = generator("cpu", seed, w.cfg_id, TID_SEL)
     c = (torch.arange(T) // w.block).view(1, T, 1, 1)
-    idx = torch.full((B, T, Hkv, S), -1, dtype=torch.int64)
+    idx = torch.full((B, T, H, S), -1, dtype=torch.int64)
     if K > 0 and NB > 1:
-        keys = torch.rand((B, T, Hkv, NB), generator=g)
+        keys = torch.rand((B, T, H, NB), generator=g)
         j = torch.arange(NB).view(1, 1, 1, NB)
         keys = torch.where(j < c, keys, torch.full_like(keys, -1.0))
         top = torch.topk(keys, min(K, NB), dim=-1)
@@ -249,9 +260,9 @@ def random_selection(w: Workload, seed: int = 0, device="cpu", K: int | None = N
         chosen, _ = torch.sort(chosen, dim=-1)
         chosen = torch.where(chosen <= NB, chosen, torch.full_like(chosen, -1))
         idx[..., :chosen.shape[-1]] = chosen
-    nsel = torch.minimum(c.expand(B, T, Hkv, 1), torch.tensor(K)).squeeze(-1)   # [B,T,Hkv]
-    idx.scatter_(-1, nsel.unsqueeze(-1), c.expand(B, T, Hkv, 1).clone())
+    nsel = torch.minimum(c.expand(B, T, H, 1), torch.tensor(K)).squeeze(-1)   # [B,T,H]
+    idx.scatter_(-1, nsel.unsqueeze(-1), c.expand(B, T, H, 1).clone())
     g2 = generator("cpu", seed, w.cfg_id, TID_SELLOGG)
-    lg = torch.randn((B, T, Hkv, S), generator=g2) - torch.log(c.float() + 1.0)
+    lg = torch.randn((B, T, H, S), generator=g2) - torch.log(c.float() + 1.0)
     logg = torch.where(idx >= 0, lg, torch.full_like(lg, float("-inf")))
     return idx.to(torch.int32).to(device), logg.to(torch.float32).to(device)

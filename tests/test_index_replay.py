@@ -25,7 +25,10 @@ CSRC = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
 SHAPES = [(1, 1024, 2, 1, 3), (1, 1000, 8, 2, 7), (1, 700, 10, 2, 5), (2, 300, 2, 2, 2),
           (1, 50, 4, 1, 3), (1, 400, 4, 2, 0), (1, 600, 4, 1, 20), (1, 260, 8, 1, 3),
           (1, 8192, 32, 8, 31), (1, 32768, 32, 8, 31), (1, 32768, 40, 8, 63), (1, 4097, 24, 3, 9),
-          (1, 1000, 6, 2, 5), (1, 777, 21, 7, 4), (1, 333, 14, 2, 6)]
+          (1, 1000, 6, 2, 5), (1, 777, 21, 7, 4), (1, 333, 14, 2, 6),
+          # one gate per query head: Hq selection heads of one query head each
+          # (the dQ kernel's rows are then those of Hkv = Hq, G = 1)
+          (1, 1000, 8, 8, 7), (1, 8192, 32, 32, 31)]
 
 
 @pytest.fixture(scope="module")

@@ -602,3 +602,129 @@ def test_attn_head_matches_row_form_and_sdpa(shape):
             ref_o = sdpa64(x["q"][b:b + 1, :, hs], x["k"][b:b + 1, :, kv:kv + 1],
                            x["v"][b:b + 1, :, kv:kv + 1], mask=mask, scale=sc)
             assert np.abs(a["o"] - ref_o[0]).max() < 1e-11
+
+
+# ------------------------------------------------ one gate per query head
+
+def _qhead_case(T=260, Hq=4, Hkv=2, D=16, dg=8, K=2, seed=30):
+    w = synth.Workload("pin_q", 99, B=1, T=T, Hq=Hq, Hkv=Hkv, D=D, dg=dg, topk=K, theta=1e4,
+                       gate="q")
+    x = synth.prefill_inputs(w, seed=seed, dtype=torch.float32)
+    return w, {k: O.as64(v) for k, v in x.items()}
+
+
+def test_per_query_head_gates_equal_shared_gates_on_split_heads():
+    """One gate per query head is the shared-gate method on a problem whose
+    every query head has its own copy of its KV head (keys, values, Kproj):
+    selection, log-gates, outputs and gradients must agree, with dk, dv the
+    sums over the copies."""
+    w, x = _qhead_case()
+    G = w.G
+    sc = 1 / math.sqrt(w.D)
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], w.topk, w.theta, w.eps)
+    assert r["idx"].shape[2] == w.Hq
+    g = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], r["idx"], r["logg"], sc)
+    ks, vs = np.repeat(x["k"], G, axis=2), np.repeat(x["v"], G, axis=2)
+    wks = np.repeat(x["wk"], G, axis=0)
+    r2 = O.route(x["q"], ks, x["wq"], wks, x["w_qn"], x["w_kn"], w.topk, w.theta, w.eps)
+    np.testing.assert_array_equal(r["idx"], r2["idx"])
+    fin = np.isfinite(r["logg"])
+    np.testing.assert_allclose(r["logg"][fin], r2["logg"][fin], atol=1e-12)
+    g2 = O.attn_bwd(x["q"], ks, vs, x["dout"], r2["idx"], r2["logg"], sc)
+    for name in ("o", "lse", "dq", "dlogg"):
+        np.testing.assert_allclose(g[name], g2[name], atol=1e-12, err_msg=name)
+    B, T = w.B, w.T
+    np.testing.assert_allclose(g["dk"], g2["dk"].reshape(B, T, w.Hkv, G, w.D).sum(3), atol=1e-12)
+    np.testing.assert_allclose(g["dv"], g2["dv"].reshape(B, T, w.Hkv, G, w.D).sum(3), atol=1e-12)
+    ra = O.route_all(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], w.topk, w.theta,
+                     w.eps)
+    np.testing.assert_array_equal(ra["idx"], r["idx"])
+    for h in range(w.Hq):
+        a = O.attn_head(x["q"], x["k"], x["v"], r["idx"], r["logg"], sc, 0, h, dout=x["dout"])
+        np.testing.assert_allclose(a["o"], g["o"][0, :, h:h + 1], atol=1e-12)
+        np.testing.assert_allclose(a["dlogg"], g["dlogg"][0, :, h], atol=1e-12)
+
+
+def test_per_query_head_backward_matches_autograd_and_fd():
+    """Per-query-head selection: torch fp64 autograd of SDPA with each head's
+    own additive block bias, and central differences of the gather form."""
+    w, x = _qhead_case(T=190, K=1, seed=31)
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], 1, w.theta, w.eps)
+    sc = 1 / math.sqrt(w.D)
+    g = O.attn_bwd(x["q"], x["k"], x["v"], x["dout"], r["idx"], r["logg"], sc)
+    bias = O.dense_bias(r["idx"], r["logg"], w.T)            # [B,Hq,T,T]
+    G = w.G
+    qt = torch.tensor(x["q"], requires_grad=True)
+    kt = torch.tensor(x["k"], requires_grad=True)
+    vt = torch.tensor(x["v"], requires_grad=True)
+    mt = torch.tensor(bias, requires_grad=True)
+    with sdpa_kernel(SDPBackend.MATH):
+        o = F.scaled_dot_product_attention(
+            qt.permute(0, 2, 1, 3), kt.permute(0, 2, 1, 3).repeat_interleave(G, 1),
+            vt.permute(0, 2, 1, 3).repeat_interleave(G, 1), attn_mask=mt,
+            scale=sc).permute(0, 2, 1, 3)
+    (o * torch.tensor(x["dout"])).sum().backward()
+    np.testing.assert_allclose(g["o"], o.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dq"], qt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(g["dk"], kt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(g["dv"], vt.grad.numpy(), atol=1e-11)
+    dm = mt.grad.numpy()
+    for t in range(w.T):
+        for h in range(w.Hq):
+            for s_i, j in enumerate(r["idx"][0, t, h]):
+                if j >= 0:
+                    assert abs(g["dlogg"][0, t, h, s_i] - dm[0, h, t, 64 * j:64 * j + 64].sum()) < 1e-11
+    np.testing.assert_allclose(g["dlogg"].sum(-1), 0.0, atol=1e-12)
+    # central differences of L = sum o * dO on log g entries
+    rng = np.random.default_rng(32)
+
+    def loss(logg):
+        o2, _ = O.attn_fwd_rows(x["q"], x["k"], x["v"], r["idx"], logg, sc)
+        return float((o2 * x["dout"]).sum())
+
+    for _ in range(6):
+        while True:
+            pos = tuple(int(rng.integers(0, s)) for s in r["logg"].shape)
+            if np.isfinite(r["logg"][pos]):
+                break
+        p, m = r["logg"].copy(), r["logg"].copy()
+        p[pos] += 1e-6
+        m[pos] -= 1e-6
+        fd = (loss(p) - loss(m)) / 2e-6
+        assert abs(fd - g["dlogg"][pos]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_per_query_head_router_parameter_count_matches_model_card():
+    """A gate per query head (Qproj Hq x D x dg) has exactly as many weights as
+    one per KV head over the concatenated group (Hkv x G*D x dg), so the
+    released sizes (model card checkpoint table) do not decide between them."""
+    g = json.load(open(os.path.join(GOLD, "router_param_counts.json")))
+    for m in g["models"]:
+        a = O.router_param_count(m["Hq"], m["Hkv"], m["D"], m["dg"], m["layers"])
+        b = O.router_param_count(m["Hq"], m["Hkv"], m["D"], m["dg"], m["layers"],
+                                 per_query_head=True)
+        assert a == b and round(b / 1e6, 1) == m["params_M"]
+
+
+def test_per_query_head_decode_equals_prefill_last_row():
+    """Decode with one gate per query head equals prefill row L-1."""
+    w, x = _qhead_case(T=300, K=2, seed=33)
+    r = O.route(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], 2, w.theta, w.eps)
+    sc = 1 / math.sqrt(w.D)
+    o_pre, _ = O.attn_fwd_rows(x["q"], x["k"], x["v"], r["idx"], r["logg"], sc)
+    kg = O.gate_key_all(x["k"], x["wk"], x["w_kn"], w.theta, w.eps)
+    L = np.array([300, 130, 64, 1])
+    B = len(L)
+    NB = -(-w.T // 64)
+    kc = np.repeat(x["k"][0].transpose(1, 0, 2)[None], B, axis=0)
+    vc = np.repeat(x["v"][0].transpose(1, 0, 2)[None], B, axis=0)
+    kgc = np.zeros((B, w.Hkv, NB, w.dg))
+    for b, Lb in enumerate(L):
+        c = (Lb - 1) // 64
+        for j in range(c):
+            kgc[b, :, j] = kg[0, 64 * j + 63]
+        kgc[b, :, c] = kg[0, Lb - 1]
+    d = O.decode(x["q"][0, L - 1], r["qg"][0, L - 1], kc, vc, kgc, L, 2, sc)
+    for b, Lb in enumerate(L):
+        np.testing.assert_array_equal(d["idx"][b], r["idx"][0, Lb - 1])
+        np.testing.assert_allclose(d["o"][b], o_pre[0, Lb - 1], atol=1e-12)
