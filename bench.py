@@ -215,10 +215,212 @@ def assert_sound(sas, what: str, **tensors):
         sys.exit(3)
 
 
+def time_layer(sas, w, K: int, seed: int, steps: int, warmup: int, backward: bool = True,
+               stats: bool = False) -> dict:
+    """One prefill / training layer of workload w at Top-K K, inputs resident
+    in HBM: gate router -> Top-K -> sparse attention forward (with the fp32
+    output when the backward follows) -> backward.  Returns ms per step,
+    per-stage ms, effective TFLOP/s (4 D forward + 10 D backward per attended
+    pair) and, with stats, the locality of the router's selection."""
+    import torch
+    import synth
+
+    dev = torch.device("cuda:0")
+    x = synth.prefill_inputs(w, seed=seed, device=dev, with_dout=backward)
+    B, T, Hq, Hkv, D, dg = w.B, w.T, w.Hq, w.Hkv, w.D, w.dg
+    Hs, S = w.Hs, K + 1
+    pq = w.gate == "q"
+    flags = sas.FLAG_GATE_PER_QUERY_HEAD if pq else 0
+    d = sas.make_dims(B, T, Hq, Hkv, D, dg, K, w.theta, w.eps, flags=flags)
+    ws_gate = torch.empty(sas.workspace_size(sas.OP_GATE_SCORE, d), dtype=torch.uint8, device=dev)
+    ws_fwd = torch.empty(sas.workspace_size(sas.OP_FWD, d), dtype=torch.uint8, device=dev)
+    ws_bwd = (torch.empty(sas.workspace_size(sas.OP_BWD, d), dtype=torch.uint8, device=dev)
+              if backward else None)
+    f32 = dict(dtype=torch.float32, device=dev)
+    qg = torch.empty((B, T, Hs, dg), **f32)
+    kg = torch.empty((B, T, Hkv, dg), **f32)
+    idx = torch.empty((B, T, Hs, S), dtype=torch.int32, device=dev)
+    logg = torch.empty((B, T, Hs, S), **f32)
+    glse = torch.empty((B, T, Hs), **f32)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, T, Hq), **f32)
+    o32 = torch.empty((B, T, Hq, D), **f32) if backward else None
+    if backward:
+        dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+        dlogg = torch.empty_like(logg)
+    sc = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        sas.gate_score(x["q"], x["k"], x["wq"], x["wk"], x["w_qn"], x["w_kn"], K, w.theta, w.eps,
+                       q_gate=qg, k_gate=kg, workspace=ws_gate, per_query_head=pq)
+        if ev:
+            ev[1].record(stream)
+        sas.topk_blocks(qg, kg, K, Hq, D, out=(idx, logg, glse))
+        if ev:
+            ev[2].record(stream)
+        sas.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, logg, sc, o=o, lse=lse, o_f32=o32,
+                            workspace=ws_fwd)
+        if ev:
+            ev[3].record(stream)
+        if backward:
+            sas.sparse_attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, logg, sc,
+                                workspace=ws_bwd, out=(dq, dk, dv, dlogg), o_f32=o32)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    outs = dict(o=o, lse=lse)
+    if backward:
+        outs.update(o_f32=o32, dq=dq, dk=dk, dv=dv, dlogg=dlogg)
+    assert_sound(sas, f"{w.name} K={K}", **outs)
+    ms = t0.elapsed_time(t1) / steps
+    st = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(4)]
+    pairs = attended_pairs(T, K) * Hq * B
+    fl_f, fl_b = 4.0 * D * pairs, (10.0 * D * pairs if backward else 0.0)
+    res = {"workload": w.name, "gate": "per_query_head" if pq else "per_kv_head", "topk": K,
+           "budget": 64 * (K + 1), "Hq": Hq, "Hkv": Hkv, "T": T,
+           "ms_per_step": round(ms, 4),
+           "stages_ms": {"gate_score": round(st[0], 4), "topk": round(st[1], 4),
+                         "fwd": round(st[2], 4), "bwd": round(st[3], 4)},
+           "tflops": round((fl_f + fl_b) / (ms * 1e-3) / 1e12, 2),
+           "fwd_tflops": round(fl_f / (st[2] * 1e-3) / 1e12, 2),
+           "frac_of_peak": round((fl_f + fl_b) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if backward:
+        res["bwd_tflops"] = round(fl_b / (st[3] * 1e-3) / 1e12, 2)
+    if stats:
+        res["selection"] = selection_stats(idx)
+    return res
+
+
+def time_decode_budget(sas, wd, K: int, seed: int, steps: int) -> dict:
+    """Cold decode step (a 1 GiB read between steps evicts the cache) at
+    Top-K K (budget 64 (K + 1)) on the batched decode workload."""
+    import torch
+    import synth
+
+    dev = torch.device("cuda:0")
+    xd = synth.decode_inputs(wd, seed=seed, device=dev)
+    od = torch.empty((wd.B, wd.Hq, wd.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(sas.decode_workspace_size(sas.DecodeDims(
+        wd.B, wd.Hq, wd.Hkv, wd.D, wd.dg, 64, K, xd["Lmax"], xd["NBmax"], 1)),
+        dtype=torch.uint8, device=dev)
+    sc = 1.0 / math.sqrt(wd.D)
+
+    def dstep():
+        sas.decode(xd["q"], xd["q_gate"], xd["k_cache"], xd["v_cache"], xd["kg_cache"],
+                   xd["ctx_len"], K, sc, want_idx=False, workspace=ws, out=(od, None, None))
+
+    for _ in range(3):
+        dstep()
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cold = []
+    for _ in range(steps):
+        flush.sum()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        dstep()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a0.elapsed_time(a1) * 1e3)
+    assert_sound(sas, f"decode K={K}", o=od)
+    cold.sort()
+    us = cold[len(cold) // 2]
+    kvb, gkb, smb = decode_bytes(xd["ctx_len"].cpu().tolist(), wd.Hkv, wd.D, wd.dg, K, wd.G)
+    tot = kvb + gkb + smb
+    return {"budget": 64 * (K + 1), "topk": K, "us_per_step_cold": round(us, 2),
+            "algorithmic_bytes": tot, "GBps_cold": round(tot / (us * 1e-6) / 1e9, 1),
+            "KV_GBps_cold": round(kvb / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(tot / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+COUNTER_KERNELS = ("sparse_fwd_kernel", "dkdv_kernel", "dq_kernel", "topk_kernel",
+                   "gate_query_kernel", "gate_key_kernel")
+
+
+def summarize_counters(dirs, out_json: str):
+    """Per-kernel averages (per dispatch) of every counter found in rocprofv3
+    --pmc runs (one directory per pass) for the attention, Top-K and router
+    kernels, with derived figures: executed MFMA FLOPs (the MOPS counters
+    count 512 FLOPs each), MFMA busy share of the SIMD cycles, L2 hit rate,
+    and the bytes behind the L1 -> L2 requests (128-byte lines).  Written to
+    profiles/counters.json with each kernel's source hash."""
+    import csv
+    import glob
+
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = next((n for n in COUNTER_KERNELS if n in r["Kernel_Name"]), None)
+                if k is None:
+                    continue
+                vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
+    src = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
+           "dq_kernel": "attn_bwd.hip", "topk_kernel": "topk.hip",
+           "gate_query_kernel": "router.hip", "gate_key_kernel": "router.hip"}
+    res, lines = {}, []
+    for k, cs in vals.items():
+        e = {c: sum(v) / len(v) for c, v in cs.items()}
+        mops = sum(e.get(c, 0.0) for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                           "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                                           "SQ_INSTS_VALU_MFMA_MOPS_F32"))
+        d = {"counters_per_dispatch": {c: round(v, 1) for c, v in e.items()},
+             "dispatches": max(len(v) for v in cs.values())}
+        if mops:
+            d["executed_mfma_flops"] = mops * 512
+        if e.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in e:
+            # GRBM_GUI_ACTIVE comes summed over the 8 XCDs; 1024 SIMDs
+            d["mfma_busy_frac"] = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (e["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        if e.get("TCC_REQ_sum"):
+            d["l2_hit_rate"] = e.get("TCC_HIT_sum", 0.0) / e["TCC_REQ_sum"]
+        if "TCP_TCC_READ_REQ_sum" in e:
+            d["l1_to_l2_read_bytes"] = e["TCP_TCC_READ_REQ_sum"] * 128
+        d["source_hash"] = source_hash([os.path.join(csrc, f) for f in
+                                        (src[k], "sas_device.h", "sas_kernels.h")])
+        res[k] = d
+        lines.append(f"{k}: " + ", ".join(f"{n} {d[n]:.4g}" for n in
+                                          ("executed_mfma_flops", "mfma_busy_frac", "l2_hit_rate",
+                                           "l1_to_l2_read_bytes") if n in d))
+    json.dump(res, open(out_json, "w"), indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
+def load_counters(kernel_key: str, src_hash: str):
+    """Counter figures of profiles/counters.json for a kernel, if taken on
+    the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        e = json.load(open(p)).get(kernel_key)
+    except Exception:
+        return None
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return {k: e[k] for k in ("executed_mfma_flops", "mfma_busy_frac", "l2_hit_rate",
+                              "l1_to_l2_read_bytes") if k in e}
+
+
 def cpu_baseline(seed: int, n_tokens: int):
     """The fp64 oracle, as it stands, on a bounded sample of the 32K workload:
     forward + backward of every query head for n_tokens query tokens spread
-    over the sequence (all 8 KV heads), BLAS limited to one thread."""
+    over the sequence (all 8 KV heads), with BLAS and torch on the host's
+    cores (OMP_NUM_THREADS if set, else every core)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -231,8 +433,9 @@ def cpu_baseline(seed: int, n_tokens: int):
     x64 = {k: O.as64(v) for k, v in x.items()}
     T = w.T
     toks = np.unique(np.linspace(64 * (w.topk + 2), T - 1, n_tokens).astype(int))
-    with threadpool_limits(limits=1):
-        torch.set_num_threads(1)
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    with threadpool_limits(limits=cores):
+        torch.set_num_threads(cores)
         r = O.route(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"], w.topk,
                     w.theta, w.eps, tokens=toks)
         S = w.topk + 1
@@ -249,9 +452,10 @@ def cpu_baseline(seed: int, n_tokens: int):
         c = t // 64
         n = 64 * min(w.topk, c) + (t - 64 * c) + 1
         flops += 14 * w.D * n * w.Hq
-    return dict(value=float(round(flops / dt / 1e12, 6)), unit="TFLOP/s", cores=1, kind="oracle",
+    return dict(value=float(round(flops / dt / 1e12, 6)), unit="TFLOP/s", cores=cores,
+                kind="oracle",
                 sample=f"{len(toks)} query tokens x {w.Hq} heads of the 32K training layer, "
-                       f"fp64 forward+backward (numpy, 1 BLAS thread), {dt:.1f} s",
+                       f"fp64 forward+backward (numpy, {cores} BLAS threads), {dt:.1f} s",
                 seconds=round(dt, 2))
 
 
@@ -266,14 +470,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-router-bwd", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 8K, G=5 budget-sweep, per-query-head and decode-budget timings")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for traffic)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/counters.json from rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, os.path.join(ROOT, "profiles", "traffic.json"))
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, os.path.join(ROOT, "profiles", "counters.json"))
         return
 
     if args.gpus != 1:
@@ -426,6 +637,17 @@ def main():
         "algorithmic_flops_per_launch": kflops[dom],
         "launch_ms": round(kern_ms[dom], 4),
     }
+    cnt = load_counters(dom, dom_hash)
+    if cnt:
+        # executed MFMA work (masked tile rows and the hi + lo halves of the
+        # fp32-accurate products included) against the algorithmic FLOPs
+        roofline["counters"] = dict(cnt, executed_over_algorithmic=round(
+            cnt["executed_mfma_flops"] / kflops[dom], 3)) if "executed_mfma_flops" in cnt else cnt
+    for kname in kflops:
+        c = load_counters(kname, source_hash([os.path.join(csrc, f) for f in
+                                              (ksrc[kname], "sas_device.h", "sas_kernels.h")]))
+        if c:
+            kernels[kname]["counters"] = c
 
     out = {
         "metric": "sparse-attn fwd+bwd TFLOP/s @32K (% MFMA peak); decode KV GB/s @budget 2048",
@@ -629,6 +851,36 @@ def main():
                          "frac": round(tot / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("sas_decode", dec_hash)},
         }
+    # ------------------------------------------------------------ other configurations
+    # (reported beside the headline, not part of it): the 8K prefill layer
+    # (router + Top-K + forward); the Qwen3-14B-shaped G = 5 layer at budgets
+    # 1,024 / 2,048 / 4,096 for both skew recipes, with the locality of the
+    # router's selections; the 32K training layer with one gate per query
+    # head; decode at budgets 1,024 and 4,096
+    if not args.no_configs:
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        cfg = {"prefill_8k": time_layer(sas, synth.PREFILL_8K, synth.PREFILL_8K.topk, args.seed,
+                                        steps=10, warmup=3, backward=False)}
+        skew = []
+        for w5 in (synth.SKEW_32K, synth.SKEW5B_32K):
+            for K5 in (15, 31, 63):
+                skew.append(time_layer(sas, w5.replace(topk=K5), K5, args.seed, steps=3,
+                                       warmup=1, stats=True))
+                gc.collect()
+                torch.cuda.empty_cache()
+        cfg["g5_32k_budgets"] = skew
+        wq = synth.TRAIN_32K.replace(name=synth.TRAIN_32K.name + "_per_query_head_gates", gate="q")
+        cfg["train_32k_per_query_head"] = time_layer(sas, wq, wq.topk, args.seed, steps=3,
+                                                     warmup=1, stats=True)
+        gc.collect()
+        torch.cuda.empty_cache()
+        if "decode" in out:
+            out["decode"]["other_budgets"] = [
+                time_decode_budget(sas, synth.DECODE_B64, K4, args.seed, args.decode_steps)
+                for K4 in (15, 63)]
+        out["configs"] = cfg
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)
     print(json.dumps(out), flush=True)

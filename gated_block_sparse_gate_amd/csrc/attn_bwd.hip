@@ -234,30 +234,46 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     seg_cum[p.kdiv] = cum;
   }
   __syncthreads();
-  const int n = seg_cum[p.kdiv];
+  // uniform over the workgroup: read from LDS, so made scalar explicitly (a
+  // loop bound the compiler sees as per-lane turns every branch on it into
+  // an exec-masked one)
+  const int n = __builtin_amdgcn_readfirstlane(seg_cum[p.kdiv]);
   const int nit = (n + 2 * TPT - 1) / (2 * TPT);
+  const size_t bs0 = static_cast<size_t>(b) * p.Hs + kv * p.kdiv;
+  const int32_t* const ent0 =            // head i = 0's list (the only one when kdiv == 1)
+      p.entries + bs0 * static_cast<size_t>(p.T) * p.S + p.rowptr[bs0 * (p.NB + 1) + j];
   const float sl2 = p.scale_log2;
 
   // ---- per-row metadata (threads 0..31, one row each)
   const int mr = tid & 31, mtt = mr >> 4, mrr = mr & 15;
   const int mhh = mrr - (mrr / G) * G;
-  // CSR entry of this row in tile pair `it` (-1 past the lists), repacked as
-  // (token << 9) | (head index i in the KV head's group << 6) | slot; it is
-  // checked only when used, an iteration later, so the load is not waited for
-  auto load_ent = [&](int it) -> int {
-    const int ti = (nit - 1 - it) * 2 * TPT + mtt * TPT + mrr / G;
-    if (mrr >= RT || ti >= n) return -1;
+  // list position of this row in tile pair `it`, and which selection head's
+  // list (i, the head's index in the KV head's group) it falls in
+  auto ent_pos = [&](int it) -> int { return (nit - 1 - it) * 2 * TPT + mtt * TPT + mrr / G; };
+  auto seg_of = [&](int ti) -> int {
     int i = 0;
     while (i + 1 < p.kdiv && seg_cum[i + 1] <= ti) ++i;
-    const int raw = p.entries[seg_base[i] + (ti - seg_cum[i])];
-    return ((raw >> 6) << 9) | (i << 6) | (raw & 63);
+    return i;
+  };
+  // raw CSR entry (token << 6 | slot) of this row in tile pair `it` (-1 past
+  // the lists); it is checked and repacked only when used, an iteration
+  // later, so the load is not waited for here
+  auto load_ent = [&](int it) -> int {
+    const int ti = ent_pos(it);
+    if (mrr >= RT || ti >= n) return -1;
+    if (p.kdiv == 1) return ent0[ti];
+    const int i = seg_of(ti);
+    return p.entries[seg_base[i] + (ti - seg_cum[i])];
   };
   float r_lse = -INFINITY, r_del = 0.f, r_lg = 0.f;
   int r_t = -1, r_src = -1, r_en = -1;
-  auto meta_issue = [&](int en) {
+  // metadata of the row whose raw entry `en` load_ent(it) gave; the entry is
+  // kept repacked as (token << 9) | (i << 6) | slot
+  auto meta_issue = [&](int en, int it) {
     if (en >= 0) {
-      const int tk = en >> 9, s = en & 63;
+      const int tk = en >> 6, s = en & 63;
       if (tk < j * 64 || tk >= p.T || s >= p.S) en = -1;
+      else en = (tk << 9) | ((p.kdiv == 1 ? 0 : seg_of(ent_pos(it))) << 6) | s;
     }
     r_t = -1; r_src = -1; r_en = en;
     if (en >= 0) {
@@ -319,9 +335,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   if (tid < 32) {
     const int en0 = load_ent(0);
     const int en1 = (nit > 1) ? load_ent(1) : -1;
-    meta_issue(en0);
+    meta_issue(en0, 0);
     meta_store(0);
-    meta_issue(en1);
+    meta_issue(en1, 1);
     meta_store(1);
     en_n2 = (nit > 2) ? load_ent(2) : -1;
   }
@@ -400,7 +416,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   for (int it = 0; it < nit; ++it) {
     const int buf = it & 1, ms = it % 3;
     if (tid < 32) {
-      if (it + 2 < nit) meta_issue(en_n2);
+      if (it + 2 < nit) meta_issue(en_n2, it + 2);
       en_n3 = (it + 3 < nit) ? load_ent(it + 3) : -1;
     }
     if (it + 1 < nit) rows_issue((it + 1) % 3);
