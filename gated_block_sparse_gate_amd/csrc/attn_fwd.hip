@@ -141,6 +141,8 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     // lds_swz(r) of K row r = p / KCPR, else chunk (v % 8) ^ tr_swz(d) of V^T
     // row d = v / 8 (v = p - KU); lane i of copy m fetches unit 64 m + i of
     // its stager's tile.
+    // the copies are what the compute waves wait on: issue them first
+    __builtin_amdgcn_s_setprio(3);
     const int stg = wv - ncw;
     const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
     const uint16_t* vtbase =
