@@ -77,48 +77,89 @@ __device__ __forceinline__ void norm_rope_store(floatx4 (&acc)[DG / 16], const f
   }
 }
 
-// One wave = 32 token rows x DG gate columns; workgroup = 4 waves = 128 rows
-// of one selection head.
+// One workgroup = 128 token rows of one selection head, wave w owning rows
+// 32 w .. 32 w + 31 (two 16-row tiles) x all DG gate columns.  The weight
+// columns are staged through LDS in 32-wide steps shared by the four waves
+// (asynchronous global -> LDS copies, double-buffered; 64-byte rows whose
+// 16-byte chunks are XOR-swizzled by (row >> 2) & 3, so that 16 lanes reading
+// one chunk of 16 consecutive rows hit distinct banks), and each wave's query
+// operands for the next step load while the current step runs.
 template <int DG>
 __global__ __launch_bounds__(256) void gate_query_kernel(RouterParams p) {
   constexpr int NT = DG / 16;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int MT = 2;
+  constexpr int WROWB = 64;                      // bytes per staged weight row
+  __shared__ __attribute__((aligned(16))) uint8_t wls[2][DG * WROWB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int sg = blockIdx.y;
   const int F = p.Gs * p.D;
   const long nrows = static_cast<long>(p.B) * p.T;
-  const long r0 = static_cast<long>(blockIdx.x) * 128 + wv * 32;
+  const long r0 = static_cast<long>(blockIdx.x) * (64 * MT) + wv * 16 * MT;
 
-  floatx4 acc[2][NT];
+  floatx4 acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* xr[2];
-  bool ok[2];
+  const uint16_t* xr[MT];
+  bool ok[MT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const long r = r0 + mt * 16 + l16;
     ok[mt] = r < nrows;
     xr[mt] = p.q + ((ok[mt] ? r : 0) * p.Hq + static_cast<long>(sg) * p.Gs) * p.D;
   }
   const uint16_t* wt = p.wqT + static_cast<size_t>(sg) * DG * F;
-  for (int f = 0; f < F; f += 32) {
-    uint4 av[2];
+  // weight columns f .. f + 31 of all DG rows into buffer buf: copy m moves
+  // units 64 m .. 64 m + 63 (unit u = row u / 4, slot u % 4 holding chunk
+  // (u % 4) ^ swizzle)
+  auto wstage = [&](int f, int buf) __attribute__((always_inline)) {
+    for (int m = wv; m < DG / 16; m += 4) {
+      const int u = m * 64 + lane, n = u >> 2;
+      load_lds16(wt + static_cast<size_t>(n) * F + f + (((u & 3) ^ ((n >> 2) & 3)) << 3),
+                 &wls[buf][m * 1024]);
+    }
+  };
+  auto qload = [&](int f, uint4 (&a)[MT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      av[mt] = ok[mt] ? *reinterpret_cast<const uint4*>(xr[mt] + f + g4 * 8)
-                      : make_uint4(0, 0, 0, 0);
+    for (int mt = 0; mt < MT; ++mt)
+      a[mt] = ok[mt] ? ld16(xr[mt] + f + g4 * 8) : make_uint4(0, 0, 0, 0);
+  };
+  uint4 av[MT];
+  wstage(0, 0);
+  qload(0, av);
+  wait_vmem_all();
+  __syncthreads();
+  for (int f = 0, it = 0; f < F; f += 32, ++it) {
+    const int buf = it & 1;
+    const bool more = f + 32 < F;
+    uint4 an[MT];
+    if (more) {
+      wstage(f + 32, buf ^ 1);     // the copies first, then this wave's query loads
+      qload(f + 32, an);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint4 bv = *reinterpret_cast<const uint4*>(wt + (nt * 16 + l16) * F + f + g4 * 8);
+      const int n = nt * 16 + l16;
+      const uint4 bv = ld16(&wls[buf][n * WROWB + ((g4 ^ ((n >> 2) & 3)) << 4)]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16x16x32(av[mt], bv, acc[mt][nt]);
+      for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma16x16x32(av[mt], bv, acc[mt][nt]);
     }
+    if (more) {
+      // all but the MT query loads: the next step's weights have landed
+      static_assert(MT < 16, "vmcnt immediate");
+      __builtin_amdgcn_s_waitcnt(0x0f70 | MT);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) av[mt] = an[mt];
+    }
+    __syncthreads();
   }
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     int pos[4];
     float* out[4];
 #pragma unroll
@@ -147,6 +188,9 @@ __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
   __shared__ float segmx[NSEG * D];
   __shared__ float segmn[NSEG * D];
   __shared__ float wsum[4][DG];
+  // weight columns of 32-wide steps, double-buffered (as in gate_query_kernel)
+  constexpr int WROWB = 64;
+  __shared__ __attribute__((aligned(16))) uint8_t wls[2][DG * WROWB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -154,6 +198,16 @@ __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
   const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int t0 = c * 64;
   const int ntok = min(64, p.T - t0);
+
+  const uint16_t* wt = p.wkT + static_cast<size_t>(kv) * DG * (3 * D);
+  auto wstage = [&](int f, int buf) __attribute__((always_inline)) {
+    for (int m = wv; m < DG / 16; m += 4) {
+      const int u = m * 64 + lane, n = u >> 2;
+      load_lds16(wt + static_cast<size_t>(n) * (3 * D) + f + (((u & 3) ^ ((n >> 2) & 3)) << 3),
+                 &wls[buf][m * 1024]);
+    }
+  };
+  wstage(0, 0);                 // lands while the block is pooled
 
   for (int u = tid; u < 64 * (D / 8); u += 256) {
     const int row = u / (D / 8), ch = u - row * (D / 8);
@@ -210,7 +264,6 @@ __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
   }
   __syncthreads();
 
-  const uint16_t* wt = p.wkT + static_cast<size_t>(kv) * DG * (3 * D);
   const int arow = wv * 16 + l16;
   floatx4 amm[NT], ak[NT];
 #pragma unroll
@@ -218,24 +271,28 @@ __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
     amm[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     ak[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int f = 0; f < 2 * D; f += 32) {
-    const uint16_t* src = (f < D) ? &pmx[arow * KP + f] : &pmn[arow * KP + f - D];
-    const uint4 av = *reinterpret_cast<const uint4*>(src + g4 * 8);
+  // inputs f .. f + 31 of the 3D (max, min, mean sections) against the
+  // staged weight columns; the next step's weights land meanwhile
+  wait_vmem_all();
+  __syncthreads();
+  for (int f = 0, it = 0; f < 3 * D; f += 32, ++it) {
+    const int buf = it & 1;
+    const bool more = f + 32 < 3 * D;
+    if (more) wstage(f + 32, buf ^ 1);
+    const uint16_t* src = (f < D) ? &pmx[arow * KP + f]
+                                  : (f < 2 * D) ? &pmn[arow * KP + f - D] : &kb[arow * KP + f - 2 * D];
+    const uint4 av = ld16(src + g4 * 8);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint4 bv =
-          *reinterpret_cast<const uint4*>(wt + (nt * 16 + l16) * (3 * D) + f + g4 * 8);
-      amm[nt] = mfma16x16x32(av, bv, amm[nt]);
+      const int n = nt * 16 + l16;
+      const uint4 bv = ld16(&wls[buf][n * WROWB + ((g4 ^ ((n >> 2) & 3)) << 4)]);
+      if (f < 2 * D)
+        amm[nt] = mfma16x16x32(av, bv, amm[nt]);
+      else
+        ak[nt] = mfma16x16x32(av, bv, ak[nt]);
     }
-  }
-  for (int f = 0; f < D; f += 32) {
-    const uint4 av = *reinterpret_cast<const uint4*>(&kb[arow * KP + f + g4 * 8]);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint4 bv =
-          *reinterpret_cast<const uint4*>(wt + (nt * 16 + l16) * (3 * D) + 2 * D + f + g4 * 8);
-      ak[nt] = mfma16x16x32(av, bv, ak[nt]);
-    }
+    if (more) wait_vmem_all();
+    __syncthreads();
   }
 
   // prefix sum of the per-token mean-section projections over the block
