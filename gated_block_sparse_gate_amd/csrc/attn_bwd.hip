@@ -709,7 +709,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
             failed = true;
             break;
           }
-          __builtin_amdgcn_s_sleep(1);
+          __builtin_amdgcn_s_sleep(kStagerNap);
         }
         if (failed) break;
       }
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
         failed = true;
         return;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(kComputeNap);
     }
     const uint8_t* st = ring + sl * STAGE;
     int tbase = tbase0;

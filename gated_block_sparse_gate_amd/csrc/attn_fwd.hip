@@ -184,7 +184,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
             failed = true;
             break;
           }
-          __builtin_amdgcn_s_sleep(1);
+          __builtin_amdgcn_s_sleep(kStagerNap);
         }
         if (failed) break;
       }
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         failed = true;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(kComputeNap);
     }
     if (failed) break;
     const uint8_t* st = ring + sl * STAGE;

@@ -237,7 +237,12 @@ __device__ __forceinline__ void wait_vmem_all() {
 // of one wave are performed in order, so a bump issued after a wave's stores
 // (or reads) of a slot is observed only after them; the asm statements keep the
 // compiler from moving memory accesses across a bump or a poll.
-constexpr int kSpinLimit = 1 << 21;   // polls (about 0.1 s) before a wait gives up
+constexpr int kSpinLimit = 1 << 21;   // polls (0.1 - 0.5 s) before a wait gives up
+// s_sleep between polls (about 64 cycles per unit): a compute wave's poll
+// takes SIMD issue slots from the waves that have work, so compute waves nap
+// longer (512 cycles, a seventh of a block visit) than the stagers
+constexpr int kComputeNap = 8;
+constexpr int kStagerNap = 4;
 
 // The counters are read with plain LDS loads and bumped with an LDS atomic
 // add written as an instruction without results: the compiler treats atomic
