@@ -16,7 +16,10 @@ it), on outputs the fp64 oracle computes one by one:
 * batched decode at 64 sequences with contexts U[8192, 65536] and budget
   2,048: indices of every (sequence, KV head) unit, outputs of sampled units;
 * router backward at the 32K training shape: every output, against the
-  oracle taken one KV head at a time.
+  oracle taken one KV head at a time;
+* the longest sequence the ABI takes (T = 65,536) with the largest budget
+  (K = 63): router and Top-K on every row, forward and backward on sampled
+  rows and key blocks.
 
 Tolerances are those of the small-shape parity tests: for bf16 outputs the
 max-abs bound applies to the error beyond half a bf16 ulp of the exact value
@@ -225,6 +228,65 @@ def test_full_attention(w, K, bwd, sel):
         lo, hi = 64 * j, min(64 * j + 64, w.T)
         check(f"dk[{kv2},{j}]", dk[b, lo:hi, kv2], rdk, rounding_floor=skew)
         check(f"dv[{kv2},{j}]", dv[b, lo:hi, kv2], rdv, rounding_floor=skew)
+
+
+# ------------------------------------------------- the longest sequence
+
+MAXLEN = synth.Workload("max_T65536_G2_K63", 91, B=1, T=65536, Hq=4, Hkv=2, D=128, dg=128,
+                        topk=63, kind="train")
+
+
+def test_max_length_chain():
+    """The ABI's longest sequence (T = 65,536: 1,024 blocks, the Top-K
+    kernel's widest score rows) with the largest budget (K = 63, 64 slots):
+    router and Top-K on every row against the oracle router; forward and
+    backward on the oracle router's selection, on sampled rows of every head
+    and two key blocks; d log g sums to zero on every row."""
+    w = MAXLEN
+    x, x64, d = inputs(w)
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    idx, logg, glse, _ = sas.topk_blocks(qg, kg, w.topk, w.Hq, w.D)
+    torch.cuda.synchronize()
+    ra = oracle_route(w, x64)
+    check("q_gate", qg, ra["qg"], ROUTER_ABS, ROUTER_ABS)
+    check("k_gate", kg, ra["kg"], ROUTER_ABS, ROUTER_ABS)
+    ok = ~ra["near_tie"]
+    assert ok.mean() > 0.99, "too many near-tie rows"
+    gi = idx.cpu().numpy()
+    bad = (gi != ra["idx"]).any(-1) & ok
+    assert not bad.any(), f"{int(bad.sum())} rows differ, first at {np.argwhere(bad)[0].tolist()}"
+    fin = np.isfinite(ra["logg"]) & ok[..., None]
+    assert np.abs(logg.cpu().numpy()[fin] - ra["logg"][fin]).max() < ROUTER_ABS
+    assert np.abs(glse.cpu().numpy() - ra["lse"]).max() < ROUTER_ABS
+    # attention on the oracle router's selection
+    idx_n, logg_n = ra["idx"], ra["logg"]
+    idx_o = torch.from_numpy(idx_n.astype(np.int32)).cuda()
+    logg_o = torch.from_numpy(logg_n.astype(np.float32)).cuda()
+    sc = 1.0 / math.sqrt(w.D)
+    o, lse, o32 = sas.sparse_attn_fwd(d["q"], d["k"], d["v"], idx_o, logg_o, sc, want_f32=True)
+    dq, dk, dv, dlogg = sas.sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, idx_o,
+                                            logg_o, sc, o_f32=o32)
+    torch.cuda.synchronize()
+    tok = sample_tokens(w.T, 96, seed=11)
+    tt = torch.as_tensor(tok, device="cuda")
+    ro, rl = O.attn_fwd_rows(x64["q"], x64["k"], x64["v"], idx_n, logg_n, sc, tokens=tok)
+    check("o (sampled rows)", o[:, tt], ro)
+    check("o_f32 (sampled rows)", o32[:, tt], ro)
+    assert np.abs(lse[:, tt].cpu().numpy() - rl).max() < 1e-4
+    assert float(dlogg.sum(-1).abs().max()) < 1e-3
+    assert bool((dlogg[idx_o < 0] == 0).all())
+    rdq, rdl = O.attn_bwd_rows(x64["q"], x64["k"], x64["v"], x64["dout"], idx_n, logg_n, sc, tok)
+    check("dq (sampled rows)", dq[:, tt], rdq)
+    check("dlogg (sampled rows)", dlogg[:, tt], rdl)
+    # (the oracle gathers every row that selected the block: late blocks keep
+    # it to seconds)
+    for kv2, j in [(0, 900), (1, w.NB - 1)]:
+        rdk, rdv = O.attn_bwd_block(x64["q"], x64["k"], x64["v"], x64["dout"], idx_n, logg_n,
+                                    sc, 0, kv2, j)
+        lo, hi = 64 * j, min(64 * j + 64, w.T)
+        check(f"dk[{kv2},{j}]", dk[0, lo:hi, kv2], rdk)
+        check(f"dv[{kv2},{j}]", dv[0, lo:hi, kv2], rdv)
 
 
 # ------------------------------------------------------------------- decode
