@@ -31,13 +31,13 @@ LIB_PATH = os.path.join(_PKG, "libsas.so")
 
 SAS_OK, SAS_ERR_INVALID, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
 FLAG_GATE_PER_QUERY_HEAD = 1
-OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD, OP_GATE_BWD = range(5)
+OP_GATE_SCORE, OP_TOPK, OP_FWD, OP_BWD, OP_GATE_BWD, OP_WALK_ORDER = range(6)
 
 EXPORTED_SYMBOLS = (
     "sas_version", "sas_last_error", "sas_workspace_size", "sas_decode_workspace_size",
     "sas_gate_score", "sas_topk_blocks", "sas_sparse_attn_fwd", "sas_sparse_attn_bwd",
     "sas_decode", "sas_set_timing_events", "sas_take_device_fault", "sas_gate_score_bwd",
-    "sas_decode_paged", "sas_decode_gate_key", "sas_decode_noalloc",
+    "sas_decode_paged", "sas_decode_gate_key", "sas_decode_noalloc", "sas_walk_order",
 )
 
 
@@ -96,11 +96,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      + [F32] + [P] * 3 + [P, S, P])
     lib.sas_decode_gate_key.argtypes = ([ctypes.POINTER(DecodeDims)] + [P, P, I32, P, P]
                                         + [ctypes.c_double, F32] + [P, P, P])
+    lib.sas_walk_order.argtypes = [ctypes.POINTER(Dims), P, P, S, P]
     lib.sas_set_timing_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     lib.sas_take_device_fault.argtypes = [ctypes.POINTER(ctypes.c_uint)]
     for fn in ("sas_gate_score", "sas_gate_score_bwd", "sas_topk_blocks", "sas_sparse_attn_fwd",
                "sas_sparse_attn_bwd", "sas_decode", "sas_decode_paged", "sas_decode_gate_key",
-               "sas_decode_noalloc",
+               "sas_decode_noalloc", "sas_walk_order",
                "sas_set_timing_events",
                "sas_take_device_fault"):
         getattr(lib, fn).restype = I32
@@ -354,6 +355,25 @@ def sparse_attn_fwd(q, k, v, idx, logg, scale: float | None = None, o=None, lse=
                                    _ptr(o_f32), _ptr(ws), ws.numel() if ws is not None else 0,
                                    _stream(dev)))
     return (o, lse, o_f32) if o_f32 is not None else (o, lse)
+
+
+def walk_order(idx, Hq: int, Hkv: int):
+    """Staging order of the query-group walks for selection idx [B,T,Hs,S]
+    (diagnostic): uint16 [groups, stride], row g = (b * Hs + sg) * ngrp + grp
+    holding the union size nU and then the nU blocks in the order the forward
+    and dQ kernels take them."""
+    lib = load_library()
+    dev = _device_of(idx)
+    B, T, Hs, S = idx.shape
+    flags = _sel_flags(Hs, Hq, Hkv, "idx")
+    _req(idx, "idx", torch.int32, (B, T, Hs, S), dev)
+    d = make_dims(B, T, Hq, Hkv, 128, 128, S - 1, flags=flags)
+    nbytes = workspace_size(OP_WALK_ORDER, d)
+    NB = -(-T // 64)
+    stride = (NB + 8) & ~7
+    out = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    _check(lib.sas_walk_order(ctypes.byref(d), _ptr(idx), _ptr(out), nbytes, _stream(dev)))
+    return out.view(-1, stride)
 
 
 def sparse_attn_bwd(q, k, v, o, dout, lse, idx, logg, scale: float | None = None,

@@ -553,17 +553,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 // One workgroup = (b, kappa, a group of TPW <= 64 consecutive tokens): NCW
 // compute waves, each owning one 16-row tile (TPT tokens x G heads), plus two
 // stager waves.  The stagers copy the K tile of every block in the union of
-// the group's selections, in ascending order, into a ring of R LDS slots with
-// asynchronous global -> LDS copies (up to L blocks in flight each).  A compute
-// wave visits only the blocks its tile needs: it waits for the block's slot to
+// the group's selections, in the order walk_order.hip makes for the group,
+// into a ring of R LDS slots with asynchronous global -> LDS copies (up to L
+// blocks in flight each).  A compute wave visits only the blocks its tile
+// needs: it waits for the block's slot to
 // be filled, runs dQ^T += K^T dS^T on bf16 MFMA 16x16x32 (K^T read from the K
 // rows with transposing LDS reads, dS rows loaded from memory, zero rows for
 // tokens that did not select the block), and the dS rows of its next needed
 // block start loading right after.
 //
 // Protocol (all counters in LDS, only growing; no workgroup barrier):
-//  * prog[c]: compute wave c is done with every block below prog[c] (it sets
-//    it to its next needed block after reading one, nU at the end);
+//  * prog[c]: compute wave c is done with every staged position below
+//    prog[c] (it sets it to the position of its next needed block after
+//    reading one, nU at the end);
 //  * a stager copies its half of block n into slot n % R once
 //    min_c prog[c] >= n - R + 1, and bumps fill[n % R] once the copies have
 //    landed (s_waitcnt vmcnt); before it waits for a slot it publishes all
@@ -588,8 +590,7 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
   __shared__ __attribute__((aligned(16))) uint8_t ring[R * STAGE];
   __shared__ uint32_t bits[64 * kMaxNBW];     // per-token selection bitmaps [64][NBW]
   __shared__ uint8_t pcnt[64 * kMaxNBW];      // popcount prefix per word
-  __shared__ uint32_t ubits[kMaxNBW];
-  __shared__ uint16_t ulist[kMaxNB];
+  __shared__ uint16_t ulist[kMaxNB];          // union blocks in staging order
   __shared__ uint8_t slot_of[64 * kMaxS];     // slot numbers by selection rank [64][S]
   __shared__ uint32_t actw[14 * kMaxNBW];     // per compute wave: which union blocks it needs
   __shared__ int prog[16];
@@ -617,7 +618,6 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
 
   // ---- selection bitmaps of the group's tokens, their union, slots by rank
   for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
-  if (tid < NBW) ubits[tid] = 0u;
   if (tid < 16) prog[tid] = 0;
   if (tid < R) fill_cnt[tid] = 0u;
   __syncthreads();
@@ -628,7 +628,6 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
     const int j = a.idx[off];
     if (j >= 0 && j <= (t0 + tl) / 64) {
       atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
-      atomicOr(&ubits[j >> 5], 1u << (j & 31));
     } else {
       a.dlogg[off] = 0.f;     // padding / ignored slot (the others come from dK/dV)
     }
@@ -651,22 +650,14 @@ __global__ __launch_bounds__(1024) void dq_kernel(BwdParams a, int ncw, int tpw)
       if (rank < S) slot_of[tl * S + rank] = static_cast<uint8_t>(s);
     }
   }
-  if (wv == 0) {
-    int base = 0;
-    for (int w0 = 0; w0 < NBW; w0 += 64) {
-      const uint32_t word = (w0 + lane < NBW) ? ubits[w0 + lane] : 0u;
-      const int cnt = __popc(word);
-      const int incl = wave_incl_scan(cnt);
-      int pos = base + incl - cnt;
-      uint32_t wb = word;
-      while (wb) {
-        const int bp = __ffs(wb) - 1;
-        wb &= wb - 1;
-        ulist[pos++] = static_cast<uint16_t>((w0 + lane) * 32 + bp);
-      }
-      base += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) s_nU = base;
+  // the union of the group's selections in the staging order that spreads
+  // each compute wave's blocks over the ring windows (walk_order.hip)
+  {
+    const uint16_t* ord =
+        a.order + ((static_cast<size_t>(b) * a.Hs + sg) * ngrp + grp) * static_cast<size_t>(a.ost);
+    const int n = min(static_cast<int>(ord[0]), a.NB);    // in range whatever it holds
+    for (int i = tid; i < n; i += NT) ulist[i] = static_cast<uint16_t>(min(static_cast<int>(ord[1 + i]), a.NB - 1));
+    if (tid == 0) s_nU = n;
   }
   wait_vmem_all();
   __syncthreads();
@@ -928,6 +919,9 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hs), dim3(256), 0, st, p);
   hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hs), dim3(1024), 0, st, p);
   hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
+  const WalkOrderParams wo{p.idx, p.order, p.B, p.T, p.Hs, p.S, p.NB, p.TPT, p.ost};
+  const hipError_t eo = launch_walk_order(wo, st);
+  if (eo != hipSuccess) return eo;
   timing_mark(1, st);
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
                      dim3(256), 0, st, p);

@@ -12,9 +12,9 @@
 //   has its own gate), plus two stager waves.  The stagers copy the K tile and
 //   the V^T tile (from a transposed copy of V made once per call, keys in
 //   operand order) of every block in the union of the group's selections, in
-//   ascending order, into a ring of R LDS slots with asynchronous global ->
-//   LDS copies (16-byte chunks XOR-swizzled per row, so that the MFMA operand
-//   reads are conflict-free).  A compute wave visits only the blocks its tile
+//   the order walk_order.hip makes for the group, into a ring of R LDS slots
+//   with asynchronous global -> LDS copies (16-byte chunks XOR-swizzled per
+//   row, so that the MFMA operand reads are conflict-free).  A compute wave visits only the blocks its tile
 //   needs: S^T = K Q^T and O^T += V^T P^T on MFMA 16x16x32, with rows outside
 //   the selection masked out.  Online-softmax state stays in registers (one
 //   query row per lane column); the running reference maximum is moved only
@@ -52,8 +52,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   __shared__ __attribute__((aligned(16))) uint8_t ring[R * STAGE];
   __shared__ uint32_t bits[64 * kMaxNBW];     // per-token selection bitmaps [64][NBW]
   __shared__ uint8_t pcnt[64 * kMaxNBW];      // popcount prefix per word
-  __shared__ uint32_t ubits[kMaxNBW];
-  __shared__ uint16_t ulist[kMaxNB];
+  __shared__ uint16_t ulist[kMaxNB];          // union blocks in staging order
   __shared__ float lgs[64 * kMaxS];           // log2 gates by selection rank [64][S]
   __shared__ uint32_t actw[14 * kMaxNBW];     // per compute wave: which union blocks it needs
   __shared__ int prog[16];
@@ -82,7 +81,6 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 
   // ---- selection bitmaps of the group's tokens, their union, log-gates by rank
   for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
-  if (tid < NBW) ubits[tid] = 0u;
   if (tid < 16) prog[tid] = 0;
   if (tid < R) fill_cnt[tid] = 0u;
   __syncthreads();
@@ -90,10 +88,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   for (int e = tid; e < ntok * S; e += NT) {
     const int tl = e / S, s = e - tl * S;
     const int j = a.idx[(rowbase + static_cast<size_t>(tl) * a.Hs) * S + s];
-    if (j >= 0 && j <= (t0 + tl) / 64) {
-      atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
-      atomicOr(&ubits[j >> 5], 1u << (j & 31));
-    }
+    if (j >= 0 && j <= (t0 + tl) / 64) atomicOr(&bits[tl * NBW + (j >> 5)], 1u << (j & 31));
   }
   __syncthreads();
   if (tid < 64) {
@@ -114,22 +109,14 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
       if (rank < S) lgs[tl * S + rank] = a.logg[off] * kLog2e;
     }
   }
-  if (wv == 0) {
-    int base = 0;
-    for (int w0 = 0; w0 < NBW; w0 += 64) {
-      const uint32_t word = (w0 + lane < NBW) ? ubits[w0 + lane] : 0u;
-      const int cnt = __popc(word);
-      const int incl = wave_incl_scan(cnt);
-      int pos = base + incl - cnt;
-      uint32_t wb = word;
-      while (wb) {
-        const int bp = __ffs(wb) - 1;
-        wb &= wb - 1;
-        ulist[pos++] = static_cast<uint16_t>((w0 + lane) * 32 + bp);
-      }
-      base += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) s_nU = base;
+  // the union of the group's selections in the staging order that spreads
+  // each compute wave's blocks over the ring windows (walk_order.hip)
+  {
+    const uint16_t* ord =
+        a.order + ((static_cast<size_t>(b) * a.Hs + sg) * ngrp + grp) * static_cast<size_t>(a.ost);
+    const int n = min(static_cast<int>(ord[0]), a.NB);    // in range whatever it holds
+    for (int i = tid; i < n; i += NT) ulist[i] = static_cast<uint16_t>(min(static_cast<int>(ord[1 + i]), a.NB - 1));
+    if (tid == 0) s_nU = n;
   }
   wait_vmem_all();
   __syncthreads();
@@ -436,8 +423,8 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 // static LDS: a ring of 4 (K, V^T) tile pairs plus the selection data.
 template <int D, bool HILO>
 hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
-  const int tpw = min(64, 14 * p.TPT);
-  const int ncw = (tpw + p.TPT - 1) / p.TPT;
+  const int tpw = walk_tpw(p.TPT);
+  const int ncw = walk_ncw(p.TPT);
   const unsigned ngrp = (p.T + tpw - 1) / tpw;
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hs * ngrp);
   hipLaunchKernelGGL((sparse_fwd_kernel<D, HILO, 4>), grid, dim3((ncw + kFwdStagers) * 64), 0, st,
@@ -454,8 +441,11 @@ hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
 
 hipError_t launch_sparse_fwd(const FwdParams& p, hipStream_t st) {
   timing_mark(0, st);
+  WalkOrderParams wo{p.idx, p.order, p.B, p.T, p.Hs, p.S, p.NB, p.TPT, p.ost};
+  hipError_t e = launch_walk_order(wo, st);
+  if (e != hipSuccess) return e;
   // V^T: bf16 for the hi/lo product (fp32 output requested), else scaled fp16
-  hipError_t e = p.o32 ? launch_transpose_tokens(p.v, p.vt, p.B, p.T, p.Hkv, p.D, st)
+  e = p.o32 ? launch_transpose_tokens(p.v, p.vt, p.B, p.T, p.Hkv, p.D, st)
                        : launch_transpose_tokens_f16(p.v, p.vt, p.vamax, p.vscale, p.B, p.T,
                                                      p.Hkv, p.D, st);
   if (e != hipSuccess) return e;

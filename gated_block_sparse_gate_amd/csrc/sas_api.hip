@@ -130,19 +130,28 @@ GateBwdWs gate_bwd_ws(const sas_dims* d) {
   return w;
 }
 
-struct FwdWs { size_t vt, amax, vscale, total; };
+// staging orders of the query-group walks (forward, dQ): one per token group
+size_t walk_order_bytes(const sas_dims* d) {
+  const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+  const int NB = (d->T + 63) / 64;
+  return sizeof(uint16_t) * sas::walk_order_stride(NB) *
+         sas::walk_order_groups(d->B, d->T, sh.Hs, 16 / sh.Gs);
+}
+
+struct FwdWs { size_t vt, amax, vscale, order, total; };
 FwdWs fwd_ws_layout(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
   FwdWs w;
   w.vt = 0;
   w.amax = align_up(sizeof(uint16_t) * d->B * d->Hkv * d->D * NB * 64);
   w.vscale = align_up(w.amax + sizeof(float) * d->B * d->Hkv * NB);
-  w.total = align_up(w.vscale + sizeof(float) * d->B * d->Hkv);
+  w.order = align_up(w.vscale + sizeof(float) * d->B * d->Hkv);
+  w.total = align_up(w.order + walk_order_bytes(d));
   return w;
 }
 size_t fwd_ws(const sas_dims* d) { return fwd_ws_layout(d).total; }
 
-struct BwdWs { size_t delta, cnt2d, rowptr, entries, ds, total; };
+struct BwdWs { size_t delta, cnt2d, rowptr, entries, order, ds, total; };
 BwdWs bwd_ws(const sas_dims* d) {
   const size_t NB = (d->T + 63) / 64;
   const size_t S = d->topk + 1;
@@ -152,7 +161,8 @@ BwdWs bwd_ws(const sas_dims* d) {
   w.cnt2d = align_up(w.delta + sizeof(float) * static_cast<size_t>(d->B) * d->T * d->Hq);
   w.rowptr = align_up(w.cnt2d + sizeof(int32_t) * d->B * Hs * NB * NB);
   w.entries = align_up(w.rowptr + sizeof(int32_t) * d->B * Hs * (NB + 1));
-  w.ds = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * Hs * d->T * S);
+  w.order = align_up(w.entries + sizeof(int32_t) * static_cast<size_t>(d->B) * Hs * d->T * S);
+  w.ds = align_up(w.order + walk_order_bytes(d));
   // dS of every selected (token, head, slot): 64 keys x (hi, lo) bf16
   w.total = align_up(w.ds + 256 * static_cast<size_t>(d->B) * d->T * d->Hq * S);
   return w;
@@ -291,6 +301,7 @@ size_t sas_workspace_size(int op, const sas_dims* d) {
     case SAS_OP_GATE_SCORE: return gate_ws(d).total;
     case SAS_OP_TOPK: return 0;
     case SAS_OP_FWD: return fwd_ws(d);
+    case SAS_OP_WALK_ORDER: return walk_order_bytes(d);
     case SAS_OP_BWD: return bwd_ws(d).total;
     case SAS_OP_GATE_BWD: return gate_bwd_ws(d).total;
     default: fail(SAS_ERR_INVALID, "unknown op %d", op); return static_cast<size_t>(-1);
@@ -367,6 +378,8 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
   p.vt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fw.vt);
   p.vamax = reinterpret_cast<float*>(static_cast<char*>(ws) + fw.amax);
   p.vscale = reinterpret_cast<float*>(static_cast<char*>(ws) + fw.vscale);
+  p.order = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fw.order);
+  p.ost = sas::walk_order_stride((d->T + 63) / 64);
   p.q = q; p.k = k; p.v = v; p.idx = idx; p.logg = logg; p.o = o; p.lse = lse; p.o32 = o_f32;
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
@@ -380,6 +393,23 @@ sas_status sas_sparse_attn_fwd(const sas_dims* d, const uint16_t* q, const uint1
   g_err.clear();
   return hip_status(sas::launch_sparse_fwd(p, static_cast<hipStream_t>(stream)),
                     "sas_sparse_attn_fwd launch");
+}
+
+sas_status sas_walk_order(const sas_dims* d, const int32_t* idx, uint16_t* order,
+                          size_t order_bytes, void* stream) {
+  sas_status st = check_dims(d);
+  if (st) return st;
+  REQ_PTR(idx); REQ_PTR(order);
+  const size_t need = walk_order_bytes(d);
+  if (order_bytes < need)
+    return fail(SAS_ERR_INVALID, "order buffer too small: %zu < %zu bytes", order_bytes, need);
+  const SelHeads sh = sel_heads(d->Hq, d->Hkv, d->flags);
+  const int NB = (d->T + 63) / 64;
+  const sas::WalkOrderParams p{idx, order, d->B, d->T, sh.Hs, d->topk + 1, NB, 16 / sh.Gs,
+                               sas::walk_order_stride(NB)};
+  g_err.clear();
+  return hip_status(sas::launch_walk_order(p, static_cast<hipStream_t>(stream)),
+                    "sas_walk_order launch");
 }
 
 sas_status sas_gate_score_bwd(const sas_dims* d, const uint16_t* q, const uint16_t* k,
@@ -458,6 +488,8 @@ sas_status sas_sparse_attn_bwd(const sas_dims* d, const uint16_t* q, const uint1
   p.rowptr = reinterpret_cast<int32_t*>(base + w.rowptr);
   p.entries = reinterpret_cast<int32_t*>(base + w.entries);
   p.dsbuf = reinterpret_cast<uint16_t*>(base + w.ds);
+  p.order = reinterpret_cast<uint16_t*>(base + w.order);
+  p.ost = sas::walk_order_stride((d->T + 63) / 64);
   p.B = d->B; p.T = d->T; p.Hq = d->Hq; p.Hkv = d->Hkv; p.D = d->D; p.G = d->Hq / d->Hkv;
   p.S = d->topk + 1; p.NB = (d->T + 63) / 64;
   {

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bwd_index.h"
 #include "sas_device.h"
 
 namespace sas {
@@ -124,6 +125,8 @@ struct FwdParams {
   uint16_t* vt; // workspace: V^T [B,Hkv,D,64*NB] in fp16, scaled by 1/vscale
   float* vamax; // workspace: [B,Hkv,NB] max |v| per 64-token block
   float* vscale;// workspace: [B,Hkv] power of two restoring the V^T scaling
+  uint16_t* order;        // workspace: staging order of each token group (walk_order)
+  int ost;      // its per-group stride (uint16 entries)
   int B, T, Hq, Hkv, D, G, S, NB;
   int Hs, Gs, kdiv;   // selection heads (idx, logg [B,T,Hs,S]); rows per token = Gs
   int TPT;      // tokens per 16-row tile = floor(16 / Gs)
@@ -155,6 +158,8 @@ struct BwdParams {
   // (position 32 k2 + 8 g + e holds key 32 k2 + 4 g + e for e < 4, else
   // key 32 k2 + 16 + 4 g + e - 4)
   uint16_t* dsbuf;
+  uint16_t* order;        // workspace: staging order of each dQ token group (walk_order)
+  int ost;              // its per-group stride (uint16 entries)
   int B, T, Hq, Hkv, D, G, S, NB;
   int Hs, Gs, kdiv;     // selection heads (idx, logg, dlogg [B,T,Hs,S])
   int TPT, ntiles;      // tokens per 16-row tile = floor(16 / Gs)
@@ -234,6 +239,23 @@ void decode_split(int S, int units, int* nsplit, int* spw);
 // per-head running max (16 slots) and sum (16 slots); a multiple of 32 floats,
 // so every partial starts on a 128-byte line and is written in whole lines
 constexpr int decode_part_floats(int G, int D) { return G * D + 32; }
+
+// Staging order of the union blocks of every token group of the query-group
+// walks: group g = (b * Hs + sg) * ngrp + grp (tpw = walk_tpw(TPT) tokens per
+// group) gets [nU, nU block indices] at order + g * ost.
+struct WalkOrderParams {
+  const int32_t* idx;   // [B,T,Hs,S]
+  uint16_t* order;      // [B * Hs * ngrp][ost]
+  int B, T, Hs, S, NB, TPT, ost;
+};
+hipError_t launch_walk_order(const WalkOrderParams& p, hipStream_t st);
+size_t walk_order_smem_bytes(int NB);
+// uint16 entries per group of the order buffer, and the groups of a call
+inline int walk_order_stride(int NB) { return (NB + 1 + 7) & ~7; }
+inline size_t walk_order_groups(int B, int T, int Hs, int TPT) {
+  const int tpw = walk_tpw(TPT);
+  return static_cast<size_t>(B) * Hs * ((T + tpw - 1) / tpw);
+}
 
 // dynamic LDS bytes of the Top-K kernel
 size_t topk_smem_bytes(int NB, int dg);

@@ -78,7 +78,8 @@ enum {
   SAS_OP_TOPK = 1,
   SAS_OP_FWD = 2,
   SAS_OP_BWD = 3,
-  SAS_OP_GATE_BWD = 4
+  SAS_OP_GATE_BWD = 4,
+  SAS_OP_WALK_ORDER = 5   /* bytes of the order buffer of sas_walk_order */
 };
 
 /*
@@ -124,8 +125,10 @@ const char* sas_last_error(void);
  * NULL / 0 to switch the hook off.  While set (per thread), each following
  * sas_sparse_attn_fwd / sas_sparse_attn_bwd call records events[i] on its
  * stream at stage boundary i (boundaries beyond n_events are skipped):
- *   fwd: 0 start, 1 after the V transpose, 2 after the attention kernel;
- *   bwd: 0 start, 1 after Delta + the CSR build, 2 after dK/dV, 3 after dQ.
+ *   fwd: 0 start, 1 after the staging order and the V transpose, 2 after
+ *        the attention kernel;
+ *   bwd: 0 start, 1 after Delta, the CSR build and the dQ staging order,
+ *        2 after dK/dV, 3 after dQ.
  * The caller owns the events and keeps them alive while the hook is set.
  */
 sas_status sas_set_timing_events(void* const* events, int n_events);
@@ -139,6 +142,33 @@ sas_status sas_set_timing_events(void* const* events, int n_events);
  * cleared.  Synchronises with the device.
  */
 sas_status sas_take_device_fault(unsigned* fault);
+
+/*
+ * Staging order of the query-group walks (diagnostic; the forward and dQ
+ * calls make it themselves, in their workspace).  Their kernels take a group
+ * of tpw consecutive tokens of one selection head, tpw = min(64, 14 * TPT)
+ * with TPT = floor(16 / Gs) tokens per 16-row tile (Gs query heads per
+ * selection head), and copy every KV block some token of the group selected
+ * (the union) through a small LDS ring shared by the group's tiles.  This
+ * writes the order in which they take the union: per group
+ * g = (b * Hs + sg) * ngrp + grp (ngrp = ceil(T / tpw)), at
+ * order + g * stride with stride = (NB + 8) & ~7 entries, the count nU and
+ * then nU distinct block indices.  The candidates are the first 64 union
+ * blocks (ascending) not yet placed, ranked by how many of the last three
+ * placed blocks their busiest tile needed (fewer first), then by how many
+ * tiles need them (more first), then by block; each step places the best
+ * candidate and then, on the same ranking, the best one whose tiles are
+ * disjoint from the first's.  Any order gives the same attention up to
+ * floating-point summation order; this one balances the tiles' work inside
+ * each window of the ring.
+ *   idx: [B,T,Hs,S] int32 as sas_topk_blocks writes it (entries outside
+ *        0..c(t) are ignored, as in the forward);
+ *   order: device, sas_workspace_size(SAS_OP_WALK_ORDER, d) bytes.
+ * Errors: SAS_ERR_INVALID (null / unaligned pointer, order_bytes too small),
+ * SAS_ERR_UNSUPPORTED (dims); nothing is launched on error.
+ */
+sas_status sas_walk_order(const sas_dims* d, const int32_t* idx, uint16_t* order,
+                          size_t order_bytes, void* stream);
 
 /* Workspace bytes needed by op (SAS_OP_*) for dims d; 0 if none; (size_t)-1
  * if d is invalid. */

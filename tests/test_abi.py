@@ -98,8 +98,12 @@ def test_workspace_checks():
     d = _dims(T=4096)
     need = sas.workspace_size(sas.OP_BWD, d)
     assert need > 0
-    # fp16 transposed v, per-block |v| maxima (64 blocks), per-head scales; 256-byte aligned
-    assert sas.workspace_size(sas.OP_FWD, d) == 1 * 2 * 128 * 4096 * 2 + 512 + 256
+    # fp16 transposed v, per-block |v| maxima (64 blocks), per-head scales, and the
+    # staging orders (2 heads x 74 groups of 56 tokens x 72 uint16); 256-byte aligned
+    order = 2 * 74 * 72 * 2
+    assert sas.workspace_size(sas.OP_WALK_ORDER, d) == order
+    assert sas.workspace_size(sas.OP_FWD, d) == (1 * 2 * 128 * 4096 * 2 + 512 + 256
+                                                 + (order + 255) // 256 * 256)
     assert sas.workspace_size(sas.OP_TOPK, d) == 0
     p = ctypes.c_void_p(4096)
     args = [p] * 9 + [ctypes.c_float(0.1)] + [p] * 4
