@@ -17,11 +17,12 @@
 //  2. placement: the candidates are the first 64 union blocks not yet placed
 //     (one per lane); a candidate ranks by the load of its busiest tile in
 //     the window of the last kWin - 1 placed blocks, then by the number of
-//     tiles that need it (more first), then by position.  Each step places
-//     the best candidate and then, ranked on the same window, the best one
-//     whose tiles are disjoint from the first's (its rank is unchanged by
-//     the first), so the serial chain has half as many steps; the next
-//     unplaced blocks take their lanes.
+//     tiles that need it (more first), then by position.  Each step ranks
+//     the candidates once and places up to kPick of them: the best, then the
+//     best whose tiles are disjoint from all tiles picked so far, and so on
+//     (a disjoint pick's load is not changed by the picks before it), so the
+//     serial chain has 1 / kPick as many steps; the next unplaced blocks
+//     take the picked candidates' lanes.
 // Output per group (stride ost uint16): [nU, block of position 0, ...].
 #include "sas_kernels.h"
 
@@ -30,16 +31,27 @@ namespace sas {
 namespace {
 
 constexpr int kWin = 4;     // ring window the placement balances (the forward's ring depth)
+constexpr int kPick = 2;    // placements per step
 
-// minimum over the wave: within each 16-lane row by DPP, then the four rows
+// v = min(v, v of another lane) by a DPP move; lanes outside row_mask (or
+// reading outside the wave) take the minimum's identity
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_min(uint32_t v) {
+  const uint32_t t = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(-1, static_cast<int>(v), CTRL, ROWS, 0xF, false));
+  return min(v, t);
+}
+// minimum over the wave: within each 16-lane row, then rows 0 -> 1 and
+// 2 -> 3 by row broadcast 15, then rows 0..1 -> 2..3 by row broadcast 31;
+// lane 63 ends up with the whole wave's minimum
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, __float_as_uint(dpp_mov<0xB1>(__uint_as_float(v))));    // quad_perm [1,0,3,2]
-  v = min(v, __float_as_uint(dpp_mov<0x4E>(__uint_as_float(v))));    // quad_perm [2,3,0,1]
-  v = min(v, __float_as_uint(dpp_mov<0x141>(__uint_as_float(v))));   // row_half_mirror
-  v = min(v, __float_as_uint(dpp_mov<0x140>(__uint_as_float(v))));   // row_mirror
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return min(min(r0, r1), min(r2, r3));
+  v = dpp_min<0xB1>(v);           // quad_perm [1,0,3,2]
+  v = dpp_min<0x4E>(v);           // quad_perm [2,3,0,1]
+  v = dpp_min<0x141>(v);          // row_half_mirror
+  v = dpp_min<0x140>(v);          // row_mirror
+  v = dpp_min<0x142, 0xA>(v);     // row_bcast:15
+  v = dpp_min<0x143, 0xC>(v);     // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __global__ __launch_bounds__(64) void walk_order_kernel(WalkOrderParams a) {
@@ -70,47 +82,40 @@ __global__ __launch_bounds__(64) void walk_order_kernel(WalkOrderParams a) {
   }
   __syncthreads();
 
-  // union positions and tile masks, one bitmap word per lane
+  // union positions and tile masks, one block per lane: bit w of block j's
+  // mask is bit j of tile w's bitmap
   int nU = 0;
-  for (int w0 = 0; w0 < NBW; w0 += 64) {
-    const int wd = w0 + lane;
-    uint32_t tw[14];
-    uint32_t u = 0u;
-#pragma unroll
-    for (int w = 0; w < 14; ++w) {
-      tw[w] = (w < ncw && wd < NBW) ? tb[w * NBW + wd] : 0u;
-      u |= tw[w];
+  for (int j0 = 0; j0 < a.NB; j0 += 64) {
+    const int j = j0 + lane;
+    uint32_t m = 0u;
+    if (j < a.NB) {
+      const uint32_t* col = tb + (j >> 5);
+      for (int w = 0; w < ncw; ++w) m |= ((col[w * NBW] >> (j & 31)) & 1u) << w;
     }
-    const int cnt = __popc(u);
-    const int incl = wave_incl_scan(cnt);
-    int pos = nU + incl - cnt;
-    while (u) {
-      const int bit = __ffs(u) - 1;
-      u &= u - 1;
-      uint32_t m = 0u;
-#pragma unroll
-      for (int w = 0; w < 14; ++w) m |= ((tw[w] >> bit) & 1u) << w;
+    const uint64_t in = ballot64(m != 0u);
+    if (m != 0u) {
+      const int pos = nU + static_cast<int>(__popcll(in & ((1ull << lane) - 1ull)));
       mask[pos] = static_cast<uint16_t>(m);
-      asc[pos] = static_cast<uint16_t>(wd * 32 + bit);
-      ++pos;
+      asc[pos] = static_cast<uint16_t>(j);
     }
-    nU += __shfl(incl, 63, 64);
+    nU += static_cast<int>(__popcll(in));
   }
   nU = __builtin_amdgcn_readfirstlane(nU);
   __syncthreads();
 
-  // placement.  Lane l holds a candidate: its position cp, tile mask cm and
-  // base key kb = (64 - tiles needing it) << 16 | cp; a step's key adds the
-  // window load ml << 22, so the smallest key is the least loaded, then the
-  // most needed, then the earliest candidate.  No candidate: kb above every
-  // key.  sb holds the masks of the 64-position chunk of the stream that nxt
-  // (the next unplaced position) is in; ordv collects the current 64-entry
-  // chunk of placements.  Each step places the best candidate and then, on
-  // the same window, the best one whose tiles are disjoint from its tiles.
+  // placement.  Lane l holds a candidate: its tile mask cm and base key
+  // kb = (64 - tiles needing it) << 16 | position << 6 | l; a step's key adds
+  // the window load ml << 22, so the smallest key is the least loaded, then
+  // the most needed, then the earliest candidate, and its low bits name the
+  // lane.  No candidate: kb above every key.  sb holds the masks of the
+  // 64-position chunk of the stream that nxt (the next unplaced position) is
+  // in; ordv collects the current 64-entry chunk of placements.  Each step
+  // ranks the candidates on the current window and places up to kPick of
+  // them: the best, then the best whose tiles are disjoint from the tiles
+  // already picked, and so on.
   constexpr uint32_t kNone = 0xFF000000u;
-  uint32_t cp = lane < nU ? lane : 0xFFFFu;
   uint32_t cm = lane < nU ? mask[lane] : 0u;
-  uint32_t kb = lane < nU ? (((64u - __popc(cm)) << 16) | lane) : kNone;
+  uint32_t kb = lane < nU ? (((64u - __popc(cm)) << 16) | (lane << 6) | lane) : kNone;
   int nxt = min(64, nU);
   uint32_t sb = (nxt + lane < nU) ? mask[nxt + lane] : 0u;
   uint32_t ordv = 0u;
@@ -118,22 +123,21 @@ __global__ __launch_bounds__(64) void walk_order_kernel(WalkOrderParams a) {
   uint32_t h0 = 0u, h1 = 0u, h2 = 0u;           // masks of the last three placed blocks
   static_assert(kWin == 4, "three-deep history");
   int n = 0;
-  // record position p (mask m, held by lane wl) as placement n; its lane
-  // takes the next unplaced position; the window moves on by one block
-  auto commit = [&](uint32_t p, uint32_t m, int wl) __attribute__((always_inline)) {
-    ordv = (lane == (n & 63)) ? p : ordv;
+  // record the candidate of key k (mask m) as placement n; its lane takes the
+  // next unplaced position; the window moves on by one block
+  auto commit = [&](uint32_t k, uint32_t m) __attribute__((always_inline)) {
+    const int wl = static_cast<int>(k & 63u);
+    ordv = (lane == (n & 63)) ? ((k >> 6) & 1023u) : ordv;
     if ((n & 63) == 63) ord[(n & ~63) + lane] = static_cast<uint16_t>(ordv);
     ++n;
-    uint32_t ncp = 0xFFFFu, ncm = 0u, nkb = kNone;
+    uint32_t ncm = 0u, nkb = kNone;
     if (nxt < nU) {
       ncm = __builtin_amdgcn_readlane(sb, nxt & 63);
-      ncp = static_cast<uint32_t>(nxt);
-      nkb = ((64u - __popc(ncm)) << 16) | ncp;
+      nkb = ((64u - __popc(ncm)) << 16) | (static_cast<uint32_t>(nxt) << 6) | static_cast<uint32_t>(wl);
       ++nxt;
       if ((nxt & 63) == 0) sb = (nxt + lane < nU) ? mask[nxt + lane] : 0u;
     }
     const bool win = lane == wl;
-    cp = win ? ncp : cp;
     cm = win ? ncm : cm;
     kb = win ? nkb : kb;
     // drop the block placed kWin - 1 steps ago, add this one
@@ -151,17 +155,19 @@ __global__ __launch_bounds__(64) void walk_order_kernel(WalkOrderParams a) {
     // window load of the candidate's busiest tile, in bits 22..23 of the key
     const uint32_t b1 = min(cm & c0, 1u), b2 = min(cm & c1, 1u), b3 = min(cm & c0 & c1, 1u);
     const uint32_t key = kb + (max(max(b1, b2 << 1), b3 * 3u) << 22);
-    const uint32_t k1 = wave_min_u32(key);
-    const uint32_t p1 = k1 & 0xFFFFu;
-    const int w1 = static_cast<int>(__builtin_ctzll(ballot64(cp == p1)));   // one lane
-    const uint32_t m1 = __builtin_amdgcn_readlane(cm, w1);
-    const uint32_t k2 = wave_min_u32((cp != p1 && (cm & m1) == 0u) ? key : 0xFFFFFFFFu);
-    commit(p1, m1, w1);
-    if (k2 < kNone) {
-      const uint32_t p2 = k2 & 0xFFFFu;
-      const int w2 = static_cast<int>(__builtin_ctzll(ballot64(cp == p2)));
-      commit(p2, __builtin_amdgcn_readlane(cm, w2), w2);
+    // up to kPick picks on this window, each the best candidate whose tiles
+    // are disjoint from the tiles of the picks before it
+    uint32_t pk[kPick], pm[kPick];
+    uint32_t used = 0u;
+#pragma unroll
+    for (int i = 0; i < kPick; ++i) {
+      pk[i] = wave_min_u32((cm & used) == 0u ? key : 0xFFFFFFFFu);
+      pm[i] = pk[i] < kNone ? __builtin_amdgcn_readlane(cm, static_cast<int>(pk[i] & 63u)) : 0u;
+      used |= pm[i];
     }
+#pragma unroll
+    for (int i = 0; i < kPick; ++i)
+      if (pk[i] < kNone) commit(pk[i], pm[i]);
   }
   if ((nU & 63) != 0 && lane < (nU & 63)) ord[(nU & ~63) + lane] = static_cast<uint16_t>(ordv);
   __syncthreads();

@@ -156,9 +156,9 @@ sas_status sas_take_device_fault(unsigned* fault);
  * then nU distinct block indices.  The candidates are the first 64 union
  * blocks (ascending) not yet placed, ranked by how many of the last three
  * placed blocks their busiest tile needed (fewer first), then by how many
- * tiles need them (more first), then by block; each step places the best
- * candidate and then, on the same ranking, the best one whose tiles are
- * disjoint from the first's.  Any order gives the same attention up to
+ * tiles need them (more first), then by block; each step ranks them once
+ * and places up to two: the best, then the best whose tiles are disjoint
+ * from the first's.  Any order gives the same attention up to
  * floating-point summation order; this one balances the tiles' work inside
  * each window of the ring.
  *   idx: [B,T,Hs,S] int32 as sas_topk_blocks writes it (entries outside

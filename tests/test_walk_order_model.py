@@ -8,9 +8,9 @@ tile's blocks fall into the ring's windows.  The model:
   * union blocks ascending, mask[p] = the tiles whose tokens selected block p;
   * candidates: the first 64 unplaced union positions, ranked by (largest
     window load among its tiles, 64 - tiles needing it, position), the window
-    being the last three placed blocks; each step places the best candidate
-    and then, ranked on the same window, the best one whose tiles are
-    disjoint from the first's.
+    being the last three placed blocks; each step ranks them once and places
+    up to two: the best, then the best whose tiles are disjoint from the
+    first's.
 CPU tests check the model (a permutation of the union, better-balanced
 windows than ascending order on random selections, edge cases); GPU tests
 compare the kernel's order with the model bit-exactly (integer work).
@@ -22,6 +22,7 @@ import torch
 import synth
 
 WIN = 4
+PICK = 2
 
 
 def walk_tpw(TPT):
@@ -70,12 +71,15 @@ def place(masks):
             m = masks[p]
             ml = max(cnt.get(w, 0) for w in range(16) if m >> w & 1)
             return (ml, 64 - bin(m).count("1"), p)
-        ranked = sorted(cand, key=key)
-        p1 = ranked[0]
-        p2 = next((q for q in ranked[1:] if masks[q] & masks[p1] == 0), None)
-        push(p1)
-        if p2 is not None:
-            push(p2)
+        picks, used = [], 0
+        for q in sorted(cand, key=key):
+            if masks[q] & used == 0:
+                picks.append(q)
+                used |= masks[q]
+                if len(picks) == PICK:
+                    break
+        for q in picks:
+            push(q)
     return out
 
 
@@ -161,9 +165,10 @@ def test_small_unions_and_empty_rows():
 
 
 def test_window_rule_matches_the_plain_definition():
-    """Every placement is the best candidate by a recount of the window (the
-    last three placed blocks) or the disjoint second of its step, ranked on
-    the window before the step's first (a check of the model's bookkeeping)."""
+    """Each step's placements are, in turn, the best candidate by a recount
+    of the window (the last three blocks placed before the step) among those
+    whose tiles are disjoint from the step's earlier picks, at most PICK per
+    step (a check of the model's bookkeeping)."""
     rng = np.random.default_rng(5)
     rows, t0 = random_group(rng, 200)
     _, masks = union_and_masks(rows, t0, 4)
@@ -178,15 +183,15 @@ def test_window_rule_matches_the_plain_definition():
     while n < len(order):
         window = order[max(0, n - (WIN - 1)):n]
         cand = left[:64]
-        p1 = min(cand, key=lambda q: key(q, window))
-        assert order[n] == p1
-        rest = [q for q in cand if q != p1 and masks[q] & masks[p1] == 0]
-        left.remove(p1)
-        n += 1
-        if rest:
-            p2 = min(rest, key=lambda q: key(q, window))
-            assert order[n] == p2
-            left.remove(p2)
+        used = 0
+        for _ in range(PICK):
+            rest = [q for q in cand if masks[q] & used == 0]
+            if not rest:
+                break
+            p = min(rest, key=lambda q: key(q, window))
+            assert order[n] == p
+            used |= masks[p]
+            left.remove(p)
             n += 1
 
 
