@@ -11,9 +11,11 @@
 //
 // One workgroup = 16 consecutive tokens of one (batch, selection head: a KV
 // head, or a query head when every query head has its own gate, scoring the
-// gate keys of its KV head); all 16 share
-// the same block c, so the historical block keys form one fp32 tile product
-// (fp32 MFMA: index parity needs fp32-accurate scores).
+// gate keys of its KV head); all 16 share the same block c, so the
+// historical block keys form one fp32 tile product (fp32 MFMA: index parity
+// needs fp32-accurate scores), its block-key operand read from memory (L2:
+// the keys of one head are shared by all its workgroups) straight into
+// registers.  The scores go through LDS to one wave per token row.
 // Selection: exact K-th largest order key by bitwise searches with wave-wide
 // counts (over the keys above the K-th largest lane maximum when they fit one
 // per lane), then equal keys taken in ascending block order.
@@ -26,32 +28,34 @@ namespace sas {
 namespace {
 
 constexpr int kTokPerWG = 16;
+// floats per score row: room for every candidate, odd so that the 16 rows
+// start on different LDS banks
+__host__ __device__ inline int topk_score_pitch(int NB) { return NB | 1; }
 
 template <int DG>
 __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
-  constexpr int KCH = 64;            // block keys per chunk (16 per wave)
-  constexpr int KP = DG + 4;         // LDS pitch (floats) of a staged key
   constexpr int NS = DG / 16;        // 16-wide d groups
-  constexpr int KU = KCH * DG / 4 / 256;   // float4 per thread per chunk
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ uint32_t gath[4][64];             // per wave: keys above the lane-maximum bound
-  float* ks = smem;                            // [64][KP]
-  float* sc = ks + KCH * KP;                   // [16][NBP]
-  const int NBP = ((p.NB + 3) / 4) * 4;
+  float* sc = smem;                            // [16][NBP] scores (odd pitch: no bank conflicts)
+  const int NBP = topk_score_pitch(p.NB);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int sg = blockIdx.y, b = blockIdx.z;   // selection head
   const int kv = sg / p.kdiv;                    // its KV head (gate keys)
-  const int t0 = blockIdx.x * kTokPerWG;
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * kTokPerWG;   // late (long) rows first
   const int c = t0 / 64;
   const int ntok = min(kTokPerWG, p.T - t0);
   const float inv_sqrt_dg = 1.0f / sqrtf(static_cast<float>(DG));
 
   // historical scores S^T[key, token] = K Q^T on fp32 MFMA 16x16x4; the k
   // index of MFMA step (s, i) is d = 16 s + 4 (lane / 16) + i, the same for
-  // both operands.  Query operand (token = lane % 16) in registers.
+  // both operands.  Query operand (token = lane % 16) in registers; wave w
+  // takes keys 16 w .. 16 w + 15 of each 64-key chunk, its block-key operand
+  // (key = lane % 16) loaded from memory straight into registers, the next
+  // chunk's while the current one is used.
   float qb[NS][4];
   {
     const float* qrow =
@@ -62,40 +66,24 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       qb[dq][0] = v.x; qb[dq][1] = v.y; qb[dq][2] = v.z; qb[dq][3] = v.w;
     }
   }
-  // block keys k_gate[64 j + 63], staged per 64-key chunk through registers
-  // (the next chunk's loads are in flight while the current one is used)
-  float4 kst[KU];
-  auto kload = [&](int j0) __attribute__((always_inline)) {
+  float4 ka[NS], kn[NS];
+  auto kload = [&](int j0, float4* dst) __attribute__((always_inline)) {
+    const int j = j0 + 16 * wv + l16;
+    const float* krow =
+        p.k_gate + ((static_cast<size_t>(b) * p.T + 64 * min(j, c - 1) + 63) * p.Hkv + kv) * DG + 4 * g4;
 #pragma unroll
-    for (int x = 0; x < KU; ++x) {
-      const int u = tid + 256 * x;
-      const int r = u / (DG / 4), f = u - r * (DG / 4);
-      const int j = j0 + r;
-      kst[x] = (j < c) ? *reinterpret_cast<const float4*>(
-                             p.k_gate + ((static_cast<size_t>(b) * p.T + 64 * j + 63) * p.Hkv + kv) * DG + 4 * f)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int dq = 0; dq < NS; ++dq) dst[dq] = *reinterpret_cast<const float4*>(krow + 16 * dq);
   };
-  if (c > 0) kload(0);
-  for (int j0 = 0; j0 < c; j0 += KCH) {
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < KU; ++x) {
-      const int u = tid + 256 * x;
-      const int r = u / (DG / 4), f = u - r * (DG / 4);
-      *reinterpret_cast<float4*>(&ks[r * KP + 4 * f]) = kst[x];
-    }
-    __syncthreads();
-    if (j0 + KCH < c) kload(j0 + KCH);
+  if (c > 0) kload(0, ka);
+  for (int j0 = 0; j0 < c; j0 += 64) {
+    if (j0 + 64 < c) kload(j0 + 64, kn);
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-    const float* krow = &ks[(16 * wv + l16) * KP + 4 * g4];
 #pragma unroll
     for (int dq = 0; dq < NS; ++dq) {
-      const float4 a = *reinterpret_cast<const float4*>(krow + 16 * dq);
-      acc = mfma16x16x4f32(a.x, qb[dq][0], acc);
-      acc = mfma16x16x4f32(a.y, qb[dq][1], acc);
-      acc = mfma16x16x4f32(a.z, qb[dq][2], acc);
-      acc = mfma16x16x4f32(a.w, qb[dq][3], acc);
+      acc = mfma16x16x4f32(ka[dq].x, qb[dq][0], acc);
+      acc = mfma16x16x4f32(ka[dq].y, qb[dq][1], acc);
+      acc = mfma16x16x4f32(ka[dq].z, qb[dq][2], acc);
+      acc = mfma16x16x4f32(ka[dq].w, qb[dq][3], acc);
     }
     const int jb = j0 + 16 * wv + 4 * g4;     // keys jb .. jb+3 of token l16
     if (l16 < ntok) {
@@ -103,6 +91,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       for (int i = 0; i < 4; ++i)
         if (jb + i < c) sc[l16 * NBP + jb + i] = acc[i] * inv_sqrt_dg;
     }
+#pragma unroll
+    for (int dq = 0; dq < NS; ++dq) ka[dq] = kn[dq];
   }
   __syncthreads();
   // current-block score with the token's own prefix key
@@ -148,9 +138,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       mx = wave_max(mx);
       float se = 0.f;
 #pragma unroll
-      for (int e = 0; e < EM; ++e) se += expf(sv[e] - mx);
+      for (int e = 0; e < EM; ++e) se += fast_exp2((sv[e] - mx) * kLog2e);
       se = wave_sum(se);
-      const float lse = mx + logf(se);
+      const float lse = mx + __builtin_amdgcn_logf(se) * kLn2;
       const size_t rowid = (static_cast<size_t>(b) * p.T + t0 + tl) * p.Hs + sg;
       // order keys of the historical candidates; 0 elsewhere, which no
       // candidate threshold (always >= 1) reaches
@@ -161,16 +151,18 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       int need_eq = 0;
       if (!all) {
         // thr = the largest t with #(keys >= t) >= K, by a bitwise search.
-        // The K-th largest lane maximum t0 bounds it from below (the K
-        // largest lane maxima are K keys at or above t0; at least K lanes hold
-        // a candidate since c > K and K < 64), so when the keys >= t0 fit one
-        // per lane the search runs over them alone (same counts for every
-        // t >= t0).
+        // The K-th largest lane maximum bounds it from below (the K largest
+        // lane maxima are K keys at or above it; at least K lanes hold a
+        // candidate since c > K and K < 64), and so does t0, that maximum
+        // with its low 16 bits cleared; when the keys >= t0 fit one per lane
+        // the search runs over them alone (same counts for every t >= t0).
         uint32_t lmax = 0;
 #pragma unroll
         for (int e = 0; e < EM; ++e) lmax = max(lmax, kreg[e]);
+        // (its top 16 bits suffice for a bound: any t with K keys at or
+        // above it and few enough above it to gather will do)
         uint32_t t0k = 0;
-        for (int bit = 31; bit >= 0; --bit) {
+        for (int bit = 31; bit >= 16; --bit) {
           const uint32_t cand = t0k | (1u << bit);
           if (wave_count(lmax >= cand) >= K) t0k = cand;
         }
@@ -250,8 +242,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
 }  // namespace
 
 size_t topk_smem_bytes(int NB, int dg) {
-  const int NBP = ((NB + 3) / 4) * 4;
-  return sizeof(float) * (64 * (dg + 4) + static_cast<size_t>(kTokPerWG) * NBP);
+  (void)dg;
+  return sizeof(float) * static_cast<size_t>(kTokPerWG) * topk_score_pitch(NB);
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
