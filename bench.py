@@ -84,17 +84,33 @@ def load_traffic(kernel_key: str, src_hash: str):
 
 
 COPY_BYTES = 1 << 30          # the calibration copy (--copy-calib)
-TRAFFIC_SOURCES = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
-                   "dq_kernel": "attn_bwd.hip", "topk_kernel": "topk.hip",
-                   "decode_attn_kernel": "decode.hip",
-                   # fp32 gate keys (the bench also runs the bf16-key variant)
-                   "decode_score_kernel<128, false>": "decode.hip",
-                   "decode_topk_kernel": "decode.hip", "decode_merge_kernel": "decode.hip",
-                   "gbwd_key_kernel": "router_bwd.hip", "gbwd_query_kernel": "router_bwd.hip",
-                   "gbwd_blockkey_kernel": "router_bwd.hip", "gbwd_wsum_kernel": "router_bwd.hip",
-                   "gbwd_rows_kernel": "router_bwd.hip", "gbwd_reduce_kernel": "router_bwd.hip",
-                   "gbwd_colsum_kernel": "router_bwd.hip",
-                   "gbwd_blockkey_sum_kernel": "router_bwd.hip"}
+# sources each kernel's behaviour depends on (besides the shared headers): a
+# profile taken on other sources is stale and not reported.  The forward and
+# dQ walks also depend on the staging order walk_order.hip makes for them.
+KERNEL_SOURCES = {"sparse_fwd_kernel": ("attn_fwd.hip", "walk_order.hip"),
+                  "dkdv_kernel": ("attn_bwd.hip",),
+                  "dq_kernel": ("attn_bwd.hip", "walk_order.hip"),
+                  "walk_order_kernel": ("walk_order.hip",),
+                  "topk_kernel": ("topk.hip",),
+                  "gate_query_kernel": ("router.hip",), "gate_key_kernel": ("router.hip",),
+                  "decode_attn_kernel": ("decode.hip",),
+                  # fp32 gate keys (the bench also runs the bf16-key variant)
+                  "decode_score_kernel<128, false>": ("decode.hip",),
+                  "decode_topk_kernel": ("decode.hip",), "decode_merge_kernel": ("decode.hip",),
+                  "sas_decode": ("decode.hip",)}
+for _k in ("gbwd_key_kernel", "gbwd_query_kernel", "gbwd_blockkey_kernel", "gbwd_wsum_kernel",
+           "gbwd_rows_kernel", "gbwd_reduce_kernel", "gbwd_colsum_kernel",
+           "gbwd_blockkey_sum_kernel", "sas_gate_score_bwd"):
+    KERNEL_SOURCES[_k] = ("router_bwd.hip",)
+SHARED_HEADERS = ("sas_device.h", "sas_kernels.h", "bwd_index.h")
+# kernels whose HBM traffic the counter summary records
+TRAFFIC_KERNELS = tuple(k for k in KERNEL_SOURCES if not k.startswith("sas_")
+                        and k not in ("gate_query_kernel", "gate_key_kernel"))
+
+
+def kernel_hash(key: str) -> str:
+    csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
+    return source_hash([os.path.join(csrc, f) for f in KERNEL_SOURCES[key] + SHARED_HEADERS])
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
@@ -116,7 +132,6 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
                 vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
-    csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
     res, lines = {}, []
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = per_kernel(d, counter)
@@ -128,7 +143,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
         factor = COPY_BYTES / ref
         lines.append(f"{counter}: calibration copy of {COPY_BYTES} B reads {ref:.0f} KiB "
                      f"per dispatch -> factor {factor:.4f} B per KiB")
-        for key in TRAFFIC_SOURCES:
+        for key in TRAFFIC_KERNELS:
             # the key as a whole name ("::topk_kernel" is not inside
             # "::decode_topk_kernel")
             l = [v for k, ll in vals.items() if k.startswith(key) or ("::" + key) in k
@@ -142,8 +157,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
             e["dispatches"] = len(l)
     for key, e in res.items():
         e["bytes_per_launch"] = e.get("fetch_size_bytes", 0) + e.get("write_size_bytes", 0)
-        e["source_hash"] = source_hash([os.path.join(csrc, f) for f in
-                                        (TRAFFIC_SOURCES[key], "sas_device.h", "sas_kernels.h")])
+        e["source_hash"] = kernel_hash(key)
         lines.append(f"{key}: fetch {e.get('fetch_size_bytes', 0) / 1e9:.3f} GB + write "
                      f"{e.get('write_size_bytes', 0) / 1e9:.3f} GB per launch "
                      f"({e['dispatches']} dispatches)")
@@ -156,8 +170,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
             "bytes_per_launch": round(sum(res[k]["bytes_per_launch"] * res[k]["dispatches"]
                                           for k in gb) / calls),
             "kernels": sorted(gb),
-            "source_hash": source_hash([os.path.join(csrc, f) for f in
-                                        ("router_bwd.hip", "sas_device.h", "sas_kernels.h")])}
+            "source_hash": kernel_hash("sas_gate_score_bwd")}
         lines.append(f"sas_gate_score_bwd: {res['sas_gate_score_bwd']['bytes_per_launch'] / 1e9:.3f}"
                      f" GB per call ({' + '.join(sorted(gb))})")
     # the decode step as a whole: each of its kernels runs once per step
@@ -166,8 +179,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_json: str):
         res["sas_decode"] = {
             "bytes_per_launch": sum(res[k]["bytes_per_launch"] for k in dec),
             "kernels": sorted(dec),
-            "source_hash": source_hash([os.path.join(csrc, f) for f in
-                                        ("decode.hip", "sas_device.h", "sas_kernels.h")])}
+            "source_hash": kernel_hash("sas_decode")}
         lines.append(f"sas_decode: {res['sas_decode']['bytes_per_launch'] / 1e9:.3f} GB per step "
                      f"({' + '.join(sorted(dec))})")
     json.dump(res, open(out_json, "w"), indent=1, sort_keys=True)
@@ -349,7 +361,7 @@ def time_decode_budget(sas, wd, K: int, seed: int, steps: int) -> dict:
 
 
 COUNTER_KERNELS = ("sparse_fwd_kernel", "dkdv_kernel", "dq_kernel", "topk_kernel",
-                   "gate_query_kernel", "gate_key_kernel")
+                   "walk_order_kernel", "gate_query_kernel", "gate_key_kernel")
 
 
 def summarize_counters(dirs, out_json: str):
@@ -371,10 +383,6 @@ def summarize_counters(dirs, out_json: str):
                     continue
                 vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
-    csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
-    src = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
-           "dq_kernel": "attn_bwd.hip", "topk_kernel": "topk.hip",
-           "gate_query_kernel": "router.hip", "gate_key_kernel": "router.hip"}
     res, lines = {}, []
     for k, cs in vals.items():
         e = {c: sum(v) / len(v) for c, v in cs.items()}
@@ -392,8 +400,7 @@ def summarize_counters(dirs, out_json: str):
             d["l2_hit_rate"] = e.get("TCC_HIT_sum", 0.0) / e["TCC_REQ_sum"]
         if "TCP_TCC_READ_REQ_sum" in e:
             d["l1_to_l2_read_bytes"] = e["TCP_TCC_READ_REQ_sum"] * 128
-        d["source_hash"] = source_hash([os.path.join(csrc, f) for f in
-                                        (src[k], "sas_device.h", "sas_kernels.h")])
+        d["source_hash"] = kernel_hash(k)
         res[k] = d
         lines.append(f"{k}: " + ", ".join(f"{n} {d[n]:.4g}" for n in
                                           ("executed_mfma_flops", "mfma_busy_frac", "l2_hit_rate",
@@ -591,8 +598,9 @@ def main():
     def avg_ms(lst, a, b):
         return sum(l[a].elapsed_time(l[b]) for l in lst) / len(lst)
 
-    kern_ms = {"sparse_fwd_kernel": avg_ms(fevs, 1, 2), "transpose_v": avg_ms(fevs, 0, 1),
-               "bwd_delta+csr": avg_ms(bevs, 0, 1), "dkdv_kernel": avg_ms(bevs, 1, 2),
+    kern_ms = {"sparse_fwd_kernel": avg_ms(fevs, 1, 2),
+               "walk_order+transpose_v": avg_ms(fevs, 0, 1),
+               "bwd_delta+csr+walk_order": avg_ms(bevs, 0, 1), "dkdv_kernel": avg_ms(bevs, 1, 2),
                "dq_kernel": avg_ms(bevs, 2, 3)}
 
     if args.copy_calib:
@@ -611,15 +619,12 @@ def main():
     bwd_tflops = bwd_flops / (stage_ms[3] * 1e-3) / 1e12
     attn_tflops = (fwd_flops + bwd_flops) / ((stage_ms[2] + stage_ms[3]) * 1e-3) / 1e12
 
-    csrc = os.path.join(ROOT, "gated_block_sparse_gate_amd", "csrc")
     # algorithmic FLOPs per launch: the contractions each kernel must perform,
     # 2 D per attended (query head, key) pair each: forward S and PV (4 D);
     # dK/dV kernel S, dP, dV, dK (8 D; it also writes dS); dQ kernel dQ = dS K
     # (2 D, reading dS)
     kflops = {"sparse_fwd_kernel": 4.0 * D * pairs, "dkdv_kernel": 8.0 * D * pairs,
               "dq_kernel": 2.0 * D * pairs}
-    ksrc = {"sparse_fwd_kernel": "attn_fwd.hip", "dkdv_kernel": "attn_bwd.hip",
-            "dq_kernel": "attn_bwd.hip"}
     kernels = {}
     for kname, fl in kflops.items():
         ms = kern_ms[kname]
@@ -627,8 +632,7 @@ def main():
                           "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     dom = max(kflops, key=lambda k: kern_ms[k])
     dom_tf = kflops[dom] / (kern_ms[dom] * 1e-3) / 1e12
-    dom_hash = source_hash([os.path.join(csrc, f) for f in (ksrc[dom], "sas_device.h",
-                                                            "sas_kernels.h")])
+    dom_hash = kernel_hash(dom)
     roofline = {
         "kernel": dom,
         "bound": "mfma",
@@ -647,8 +651,7 @@ def main():
         roofline["counters"] = dict(cnt, executed_over_algorithmic=round(
             cnt["executed_mfma_flops"] / kflops[dom], 3)) if "executed_mfma_flops" in cnt else cnt
     for kname in kflops:
-        c = load_counters(kname, source_hash([os.path.join(csrc, f) for f in
-                                              (ksrc[kname], "sas_device.h", "sas_kernels.h")]))
+        c = load_counters(kname, kernel_hash(kname))
         if c:
             kernels[kname]["counters"] = c
 
@@ -709,8 +712,7 @@ def main():
         rb_flops = 2.0 * rows * Hkv * dg * (3 * G * D + 3 * 3 * D + 2 * S)
         t_hbm = rb_bytes / (PEAK_HBM_GBS * 1e9)
         t_mfma = rb_flops / (PEAK_FP32_TFLOPS * 1e12)
-        rb_traffic = load_traffic("sas_gate_score_bwd", source_hash(
-            [os.path.join(csrc, f) for f in ("router_bwd.hip", "sas_device.h", "sas_kernels.h")]))
+        rb_traffic = load_traffic("sas_gate_score_bwd", kernel_hash("sas_gate_score_bwd"))
         out["router_bwd"] = {
             "workload": w.name, "ms": round(rb_ms, 4),
             "algorithmic_bytes": rb_bytes, "algorithmic_flops": rb_flops,
@@ -836,8 +838,7 @@ def main():
         lens = xd["ctx_len"].cpu().tolist()
         kvb, gkb, smb = decode_bytes(lens, wd.Hkv, wd.D, wd.dg, Kd, wd.G)
         tot = kvb + gkb + smb
-        dec_hash = source_hash([os.path.join(csrc, f) for f in ("decode.hip", "sas_device.h",
-                                                                "sas_kernels.h")])
+        dec_hash = kernel_hash("sas_decode")
         out["decode"] = {
             "workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D, "dg": wd.dg,
             "budget": 64 * (Kd + 1), "ctx_len_range": [wd.Lmin, wd.Lmax],

@@ -14,8 +14,8 @@
 //  1. per compute tile w (TPT consecutive tokens), the bitmap of the blocks
 //     some token of the tile selected; their union, in ascending order, with
 //     mask[p] = the set of tiles that need union block p;
-//  2. placement: the candidates are the first 64 union blocks not yet placed
-//     (one per lane); a candidate ranks by the load of its busiest tile in
+//  2. placement: the candidates are the first kLook union blocks not yet
+//     placed (one per lane); a candidate ranks by the load of its busiest tile in
 //     the window of the last kWin - 1 placed blocks, then by the number of
 //     tiles that need it (more first), then by position.  Each step ranks
 //     the candidates once and places up to kPick of them: the best, then the
@@ -32,6 +32,8 @@ namespace {
 
 constexpr int kWin = 4;     // ring window the placement balances (the forward's ring depth)
 constexpr int kPick = 2;    // placements per step
+constexpr int kLook = 64;   // candidates: the first kLook unplaced blocks
+static_assert(kLook >= 1 && kLook <= 64, "one candidate per lane");
 
 // v = min(v, v of another lane) by a DPP move; lanes outside row_mask (or
 // reading outside the wave) take the minimum's identity
@@ -114,10 +116,11 @@ __global__ __launch_bounds__(64) void walk_order_kernel(WalkOrderParams a) {
   // them: the best, then the best whose tiles are disjoint from the tiles
   // already picked, and so on.
   constexpr uint32_t kNone = 0xFF000000u;
-  uint32_t cm = lane < nU ? mask[lane] : 0u;
-  uint32_t kb = lane < nU ? (((64u - __popc(cm)) << 16) | (lane << 6) | lane) : kNone;
-  int nxt = min(64, nU);
-  uint32_t sb = (nxt + lane < nU) ? mask[nxt + lane] : 0u;
+  const bool cand0 = lane < min(kLook, nU);
+  uint32_t cm = cand0 ? mask[lane] : 0u;
+  uint32_t kb = cand0 ? (((64u - __popc(cm)) << 16) | (lane << 6) | lane) : kNone;
+  int nxt = min(kLook, nU);
+  uint32_t sb = ((nxt & ~63) + lane < nU) ? mask[(nxt & ~63) + lane] : 0u;
   uint32_t ordv = 0u;
   uint32_t c0 = 0u, c1 = 0u;                    // per-tile window load, bit-sliced (0..3)
   uint32_t h0 = 0u, h1 = 0u, h2 = 0u;           // masks of the last three placed blocks
