@@ -116,6 +116,26 @@ def test_workspace_checks():
     assert st == sas.SAS_ERR_WORKSPACE
 
 
+def test_walk_order_validation():
+    """sas_walk_order rejects bad dims, null / unaligned pointers and a short
+    order buffer before launching anything."""
+    lib = sas.load_library()
+    d = _dims(T=4096)
+    need = sas.workspace_size(sas.OP_WALK_ORDER, d)
+    p = ctypes.c_void_p(4096)
+    assert lib.sas_walk_order(ctypes.byref(d), None, p, need, None) == sas.SAS_ERR_INVALID
+    assert b"'idx'" in lib.sas_last_error()
+    assert lib.sas_walk_order(ctypes.byref(d), p, ctypes.c_void_p(4098), need, None) == \
+        sas.SAS_ERR_INVALID
+    assert lib.sas_walk_order(ctypes.byref(d), p, p, need - 1, None) == sas.SAS_ERR_INVALID
+    assert b"too small" in lib.sas_last_error()
+    bad = _dims(T=4096, D=96)
+    assert lib.sas_walk_order(ctypes.byref(bad), p, p, need, None) == sas.SAS_ERR_UNSUPPORTED
+    # per-query-head gates: Hq selection heads of 64-token groups (TPT = 16)
+    pq = _dims(T=4096, flags=sas.FLAG_GATE_PER_QUERY_HEAD)
+    assert sas.workspace_size(sas.OP_WALK_ORDER, pq) == 8 * 64 * 72 * 2
+
+
 def test_decode_dims_validation():
     lib = sas.load_library()
     good = sas.DecodeDims(64, 32, 8, 128, 128, 64, 31, 65536, 1024, 1)
