@@ -86,11 +86,12 @@ def load_traffic(kernel_key: str, src_hash: str):
 COPY_BYTES = 1 << 30          # the calibration copy (--copy-calib)
 # sources each kernel's behaviour depends on (besides the shared headers): a
 # profile taken on other sources is stale and not reported.  The forward and
-# dQ walks also depend on the staging order walk_order.hip makes for them.
-KERNEL_SOURCES = {"sparse_fwd_kernel": ("attn_fwd.hip", "walk_order.hip"),
+# dQ walks also depend on the staging order walk_order.h makes for them.
+KERNEL_SOURCES = {"sparse_fwd_kernel": ("attn_fwd.hip", "walk_order.hip", "walk_order.h"),
                   "dkdv_kernel": ("attn_bwd.hip",),
-                  "dq_kernel": ("attn_bwd.hip", "walk_order.hip"),
-                  "walk_order_kernel": ("walk_order.hip",),
+                  "dq_kernel": ("attn_bwd.hip", "walk_order.h"),
+                  "walk_order_kernel": ("walk_order.hip", "walk_order.h"),
+                  "bwd_prep_kernel": ("attn_bwd.hip", "walk_order.h"),
                   "topk_kernel": ("topk.hip",),
                   "gate_query_kernel": ("router.hip",), "gate_key_kernel": ("router.hip",),
                   "decode_attn_kernel": ("decode.hip",),

@@ -22,18 +22,20 @@
 //   dq         : query-block stationary, same walk as the forward; also
 //                produces dlogg (each (t, j) pair is visited exactly once).
 #include "bwd_index.h"
-#include "sas_kernels.h"
+#include "walk_order.h"
 
 namespace sas {
 
 namespace {
 
+// Delta = rowsum(dO * o) of 16 rows per 256 threads (16 threads per row),
+// rows of workgroup blk
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const float* o32,
-                                                        const uint16_t* dout, float* delta,
-                                                        long nrows) {
+__device__ __forceinline__ void delta_rows(const uint16_t* o, const float* o32,
+                                           const uint16_t* dout, float* delta, long nrows,
+                                           long blk) {
   constexpr int EPL = D / 16;
-  const long gid = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x;
+  const long gid = blk * 256 + threadIdx.x;
   const long row = gid >> 4;
   const int part = static_cast<int>(gid & 15);
   float acc = 0.f;
@@ -54,6 +56,24 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* o, const
   acc += __shfl_xor(acc, 4, 64);
   acc += __shfl_xor(acc, 8, 64);
   if (part == 0 && row < nrows) delta[row] = acc;
+}
+
+// The backward's first launch: the dQ walk's staging order and Delta side by
+// side.  The order's workgroups (one token group per wave; a serial,
+// latency-bound placement) come first, and the Delta rows (bandwidth-bound)
+// fill the slots beside them, so the two overlap.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, WalkOrderParams wo,
+                                                       int nord_blocks, int ngroups,
+                                                       int wave_words, long nrows) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t prep_smem[];
+  if (static_cast<int>(blockIdx.x) < nord_blocks) {
+    const int w = threadIdx.x >> 6;
+    const int g = blockIdx.x * 4 + w;
+    walk_order_group(wo, g, g < ngroups, threadIdx.x & 63, prep_smem + w * wave_words);
+    return;
+  }
+  delta_rows<D>(p.o, p.o32, p.dout, p.delta, nrows, static_cast<long>(blockIdx.x) - nord_blocks);
 }
 
 // Per (b, selection head sg, query block c): which of the 64 tokens selected
@@ -911,17 +931,22 @@ template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   const long nrows = static_cast<long>(p.B) * p.T * p.Hq;
   timing_mark(0, st);
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((nrows * 16 + 255) / 256), dim3(256), 0, st,
-                     p.o, p.o32, p.dout, p.delta, nrows);
+  {
+    const WalkOrderParams wo{p.idx, p.order, p.B, p.T, p.Hs, p.S, p.NB, p.TPT, p.ost};
+    const int ngroups = static_cast<int>(walk_order_groups(p.B, p.T, p.Hs, p.TPT));
+    const int nord = (ngroups + 3) / 4;
+    const size_t wave_bytes = walk_order_smem_bytes(p.NB);
+    const long ndelta = (nrows * 16 + 255) / 256;
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(static_cast<unsigned>(nord + ndelta)), dim3(256),
+                       4 * wave_bytes, st, p, wo, nord, ngroups,
+                       static_cast<int>(wave_bytes / 4), nrows);
+  }
   const int NQB = p.NB;
   const unsigned nblk = static_cast<unsigned>(p.B) * p.Hs * NQB;
   hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);
   hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hs), dim3(256), 0, st, p);
   hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hs), dim3(1024), 0, st, p);
   hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
-  const WalkOrderParams wo{p.idx, p.order, p.B, p.T, p.Hs, p.S, p.NB, p.TPT, p.ost};
-  const hipError_t eo = launch_walk_order(wo, st);
-  if (eo != hipSuccess) return eo;
   timing_mark(1, st);
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<unsigned>(p.B) * p.Hkv * p.NB),
                      dim3(256), 0, st, p);

@@ -250,6 +250,7 @@ struct WalkOrderParams {
 };
 hipError_t launch_walk_order(const WalkOrderParams& p, hipStream_t st);
 size_t walk_order_smem_bytes(int NB);
+
 // uint16 entries per group of the order buffer, and the groups of a call
 inline int walk_order_stride(int NB) { return (NB + 1 + 7) & ~7; }
 inline size_t walk_order_groups(int B, int T, int Hs, int TPT) {
