@@ -362,7 +362,7 @@ def time_decode_budget(sas, wd, K: int, seed: int, steps: int) -> dict:
 
 
 COUNTER_KERNELS = ("sparse_fwd_kernel", "dkdv_kernel", "dq_kernel", "topk_kernel",
-                   "walk_order_kernel", "gate_query_kernel", "gate_key_kernel")
+                   "walk_order_kernel", "bwd_prep_kernel", "gate_query_kernel", "gate_key_kernel")
 
 
 def summarize_counters(dirs, out_json: str):
