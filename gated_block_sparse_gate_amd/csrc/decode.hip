@@ -168,9 +168,9 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
     float se = 0.f;
 #pragma unroll
     for (int e = 0; e < ne; ++e)
-      if (e < E) se += expf(score(e) - mx);
+      if (e < E) se += fast_exp2((score(e) - mx) * kLog2e);
     se = wave_sum(se);
-    lse = mx + logf(se);
+    lse = mx + __builtin_amdgcn_logf(se) * kLn2;
     // order keys of the historical candidates; 0 for everything else, which
     // no candidate threshold (always >= 1) reaches
     uint32_t kreg[REG ? EMAX : 1];
@@ -186,15 +186,16 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
     int need_eq = 0;
     if (!all) {
       // thr = the largest t with #(keys >= t) >= K, by a bitwise search.
-      // The K-th largest lane maximum t0 bounds it from below (the K largest
-      // lane maxima are K keys at or above t0; at least K lanes hold a
-      // candidate since c > K and K < 64), so when the keys >= t0 fit one per
-      // lane the search runs over them alone (same counts for every t >= t0).
+      // The K-th largest lane maximum bounds it from below (the K largest
+      // lane maxima are K keys at or above it; at least K lanes hold a
+      // candidate since c > K and K < 64), and so does t0, that maximum with
+      // its low 16 bits cleared; when the keys >= t0 fit one per lane the
+      // search runs over them alone (same counts for every t >= t0).
       uint32_t lmax = 0;
 #pragma unroll
       for (int e = 0; e < ne; ++e) lmax = max(lmax, key(e));
       uint32_t t0 = 0;
-      for (int bit = 31; bit >= 0; --bit) {
+      for (int bit = 31; bit >= 16; --bit) {
         const uint32_t cand = t0 | (1u << bit);
         if (wave_count(lmax >= cand) >= K) t0 = cand;
       }
