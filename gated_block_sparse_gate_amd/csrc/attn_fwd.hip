@@ -19,9 +19,11 @@
 //   the selection masked out.  Online-softmax state stays in registers (one
 //   query row per lane column); the running reference maximum is moved only
 //   when a row's new maximum exceeds it by more than 2^kLazyLog2, so the
-//   output rescale is rare.  The ring protocol is the dQ kernel's (progress
-//   words of the compute waves, fill counters of the stagers, no workgroup
-//   barrier; see attn_bwd.hip).
+//   output rescale is rare.  K and V^T travel in two rings of R slots with the
+//   dQ kernel's protocol each (progress words of the compute waves, fill
+//   counters of the stager, no workgroup barrier; see attn_bwd.hip): a wave
+//   releases a block's K slot right after its S^T reads, so the K stager
+//   waits only on the waves' score steps and runs ahead of the P.V steps.
 #include "sas_kernels.h"
 
 namespace sas {
@@ -55,8 +57,8 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   __shared__ uint16_t ulist[kMaxNB];          // union blocks in staging order
   __shared__ float lgs[64 * kMaxS];           // log2 gates by selection rank [64][S]
   __shared__ uint32_t actw[14 * kMaxNBW];     // per compute wave: which union blocks it needs
-  __shared__ int prog[16];
-  __shared__ unsigned fill_cnt[R];
+  __shared__ int prog[kFwdStagers][16];        // per ring: each compute wave's next block
+  __shared__ unsigned fill_cnt[kFwdStagers][R];
   __shared__ int s_nU;
 
   const int tid = threadIdx.x;
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 
   // ---- selection bitmaps of the group's tokens, their union, log-gates by rank
   for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
-  if (tid < 16) prog[tid] = 0;
-  if (tid < R) fill_cnt[tid] = 0u;
+  if (tid < kFwdStagers * 16) prog[tid >> 4][tid & 15] = 0;
+  if (tid < kFwdStagers * R) fill_cnt[tid / R][tid % R] = 0u;
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hs + sg;
   for (int e = tid; e < ntok * S; e += NT) {
@@ -130,7 +132,9 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     // its stager's tile.
     // the copies are what the compute waves wait on: issue them first
     __builtin_amdgcn_s_setprio(3);
-    const int stg = wv - ncw;
+    const int stg = wv - ncw;           // the ring it fills (0: K, 1: V^T)
+    const int* sprog = prog[stg];
+    unsigned* sfill = fill_cnt[stg];
     const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
     const uint16_t* vtbase =
         a.vt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     }
     auto min_prog = [&]() __attribute__((always_inline)) {
       asm volatile("" ::: "memory");
-      int v = l16 < ncw ? prog[l16] : 0x7fffffff;
+      int v = l16 < ncw ? sprog[l16] : 0x7fffffff;
       asm volatile("" ::: "memory");
       v = min(v, __float_as_int(dpp_mov<0xB1>(__int_as_float(v))));
       v = min(v, __float_as_int(dpp_mov<0x4E>(__int_as_float(v))));
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         // publish everything in flight, then wait for the slot
         wait_vmem_all();
         asm volatile("" ::: "memory");
-        for (; oldest < n; ++oldest) ring_bump(&fill_cnt[oldest % R], lane);
+        for (; oldest < n; ++oldest) ring_bump(&sfill[oldest % R], lane);
         for (int it = 0; min_prog() < n - R + 1; ++it) {
           if (it == kSpinLimit) {
             failed = true;
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         static_assert(kNewer < 64, "vmcnt immediate");
         __builtin_amdgcn_s_waitcnt(0x0f70 | (kNewer & 15) | ((kNewer >> 4) << 14));
         asm volatile("" ::: "memory");
-        ring_bump(&fill_cnt[oldest % R], lane);
+        ring_bump(&sfill[oldest % R], lane);
         ++oldest;
       }
     }
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     if (failed) {
       ring_fault(lane);
     } else {
-      for (; oldest < nU; ++oldest) ring_bump(&fill_cnt[oldest % R], lane);
+      for (; oldest < nU; ++oldest) ring_bump(&sfill[oldest % R], lane);
     }
     return;
   }
@@ -265,24 +269,29 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   for (int k2 = 0; k2 < 2; ++k2) vofs[k2] = KB + l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
 
   const float sl2 = a.scale_log2;
-  const unsigned nstg = kFwdStagers;
   const int cfirst = t0 / 64;            // earliest current block of the group's tokens
-  int v = next_active(0);
-  asm volatile("" ::: "memory");
-  if (lane == 0) prog[wv] = v;           // done with every block before its first needed one
-  bool failed = false;
-  while (v < nU) {
-    const int sl = v % R;
-    const unsigned need = nstg * static_cast<unsigned>(v / R + 1);
-    for (int it = 0; ring_count(&fill_cnt[sl]) < need; ++it) {
-      if (it == kSpinLimit) {
-        failed = true;
-        break;
-      }
+  // wait until ring r's slot holds block u; false if the wait gave up
+  auto wait_slot = [&](int r, int u) __attribute__((always_inline)) {
+    const unsigned need = static_cast<unsigned>(u / R + 1);
+    for (int it = 0; ring_count(&fill_cnt[r][u % R]) < need; ++it) {
+      if (it == kSpinLimit) return false;
       __builtin_amdgcn_s_sleep(kComputeNap);
     }
-    if (failed) break;
-    const uint8_t* st = ring + sl * STAGE;
+    return true;
+  };
+  int v = next_active(0);
+  asm volatile("" ::: "memory");
+  if (lane == 0) {                       // done with every block before its first needed one
+    prog[0][wv] = v;
+    prog[1][wv] = v;
+  }
+  bool failed = false;
+  while (v < nU) {
+    if (!wait_slot(0, v)) {
+      failed = true;
+      break;
+    }
+    const uint8_t* st = ring + (v % R) * STAGE;
     const int j = ulist[v];
     const uint32_t jbit = 1u << (j & 31);
     const int jw = j >> 5;
@@ -304,6 +313,10 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         sacc[mt] = mfma16x16x32(ka, qa[ks], sacc[mt]);
       }
     }
+    const int vnext = next_active(v + 1);
+    asm volatile("" ::: "memory");
+    if (lane == 0) prog[0][wv] = vnext;  // after this wave's last K read of the slot
+    asm volatile("" ::: "memory");
     // maximum of this lane's raw scores over the keys its row may see (the
     // row's 64 keys are spread over the 4 lanes g4 of the row); in the
     // current block the row sees keys 0 .. t - 64 j
@@ -370,6 +383,10 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         pb[k2].w = pack_h2(x[2 * k2 + 1][2], x[2 * k2 + 1][3]);
       }
     }
+    if (!wait_slot(1, v)) {
+      failed = true;
+      break;
+    }
     // O^T[d, row] += V^T[d, keys] . P^T[keys, row]; inside a 32-key step the
     // lane's 8 keys are {4g..4g+3, 16+4g..16+4g+3}, stored contiguously in
     // the transposed copy.
@@ -386,16 +403,19 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         }
       }
     }
-    v = next_active(v + 1);
+    v = vnext;
     asm volatile("" ::: "memory");
-    if (lane == 0) prog[wv] = v;         // after this wave's last read of the slot
+    if (lane == 0) prog[1][wv] = v;      // after this wave's last V^T read of the slot
     asm volatile("" ::: "memory");
   }
   if (failed) {
     ring_fault(lane);
     l_run = NAN;
     asm volatile("" ::: "memory");
-    if (lane == 0) prog[wv] = nU;        // let the stagers finish
+    if (lane == 0) {                     // let the stagers finish
+      prog[0][wv] = nU;
+      prog[1][wv] = nU;
+    }
   }
 
   // ---- epilogue
