@@ -12,14 +12,14 @@
 //   has its own gate), plus two stager waves.  The stagers copy the K tile and
 //   the V^T tile (from a transposed copy of V made once per call, keys in
 //   operand order) of every block in the union of the group's selections, in
-//   the order walk_order.hip makes for the group, into a ring of R LDS slots
+//   the order walk_order.hip makes for the group, into LDS ring slots
 //   with asynchronous global -> LDS copies (16-byte chunks XOR-swizzled per
 //   row, so that the MFMA operand reads are conflict-free).  A compute wave visits only the blocks its tile
 //   needs: S^T = K Q^T and O^T += V^T P^T on MFMA 16x16x32, with rows outside
 //   the selection masked out.  Online-softmax state stays in registers (one
 //   query row per lane column); the running reference maximum is moved only
 //   when a row's new maximum exceeds it by more than 2^kLazyLog2, so the
-//   output rescale is rare.  K and V^T travel in two rings of R slots with the
+//   output rescale is rare.  K and V^T travel in two rings of LDS slots, with the
 //   dQ kernel's protocol each (progress words of the compute waves, fill
 //   counters of the stager, no workgroup barrier; see attn_bwd.hip): a wave
 //   releases a block's K slot right after its S^T reads, so the K stager
@@ -32,33 +32,35 @@ namespace {
 
 constexpr float kLazyLog2 = 8.f;   // weights stay below 2^8 between rescales
 constexpr int kFwdStagers = 2;     // stager 0 copies K tiles, stager 1 V^T tiles
-constexpr int kFwdInflight = 1;    // blocks in flight per stager (< R): each is published as soon as it lands
+constexpr int kFwdInflight = 1;    // blocks in flight per stager (< ring depth): each is published as soon as it lands
+constexpr int kFwdRingK = 4;       // ring depths (K tiles, V^T tiles): 128 KiB of LDS at D = 128
+constexpr int kFwdRingV = 4;
 
 // HILO (the fp32 output is requested, for the backward's Delta): V^T is the
 // bf16 copy and P enters PV as bf16 hi + lo parts (exact to ~2^-16).
 // Otherwise V^T is the scaled fp16 copy and P enters once, in fp16.
-template <int D, bool HILO, int R>
+template <int D, bool HILO, int RK, int RV>
 __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, int tpw) {
   constexpr int KROWB = D * 2;              // bytes per K row
   constexpr int KB = 64 * KROWB;            // K tile bytes
   constexpr int VB = D * 128;               // V^T tile bytes (D rows x 64 keys)
-  constexpr int STAGE = KB + VB;
+  constexpr int RMAX = RK > RV ? RK : RV;
   constexpr int KU = KB / 16;               // 16-byte units per tile
   constexpr int MPS = KU / 64;              // copies per stager per block
   constexpr int KCPR = KROWB / 16;          // 16-byte chunks per K row
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
   static_assert(KB == VB && KU % 64 == 0, "one tile per stager");
-  static_assert(R > kFwdInflight, "ring depth");
+  static_assert(RK > kFwdInflight && RV > kFwdInflight, "ring depth");
 
-  __shared__ __attribute__((aligned(16))) uint8_t ring[R * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RK * KB + RV * VB];   // K ring, then V^T ring
   __shared__ uint32_t bits[64 * kMaxNBW];     // per-token selection bitmaps [64][NBW]
   __shared__ uint8_t pcnt[64 * kMaxNBW];      // popcount prefix per word
   __shared__ uint16_t ulist[kMaxNB];          // union blocks in staging order
   __shared__ float lgs[64 * kMaxS];           // log2 gates by selection rank [64][S]
   __shared__ uint32_t actw[14 * kMaxNBW];     // per compute wave: which union blocks it needs
   __shared__ int prog[kFwdStagers][16];        // per ring: each compute wave's next block
-  __shared__ unsigned fill_cnt[kFwdStagers][R];
+  __shared__ unsigned fill_cnt[kFwdStagers][RMAX];
   __shared__ int s_nU;
 
   const int tid = threadIdx.x;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
   // ---- selection bitmaps of the group's tokens, their union, log-gates by rank
   for (int i = tid; i < 64 * NBW; i += NT) bits[i] = 0u;
   if (tid < kFwdStagers * 16) prog[tid >> 4][tid & 15] = 0;
-  if (tid < kFwdStagers * R) fill_cnt[tid / R][tid % R] = 0u;
+  if (tid < kFwdStagers * RMAX) fill_cnt[tid / RMAX][tid % RMAX] = 0u;
   __syncthreads();
   const size_t rowbase = (static_cast<size_t>(b) * a.T + t0) * a.Hs + sg;
   for (int e = tid; e < ntok * S; e += NT) {
@@ -126,15 +128,17 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 
   if (wv >= ncw) {
     // ================================================================ stager
-    // LDS unit p (16 bytes) of a slot holds, for p < KU, chunk (p % KCPR) ^
-    // lds_swz(r) of K row r = p / KCPR, else chunk (v % 8) ^ tr_swz(d) of V^T
-    // row d = v / 8 (v = p - KU); lane i of copy m fetches unit 64 m + i of
-    // its stager's tile.
+    // LDS unit p (16 bytes) of a K slot holds chunk (p % KCPR) ^ lds_swz(r)
+    // of K row r = p / KCPR; unit p of a V^T slot holds chunk (p % 8) ^
+    // tr_swz(d) of V^T row d = p / 8; lane i of copy m fetches unit 64 m + i
+    // of its stager's tile.
     // the copies are what the compute waves wait on: issue them first
     __builtin_amdgcn_s_setprio(3);
     const int stg = wv - ncw;           // the ring it fills (0: K, 1: V^T)
     const int* sprog = prog[stg];
     unsigned* sfill = fill_cnt[stg];
+    const int Rs = stg == 0 ? RK : RV;   // its ring's depth
+    auto slot_of = [&](int n) __attribute__((always_inline)) { return stg == 0 ? n % RK : n % RV; };
     const uint16_t* kbase = a.k + (static_cast<size_t>(b) * a.T * a.Hkv + kv) * D;
     const uint16_t* vtbase =
         a.vt + (static_cast<size_t>(b) * a.Hkv + kv) * D * static_cast<size_t>(Tp);
@@ -165,12 +169,12 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     int oldest = 0;                  // oldest block copied but not published
     bool failed = false;
     for (int n = 0; n < nU && !failed; ++n) {
-      if (min_prog() < n - R + 1) {
+      if (min_prog() < n - Rs + 1) {
         // publish everything in flight, then wait for the slot
         wait_vmem_all();
         asm volatile("" ::: "memory");
-        for (; oldest < n; ++oldest) ring_bump(&sfill[oldest % R], lane);
-        for (int it = 0; min_prog() < n - R + 1; ++it) {
+        for (; oldest < n; ++oldest) ring_bump(&sfill[slot_of(oldest)], lane);
+        for (int it = 0; min_prog() < n - Rs + 1; ++it) {
           if (it == kSpinLimit) {
             failed = true;
             break;
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         if (failed) break;
       }
       const int j = ulist[n];
-      uint8_t* dst = ring + (n % R) * STAGE + stg * KB;
+      uint8_t* dst = stg == 0 ? ring + slot_of(n) * KB : ring + RK * KB + slot_of(n) * VB;
       if (stg == 0) {
 #pragma unroll
         for (int m = 0; m < MPS; ++m)
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
         static_assert(kNewer < 64, "vmcnt immediate");
         __builtin_amdgcn_s_waitcnt(0x0f70 | (kNewer & 15) | ((kNewer >> 4) << 14));
         asm volatile("" ::: "memory");
-        ring_bump(&sfill[oldest % R], lane);
+        ring_bump(&sfill[slot_of(oldest)], lane);
         ++oldest;
       }
     }
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     if (failed) {
       ring_fault(lane);
     } else {
-      for (; oldest < nU; ++oldest) ring_bump(&sfill[oldest % R], lane);
+      for (; oldest < nU; ++oldest) ring_bump(&sfill[slot_of(oldest)], lane);
     }
     return;
   }
@@ -266,14 +270,15 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     kofs[ks] = l16 * KROWB + (((ks * 4 + g4) ^ lds_swz<KROWB>(l16)) << 4);
   int vofs[2];
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) vofs[k2] = KB + l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
+  for (int k2 = 0; k2 < 2; ++k2) vofs[k2] = l16 * 128 + (((k2 * 4 + g4) ^ tr_swz(l16)) << 4);
 
   const float sl2 = a.scale_log2;
   const int cfirst = t0 / 64;            // earliest current block of the group's tokens
   // wait until ring r's slot holds block u; false if the wait gave up
   auto wait_slot = [&](int r, int u) __attribute__((always_inline)) {
-    const unsigned need = static_cast<unsigned>(u / R + 1);
-    for (int it = 0; ring_count(&fill_cnt[r][u % R]) < need; ++it) {
+    const int Rr = r == 0 ? RK : RV;
+    const unsigned need = static_cast<unsigned>(u / Rr + 1);
+    for (int it = 0; ring_count(&fill_cnt[r][u % Rr]) < need; ++it) {
       if (it == kSpinLimit) return false;
       __builtin_amdgcn_s_sleep(kComputeNap);
     }
@@ -291,7 +296,8 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
       failed = true;
       break;
     }
-    const uint8_t* st = ring + (v % R) * STAGE;
+    const uint8_t* stk = ring + (v % RK) * KB;
+    const uint8_t* stv = ring + RK * KB + (v % RV) * VB;
     const int j = ulist[v];
     const uint32_t jbit = 1u << (j & 31);
     const int jw = j >> 5;
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
       sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(st + mt * 16 * KROWB + kofs[ks]);
+        const uint4 ka = *reinterpret_cast<const uint4*>(stk + mt * 16 * KROWB + kofs[ks]);
         sacc[mt] = mfma16x16x32(ka, qa[ks], sacc[mt]);
       }
     }
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const uint4 va = *reinterpret_cast<const uint4*>(st + dt * 2048 + vofs[k2]);
+        const uint4 va = *reinterpret_cast<const uint4*>(stv + dt * 2048 + vofs[k2]);
         if (HILO) {
           oacc[dt] = mfma16x16x32(va, pb[k2], oacc[dt]);
           oacc[dt] = mfma16x16x32(va, pl[k2], oacc[dt]);
@@ -440,14 +446,14 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
 }
 
 // Tokens per workgroup: 14 compute waves of TPT tokens each, at most 64;
-// static LDS: a ring of 4 (K, V^T) tile pairs plus the selection data.
+// static LDS: the K and V^T rings plus the selection data.
 template <int D, bool HILO>
 hipError_t launch_fwd_dh(const FwdParams& p, hipStream_t st) {
   const int tpw = walk_tpw(p.TPT);
   const int ncw = walk_ncw(p.TPT);
   const unsigned ngrp = (p.T + tpw - 1) / tpw;
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hs * ngrp);
-  hipLaunchKernelGGL((sparse_fwd_kernel<D, HILO, 4>), grid, dim3((ncw + kFwdStagers) * 64), 0, st,
+  hipLaunchKernelGGL((sparse_fwd_kernel<D, HILO, kFwdRingK, kFwdRingV>), grid, dim3((ncw + kFwdStagers) * 64), 0, st,
                      p, ncw, tpw);
   return hipGetLastError();
 }
