@@ -157,18 +157,31 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
       const int j = lane + 64 * e;
       return j < ncand ? sc[j] : -INFINITY;
     };
-    // trip count EMAX (unrolled, guarded) in registers, E (rolled) otherwise
-    constexpr int NE = REG ? EMAX : 0;
-    const int ne = REG ? NE : E;
-    float mx = -INFINITY;
+    // loops over the lane's slots e: unrolled over the EMAX register slots
+    // (each_cand: only e < E; each_slot: all, the keys past E being 0), a
+    // rolled loop of E trips otherwise
+    auto each_cand = [&](auto&& f) __attribute__((always_inline)) {
+      if constexpr (REG) {
 #pragma unroll
-    for (int e = 0; e < ne; ++e)
-      if (e < E) mx = fmaxf(mx, score(e));
+        for (int e = 0; e < EMAX; ++e)
+          if (e < E) f(e);
+      } else {
+        for (int e = 0; e < E; ++e) f(e);
+      }
+    };
+    auto each_slot = [&](auto&& f) __attribute__((always_inline)) {
+      if constexpr (REG) {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) f(e);
+      } else {
+        for (int e = 0; e < E; ++e) f(e);
+      }
+    };
+    float mx = -INFINITY;
+    each_cand([&](int e) { mx = fmaxf(mx, score(e)); });
     mx = wave_max(mx);
     float se = 0.f;
-#pragma unroll
-    for (int e = 0; e < ne; ++e)
-      if (e < E) se += fast_exp2((score(e) - mx) * kLog2e);
+    each_cand([&](int e) { se += fast_exp2((score(e) - mx) * kLog2e); });
     se = wave_sum(se);
     lse = mx + __builtin_amdgcn_logf(se) * kLn2;
     // order keys of the historical candidates; 0 for everything else, which
@@ -192,26 +205,23 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
       // its low 16 bits cleared; when the keys >= t0 fit one per lane the
       // search runs over them alone (same counts for every t >= t0).
       uint32_t lmax = 0;
-#pragma unroll
-      for (int e = 0; e < ne; ++e) lmax = max(lmax, key(e));
+      each_slot([&](int e) { lmax = max(lmax, key(e)); });
       uint32_t t0 = 0;
       for (int bit = 31; bit >= 16; --bit) {
         const uint32_t cand = t0 | (1u << bit);
         if (wave_count(lmax >= cand) >= K) t0 = cand;
       }
       int n0 = 0;
-#pragma unroll
-      for (int e = 0; e < ne; ++e) n0 += wave_count(key(e) >= t0);
+      each_slot([&](int e) { n0 += wave_count(key(e) >= t0); });
       if (n0 <= 64) {
         int nb = 0;
-#pragma unroll
-        for (int e = 0; e < ne; ++e) {
+        each_slot([&](int e) {
           const uint32_t kk = key(e);
           const bool in = kk >= t0;
           const uint64_t m = ballot64(in);
           if (in) gath[wv][nb + __popcll(m & lt_mask)] = kk;
           nb += __popcll(m);
-        }
+        });
         // the wave's LDS accesses complete in order
         const uint32_t v = lane < n0 ? gath[wv][lane] : 0u;
         for (int bit = 31; bit >= 0; --bit) {
@@ -222,34 +232,29 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
         for (int bit = 31; bit >= 0; --bit) {
           const uint32_t cand = thr | (1u << bit);
           int cnt = 0;
-#pragma unroll
-          for (int e = 0; e < ne; ++e) cnt += wave_count(key(e) >= cand);
+          each_slot([&](int e) { cnt += wave_count(key(e) >= cand); });
           if (cnt >= K) thr = cand;
         }
       }
       int gt = 0;
-#pragma unroll
-      for (int e = 0; e < ne; ++e) gt += wave_count(key(e) > thr);
+      each_slot([&](int e) { gt += wave_count(key(e) > thr); });
       need_eq = K - gt;
     }
     int base = 0, eq_seen = 0;
-#pragma unroll
-    for (int e = 0; e < ne; ++e) {
-      if (e < E) {
-        const int j = lane + 64 * e;
-        const bool hist = j < c;
-        const uint32_t kk = key(e);
-        const bool gt = hist && !all && kk > thr;
-        const bool eq = hist && !all && kk == thr;
-        const uint64_t em = ballot64(eq);
-        const bool s_in =
-            hist && (all || gt || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
-        eq_seen += __popcll(em);
-        const uint64_t sm = ballot64(s_in);
-        if (s_in) put(base + __popcll(sm & lt_mask), j, score(e) - lse);
-        base += __popcll(sm);
-      }
-    }
+    each_cand([&](int e) {
+      const int j = lane + 64 * e;
+      const bool hist = j < c;
+      const uint32_t kk = key(e);
+      const bool gt = hist && !all && kk > thr;
+      const bool eq = hist && !all && kk == thr;
+      const uint64_t em = ballot64(eq);
+      const bool s_in =
+          hist && (all || gt || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
+      eq_seen += __popcll(em);
+      const uint64_t sm = ballot64(s_in);
+      if (s_in) put(base + __popcll(sm & lt_mask), j, score(e) - lse);
+      base += __popcll(sm);
+    });
   };
   if constexpr (!LONG)
     select(std::integral_constant<int, kMaxNB / 64>{}, std::true_type{});
