@@ -196,19 +196,23 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   constexpr int UPT = (UNITS + 255) / 256;
   __shared__ __attribute__((aligned(16))) uint8_t Qs[2][32 * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t dOs[2][32 * ROWB];
-  // row metadata of three tile pairs in flight, read as 4-row vectors:
-  // token (-1 = no row), log2-domain bias log g - lse, Delta, source row, entry
-  __shared__ __attribute__((aligned(16))) int m_t[3][32];
-  __shared__ __attribute__((aligned(16))) float m_bias[3][32];
-  __shared__ __attribute__((aligned(16))) float m_delta[3][32];
-  __shared__ __attribute__((aligned(16))) int m_src[3][32];
-  __shared__ __attribute__((aligned(16))) int m_ent[3][32];
+  // row metadata of the tile pairs in flight (slot it % 4), read as 4-row
+  // vectors: token (-1 = no row), log2-domain bias log g - lse, Delta, source
+  // row, entry.  Pair it's slot is written during pair it - 2; its previous
+  // contents (pair it - 4) were last read by that pair's dS stores during
+  // pair it - 3, so the barrier that ends each pair orders every reuse.
+  __shared__ __attribute__((aligned(16))) int m_t[4][32];
+  __shared__ __attribute__((aligned(16))) float m_bias[4][32];
+  __shared__ __attribute__((aligned(16))) float m_delta[4][32];
+  __shared__ __attribute__((aligned(16))) int m_src[4][32];
+  __shared__ __attribute__((aligned(16))) int m_ent[4][32];
   // dS of the tile pair, [32 rows][hi 64 | lo 64] bf16 in operand key order
   // (row pitch 272 bytes: rows 4 apart start on different banks), and each
-  // wave's row sums of dS over its 16 keys
+  // wave's row sums of dS over its 16 keys; two of each, so that pair `it`
+  // is written while pair it - 1 is stored
   constexpr int DSP = 272;
-  __shared__ __attribute__((aligned(16))) uint8_t dsT[32 * DSP];
-  __shared__ __attribute__((aligned(16))) float dsum[4][32];
+  __shared__ __attribute__((aligned(16))) uint8_t dsT[2][32 * DSP];
+  __shared__ __attribute__((aligned(16))) float dsum[2][4][32];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -391,12 +395,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   // of each (token, slot) = sum of its G heads' dS over the block's 64 keys
   // (each (token, slot) is in exactly one tile pair of one workgroup)
   auto store_ds = [&](int pp) __attribute__((always_inline)) {
-    const int msp = pp % 3;
+    const int msp = pp & 3;
     // thread: 16-byte part `part` of rows r0 and r0 + 16 (same head)
     const int r0 = tid >> 4, part = tid & 15, hh = r0 % G;
     const int en0 = m_ent[msp][r0], en1 = m_ent[msp][r0 + 16];
-    const uint4 v0 = ld16(dsT + r0 * DSP + part * 16);
-    const uint4 v1 = ld16(dsT + (r0 + 16) * DSP + part * 16);
+    const uint8_t* dsp = dsT[pp & 1];
+    const float(*dsu)[32] = dsum[pp & 1];
+    const uint4 v0 = ld16(dsp + r0 * DSP + part * 16);
+    const uint4 v1 = ld16(dsp + (r0 + 16) * DSP + part * 16);
     auto dst = [&](int en) {
       const int sg = kv * p.kdiv + ((en >> 6) & 7);
       return p.dsbuf +
@@ -414,10 +420,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       float tot = 0.f;
       if ((G & 3) == 0) {
         for (int h = 0; h < G; h += 4) {
-          const float4 a0 = *reinterpret_cast<const float4*>(&dsum[0][rr + h]);
-          const float4 a1 = *reinterpret_cast<const float4*>(&dsum[1][rr + h]);
-          const float4 a2 = *reinterpret_cast<const float4*>(&dsum[2][rr + h]);
-          const float4 a3 = *reinterpret_cast<const float4*>(&dsum[3][rr + h]);
+          const float4 a0 = *reinterpret_cast<const float4*>(&dsu[0][rr + h]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&dsu[1][rr + h]);
+          const float4 a2 = *reinterpret_cast<const float4*>(&dsu[2][rr + h]);
+          const float4 a3 = *reinterpret_cast<const float4*>(&dsu[3][rr + h]);
           tot += (a0.x + a1.x) + (a2.x + a3.x);
           tot += (a0.y + a1.y) + (a2.y + a3.y);
           tot += (a0.z + a1.z) + (a2.z + a3.z);
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         }
       } else {
         for (int h = 0; h < G; ++h)
-          tot += (dsum[0][rr + h] + dsum[1][rr + h]) + (dsum[2][rr + h] + dsum[3][rr + h]);
+          tot += (dsu[0][rr + h] + dsu[1][rr + h]) + (dsu[2][rr + h] + dsu[3][rr + h]);
       }
       if (en >= 0)
         p.dlogg[((static_cast<size_t>(b) * p.T + (en >> 9)) * p.Hs + kv * p.kdiv +
@@ -434,12 +440,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   };
 
   for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1, ms = it % 3;
+    const int buf = it & 1, ms = it & 3;
     if (tid < 32) {
       if (it + 2 < nit) meta_issue(en_n2, it + 2);
       en_n3 = (it + 3 < nit) ? load_ent(it + 3) : -1;
     }
-    if (it + 1 < nit) rows_issue((it + 1) % 3);
+    if (it + 1 < nit) rows_issue((it + 1) & 3);
     if (it > 0) store_ds(it - 1);
 
     // S, dP for the two row tiles: [rows x 16 keys of this wave]
@@ -475,9 +481,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         ds[tt][i] = pp * (pacc[tt][i] - da[i]);
       }
     }
-    // the previous pair's dS tile has been read (store_ds) by every thread
-    __syncthreads();
-    // dS as bf16 hi + lo into the tile.  Lane (l16, g4) holds rows 4 g4 + i
+    // dS as bf16 hi + lo into tile `buf` (the other one holds pair it - 1,
+    // being stored; this one was last read by the stores of pair it - 2,
+    // during pair it - 1, before the barrier that ended it).  Lane (l16, g4) holds rows 4 g4 + i
     // (i = 0..3) of its key 16 wv + l16; the lanes of an even/odd key pair
     // (adjacent operand positions) swap halves so that each writes two rows
     // as 32-bit (two-key) words: the even lane rows 0, 1, the odd lane rows 2, 3.
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         const uint32_t rl = __float_as_uint(dpp_mov<0xB1>(__uint_as_float(odd ? l01 : l23)));
         const uint32_t ah = odd ? rh : h01, bh = odd ? h23 : rh;   // even key, odd key
         const uint32_t al = odd ? rl : l01, bl = odd ? l23 : rl;
-        uint8_t* row0 = dsT + (tt * 16 + 4 * g4 + 2 * (l16 & 1)) * DSP + 2 * pe;
+        uint8_t* row0 = dsT[buf] + (tt * 16 + 4 * g4 + 2 * (l16 & 1)) * DSP + 2 * pe;
         *reinterpret_cast<uint32_t*>(row0) = __builtin_amdgcn_perm(bh, ah, 0x05040100u);
         *reinterpret_cast<uint32_t*>(row0 + 128) = __builtin_amdgcn_perm(bl, al, 0x05040100u);
         *reinterpret_cast<uint32_t*>(row0 + DSP) = __builtin_amdgcn_perm(bh, ah, 0x07060302u);
@@ -510,7 +516,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         z += dpp_mov<0x124>(z);                // row_ror:4
         z += dpp_mov<0x128>(z);                // row_ror:8
         // lane l16 < 4 now holds row 2 (l16 & 1) + (l16 >> 1) of its g4 group
-        if (l16 < 4) dsum[wv][tt * 16 + 4 * g4 + 2 * (l16 & 1) + (l16 >> 1)] = z;
+        if (l16 < 4) dsum[buf][wv][tt * 16 + 4 * g4 + 2 * (l16 & 1) + (l16 >> 1)] = z;
       }
     }
     // P and dS enter the products as bf16 hi + lo parts (exact to ~2^-16)
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       dk[dt] = mfma16x16x32(qta, dl, dk[dt]);
     }
     if (tid < 32 && it + 2 < nit) {
-      meta_store((it + 2) % 3);
+      meta_store((it + 2) & 3);
       en_n2 = en_n3;
     }
     if (it + 1 < nit) rows_store(buf ^ 1);
