@@ -184,6 +184,23 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+// Maximum / sum over the whole wave without an LDS round trip: the four
+// butterflies inside each 16-lane row on DPP, then the row swaps; every lane
+// ends with the same, order-fixed result.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));     // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));     // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x));    // row_half_mirror
+  x = fmaxf(x, dpp_mov<0x140>(x));    // row_mirror
+  return row4_max(x);
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return row4_sum(x);
+}
 // Sum over aligned groups of n consecutive lanes, n in {1, 2, 4, 8}
 // (wave-uniform n): xor-1, xor-2, then the 8-lane mirror.
 __device__ __forceinline__ float group_sum_pow2(float x, int n) {

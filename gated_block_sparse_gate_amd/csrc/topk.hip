@@ -33,10 +33,12 @@ constexpr int kTokPerWG = 16;
 __host__ __device__ inline int topk_score_pitch(int NB) { return NB | 1; }
 
 template <int DG>
-__global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void topk_kernel(TopkParams p) {
   constexpr int NS = DG / 16;        // 16-wide d groups
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ uint32_t gath[4][64];             // per wave: keys above the lane-maximum bound
+  __shared__ int selj[4][64];                  // per wave: selected blocks in output order
+  __shared__ float sell[4][64];                // and their log-gates
   float* sc = smem;                            // [16][NBP] scores (odd pitch: no bank conflicts)
   const int NBP = topk_score_pitch(p.NB);
 
@@ -50,6 +52,32 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   const int ntok = min(kTokPerWG, p.T - t0);
   const float inv_sqrt_dg = 1.0f / sqrtf(static_cast<float>(DG));
 
+  // current-block score operands (the token's query and its own prefix key,
+  // DG / 16 consecutive dims per thread) are requested first, so that their
+  // memory latency overlaps the historical scores
+  constexpr int CPT = DG / 16;
+  const int tl_s = tid >> 4, part = tid & 15;
+  float cq[CPT], ck[CPT];
+  {
+    const size_t tok = static_cast<size_t>(b) * p.T + t0 + min(tl_s, ntok - 1);
+    const float* kg = p.k_gate + (tok * p.Hkv + kv) * DG + part * CPT;
+    const float* qg = p.q_gate + (tok * p.Hs + sg) * DG + part * CPT;
+    if constexpr (CPT % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < CPT; i += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(qg + i);
+        const float4 b4 = *reinterpret_cast<const float4*>(kg + i);
+        cq[i] = a4.x; cq[i + 1] = a4.y; cq[i + 2] = a4.z; cq[i + 3] = a4.w;
+        ck[i] = b4.x; ck[i + 1] = b4.y; ck[i + 2] = b4.z; ck[i + 3] = b4.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        cq[i] = qg[i];
+        ck[i] = kg[i];
+      }
+    }
+  }
   // historical scores S^T[key, token] = K Q^T on fp32 MFMA 16x16x4; the k
   // index of MFMA step (s, i) is d = 16 s + 4 (lane / 16) + i, the same for
   // both operands.  Query operand (token = lane % 16) in registers; wave w
@@ -97,14 +125,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
   __syncthreads();
   // current-block score with the token's own prefix key
   {
-    const int tl_s = tid >> 4, part = tid & 15;
     float acc = 0.f;
-    if (tl_s < ntok) {
-      const size_t tok = static_cast<size_t>(b) * p.T + t0 + tl_s;
-      const float* kg = p.k_gate + (tok * p.Hkv + kv) * DG;
-      const float* qg = p.q_gate + (tok * p.Hs + sg) * DG;
-      for (int d = part; d < DG; d += 16) acc = fmaf(qg[d], kg[d], acc);
-    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) acc = fmaf(cq[i], ck[i], acc);
     acc += dpp_mov<0xB1>(acc);
     acc += dpp_mov<0x4E>(acc);
     acc += dpp_mov<0x141>(acc);
@@ -135,11 +158,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
       float mx = sv[0];
 #pragma unroll
       for (int e = 1; e < EM; ++e) mx = fmaxf(mx, sv[e]);
-      mx = wave_max(mx);
+      mx = wave_max_dpp(mx);
       float se = 0.f;
 #pragma unroll
       for (int e = 0; e < EM; ++e) se += fast_exp2((sv[e] - mx) * kLog2e);
-      se = wave_sum(se);
+      se = wave_sum_dpp(se);
       const float lse = mx + __builtin_amdgcn_logf(se) * kLn2;
       const size_t rowid = (static_cast<size_t>(b) * p.T + t0 + tl) * p.Hs + sg;
       // order keys of the historical candidates; 0 elsewhere, which no
@@ -148,7 +171,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
 #pragma unroll
       for (int e = 0; e < EM; ++e) kreg[e] = (lane + 64 * e < c) ? order_key(sv[e]) : 0u;
       uint32_t thr = 0;
-      int need_eq = 0;
+      int n_ge = 0;                 // keys at or above thr
       if (!all) {
         // thr = the largest t with #(keys >= t) >= K, by a bitwise search.
         // The K-th largest lane maximum bounds it from below (the K largest
@@ -184,6 +207,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
             const uint32_t cand = thr | (1u << bit);
             if (wave_count(v >= cand) >= K) thr = cand;
           }
+          // every key >= thr (>= t0k) is among the gathered ones
+          n_ge = wave_count(v >= thr);
         } else {
           for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = thr | (1u << bit);
@@ -192,40 +217,67 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
             for (int e = 0; e < EM; ++e) cnt += wave_count(kreg[e] >= cand);
             if (cnt >= K) thr = cand;
           }
+#pragma unroll
+          for (int e = 0; e < EM; ++e) n_ge += wave_count(kreg[e] >= thr);
         }
+      }
+      // selected historical blocks in ascending order into the wave's LDS
+      // slots, then one contiguous store of the row
+      int base = 0;
+      if (all || n_ge == K) {
+        // every key at or above the threshold is taken (no tie crosses it)
+#pragma unroll
+        for (int e = 0; e < EM; ++e) {
+          const int j = lane + 64 * e;
+          const bool s_in = j < c && (all || kreg[e] >= thr);
+          const uint64_t sm = ballot64(s_in);
+          if (s_in) {
+            const int pos = base + __popcll(sm & lt_mask);
+            selj[wv][pos] = j;
+            sell[wv][pos] = sv[e] - lse;
+          }
+          base += __popcll(sm);
+        }
+      } else {
+        // equal keys at the threshold: the lower block indices first
         int gt = 0;
 #pragma unroll
         for (int e = 0; e < EM; ++e) gt += wave_count(kreg[e] > thr);
-        need_eq = K - gt;
-      }
-      int base = 0, eq_seen = 0;
+        const int need_eq = K - gt;
+        int eq_seen = 0;
 #pragma unroll
-      for (int e = 0; e < EM; ++e) {
-        const int j = lane + 64 * e;
-        const bool hist = j < c;
-        const bool gt = hist && !all && kreg[e] > thr;
-        const bool eq = hist && !all && kreg[e] == thr;
-        const uint64_t em = ballot64(eq);
-        const bool s_in =
-            hist && (all || gt || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
-        eq_seen += __popcll(em);
-        const uint64_t sm = ballot64(s_in);
-        if (s_in) {
-          const int pos = base + __popcll(sm & lt_mask);
-          p.idx[rowid * S + pos] = j;
-          p.logg[rowid * S + pos] = sv[e] - lse;
+        for (int e = 0; e < EM; ++e) {
+          const int j = lane + 64 * e;
+          const bool hist = j < c;
+          const bool eq = hist && kreg[e] == thr;
+          const uint64_t em = ballot64(eq);
+          const bool s_in =
+              hist && (kreg[e] > thr || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
+          eq_seen += __popcll(em);
+          const uint64_t sm = ballot64(s_in);
+          if (s_in) {
+            const int pos = base + __popcll(sm & lt_mask);
+            selj[wv][pos] = j;
+            sell[wv][pos] = sv[e] - lse;
+          }
+          base += __popcll(sm);
         }
-        base += __popcll(sm);
       }
-      if (lane == 0) {
-        p.idx[rowid * S + nsel] = c;
-        p.logg[rowid * S + nsel] = row[c] - lse;
-        p.gate_lse[rowid] = lse;
+      // (base == nsel) the current block, then the padding
+      for (int s2 = lane; s2 < S; s2 += 64) {
+        int jo = -1;
+        float lo = -INFINITY;
+        if (s2 < nsel) {
+          jo = selj[wv][s2];
+          lo = sell[wv][s2];
+        } else if (s2 == nsel) {
+          jo = c;
+          lo = row[c] - lse;
+        }
+        p.idx[rowid * S + s2] = jo;
+        p.logg[rowid * S + s2] = lo;
       }
-      for (int s2 = nsel + 1 + lane; s2 < S; s2 += 64) {
-        p.idx[rowid * S + s2] = -1;
-        p.logg[rowid * S + s2] = -INFINITY;
-      }
+      if (lane == 0) p.gate_lse[rowid] = lse;
       if (p.gate_probs) {
         for (int j = lane; j < p.NB; j += 64)
           p.gate_probs[rowid * p.NB + j] = (j <= c) ? expf(row[j] - lse) : 0.f;
