@@ -18,19 +18,24 @@ namespace sas {
 
 namespace {
 
-// (cos, sin) of pos * theta^(-2i/dg), argument built and reduced in double.
+// (cos, sin) of pos * theta^(-2i/dg), argument built and reduced in double:
+// each thread keeps one frequency i (the thread count is a multiple of dg / 2)
+// and walks positions; the angle is reduced by a two-part 2 pi before sincos.
 __global__ void rope_table_kernel(float2* tab, int T, int dg, double theta) {
   const int half = dg / 2;
-  const long n = static_cast<long>(T) * half;
-  for (long e = blockIdx.x * static_cast<long>(blockDim.x) + threadIdx.x; e < n;
-       e += static_cast<long>(gridDim.x) * blockDim.x) {
-    const int t = static_cast<int>(e / half);
-    const int i = static_cast<int>(e - static_cast<long>(t) * half);
-    const double inv_freq = pow(theta, -2.0 * i / dg);
+  const int nthr = gridDim.x * blockDim.x;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = gid % half;
+  const double inv_freq = pow(theta, -2.0 * i / dg);
+  constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to double
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
+  for (int t = gid / half; t < T; t += nthr / half) {
     const double ang = static_cast<double>(t) * inv_freq;
+    const double k = rint(ang * (1.0 / kTwoPiHi));
+    const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
     double s, c;
-    sincos(ang, &s, &c);
-    tab[e] = make_float2(static_cast<float>(c), static_cast<float>(s));
+    sincos(r, &s, &c);
+    tab[static_cast<size_t>(t) * half + i] = make_float2(static_cast<float>(c), static_cast<float>(s));
   }
 }
 
@@ -173,24 +178,38 @@ __global__ __launch_bounds__(256) void gate_query_kernel(RouterParams p) {
   }
 }
 
-// One workgroup = one 64-token block of one (batch, KV head); wave w owns
-// tokens 16w .. 16w+15.
+// One workgroup = one 64-token block of one (batch, KV head).  Wave w owns a
+// slice of the DG output columns for the block's rows (all 64 rows and DG / 4
+// columns when DG >= 64; at DG = 32 two waves per column tile, 32 rows each),
+// with that slice of the projection weights loaded once into registers as the
+// MFMA B operands, requested before the block is pooled so that they land
+// meanwhile; no weight staging and no barrier between the projection steps.
+// The RMSNorm sums and the RoPE pairs (columns n and n + DG / 2 sit in
+// different waves) go through LDS, and the rows leave as contiguous stores.
 template <int D, int DG>
 __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
-  constexpr int NT = DG / 16;
   constexpr int KP = D + 8;
   constexpr int NPAIR = D / 2;
   constexpr int NSEG = 256 / NPAIR;     // token segments for the prefix scan
   constexpr int SEGL = 64 / NSEG;
-  __shared__ __attribute__((aligned(16))) uint16_t kb[64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t pmx[64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t pmn[64 * KP];
+  constexpr int NTT = DG / 16;          // column tiles
+  constexpr int WC = NTT >= 4 ? 4 : NTT;   // waves across the columns
+  constexpr int WR = 4 / WC;               // waves across the rows
+  constexpr int NTW = NTT / WC;            // column tiles per wave
+  constexpr int MTW = 4 / WR;              // 16-row tiles per wave
+  constexpr int NSTEP = 3 * D / 32;        // projection steps (max, min, mean sections)
+  constexpr int KBUF = 3 * 64 * KP * 2;    // bytes of the key rows and the two prefix pools
+  constexpr int YBUF = 64 * DG * 4;        // bytes of the normalised rows (reuse the same LDS)
+  static_assert(WC * NTW == NTT && WR * MTW == 4, "wave tiling");
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[KBUF > YBUF ? KBUF : YBUF];
   __shared__ float segmx[NSEG * D];
   __shared__ float segmn[NSEG * D];
-  __shared__ float wsum[4][DG];
-  // weight columns of 32-wide steps, double-buffered (as in gate_query_kernel)
-  constexpr int WROWB = 64;
-  __shared__ __attribute__((aligned(16))) uint8_t wls[2][DG * WROWB];
+  __shared__ float csum[4][DG];          // per wave: its rows' mean-section column totals
+  __shared__ float ssum[WC][64];         // per column group: each row's sum of squares
+  uint16_t* const kb = reinterpret_cast<uint16_t*>(kbuf);
+  uint16_t* const pmx = kb + 64 * KP;
+  uint16_t* const pmn = kb + 2 * 64 * KP;
+  float* const ybuf = reinterpret_cast<float*>(kbuf);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -198,16 +217,20 @@ __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
   const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int t0 = c * 64;
   const int ntok = min(64, p.T - t0);
+  const int cg = wv % WC, rg = wv / WC;   // the wave's column group and row group
 
-  const uint16_t* wt = p.wkT + static_cast<size_t>(kv) * DG * (3 * D);
-  auto wstage = [&](int f, int buf) __attribute__((always_inline)) {
-    for (int m = wv; m < DG / 16; m += 4) {
-      const int u = m * 64 + lane, n = u >> 2;
-      load_lds16(wt + static_cast<size_t>(n) * (3 * D) + f + (((u & 3) ^ ((n >> 2) & 3)) << 3),
-                 &wls[buf][m * 1024]);
+  // the wave's weight slice, B operand of step s and column tile nt: column
+  // n = 16 (cg NTW + nt) + lane % 16, inputs 32 s + 8 (lane / 16) .. + 7
+  uint4 bw[NSTEP][NTW];
+  {
+    const uint16_t* wt = p.wkT + static_cast<size_t>(kv) * DG * (3 * D) + 8 * g4;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const uint16_t* wr = wt + static_cast<size_t>(16 * (cg * NTW + nt) + l16) * (3 * D);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) bw[st][nt] = ld16(wr + 32 * st);
     }
-  };
-  wstage(0, 0);                 // lands while the block is pooled
+  }
 
   for (int u = tid; u < 64 * (D / 8); u += 256) {
     const int row = u / (D / 8), ch = u - row * (D / 8);
@@ -264,80 +287,134 @@ __global__ __launch_bounds__(256) void gate_key_kernel(RouterParams p) {
   }
   __syncthreads();
 
-  const int arow = wv * 16 + l16;
-  floatx4 amm[NT], ak[NT];
+  // [max; min] and mean-section projections of the wave's rows and columns;
+  // C layout: element i of tile (mt, nt) is row 16 (rg MTW + mt) + 4 (lane /
+  // 16) + i of the block, column 16 (cg NTW + nt) + lane % 16
+  floatx4 amm[MTW][NTW], ak[MTW][NTW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    amm[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    ak[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  // inputs f .. f + 31 of the 3D (max, min, mean sections) against the
-  // staged weight columns; the next step's weights land meanwhile
-  wait_vmem_all();
-  __syncthreads();
-  for (int f = 0, it = 0; f < 3 * D; f += 32, ++it) {
-    const int buf = it & 1;
-    const bool more = f + 32 < 3 * D;
-    if (more) wstage(f + 32, buf ^ 1);
-    const uint16_t* src = (f < D) ? &pmx[arow * KP + f]
-                                  : (f < 2 * D) ? &pmn[arow * KP + f - D] : &kb[arow * KP + f - 2 * D];
-    const uint4 av = ld16(src + g4 * 8);
+  for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = nt * 16 + l16;
-      const uint4 bv = ld16(&wls[buf][n * WROWB + ((g4 ^ ((n >> 2) & 3)) << 4)]);
-      if (f < 2 * D)
-        amm[nt] = mfma16x16x32(av, bv, amm[nt]);
-      else
-        ak[nt] = mfma16x16x32(av, bv, ak[nt]);
+    for (int nt = 0; nt < NTW; ++nt) {
+      amm[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      ak[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    if (more) wait_vmem_all();
-    __syncthreads();
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    const int f = 32 * st;
+    const uint16_t* src = (f < D) ? pmx + f : (f < 2 * D) ? pmn + (f - D) : kb + (f - 2 * D);
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+      const uint4 av = ld16(src + (16 * (rg * MTW + mt) + l16) * KP + 8 * g4);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        if (f < 2 * D)
+          amm[mt][nt] = mfma16x16x32(av, bw[st][nt], amm[mt][nt]);
+        else
+          ak[mt][nt] = mfma16x16x32(av, bw[st][nt], ak[mt][nt]);
+      }
+    }
   }
 
-  // prefix sum of the per-token mean-section projections over the block
+  // prefix sum over the block's rows of the per-token mean-section
+  // projections: inside a lane, across the four lane groups, across the
+  // wave's row tiles, then across the row groups (WR > 1)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    floatx4 v = ak[nt];
-    v[1] += v[0];
-    v[2] += v[1];
-    v[3] += v[2];
-    const float tot = v[3];
-    float s = tot;
-    float t = __shfl_up(s, 16, 64);
-    if (g4 >= 1) s += t;
-    t = __shfl_up(s, 32, 64);
-    if (g4 >= 2) s += t;
-    const float excl = s - tot;
-    v[0] += excl;
-    v[1] += excl;
-    v[2] += excl;
-    v[3] += excl;
-    ak[nt] = v;
-    if (g4 == 3) wsum[wv][nt * 16 + l16] = s;
+  for (int nt = 0; nt < NTW; ++nt) {
+    float carry = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+      floatx4 v = ak[mt][nt];
+      v[1] += v[0];
+      v[2] += v[1];
+      v[3] += v[2];
+      float sg = v[3];
+      float t = __shfl_up(sg, 16, 64);
+      if (g4 >= 1) sg += t;
+      t = __shfl_up(sg, 32, 64);
+      if (g4 >= 2) sg += t;
+      const float excl = carry + sg - v[3];
+      v[0] += excl;
+      v[1] += excl;
+      v[2] += excl;
+      v[3] += excl;
+      ak[mt][nt] = v;
+      carry += __shfl(sg, 48 + l16, 64);    // the tile's total (lane group 3)
+    }
+    if (g4 == 0) csum[wv][16 * (cg * NTW + nt) + l16] = carry;
   }
   __syncthreads();
+  float ss_part[MTW][4];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss_part[mt][i] = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int col = 16 * (cg * NTW + nt) + l16;
     float off = 0.f;
-    for (int w2 = 0; w2 < wv; ++w2) off += wsum[w2][nt * 16 + l16];
+    for (int r2 = 0; r2 < rg; ++r2) off += csum[r2 * WC + cg][col];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tl = 16 * (rg * MTW + mt) + 4 * g4 + i;
+        const float y = amm[mt][nt][i] + (ak[mt][nt][i] + off) / static_cast<float>(tl + 1);
+        amm[mt][nt][i] = y;
+        ss_part[mt][i] += y * y;
+      }
+  }
+  // each row's sum of squares over the wave's columns (16 lanes of a row
+  // group), then over the column groups through LDS
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tl = wv * 16 + g4 * 4 + i;
-      amm[nt][i] += (ak[nt][i] + off) / static_cast<float>(tl + 1);
+      const float r = row16_sum(ss_part[mt][i]);
+      if (l16 == 0) ssum[cg][16 * (rg * MTW + mt) + 4 * g4 + i] = r;
+    }
+  __syncthreads();                       // (also: every read of the pooled rows is done)
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tl = 16 * (rg * MTW + mt) + 4 * g4 + i;
+      float ss = 0.f;
+#pragma unroll
+      for (int g = 0; g < WC; ++g) ss += ssum[g][tl];
+      const float rs = 1.0f / sqrtf(ss * (1.0f / DG) + p.eps);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int col = 16 * (cg * NTW + nt) + l16;
+        ybuf[tl * DG + col] = amm[mt][nt][i] * rs * p.w_kn[col];
+      }
+    }
+  __syncthreads();
+  // rotate-half RoPE at the block start 64 c; four threads per row, each
+  // DG / 8 consecutive pairs (n, n + DG / 2)
+  {
+    constexpr int HALF = DG / 2, PPT = DG / 8;
+    const int tl = tid >> 2, n0 = (tid & 3) * PPT;
+    if (tl < ntok) {
+      float* out = p.k_gate + ((static_cast<size_t>(b) * p.T + t0 + tl) * p.Hkv + kv) * DG;
+      const float2* rope = p.rope + static_cast<size_t>(t0) * HALF;
+#pragma unroll
+      for (int q = 0; q < PPT; q += 4) {
+        float4 o1, o2;
+        float* a1 = &o1.x;
+        float* a2 = &o2.x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + q + e;
+          const float y1 = ybuf[tl * DG + n], y2 = ybuf[tl * DG + n + HALF];
+          const float2 cs = rope[n];
+          a1[e] = y1 * cs.x - y2 * cs.y;
+          a2[e] = y2 * cs.x + y1 * cs.y;
+        }
+        *reinterpret_cast<float4*>(out + n0 + q) = o1;
+        *reinterpret_cast<float4*>(out + n0 + q + HALF) = o2;
+      }
     }
   }
-  int pos[4];
-  float* out[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tl = wv * 16 + g4 * 4 + i;
-    pos[i] = t0;
-    out[i] = (tl < ntok)
-                 ? p.k_gate + ((static_cast<size_t>(b) * p.T + t0 + tl) * p.Hkv + kv) * DG
-                 : nullptr;
-  }
-  norm_rope_store<DG>(amm, p.w_kn, p.eps, p.rope, pos, out, l16);
 }
 
 template <int D, int DG>
@@ -361,8 +438,9 @@ hipError_t launch_transpose_w(const uint16_t* in, uint16_t* out, int H, int F, i
 }
 
 hipError_t launch_rope_table(float2* tab, int T, int dg, double theta, hipStream_t st) {
+  // 256 threads per workgroup: a multiple of dg / 2 (16, 32 or 64)
   const long nr = static_cast<long>(T) * (dg / 2);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(min(4096L, (nr + 255) / 256))),
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(min(1024L, (nr + 255) / 256))),
                      dim3(256), 0, st, tab, T, dg, theta);
   return hipGetLastError();
 }
@@ -375,7 +453,7 @@ hipError_t launch_router(const RouterParams& p0, const uint16_t* wq, const uint1
   p.wkT = wkT;
   p.rope = rope;
   const long nr = static_cast<long>(p.T) * (p.dg / 2);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(min(4096L, (nr + 255) / 256))),
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(min(1024L, (nr + 255) / 256))),
                      dim3(256), 0, st, rope, p.T, p.dg, theta);
   const long nq = static_cast<long>(p.Hs) * p.Gs * p.D * p.dg;
   const long nk = static_cast<long>(p.Hkv) * 3 * p.D * p.dg;
