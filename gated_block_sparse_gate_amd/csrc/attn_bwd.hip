@@ -104,30 +104,36 @@ __global__ __launch_bounds__(256) void csr_count_kernel(BwdParams p) {
 }
 
 // cnt2d[c][j] -> exclusive offset of query block c inside column j; column
-// totals -> rowptr[j].
+// totals -> rowptr[j].  Workgroup = 16 columns x 16 segments of query blocks
+// (thread: column tid % 16, segment tid / 16; 16 consecutive columns make a
+// 64-byte row piece); segment sums, their exclusive scan through LDS, then
+// the offsets.
 __global__ __launch_bounds__(256) void csr_colscan_kernel(BwdParams p) {
-  __shared__ int part[4][64];
-  const int lane = threadIdx.x & 63, sg = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + lane;
+  constexpr int NC = 16, NSG = 16;
+  __shared__ int part[NSG][NC];
+  const int cl = threadIdx.x % NC, sg = threadIdx.x / NC;
+  const int j = blockIdx.x * NC + cl;
   const int bk = blockIdx.y;
   const int NQB = p.NB;
-  const int seglen = (NQB + 3) / 4;
+  const int seglen = (NQB + NSG - 1) / NSG;
   const int c0 = min(NQB, sg * seglen), c1 = min(NQB, c0 + seglen);
   int32_t* col = p.cnt2d + static_cast<size_t>(bk) * NQB * p.NB + j;
   int sum = 0;
-  if (j < p.NB)
+  if (j < p.NB) {
+#pragma unroll 8
     for (int c = c0; c < c1; ++c) sum += col[static_cast<size_t>(c) * p.NB];
-  part[sg][lane] = sum;
+  }
+  part[sg][cl] = sum;
   __syncthreads();
   int off = 0;
-  for (int s = 0; s < sg; ++s) off += part[s][lane];
+  for (int s2 = 0; s2 < sg; ++s2) off += part[s2][cl];
   if (j < p.NB) {
     for (int c = c0; c < c1; ++c) {
       const int v = col[static_cast<size_t>(c) * p.NB];
       col[static_cast<size_t>(c) * p.NB] = off;
       off += v;
     }
-    if (sg == 3) p.rowptr[static_cast<size_t>(bk) * (p.NB + 1) + j] = off;
+    if (sg == NSG - 1) p.rowptr[static_cast<size_t>(bk) * (p.NB + 1) + j] = off;
   }
 }
 
@@ -950,7 +956,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   const int NQB = p.NB;
   const unsigned nblk = static_cast<unsigned>(p.B) * p.Hs * NQB;
   hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 63) / 64, p.B * p.Hs), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 15) / 16, p.B * p.Hs), dim3(256), 0, st, p);
   hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hs), dim3(1024), 0, st, p);
   hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
   timing_mark(1, st);
