@@ -58,24 +58,6 @@ __device__ __forceinline__ void delta_rows(const uint16_t* o, const float* o32,
   if (part == 0 && row < nrows) delta[row] = acc;
 }
 
-// The backward's first launch: the dQ walk's staging order and Delta side by
-// side.  The order's workgroups (one token group per wave; a serial,
-// latency-bound placement) come first, and the Delta rows (bandwidth-bound)
-// fill the slots beside them, so the two overlap.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, WalkOrderParams wo,
-                                                       int nord_blocks, int ngroups,
-                                                       int wave_words, long nrows) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t prep_smem[];
-  if (static_cast<int>(blockIdx.x) < nord_blocks) {
-    const int w = threadIdx.x >> 6;
-    const int g = blockIdx.x * 4 + w;
-    walk_order_group(wo, g, g < ngroups, threadIdx.x & 63, prep_smem + w * wave_words);
-    return;
-  }
-  delta_rows<D>(p.o, p.o32, p.dout, p.delta, nrows, static_cast<long>(blockIdx.x) - nord_blocks);
-}
-
 // Per (b, selection head sg, query block c): which of the 64 tokens selected
 // each block j.
 __device__ __forceinline__ void build_token_masks(const BwdParams& p, unsigned long long* mask,
@@ -88,19 +70,46 @@ __device__ __forceinline__ void build_token_masks(const BwdParams& p, unsigned l
   }
 }
 
-__global__ __launch_bounds__(256) void csr_count_kernel(BwdParams p) {
-  __shared__ unsigned long long mask[kMaxNB];
+// CSR counts of query block (b, sg, c) = workgroup index bid: cnt2d[c][j] =
+// how many of its tokens selected block j (mask: NB words of LDS).
+__device__ __forceinline__ void csr_count_block(const BwdParams& p, unsigned long long* mask,
+                                                int bid) {
   const int NQB = p.NB;
-  const int bid = blockIdx.x;
   const int sg = bid % p.Hs, rest = bid / p.Hs;
   const int c = rest % NQB, b = rest / NQB;
   const int ntok = min(64, p.T - c * 64);
-  for (int j = threadIdx.x; j < p.NB; j += 256) mask[j] = 0ull;
+  for (int j = threadIdx.x; j < p.NB; j += blockDim.x) mask[j] = 0ull;
   __syncthreads();
   build_token_masks(p, mask, b, sg, c, ntok);
   __syncthreads();
   int32_t* out = p.cnt2d + ((static_cast<size_t>(b) * p.Hs + sg) * NQB + c) * p.NB;
-  for (int j = threadIdx.x; j < p.NB; j += 256) out[j] = __popcll(mask[j]);
+  for (int j = threadIdx.x; j < p.NB; j += blockDim.x) out[j] = __popcll(mask[j]);
+}
+
+// The backward's first launch: the dQ walk's staging order, the CSR counts
+// and Delta side by side.  The order's workgroups (one token group per wave; a
+// serial, latency-bound placement) come first, then the counts' (one query
+// block each, short and latency-bound), and the Delta rows (bandwidth-bound)
+// fill the slots beside them, so the three overlap.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, WalkOrderParams wo,
+                                                       int nord_blocks, int ngroups,
+                                                       int wave_words, int ncnt_blocks,
+                                                       long nrows) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t prep_smem[];
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid < nord_blocks) {
+    const int w = threadIdx.x >> 6;
+    const int g = bid * 4 + w;
+    walk_order_group(wo, g, g < ngroups, threadIdx.x & 63, prep_smem + w * wave_words);
+    return;
+  }
+  if (bid < nord_blocks + ncnt_blocks) {
+    csr_count_block(p, reinterpret_cast<unsigned long long*>(prep_smem), bid - nord_blocks);
+    return;
+  }
+  delta_rows<D>(p.o, p.o32, p.dout, p.delta, nrows,
+                static_cast<long>(bid) - nord_blocks - ncnt_blocks);
 }
 
 // cnt2d[c][j] -> exclusive offset of query block c inside column j; column
@@ -949,13 +958,15 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
     const int nord = (ngroups + 3) / 4;
     const size_t wave_bytes = walk_order_smem_bytes(p.NB);
     const long ndelta = (nrows * 16 + 255) / 256;
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(static_cast<unsigned>(nord + ndelta)), dim3(256),
-                       4 * wave_bytes, st, p, wo, nord, ngroups,
-                       static_cast<int>(wave_bytes / 4), nrows);
+    const int ncnt = p.B * p.Hs * p.NB;
+    // four waves' staging-order scratch; the counts' NB mask words fit in it
+    const size_t lds = std::max(4 * wave_bytes, sizeof(unsigned long long) * p.NB);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(static_cast<unsigned>(nord + ncnt + ndelta)),
+                       dim3(256), lds, st, p, wo, nord, ngroups, static_cast<int>(wave_bytes / 4),
+                       ncnt, nrows);
   }
   const int NQB = p.NB;
   const unsigned nblk = static_cast<unsigned>(p.B) * p.Hs * NQB;
-  hipLaunchKernelGGL(csr_count_kernel, dim3(nblk), dim3(256), 0, st, p);
   hipLaunchKernelGGL(csr_colscan_kernel, dim3((p.NB + 15) / 16, p.B * p.Hs), dim3(256), 0, st, p);
   hipLaunchKernelGGL(csr_rowptr_kernel, dim3(p.B * p.Hs), dim3(1024), 0, st, p);
   hipLaunchKernelGGL(csr_fill_kernel, dim3(nblk), dim3(256), 0, st, p);
