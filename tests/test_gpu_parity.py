@@ -99,6 +99,32 @@ def test_gate_score(w):
     assert_close("k_gate", kg, P["kg_all"], ROUTER_ABS, ROUTER_ABS)
 
 
+# (D, dg) pairs the parity shapes above leave out, so that every tiling of
+# the gate-key projection (column groups of four waves at dg >= 64, two
+# column groups of two row groups at dg = 32) runs with both head sizes;
+# ragged last blocks
+ROUTER_DIMS = [
+    W("d128_dg32", 300, 4, 2, 128, 32, 3),
+    W("d128_dg64", 200, 8, 2, 128, 64, 3),
+    W("d64_dg128", 260, 4, 1, 64, 128, 3),
+]
+
+
+@pytest.mark.parametrize("w", ROUTER_DIMS, ids=[c.name for c in ROUTER_DIMS])
+def test_gate_score_dims(w):
+    x = synth.prefill_inputs(w, seed=3, device="cpu", with_dout=False)
+    x64 = {k: O.as64(v) for k, v in x.items()}
+    r = O.route(x64["q"], x64["k"], x64["wq"], x64["wk"], x64["w_qn"], x64["w_kn"], w.topk,
+                w.theta, w.eps)
+    kg_all = O.gate_key(x64["k"], x64["wk"], x64["w_kn"], w.theta, w.eps)
+    d = {k: v.cuda() for k, v in x.items()}
+    qg, kg = sas.gate_score(d["q"], d["k"], d["wq"], d["wk"], d["w_qn"], d["w_kn"], w.topk,
+                            w.theta, w.eps)
+    torch.cuda.synchronize()
+    assert_close("q_gate", qg, r["qg"], ROUTER_ABS, ROUTER_ABS)
+    assert_close("k_gate", kg, kg_all, ROUTER_ABS, ROUTER_ABS)
+
+
 def _nontie(r):
     return ~r["near_tie"]
 
