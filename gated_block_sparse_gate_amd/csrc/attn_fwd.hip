@@ -284,12 +284,33 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     }
     return true;
   };
+  // the block of union position u, whether this lane's row selected it, and
+  // the row's log2 gate for it (looked up one visit ahead, so that the LDS
+  // round trips overlap the current visit's MFMA work)
+  struct Visit {
+    int j;
+    bool sel;
+    float lgv;
+  };
+  auto look = [&](int u) __attribute__((always_inline)) {
+    Visit r{0, false, 0.f};
+    if (u < nU) {
+      r.j = ulist[u];
+      const uint32_t jbit = 1u << (r.j & 31);
+      const int jw = r.j >> 5;
+      const uint32_t w = bits[tl * NBW + jw];
+      r.sel = valid && (w & jbit);
+      if (r.sel) r.lgv = lgs[tl * S + pcnt[tl * NBW + jw] + __popc(w & (jbit - 1u))];
+    }
+    return r;
+  };
   int v = next_active(0);
   asm volatile("" ::: "memory");
   if (lane == 0) {                       // done with every block before its first needed one
     prog[0][wv] = v;
     prog[1][wv] = v;
   }
+  Visit cur = look(v);
   bool failed = false;
   while (v < nU) {
     if (!wait_slot(0, v)) {
@@ -298,16 +319,10 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     }
     const uint8_t* stk = ring + (v % RK) * KB;
     const uint8_t* stv = ring + RK * KB + (v % RV) * VB;
-    const int j = ulist[v];
-    const uint32_t jbit = 1u << (j & 31);
-    const int jw = j >> 5;
-    const bool sel = valid && (bits[tl * NBW + jw] & jbit);
+    const int j = cur.j;
+    const bool sel = cur.sel;
     const bool maybe_cur = j >= cfirst;  // the current block of some token of the group
-    float lgv = 0.f;
-    if (sel) {
-      const int rank = pcnt[tl * NBW + jw] + __popc(bits[tl * NBW + jw] & (jbit - 1u));
-      lgv = lgs[tl * S + rank];
-    }
+    const float lgv = cur.lgv;
     // S^T[key, row] = K[key,:] . Q[row,:]
     floatx4 sacc[4];
 #pragma unroll
@@ -323,6 +338,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
     asm volatile("" ::: "memory");
     if (lane == 0) prog[0][wv] = vnext;  // after this wave's last K read of the slot
     asm volatile("" ::: "memory");
+    const Visit nxt = look(vnext);
     // maximum of this lane's raw scores over the keys its row may see (the
     // row's 64 keys are spread over the 4 lanes g4 of the row); in the
     // current block the row sees keys 0 .. t - 64 j
@@ -410,6 +426,7 @@ __global__ __launch_bounds__(1024) void sparse_fwd_kernel(FwdParams a, int ncw, 
       }
     }
     v = vnext;
+    cur = nxt;
     asm volatile("" ::: "memory");
     if (lane == 0) prog[1][wv] = v;      // after this wave's last V^T read of the slot
     asm volatile("" ::: "memory");
