@@ -90,11 +90,14 @@ __device__ __forceinline__ void norm_rope_store(floatx4 (&acc)[DG / 16], const f
 // one chunk of 16 consecutive rows hit distinct banks), and each wave's query
 // operands for the next step load while the current step runs.
 template <int DG>
-__global__ __launch_bounds__(256) void gate_query_kernel(RouterParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gate_query_kernel(RouterParams p) {
   constexpr int NT = DG / 16;
   constexpr int MT = 2;
   constexpr int WROWB = 64;                      // bytes per staged weight row
   __shared__ __attribute__((aligned(16))) uint8_t wls[2][DG * WROWB];
+  constexpr int YP = DG + 16;          // floats per staged output row (the four row
+                                       // groups of a store fall on distinct banks)
+  __shared__ __attribute__((aligned(16))) float yrows[4 * 16 * YP];   // per wave: one 16-row tile
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -163,18 +166,30 @@ __global__ __launch_bounds__(256) void gate_query_kernel(RouterParams p) {
     }
     __syncthreads();
   }
+  // each 16-row tile: RMSNorm and RoPE into the wave's LDS rows, then whole
+  // rows out as 16-byte stores (the wave's LDS accesses are performed in
+  // order, so its rows are complete when it reads them back, and the next
+  // tile's writes come after these reads)
+  float* const yb = yrows + wv * 16 * YP;
+  constexpr int CH = DG / 4;             // 16-byte chunks per row
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     int pos[4];
-    float* out[4];
+    float* yrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const long r = r0 + mt * 16 + g4 * 4 + i;
-      const bool v = r < nrows;
-      pos[i] = v ? static_cast<int>(r % p.T) : 0;
-      out[i] = v ? p.q_gate + (r * p.Hs + sg) * DG : nullptr;
+      pos[i] = r < nrows ? static_cast<int>(r % p.T) : 0;
+      yrow[i] = yb + (g4 * 4 + i) * YP;
     }
-    norm_rope_store<DG>(acc[mt], p.w_qn, p.eps, p.rope, pos, out, l16);
+    norm_rope_store<DG>(acc[mt], p.w_qn, p.eps, p.rope, pos, yrow, l16);
+    for (int e = lane; e < 16 * CH; e += 64) {
+      const int rl = e / CH, ch = e - rl * CH;
+      const long r = r0 + mt * 16 + rl;
+      if (r < nrows)
+        *reinterpret_cast<float4*>(p.q_gate + (r * p.Hs + sg) * DG + 4 * ch) =
+            *reinterpret_cast<const float4*>(yb + rl * YP + 4 * ch);
+    }
   }
 }
 
