@@ -83,21 +83,25 @@ __device__ __forceinline__ void norm_rope_store(floatx4 (&acc)[DG / 16], const f
 }
 
 // One workgroup = 128 token rows of one selection head, wave w owning rows
-// 32 w .. 32 w + 31 (two 16-row tiles) x all DG gate columns.  The weight
-// columns are staged through LDS in 32-wide steps shared by the four waves
-// (asynchronous global -> LDS copies, double-buffered; 64-byte rows whose
-// 16-byte chunks are XOR-swizzled by (row >> 2) & 3, so that 16 lanes reading
+// 32 w .. 32 w + 31 (two 16-row tiles) x all DG gate columns.  The weights
+// are staged through LDS 64 inputs at a time, shared by the four waves
+// (asynchronous global -> LDS copies, double-buffered; 128-byte rows whose
+// 16-byte chunks are XOR-swizzled by (row >> 1) & 7, so that 16 lanes reading
 // one chunk of 16 consecutive rows hit distinct banks), and each wave's query
-// operands for the next step load while the current step runs.
+// operands for the next stage load while the current one runs: 32 contiguous
+// bytes of a row per lane, so each row's 128-byte line is read whole.
 template <int DG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gate_query_kernel(RouterParams p) {
   constexpr int NT = DG / 16;
   constexpr int MT = 2;
-  constexpr int WROWB = 64;                      // bytes per staged weight row
-  __shared__ __attribute__((aligned(16))) uint8_t wls[2][DG * WROWB];
+  constexpr int WROWB = 128;                     // bytes per staged weight row (64 inputs)
   constexpr int YP = DG + 16;          // floats per staged output row (the four row
                                        // groups of a store fall on distinct banks)
-  __shared__ __attribute__((aligned(16))) float yrows[4 * 16 * YP];   // per wave: one 16-row tile
+  constexpr int WLSB = 2 * DG * WROWB, YRB = 4 * 16 * YP * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[WLSB > YRB ? WLSB : YRB];
+  uint8_t (*wls)[DG * WROWB] = reinterpret_cast<uint8_t (*)[DG * WROWB]>(lds_raw);
+  // the output rows reuse the weight stage's LDS after the loop's last barrier
+  float* const yrows = reinterpret_cast<float*>(lds_raw);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -121,48 +125,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     xr[mt] = p.q + ((ok[mt] ? r : 0) * p.Hq + static_cast<long>(sg) * p.Gs) * p.D;
   }
   const uint16_t* wt = p.wqT + static_cast<size_t>(sg) * DG * F;
-  // weight columns f .. f + 31 of all DG rows into buffer buf: copy m moves
-  // units 64 m .. 64 m + 63 (unit u = row u / 4, slot u % 4 holding chunk
-  // (u % 4) ^ swizzle)
+  // weight inputs f .. f + 63 of all DG rows into buffer buf: copy m moves
+  // units 64 m .. 64 m + 63 (unit u = row u / 8, slot u % 8 holding chunk
+  // (u % 8) ^ swizzle)
   auto wstage = [&](int f, int buf) __attribute__((always_inline)) {
-    for (int m = wv; m < DG / 16; m += 4) {
-      const int u = m * 64 + lane, n = u >> 2;
-      load_lds16(wt + static_cast<size_t>(n) * F + f + (((u & 3) ^ ((n >> 2) & 3)) << 3),
+    for (int m = wv; m < DG * WROWB / 1024; m += 4) {
+      const int u = m * 64 + lane, n = u >> 3;
+      load_lds16(wt + static_cast<size_t>(n) * F + f + (((u & 7) ^ ((n >> 1) & 7)) << 3),
                  &wls[buf][m * 1024]);
     }
   };
-  auto qload = [&](int f, uint4 (&a)[MT]) __attribute__((always_inline)) {
+  // inputs f + 16 (lane / 16) .. + 15 of each tile row: 32 contiguous bytes
+  // per lane, whole 128-byte lines per row and instruction pair; MFMA half
+  // h takes the inputs f + 16 (lane / 16) + 8 h .. + 7 on both operands
+  auto qload = [&](int f, uint4 (&a)[MT][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      a[mt] = ok[mt] ? ld16(xr[mt] + f + g4 * 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        a[mt][h] = ok[mt] ? ld16(xr[mt] + f + g4 * 16 + 8 * h) : make_uint4(0, 0, 0, 0);
   };
-  uint4 av[MT];
+  uint4 av[MT][2];
   wstage(0, 0);
   qload(0, av);
   wait_vmem_all();
   __syncthreads();
-  for (int f = 0, it = 0; f < F; f += 32, ++it) {
+  for (int f = 0, it = 0; f < F; f += 64, ++it) {
     const int buf = it & 1;
-    const bool more = f + 32 < F;
-    uint4 an[MT];
+    const bool more = f + 64 < F;
+    uint4 an[MT][2];
     if (more) {
-      wstage(f + 32, buf ^ 1);     // the copies first, then this wave's query loads
-      qload(f + 32, an);
+      wstage(f + 64, buf ^ 1);     // the copies first, then this wave's query loads
+      qload(f + 64, an);
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = nt * 16 + l16;
-      const uint4 bv = ld16(&wls[buf][n * WROWB + ((g4 ^ ((n >> 2) & 3)) << 4)]);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma16x16x32(av[mt], bv, acc[mt][nt]);
-    }
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = nt * 16 + l16;
+        const uint4 bv = ld16(&wls[buf][n * WROWB + (((2 * g4 + h) ^ ((n >> 1) & 7)) << 4)]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma16x16x32(av[mt][h], bv, acc[mt][nt]);
+      }
     if (more) {
-      // all but the MT query loads: the next step's weights have landed
-      static_assert(MT < 16, "vmcnt immediate");
-      __builtin_amdgcn_s_waitcnt(0x0f70 | MT);
+      // all but the 2 MT query loads: the next stage's weights have landed
+      static_assert(2 * MT < 16, "vmcnt immediate");
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * MT));
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) av[mt] = an[mt];
+      for (int mt = 0; mt < MT; ++mt) {
+        av[mt][0] = an[mt][0];
+        av[mt][1] = an[mt][1];
+      }
     }
     __syncthreads();
   }
