@@ -107,6 +107,8 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeParams p) {
 template <bool LONG>
 __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
   __shared__ uint32_t gath[4][64];
+  __shared__ int selj[4][64];                  // per wave: selected blocks in output order
+  __shared__ float sell[4][64];                // and their log-gates
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int unit = blockIdx.x * 4 + wv;
   if (unit >= p.B * p.Hs) return;
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
       return (lane + 64 * e < c) ? order_key(score(e)) : 0u;
     };
     uint32_t thr = 0;
-    int need_eq = 0;
+    int n_ge = 0;                 // keys at or above thr
     if (!all) {
       // thr = the largest t with #(keys >= t) >= K, by a bitwise search.
       // The K-th largest lane maximum bounds it from below (the K largest
@@ -236,32 +238,59 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeParams p) {
           if (cnt >= K) thr = cand;
         }
       }
+      n_ge = 0;
+      each_slot([&](int e) { n_ge += wave_count(key(e) >= thr); });
+    }
+    // selected historical blocks in ascending order into the wave's LDS
+    // slots (read back for one contiguous store of the unit's row)
+    int base = 0;
+    if (all || n_ge == K) {
+      // every key at or above the threshold is taken (no tie crosses it)
+      each_cand([&](int e) {
+        const int j = lane + 64 * e;
+        const bool s_in = j < c && (all || key(e) >= thr);
+        const uint64_t sm = ballot64(s_in);
+        if (s_in) {
+          const int pos = base + __popcll(sm & lt_mask);
+          selj[wv][pos] = j;
+          sell[wv][pos] = score(e) - lse;
+        }
+        base += __popcll(sm);
+      });
+    } else {
+      // equal keys at the threshold: the lower block indices first
       int gt = 0;
       each_slot([&](int e) { gt += wave_count(key(e) > thr); });
-      need_eq = K - gt;
+      const int need_eq = K - gt;
+      int eq_seen = 0;
+      each_cand([&](int e) {
+        const int j = lane + 64 * e;
+        const bool hist = j < c;
+        const uint32_t kk = key(e);
+        const bool eq = hist && kk == thr;
+        const uint64_t em = ballot64(eq);
+        const bool s_in = hist && (kk > thr || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
+        eq_seen += __popcll(em);
+        const uint64_t sm = ballot64(s_in);
+        if (s_in) {
+          const int pos = base + __popcll(sm & lt_mask);
+          selj[wv][pos] = j;
+          sell[wv][pos] = score(e) - lse;
+        }
+        base += __popcll(sm);
+      });
     }
-    int base = 0, eq_seen = 0;
-    each_cand([&](int e) {
-      const int j = lane + 64 * e;
-      const bool hist = j < c;
-      const uint32_t kk = key(e);
-      const bool gt = hist && !all && kk > thr;
-      const bool eq = hist && !all && kk == thr;
-      const uint64_t em = ballot64(eq);
-      const bool s_in =
-          hist && (all || gt || (eq && (eq_seen + __popcll(em & lt_mask)) < need_eq));
-      eq_seen += __popcll(em);
-      const uint64_t sm = ballot64(s_in);
-      if (s_in) put(base + __popcll(sm & lt_mask), j, score(e) - lse);
-      base += __popcll(sm);
-    });
   };
   if constexpr (!LONG)
     select(std::integral_constant<int, kMaxNB / 64>{}, std::true_type{});
   else
     select(std::integral_constant<int, kMaxDecodeNB / 64>{}, std::false_type{});
-  if (lane == 0) put(nsel, c, sc[c] - lse);
-  for (int s2 = nsel + 1 + lane; s2 < S; s2 += 64) put(s2, -1, -INFINITY);
+  // the wave's LDS accesses are performed in order: its slots are complete
+  for (int s2 = lane; s2 < S; s2 += 64) {
+    if (s2 < nsel) put(s2, selj[wv][s2], sell[wv][s2]);
+    else if (s2 == nsel) put(s2, c, sc[c] - lse);
+    else put(s2, -1, -INFINITY);
+  }
 }
 
 // Sum over aligned groups of N consecutive lanes inside 16-lane rows
